@@ -1,0 +1,175 @@
+/*
+ * gdr2_oracle.c -- fp64 CPU oracle for the Gated DeltaNet-2 state recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * HIP library is checked against.  Only the tests, the smoke entry point and
+ * the CPU-baseline leg of the benchmark may load it; the library itself never
+ * links, loads or calls it, and it shares no code with the library.
+ *
+ * Sources (cited by page title and section):
+ *   [GDN2]  "Gated DeltaNet-2: 선형 어텐션에서 삭제와 쓰기 게이트 분리"
+ *           (juhoplayground.github.io), section "Gated Delta Rule-2 업데이트
+ *           수식" (the update equation and its symbol table).
+ *   [SDM]   "[논문리뷰] Sparse Delta Memory: Scaling the State of Linear RNNs
+ *           through Sparsity", section 3 "Method & Key Results" (a learned
+ *           initial memory M_0: the optional initial state S0 below).
+ *   [MC]    "Memory Caching(MC): 길이에 따라 메모리가 커지는 RNN에 대한 연구",
+ *           section "체크포인트를 캐싱할까, 독립 압축기를 쓸까?" (a segment
+ *           starts from the previous segment's final state: S_final of one
+ *           call is the S0 of the next).
+ *
+ * What is computed, for every (batch b, head h) independently, strictly one
+ * token after another (this is the plain definition; nothing is blocked,
+ * fused or reordered):
+ *
+ *   [GDN2, update equation]
+ *     S_t = (I - k_t (b_t . k_t)^T) D_t S_{t-1} + k_t (w_t . v_t)^T
+ *   with S_t a d_k x d_v matrix, D_t = diag(exp(g_t)) a per-key-channel
+ *   decay given as its logarithm g_t, b_t a per-key-channel erase gate,
+ *   w_t a per-value-channel write gate ('.' is the elementwise product).
+ *   Expanding the product in the order printed (decay first, then erase):
+ *     S'  = D_t S_{t-1}
+ *     r   = S'^T (b_t . k_t)           (what the erase removes, per value ch.)
+ *     S_t = S' + k_t (w_t . v_t - r)^T
+ *   Readout (the pages give none; the standard linear-attention convention):
+ *     o_t = S_t^T q_t                  (after the update, no scaling)
+ *
+ * Gate widths: b has width 1 or d_k, w width 1 or d_v, g width 1 or d_k.
+ * A width-1 gate is one scalar per (token, head), broadcast over its channels
+ * ([GDN2, update equation]: tying b = w to one scalar gives KDA, and a scalar
+ * decay on top gives Gated DeltaNet).
+ *
+ * Layouts (all row-major, contiguous, float64):
+ *   q, k    [B, T, H, d_k]        v        [B, T, H, d_v]
+ *   b       [B, T, H, bw]         w        [B, T, H, ww]
+ *   g       [B, T, H, gw]         o        [B, T, H, d_v]
+ *   S0, S_out [B, H, d_k, d_v]    (S0 may be NULL: zero initial state;
+ *                                  S_out may be NULL or equal to S0)
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC -std=c11 gdr2_oracle.c -lm
+ * (no -ffast-math, no intrinsics).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One token of the recurrence for one head, in place on S (d_k x d_v). */
+static void gdr2_token(long dk, long dv, double *S, double *r,
+                       const double *q, const double *k, const double *v,
+                       const double *b, long bw, const double *w, long ww,
+                       const double *g, long gw, double *o)
+{
+    long i, j;
+    /* S' = D_t S_{t-1}: row i (key channel i) is scaled by exp(g_t[i]). */
+    for (i = 0; i < dk; ++i) {
+        double d = exp(gw == 1 ? g[0] : g[i]);
+        for (j = 0; j < dv; ++j)
+            S[i * dv + j] *= d;
+    }
+    /* r = S'^T (b_t . k_t): the old memory read through the erase-weighted key. */
+    for (j = 0; j < dv; ++j)
+        r[j] = 0.0;
+    for (i = 0; i < dk; ++i) {
+        double e = (bw == 1 ? b[0] : b[i]) * k[i];
+        for (j = 0; j < dv; ++j)
+            r[j] += e * S[i * dv + j];
+    }
+    /* S_t = S' - k_t r^T + k_t (w_t . v_t)^T. */
+    for (i = 0; i < dk; ++i) {
+        for (j = 0; j < dv; ++j) {
+            double u = (ww == 1 ? w[0] : w[j]) * v[j];
+            S[i * dv + j] += k[i] * (u - r[j]);
+        }
+    }
+    /* o_t = S_t^T q_t. */
+    for (j = 0; j < dv; ++j)
+        o[j] = 0.0;
+    for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j)
+            o[j] += q[i] * S[i * dv + j];
+}
+
+/*
+ * Returns 0 on success, -1 on bad arguments, -2 when memory runs out.
+ * threads <= 0 keeps the OpenMP default.
+ */
+int gdr2_oracle_forward(long B, long T, long H, long dk, long dv,
+                        const double *q, const double *k, const double *v,
+                        const double *b, long bw, const double *w, long ww,
+                        const double *g, long gw, const double *S0,
+                        double *o, double *S_out, int threads)
+{
+    long bh, n_bh = B * H;
+    int failed = 0;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (!(bw == 1 || bw == dk) || !(ww == 1 || ww == dv) || !(gw == 1 || gw == dk))
+        return -1;
+    if (T > 0 && (!q || !k || !v || !b || !w || !g || !o))
+        return -1;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(|| : failed)
+    for (bh = 0; bh < n_bh; ++bh) {
+        long bi = bh / H, h = bh % H, t;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+        double *r = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !r) {
+            free(S);
+            free(r);
+            failed = 1;
+            continue;
+        }
+        if (S0)
+            memcpy(S, S0 + bh * dk * dv, sizeof(double) * (size_t)(dk * dv));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(dk * dv));
+        for (t = 0; t < T; ++t) {
+            long row = (bi * T + t) * H + h; /* token row in [B, T, H, .] */
+            gdr2_token(dk, dv, S, r,
+                       q + row * dk, k + row * dk, v + row * dv,
+                       b + row * bw, bw, w + row * ww, ww,
+                       g + row * gw, gw, o + row * dv);
+        }
+        if (S_out)
+            memcpy(S_out + bh * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
+        free(S);
+        free(r);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * One decode step for N independent sequences x H heads: the same token
+ * update applied once per state, in place on state [N, H, d_k, d_v].
+ * Token inputs are [N, H, .] (one token each); o is [N, H, d_v].
+ */
+int gdr2_oracle_decode(long N, long H, long dk, long dv,
+                       const double *q, const double *k, const double *v,
+                       const double *b, long bw, const double *w, long ww,
+                       const double *g, long gw, double *state, double *o,
+                       int threads)
+{
+    if (!state)
+        return -1;
+    /* A decode step is a forward over T = 1 that starts from and ends in state. */
+    return gdr2_oracle_forward(N, 1, H, dk, dv, q, k, v, b, bw, w, ww, g, gw,
+                               state, o, state, threads);
+}
+
+int gdr2_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
