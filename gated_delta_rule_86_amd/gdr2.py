@@ -1,0 +1,188 @@
+"""ctypes binding of ``libgdr2.so`` (the C ABI declared in include/gdr2.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory (``torch.empty``)
+and the current HIP stream.  There is no fallback: if the library is missing
+or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdr2.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+ALGO_AUTO, ALGO_STAGED = 0, 1
+ALGOS = {"auto": ALGO_AUTO, "staged": ALGO_STAGED}
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("B", _c_i64), ("T", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
+                ("chunk", _c_i32), ("dtype", _c_i32), ("algo", _c_i32),
+                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp),
+                ("g", _vp), ("S0", _vp), ("o", _vp), ("S_out", _vp),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("N", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
+                ("dtype", _c_i32), ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp),
+                ("g", _vp), ("state", _vp), ("o", _vp)]
+
+
+# Every symbol include/gdr2.h declares (checked by the tests).
+EXPORTS = ("gdr2_forward_workspace_size", "gdr2_forward_chunked", "gdr2_decode_step",
+           "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version")
+ABI_VERSION = 1
+
+
+class Gdr2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gdr2 status {status}: {message}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (no build, no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
+                               "or python gated_delta_rule_86_amd/build.py")
+        lib = ctypes.CDLL(path)
+        lib.gdr2_forward_workspace_size.restype = ctypes.c_size_t
+        lib.gdr2_forward_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
+        lib.gdr2_forward_chunked.restype = ctypes.c_int
+        lib.gdr2_forward_chunked.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+        lib.gdr2_decode_step.restype = ctypes.c_int
+        lib.gdr2_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        lib.gdr2_status_string.restype = ctypes.c_char_p
+        lib.gdr2_status_string.argtypes = [ctypes.c_int]
+        lib.gdr2_last_error.restype = ctypes.c_char_p
+        lib.gdr2_last_error.argtypes = []
+        lib.gdr2_abi_version.restype = ctypes.c_int
+        lib.gdr2_abi_version.argtypes = []
+        if lib.gdr2_abi_version() != ABI_VERSION:
+            raise RuntimeError("libgdr2.so ABI version mismatch")
+        _lib = lib
+        return lib
+
+
+def _check(lib, status: int):
+    if status != OK:
+        raise Gdr2Error(status, lib.gdr2_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _req(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
+             algo: str = "auto", workspace=None) -> FwdArgs:
+    B, T, H, Dk = q.shape
+    a = FwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, v.shape[-1]
+    a.chunk, a.dtype, a.algo = chunk, _dtype_code(q), ALGOS[algo]
+    a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
+    a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
+    a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
+            out=None, S_out=None, workspace=None, final_state: bool = True):
+    """Chunked forward.  q,k [B,T,H,Dk]; v [B,T,H,Dv]; b [B,T,H,1|Dk];
+    w [B,T,H,1|Dv] (all float32 or bfloat16); g float32 [B,T,H,1|Dk];
+    S0 float32 [B,H,Dk,Dv] or None.  Returns (o, S_final)."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w)):
+        _req(t, n, q.dtype)
+    _req(g, "g", torch.float32)
+    if S0 is not None:
+        _req(S0, "S0", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if S_out is None and final_state:
+        S_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo)
+    need = lib.gdr2_forward_workspace_size(ctypes.byref(a))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib, lib.gdr2_forward_chunked(ctypes.byref(a), stream))
+    return out, S_out
+
+
+def workspace_size(q, k, v, b, w, g, chunk: int = 64, algo: str = "auto") -> int:
+    lib = load_library()
+    return int(lib.gdr2_forward_workspace_size(ctypes.byref(fwd_args(q, k, v, b, w, g, chunk=chunk, algo=algo))))
+
+
+def decode_args(state, q, k, v, b, w, g, o) -> DecodeArgs:
+    N, H, Dk, Dv = state.shape
+    a = DecodeArgs()
+    a.N, a.H, a.Dk, a.Dv = N, H, Dk, Dv
+    a.dtype = _dtype_code(q)
+    a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
+    a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
+    a.state, a.o = _ptr(state), _ptr(o)
+    return a
+
+
+def decode_step(state, q, k, v, b, w, g, out=None):
+    """One decode step, in place on ``state`` float32 [N,H,Dk,Dv].
+    q,k [N,H,Dk]; v [N,H,Dv]; b [N,H,1|Dk]; w [N,H,1|Dv]; g float32 [N,H,1|Dk].
+    Returns o [N,H,Dv]."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w)):
+        _req(t, n, q.dtype)
+    _req(g, "g", torch.float32)
+    _req(state, "state", torch.float32)
+    N, H, Dk, Dv = state.shape
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
+    a = decode_args(state, q, k, v, b, w, g, out)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib, lib.gdr2_decode_step(ctypes.byref(a), stream))
+    return out

@@ -107,6 +107,23 @@ def draw(wl: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def draw_decode_tokens(wl: Workload, step: int) -> dict:
+    """Fresh tokens for decode step `step` (no state): same recipe as `draw`,
+    seed wl.seed + 1000 * (step + 1)."""
+    return draw(wl.with_(s0_std=0.0), seed=wl.seed + 1000 * (step + 1))
+
+
+def select_heads(inp: dict, pairs) -> dict:
+    """Restrict forward inputs to the given (b, h) pairs, each as its own
+    batch row of one head: every (b, h) recurrence is independent."""
+    out = {}
+    for n in ("q", "k", "v", "b", "w", "g"):
+        out[n] = torch.stack([inp[n][b, :, h:h + 1] for b, h in pairs])
+    S0 = inp.get("S0")
+    out["S0"] = None if S0 is None else torch.stack([S0[b, h:h + 1] for b, h in pairs])
+    return out
+
+
 def to_f64(t):
     """Exact upcast of a (quantised) CPU/GPU tensor to a float64 numpy array."""
     if t is None:

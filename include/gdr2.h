@@ -1,0 +1,166 @@
+/*
+ * gdr2.h -- C ABI of the Gated DeltaNet-2 forward library for AMD MI355X
+ * (gfx950).  Plain C: no C++ or HIP types.  Streams are passed as void*
+ * holding a hipStream_t (NULL = the default stream).
+ *
+ * The operation (page "Gated DeltaNet-2: 선형 어텐션에서 삭제와 쓰기 게이트
+ * 분리", section "Gated Delta Rule-2 업데이트 수식", the update equation and
+ * its symbol table), for every batch row b and head h independently:
+ *
+ *     S_t = (I - k_t (b_t * k_t)^T) D_t S_{t-1} + k_t (w_t * v_t)^T
+ *     o_t = S_t^T q_t
+ *
+ *   S_t    d_k x d_v memory state (fp32 here), row index = key channel
+ *   k_t    key (the pages take it L2-normalised; the caller normalises, the
+ *          library computes the formula for any k)
+ *   b_t    erase gate, per key channel (width d_k) or one scalar (width 1)
+ *   w_t    write gate, per value channel (width d_v) or one scalar (width 1)
+ *   D_t    diag(exp(g_t)): per-key-channel decay, passed as its logarithm g_t
+ *          (fp32, width d_k or 1; g <= 0 is expected but not required)
+ *   o_t    readout after the update at t, without scaling (the pages give no
+ *          readout; this is the usual linear-attention convention)
+ *   '*'    elementwise product
+ *
+ * Width-1 gates broadcast over their channels: b = w = one scalar beta is
+ * KDA, and a scalar decay on top is Gated DeltaNet (same section).
+ *
+ * Optional initial state S0: a learned prefilled memory (page "[논문리뷰]
+ * Sparse Delta Memory: Scaling the State of Linear RNNs through Sparsity",
+ * section 3, the learned initial state M_0).  S_out of one call may be passed
+ * as S0 of the next to continue a sequence segment by segment (page "Memory
+ * Caching(MC): ...", section "체크포인트를 캐싱할까, 독립 압축기를 쓸까?");
+ * the result equals one call over the whole sequence up to rounding.
+ *
+ * Chunked prefill: fixed-size chunks (page "Gated DeltaNet-2 ...", section
+ * "효율적 구현": a chunkwise algorithm with a WY form that absorbs the
+ * cumulative per-channel decay into the rank-1 erase factors).  The decode
+ * step is the pure recurrent mode of the same page (section "개요"): one
+ * token per sequence, state updated in place.
+ *
+ * Common rules for every entry point
+ *   Ownership : the caller allocates and frees every device buffer (inputs,
+ *               outputs, workspace).  The library allocates no device memory,
+ *               does not synchronise, and keeps no pointer after returning.
+ *               Work is enqueued on `stream` and runs asynchronously.
+ *   Errors    : arguments are validated on the host before any launch; on
+ *               error the call returns a non-zero gdr2_status, records a
+ *               message for gdr2_last_error() in the calling thread, launches
+ *               nothing and leaves every output untouched.  A failed HIP
+ *               launch returns GDR2_ERR_HIP with the HIP error text.  NaN or
+ *               Inf inputs are not checked; they propagate.
+ *   Layout    : every tensor is dense, row-major, contiguous, in device memory,
+ *               16-byte aligned.
+ *   Threads   : calls are reentrant; calls on different streams run
+ *               concurrently as long as their buffers do not overlap.
+ */
+#ifndef GDR2_H
+#define GDR2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR2_ABI_VERSION 1
+
+typedef enum gdr2_status {
+    GDR2_OK = 0,
+    GDR2_ERR_INVALID_ARG = 1,  /* null / misaligned / overlapping pointer, bad size */
+    GDR2_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set below */
+    GDR2_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    GDR2_ERR_HIP = 4           /* the HIP runtime reported an error */
+} gdr2_status;
+
+/* Element type of q, k, v, b, w and o.  g, S0, S_out and state are fp32. */
+typedef enum gdr2_dtype {
+    GDR2_F32 = 0,
+    GDR2_BF16 = 1  /* bfloat16; o is rounded to nearest-even once, at store */
+} gdr2_dtype;
+
+/* Algorithm of the chunked forward. */
+typedef enum gdr2_algo {
+    GDR2_ALGO_AUTO = 0,    /* the library picks */
+    GDR2_ALGO_STAGED = 1   /* intra-chunk kernel writes per-chunk factors to the
+                              workspace; a propagation kernel carries the state
+                              through the chunks and writes o */
+} gdr2_algo;
+
+/*
+ * Arguments of the chunked forward.
+ *   q, k   [B, T, H, Dk]        dtype
+ *   v      [B, T, H, Dv]        dtype
+ *   b      [B, T, H, b_width]   dtype, b_width in {1, Dk}
+ *   w      [B, T, H, w_width]   dtype, w_width in {1, Dv}
+ *   g      [B, T, H, g_width]   fp32 log-decay, g_width in {1, Dk}
+ *   S0     [B, H, Dk, Dv]       fp32, may be NULL (zero initial state)
+ *   o      [B, T, H, Dv]        dtype, written
+ *   S_out  [B, H, Dk, Dv]       fp32, written, may be NULL; may be the same
+ *                               pointer as S0 (in-place continuation), must
+ *                               not otherwise overlap anything
+ *   o must not overlap any input.
+ * Supported set: Dk == Dv in {64, 128}; chunk in {32, 64}; dtype F32 or BF16,
+ * with Dk * chunk <= 4096 for F32; B, T, H >= 0 (T need not be a multiple of
+ * chunk; T == 0 writes S0, or zeros, to S_out).  Anything else returns
+ * GDR2_ERR_UNSUPPORTED.
+ */
+typedef struct gdr2_fwd_args {
+    int64_t B, T, H, Dk, Dv;
+    int32_t chunk;
+    int32_t dtype;        /* gdr2_dtype */
+    int32_t algo;         /* gdr2_algo */
+    int32_t b_width, w_width, g_width;
+    const void *q, *k, *v, *b, *w;
+    const float *g;
+    const float *S0;
+    void *o;
+    float *S_out;
+    void *workspace;      /* device memory, >= gdr2_forward_workspace_size() bytes */
+    size_t workspace_bytes;
+} gdr2_fwd_args;
+
+/*
+ * Arguments of one batched decode step: N sequences x H heads, one token each.
+ *   q, k   [N, H, Dk]   dtype        v  [N, H, Dv]   dtype
+ *   b      [N, H, b_width]           w  [N, H, w_width]       (dtype)
+ *   g      [N, H, g_width] fp32
+ *   state  [N, H, Dk, Dv] fp32, read and overwritten in place with S_t
+ *   o      [N, H, Dv] dtype, written; must not overlap any other buffer
+ * Supported set: Dk == Dv in {64, 128}; dtype F32 or BF16; N, H >= 0.
+ */
+typedef struct gdr2_decode_args {
+    int64_t N, H, Dk, Dv;
+    int32_t dtype;        /* gdr2_dtype */
+    int32_t b_width, w_width, g_width;
+    const void *q, *k, *v, *b, *w;
+    const float *g;
+    float *state;
+    void *o;
+} gdr2_decode_args;
+
+/* Bytes of device workspace gdr2_forward_chunked needs for these arguments
+ * (pointers are not read).  0 when none is needed or the arguments are
+ * invalid or unsupported. */
+size_t gdr2_forward_workspace_size(const gdr2_fwd_args *args);
+
+/* Chunked forward: o for every token and the final state S_out. */
+gdr2_status gdr2_forward_chunked(const gdr2_fwd_args *args, void *stream);
+
+/* One recurrent decode step for every (sequence, head) state. */
+gdr2_status gdr2_decode_step(const gdr2_decode_args *args, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *gdr2_status_string(gdr2_status status);
+
+/* Message of the last failed call in this thread ("" if none). */
+const char *gdr2_last_error(void);
+
+/* GDR2_ABI_VERSION of the built library. */
+int gdr2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR2_H */

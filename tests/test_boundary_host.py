@@ -1,0 +1,224 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every symbol include/gdr2.h declares, and rejects every invalid or
+unsupported argument before any launch -- so these calls never touch a
+device.  Pointers below are fake, aligned, non-overlapping addresses; the
+library only compares them, it never dereferences them on these paths."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_86_amd import gdr2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr2.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# The fake pointers below must never reach a kernel launch.  Every case is an
+# argument error caught on the host, but as a second line of defence this
+# module does not run where a GPU is visible.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only tests use fake device pointers")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdr2.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr2_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(gdr2.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.gdr2_abi_version() == gdr2.ABI_VERSION
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.gdr2_status_string(s)
+    assert lib.gdr2_status_string(99) == b"unknown status"
+
+
+BASE = 0x7F0000000000
+SPAN = 1 << 32          # far apart: no two fake tensors overlap
+
+
+def fake(i, off=0):
+    return BASE + i * SPAN + off
+
+
+def good_fwd(B=2, T=100, H=3, D=128, chunk=64, dtype=gdr2.BF16, widths=None):
+    a = gdr2.FwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, D, D
+    a.chunk, a.dtype, a.algo = chunk, dtype, gdr2.ALGO_AUTO
+    a.b_width, a.w_width, a.g_width = widths or (D, D, D)
+    a.q, a.k, a.v, a.b, a.w, a.g = (fake(i) for i in range(6))
+    a.S0, a.o, a.S_out = fake(6), fake(7), fake(8)
+    a.workspace = fake(9)
+    return a
+
+
+def call_fwd(lib, a, ws_ok=True):
+    if ws_ok:
+        a.workspace_bytes = lib.gdr2_forward_workspace_size(ctypes.byref(a))
+    return lib.gdr2_forward_chunked(ctypes.byref(a), None)
+
+
+def _mod(**kw):
+    def f(a):
+        for k, v in kw.items():
+            setattr(a, k, v)
+    return f
+
+
+FWD_CASES = [
+    ("negative_T", _mod(T=-1), gdr2.ERR_INVALID_ARG),
+    ("zero_Dk", _mod(Dk=0, Dv=0), gdr2.ERR_INVALID_ARG),
+    ("head_dim_96", _mod(Dk=96, Dv=96, b_width=96, w_width=96, g_width=96), gdr2.ERR_UNSUPPORTED),
+    ("dk_ne_dv", _mod(Dv=64), gdr2.ERR_INVALID_ARG),   # w/v widths then mismatch Dv
+    ("chunk_16", _mod(chunk=16), gdr2.ERR_UNSUPPORTED),
+    ("chunk_128", _mod(chunk=128), gdr2.ERR_UNSUPPORTED),
+    ("f32_too_large", _mod(dtype=gdr2.F32), gdr2.ERR_UNSUPPORTED),   # D=128, chunk=64
+    ("bad_dtype", _mod(dtype=7), gdr2.ERR_INVALID_ARG),
+    ("bad_algo", _mod(algo=9), gdr2.ERR_INVALID_ARG),
+    ("bad_b_width", _mod(b_width=3), gdr2.ERR_INVALID_ARG),
+    ("bad_w_width", _mod(w_width=64), gdr2.ERR_INVALID_ARG),
+    ("bad_g_width", _mod(g_width=2), gdr2.ERR_INVALID_ARG),
+    ("null_q", _mod(q=None), gdr2.ERR_INVALID_ARG),
+    ("null_g", _mod(g=None), gdr2.ERR_INVALID_ARG),
+    ("null_o", _mod(o=None), gdr2.ERR_INVALID_ARG),
+    ("misaligned_k", _mod(k=fake(1, 8)), gdr2.ERR_INVALID_ARG),
+    ("misaligned_S0", _mod(S0=fake(6, 4)), gdr2.ERR_INVALID_ARG),
+    ("o_overlaps_v", _mod(o=fake(2, 4096)), gdr2.ERR_INVALID_ARG),
+    ("o_overlaps_S0", _mod(o=fake(6, 1024)), gdr2.ERR_INVALID_ARG),
+    ("S_out_overlaps_g", _mod(S_out=fake(5, 256)), gdr2.ERR_INVALID_ARG),
+    ("S_out_partial_S0", _mod(S_out=fake(6, 4096)), gdr2.ERR_INVALID_ARG),
+    ("workspace_overlaps_q", _mod(workspace=fake(0, 4096)), gdr2.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mod,status", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_rejects(lib, name, mod, status):
+    a = good_fwd()
+    mod(a)
+    got = call_fwd(lib, a)
+    assert got == status, (name, got, lib.gdr2_last_error())
+    assert lib.gdr2_last_error()
+
+
+def test_forward_null_args(lib):
+    assert lib.gdr2_forward_chunked(None, None) == gdr2.ERR_INVALID_ARG
+    assert lib.gdr2_forward_workspace_size(None) == 0
+
+
+def test_forward_workspace_required(lib):
+    a = good_fwd()
+    need = lib.gdr2_forward_workspace_size(ctypes.byref(a))
+    assert need > 0
+    a.workspace_bytes = need - 1
+    assert lib.gdr2_forward_chunked(ctypes.byref(a), None) == gdr2.ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = None, need
+    assert lib.gdr2_forward_chunked(ctypes.byref(a), None) == gdr2.ERR_WORKSPACE
+    assert b"workspace" in lib.gdr2_last_error()
+
+
+def test_workspace_size_formula(lib):
+    # per chunk record: -W, U~, K^, Q~ ([C][D] each), P [C][C] in the input
+    # dtype, gamma [D] fp32; each array padded to 256 bytes.
+    def al(x):
+        return (x + 255) // 256 * 256
+    for (B, T, H, D, C, dt, es) in [(2, 100, 3, 128, 64, gdr2.BF16, 2), (1, 256, 1, 64, 32, gdr2.F32, 4),
+                                    (8, 4096, 16, 128, 64, gdr2.BF16, 2)]:
+        a = good_fwd(B=B, T=T, H=H, D=D, chunk=C, dtype=dt)
+        nrec = B * H * -(-T // C)
+        want = 4 * al(nrec * C * D * es) + al(nrec * C * C * es) + al(nrec * D * 4)
+        assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == want
+    a = good_fwd(D=96)
+    assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == 0
+    a = good_fwd(T=0)
+    assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_forward_empty_is_a_noop(lib):
+    # nothing to compute and no state to write: OK without any launch
+    for kw in (dict(B=0), dict(H=0)):
+        a = good_fwd(**kw)
+        assert call_fwd(lib, a) == gdr2.OK
+    a = good_fwd(T=0)
+    a.S_out = a.S0                     # continuation in place with no tokens
+    assert call_fwd(lib, a) == gdr2.OK
+    a = good_fwd(T=0)
+    a.S_out = None
+    assert call_fwd(lib, a) == gdr2.OK
+
+
+def test_forward_accepts_inplace_state(lib):
+    # S_out == S0 is allowed; make the call fail later on purpose (missing q)
+    # to prove validation got past the aliasing rule without launching.
+    a = good_fwd()
+    a.S_out = a.S0
+    a.q = None
+    assert call_fwd(lib, a) == gdr2.ERR_INVALID_ARG
+    assert b"q is NULL" in lib.gdr2_last_error()
+
+
+def good_dec(N=4, H=2, D=128, dtype=gdr2.BF16):
+    a = gdr2.DecodeArgs()
+    a.N, a.H, a.Dk, a.Dv = N, H, D, D
+    a.dtype = dtype
+    a.b_width = a.w_width = a.g_width = D
+    a.q, a.k, a.v, a.b, a.w, a.g = (fake(i) for i in range(6))
+    a.state, a.o = fake(6), fake(7)
+    return a
+
+
+DEC_CASES = [
+    ("negative_N", _mod(N=-1), gdr2.ERR_INVALID_ARG),
+    ("head_dim_32", _mod(Dk=32, Dv=32), gdr2.ERR_INVALID_ARG),   # widths then mismatch
+    ("head_dim_256", _mod(Dk=256, Dv=256, b_width=256, w_width=256, g_width=256), gdr2.ERR_UNSUPPORTED),
+    ("bad_dtype", _mod(dtype=3), gdr2.ERR_INVALID_ARG),
+    ("null_state", _mod(state=None), gdr2.ERR_INVALID_ARG),
+    ("null_w", _mod(w=None), gdr2.ERR_INVALID_ARG),
+    ("misaligned_state", _mod(state=fake(6, 2)), gdr2.ERR_INVALID_ARG),
+    ("o_overlaps_state", _mod(o=fake(6, 512)), gdr2.ERR_INVALID_ARG),
+    ("state_overlaps_k", _mod(state=fake(1, 0)), gdr2.ERR_INVALID_ARG),
+    ("bad_g_width", _mod(g_width=5), gdr2.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mod,status", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_rejects(lib, name, mod, status):
+    a = good_dec()
+    mod(a)
+    got = lib.gdr2_decode_step(ctypes.byref(a), None)
+    assert got == status, (name, got, lib.gdr2_last_error())
+
+
+def test_decode_empty_is_a_noop(lib):
+    assert lib.gdr2_decode_step(None, None) == gdr2.ERR_INVALID_ARG
+    a = good_dec(N=0)
+    assert lib.gdr2_decode_step(ctypes.byref(a), None) == gdr2.OK
+
+
+def test_python_wrappers_refuse_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        gdr2.forward(x, x, x, x, x, x)
