@@ -1,0 +1,221 @@
+"""Benchmark of the Gated DeltaNet-2 forward on one MI355X.
+
+A step is one chunked forward (every stage of the path: cumulative decay,
+decay-absorbed operands, gated Gram and scores, WY solve, state propagation
+and output) over one batch of the training-shape workload: B=8, H=16,
+T=4096, d_k=d_v=128, bf16 inputs, fp32 state, chunk 64, per-channel gates.
+Inputs are seeded synthetic tensors (gated_delta_rule_86_amd.inputs), already
+resident in device memory when the timed region starts.
+
+Prints one JSON line: tokens/s (B*T per step time), the roofline of the
+dominant kernel (HIP events on the launch stream, algorithmic bytes per
+launch), the fp64 CPU oracle on the host cores, and in "extra" the per-kernel
+split, the MFMA fraction and the batched decode step (256 x 16 states,
+1000 steps) in GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "tokens/s, GDN-2 chunked fwd H=16 d=128 T=4K; % MFMA peak; decode HBM GB/s"
+NAMES = ("q", "k", "v", "b", "w", "g")
+
+
+def algorithmic_flops_per_chunk(C: int, D: int) -> int:
+    """Dense contractions the chunked method must do per (b, h, chunk), with
+    the triangular structure exploited: gated Gram, scores, WY solve, W S,
+    K^T Delta, Q~ S, P Delta."""
+    return (C * (C - 1) * D + C * (C + 1) * D + C * (C - 1) * (D + D)
+            + 6 * C * D * D + C * (C + 1) * D)
+
+
+def staged_bytes(B, T, H, D, C, esz, bw, ww, gw, s0: bool, s_out: bool):
+    """Algorithmic HBM bytes per launch of the two staged kernels: every
+    operand read once and every result written once."""
+    rows = B * T * H
+    nrec = B * H * -(-T // C)
+    inputs = rows * ((2 * D + D + bw + ww) * esz + gw * 4)      # q,k,v,b,w (dtype) + g fp32
+    factors = nrec * (4 * C * D * esz + C * C * esz + D * 4)  # -W, U~, K^, Q~, P, gamma
+    state = B * H * D * D * 4
+    prep = inputs + factors
+    st = factors + rows * D * esz + (state if s0 else 0) + (state if s_out else 0)
+    minimum = inputs + rows * D * esz + (state if s0 else 0) + (state if s_out else 0)
+    return prep, st, minimum
+
+
+def cpu_baseline(inp, wl):
+    """The fp64 oracle (as it stands) on the host cores over the whole
+    workload batch: every (b, h) recurrence, OpenMP over them."""
+    import oracle
+    from gated_delta_rule_86_amd.inputs import to_f64
+
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(ncpu, 16, wl.B * wl.H))
+    args = [to_f64(inp[n]) for n in NAMES]
+    t0 = time.perf_counter()
+    oracle.forward(*args, S0=to_f64(inp["S0"]), threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"the whole batch: {wl.B * wl.H} (b,h) recurrences x T={wl.T}, "
+                      f"fp64, {threads} OpenMP threads"}
+
+
+def bench_decode(torch, gdr2, lib, steps: int, warmup: int):
+    from gated_delta_rule_86_amd.inputs import WORKLOADS, draw, draw_decode_tokens
+
+    wl = WORKLOADS["decode"]
+    state = draw(wl)["state"].cuda()
+    ring = []
+    for s in range(8):                         # 8 token sets reused cyclically
+        tok = {n: t.cuda() for n, t in draw_decode_tokens(wl, s).items() if t is not None}
+        o = torch.empty((wl.B, wl.H, wl.D), dtype=tok["q"].dtype, device="cuda")
+        ring.append(gdr2.decode_args(state, *(tok[n] for n in NAMES), o))
+        ring[-1]._keep = (tok, o)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        assert lib.gdr2_decode_step(ctypes.byref(ring[i % 8]), stream) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        lib.gdr2_decode_step(ctypes.byref(ring[i % 8]), stream)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nstate = wl.B * wl.H
+    byts = nstate * (2 * wl.D * wl.D * 4 + (5 * wl.D) * 2 + wl.D * 4 + wl.D * 2)
+    return {"workload": "decode: 256 sequences x 16 heads, d=128, bf16 tokens, fp32 state",
+            "steps": steps, "us_per_step": us, "algorithmic_bytes_per_step": byts,
+            "GBps": byts / (us * 1e-6) / 1e9, "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards across GPUs without communication by (batch, head); "
+              "no multi-GPU run is part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_86_amd import gdr2
+    from gated_delta_rule_86_amd.inputs import WORKLOADS, draw
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = gdr2.load_library()
+    wl = WORKLOADS["train_4k"]
+    inp = draw(wl)
+    d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    B, T, H, D, C = wl.B, wl.T, wl.H, wl.D, wl.chunk
+    o = torch.empty((B, T, H, D), dtype=d["q"].dtype, device="cuda")
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    x = [d[n] for n in NAMES]
+    need = gdr2.workspace_size(*x, chunk=C)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    a_all = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=C, workspace=ws)
+    a_prep = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=C, workspace=ws, stage="prep")
+    a_state = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=C, workspace=ws, stage="state")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call(a):
+        rc = lib.gdr2_forward_chunked(ctypes.byref(a), stream)
+        if rc != 0:
+            raise RuntimeError(lib.gdr2_last_error().decode())
+
+    for _ in range(args.warmup):
+        call(a_all)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):            # one step = the prep kernel then the state kernel
+        ev[i][0].record()
+        call(a_prep)
+        ev[i][1].record()
+        call(a_state)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    state_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+    tokens = B * T
+    value = tokens / (step_ms * 1e-3)
+
+    esz = 2
+    prep_b, state_b, min_b = staged_bytes(B, T, H, D, C, esz, D, D, D, d["S0"] is not None, True)
+    flops = algorithmic_flops_per_chunk(C, D) * B * H * (T // C)
+    kernels = {"gdr2_chunk_prep": (prep_ms, prep_b), "gdr2_chunk_state": (state_ms, state_b)}
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dom_ms, dom_b = kernels[dom]
+    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes_per_launch": dom_b}
+
+    extra = {
+        "step_ms": round(step_ms, 4), "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "prep_ms": round(prep_ms, 4), "state_ms": round(state_ms, 4),
+        "prep_GBps": round(prep_b / (prep_ms * 1e-3) / 1e9, 1),
+        "state_GBps": round(state_b / (state_ms * 1e-3) / 1e9, 1),
+        "path_min_bytes": min_b,
+        "path_hbm_frac_of_min_bytes": round(min_b / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_flops": flops,
+        "mfma_frac_bf16_dense": round(flops / (step_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+        "pages_context": "38.0 Kt/s (2K) and 36.1 Kt/s (8K): whole-model GDN-2 training "
+                         "throughput on unstated hardware; not comparable",
+    }
+    if not args.no_decode:
+        extra["decode"] = bench_decode(torch, gdr2, lib, args.decode_steps, 20)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del d, x, o, S_out, ws
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(inp, wl)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "train_4k: GDN-2 chunked forward B=8 H=16 T=4096 d_k=d_v=128, "
+                               "per-channel gates, chunk 64, bf16 inputs, fp32 state",
+                   "B": B, "T": T, "H": H, "d": D, "chunk": C, "algo": "staged"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -153,6 +153,10 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
         return s;
     if (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED)
         return fail(GDR2_ERR_INVALID_ARG, "unknown algo %d", a->algo);
+    if (a->stage != GDR2_STAGE_ALL && a->stage != GDR2_STAGE_PREP && a->stage != GDR2_STAGE_STATE)
+        return fail(GDR2_ERR_INVALID_ARG, "unknown stage %d", a->stage);
+    if (a->reserved != 0)
+        return fail(GDR2_ERR_INVALID_ARG, "reserved field must be 0");
     if (a->chunk != 32 && a->chunk != 64)
         return fail(GDR2_ERR_UNSUPPORTED, "supported chunk sizes: 32, 64 (got %d)", a->chunk);
     if (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096)

@@ -51,7 +51,7 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------------------
 // Workspace: per chunk record (sequence, head, chunk), element type E:
-//   Wn [C][D] = -W,  Ut [C][D] = U~,  Kh [C][D] = K^,  Qt [C][D] = Q~,
+//   Wn [C][D] = -W,  Ut [C][D] = U~,  Kh [D][C] = K^ transposed,  Qt [C][D] = Q~,
 //   P [C][C],  gam [D] fp32.   Records are ordered (b*H + h)*NC + n.
 // ---------------------------------------------------------------------------
 struct Layout {
@@ -94,26 +94,71 @@ struct StateArgs {
     int64_t T, H, NC, nbh;
 };
 
+// ---------------------------------------------------------------------------
+// chunk_prep: 512 threads (8 waves), one workgroup per CU, looping over chunk
+// records with the next chunk's inputs prefetched into registers while the
+// current one computes.
+//
+// Decay references.  A chunk is split into halves of 32 tokens; Gh(t) is the
+// cumulative log2-decay at the end of the previous half (0 for the first).
+//   E~_t = e_t 2^G_t,  Q~_t = q_t 2^G_t            (chunk reference, <= |e|,|q|)
+//   Kr_s = k_s 2^(Gh(s) - G_s)                      (own half's reference)
+//   E^_t = e_t 2^(G_t - Gh(t)),  Q^_t likewise       (second half only)
+// A 16x16 tile (I, J) of M (or P) with both blocks in the same half is
+// E^_I Kr_J^T (E~ in the first half), and with I in the second half and J in
+// the first it is E~_I Kr_J^T: each product equals the wanted
+// e_t k_s 2^(G_t - G_s) with no factor above 2^(half span).  The half span is
+// guarded by kSpanMax; a chunk beyond it takes an exact pair-by-pair path for
+// its same-half tiles.
+//
+// WY solve.  [W | U~] = (I + M)^-1 [E~ | u] by blocked forward substitution
+// over the four 16-row blocks:  R_I = RHS_I - sum_{J<I} M_IJ [W|U~]_J,
+// [W|U~]_I = X_II R_I, with X_II = (I + M_II)^-1 from a 16-lane substitution.
+// Each wave owns 32 columns of the right-hand side and keeps its solved blocks
+// in MFMA accumulators, which are the B operands of the next blocks.
+// ---------------------------------------------------------------------------
+constexpr int NTP = 512;           // threads of the prep kernel
+constexpr int NWP = NTP / 64;      // its waves
+
 template <typename E, int D, int C>
 struct PrepShape {
-    static constexpr int NB = C / 16;
-    static constexpr int VEC = 16 / (int)sizeof(E);      // elements per 16-byte access
-    static constexpr int NLD = C * D / (NT * VEC);        // 16-byte loads per thread per [C][D]
-    static constexpr int NLDG = C * D / (NT * 4);         // fp32 g loads per thread
-    static constexpr int LDA = D + 16 / (int)sizeof(E);   // [C][D] operands in LDS
-    static constexpr int LDT = C + 16 / (int)sizeof(E);   // [D][C] operands in LDS
-    static constexpr int LDM = C + 4;                     // fp32 [C][C] (M, X)
-    static constexpr size_t R1 = cmax((size_t)C * D * 4, 2 * (size_t)D * LDT * sizeof(E));
-    static constexpr size_t R2 = cmax(3 * (size_t)C * LDA * sizeof(E),
-                                      ((size_t)C * LDM + (NB > 1 ? NB - 1 : 1) * 256) * 4);
-    static constexpr size_t R3 = cmax((size_t)C * LDM * 4, (size_t)4 * D * 4);
-    static constexpr size_t R4 = ((size_t)NB * NB * D + 2 * (size_t)NB * D) * 4;
-    static constexpr size_t SMEM = al256(R1) + al256(R2) + al256(R3) + al256(R4) + 256;
-    static_assert(C * D % (NT * VEC) == 0 && C * D % (NT * 4) == 0, "tile / thread mismatch");
-    static_assert(NT % D == 0 && C % (NT / D) == 0, "cumsum mapping");
+    static constexpr int NB = C / 16;                       // 16-token blocks
+    static constexpr int NH = C / 32;                       // 32-token halves
+    static constexpr int VEC = 16 / (int)sizeof(E);         // elements per 16-byte access
+    static constexpr int NLD = (C * D + NTP * VEC - 1) / (NTP * VEC);  // [C][D] loads per thread
+    static constexpr int NLDG = (C * D + NTP * 4 - 1) / (NTP * 4);     // fp32 g loads per thread
+    static constexpr int LDA = D + 16 / (int)sizeof(E);     // [rows][D] E arrays in LDS
+    static constexpr int LDC = C + 16 / (int)sizeof(E);     // [C][C] E arrays (P, -M)
+    static constexpr int LDX = 20;                          // fp32 16x16 blocks
+    static constexpr int PARTS = NTP / D;                   // prefix-sum parts per channel
+    static constexpr size_t SZ_G = (size_t)C * D * 4;
+    static constexpr size_t SZ_A = (size_t)C * LDA * sizeof(E);
+    static constexpr size_t SZ_AH = (size_t)(C - 32) * LDA * sizeof(E);
+    static constexpr size_t SZ_CC = (size_t)C * LDC * sizeof(E);
+    static constexpr size_t SZ_BLK = (size_t)NB * 16 * LDX * 4;
+    static constexpr size_t OFF_G = 0;                             // sG
+    static constexpr size_t OFF_E = OFF_G + al256(SZ_G);           // sE  (E~, then -W)
+    static constexpr size_t OFF_Q = OFF_E + al256(SZ_A);           // sQ  (Q~)
+    static constexpr size_t OFF_KR = OFF_Q + al256(SZ_A);          // sKr
+    static constexpr size_t OFF_U = OFF_KR + al256(SZ_A);          // sU  (u, then U~)
+    static constexpr size_t OFF_EH = OFF_U + al256(SZ_A);          // sEh (second half)
+    static constexpr size_t OFF_QH = OFF_EH + al256(SZ_AH);        // sQh (second half)
+    static constexpr size_t OFF_MB = OFF_QH + al256(SZ_AH);        // sMb (-M below the diagonal blocks)
+    static constexpr size_t OFF_P = OFF_MB + al256(SZ_CC);         // sP  (scores)
+    static constexpr size_t OFF_MD = OFF_P + al256(SZ_CC);         // sMd (-M diagonal blocks, fp32)
+    static constexpr size_t OFF_XD = OFF_MD + al256(SZ_BLK);       // sXd (X_II, fp32)
+    static constexpr size_t OFF_T = OFF_XD + al256(SZ_BLK);        // tables [NH][D] + partials
+    static constexpr size_t SZ_T = ((size_t)NH * D + (size_t)PARTS * D) * 4;
+    static constexpr size_t OFF_FLAG = OFF_T + al256(SZ_T);
+    static constexpr size_t SMEM = OFF_FLAG + 256;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(C == 32 || C == 64, "chunk");
+    static_assert(D % VEC == 0 && NTP % D == 0 && C % PARTS == 0, "shape");
+    static_assert((2 * D) % (NWP * 16) == 0, "right-hand-side columns per wave");
 };
 
-// Raw inputs of one chunk as loaded from HBM (bit patterns of E, or fp32 g).
+// Raw inputs of one chunk as loaded (bit patterns; width-1 gates keep their
+// scalar in element 0 and are broadcast when used).
 template <typename E, int D, int C>
 struct PrepRegs {
     typedef PrepShape<E, D, C> S;
@@ -140,6 +185,25 @@ __device__ __forceinline__ void unpack<float>(const u32x4& r, float* out)
     out[3] = __uint_as_float(r[3]);
 }
 
+// 16 bytes of E as a vector.
+template <typename E> struct VecOf;
+template <> struct VecOf<bf16> { typedef bf16x8 T; };
+template <> struct VecOf<float> { typedef f32x4 T; };
+
+// The scalar held in element 0 of a width-1 gate's raw bits.
+template <typename E>
+__device__ __forceinline__ float scalar0(const u32x4& r);
+template <>
+__device__ __forceinline__ float scalar0<bf16>(const u32x4& r)
+{
+    return __uint_as_float(r[0] << 16);
+}
+template <>
+__device__ __forceinline__ float scalar0<float>(const u32x4& r)
+{
+    return __uint_as_float(r[0]);
+}
+
 template <typename E>
 __device__ __forceinline__ u32x4 pack_vec(const float* x);
 template <>
@@ -162,13 +226,38 @@ __device__ __forceinline__ u32x4 ldg16(const void* p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+__device__ __forceinline__ void stg16(void* p, u32x4 v)
+{
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ u32x4 lds16(const void* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void sts16(void* p, u32x4 v)
+{
+    *reinterpret_cast<u32x4*>(p) = v;
+}
 
-// Chunk record -> (first token row, valid length).  Token row r of the chunk
-// is the element offset ((b*T + t0 + r)*H + h) of [B,T,H,.] tensors.
+// Bits of one element, for width-1 gates.
+template <typename E>
+__device__ __forceinline__ unsigned int ld_bits(const E* p);
+template <>
+__device__ __forceinline__ unsigned int ld_bits<bf16>(const bf16* p)
+{
+    return *reinterpret_cast<const unsigned short*>(p);
+}
+template <>
+__device__ __forceinline__ unsigned int ld_bits<float>(const float* p)
+{
+    return __float_as_uint(*p);
+}
+
+// Chunk record -> position.  Token row r of the chunk is element offset
+// ((b*T + t0 + r)*H + h) of the [B,T,H,.] tensors.
 struct ChunkPos {
     int64_t row0;     // (b*T + t0)*H + h
-    int64_t H;        // row stride in tokens
-    int L;            // valid tokens
+    int L;            // valid tokens (>= 1)
 };
 
 __device__ __forceinline__ ChunkPos chunk_pos(int64_t rec, int64_t NC, int64_t T, int64_t H, int C)
@@ -178,50 +267,33 @@ __device__ __forceinline__ ChunkPos chunk_pos(int64_t rec, int64_t NC, int64_t T
     const int64_t t0 = n * C;
     ChunkPos p;
     p.row0 = (b * T + t0) * H + h;
-    p.H = H;
     p.L = (int)min((int64_t)C, T - t0);
     return p;
 }
 
-template <typename E, int D, int C>
+// Issue the loads of one chunk.  Rows past the valid length re-read the last
+// valid row (always in bounds) and are zeroed where they are used, so no load
+// sits under a per-lane branch.  FULL: every gate has full width, and the
+// load sequence is straight-line code.
+template <bool FULL, typename E, int D, int C>
 __device__ __forceinline__ void prep_load_gates(const PrepArgs& a, const ChunkPos& cp,
                                                 PrepRegs<E, D, C>& R, int tid)
 {
     typedef PrepShape<E, D, C> S;
 #pragma unroll
     for (int j = 0; j < S::NLDG; ++j) {
-        const int e = (j * NT + tid) * 4, t = e / D, c = e % D;
-        f32x4 val = {0.f, 0.f, 0.f, 0.f};
-        if (t < cp.L) {
-            const int64_t row = cp.row0 + (int64_t)t * cp.H;
-            if (a.gw == 1) {
-                const float s = a.g[row];
-                val = f32x4{s, s, s, s};
-            } else {
-                val = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.g + row * D + c));
-            }
+        const int e = (j * NTP + tid) * 4, t = min(e / D, cp.L - 1), c = e % D;
+        const int64_t row = cp.row0 + (int64_t)t * a.H;
+        if (e < C * D) {
+            if (FULL || a.gw != 1)
+                R.g[j] = __builtin_bit_cast(f32x4, ldg16(a.g + row * D + c));
+            else
+                R.g[j][0] = a.g[row];
         }
-        R.g[j] = val;
     }
 }
 
-template <typename E>
-__device__ __forceinline__ u32x4 splat_bits(const E* p);
-template <>
-__device__ __forceinline__ u32x4 splat_bits<bf16>(const bf16* p)
-{
-    const unsigned short s = *reinterpret_cast<const unsigned short*>(p);
-    const unsigned int w = (unsigned int)s | ((unsigned int)s << 16);
-    return u32x4{w, w, w, w};
-}
-template <>
-__device__ __forceinline__ u32x4 splat_bits<float>(const float* p)
-{
-    const unsigned int w = __float_as_uint(*p);
-    return u32x4{w, w, w, w};
-}
-
-template <typename E, int D, int C>
+template <bool FULL, typename E, int D, int C>
 __device__ __forceinline__ void prep_load_tokens(const PrepArgs& a, const ChunkPos& cp,
                                                  PrepRegs<E, D, C>& R, int tid)
 {
@@ -233,60 +305,85 @@ __device__ __forceinline__ void prep_load_tokens(const PrepArgs& a, const ChunkP
     const E* w = (const E*)a.w;
 #pragma unroll
     for (int j = 0; j < S::NLD; ++j) {
-        const int e = (j * NT + tid) * S::VEC, t = e / D, c = e % D;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        R.k[j] = R.q[j] = R.b[j] = R.v[j] = R.w[j] = z;
-        if (t < cp.L) {
-            const int64_t row = cp.row0 + (int64_t)t * cp.H;
-            R.k[j] = ldg16(k + row * D + c);
-            R.q[j] = ldg16(q + row * D + c);
-            R.v[j] = ldg16(v + row * D + c);
-            R.b[j] = a.bw == 1 ? splat_bits<E>(b + row) : ldg16(b + row * D + c);
-            R.w[j] = a.ww == 1 ? splat_bits<E>(w + row) : ldg16(w + row * D + c);
+        const int e = (j * NTP + tid) * S::VEC, t = min(e / D, cp.L - 1), c = e % D;
+        const int64_t row = cp.row0 + (int64_t)t * a.H, off = row * D + c;
+        if (e < C * D) {
+            R.k[j] = ldg16(k + off);
+            R.q[j] = ldg16(q + off);
+            R.v[j] = ldg16(v + off);
+            if (FULL) {
+                R.b[j] = ldg16(b + off);
+                R.w[j] = ldg16(w + off);
+            }
+        }
+    }
+    if (!FULL) {
+#pragma unroll
+        for (int j = 0; j < S::NLD; ++j) {
+            const int e = (j * NTP + tid) * S::VEC, t = min(e / D, cp.L - 1), c = e % D;
+            const int64_t row = cp.row0 + (int64_t)t * a.H, off = row * D + c;
+            if (e < C * D) {
+                if (a.bw == 1)
+                    R.b[j][0] = ld_bits<E>(b + row);
+                else
+                    R.b[j] = ldg16(b + off);
+                if (a.ww == 1)
+                    R.w[j][0] = ld_bits<E>(w + row);
+                else
+                    R.w[j] = ldg16(w + off);
+            }
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// chunk_prep: one workgroup per CU, looping over chunk records with the next
-// chunk's inputs prefetched into registers while the current one computes.
-// ---------------------------------------------------------------------------
-template <typename E, int D, int C>
-__global__ __launch_bounds__(NT, 1) void chunk_prep_kernel(PrepArgs a)
+// A operand of X_II (16x16, fp32 in LDS) for one bf16 MFMA step of k = 32:
+// the second k-tile is zero.  fp32 MFMA steps are k = 16 and need no padding.
+template <typename E> struct XiiFrag;
+template <> struct XiiFrag<bf16> {
+    static __device__ __forceinline__ Mma<bf16>::Frag load(const float* p, int ld, int lane) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
+        return Mma<bf16>::pack(lo, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+};
+template <> struct XiiFrag<float> {
+    static __device__ __forceinline__ Mma<float>::Frag load(const float* p, int ld, int lane) {
+        return Mma<float>::load(p, ld, lane);
+    }
+};
+
+template <bool FULL, typename E, int D, int C>
+__global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 {
     typedef PrepShape<E, D, C> S;
     typedef Mma<E> MM;
-    constexpr int NB = S::NB, VEC = S::VEC, LDA = S::LDA, LDT = S::LDT, LDM = S::LDM;
+    constexpr int NB = S::NB, NH = S::NH, VEC = S::VEC, LDA = S::LDA, LDC = S::LDC, LDX = S::LDX;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* r1 = smem;
-    unsigned char* r2 = r1 + al256(S::R1);
-    unsigned char* r3 = r2 + al256(S::R2);
-    unsigned char* r4 = r3 + al256(S::R3);
-    int* sFlag = reinterpret_cast<int*>(r4 + al256(S::R4));
-    float* sG = reinterpret_cast<float*>(r1);            // [C][D]  (phases 1-4)
-    E* sEtT = reinterpret_cast<E*>(r1);                  // [D][LDT] (phase 6)
-    E* sUT = sEtT + D * LDT;                             // [D][LDT] (phase 6)
-    E* sEa = reinterpret_cast<E*>(r2);                   // [C][LDA] e*alpha
-    E* sQa = sEa + C * LDA;                              // [C][LDA] q*alpha
-    E* sKb = sQa + C * LDA;                              // [C][LDA] k*beta
-    float* sX = reinterpret_cast<float*>(r2);            // [C][LDM] (phases 5-6)
-    float* sY = sX + C * LDM;                            // [NB-1][16][16]
-    float* sM = reinterpret_cast<float*>(r3);            // [C][LDM]
-    float* sPart = reinterpret_cast<float*>(r3);         // [NT/D][D] (phase 2)
-    float* sF = reinterpret_cast<float*>(r4);            // [NB][NB][D] 2^(Gb[I-1]-Gb[J])
-    float* sE0 = sF + NB * NB * D;                       // [NB][D] 2^Gb[J-1]
-    float* sEl = sE0 + NB * D;                           // [NB][D] 2^(Gb[NB-1]-Gb[J])
+    float* sG = reinterpret_cast<float*>(smem + S::OFF_G);     // [C][D] cumulative log2-decay
+    E* sE = reinterpret_cast<E*>(smem + S::OFF_E);             // [C][LDA] E~, then -W
+    E* sQ = reinterpret_cast<E*>(smem + S::OFF_Q);             // [C][LDA] Q~
+    E* sKr = reinterpret_cast<E*>(smem + S::OFF_KR);           // [C][LDA] Kr
+    E* sU = reinterpret_cast<E*>(smem + S::OFF_U);             // [C][LDA] u, then U~
+    E* sEh = reinterpret_cast<E*>(smem + S::OFF_EH);           // [C-32][LDA] E^ (rows 32..)
+    E* sQh = reinterpret_cast<E*>(smem + S::OFF_QH);           // [C-32][LDA] Q^ (rows 32..)
+    E* sMb = reinterpret_cast<E*>(smem + S::OFF_MB);           // [C][LDC] -M, blocks below the diagonal
+    E* sP = reinterpret_cast<E*>(smem + S::OFF_P);             // [C][LDC] P
+    float* sMd = reinterpret_cast<float*>(smem + S::OFF_MD);   // [NB][16][LDX] -M_II
+    float* sXd = reinterpret_cast<float*>(smem + S::OFF_XD);   // [NB][16][LDX] X_II
+    float* sFk = reinterpret_cast<float*>(smem + S::OFF_T);    // [NH][D] 2^(G_last - Gh)
+    float* sPart = sFk + NH * D;                               // [PARTS][D]
+    int* sFlag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gq = lane >> 4, cl = lane & 15;
     PrepRegs<E, D, C> R;
     int64_t rec = blockIdx.x;
     if (rec >= a.nrec)
         return;
     {
         const ChunkPos cp = chunk_pos(rec, a.NC, a.T, a.H, C);
-        prep_load_gates(a, cp, R, tid);
-        prep_load_tokens(a, cp, R, tid);
+        prep_load_gates<FULL>(a, cp, R, tid);
+        prep_load_tokens<FULL>(a, cp, R, tid);
     }
 
     for (; rec < a.nrec; rec += gridDim.x) {
@@ -295,27 +392,33 @@ __global__ __launch_bounds__(NT, 1) void chunk_prep_kernel(PrepArgs a)
         const ChunkPos np = chunk_pos(next < a.nrec ? next : rec, a.NC, a.T, a.H, C);
         E* gWn = (E*)a.Wn + rec * C * D;
         E* gUt = (E*)a.Ut + rec * C * D;
-        E* gKh = (E*)a.Kh + rec * C * D;
+        E* gKt = (E*)a.Kh + rec * C * D;
         E* gQt = (E*)a.Qt + rec * C * D;
         E* gP = (E*)a.P + rec * C * C;
         float* gGam = a.gam + rec * D;
+        const int bw = FULL ? D : a.bw, ww = FULL ? D : a.ww, gw = FULL ? D : a.gw;
 
         __syncthreads();  // the previous chunk is done with every LDS region
-        // Phase 1: log-decay into LDS (natural log -> log2 units).
+        // Phase 1: log-decay into LDS in log2 units (padding rows: 0).
 #pragma unroll
         for (int j = 0; j < S::NLDG; ++j) {
-            const int e = (j * NT + tid) * 4;
-            *reinterpret_cast<f32x4*>(sG + e) = R.g[j] * kLog2e;
+            const int e = (j * NTP + tid) * 4;
+            if (e < C * D) {
+                f32x4 gv = R.g[j];
+                if (gw == 1)
+                    gv = f32x4{gv[0], gv[0], gv[0], gv[0]};
+                *reinterpret_cast<f32x4*>(sG + e) = (e / D < cp.L) ? gv * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
         if (tid == 0)
             *sFlag = 0;
         if (next < a.nrec)
-            prep_load_gates(a, np, R, tid);
+            prep_load_gates<FULL>(a, np, R, tid);
         __syncthreads();
 
         // Phase 2: inclusive prefix sum over the chunk's tokens, per channel.
         {
-            constexpr int P = NT / D, RP = C / P;
+            constexpr int RP = C / S::PARTS;
             const int i = tid % D, p = tid / D;
             float acc = 0.f;
 #pragma unroll
@@ -326,217 +429,258 @@ __global__ __launch_bounds__(NT, 1) void chunk_prep_kernel(PrepArgs a)
             sPart[p * D + i] = acc;
             __syncthreads();
             float off = 0.f;
-            for (int pp = 0; pp < p; ++pp)
-                off += sPart[pp * D + i];
-            if (p > 0) {
 #pragma unroll
-                for (int r = 0; r < RP; ++r)
-                    sG[(p * RP + r) * D + i] += off;
-            }
-        }
-        __syncthreads();
-        // Block-boundary tables, gamma, and the span guard.
-        for (int e = tid; e < NB * NB * D; e += NT) {
-            const int i = e % D, IJ = e / D, I = IJ / NB, J = IJ % NB;
-            if (J > I)
-                continue;
-            const float gprev = I > 0 ? sG[(16 * I - 1) * D + i] : 0.f;
-            const float gj = sG[(16 * J + 15) * D + i];
-            sF[e] = fast_exp2(gprev - gj);
-            if (I == J) {
-                if (gprev - gj > kSpanMax)
-                    *sFlag = 1;
-                sE0[J * D + i] = fast_exp2(gprev);
-                sEl[J * D + i] = fast_exp2(sG[(C - 1) * D + i] - gj);
-                if (J == NB - 1)
-                    gGam[i] = fast_exp2(gj);
-            }
+            for (int pp = 0; pp < S::PARTS - 1; ++pp)
+                off += pp < p ? sPart[pp * D + i] : 0.f;
+#pragma unroll
+            for (int r = 0; r < RP; ++r)
+                sG[(p * RP + r) * D + i] += off;
         }
         __syncthreads();
 
-        // Phase 3: decay-absorbed operands.
-        u32x4 rEt[S::NLD], rU[S::NLD];
+        // Phase 3: decay-referenced operands, as 16-byte LDS rows.
+        if (tid < NH * D) {
+            const int h = tid / D, i = tid % D;
+            const float gl = sG[(C - 1) * D + i];
+            const float gh = h ? sG[31 * D + i] : 0.f;
+            sFk[tid] = fast_exp2(gl - gh);
+            if (h == 0)
+                gGam[i] = fast_exp2(gl);
+        }
 #pragma unroll
         for (int j = 0; j < S::NLD; ++j) {
-            const int e = (j * NT + tid) * VEC, t = e / D, c = e % D, blk = t >> 4;
-            float kk[VEC], qq[VEC], bb[VEC], vv[VEC], ww[VEC];
+            const int e = (j * NTP + tid) * VEC;
+            if (e >= C * D)
+                continue;
+            const int t = e / D, c = e % D, h = t >> 5;
+            const bool valid = t < cp.L;
+            float kk[VEC], qq[VEC], bb[VEC], vv[VEC], ww_[VEC];
             unpack<E>(R.k[j], kk);
             unpack<E>(R.q[j], qq);
-            unpack<E>(R.b[j], bb);
             unpack<E>(R.v[j], vv);
-            unpack<E>(R.w[j], ww);
-            float ea[VEC], qa[VEC], kb[VEC], qt[VEC], kh[VEC], et[VEC], uu[VEC];
+            unpack<E>(R.b[j], bb);
+            unpack<E>(R.w[j], ww_);
+            const float bs = scalar0<E>(R.b[j]), ws = scalar0<E>(R.w[j]);
+            const float* Gt = sG + t * D + c;
+            const float* Gh = sG + 31 * D + c;
+            typename VecOf<E>::T ve, vq, vk, vu, veh, vqh;
+            bool steep = false;
 #pragma unroll
             for (int x = 0; x < VEC; ++x) {
-                const int i = c + x;
-                const float G = sG[t * D + i];
-                const float Gp = blk > 0 ? sG[(16 * blk - 1) * D + i] : 0.f;
-                const float Gc = sG[(16 * blk + 15) * D + i];
-                const float al = fast_exp2(G - Gp);
-                const float be = fast_exp2(Gc - G);
-                const float e0 = sE0[blk * D + i];
-                ea[x] = bb[x] * kk[x] * al;
-                qa[x] = qq[x] * al;
-                kb[x] = kk[x] * be;
-                qt[x] = qa[x] * e0;
-                kh[x] = kb[x] * sEl[blk * D + i];
-                et[x] = ea[x] * e0;
-                uu[x] = ww[x] * vv[x];
+                const float kx = valid ? kk[x] : 0.f;
+                const float qx = valid ? qq[x] : 0.f;
+                const float bx = bw == 1 ? bs : bb[x];
+                const float wx = valid ? (ww == 1 ? ws : ww_[x]) : 0.f;
+                const float G = Gt[x];
+                const float gh = h ? Gh[x] : 0.f;
+                const float d2 = G - gh;                  // <= 0 for decays g <= 0
+                steep |= fabsf(d2) > kSpanMax || G > kSpanMax;
+                const float e2g = fast_exp2(G);
+                const float ekr = fast_exp2(-d2);
+                const float ex = bx * kx;
+                ve[x] = from_f32<E>(ex * e2g);
+                vq[x] = from_f32<E>(qx * e2g);
+                vk[x] = from_f32<E>(kx * ekr);
+                vu[x] = from_f32<E>(wx * vv[x]);
+                if (h) {
+                    const float eh = fast_exp2(d2);
+                    veh[x] = from_f32<E>(ex * eh);
+                    vqh[x] = from_f32<E>(qx * eh);
+                }
             }
-            *reinterpret_cast<u32x4*>(sEa + t * LDA + c) = pack_vec<E>(ea);
-            *reinterpret_cast<u32x4*>(sQa + t * LDA + c) = pack_vec<E>(qa);
-            *reinterpret_cast<u32x4*>(sKb + t * LDA + c) = pack_vec<E>(kb);
-            *reinterpret_cast<u32x4*>(gQt + t * D + c) = pack_vec<E>(qt);
-            *reinterpret_cast<u32x4*>(gKh + t * D + c) = pack_vec<E>(kh);
-            rEt[j] = pack_vec<E>(et);
-            rU[j] = pack_vec<E>(uu);
+            if (steep)
+                *sFlag = 1;
+            sts16(sE + t * LDA + c, __builtin_bit_cast(u32x4, ve));
+            sts16(sQ + t * LDA + c, __builtin_bit_cast(u32x4, vq));
+            sts16(sKr + t * LDA + c, __builtin_bit_cast(u32x4, vk));
+            sts16(sU + t * LDA + c, __builtin_bit_cast(u32x4, vu));
+            stg16(gQt + t * D + c, __builtin_bit_cast(u32x4, vq));
+            if (h) {
+                sts16(sEh + (t - 32) * LDA + c, __builtin_bit_cast(u32x4, veh));
+                sts16(sQh + (t - 32) * LDA + c, __builtin_bit_cast(u32x4, vqh));
+            }
         }
         if (next < a.nrec)
-            prep_load_tokens(a, np, R, tid);
+            prep_load_tokens<FULL>(a, np, R, tid);
         __syncthreads();
 
-        // Phase 4: gated Gram M (-> LDS) and scores P (-> workspace), MFMA.
+        // Phase 4: tiles of M (-> -M in sMb / sMd) and P (-> sP), MFMA; then
+        // K^ = Kr * 2^(G_last - Gh) leaves transposed ([D][C], tokens
+        // contiguous: the layout in which it is an A operand of the state
+        // update), VEC lanes per row of K^T.
         const bool guard = *sFlag != 0;
         {
-            constexpr int NTASK = NB * (NB + 1);
-            for (int tau = wave; tau < NTASK; tau += NT / 64) {
-                const int kind = tau & 1, pair = tau >> 1;
+            constexpr int NTILE = NB * (NB + 1) / 2;
+            const int kind = wave / 4, sub = wave % 4;
+#pragma unroll
+            for (int r = 0; r < (NTILE + 3) / 4; ++r) {
+                const int tile = sub + 4 * r;
+                if (tile >= NTILE)
+                    break;
                 int I = 0;
-                while ((I + 1) * (I + 2) / 2 <= pair)
+                while ((I + 1) * (I + 2) / 2 <= tile)
                     ++I;
-                const int J = pair - I * (I + 1) / 2;
-                if (guard && I == J)
-                    continue;
-                const E* A = (kind ? sQa : sEa) + 16 * I * LDA;
-                const E* Bm = sKb + 16 * J * LDA;
-                const float* f = sF + (I * NB + J) * D;
+                const int J = tile - I * (I + 1) / 2;
+                const bool same_half = (I >> 1) == (J >> 1);
+                if (guard)
+                    break;
+                const E* A = (I >= 2 && same_half) ? (kind ? sQh : sEh) + (16 * I - 32) * LDA
+                                                   : (kind ? sQ : sE) + 16 * I * LDA;
+                const E* Bm = sKr + 16 * J * LDA;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k0 = 0; k0 < D; k0 += MM::KB)
-                    acc = MM::mma(MM::load(A + k0, LDA, lane), MM::load_scaled(Bm + k0, LDA, f + k0, lane), acc);
-                const int r0 = 16 * I + 4 * (lane >> 4), s = 16 * J + (lane & 15);
+                    acc = MM::mma(MM::load(A + k0, LDA, lane), MM::load(Bm + k0, LDA, lane), acc);
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    const int r = r0 + ii;
-                    if (kind == 0)
-                        sM[r * LDM + s] = s < r ? acc[ii] : 0.f;
-                    else
-                        gP[r * C + s] = from_f32<E>(s <= r ? acc[ii] : 0.f);
+                    const int rr = 16 * I + 4 * gq + ii, s = 16 * J + cl;
+                    if (kind == 0) {
+                        const float m = s < rr ? -acc[ii] : 0.f;
+                        if (I == J)
+                            sMd[(I * 16 + 4 * gq + ii) * LDX + cl] = m;
+                        sMb[rr * LDC + s] = from_f32<E>(I == J ? 0.f : m);
+                    } else {
+                        sP[rr * LDC + s] = from_f32<E>(s <= rr ? acc[ii] : 0.f);
+                    }
                 }
             }
-            // P is lower triangular: zero the tiles above the diagonal.
-            for (int e = tid; e < C * C; e += NT) {
-                const int r = e / C, s = e % C;
-                if ((s >> 4) > (r >> 4))
-                    gP[e] = from_f32<E>(0.f);
+            // Tiles above the block diagonal are zero in both.
+            for (int e = tid; e < C * C; e += NTP) {
+                const int rr = e / C, s = e % C;
+                if ((s >> 4) > (rr >> 4)) {
+                    sP[rr * LDC + s] = from_f32<E>(0.f);
+                    sMb[rr * LDC + s] = from_f32<E>(0.f);
+                }
+            }
+            for (int e = tid; e < D * (C / VEC); e += NTP) {
+                const int tg = e % (C / VEC), i = e / (C / VEC);
+                float x[VEC];
+                if (!guard) {
+                    const float f = sFk[((tg * VEC) >> 5) * D + i];
+#pragma unroll
+                    for (int u = 0; u < VEC; ++u)
+                        x[u] = to_f32(sKr[(tg * VEC + u) * LDA + i]) * f;
+                } else {
+                    // steep decay: K^ = k 2^(G_last - G) directly from the inputs
+                    const E* k = (const E*)a.k;
+                    const float gl = sG[(C - 1) * D + i];
+#pragma unroll
+                    for (int u = 0; u < VEC; ++u) {
+                        const int t = tg * VEC + u;
+                        const float kv = t < cp.L ? to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) : 0.f;
+                        x[u] = kv * fast_exp2(gl - sG[t * D + i]);
+                    }
+                }
+                stg16(gKt + i * C + tg * VEC, pack_vec<E>(x));
             }
         }
         if (guard) {
-            // Exact diagonal tiles for a chunk whose decay is too steep for the
-            // block-factored form: every pair from the raw inputs.
+            // Exact tiles for a chunk whose decay is too steep for the
+            // referenced form: every pair s <= t from the raw inputs.
             __syncthreads();
             const E* q = (const E*)a.q;
             const E* k = (const E*)a.k;
             const E* b = (const E*)a.b;
-            for (int e = tid; e < NB * 256; e += NT) {
-                const int I = e >> 8, r = 16 * I + ((e >> 4) & 15), s = 16 * I + (e & 15);
+            for (int e = tid; e < C * C; e += NTP) {
+                const int rr = e / C, s = e % C;
                 float m = 0.f, p = 0.f;
-                if (s <= r && r < cp.L && s < cp.L) {
-                    const int64_t rr = cp.row0 + (int64_t)r * cp.H, rs = cp.row0 + (int64_t)s * cp.H;
+                if (s <= rr && rr < cp.L) {
+                    const int64_t xr = cp.row0 + (int64_t)rr * a.H, xs = cp.row0 + (int64_t)s * a.H;
                     for (int i = 0; i < D; ++i) {
-                        const float dec = fast_exp2(sG[r * D + i] - sG[s * D + i]);
-                        const float ks = to_f32(k[rs * D + i]) * dec;
-                        const float br = to_f32(a.bw == 1 ? b[rr] : b[rr * D + i]);
-                        m += br * to_f32(k[rr * D + i]) * ks;
-                        p += to_f32(q[rr * D + i]) * ks;
+                        const float dec = fast_exp2(sG[rr * D + i] - sG[s * D + i]);
+                        const float ks = to_f32(k[xs * D + i]) * dec;
+                        const float br = to_f32(bw == 1 ? b[xr] : b[xr * D + i]);
+                        m += br * to_f32(k[xr * D + i]) * ks;
+                        p += to_f32(q[xr * D + i]) * ks;
                     }
                 }
-                sM[r * LDM + s] = s < r ? m : 0.f;
-                gP[r * C + s] = from_f32<E>(p);
+                const float mn = s < rr ? -m : 0.f;
+                if ((rr >> 4) == (s >> 4))
+                    sMd[((rr >> 4) * 16 + (rr & 15)) * LDX + (s & 15)] = mn;
+                sMb[rr * LDC + s] = from_f32<E>((rr >> 4) == (s >> 4) ? 0.f : mn);
+                sP[rr * LDC + s] = from_f32<E>(p);
             }
         }
         __syncthreads();
 
-        // Phase 5: X = (I + M)^-1.  Diagonal 16x16 blocks by forward
-        // substitution (one lane per column), then the blocks below the
-        // diagonal level by level: X_IJ = -X_II sum_{J<=K<I} M_IK X_KJ.
-        for (int e = tid; e < C * C; e += NT) {
-            const int r = e / C, s = e % C;
-            if ((s >> 4) > (r >> 4))
-                sX[r * LDM + s] = 0.f;
-        }
-        if (wave == 0 && (lane >> 4) < NB) {
-            const int I = lane >> 4, j = lane & 15;
-            const float* m = sM + 16 * I * LDM + 16 * I;
-            float x[16];
+        // Phase 5: wave 0 inverts the diagonal blocks by forward substitution
+        // (one lane per column, fp32); the other waves write P out.
+        if (wave == 0) {
+            if (gq < NB) {
+                const float* m = sMd + gq * 16 * LDX;
+                float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == j ? 1.f : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    float acc = r == cl ? 1.f : 0.f;
 #pragma unroll
-                for (int c = 0; c < r; ++c)
-                    acc -= m[r * LDM + c] * x[c];
-                x[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sX[(16 * I + r) * LDM + 16 * I + j] = x[r];
-        }
-        __syncthreads();
-        for (int d = 1; d < NB; ++d) {
-            const int nblk = NB - d;
-            for (int e = tid; e < nblk * 256; e += NT) {
-                const int I = d + (e >> 8), J = I - d, r = (e >> 4) & 15, c = e & 15;
-                float y = 0.f;
-                for (int K = J; K < I; ++K) {
-#pragma unroll
-                    for (int s = 0; s < 16; ++s)
-                        y += sM[(16 * I + r) * LDM + 16 * K + s] * sX[(16 * K + s) * LDM + 16 * J + c];
+                    for (int c2 = 0; c2 < r; ++c2)
+                        acc += m[r * LDX + c2] * x[c2];
+                    x[r] = acc;
+                    // keep each row's LDS reads next to their use (bounded registers)
+                    __asm__ __volatile__("" ::: "memory");
                 }
-                sY[e] = y;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sXd[(gq * 16 + r) * LDX + cl] = x[r];
             }
-            __syncthreads();
-            for (int e = tid; e < nblk * 256; e += NT) {
-                const int I = d + (e >> 8), J = I - d, r = (e >> 4) & 15, c = e & 15;
-                float x = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    x -= sX[(16 * I + r) * LDM + 16 * I + m] * sY[(e >> 8) * 256 + m * 16 + c];
-                sX[(16 * I + r) * LDM + 16 * J + c] = x;
-            }
-            __syncthreads();
-        }
-
-        // Phase 6: W = X (e*2^G) and U~ = X u, with the right-hand sides
-        // stored transposed so their B fragments are contiguous along tokens.
-#pragma unroll
-        for (int j = 0; j < S::NLD; ++j) {
-            const int e = (j * NT + tid) * VEC, t = e / D, c = e % D;
-            float et[VEC], uu[VEC];
-            unpack<E>(rEt[j], et);
-            unpack<E>(rU[j], uu);
-#pragma unroll
-            for (int x = 0; x < VEC; ++x) {
-                sEtT[(c + x) * LDT + t] = from_f32<E>(et[x]);
-                sUT[(c + x) * LDT + t] = from_f32<E>(uu[x]);
+        } else {
+            for (int e = tid - 64; e < C * (C / VEC); e += NTP - 64) {
+                const int rr = e / (C / VEC), cg = e % (C / VEC);
+                stg16(gP + rr * C + cg * VEC, lds16(sP + rr * LDC + cg * VEC));
             }
         }
         __syncthreads();
+
+        // Phase 6: blocked substitution for [W | U~], 2D/8 right-hand-side
+        // columns per wave (waves 0-3: E~ -> W, waves 4-7: u -> U~), solved
+        // blocks kept as MFMA accumulators.
         {
-            constexpr int NTILE = NB * (D / 16);
-            for (int tau = wave; tau < 2 * NTILE; tau += NT / 64) {
-                const int kind = tau / NTILE, rem = tau % NTILE, mt = rem / (D / 16), nt = rem % (D / 16);
-                const E* Bm = (kind ? sUT : sEtT) + 16 * nt * LDT;
-                const float* A = sX + 16 * mt * LDM;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int k0 = 0; k0 < 16 * (mt + 1); k0 += MM::KB)
-                    acc = MM::mma(MM::load(A + k0, LDM, lane), MM::load(Bm + k0, LDT, lane), acc);
-                const int r0 = 16 * mt + 4 * (lane >> 4), col = 16 * nt + (lane & 15);
-                E* out = kind ? gUt : gWn;
-                const float sg = kind ? 1.f : -1.f;
+            constexpr int NCT = 2 * D / NWP / 16;     // 16-column tiles per wave
+            E* rhs = wave < NWP / 2 ? sE : sU;
+            const int c0 = 16 * NCT * (wave % (NWP / 2));
+            f32x4 sol[NCT][NB];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-                    out[(r0 + ii) * D + col] = from_f32<E>(sg * acc[ii]);
+            for (int n = 0; n < NCT; ++n)
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+                    sol[n][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                f32x4 res[NCT];
+#pragma unroll
+                for (int n = 0; n < NCT; ++n) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        res[n][ii] = to_f32(rhs[(16 * I + 4 * gq + ii) * LDA + c0 + 16 * n + cl]);
+                }
+#pragma unroll
+                for (int kk = 0; kk < I; kk += MM::KT) {
+                    const typename MM::Frag am = MM::load(sMb + 16 * I * LDC + 16 * kk, LDC, lane);
+#pragma unroll
+                    for (int n = 0; n < NCT; ++n)
+                        res[n] = MM::mma(am, MM::from_acc(&sol[n][kk]), res[n]);
+                }
+                const typename MM::Frag ax = XiiFrag<E>::load(sXd + I * 16 * LDX, LDX, lane);
+#pragma unroll
+                for (int n = 0; n < NCT; ++n) {
+                    const f32x4 pair[2] = {res[n], res[n]};
+                    sol[n][I] = MM::mma(ax, MM::from_acc(pair), f32x4{0.f, 0.f, 0.f, 0.f});
+                }
             }
+            const float sg = wave < NWP / 2 ? -1.f : 1.f;   // W leaves negated
+#pragma unroll
+            for (int n = 0; n < NCT; ++n)
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        rhs[(16 * I + 4 * gq + ii) * LDA + c0 + 16 * n + cl] = from_f32<E>(sg * sol[n][I][ii]);
+        }
+        __syncthreads();
+        for (int e = tid; e < C * (D / VEC); e += NTP) {
+            const int rr = e / (D / VEC), cg = e % (D / VEC);
+            stg16(gWn + rr * D + cg * VEC, lds16(sE + rr * LDA + cg * VEC));
+            stg16(gUt + rr * D + cg * VEC, lds16(sU + rr * LDA + cg * VEC));
         }
     }
 }
@@ -662,11 +806,7 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(StateArgs a)
             const int e = (j * NT + tid) * VEC, t = e / D, c = e % D;
             *reinterpret_cast<u32x4*>(sW + t * LDA + c) = R.w[j];
             *reinterpret_cast<u32x4*>(sQ + t * LDA + c) = R.q[j];
-            float kv[VEC];
-            unpack<E>(R.kh[j], kv);
-#pragma unroll
-            for (int xx = 0; xx < VEC; ++xx)
-                sKT[(c + xx) * LDT + t] = from_f32<E>(kv[xx]);
+            *reinterpret_cast<u32x4*>(sKT + (e / C) * LDT + e % C) = R.kh[j];
         }
 #pragma unroll
         for (int j = 0; j < S::NLDP; ++j) {
@@ -793,21 +933,32 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     pa.gam = reinterpret_cast<float*>(ws + L.gam);
 
     static const hipError_t attr1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<E, D, C>),
+        reinterpret_cast<const void*>(&chunk_prep_kernel<true, E, D, C>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
+    static const hipError_t attr1g = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&chunk_prep_kernel<false, E, D, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
     static const hipError_t attr2 = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&chunk_state_kernel<E, D, C, BV>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)SS::SMEM);
     if (attr1 != hipSuccess)
         return attr1;
+    if (attr1g != hipSuccess)
+        return attr1g;
     if (attr2 != hipSuccess)
         return attr2;
 
-    const int64_t grid1 = std::min<int64_t>(L.nrec, (int64_t)cu_count());
-    hipLaunchKernelGGL((chunk_prep_kernel<E, D, C>), dim3((unsigned)grid1), dim3(NT), PS::SMEM, stream, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    if (a.stage != GDR2_STAGE_STATE) {
+        const int64_t grid1 = std::min<int64_t>(L.nrec, (int64_t)cu_count());
+        const bool full = a.b_width == D && a.w_width == D && a.g_width == D;
+        if (full)
+            hipLaunchKernelGGL((chunk_prep_kernel<true, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM, stream, pa);
+        else
+            hipLaunchKernelGGL((chunk_prep_kernel<false, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM, stream, pa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.stage == GDR2_STAGE_PREP)
+            return e;
+    }
 
     StateArgs sa;
     sa.Wn = pa.Wn; sa.Ut = pa.Ut; sa.Kh = pa.Kh; sa.Qt = pa.Qt; sa.P = pa.P; sa.gam = pa.gam;

@@ -120,6 +120,15 @@ template <> struct Mma<bf16> {
         f32x4 b = {(float)hi[0] * fhi[0], (float)hi[1] * fhi[1], (float)hi[2] * fhi[2], (float)hi[3] * fhi[3]};
         return pack(a, b);
     }
+    // B operand from a matrix stored k-major (row = k, n contiguous): lane l
+    // gathers column l%16 at rows 4gq..4gq+3 and 16+4gq..16+4gq+3.
+    static __device__ __forceinline__ Frag load_kn(const bf16* p, int ld, int lane) {
+        const bf16* s = p + 4 * (lane >> 4) * ld + (lane & 15);
+        Frag f;
+        f[0] = s[0]; f[1] = s[ld]; f[2] = s[2 * ld]; f[3] = s[3 * ld];
+        f[4] = s[16 * ld]; f[5] = s[17 * ld]; f[6] = s[18 * ld]; f[7] = s[19 * ld];
+        return f;
+    }
     // B operand from accumulator tiles t[0], t[1] (two consecutive k-tiles).
     static __device__ __forceinline__ Frag from_acc(const f32x4* t) { return pack(t[0], t[1]); }
     static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
@@ -139,6 +148,10 @@ template <> struct Mma<float> {
         const int c = 4 * (lane >> 4);
         return *reinterpret_cast<const f32x4*>(p + (lane & 15) * ld + c) *
                *reinterpret_cast<const f32x4*>(f + c);
+    }
+    static __device__ __forceinline__ Frag load_kn(const float* p, int ld, int lane) {
+        const float* s = p + 4 * (lane >> 4) * ld + (lane & 15);
+        return Frag{s[0], s[ld], s[2 * ld], s[3 * ld]};
     }
     static __device__ __forceinline__ Frag from_acc(const f32x4* t) { return t[0]; }
     static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {

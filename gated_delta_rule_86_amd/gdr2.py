@@ -20,6 +20,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 ALGO_AUTO, ALGO_STAGED = 0, 1
 ALGOS = {"auto": ALGO_AUTO, "staged": ALGO_STAGED}
+STAGES = {"all": 0, "prep": 1, "state": 2}
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -28,8 +29,8 @@ _vp = ctypes.c_void_p
 
 class FwdArgs(ctypes.Structure):
     _fields_ = [("B", _c_i64), ("T", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
-                ("chunk", _c_i32), ("dtype", _c_i32), ("algo", _c_i32),
-                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32),
+                ("chunk", _c_i32), ("dtype", _c_i32), ("algo", _c_i32), ("stage", _c_i32),
+                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("reserved", _c_i32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp),
                 ("g", _vp), ("S0", _vp), ("o", _vp), ("S_out", _vp),
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
@@ -113,11 +114,11 @@ def _req(t: torch.Tensor, name: str, dtype=None):
 
 
 def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
-             algo: str = "auto", workspace=None) -> FwdArgs:
+             algo: str = "auto", workspace=None, stage: str = "all") -> FwdArgs:
     B, T, H, Dk = q.shape
     a = FwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, v.shape[-1]
-    a.chunk, a.dtype, a.algo = chunk, _dtype_code(q), ALGOS[algo]
+    a.chunk, a.dtype, a.algo, a.stage = chunk, _dtype_code(q), ALGOS[algo], STAGES[stage]
     a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
     a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
     a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
@@ -127,10 +128,13 @@ def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
 
 
 def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
-            out=None, S_out=None, workspace=None, final_state: bool = True):
+            out=None, S_out=None, workspace=None, final_state: bool = True,
+            stage: str = "all"):
     """Chunked forward.  q,k [B,T,H,Dk]; v [B,T,H,Dv]; b [B,T,H,1|Dk];
     w [B,T,H,1|Dv] (all float32 or bfloat16); g float32 [B,T,H,1|Dk];
-    S0 float32 [B,H,Dk,Dv] or None.  Returns (o, S_final)."""
+    S0 float32 [B,H,Dk,Dv] or None.  Returns (o, S_final).
+    stage='prep' / 'state' runs one kernel of the staged algorithm (pass the
+    same workspace, out and S_out to both calls)."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w)):
         _req(t, n, q.dtype)
@@ -143,7 +147,7 @@ def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
         out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
     if S_out is None and final_state:
         S_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo)
+    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, stage=stage)
     need = lib.gdr2_forward_workspace_size(ctypes.byref(a))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

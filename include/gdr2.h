@@ -87,6 +87,17 @@ typedef enum gdr2_algo {
                               through the chunks and writes o */
 } gdr2_algo;
 
+/* Which kernels of GDR2_ALGO_STAGED one call runs.  Two calls on the same
+ * stream, PREP then STATE, with identical arguments (workspace included),
+ * give exactly the result of one GDR2_STAGE_ALL call; the split exists so the
+ * two kernels can be timed or scheduled separately.  A STATE call reads the
+ * per-chunk factors the PREP call left in the workspace. */
+typedef enum gdr2_stage {
+    GDR2_STAGE_ALL = 0,
+    GDR2_STAGE_PREP = 1,   /* intra-chunk kernel only (writes the workspace) */
+    GDR2_STAGE_STATE = 2   /* propagation/output kernel only (reads it) */
+} gdr2_stage;
+
 /*
  * Arguments of the chunked forward.
  *   q, k   [B, T, H, Dk]        dtype
@@ -110,7 +121,9 @@ typedef struct gdr2_fwd_args {
     int32_t chunk;
     int32_t dtype;        /* gdr2_dtype */
     int32_t algo;         /* gdr2_algo */
+    int32_t stage;        /* gdr2_stage */
     int32_t b_width, w_width, g_width;
+    int32_t reserved;     /* must be 0 */
     const void *q, *k, *v, *b, *w;
     const float *g;
     const float *S0;

@@ -98,6 +98,8 @@ FWD_CASES = [
     ("f32_too_large", _mod(dtype=gdr2.F32), gdr2.ERR_UNSUPPORTED),   # D=128, chunk=64
     ("bad_dtype", _mod(dtype=7), gdr2.ERR_INVALID_ARG),
     ("bad_algo", _mod(algo=9), gdr2.ERR_INVALID_ARG),
+    ("bad_stage", _mod(stage=3), gdr2.ERR_INVALID_ARG),
+    ("reserved_set", _mod(reserved=1), gdr2.ERR_INVALID_ARG),
     ("bad_b_width", _mod(b_width=3), gdr2.ERR_INVALID_ARG),
     ("bad_w_width", _mod(w_width=64), gdr2.ERR_INVALID_ARG),
     ("bad_g_width", _mod(g_width=2), gdr2.ERR_INVALID_ARG),

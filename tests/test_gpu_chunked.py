@@ -176,3 +176,19 @@ def test_weak_decay_long_sequence():
     the accumulated chunk updates; the error must not grow past tolerance."""
     wl = Workload("weak", "forward", 1, 8192, 2, 128, "bf16", "full", 0.02, 64, 4321, g_scale=0.01)
     check(draw(wl), 64, "bf16", "weak decay T=8192")
+
+
+def test_stage_split_equals_one_call():
+    """PREP then STATE as two calls gives bit for bit the one-call result."""
+    wl = Workload("stages", "forward", 2, 200, 2, 128, "bf16", "full", 0.05, 64, 12)
+    inp = draw(wl)
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    o1, S1 = gdr2.forward(*args, S0=d["S0"], chunk=64)
+    ws = torch.empty(gdr2.workspace_size(*args, chunk=64), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    S2 = torch.empty_like(S1)
+    gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="prep")
+    gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="state")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
