@@ -53,6 +53,8 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 // Workspace: per chunk record (sequence, head, chunk), element type E:
 //   Wn [C][D] = -W,  Ut [C][D] = U~,  Kh [D][C] = K^ transposed,  Qt [C][D] = Q~,
 //   P [C][C],  gam [D] fp32.   Records are ordered (b*H + h)*NC + n.
+//   Wn, Qt, Kh and P (the A operands of the state kernel) store their
+//   contraction dimension in MFMA k-order (perm_chunk); U~ is plain.
 // ---------------------------------------------------------------------------
 struct Layout {
     int64_t nrec;
@@ -237,6 +239,37 @@ __device__ __forceinline__ u32x4 lds16(const void* p)
 __device__ __forceinline__ void sts16(void* p, u32x4 v)
 {
     *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// MFMA k-order of the state kernel's A operands (bf16): within every block of
+// 32 elements along k, physical 16-byte chunk g holds logical elements
+// 4g..4g+3 and 16+4g..16+4g+3 -- exactly the k values lane group g of a
+// 16x16x32 MFMA takes from accumulator-layout B operands -- so a fragment is
+// one 16-byte LDS read.  fp32 operands are already in that order (identity).
+// perm_chunk: the 16 bytes of physical chunk pc, gathered from a row held in
+// logical order.
+template <typename E>
+__device__ __forceinline__ u32x4 perm_chunk(const E* row, int pc);
+template <>
+__device__ __forceinline__ u32x4 perm_chunk<bf16>(const bf16* row, int pc)
+{
+    const bf16* p = row + 32 * (pc >> 2) + 4 * (pc & 3);
+    const unsigned int* lo = reinterpret_cast<const unsigned int*>(p);
+    const unsigned int* hi = reinterpret_cast<const unsigned int*>(p + 16);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+template <>
+__device__ __forceinline__ u32x4 perm_chunk<float>(const float* row, int pc)
+{
+    return *reinterpret_cast<const u32x4*>(row + 4 * pc);
+}
+// Logical index of element u of physical chunk pc (the same order).
+template <typename E>
+__device__ __forceinline__ int perm_index(int pc, int u)
+{
+    if (sizeof(E) == 4)
+        return 4 * pc + u;
+    return 32 * (pc >> 2) + 4 * (pc & 3) + (u < 4 ? u : 12 + u);
 }
 
 // Bits of one element, for width-1 gates.
@@ -494,7 +527,6 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             sts16(sQ + t * LDA + c, __builtin_bit_cast(u32x4, vq));
             sts16(sKr + t * LDA + c, __builtin_bit_cast(u32x4, vk));
             sts16(sU + t * LDA + c, __builtin_bit_cast(u32x4, vu));
-            stg16(gQt + t * D + c, __builtin_bit_cast(u32x4, vq));
             if (h) {
                 sts16(sEh + (t - 32) * LDA + c, __builtin_bit_cast(u32x4, veh));
                 sts16(sQh + (t - 32) * LDA + c, __builtin_bit_cast(u32x4, vqh));
@@ -559,14 +591,14 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
                     const float f = sFk[((tg * VEC) >> 5) * D + i];
 #pragma unroll
                     for (int u = 0; u < VEC; ++u)
-                        x[u] = to_f32(sKr[(tg * VEC + u) * LDA + i]) * f;
+                        x[u] = to_f32(sKr[perm_index<E>(tg, u) * LDA + i]) * f;
                 } else {
                     // steep decay: K^ = k 2^(G_last - G) directly from the inputs
                     const E* k = (const E*)a.k;
                     const float gl = sG[(C - 1) * D + i];
 #pragma unroll
                     for (int u = 0; u < VEC; ++u) {
-                        const int t = tg * VEC + u;
+                        const int t = perm_index<E>(tg, u);
                         const float kv = t < cp.L ? to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) : 0.f;
                         x[u] = kv * fast_exp2(gl - sG[t * D + i]);
                     }
@@ -626,7 +658,11 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         } else {
             for (int e = tid - 64; e < C * (C / VEC); e += NTP - 64) {
                 const int rr = e / (C / VEC), cg = e % (C / VEC);
-                stg16(gP + rr * C + cg * VEC, lds16(sP + rr * LDC + cg * VEC));
+                stg16(gP + rr * C + cg * VEC, perm_chunk<E>(sP + rr * LDC, cg));
+            }
+            for (int e = tid - 64; e < C * (D / VEC); e += NTP - 64) {
+                const int rr = e / (D / VEC), cg = e % (D / VEC);
+                stg16(gQt + rr * D + cg * VEC, perm_chunk<E>(sQ + rr * LDA, cg));
             }
         }
         __syncthreads();
@@ -679,7 +715,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         __syncthreads();
         for (int e = tid; e < C * (D / VEC); e += NTP) {
             const int rr = e / (D / VEC), cg = e % (D / VEC);
-            stg16(gWn + rr * D + cg * VEC, lds16(sE + rr * LDA + cg * VEC));
+            stg16(gWn + rr * D + cg * VEC, perm_chunk<E>(sE + rr * LDA, cg));
             stg16(gUt + rr * D + cg * VEC, lds16(sU + rr * LDA + cg * VEC));
         }
     }
@@ -688,101 +724,284 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 // ---------------------------------------------------------------------------
 // chunk_state: carries the fp32 state through the chunks of one sequence and
 // head, BV value columns per workgroup (16 per wave), and writes o.
+//
+// The factors of a chunk (-W, Q~, K^T, P, this slice of U~, gamma) are copied
+// from the workspace straight into LDS with global_load_lds_dwordx4 (no
+// register staging), double buffered: the copy of chunk n + 1 is in flight
+// while chunk n computes.  The two buffers are separate static LDS objects so
+// that reads of one are never ordered behind the copies into the other.
+// Rows are padded by 16 bytes (one extra copy slot per row, filled with a
+// harmless duplicate) so that fragment reads of 16 consecutive rows hit 16
+// different bank groups.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C, int BV>
 struct StateShape {
     static constexpr int NB = C / 16;
-    static constexpr int VEC = 16 / (int)sizeof(E);
-    static constexpr int NS = D / BV;                     // column slices per (b,h)
-    static constexpr int LDA = D + 16 / (int)sizeof(E);   // sW, sQ  [C][LDA]
-    static constexpr int LDT = C + 16 / (int)sizeof(E);   // sKT [D][LDT], sP [C][LDT]
-    static constexpr int LDU = BV + 16 / (int)sizeof(E);  // sU  [C][LDU]
-    static constexpr int NLD = C * D / (NT * VEC);
-    static constexpr int NLDP = (C * C + NT * VEC - 1) / (NT * VEC);
-    static constexpr int NLDU = (C * BV + NT * VEC - 1) / (NT * VEC);
-    static constexpr size_t SMEM = al256((size_t)C * LDA * sizeof(E)) * 2 +
-                                   al256((size_t)D * LDT * sizeof(E)) +
-                                   al256((size_t)C * LDT * sizeof(E)) +
-                                   al256((size_t)C * LDU * sizeof(E)) + al256((size_t)D * 4);
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int VEC = 16 / ES;
+    static constexpr int NS = D / BV;                       // column slices per (b,h)
+    static constexpr int LDA = D + VEC;                     // W, Q~ rows (elements)
+    static constexpr int LDT = C + VEC;                     // K^T, P rows
+    static constexpr int LDU = BV + VEC;                    // U~ slice rows
+    static constexpr int LDO = 16 + VEC;                    // per-wave output staging rows
+    static constexpr int OFF_W = 0;                         // element offsets in one buffer
+    static constexpr int OFF_Q = OFF_W + C * LDA;
+    static constexpr int OFF_KT = OFF_Q + C * LDA;
+    static constexpr int OFF_P = OFF_KT + D * LDT;
+    static constexpr int OFF_U = OFF_P + C * LDT;
+    static constexpr int OFF_G = OFF_U + C * LDU;           // gamma: D floats
+    static constexpr int BUF = OFF_G + D * 4 / ES;          // elements per buffer
+    static constexpr size_t SZ_O = (size_t)(NT / 64) * C * LDO * ES;
+    // double buffering when two buffers fit (every bf16 shape); else one
+    static constexpr int NBUF = 2 * (size_t)BUF * ES + SZ_O <= 160 * 1024 ? 2 : 1;
+    static constexpr size_t SMEM = NBUF * (size_t)BUF * ES + SZ_O;
     static_assert(BV == 16 * (NT / 64), "one 16-column tile per wave");
-    static_assert(C * D % (NT * VEC) == 0, "tile / thread mismatch");
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-template <typename E, int D, int C, int BV>
-struct StateRegs {
-    typedef StateShape<E, D, C, BV> S;
-    u32x4 w[S::NLD], q[S::NLD], kh[S::NLD], p[S::NLDP], u[S::NLDU];
-    f32x4 gam;
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename E, int D, int C, int BV>
-__device__ __forceinline__ void state_load(const StateArgs& a, int64_t rec, int slice,
-                                           StateRegs<E, D, C, BV>& R, int tid)
-{
-    typedef StateShape<E, D, C, BV> S;
-    const E* Wn = (const E*)a.Wn + rec * C * D;
-    const E* Qt = (const E*)a.Qt + rec * C * D;
-    const E* Kh = (const E*)a.Kh + rec * C * D;
-    const E* P = (const E*)a.P + rec * C * C;
-    const E* Ut = (const E*)a.Ut + rec * C * D;
+// Copy R rows of RB bytes (global rows GS bytes apart) into LDS rows of
+// RB + 16 bytes, 16 bytes per lane per instruction, instructions spread over
+// the waves (instruction j belongs to wave j % 4).  Copy slot s of the tile
+// is LDS byte 16*s; the last slot of each row is padding and receives a
+// duplicate of the row's first 16 bytes.  The per-lane source offsets are the
+// same for every chunk and are computed once.
+template <int R, int RB>
+struct TileCopy {
+    static constexpr int SPR = RB / 16 + 1, TOTAL = R * SPR, NINST = (TOTAL + 63) / 64;
+    static constexpr int PER_WAVE = (NINST + NT / 64 - 1) / (NT / 64);
+    int off[PER_WAVE];     // source byte offset, or -1 where the lane has no slot
+    __device__ __forceinline__ void init(int64_t gs, int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < S::NLD; ++j) {
-        const int e = (j * NT + tid) * S::VEC;
-        R.w[j] = *reinterpret_cast<const u32x4*>(Wn + e);
-        R.q[j] = *reinterpret_cast<const u32x4*>(Qt + e);
-        R.kh[j] = *reinterpret_cast<const u32x4*>(Kh + e);
-    }
-#pragma unroll
-    for (int j = 0; j < S::NLDP; ++j) {
-        const int e = (j * NT + tid) * S::VEC;
-        if (e < C * C)
-            R.p[j] = *reinterpret_cast<const u32x4*>(P + e);
-    }
-#pragma unroll
-    for (int j = 0; j < S::NLDU; ++j) {
-        const int e = (j * NT + tid) * S::VEC;
-        if (e < C * BV) {
-            const int t = e / BV, c = e % BV;
-            R.u[j] = *reinterpret_cast<const u32x4*>(Ut + t * D + slice * BV + c);
+        for (int u = 0; u < PER_WAVE; ++u) {
+            const int j = u * (NT / 64) + wave, sl = j * 64 + lane;
+            const int row = sl / SPR, c = sl % SPR;
+            off[u] = (j < NINST && sl < TOTAL) ? (int)(row * gs + (c == SPR - 1 ? 0 : c * 16)) : -1;
         }
     }
-    if (tid < D / 4)
-        R.gam = *reinterpret_cast<const f32x4*>(a.gam + rec * D + tid * 4);
-}
+    __device__ __forceinline__ void issue(const unsigned char* g, unsigned char* l, int wave) const {
+#pragma unroll
+        for (int u = 0; u < PER_WAVE; ++u) {
+            const int j = u * (NT / 64) + wave;
+            // wave-uniform except in a partial last instruction
+            if (j < NINST && (TOTAL % 64 == 0 || off[u] >= 0))
+                __builtin_amdgcn_global_load_lds(g + off[u], (lds_void*)(l + j * 64 * 16), 16, 0, 0);
+        }
+    }
+};
 
 template <typename E, int D, int C, int BV>
-__global__ __launch_bounds__(NT, 1) void chunk_state_kernel(StateArgs a)
+struct StateCopies {
+    TileCopy<C, D * (int)sizeof(E)> wq;     // -W and Q~ (same shape)
+    TileCopy<D, C * (int)sizeof(E)> kt;     // K^T
+    TileCopy<C, C * (int)sizeof(E)> p;      // P
+    TileCopy<C, BV * (int)sizeof(E)> u;     // this slice of U~
+    __device__ __forceinline__ void init(int wave, int lane) {
+        constexpr int ES = (int)sizeof(E);
+        wq.init(D * ES, wave, lane);
+        kt.init(C * ES, wave, lane);
+        p.init(C * ES, wave, lane);
+        u.init(D * ES, wave, lane);
+    }
+};
+
+template <typename E, int D, int C, int BV>
+__device__ __forceinline__ void state_fetch(const StateArgs& a, const StateCopies<E, D, C, BV>& cp,
+                                            int64_t rec, int slice, E* buf, int wave, int lane)
+{
+    typedef StateShape<E, D, C, BV> S;
+    constexpr int ES = S::ES;
+    unsigned char* l = reinterpret_cast<unsigned char*>(buf);
+    cp.wq.issue((const unsigned char*)((const E*)a.Wn + rec * C * D), l + S::OFF_W * ES, wave);
+    cp.wq.issue((const unsigned char*)((const E*)a.Qt + rec * C * D), l + S::OFF_Q * ES, wave);
+    cp.kt.issue((const unsigned char*)((const E*)a.Kh + rec * C * D), l + S::OFF_KT * ES, wave);
+    cp.p.issue((const unsigned char*)((const E*)a.P + rec * C * C), l + S::OFF_P * ES, wave);
+    cp.u.issue((const unsigned char*)((const E*)a.Ut + rec * C * D + slice * BV), l + S::OFF_U * ES, wave);
+    // gamma: D floats, one unpadded row
+    if (wave == 0 && lane < D / 4)
+        __builtin_amdgcn_global_load_lds(a.gam + rec * D + lane * 4, (lds_void*)(l + S::OFF_G * ES), 16, 0, 0);
+}
+
+// Scheduling hint for a phase of N MFMAs fed from LDS: issue the first
+// group of fragment reads, then alternate one MFMA with one more read, so
+// reads run ahead of the MFMAs that consume them.
+template <int N>
+__device__ __forceinline__ void sched_pipeline()
+{
+    constexpr int AHEAD = N < 8 ? N : 8;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);   // DS reads
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // DS reads
+    }
+}
+
+// s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed.
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One chunk from buffer `buf`: Delta = U~ - W S, O = Q~ S + P Delta,
+// S <- diag(gamma) S + K^T Delta; O goes out through the wave's staging rows.
+template <typename E, int D, int C, int BV>
+__device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
+                                             int slice, int64_t n, int lane, int wave);
+
+template <typename E, int D, int C, int BV>
+__device__ __forceinline__ void state_compute(const StateArgs& a, const E* buf, E* sOw, f32x4* St,
+                                              int64_t b, int64_t h, int slice, int64_t n,
+                                              int lane, int wave)
 {
     typedef StateShape<E, D, C, BV> S;
     typedef Mma<E> MM;
-    constexpr int NB = S::NB, VEC = S::VEC, LDA = S::LDA, LDT = S::LDT, LDU = S::LDU;
-    constexpr int KTS = D / 16;          // k-tiles of the state rows
+    constexpr int NB = S::NB, VEC = S::VEC, LDA = S::LDA, LDT = S::LDT, LDU = S::LDU, LDO = S::LDO;
     constexpr int NKS = D / MM::KB;      // MFMA steps over the state rows
     constexpr int NKC = C / MM::KB;      // MFMA steps over the chunk's tokens
+    constexpr int KTS = D / 16;
+    const int gq = lane >> 4, cl = lane & 15;
+    const E* sW = buf + S::OFF_W;
+    const E* sQ = buf + S::OFF_Q;
+    const E* sKT = buf + S::OFF_KT;
+    const E* sP = buf + S::OFF_P;
+    const E* sU = buf + S::OFF_U;
+    const float* sGam = reinterpret_cast<const float*>(buf + S::OFF_G);
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    E* sW = reinterpret_cast<E*>(smem);
-    E* sQ = reinterpret_cast<E*>(smem + al256((size_t)C * LDA * sizeof(E)));
-    E* sKT = reinterpret_cast<E*>(smem + 2 * al256((size_t)C * LDA * sizeof(E)));
-    E* sP = reinterpret_cast<E*>((unsigned char*)sKT + al256((size_t)D * LDT * sizeof(E)));
-    E* sU = reinterpret_cast<E*>((unsigned char*)sP + al256((size_t)C * LDT * sizeof(E)));
-    float* sGam = reinterpret_cast<float*>((unsigned char*)sU + al256((size_t)C * LDU * sizeof(E)));
+    typename MM::Frag SB[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        SB[ks] = MM::from_acc(&St[ks * MM::KT]);
+
+    // Delta = U~ - W S  (W is stored negated).  Each phase reads all of its
+    // A fragments before its MFMAs so LDS latency overlaps.
+    f32x4 dl[NB];
+    {
+        typename MM::Frag aw[NB][NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                aw[mt][ks] = MM::load_perm(sW + 16 * mt * LDA + ks * MM::KB, LDA, lane);
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dl[mt][i] = to_f32(sU[(16 * mt + 4 * gq + i) * LDU + 16 * wave + cl]);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                dl[mt] = MM::mma(aw[mt][ks], SB[ks], dl[mt]);
+        sched_pipeline<NB * NKS>();
+    }
+    typename MM::Frag DB[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        DB[kc] = MM::from_acc(&dl[kc * MM::KT]);
+    // the previous chunk's outputs leave while this one computes
+    if (n > 0)
+        state_store_o<E, D, C, BV>(a, sOw, b, h, slice, n - 1, lane, wave);
+
+    // O = Q~ S + P Delta  (P is lower triangular: skip all-zero steps).
+    f32x4 ot[NB];
+    {
+        typename MM::Frag aq[NB][NKS], ap[NB][NKC];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                aq[mt][ks] = MM::load_perm(sQ + 16 * mt * LDA + ks * MM::KB, LDA, lane);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                if (kc * MM::KT <= mt)
+                    ap[mt][kc] = MM::load_perm(sP + 16 * mt * LDT + kc * MM::KB, LDT, lane);
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                ot[mt] = MM::mma(aq[mt][ks], SB[ks], ot[mt]);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                if (kc * MM::KT <= mt)
+                    ot[mt] = MM::mma(ap[mt][kc], DB[kc], ot[mt]);
+        sched_pipeline<NB * NKS>();
+    }
+
+    // S <- diag(gamma) S + K^T Delta.
+    {
+        typename MM::Frag ak[KTS][NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int kt = 0; kt < KTS; ++kt)
+                ak[kt][kc] = MM::load_perm(sKT + 16 * kt * LDT + kc * MM::KB, LDT, lane);
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+            St[kt] = St[kt] * *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * gq);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int kt = 0; kt < KTS; ++kt)
+                St[kt] = MM::mma(ak[kt][kc], DB[kc], St[kt]);
+        sched_pipeline<KTS * NKC>();
+    }
+
+    // O: into this wave's staging rows; written out during the next chunk.
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sOw[(16 * mt + 4 * gq + i) * LDO + cl] = from_f32<E>(ot[mt][i]);
+}
+
+// 16-byte stores of one wave's 16 staged output columns of chunk n.
+template <typename E, int D, int C, int BV>
+__device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
+                                             int slice, int64_t n, int lane, int wave)
+{
+    typedef StateShape<E, D, C, BV> S;
+    constexpr int VEC = S::VEC, LDO = S::LDO, CPR = 16 / VEC;   // 16-byte pieces per staged row
+    const int64_t t0 = n * C;
+    const int L = (int)min((int64_t)C, a.T - t0);
+    E* o = (E*)a.o;
+#pragma unroll
+    for (int e = lane; e < C * CPR; e += 64) {
+        const int r = e / CPR, cg = e % CPR;
+        if (r < L)
+            *reinterpret_cast<u32x4*>(o + ((b * a.T + t0 + r) * a.H + h) * D + slice * BV + 16 * wave + cg * VEC) =
+                *reinterpret_cast<const u32x4*>(sOw + r * LDO + cg * VEC);
+    }
+}
+
+template <typename E, int D, int C, int BV>
+__global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
+{
+    typedef StateShape<E, D, C, BV> S;
+    constexpr int KTS = D / 16;
+    __shared__ __align__(16) E buf0[S::BUF];
+    __shared__ __align__(16) E buf1[S::NBUF == 2 ? S::BUF : 1];
+    __shared__ __align__(16) E sO[(NT / 64) * C * S::LDO];
 
     // Workgroup -> (sequence*head, column slice).  The NS slices of one
     // (b,h) read the same chunk records: give them the same blockIdx % 8 so
     // they land on the same XCD and share its L2.
-    const int64_t x = blockIdx.x;
-    const int64_t grp = x / (8 * S::NS);
-    const int within = (int)(x % (8 * S::NS));
+    const int64_t bx = blockIdx.x;
+    const int64_t grp = bx / (8 * S::NS);
+    const int within = (int)(bx % (8 * S::NS));
     const int slice = within / 8;
     const int64_t bh = grp * 8 + within % 8;
     if (bh >= a.nbh)
         return;
-    const int64_t b = bh / a.H, h = bh - b * a.H;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gq = lane >> 4, cl = lane & 15;
-    const int col = slice * BV + 16 * wave + cl;     // this lane's state / output column
+    const int64_t b = bh / a.H, h = bh - b * a.H, rec0 = bh * a.NC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int col = slice * BV + 16 * wave + cl;     // this lane's state column
+    E* sOw = sO + wave * C * S::LDO;
 
     f32x4 St[KTS];
     {
@@ -794,96 +1013,36 @@ __global__ __launch_bounds__(NT, 1) void chunk_state_kernel(StateArgs a)
                 St[kt][i] = s0 ? s0[(16 * kt + 4 * gq + i) * D + col] : 0.f;
     }
 
-    StateRegs<E, D, C, BV> R;
-    const int64_t rec0 = bh * a.NC;
-    state_load(a, rec0, slice, R, tid);
-    E* o = (E*)a.o;
-
-    for (int64_t n = 0; n < a.NC; ++n) {
-        __syncthreads();  // previous chunk done reading LDS
-#pragma unroll
-        for (int j = 0; j < S::NLD; ++j) {
-            const int e = (j * NT + tid) * VEC, t = e / D, c = e % D;
-            *reinterpret_cast<u32x4*>(sW + t * LDA + c) = R.w[j];
-            *reinterpret_cast<u32x4*>(sQ + t * LDA + c) = R.q[j];
-            *reinterpret_cast<u32x4*>(sKT + (e / C) * LDT + e % C) = R.kh[j];
+    StateCopies<E, D, C, BV> cp;
+    cp.init(wave, lane);
+    state_fetch<E, D, C, BV>(a, cp, rec0, slice, buf0, wave, lane);
+    if (S::NBUF == 2) {
+        for (int64_t n = 0; n < a.NC; n += 2) {
+            wait_copies();
+            __syncthreads();          // chunk n is in buf0; everyone is done with buf1
+            if (n + 1 < a.NC)
+                state_fetch<E, D, C, BV>(a, cp, rec0 + n + 1, slice, buf1, wave, lane);
+            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
+            if (n + 1 >= a.NC)
+                break;
+            wait_copies();
+            __syncthreads();          // chunk n + 1 is in buf1; everyone is done with buf0
+            if (n + 2 < a.NC)
+                state_fetch<E, D, C, BV>(a, cp, rec0 + n + 2, slice, buf0, wave, lane);
+            state_compute<E, D, C, BV>(a, buf1, sOw, St, b, h, slice, n + 1, lane, wave);
         }
-#pragma unroll
-        for (int j = 0; j < S::NLDP; ++j) {
-            const int e = (j * NT + tid) * VEC;
-            if (e < C * C)
-                *reinterpret_cast<u32x4*>(sP + (e / C) * LDT + e % C) = R.p[j];
+    } else {
+        for (int64_t n = 0; n < a.NC; ++n) {
+            wait_copies();
+            __syncthreads();          // chunk n is in buf0
+            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
+            __syncthreads();          // everyone is done with buf0
+            if (n + 1 < a.NC)
+                state_fetch<E, D, C, BV>(a, cp, rec0 + n + 1, slice, buf0, wave, lane);
         }
-#pragma unroll
-        for (int j = 0; j < S::NLDU; ++j) {
-            const int e = (j * NT + tid) * VEC;
-            if (e < C * BV)
-                *reinterpret_cast<u32x4*>(sU + (e / BV) * LDU + e % BV) = R.u[j];
-        }
-        if (tid < D / 4)
-            *reinterpret_cast<f32x4*>(sGam + tid * 4) = R.gam;
-        if (n + 1 < a.NC)
-            state_load(a, rec0 + n + 1, slice, R, tid);
-        __syncthreads();
-
-        // B operands from the chunk-start state.
-        typename MM::Frag SB[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            SB[ks] = MM::from_acc(&St[ks * MM::KT]);
-
-        // Delta = U~ - W S  (W is stored negated).
-        f32x4 dl[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dl[mt][i] = to_f32(sU[(16 * mt + 4 * gq + i) * LDU + 16 * wave + cl]);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                dl[mt] = MM::mma(MM::load(sW + 16 * mt * LDA + ks * MM::KB, LDA, lane), SB[ks], dl[mt]);
-        }
-        typename MM::Frag DB[NKC];
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-            DB[kc] = MM::from_acc(&dl[kc * MM::KT]);
-
-        // O = Q~ S + P Delta  (P is lower triangular: skip all-zero steps).
-        f32x4 ot[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
-            ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                ot[mt] = MM::mma(MM::load(sQ + 16 * mt * LDA + ks * MM::KB, LDA, lane), SB[ks], ot[mt]);
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-                if (kc * MM::KT <= mt)
-                    ot[mt] = MM::mma(MM::load(sP + 16 * mt * LDT + kc * MM::KB, LDT, lane), DB[kc], ot[mt]);
-        }
-
-        // S <- diag(gamma) S + K^T Delta.
-#pragma unroll
-        for (int kt = 0; kt < KTS; ++kt) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * gq);
-            St[kt] = St[kt] * gm;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-                St[kt] = MM::mma(MM::load(sKT + 16 * kt * LDT + kc * MM::KB, LDT, lane), DB[kc], St[kt]);
-        }
-
-        // Store this chunk's outputs (valid rows only).
-        const int64_t t0 = n * C;
-        const int L = (int)min((int64_t)C, a.T - t0);
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * gq + i;
-                if (r < L)
-                    o[((b * a.T + t0 + r) * a.H + h) * D + col] = from_f32<E>(ot[mt][i]);
-            }
     }
+
+    state_store_o<E, D, C, BV>(a, sOw, b, h, slice, a.NC - 1, lane, wave);
 
     if (a.S_out) {
         float* so = a.S_out + bh * D * D;
@@ -938,9 +1097,7 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     static const hipError_t attr1g = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&chunk_prep_kernel<false, E, D, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
-    static const hipError_t attr2 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_state_kernel<E, D, C, BV>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)SS::SMEM);
+    static const hipError_t attr2 = hipSuccess;
     if (attr1 != hipSuccess)
         return attr1;
     if (attr1g != hipSuccess)
@@ -965,7 +1122,7 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     sa.S0 = a.S0; sa.S_out = a.S_out; sa.o = a.o;
     sa.T = a.T; sa.H = a.H; sa.NC = pa.NC; sa.nbh = a.B * a.H;
     const int64_t grid2 = ceil_div(sa.nbh, 8) * 8 * SS::NS;
-    hipLaunchKernelGGL((chunk_state_kernel<E, D, C, BV>), dim3((unsigned)grid2), dim3(NT), SS::SMEM, stream, sa);
+    hipLaunchKernelGGL((chunk_state_kernel<E, D, C, BV>), dim3((unsigned)grid2), dim3(NT), 0, stream, sa);
     return hipGetLastError();
 }
 

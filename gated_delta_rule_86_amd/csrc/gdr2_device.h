@@ -103,6 +103,10 @@ template <> struct Mma<bf16> {
         f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
         return f;
     }
+    // Fragment from storage in MFMA k-order (see perm_chunk): one 16-byte read.
+    static __device__ __forceinline__ Frag load_perm(const bf16* p, int ld, int lane) {
+        return *reinterpret_cast<const bf16x8*>(p + (lane & 15) * ld + 8 * (lane >> 4));
+    }
     // Same, from fp32 storage (rounded to bf16).
     static __device__ __forceinline__ Frag load(const float* p, int ld, int lane) {
         const float* s = p + (lane & 15) * ld + 4 * (lane >> 4);
@@ -143,6 +147,9 @@ template <> struct Mma<float> {
 
     static __device__ __forceinline__ Frag load(const float* p, int ld, int lane) {
         return *reinterpret_cast<const f32x4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
+    }
+    static __device__ __forceinline__ Frag load_perm(const float* p, int ld, int lane) {
+        return load(p, ld, lane);
     }
     static __device__ __forceinline__ Frag load_scaled(const float* p, int ld, const float* f, int lane) {
         const int c = 4 * (lane >> 4);
