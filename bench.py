@@ -106,6 +106,29 @@ def bench_decode(torch, gdr2, lib, steps: int, warmup: int):
             "GBps": byts / (us * 1e-6) / 1e9, "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+COPY_BYTES = 1 << 30
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_train_4k.md")
+
+
+def plain_copy(torch, reps: int = 3):
+    """A plain device copy of COPY_BYTES: the achievable-bandwidth reference
+    of this run, and the known-size kernel the HBM counters are scaled by."""
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x, y
+    return {"bytes_moved": 2 * COPY_BYTES, "ms": round(ms, 4),
+            "GBps": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +137,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy bandwidth reference")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -177,8 +201,10 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_b = kernels[dom]
     achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    from gated_delta_rule_86_amd.rocprof_summary import read_traffic
+    measured = read_traffic(TRAFFIC_SUMMARY) or {}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured.get(dom), "kernel": dom,
                 "algorithmic_bytes_per_launch": dom_b}
 
     extra = {
@@ -195,11 +221,17 @@ def main():
     }
     if not args.no_decode:
         extra["decode"] = bench_decode(torch, gdr2, lib, args.decode_steps, 20)
+    if measured:
+        extra["hbm_traffic_bytes_per_launch"] = measured
 
+    del d, x, o, S_out, ws
+    torch.cuda.empty_cache()
+    if not args.no_copy:
+        extra["plain_copy"] = plain_copy(torch)
+        pc = extra["plain_copy"]["GBps"]
+        extra["step_frac_of_plain_copy_bw"] = round(min_b / (step_ms * 1e-3) / 1e9 / pc, 4)
     cpu = None
     if not args.no_cpu_baseline:
-        del d, x, o, S_out, ws
-        torch.cuda.empty_cache()
         cpu = cpu_baseline(inp, wl)
 
     line = {

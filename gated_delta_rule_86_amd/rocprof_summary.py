@@ -1,0 +1,148 @@
+"""Turn rocprofv3 outputs of the benchmark into the short text summaries kept
+under profiles/.
+
+    python -m gated_delta_rule_86_amd.rocprof_summary stats  <kernel_stats.csv> <out.md> --command "..."
+    python -m gated_delta_rule_86_amd.rocprof_summary traffic <fetch_dir> <write_dir> <out.md> --command "..."
+
+`stats` summarises a --kernel-trace --stats run (calls, average and total
+duration per kernel).  `traffic` takes two --pmc runs (FETCH_SIZE, then
+WRITE_SIZE; KiB per dispatch) of ``bench.py --calibrate-copy``, scales each
+counter by what it reads for the plain device copy of known size the
+benchmark runs, and reports HBM bytes per launch for each kernel.  The
+summary records a hash of the kernel sources it was measured on; bench.py
+reports the traffic only while the sources still hash the same.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+# Kernel-name fragments -> short names used in the summaries and bench.py.
+KERNELS = (("chunk_prep_kernel", "gdr2_chunk_prep"), ("chunk_state_kernel", "gdr2_chunk_state"),
+           ("decode_step_kernel", "gdr2_decode_step"), ("copy", "plain_copy"))
+COPY_BYTES_MARK = "calibration copy bytes:"
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources of the library (what the counters measure)."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str | None:
+    for frag, name in KERNELS:
+        if frag in kernel:
+            return name
+    return None
+
+
+def _find(path, pattern):
+    if os.path.isfile(path):
+        return path
+    hits = glob.glob(os.path.join(path, "**", pattern), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {path}")
+    return hits[0]
+
+
+def stats(args):
+    f = _find(args.csv, "*kernel_stats.csv")
+    rows = list(csv.DictReader(open(f)))
+    out = [f"# rocprofv3 kernel statistics: {args.title}", "",
+           f"Command (from the repository root on the GPU box):", "", f"    {args.command}", "",
+           f"Kernel sources hash: `{source_hash()}`", "",
+           "| kernel | calls | average (us) | total (us) |", "|---|---|---|---|"]
+    for r in rows:
+        name = short_name(r["Name"]) or r["Name"][:60]
+        out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['TotalDurationNs']) / 1e3:.1f} |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def _counter_per_kernel(path, counter):
+    f = _find(path, "*counter_collection.csv")
+    vals = {}
+    for r in csv.DictReader(open(f)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = short_name(r["Kernel_Name"])
+        if name:
+            vals.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def traffic(args):
+    copy_bytes = args.copy_bytes
+    fetch = _counter_per_kernel(args.fetch_dir, "FETCH_SIZE")
+    write = _counter_per_kernel(args.write_dir, "WRITE_SIZE")
+    if "plain_copy" not in fetch or "plain_copy" not in write:
+        raise SystemExit("the plain copy kernel is missing from the counter runs")
+    # a copy of N bytes reads N and writes N bytes
+    kf = copy_bytes / fetch["plain_copy"]
+    kw = copy_bytes / write["plain_copy"]
+    out = [f"# HBM traffic per launch (rocprofv3 --pmc): {args.title}", "",
+           "Commands (from the repository root on the GPU box), one counter per run:", "",
+           f"    {args.command_fetch}", f"    {args.command_write}", "",
+           f"Counters are KiB per dispatch.  Each is scaled by what it reads for the "
+           f"plain device copy of {copy_bytes} bytes that the benchmark runs "
+           f"(bytes per counter unit: FETCH {kf:.1f}, WRITE {kw:.1f}).", "",
+           f"Kernel sources hash: `{source_hash()}`", "",
+           "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read bytes | written bytes | total bytes |",
+           "|---|---|---|---|---|---|"]
+    machine = []
+    for name in sorted(set(fetch) & set(write)):
+        rb, wb = fetch[name] * kf, write[name] * kw
+        out.append(f"| {name} | {fetch[name]:.0f} | {write[name]:.0f} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} |")
+        machine.append(f"traffic {name} {rb + wb:.0f}")
+    out += ["", "Machine-readable (bytes per launch):", "", "```"] + machine + \
+           [f"source_hash {source_hash()}", "```"]
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def read_traffic(path: str) -> dict | None:
+    """Bytes per launch by kernel from a traffic summary, if it was measured on
+    the current sources; else None."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^source_hash (\w+)$", text, re.M)
+    if not m or m.group(1) != source_hash():
+        return None
+    return {k: float(v) for k, v in re.findall(r"^traffic (\S+) ([0-9.eE+]+)$", text, re.M)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="benchmark")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("out")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--title", default="benchmark")
+    a = ap.parse_args()
+    stats(a) if a.cmd == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
