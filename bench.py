@@ -48,7 +48,9 @@ def staged_bytes(B, T, H, D, C, esz, bw, ww, gw, s0: bool, s_out: bool):
     rows = B * T * H
     nrec = B * H * -(-T // C)
     inputs = rows * ((2 * D + D + bw + ww) * esz + gw * 4)      # q,k,v,b,w (dtype) + g fp32
-    factors = nrec * (4 * C * D * esz + C * C * esz + D * 4)  # -W, U~, K^, Q~, P, gamma
+    kt = 2 if esz == 2 else 1                                  # 16-token blocks per P fragment
+    p_frags = sum(t // kt + 1 for t in range(C // 16))         # nonzero 1 KB fragments of P
+    factors = nrec * (4 * C * D * esz + p_frags * 1024 + D * 4)  # -W, U~, K^T, Q~, P, gamma
     state = B * H * D * D * 4
     prep = inputs + factors
     st = factors + rows * D * esz + (state if s0 else 0) + (state if s_out else 0)

@@ -13,27 +13,21 @@
 //   S_next = diag(2^G_L) S + K^T Delta,   K^_s = k_s*2^(G_L-G_s)
 // (G is kept in log2 units, so every decay factor is one v_exp_f32.)
 //
-// Two kernels:
-//   chunk_prep  (every chunk of every sequence in parallel): the cumulative
-//               decay, the gated Gram M and scores P (MFMA), X by blocked
-//               substitution, W and U~ (MFMA).  It writes -W, U~, K^, Q~ =
-//               q*2^G, P and gamma = 2^G_L per chunk to the workspace.
+// Two kernels joined by a workspace:
+//   chunk_prep  (every chunk of every sequence in parallel) writes -W, U~,
+//               K^T, Q~ = q*2^G, P and gamma = 2^G_L per chunk;
 //   chunk_state (one workgroup per (sequence, head, 64 value columns); the
 //               value columns of S evolve independently, so they split
-//               exactly): walks the chunks in order with the fp32 state in
-//               MFMA accumulators; Delta, O and the state update are MFMAs
-//               whose B operands are the accumulators themselves.
+//               exactly) walks the chunks in order with the fp32 state in
+//               MFMA accumulators.
 //
-// Decay absorption without overflow.  Factors are taken relative to the
-// cumulative decay at 16-token block boundaries Gb[J] = G at the last token
-// of block J (Gb[-1] = 0):
-//   alpha_t = 2^(G_t - Gb[blk(t)-1]) <= 1,   beta_s = 2^(Gb[blk(s)] - G_s) <= 1
-//   tile (I,J), J < I:  2^(G_t-G_s) = alpha_t * 2^(Gb[I-1]-Gb[J]) * beta_s,
-//                       every factor <= 1 (underflow is the true limit);
-//   tile (I,I):         the middle factor is 2^(span of block I) >= 1.
-// The diagonal tiles are exact while the span of every 16-token block stays
-// below kSpanMax (log2 units); a chunk that exceeds it recomputes its
-// diagonal tiles pair by pair from the raw inputs (slow, exact).
+// The workspace holds every factor in MFMA operand order.  A "fragment" is
+// one A operand tile of the state kernel -- 16 rows x KB k-values (KB = 32
+// for bf16, 16 for fp32), 16 bytes per lane, 1 KB -- stored lane-major; U~ is
+// stored as accumulator tiles (4 values per lane).  The prep kernel produces
+// each fragment in registers and writes it with one coalesced 16-byte store
+// per lane; the state kernel copies a chunk's fragments into LDS linearly and
+// reads each one with a single conflict-free 16-byte LDS read per lane.
 #include "gdr2_device.h"
 #include "gdr2_internal.h"
 
@@ -42,31 +36,97 @@
 namespace gdr2 {
 namespace {
 
-constexpr int NT = 256;            // threads per workgroup (4 waves)
-constexpr float kSpanMax = 80.f;   // log2 units per 16-token block
+constexpr int NT = 256;            // threads of the state kernel (4 waves)
+constexpr float kSpanMax = 80.f;   // largest decay exponent (log2) a factor may carry
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
-constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------------------
-// Workspace: per chunk record (sequence, head, chunk), element type E:
-//   Wn [C][D] = -W,  Ut [C][D] = U~,  Kh [D][C] = K^ transposed,  Qt [C][D] = Q~,
-//   P [C][C],  gam [D] fp32.   Records are ordered (b*H + h)*NC + n.
-//   Wn, Qt, Kh and P (the A operands of the state kernel) store their
-//   contraction dimension in MFMA k-order (perm_chunk); U~ is plain.
+// 16x16x16 products in the accumulator-compatible k order: lane l holds
+// k = 4*(l/16) .. 4*(l/16)+3 of a 16-deep contraction, for A (row l%16) and
+// B (column l%16) alike -- an accumulator tile is directly a B operand.
+// bf16: v_mfma_f32_16x16x16_bf16; fp32: four v_mfma_f32_16x16x4f32.
 // ---------------------------------------------------------------------------
+template <typename E> struct Mma16;
+template <> struct Mma16<bf16> {
+    typedef bf16x4 Frag;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ Frag pack(f32x4 x) {
+        Frag f;
+        f[0] = (bf16)x[0]; f[1] = (bf16)x[1]; f[2] = (bf16)x[2]; f[3] = (bf16)x[3];
+        return f;
+    }
+    static __device__ __forceinline__ Frag load(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                         __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    }
+};
+template <> struct Mma16<float> {
+    typedef f32x4 Frag;
+    static __device__ __forceinline__ Frag pack(f32x4 x) { return x; }
+    static __device__ __forceinline__ Frag load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) { return Mma<float>::mma(a, b, c); }
+};
+
+// A full-width fragment (KT 16-blocks along k) from KT accumulator tiles.
+template <typename E> __device__ __forceinline__ typename Mma<E>::Frag frag_of(const f32x4* t);
+template <> __device__ __forceinline__ Mma<bf16>::Frag frag_of<bf16>(const f32x4* t) { return Mma<bf16>::pack(t[0], t[1]); }
+template <> __device__ __forceinline__ Mma<float>::Frag frag_of<float>(const f32x4* t) { return t[0]; }
+
+// ---------------------------------------------------------------------------
+// Fragment geometry of one chunk record.
+//   -W  [T][m]: rows t = 16T + l%16, k = key channels (m-th KB block)
+//   Q~  [T][m]: same
+//   K^T [c][m]: rows = key channels 16c + l%16, k = tokens (m-th KB block)
+//   P   [T][m] for m*KT <= T only (the rest of P is zero above the diagonal)
+//   U~  [n][T]: accumulator tiles, rows = tokens 16T.., columns 16n..
+// Within a KB block, lane group g = l/16 holds k = 4g..4g+3 (and, for bf16,
+// 16+4g..16+4g+3 in its upper four slots).
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C>
+struct Frags {
+    static constexpr int KB = Mma<E>::KB, KT = KB / 16;
+    static constexpr int NB = C / 16;
+    static constexpr int NKS = D / KB;               // k-steps over key channels
+    static constexpr int NKC = C / KB;               // k-steps over tokens
+    static constexpr int FRAG = 1024;
+    static constexpr int TILE_U = 64 * 4 * (int)sizeof(E);
+    static constexpr int p_count(int T) { return T / KT + 1; }
+    static constexpr int p_offset(int T) { return T == 0 ? 0 : p_offset(T - 1) + p_count(T - 1); }
+    static constexpr int NP = p_offset(NB);
+    static constexpr size_t W_BYTES = (size_t)NB * NKS * FRAG;       // = C*D*sizeof(E)
+    static constexpr size_t K_BYTES = (size_t)(D / 16) * NKC * FRAG;  // = C*D*sizeof(E)
+    static constexpr size_t P_BYTES = (size_t)NP * FRAG;
+    static constexpr size_t U_BYTES = (size_t)NB * (D / 16) * TILE_U; // = C*D*sizeof(E)
+    static_assert(W_BYTES == (size_t)C * D * sizeof(E) && K_BYTES == W_BYTES && U_BYTES == W_BYTES, "sizes");
+};
+
+// Workspace: per record (sequence, head, chunk) in the order (b*H + h)*NC + n,
+// arrays -W, U~, K^T, Q~ (C*D elements each), P (NP fragments), gamma (D fp32).
 struct Layout {
     int64_t nrec;
     size_t wn, ut, kh, qt, p, gam, total;
 };
+
+int p_frags(int C, int es)
+{
+    const int KT = es == 2 ? 2 : 1;
+    int n = 0;
+    for (int T = 0; T < C / 16; ++T)
+        n += T / KT + 1;
+    return n;
+}
 
 Layout staged_layout(int64_t B, int64_t H, int64_t T, int D, int C, int esz)
 {
     Layout L;
     L.nrec = B * H * ceil_div(T, C);
     const size_t mat = al256((size_t)L.nrec * C * D * esz);
-    const size_t pm = al256((size_t)L.nrec * C * C * esz);
+    const size_t pm = al256((size_t)L.nrec * p_frags(C, esz) * 1024);
     const size_t gm = al256((size_t)L.nrec * D * 4);
     L.wn = 0;
     L.ut = mat;
@@ -97,117 +157,33 @@ struct StateArgs {
 };
 
 // ---------------------------------------------------------------------------
-// chunk_prep: 512 threads (8 waves), one workgroup per CU, looping over chunk
-// records with the next chunk's inputs prefetched into registers while the
-// current one computes.
-//
-// Decay references.  A chunk is split into halves of 32 tokens; Gh(t) is the
-// cumulative log2-decay at the end of the previous half (0 for the first).
-//   E~_t = e_t 2^G_t,  Q~_t = q_t 2^G_t            (chunk reference, <= |e|,|q|)
-//   Kr_s = k_s 2^(Gh(s) - G_s)                      (own half's reference)
-//   E^_t = e_t 2^(G_t - Gh(t)),  Q^_t likewise       (second half only)
-// A 16x16 tile (I, J) of M (or P) with both blocks in the same half is
-// E^_I Kr_J^T (E~ in the first half), and with I in the second half and J in
-// the first it is E~_I Kr_J^T: each product equals the wanted
-// e_t k_s 2^(G_t - G_s) with no factor above 2^(half span).  The half span is
-// guarded by kSpanMax; a chunk beyond it takes an exact pair-by-pair path for
-// its same-half tiles.
-//
-// WY solve.  [W | U~] = (I + M)^-1 [E~ | u] by blocked forward substitution
-// over the four 16-row blocks:  R_I = RHS_I - sum_{J<I} M_IJ [W|U~]_J,
-// [W|U~]_I = X_II R_I, with X_II = (I + M_II)^-1 from a 16-lane substitution.
-// Each wave owns 32 columns of the right-hand side and keeps its solved blocks
-// in MFMA accumulators, which are the B operands of the next blocks.
+// Small element helpers.
 // ---------------------------------------------------------------------------
-constexpr int NTP = 512;           // threads of the prep kernel
-constexpr int NWP = NTP / 64;      // its waves
-
-template <typename E, int D, int C>
-struct PrepShape {
-    static constexpr int NB = C / 16;                       // 16-token blocks
-    static constexpr int NH = C / 32;                       // 32-token halves
-    static constexpr int VEC = 16 / (int)sizeof(E);         // elements per 16-byte access
-    static constexpr int NLD = (C * D + NTP * VEC - 1) / (NTP * VEC);  // [C][D] loads per thread
-    static constexpr int NLDG = (C * D + NTP * 4 - 1) / (NTP * 4);     // fp32 g loads per thread
-    static constexpr int LDA = D + 16 / (int)sizeof(E);     // [rows][D] E arrays in LDS
-    static constexpr int LDC = C + 16 / (int)sizeof(E);     // [C][C] E arrays (P, -M)
-    static constexpr int LDX = 20;                          // fp32 16x16 blocks
-    static constexpr int PARTS = NTP / D;                   // prefix-sum parts per channel
-    static constexpr size_t SZ_G = (size_t)C * D * 4;
-    static constexpr size_t SZ_A = (size_t)C * LDA * sizeof(E);
-    static constexpr size_t SZ_AH = (size_t)(C - 32) * LDA * sizeof(E);
-    static constexpr size_t SZ_CC = (size_t)C * LDC * sizeof(E);
-    static constexpr size_t SZ_BLK = (size_t)NB * 16 * LDX * 4;
-    static constexpr size_t OFF_G = 0;                             // sG
-    static constexpr size_t OFF_E = OFF_G + al256(SZ_G);           // sE  (E~, then -W)
-    static constexpr size_t OFF_Q = OFF_E + al256(SZ_A);           // sQ  (Q~)
-    static constexpr size_t OFF_KR = OFF_Q + al256(SZ_A);          // sKr
-    static constexpr size_t OFF_U = OFF_KR + al256(SZ_A);          // sU  (u, then U~)
-    static constexpr size_t OFF_EH = OFF_U + al256(SZ_A);          // sEh (second half)
-    static constexpr size_t OFF_QH = OFF_EH + al256(SZ_AH);        // sQh (second half)
-    static constexpr size_t OFF_MB = OFF_QH + al256(SZ_AH);        // sMb (-M below the diagonal blocks)
-    static constexpr size_t OFF_P = OFF_MB + al256(SZ_CC);         // sP  (scores)
-    static constexpr size_t OFF_MD = OFF_P + al256(SZ_CC);         // sMd (-M diagonal blocks, fp32)
-    static constexpr size_t OFF_XD = OFF_MD + al256(SZ_BLK);       // sXd (X_II, fp32)
-    static constexpr size_t OFF_T = OFF_XD + al256(SZ_BLK);        // tables [NH][D] + partials
-    static constexpr size_t SZ_T = ((size_t)NH * D + (size_t)PARTS * D) * 4;
-    static constexpr size_t OFF_FLAG = OFF_T + al256(SZ_T);
-    static constexpr size_t SMEM = OFF_FLAG + 256;
-    static_assert(SMEM <= 160 * 1024, "LDS budget");
-    static_assert(C == 32 || C == 64, "chunk");
-    static_assert(D % VEC == 0 && NTP % D == 0 && C % PARTS == 0, "shape");
-    static_assert((2 * D) % (NWP * 16) == 0, "right-hand-side columns per wave");
-};
-
-// Raw inputs of one chunk as loaded (bit patterns; width-1 gates keep their
-// scalar in element 0 and are broadcast when used).
-template <typename E, int D, int C>
-struct PrepRegs {
-    typedef PrepShape<E, D, C> S;
-    u32x4 k[S::NLD], q[S::NLD], b[S::NLD], v[S::NLD], w[S::NLD];
-    f32x4 g[S::NLDG];
-};
-
 template <typename E>
 __device__ __forceinline__ void unpack(const u32x4& r, float* out);
 template <>
 __device__ __forceinline__ void unpack<bf16>(const u32x4& r, float* out)
 {
-    const bf16x8 v = __builtin_bit_cast(bf16x8, r);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        out[i] = (float)v[i];
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(r[i] << 16);
+        out[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
 }
 template <>
 __device__ __forceinline__ void unpack<float>(const u32x4& r, float* out)
 {
-    out[0] = __uint_as_float(r[0]);
-    out[1] = __uint_as_float(r[1]);
-    out[2] = __uint_as_float(r[2]);
-    out[3] = __uint_as_float(r[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        out[i] = __uint_as_float(r[i]);
 }
-
-// 16 bytes of E as a vector.
-template <typename E> struct VecOf;
-template <> struct VecOf<bf16> { typedef bf16x8 T; };
-template <> struct VecOf<float> { typedef f32x4 T; };
 
 // The scalar held in element 0 of a width-1 gate's raw bits.
-template <typename E>
-__device__ __forceinline__ float scalar0(const u32x4& r);
-template <>
-__device__ __forceinline__ float scalar0<bf16>(const u32x4& r)
-{
-    return __uint_as_float(r[0] << 16);
-}
-template <>
-__device__ __forceinline__ float scalar0<float>(const u32x4& r)
-{
-    return __uint_as_float(r[0]);
-}
+template <typename E> __device__ __forceinline__ float scalar0(const u32x4& r);
+template <> __device__ __forceinline__ float scalar0<bf16>(const u32x4& r) { return __uint_as_float(r[0] << 16); }
+template <> __device__ __forceinline__ float scalar0<float>(const u32x4& r) { return __uint_as_float(r[0]); }
 
-template <typename E>
-__device__ __forceinline__ u32x4 pack_vec(const float* x);
+template <typename E> __device__ __forceinline__ u32x4 pack_vec(const float* x);
 template <>
 __device__ __forceinline__ u32x4 pack_vec<bf16>(const float* x)
 {
@@ -220,503 +196,872 @@ __device__ __forceinline__ u32x4 pack_vec<bf16>(const float* x)
 template <>
 __device__ __forceinline__ u32x4 pack_vec<float>(const float* x)
 {
-    return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                 __float_as_uint(x[3])};
+    return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ void stg16(void* p, u32x4 v)
-{
-    *reinterpret_cast<u32x4*>(p) = v;
-}
-__device__ __forceinline__ u32x4 lds16(const void* p)
-{
-    return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ void sts16(void* p, u32x4 v)
-{
-    *reinterpret_cast<u32x4*>(p) = v;
-}
-
-// MFMA k-order of the state kernel's A operands (bf16): within every block of
-// 32 elements along k, physical 16-byte chunk g holds logical elements
-// 4g..4g+3 and 16+4g..16+4g+3 -- exactly the k values lane group g of a
-// 16x16x32 MFMA takes from accumulator-layout B operands -- so a fragment is
-// one 16-byte LDS read.  fp32 operands are already in that order (identity).
-// perm_chunk: the 16 bytes of physical chunk pc, gathered from a row held in
-// logical order.
-template <typename E>
-__device__ __forceinline__ u32x4 perm_chunk(const E* row, int pc);
-template <>
-__device__ __forceinline__ u32x4 perm_chunk<bf16>(const bf16* row, int pc)
-{
-    const bf16* p = row + 32 * (pc >> 2) + 4 * (pc & 3);
-    const unsigned int* lo = reinterpret_cast<const unsigned int*>(p);
-    const unsigned int* hi = reinterpret_cast<const unsigned int*>(p + 16);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-template <>
-__device__ __forceinline__ u32x4 perm_chunk<float>(const float* row, int pc)
-{
-    return *reinterpret_cast<const u32x4*>(row + 4 * pc);
-}
-// Logical index of element u of physical chunk pc (the same order).
-template <typename E>
-__device__ __forceinline__ int perm_index(int pc, int u)
-{
-    if (sizeof(E) == 4)
-        return 4 * pc + u;
-    return 32 * (pc >> 2) + 4 * (pc & 3) + (u < 4 ? u : 12 + u);
-}
+__device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void sts16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Bits of one element, for width-1 gates.
-template <typename E>
-__device__ __forceinline__ unsigned int ld_bits(const E* p);
-template <>
-__device__ __forceinline__ unsigned int ld_bits<bf16>(const bf16* p)
+template <typename E> __device__ __forceinline__ unsigned int ld_bits(const E* p);
+template <> __device__ __forceinline__ unsigned int ld_bits<bf16>(const bf16* p)
 {
     return *reinterpret_cast<const unsigned short*>(p);
 }
-template <>
-__device__ __forceinline__ unsigned int ld_bits<float>(const float* p)
+template <> __device__ __forceinline__ unsigned int ld_bits<float>(const float* p) { return __float_as_uint(*p); }
+
+// Position of logical k index `col` inside its fragment row (see Frags).
+template <typename E> __device__ __forceinline__ int kpos(int col);
+template <> __device__ __forceinline__ int kpos<bf16>(int col)
 {
-    return __float_as_uint(*p);
+    const int c = col & 31;
+    return (col & ~31) + 8 * ((c & 15) >> 2) + (c & 3) + 4 * (c >> 4);
+}
+template <> __device__ __forceinline__ int kpos<float>(int col) { return col; }
+
+// s_waitcnt lgkmcnt(0) with a compiler barrier: LDS writes of this wave are
+// complete before any later LDS read of it (lanes exchange data this way).
+__device__ __forceinline__ void lds_fence_wave()
+{
+    __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Chunk record -> position.  Token row r of the chunk is element offset
-// ((b*T + t0 + r)*H + h) of the [B,T,H,.] tensors.
+// Workgroup barrier that orders LDS data only: this wave's LDS operations
+// have completed, then s_barrier.  (__syncthreads() also waits for every
+// outstanding global access, including loads still being prefetched.)
+__device__ __forceinline__ void lds_barrier()
+{
+    __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed.
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Inclusive-scan step: the value of the lane `d` below within the 16-lane row.
+template <int d>
+__device__ __forceinline__ float dpp_shr(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + d, 0xF, 0xF, true));
+}
+
+// Work item -> chunk.  Items run in (sequence, chunk, head) order, so the
+// workgroups in flight together read whole token rows: the H heads of a
+// token are one contiguous run of H*D elements of the [B,T,H,.] inputs.
+// Token row r of the chunk is element offset ((b*T + t0 + r)*H + h); the
+// chunk's record in the workspace is (b*H + h)*NC + n.
 struct ChunkPos {
+    int64_t rec;      // workspace record
     int64_t row0;     // (b*T + t0)*H + h
     int L;            // valid tokens (>= 1)
 };
 
-__device__ __forceinline__ ChunkPos chunk_pos(int64_t rec, int64_t NC, int64_t T, int64_t H, int C)
+// Walks the items blockIdx.x, blockIdx.x + gridDim.x, ... as (b, n, h) with
+// carries, so the loop divides only once.
+struct ItemWalk {
+    int64_t b, n, h;          // current item
+    int64_t db, dn, dh;       // one step of gridDim.x items
+    __device__ __forceinline__ void init(int64_t i, int64_t step, int64_t NC, int64_t H)
+    {
+        const int64_t bn = i / H, sn = step / H;
+        h = i - bn * H;
+        n = bn % NC;
+        b = bn / NC;
+        dh = step - sn * H;
+        dn = sn % NC;
+        db = sn / NC;
+    }
+    __device__ __forceinline__ void advance(int64_t NC, int64_t H)
+    {
+        h += dh;
+        const int64_t ch = h >= H;
+        h -= ch * H;
+        n += dn + ch;
+        const int64_t cn = n >= NC;
+        n -= cn * NC;
+        b += db + cn;
+    }
+    __device__ __forceinline__ ChunkPos pos(int64_t NC, int64_t T, int64_t H, int C) const
+    {
+        const int64_t t0 = n * C;
+        ChunkPos p;
+        p.rec = (b * H + h) * NC + n;
+        p.row0 = (b * T + t0) * H + h;
+        p.L = (int)min((int64_t)C, T - t0);
+        return p;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// chunk_prep: 512 threads (8 waves), one workgroup per CU, looping over chunk
+// records; the next chunk's inputs are loaded into registers while the
+// current one computes.  Per chunk:
+//
+//  A  Cumulative log-decay, in registers.  Each lane owns VEC key channels of
+//     TPL consecutive tokens (its 16-byte loads); the prefix sum runs within
+//     the lane, across the LPC lanes sharing the channels (DPP row shifts) and
+//     across waves through a small table of wave totals.
+//  B  Decay-referenced operands, written to LDS rows (16-byte chunks XOR-
+//     swizzled by row so fragment reads are conflict-free).  A chunk is split
+//     into halves of 32 tokens; Gh is the cumulative decay at the end of the
+//     first half (0 for tokens of the first half):
+//        E^ = e 2^(G-Gh),  Q^ = q 2^(G-Gh),  Kr = k 2^(Gh-G),  u = w v,
+//        second half also E~ = e 2^G, Q~ = q 2^G (chunk reference).
+//     A tile of M (or P) with both 16-token blocks in one half is E^ Kr^T,
+//     one across the halves is E~ Kr^T; both equal e_t k_s 2^(G_t-G_s) and no
+//     factor exceeds 2^(half span).  A chunk whose exponents exceed kSpanMax
+//     takes an exact pair-by-pair path for M, P and K^ instead.
+//  C1 M tiles (transposed products, so each lane holds four consecutive
+//     columns of one row) into LDS; P fragments straight to the workspace.
+//  C2 One wave inverts I + M: the 16x16 diagonal blocks by lane-per-column
+//     substitution (fp32), then X_IJ = -X_II sum_K M_IK X_KJ block by block
+//     on MFMA with the earlier blocks kept as accumulators.  Meanwhile the
+//     other waves form the K^T and Q~ fragments (transposes are MFMAs with an
+//     identity operand, exact in bf16).
+//  D  W^T = E~^T X^T gives the -W fragments in registers; U~ = X u gives the
+//     U~ accumulator tiles.  Both go straight to the workspace.
+// ---------------------------------------------------------------------------
+constexpr int NTP = 512;           // threads of the prep kernel
+constexpr int NWP = NTP / 64;      // its waves
+
+template <typename E, int D, int C>
+struct PrepShape {
+    typedef Frags<E, D, C> F;
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int VEC = 16 / ES;                      // elements per 16-byte access
+    static constexpr int NB = C / 16, NH = C / 32;
+    static constexpr int NCG = D / VEC;                      // 16-byte chunks per row
+    static constexpr int NWB0 = C * D / VEC / 64;
+    static constexpr int NWB = NWB0 < NWP ? NWB0 : NWP;      // waves of phases A and B
+    static constexpr int TW = C / NWB;                       // tokens per wave
+    static constexpr int LPC = 64 / NCG;                     // lanes sharing a channel group
+    static constexpr int TPL = TW / LPC;                     // tokens per lane
+    static constexpr int LDM = C + 4;                        // rows of M (elements)
+    static constexpr int LDXP = C + VEC;                     // rows of X (elements)
+    static constexpr int LDX = 20;                           // rows of fp32 16x16 blocks
+    static constexpr size_t ROWB = (size_t)D * ES;
+    static constexpr size_t OFF_EH = 0;                              // E^ [C][D]
+    static constexpr size_t OFF_QH = OFF_EH + C * ROWB;              // Q^ [C][D]
+    static constexpr size_t OFF_KR = OFF_QH + C * ROWB;              // Kr [C][D] (exact path: K^)
+    static constexpr size_t OFF_U = OFF_KR + C * ROWB;               // u  [C][D]
+    static constexpr size_t OFF_E2 = OFF_U + C * ROWB;               // E~ [C-32][D] second half
+    static constexpr size_t OFF_Q2 = OFF_E2 + (NH - 1) * 32 * ROWB;  // Q~ [C-32][D] second half
+    static constexpr size_t OFF_M = al256(OFF_Q2 + (NH - 1) * 32 * ROWB);       // M [C][LDM], blocks below the diagonal
+    static constexpr size_t OFF_MD = al256(OFF_M + (size_t)C * LDM * ES);       // M_II fp32 [NB][16][LDX]
+    static constexpr size_t OFF_XC = OFF_MD + (size_t)NB * 16 * LDX * 4;        // X_II fp32, column j as row j
+    static constexpr size_t OFF_X = al256(OFF_XC + (size_t)NB * 16 * LDX * 4);  // X [C][LDXP] in fragment k order
+    static constexpr size_t OFF_TOT = al256(OFF_X + (size_t)C * LDXP * ES);     // wave totals [NWB][D]
+    static constexpr size_t OFF_FK = OFF_TOT + (size_t)NWB * D * 4;             // 2^(G_L - Gh) [NH][D]
+    static constexpr size_t OFF_FLAG = OFF_FK + (size_t)NH * D * 4;
+    static constexpr size_t SMEM = OFF_FLAG + 16;                               // dynamic LDS
+    // raw g [C][D] (exact path: G) lives in its own static LDS object, so the
+    // compiler knows the asynchronous copies into it touch nothing else
+    static constexpr size_t SZ_G = (size_t)C * D * 4;
+    static_assert(SMEM + SZ_G <= 160 * 1024, "LDS budget");
+    static_assert(C == 32 || C == 64, "chunk");
+    static_assert(64 % NCG == 0 && NCG >= 8 && TPL >= 1 && TW == LPC * TPL, "lane mapping");
+    static_assert(NWB == NWP || NH == 1, "halves need every wave in phase B");
+};
+
+// Element offset of element `col` of row `r` in a swizzled [rows][D] array:
+// 16-byte chunk j of row r sits at chunk j ^ (r & 7).
+template <typename E, int D>
+__device__ __forceinline__ int swz(int r, int col)
 {
-    const int64_t bh = rec / NC, n = rec - bh * NC;
-    const int64_t b = bh / H, h = bh - b * H;
-    const int64_t t0 = n * C;
-    ChunkPos p;
-    p.row0 = (b * T + t0) * H + h;
-    p.L = (int)min((int64_t)C, T - t0);
-    return p;
+    constexpr int VEC = 16 / (int)sizeof(E);
+    return r * D + (((col / VEC) ^ (r & 7)) * VEC) + (col % VEC);
 }
 
-// Issue the loads of one chunk.  Rows past the valid length re-read the last
-// valid row (always in bounds) and are zeroed where they are used, so no load
-// sits under a per-lane branch.  FULL: every gate has full width, and the
-// load sequence is straight-line code.
-template <bool FULL, typename E, int D, int C>
-__device__ __forceinline__ void prep_load_gates(const PrepArgs& a, const ChunkPos& cp,
-                                                PrepRegs<E, D, C>& R, int tid)
+// Raw inputs of one lane's TPL tokens (bit patterns; width-1 gates keep their
+// scalar in element 0 and are broadcast when used).
+template <typename E, int D, int C>
+struct PrepRegs {
+    typedef PrepShape<E, D, C> S;
+    u32x4 k[S::TPL], q[S::TPL], v[S::TPL], b[S::TPL], w[S::TPL];
+};
+
+// Issue the token loads of one chunk for tokens t0.. of this lane, channels
+// c0...  Rows past the valid length re-read the last valid row (in bounds)
+// and are zeroed where they are used, so no load sits under a per-lane branch.
+// PART: 0 = k, 1 = q, 2 = v, 3 = b, 4 = w (issued at different points of
+// the previous chunk, so no wave stalls on a full memory queue).
+template <int PART, bool FULL, typename E, int D, int C>
+__device__ __forceinline__ void prep_load(const PrepArgs& a, const ChunkPos& cp, PrepRegs<E, D, C>& R,
+                                          int t0, int c0)
 {
     typedef PrepShape<E, D, C> S;
 #pragma unroll
-    for (int j = 0; j < S::NLDG; ++j) {
-        const int e = (j * NTP + tid) * 4, t = min(e / D, cp.L - 1), c = e % D;
-        const int64_t row = cp.row0 + (int64_t)t * a.H;
-        if (e < C * D) {
-            if (FULL || a.gw != 1)
-                R.g[j] = __builtin_bit_cast(f32x4, ldg16(a.g + row * D + c));
+    for (int j = 0; j < S::TPL; ++j) {
+        const int t = min(t0 + j, cp.L - 1);
+        const int64_t row = cp.row0 + (int64_t)t * a.H, off = row * D + c0;
+        if (PART == 0)
+            R.k[j] = ldg16((const E*)a.k + off);
+        if (PART == 1)
+            R.q[j] = ldg16((const E*)a.q + off);
+        if (PART == 2)
+            R.v[j] = ldg16((const E*)a.v + off);
+        if (PART == 3) {
+            if (FULL || a.bw != 1)
+                R.b[j] = ldg16((const E*)a.b + off);
             else
-                R.g[j][0] = a.g[row];
+                R.b[j][0] = ld_bits<E>((const E*)a.b + row);
+        }
+        if (PART == 4) {
+            if (FULL || a.ww != 1)
+                R.w[j] = ldg16((const E*)a.w + off);
+            else
+                R.w[j][0] = ld_bits<E>((const E*)a.w + row);
         }
     }
 }
 
+// Copy one chunk's log-decay rows straight into LDS (global_load_lds, no
+// registers): [C][D] fp32, or C floats for a width-1 gate.  Rows past the
+// valid length repeat the last valid row and are zeroed by the reader.
 template <bool FULL, typename E, int D, int C>
-__device__ __forceinline__ void prep_load_tokens(const PrepArgs& a, const ChunkPos& cp,
-                                                 PrepRegs<E, D, C>& R, int tid)
+__device__ __forceinline__ void prep_copy_g(const PrepArgs& a, const ChunkPos& cp, unsigned char* sGraw,
+                                            int wave, int lane)
+{
+    typedef __attribute__((address_space(3))) void lds_t;
+    if (FULL || a.gw != 1) {
+        constexpr int NI = C * D * 4 / 1024;
+        for (int j = wave; j < NI; j += NWP) {
+            const int byte = j * 1024 + lane * 16, t = min(byte / (D * 4), cp.L - 1), col = (byte % (D * 4)) / 4;
+            __builtin_amdgcn_global_load_lds(a.g + (cp.row0 + (int64_t)t * a.H) * D + col,
+                                             (lds_t*)(sGraw + j * 1024), 16, 0, 0);
+        }
+    } else if (wave == 0 && lane < C) {
+        __builtin_amdgcn_global_load_lds(a.g + cp.row0 + (int64_t)min(lane, cp.L - 1) * a.H, (lds_t*)sGraw, 4, 0, 0);
+    }
+}
+
+// Phase B for one lane: decay-referenced operands of its tokens into LDS.
+// VALID: every token of the chunk is valid (no zeroing needed).
+template <bool VALID, bool SECOND, typename E, int D, int C>
+__device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const float (*G)[16 / sizeof(E)],
+                                               const float* gh, int bw, int ww, int L, int t0, int c0,
+                                               unsigned char* smem)
 {
     typedef PrepShape<E, D, C> S;
-    const E* q = (const E*)a.q;
-    const E* k = (const E*)a.k;
-    const E* v = (const E*)a.v;
-    const E* b = (const E*)a.b;
-    const E* w = (const E*)a.w;
+    constexpr int VEC = S::VEC;
+    E* sEh = reinterpret_cast<E*>(smem + S::OFF_EH);
+    E* sQh = reinterpret_cast<E*>(smem + S::OFF_QH);
+    E* sKr = reinterpret_cast<E*>(smem + S::OFF_KR);
+    E* sU = reinterpret_cast<E*>(smem + S::OFF_U);
+    E* sE2 = reinterpret_cast<E*>(smem + S::OFF_E2);
+    E* sQ2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
+    float fh[VEC];
+    if (SECOND) {
 #pragma unroll
-    for (int j = 0; j < S::NLD; ++j) {
-        const int e = (j * NTP + tid) * S::VEC, t = min(e / D, cp.L - 1), c = e % D;
-        const int64_t row = cp.row0 + (int64_t)t * a.H, off = row * D + c;
-        if (e < C * D) {
-            R.k[j] = ldg16(k + off);
-            R.q[j] = ldg16(q + off);
-            R.v[j] = ldg16(v + off);
-            if (FULL) {
-                R.b[j] = ldg16(b + off);
-                R.w[j] = ldg16(w + off);
+        for (int x = 0; x < VEC; ++x)
+            fh[x] = fast_exp2(gh[x]);
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < S::TPL; ++j) {
+        // one output array at a time keeps few values live
+        const int t = t0 + j;
+        const bool valid = VALID || t < L;
+        const int o = swz<E, D>(t, c0);
+        const int o2 = SECOND ? swz<E, D>(t - 32, c0) : 0;
+        float eh[VEC], d[VEC], kk[VEC], tmp[VEC], tmp2[VEC];
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) {
+            const float g = G[j][x];
+            d[x] = SECOND ? g - gh[x] : g;
+            mx = fmaxf(mx, fmaxf(fabsf(d[x]), g));
+        }
+        unpack<E>(R.k[j], kk);
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) {
+            kk[x] = valid ? kk[x] : 0.f;
+            tmp[x] = kk[x] * fast_exp2(-d[x]);
+            eh[x] = fast_exp2(d[x]);
+        }
+        sts16(sKr + o, pack_vec<E>(tmp));
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            float bb[VEC];
+            unpack<E>(R.b[j], bb);
+            const float bs = scalar0<E>(R.b[j]);
+#pragma unroll
+            for (int x = 0; x < VEC; ++x) {
+                tmp[x] = (bw == 1 ? bs : bb[x]) * kk[x] * eh[x];
+                if (SECOND)
+                    tmp2[x] = tmp[x] * fh[x];
             }
         }
-    }
-    if (!FULL) {
+        sts16(sEh + o, pack_vec<E>(tmp));
+        if (SECOND)
+            sts16(sE2 + o2, pack_vec<E>(tmp2));
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            float qq[VEC];
+            unpack<E>(R.q[j], qq);
 #pragma unroll
-        for (int j = 0; j < S::NLD; ++j) {
-            const int e = (j * NTP + tid) * S::VEC, t = min(e / D, cp.L - 1), c = e % D;
-            const int64_t row = cp.row0 + (int64_t)t * a.H, off = row * D + c;
-            if (e < C * D) {
-                if (a.bw == 1)
-                    R.b[j][0] = ld_bits<E>(b + row);
-                else
-                    R.b[j] = ldg16(b + off);
-                if (a.ww == 1)
-                    R.w[j][0] = ld_bits<E>(w + row);
-                else
-                    R.w[j] = ldg16(w + off);
+            for (int x = 0; x < VEC; ++x) {
+                tmp[x] = (valid ? qq[x] : 0.f) * eh[x];
+                if (SECOND)
+                    tmp2[x] = tmp[x] * fh[x];
             }
         }
+        sts16(sQh + o, pack_vec<E>(tmp));
+        if (SECOND)
+            sts16(sQ2 + o2, pack_vec<E>(tmp2));
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            float vv[VEC], wv[VEC];
+            unpack<E>(R.v[j], vv);
+            unpack<E>(R.w[j], wv);
+            const float ws = scalar0<E>(R.w[j]);
+#pragma unroll
+            for (int x = 0; x < VEC; ++x)
+                tmp[x] = (valid ? (ww == 1 ? ws : wv[x]) : 0.f) * vv[x];
+        }
+        sts16(sU + o, pack_vec<E>(tmp));
+        __builtin_amdgcn_sched_barrier(0);
     }
+    return mx;
 }
 
-// A operand of X_II (16x16, fp32 in LDS) for one bf16 MFMA step of k = 32:
-// the second k-tile is zero.  fp32 MFMA steps are k = 16 and need no padding.
-template <typename E> struct XiiFrag;
-template <> struct XiiFrag<bf16> {
-    static __device__ __forceinline__ Mma<bf16>::Frag load(const float* p, int ld, int lane) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
-        return Mma<bf16>::pack(lo, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-};
-template <> struct XiiFrag<float> {
-    static __device__ __forceinline__ Mma<float>::Frag load(const float* p, int ld, int lane) {
-        return Mma<float>::load(p, ld, lane);
-    }
-};
+// 16 bytes of a swizzled row array as a full-width fragment: logical chunk
+// ch (k-values VEC*ch ..) of row r.
+template <typename E, int D>
+__device__ __forceinline__ typename Mma<E>::Frag row_frag(const E* base, int r, int ch)
+{
+    constexpr int VEC = 16 / (int)sizeof(E);
+    return *reinterpret_cast<const typename Mma<E>::Frag*>(base + r * D + ((ch ^ (r & 7)) * VEC));
+}
+
+// Four consecutive elements (col a multiple of 4) of a swizzled row array.
+template <typename E, int D>
+__device__ __forceinline__ typename Mma16<E>::Frag row4(const E* base, int r, int col)
+{
+    return Mma16<E>::load(base + swz<E, D>(r, col));
+}
 
 template <bool FULL, typename E, int D, int C>
 __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 {
     typedef PrepShape<E, D, C> S;
+    typedef Frags<E, D, C> F;
     typedef Mma<E> MM;
-    constexpr int NB = S::NB, NH = S::NH, VEC = S::VEC, LDA = S::LDA, LDC = S::LDC, LDX = S::LDX;
+    typedef Mma16<E> M16;
+    constexpr int NB = S::NB, NH = S::NH, VEC = S::VEC, LDM = S::LDM, LDXP = S::LDXP, LDX = S::LDX;
+    constexpr int KB = F::KB, KT = F::KT, NKS = F::NKS, NKC = F::NKC, NP = F::NP;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float* sG = reinterpret_cast<float*>(smem + S::OFF_G);     // [C][D] cumulative log2-decay
-    E* sE = reinterpret_cast<E*>(smem + S::OFF_E);             // [C][LDA] E~, then -W
-    E* sQ = reinterpret_cast<E*>(smem + S::OFF_Q);             // [C][LDA] Q~
-    E* sKr = reinterpret_cast<E*>(smem + S::OFF_KR);           // [C][LDA] Kr
-    E* sU = reinterpret_cast<E*>(smem + S::OFF_U);             // [C][LDA] u, then U~
-    E* sEh = reinterpret_cast<E*>(smem + S::OFF_EH);           // [C-32][LDA] E^ (rows 32..)
-    E* sQh = reinterpret_cast<E*>(smem + S::OFF_QH);           // [C-32][LDA] Q^ (rows 32..)
-    E* sMb = reinterpret_cast<E*>(smem + S::OFF_MB);           // [C][LDC] -M, blocks below the diagonal
-    E* sP = reinterpret_cast<E*>(smem + S::OFF_P);             // [C][LDC] P
-    float* sMd = reinterpret_cast<float*>(smem + S::OFF_MD);   // [NB][16][LDX] -M_II
-    float* sXd = reinterpret_cast<float*>(smem + S::OFF_XD);   // [NB][16][LDX] X_II
-    float* sFk = reinterpret_cast<float*>(smem + S::OFF_T);    // [NH][D] 2^(G_last - Gh)
-    float* sPart = sFk + NH * D;                               // [PARTS][D]
+    E* sEh = reinterpret_cast<E*>(smem + S::OFF_EH);
+    E* sQh = reinterpret_cast<E*>(smem + S::OFF_QH);
+    E* sKr = reinterpret_cast<E*>(smem + S::OFF_KR);
+    E* sU = reinterpret_cast<E*>(smem + S::OFF_U);
+    E* sE2 = reinterpret_cast<E*>(smem + S::OFF_E2);
+    E* sQ2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
+    E* sM = reinterpret_cast<E*>(smem + S::OFF_M);
+    float* sMd = reinterpret_cast<float*>(smem + S::OFF_MD);
+    float* sXc = reinterpret_cast<float*>(smem + S::OFF_XC);
+    E* sX = reinterpret_cast<E*>(smem + S::OFF_X);
+    float* sTot = reinterpret_cast<float*>(smem + S::OFF_TOT);
+    float* sFk = reinterpret_cast<float*>(smem + S::OFF_FK);
     int* sFlag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
+    __shared__ __align__(16) float sG[C * D];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gq = lane >> 4, cl = lane & 15;
-    PrepRegs<E, D, C> R;
-    int64_t rec = blockIdx.x;
-    if (rec >= a.nrec)
+    const int wave = threadIdx.x >> 6;
+    const bool ab = wave < S::NWB;              // waves of phases A and B
+    const bool second = NH == 2 && wave >= S::NWB / 2;
+    const int bw = FULL ? D : a.bw, ww = FULL ? D : a.ww, gw = FULL ? D : a.gw;
+
+    // X: the blocks above the diagonal that fragments cover stay zero
+    for (int e = threadIdx.x; e < C * LDXP; e += NTP)
+        sX[e] = from_f32<E>(0.f);
+
+    // Token inputs: two register sets, Rn receives chunk n+1 while chunk n
+    // computes from R, so every token load is issued a whole chunk ahead of
+    // its use.  The log-decay goes straight to LDS (sG), issued as soon as
+    // the previous chunk's rows have been read.
+    PrepRegs<E, D, C> R, Rn;
+    int64_t it = blockIdx.x;
+    if (it >= a.nrec)
         return;
+    ItemWalk walk;
+    walk.init(it, gridDim.x, a.NC, a.H);
     {
-        const ChunkPos cp = chunk_pos(rec, a.NC, a.T, a.H, C);
-        prep_load_gates<FULL>(a, cp, R, tid);
-        prep_load_tokens<FULL>(a, cp, R, tid);
+        const int lane = threadIdx.x & 63;
+        const ChunkPos cp0 = walk.pos(a.NC, a.T, a.H, C);
+        const int t0 = wave * S::TW + (lane % S::LPC) * S::TPL, c0 = (lane / S::LPC) * VEC;
+        prep_copy_g<FULL, E, D, C>(a, cp0, reinterpret_cast<unsigned char*>(sG), wave, lane);
+        if (ab) {
+            prep_load<0, FULL>(a, cp0, Rn, t0, c0);
+            prep_load<1, FULL>(a, cp0, Rn, t0, c0);
+            prep_load<2, FULL>(a, cp0, Rn, t0, c0);
+            prep_load<3, FULL>(a, cp0, Rn, t0, c0);
+            prep_load<4, FULL>(a, cp0, Rn, t0, c0);
+        }
     }
 
-    for (; rec < a.nrec; rec += gridDim.x) {
-        const ChunkPos cp = chunk_pos(rec, a.NC, a.T, a.H, C);
-        const int64_t next = rec + gridDim.x;
-        const ChunkPos np = chunk_pos(next < a.nrec ? next : rec, a.NC, a.T, a.H, C);
-        E* gWn = (E*)a.Wn + rec * C * D;
-        E* gUt = (E*)a.Ut + rec * C * D;
-        E* gKt = (E*)a.Kh + rec * C * D;
-        E* gQt = (E*)a.Qt + rec * C * D;
-        E* gP = (E*)a.P + rec * C * C;
-        float* gGam = a.gam + rec * D;
-        const int bw = FULL ? D : a.bw, ww = FULL ? D : a.ww, gw = FULL ? D : a.gw;
-
-        __syncthreads();  // the previous chunk is done with every LDS region
-        // Phase 1: log-decay into LDS in log2 units (padding rows: 0).
+    for (; it < a.nrec; it += gridDim.x) {
+        // Lane indices are rederived every chunk from an opaque copy of the
+        // thread id, so the compiler does not keep every lane-dependent
+        // address of the loop body live across iterations.
+        int tid = threadIdx.x;
+        __asm__ __volatile__("" : "+v"(tid));
+        const int lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+        const int cgp = lane / S::LPC, lpc = lane % S::LPC;
+        const int t0 = wave * S::TW + lpc * S::TPL, c0 = cgp * VEC;
+        wait_copies();
+        __syncthreads();   // B0: this chunk's g rows are in LDS, its tokens in Rn
+        R = Rn;
+        const ChunkPos cp = walk.pos(a.NC, a.T, a.H, C);
+        walk.advance(a.NC, a.H);
+        const int64_t next = it + gridDim.x;
+        const bool pre = ab && next < a.nrec;   // this lane prefetches tokens
+        const ChunkPos np = walk.pos(a.NC, a.T, a.H, C);
+        if (pre) {
+            prep_load<0, FULL>(a, np, Rn, t0, c0);
+            prep_load<1, FULL>(a, np, Rn, t0, c0);
+        }
+        // identity B operand of the transposes: element (k = 4gq + i, n = cl)
+        typename M16::Frag ident;
+        {
+            f32x4 id;
 #pragma unroll
-        for (int j = 0; j < S::NLDG; ++j) {
-            const int e = (j * NTP + tid) * 4;
-            if (e < C * D) {
-                f32x4 gv = R.g[j];
-                if (gw == 1)
-                    gv = f32x4{gv[0], gv[0], gv[0], gv[0]};
-                *reinterpret_cast<f32x4*>(sG + e) = (e / D < cp.L) ? gv * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 4; ++i)
+                id[i] = (4 * gq + i == cl) ? 1.f : 0.f;
+            ident = M16::pack(id);
+        }
+        const int64_t rec = cp.rec;
+        const bool full_chunk = cp.L == C;
+
+        // ---- A: cumulative log2-decay in registers -------------------------
+        float G[S::TPL][VEC];
+        float excl[VEC];
+        if (ab) {
+#pragma unroll
+            for (int j = 0; j < S::TPL; ++j) {
+                const bool valid = full_chunk || t0 + j < cp.L;
+                if (gw == 1) {
+                    const float gv = sG[t0 + j];
+#pragma unroll
+                    for (int x = 0; x < VEC; ++x)
+                        G[j][x] = valid ? gv * kLog2e : 0.f;
+                } else {
+#pragma unroll
+                    for (int x4 = 0; x4 < VEC / 4; ++x4) {
+                        const f32x4 gv = *reinterpret_cast<const f32x4*>(sG + (t0 + j) * D + c0 + 4 * x4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            G[j][4 * x4 + i] = valid ? gv[i] * kLog2e : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 1; j < S::TPL; ++j)
+#pragma unroll
+                for (int x = 0; x < VEC; ++x)
+                    G[j][x] += G[j - 1][x];
+            float inc[VEC];
+#pragma unroll
+            for (int x = 0; x < VEC; ++x)
+                inc[x] = G[S::TPL - 1][x];
+            if (S::LPC > 1) {
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) {
+                    const float y = dpp_shr<1>(inc[x]);
+                    inc[x] += lpc >= 1 ? y : 0.f;
+                }
+            }
+            if (S::LPC > 2) {
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) {
+                    const float y = dpp_shr<2>(inc[x]);
+                    inc[x] += lpc >= 2 ? y : 0.f;
+                }
+            }
+            if (S::LPC > 4) {
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) {
+                    const float y = dpp_shr<4>(inc[x]);
+                    inc[x] += lpc >= 4 ? y : 0.f;
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < VEC; ++x)
+                excl[x] = inc[x] - G[S::TPL - 1][x];
+            if (lpc == S::LPC - 1) {
+#pragma unroll
+                for (int x4 = 0; x4 < VEC / 4; ++x4)
+                    *reinterpret_cast<f32x4*>(sTot + wave * D + c0 + 4 * x4) =
+                        f32x4{inc[4 * x4], inc[4 * x4 + 1], inc[4 * x4 + 2], inc[4 * x4 + 3]};
             }
         }
         if (tid == 0)
             *sFlag = 0;
-        if (next < a.nrec)
-            prep_load_gates<FULL>(a, np, R, tid);
-        __syncthreads();
+        lds_barrier();   // B1: wave totals; the previous chunk is done with LDS
+        if (pre)
+            prep_load<2, FULL>(a, np, Rn, t0, c0);
 
-        // Phase 2: inclusive prefix sum over the chunk's tokens, per channel.
-        {
-            constexpr int RP = C / S::PARTS;
-            const int i = tid % D, p = tid / D;
-            float acc = 0.f;
+        // ---- B: decay-referenced operands ----------------------------------
+        float gh[VEC];
+        if (ab) {
+            float off[VEC];
 #pragma unroll
-            for (int r = 0; r < RP; ++r) {
-                acc += sG[(p * RP + r) * D + i];
-                sG[(p * RP + r) * D + i] = acc;
-            }
-            sPart[p * D + i] = acc;
-            __syncthreads();
-            float off = 0.f;
+            for (int x = 0; x < VEC; ++x)
+                off[x] = gh[x] = 0.f;
 #pragma unroll
-            for (int pp = 0; pp < S::PARTS - 1; ++pp)
-                off += pp < p ? sPart[pp * D + i] : 0.f;
+            for (int w2 = 0; w2 < S::NWB - 1; ++w2) {
+                if (w2 < wave) {
 #pragma unroll
-            for (int r = 0; r < RP; ++r)
-                sG[(p * RP + r) * D + i] += off;
-        }
-        __syncthreads();
-
-        // Phase 3: decay-referenced operands, as 16-byte LDS rows.
-        if (tid < NH * D) {
-            const int h = tid / D, i = tid % D;
-            const float gl = sG[(C - 1) * D + i];
-            const float gh = h ? sG[31 * D + i] : 0.f;
-            sFk[tid] = fast_exp2(gl - gh);
-            if (h == 0)
-                gGam[i] = fast_exp2(gl);
-        }
+                    for (int x4 = 0; x4 < VEC / 4; ++x4) {
+                        const f32x4 tv = *reinterpret_cast<const f32x4*>(sTot + w2 * D + c0 + 4 * x4);
 #pragma unroll
-        for (int j = 0; j < S::NLD; ++j) {
-            const int e = (j * NTP + tid) * VEC;
-            if (e >= C * D)
-                continue;
-            const int t = e / D, c = e % D, h = t >> 5;
-            const bool valid = t < cp.L;
-            float kk[VEC], qq[VEC], bb[VEC], vv[VEC], ww_[VEC];
-            unpack<E>(R.k[j], kk);
-            unpack<E>(R.q[j], qq);
-            unpack<E>(R.v[j], vv);
-            unpack<E>(R.b[j], bb);
-            unpack<E>(R.w[j], ww_);
-            const float bs = scalar0<E>(R.b[j]), ws = scalar0<E>(R.w[j]);
-            const float* Gt = sG + t * D + c;
-            const float* Gh = sG + 31 * D + c;
-            typename VecOf<E>::T ve, vq, vk, vu, veh, vqh;
-            bool steep = false;
+                        for (int i = 0; i < 4; ++i)
+                            off[4 * x4 + i] += tv[i];
+                    }
+                }
+                if (NH == 2 && w2 == S::NWB / 2 - 1) {
 #pragma unroll
-            for (int x = 0; x < VEC; ++x) {
-                const float kx = valid ? kk[x] : 0.f;
-                const float qx = valid ? qq[x] : 0.f;
-                const float bx = bw == 1 ? bs : bb[x];
-                const float wx = valid ? (ww == 1 ? ws : ww_[x]) : 0.f;
-                const float G = Gt[x];
-                const float gh = h ? Gh[x] : 0.f;
-                const float d2 = G - gh;                  // <= 0 for decays g <= 0
-                steep |= fabsf(d2) > kSpanMax || G > kSpanMax;
-                const float e2g = fast_exp2(G);
-                const float ekr = fast_exp2(-d2);
-                const float ex = bx * kx;
-                ve[x] = from_f32<E>(ex * e2g);
-                vq[x] = from_f32<E>(qx * e2g);
-                vk[x] = from_f32<E>(kx * ekr);
-                vu[x] = from_f32<E>(wx * vv[x]);
-                if (h) {
-                    const float eh = fast_exp2(d2);
-                    veh[x] = from_f32<E>(ex * eh);
-                    vqh[x] = from_f32<E>(qx * eh);
+                    for (int x = 0; x < VEC; ++x)
+                        gh[x] = off[x];
                 }
             }
-            if (steep)
+#pragma unroll
+            for (int j = 0; j < S::TPL; ++j)
+#pragma unroll
+                for (int x = 0; x < VEC; ++x)
+                    G[j][x] += off[x] + excl[x];
+            if (wave == S::NWB - 1 && lpc == S::LPC - 1) {
+                // the chunk's last token: gamma and the K^ factors per half
+                float f0[VEC], f1[VEC];
+#pragma unroll
+                for (int x = 0; x < VEC; ++x) {
+                    const float gl = G[S::TPL - 1][x];
+                    f0[x] = fast_exp2(gl);
+                    f1[x] = fast_exp2(gl - gh[x]);
+                }
+#pragma unroll
+                for (int x4 = 0; x4 < VEC / 4; ++x4) {
+                    const f32x4 v0 = f32x4{f0[4 * x4], f0[4 * x4 + 1], f0[4 * x4 + 2], f0[4 * x4 + 3]};
+                    *reinterpret_cast<f32x4*>(sFk + c0 + 4 * x4) = v0;
+                    *reinterpret_cast<f32x4*>(a.gam + rec * D + c0 + 4 * x4) = v0;
+                    if (NH == 2)
+                        *reinterpret_cast<f32x4*>(sFk + D + c0 + 4 * x4) =
+                            f32x4{f1[4 * x4], f1[4 * x4 + 1], f1[4 * x4 + 2], f1[4 * x4 + 3]};
+                }
+            }
+            float mx;
+            if (second)
+                mx = full_chunk ? prep_operands<true, true, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem)
+                                : prep_operands<false, true, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem);
+            else
+                mx = full_chunk ? prep_operands<true, false, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem)
+                                : prep_operands<false, false, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem);
+            if (mx > kSpanMax)
                 *sFlag = 1;
-            sts16(sE + t * LDA + c, __builtin_bit_cast(u32x4, ve));
-            sts16(sQ + t * LDA + c, __builtin_bit_cast(u32x4, vq));
-            sts16(sKr + t * LDA + c, __builtin_bit_cast(u32x4, vk));
-            sts16(sU + t * LDA + c, __builtin_bit_cast(u32x4, vu));
-            if (h) {
-                sts16(sEh + (t - 32) * LDA + c, __builtin_bit_cast(u32x4, veh));
-                sts16(sQh + (t - 32) * LDA + c, __builtin_bit_cast(u32x4, vqh));
-            }
+            if (pre)
+                prep_load<3, FULL>(a, np, Rn, t0, c0);
         }
-        if (next < a.nrec)
-            prep_load_tokens<FULL>(a, np, R, tid);
-        __syncthreads();
+        lds_barrier();   // B2: operands in LDS
 
-        // Phase 4: tiles of M (-> -M in sMb / sMd) and P (-> sP), MFMA; then
-        // K^ = Kr * 2^(G_last - Gh) leaves transposed ([D][C], tokens
-        // contiguous: the layout in which it is an A operand of the state
-        // update), VEC lanes per row of K^T.
+        E* gP = (E*)a.P + rec * (F::P_BYTES / sizeof(E));
+        if (pre)
+            prep_load<4, FULL>(a, np, Rn, t0, c0);
         const bool guard = *sFlag != 0;
-        {
-            constexpr int NTILE = NB * (NB + 1) / 2;
-            const int kind = wave / 4, sub = wave % 4;
+        if (!guard) {
+            if (next < a.nrec)
+                prep_copy_g<FULL, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
+            // ---- C1: M tiles (waves 0-3) and P fragments (waves 4-7) -------
+            if (wave < NWP / 2) {
+                constexpr int NTM = NB * (NB + 1) / 2;
+                for (int tile = wave; tile < NTM; tile += NWP / 2) {
+                    int I = 0;
+                    while ((I + 1) * (I + 2) / 2 <= tile)
+                        ++I;
+                    const int J = tile - I * (I + 1) / 2;
+                    const bool same = NH == 1 || (I >> 1) == (J >> 1);
+                    const E* Bs = same ? sEh : sE2;
+                    const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < (NTILE + 3) / 4; ++r) {
-                const int tile = sub + 4 * r;
-                if (tile >= NTILE)
-                    break;
-                int I = 0;
-                while ((I + 1) * (I + 2) / 2 <= tile)
-                    ++I;
-                const int J = tile - I * (I + 1) / 2;
-                const bool same_half = (I >> 1) == (J >> 1);
-                if (guard)
-                    break;
-                const E* A = (I >= 2 && same_half) ? (kind ? sQh : sEh) + (16 * I - 32) * LDA
-                                                   : (kind ? sQ : sE) + 16 * I * LDA;
-                const E* Bm = sKr + 16 * J * LDA;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k0 = 0; k0 < D; k0 += MM::KB)
-                    acc = MM::mma(MM::load(A + k0, LDA, lane), MM::load(Bm + k0, LDA, lane), acc);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int rr = 16 * I + 4 * gq + ii, s = 16 * J + cl;
-                    if (kind == 0) {
-                        const float m = s < rr ? -acc[ii] : 0.f;
-                        if (I == J)
-                            sMd[(I * 16 + 4 * gq + ii) * LDX + cl] = m;
-                        sMb[rr * LDC + s] = from_f32<E>(I == J ? 0.f : m);
+                    for (int ks = 0; ks < NKS; ++ks)
+                        acc = MM::mma(row_frag<E, D>(sKr, 16 * J + cl, 4 * ks + gq),
+                                      row_frag<E, D>(Bs, rb, 4 * ks + gq), acc);
+                    // lane: M[16I + cl][16J + 4gq + i]
+                    if (J < I) {
+                        *reinterpret_cast<typename M16::Frag*>(sM + (16 * I + cl) * LDM + 16 * J + 4 * gq) =
+                            M16::pack(acc);
                     } else {
-                        sP[rr * LDC + s] = from_f32<E>(s <= rr ? acc[ii] : 0.f);
+                        f32x4 m;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            m[i] = 4 * gq + i < cl ? acc[i] : 0.f;
+                        *reinterpret_cast<f32x4*>(sMd + (16 * I + cl) * LDX + 4 * gq) = m;
                     }
                 }
-            }
-            // Tiles above the block diagonal are zero in both.
-            for (int e = tid; e < C * C; e += NTP) {
-                const int rr = e / C, s = e % C;
-                if ((s >> 4) > (rr >> 4)) {
-                    sP[rr * LDC + s] = from_f32<E>(0.f);
-                    sMb[rr * LDC + s] = from_f32<E>(0.f);
-                }
-            }
-            for (int e = tid; e < D * (C / VEC); e += NTP) {
-                const int tg = e % (C / VEC), i = e / (C / VEC);
-                float x[VEC];
-                if (!guard) {
-                    const float f = sFk[((tg * VEC) >> 5) * D + i];
+            } else {
+                for (int f = wave - NWP / 2; f < NP; f += NWP / 2) {
+                    int I = 0;
+                    while (I + 1 < NB && F::p_offset(I + 1) <= f)
+                        ++I;
+                    const int m = f - F::p_offset(I);
+                    f32x4 acc[KT];
 #pragma unroll
-                    for (int u = 0; u < VEC; ++u)
-                        x[u] = to_f32(sKr[perm_index<E>(tg, u) * LDA + i]) * f;
-                } else {
-                    // steep decay: K^ = k 2^(G_last - G) directly from the inputs
-                    const E* k = (const E*)a.k;
-                    const float gl = sG[(C - 1) * D + i];
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const int J = KT * m + kt;
+                        acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (J > I)
+                            continue;
+                        const bool same = NH == 1 || (I >> 1) == (J >> 1);
+                        const E* Bs = same ? sQh : sQ2;
+                        const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
 #pragma unroll
-                    for (int u = 0; u < VEC; ++u) {
-                        const int t = perm_index<E>(tg, u);
-                        const float kv = t < cp.L ? to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) : 0.f;
-                        x[u] = kv * fast_exp2(gl - sG[t * D + i]);
+                        for (int ks = 0; ks < NKS; ++ks)
+                            acc[kt] = MM::mma(row_frag<E, D>(sKr, 16 * J + cl, 4 * ks + gq),
+                                              row_frag<E, D>(Bs, rb, 4 * ks + gq), acc[kt]);
+                        if (J == I) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                acc[kt][i] = 4 * gq + i <= cl ? acc[kt][i] : 0.f;
+                        }
                     }
+                    stg16(reinterpret_cast<unsigned char*>(gP) + f * F::FRAG + lane * 16,
+                          __builtin_bit_cast(u32x4, frag_of<E>(acc)));
                 }
-                stg16(gKt + i * C + tg * VEC, pack_vec<E>(x));
             }
-        }
-        if (guard) {
-            // Exact tiles for a chunk whose decay is too steep for the
-            // referenced form: every pair s <= t from the raw inputs.
+        } else {
+            // ---- exact path for a chunk with steep decay -------------------
+            // G over the raw rows in sG (phase A has read them all)
+            if (ab) {
+#pragma unroll
+                for (int j = 0; j < S::TPL; ++j)
+#pragma unroll
+                    for (int x4 = 0; x4 < VEC / 4; ++x4)
+                        *reinterpret_cast<f32x4*>(sG + (t0 + j) * D + c0 + 4 * x4) =
+                            f32x4{G[j][4 * x4], G[j][4 * x4 + 1], G[j][4 * x4 + 2], G[j][4 * x4 + 3]};
+            }
             __syncthreads();
             const E* q = (const E*)a.q;
             const E* k = (const E*)a.k;
             const E* b = (const E*)a.b;
+            // M, every pair s < t
             for (int e = tid; e < C * C; e += NTP) {
-                const int rr = e / C, s = e % C;
-                float m = 0.f, p = 0.f;
-                if (s <= rr && rr < cp.L) {
-                    const int64_t xr = cp.row0 + (int64_t)rr * a.H, xs = cp.row0 + (int64_t)s * a.H;
+                const int t = e / C, s = e % C;
+                if (s >= t)
+                    continue;
+                float m = 0.f;
+                if (t < cp.L) {
+                    const int64_t xr = cp.row0 + (int64_t)t * a.H, xs = cp.row0 + (int64_t)s * a.H;
                     for (int i = 0; i < D; ++i) {
-                        const float dec = fast_exp2(sG[rr * D + i] - sG[s * D + i]);
-                        const float ks = to_f32(k[xs * D + i]) * dec;
                         const float br = to_f32(bw == 1 ? b[xr] : b[xr * D + i]);
-                        m += br * to_f32(k[xr * D + i]) * ks;
-                        p += to_f32(q[xr * D + i]) * ks;
+                        m += br * to_f32(k[xr * D + i]) * to_f32(k[xs * D + i]) *
+                             fast_exp2(sG[t * D + i] - sG[s * D + i]);
                     }
                 }
-                const float mn = s < rr ? -m : 0.f;
-                if ((rr >> 4) == (s >> 4))
-                    sMd[((rr >> 4) * 16 + (rr & 15)) * LDX + (s & 15)] = mn;
-                sMb[rr * LDC + s] = from_f32<E>((rr >> 4) == (s >> 4) ? 0.f : mn);
-                sP[rr * LDC + s] = from_f32<E>(p);
+                if ((t >> 4) == (s >> 4))
+                    sMd[t * LDX + (s & 15)] = m;
+                else
+                    sM[t * LDM + s] = from_f32<E>(m);
             }
+            // P, straight into its fragments (zeros above the diagonal)
+            for (int e = tid; e < NP * 16 * KB; e += NTP) {
+                const int f = e / (16 * KB), r = (e / KB) % 16, kk = e % KB;
+                int I = 0;
+                while (I + 1 < NB && F::p_offset(I + 1) <= f)
+                    ++I;
+                const int m = f - F::p_offset(I);
+                const int t = 16 * I + r, s = KB * m + kk;
+                float p = 0.f;
+                if (s <= t && t < cp.L) {
+                    const int64_t xr = cp.row0 + (int64_t)t * a.H, xs = cp.row0 + (int64_t)s * a.H;
+                    for (int i = 0; i < D; ++i)
+                        p += to_f32(q[xr * D + i]) * to_f32(k[xs * D + i]) * fast_exp2(sG[t * D + i] - sG[s * D + i]);
+                }
+                // lane (g, r) holds k = 4g..4g+3 of each 16-block of the fragment
+                const int k16 = kk & 15, slot = 4 * (kk >> 4) + (k16 & 3);
+                gP[f * (F::FRAG / sizeof(E)) + ((k16 >> 2) * 16 + r) * (16 / sizeof(E)) + slot] = from_f32<E>(p);
+            }
+            // K^ = k 2^(G_L - G) into the Kr rows (used below unscaled)
+            for (int e = tid; e < C * D; e += NTP) {
+                const int t = e / D, i = e % D;
+                float kh = 0.f;
+                if (t < cp.L)
+                    kh = to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) * fast_exp2(sG[(C - 1) * D + i] - sG[t * D + i]);
+                sKr[swz<E, D>(t, i)] = from_f32<E>(kh);
+            }
+            __syncthreads();   // every read of G is done
+            if (next < a.nrec)
+                prep_copy_g<FULL, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
         }
-        __syncthreads();
+        lds_barrier();   // B3: M in LDS
 
-        // Phase 5: wave 0 inverts the diagonal blocks by forward substitution
-        // (one lane per column, fp32); the other waves write P out.
+        // ---- C2: X = (I + M)^-1 (wave 0); K^T and Q~ fragments (others) --
         if (wave == 0) {
             if (gq < NB) {
+                // column cl of X_gq,gq by forward substitution
                 const float* m = sMd + gq * 16 * LDX;
                 float x[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float acc = r == cl ? 1.f : 0.f;
+                    float acc0 = r == cl ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-                    for (int c2 = 0; c2 < r; ++c2)
-                        acc += m[r * LDX + c2] * x[c2];
-                    x[r] = acc;
-                    // keep each row's LDS reads next to their use (bounded registers)
-                    __asm__ __volatile__("" ::: "memory");
+                    for (int c = 0; c + 1 < r; c += 2) {
+                        acc0 -= m[r * LDX + c] * x[c];
+                        acc1 -= m[r * LDX + c + 1] * x[c + 1];
+                    }
+                    if (r & 1)
+                        acc0 -= m[r * LDX + r - 1] * x[r - 1];
+                    x[r] = acc0 + acc1;
                 }
+                float* xc = sXc + (gq * 16 + cl) * LDX;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sXd[(gq * 16 + r) * LDX + cl] = x[r];
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<f32x4*>(xc + 4 * r4) = f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
             }
-        } else {
-            for (int e = tid - 64; e < C * (C / VEC); e += NTP - 64) {
-                const int rr = e / (C / VEC), cg = e % (C / VEC);
-                stg16(gP + rr * C + cg * VEC, perm_chunk<E>(sP + rr * LDC, cg));
-            }
-            for (int e = tid - 64; e < C * (D / VEC); e += NTP - 64) {
-                const int rr = e / (D / VEC), cg = e % (D / VEC);
-                stg16(gQt + rr * D + cg * VEC, perm_chunk<E>(sQ + rr * LDA, cg));
-            }
-        }
-        __syncthreads();
-
-        // Phase 6: blocked substitution for [W | U~], 2D/8 right-hand-side
-        // columns per wave (waves 0-3: E~ -> W, waves 4-7: u -> U~), solved
-        // blocks kept as MFMA accumulators.
-        {
-            constexpr int NCT = 2 * D / NWP / 16;     // 16-column tiles per wave
-            E* rhs = wave < NWP / 2 ? sE : sU;
-            const int c0 = 16 * NCT * (wave % (NWP / 2));
-            f32x4 sol[NCT][NB];
-#pragma unroll
-            for (int n = 0; n < NCT; ++n)
-#pragma unroll
-                for (int I = 0; I < NB; ++I)
-                    sol[n][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+            lds_fence_wave();
+            f32x4 Xt[NB][NB];
+            typename M16::Frag nx[NB];
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
-                f32x4 res[NCT];
+                // accumulator tile X_II[4gq + i][cl]
+                Xt[I][I] = *reinterpret_cast<const f32x4*>(sXc + (16 * I + cl) * LDX + 4 * gq);
+                // A operand -X_II[cl][4gq + i]
+                f32x4 t;
 #pragma unroll
-                for (int n = 0; n < NCT; ++n) {
+                for (int i = 0; i < 4; ++i)
+                    t[i] = -sXc[(16 * I + 4 * gq + i) * LDX + cl];
+                nx[I] = M16::pack(t);
+            }
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        res[n][ii] = to_f32(rhs[(16 * I + 4 * gq + ii) * LDA + c0 + 16 * n + cl]);
-                }
+            for (int d = 1; d < NB; ++d) {
 #pragma unroll
-                for (int kk = 0; kk < I; kk += MM::KT) {
-                    const typename MM::Frag am = MM::load(sMb + 16 * I * LDC + 16 * kk, LDC, lane);
+                for (int I = d; I < NB; ++I) {
+                    const int J = I - d;
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int n = 0; n < NCT; ++n)
-                        res[n] = MM::mma(am, MM::from_acc(&sol[n][kk]), res[n]);
-                }
-                const typename MM::Frag ax = XiiFrag<E>::load(sXd + I * 16 * LDX, LDX, lane);
-#pragma unroll
-                for (int n = 0; n < NCT; ++n) {
-                    const f32x4 pair[2] = {res[n], res[n]};
-                    sol[n][I] = MM::mma(ax, MM::from_acc(pair), f32x4{0.f, 0.f, 0.f, 0.f});
+                    for (int K = J; K < I; ++K)
+                        y = M16::mma(M16::load(sM + (16 * I + cl) * LDM + 16 * K + 4 * gq), M16::pack(Xt[K][J]), y);
+                    Xt[I][J] = M16::mma(nx[I], M16::pack(y), f32x4{0.f, 0.f, 0.f, 0.f});
                 }
             }
-            const float sg = wave < NWP / 2 ? -1.f : 1.f;   // W leaves negated
+            // X into LDS rows in fragment k order
 #pragma unroll
-            for (int n = 0; n < NCT; ++n)
+            for (int I = 0; I < NB; ++I)
 #pragma unroll
-                for (int I = 0; I < NB; ++I)
+                for (int J = 0; J <= I; ++J)
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        rhs[(16 * I + 4 * gq + ii) * LDA + c0 + 16 * n + cl] = from_f32<E>(sg * sol[n][I][ii]);
+                    for (int i = 0; i < 4; ++i)
+                        sX[(16 * I + 4 * gq + i) * LDXP + kpos<E>(16 * J + cl)] = from_f32<E>(Xt[I][J][i]);
+        } else {
+            constexpr int NK = (D / 16) * NKC, NQ = NB * NKS;
+            E* gKh = (E*)a.Kh + rec * (F::K_BYTES / sizeof(E));
+            E* gQt = (E*)a.Qt + rec * (F::W_BYTES / sizeof(E));
+            for (int task = wave - 1; task < NK + NQ; task += NWP - 1) {
+                if (task < NK) {
+                    // K^T fragment (channel block c, token step m)
+                    const int c = task / NKC, m = task % NKC;
+                    f32x4 acc[KT];
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const int tb = KT * m + kt;
+                        acc[kt] = M16::mma(row4<E, D>(sKr, 16 * tb + cl, 16 * c + 4 * gq), ident,
+                                           f32x4{0.f, 0.f, 0.f, 0.f});
+                        const float f = guard ? 1.f : sFk[(NH == 2 ? (tb >> 1) : 0) * D + 16 * c + cl];
+                        acc[kt] = acc[kt] * f;
+                    }
+                    stg16(reinterpret_cast<unsigned char*>(gKh) + task * F::FRAG + lane * 16,
+                          __builtin_bit_cast(u32x4, frag_of<E>(acc)));
+                } else {
+                    // Q~ fragment (token block T, channel step m)
+                    const int fq = task - NK, T = fq / NKS, m = fq % NKS;
+                    const bool sec = NH == 2 && T >= 2;
+                    const E* src = sec ? sQ2 : sQh;
+                    const int r = sec ? 16 * T - 32 + cl : 16 * T + cl;
+                    u32x4 v;
+                    if constexpr (sizeof(E) == 2) {
+                        const u32x2 lo = __builtin_bit_cast(u32x2, row4<E, D>(src, r, KB * m + 4 * gq));
+                        const u32x2 hi = __builtin_bit_cast(u32x2, row4<E, D>(src, r, KB * m + 16 + 4 * gq));
+                        v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                    } else {
+                        v = __builtin_bit_cast(u32x4, row4<E, D>(src, r, KB * m + 4 * gq));
+                    }
+                    stg16(reinterpret_cast<unsigned char*>(gQt) + fq * F::FRAG + lane * 16, v);
+                }
+            }
         }
-        __syncthreads();
-        for (int e = tid; e < C * (D / VEC); e += NTP) {
-            const int rr = e / (D / VEC), cg = e % (D / VEC);
-            stg16(gWn + rr * D + cg * VEC, perm_chunk<E>(sE + rr * LDA, cg));
-            stg16(gUt + rr * D + cg * VEC, lds16(sU + rr * LDA + cg * VEC));
+        lds_barrier();   // B4: X in LDS
+
+        // ---- D: -W fragments (waves 0-3), U~ tiles (waves 4-7) ------------
+        {
+            typename MM::Frag xf[NP];
+#pragma unroll
+            for (int T = 0; T < NB; ++T)
+#pragma unroll
+                for (int m = 0; m <= T / KT; ++m)
+                    xf[F::p_offset(T) + m] =
+                        *reinterpret_cast<const typename MM::Frag*>(sX + (16 * T + cl) * LDXP + KB * m + VEC * gq);
+            if (wave < NWP / 2) {
+                E* gWn = (E*)a.Wn + rec * (F::W_BYTES / sizeof(E));
+                for (int m2 = wave; m2 < NKS; m2 += NWP / 2) {
+                    // E~^T fragments of channel blocks KT*m2.., every token step
+                    typename MM::Frag ea[KT][NKC];
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const int cb = KT * m2 + kt;
+#pragma unroll
+                        for (int m = 0; m < NKC; ++m) {
+                            f32x4 tt[KT];
+#pragma unroll
+                            for (int k2 = 0; k2 < KT; ++k2) {
+                                const int tb = KT * m + k2;
+                                const bool sec = NH == 2 && tb >= 2;
+                                tt[k2] = M16::mma(row4<E, D>(sec ? sE2 : sEh, sec ? 16 * tb - 32 + cl : 16 * tb + cl,
+                                                             16 * cb + 4 * gq),
+                                                  ident, f32x4{0.f, 0.f, 0.f, 0.f});
+                            }
+                            ea[kt][m] = frag_of<E>(tt);
+                        }
+                    }
+#pragma unroll
+                    for (int T = 0; T < NB; ++T) {
+                        f32x4 wt[KT];
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt) {
+                            wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int m = 0; m <= T / KT; ++m)
+                                wt[kt] = MM::mma(ea[kt][m], xf[F::p_offset(T) + m], wt[kt]);
+                            wt[kt] = -wt[kt];
+                        }
+                        stg16(reinterpret_cast<unsigned char*>(gWn) + (T * NKS + m2) * F::FRAG + lane * 16,
+                              __builtin_bit_cast(u32x4, frag_of<E>(wt)));
+                    }
+                }
+            } else {
+                E* gUt = (E*)a.Ut + rec * (F::U_BYTES / sizeof(E));
+                for (int n = wave - NWP / 2; n < D / 16; n += NWP / 2) {
+                    typename MM::Frag ub[NKC];
+#pragma unroll
+                    for (int m = 0; m < NKC; ++m) {
+                        f32x4 tt[KT];
+#pragma unroll
+                        for (int k2 = 0; k2 < KT; ++k2)
+                            tt[k2] = M16::mma(row4<E, D>(sU, 16 * (KT * m + k2) + cl, 16 * n + 4 * gq), ident,
+                                              f32x4{0.f, 0.f, 0.f, 0.f});
+                        ub[m] = frag_of<E>(tt);
+                    }
+#pragma unroll
+                    for (int T = 0; T < NB; ++T) {
+                        f32x4 ut = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int m = 0; m <= T / KT; ++m)
+                            ut = MM::mma(xf[F::p_offset(T) + m], ub[m], ut);
+                        E* dst = gUt + (n * NB + T) * (F::TILE_U / sizeof(E)) + lane * 4;
+                        *reinterpret_cast<typename Mma16<E>::Frag*>(dst) = M16::pack(ut);
+                    }
+                }
+            }
         }
     }
 }
@@ -725,102 +1070,67 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 // chunk_state: carries the fp32 state through the chunks of one sequence and
 // head, BV value columns per workgroup (16 per wave), and writes o.
 //
-// The factors of a chunk (-W, Q~, K^T, P, this slice of U~, gamma) are copied
-// from the workspace straight into LDS with global_load_lds_dwordx4 (no
-// register staging), double buffered: the copy of chunk n + 1 is in flight
-// while chunk n computes.  The two buffers are separate static LDS objects so
-// that reads of one are never ordered behind the copies into the other.
-// Rows are padded by 16 bytes (one extra copy slot per row, filled with a
-// harmless duplicate) so that fragment reads of 16 consecutive rows hit 16
-// different bank groups.
+// A chunk's fragments (-W, Q~, K^T, P, this slice's U~ tiles, gamma) are
+// copied from the workspace straight into LDS with global_load_lds_dwordx4
+// (no register staging), double buffered: the copy of chunk n + 1 is in
+// flight while chunk n computes.  The two buffers are separate static LDS
+// objects so that reads of one are never ordered behind the copies into the
+// other.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C, int BV>
 struct StateShape {
+    typedef Frags<E, D, C> F;
     static constexpr int NB = C / 16;
     static constexpr int ES = (int)sizeof(E);
     static constexpr int VEC = 16 / ES;
     static constexpr int NS = D / BV;                       // column slices per (b,h)
-    static constexpr int LDA = D + VEC;                     // W, Q~ rows (elements)
-    static constexpr int LDT = C + VEC;                     // K^T, P rows
-    static constexpr int LDU = BV + VEC;                    // U~ slice rows
+    static constexpr int NTU = BV / 16;                     // value tiles per slice
     static constexpr int LDO = 16 + VEC;                    // per-wave output staging rows
-    static constexpr int OFF_W = 0;                         // element offsets in one buffer
-    static constexpr int OFF_Q = OFF_W + C * LDA;
-    static constexpr int OFF_KT = OFF_Q + C * LDA;
-    static constexpr int OFF_P = OFF_KT + D * LDT;
-    static constexpr int OFF_U = OFF_P + C * LDT;
-    static constexpr int OFF_G = OFF_U + C * LDU;           // gamma: D floats
-    static constexpr int BUF = OFF_G + D * 4 / ES;          // elements per buffer
+    static constexpr size_t U_SLICE = (size_t)NTU * NB * F::TILE_U;
+    static constexpr size_t OFF_W = 0;                      // byte offsets in one buffer
+    static constexpr size_t OFF_Q = OFF_W + F::W_BYTES;
+    static constexpr size_t OFF_KT = OFF_Q + F::W_BYTES;
+    static constexpr size_t OFF_P = OFF_KT + F::K_BYTES;
+    static constexpr size_t OFF_U = OFF_P + F::P_BYTES;
+    static constexpr size_t OFF_G = OFF_U + U_SLICE;        // gamma: D floats
+    static constexpr size_t BUF = OFF_G + (size_t)D * 4;
     static constexpr size_t SZ_O = (size_t)(NT / 64) * C * LDO * ES;
-    // double buffering when two buffers fit (every bf16 shape); else one
-    static constexpr int NBUF = 2 * (size_t)BUF * ES + SZ_O <= 160 * 1024 ? 2 : 1;
-    static constexpr size_t SMEM = NBUF * (size_t)BUF * ES + SZ_O;
+    // double buffering when two buffers fit; else one
+    static constexpr int NBUF = 2 * BUF + SZ_O <= 160 * 1024 ? 2 : 1;
+    static constexpr size_t SMEM = NBUF * BUF + SZ_O;
     static_assert(BV == 16 * (NT / 64), "one 16-column tile per wave");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(U_SLICE % 1024 == 0, "U~ slice copies");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copy R rows of RB bytes (global rows GS bytes apart) into LDS rows of
-// RB + 16 bytes, 16 bytes per lane per instruction, instructions spread over
-// the waves (instruction j belongs to wave j % 4).  Copy slot s of the tile
-// is LDS byte 16*s; the last slot of each row is padding and receives a
-// duplicate of the row's first 16 bytes.  The per-lane source offsets are the
-// same for every chunk and are computed once.
-template <int R, int RB>
-struct TileCopy {
-    static constexpr int SPR = RB / 16 + 1, TOTAL = R * SPR, NINST = (TOTAL + 63) / 64;
-    static constexpr int PER_WAVE = (NINST + NT / 64 - 1) / (NT / 64);
-    int off[PER_WAVE];     // source byte offset, or -1 where the lane has no slot
-    __device__ __forceinline__ void init(int64_t gs, int wave, int lane) {
+// Copy BYTES (a multiple of 1 KB) from global to LDS, 16 bytes per lane per
+// instruction; instruction j belongs to wave j % 4.
+template <size_t BYTES>
+__device__ __forceinline__ void copy_linear(const unsigned char* g, unsigned char* l, int wave, int lane)
+{
+    constexpr int NINST = (int)(BYTES / 1024);
 #pragma unroll
-        for (int u = 0; u < PER_WAVE; ++u) {
-            const int j = u * (NT / 64) + wave, sl = j * 64 + lane;
-            const int row = sl / SPR, c = sl % SPR;
-            off[u] = (j < NINST && sl < TOTAL) ? (int)(row * gs + (c == SPR - 1 ? 0 : c * 16)) : -1;
-        }
-    }
-    __device__ __forceinline__ void issue(const unsigned char* g, unsigned char* l, int wave) const {
-#pragma unroll
-        for (int u = 0; u < PER_WAVE; ++u) {
-            const int j = u * (NT / 64) + wave;
-            // wave-uniform except in a partial last instruction
-            if (j < NINST && (TOTAL % 64 == 0 || off[u] >= 0))
-                __builtin_amdgcn_global_load_lds(g + off[u], (lds_void*)(l + j * 64 * 16), 16, 0, 0);
-        }
-    }
-};
+    for (int j = wave; j < NINST; j += NT / 64)
+        __builtin_amdgcn_global_load_lds(g + j * 1024 + lane * 16, (lds_void*)(l + j * 1024), 16, 0, 0);
+}
 
 template <typename E, int D, int C, int BV>
-struct StateCopies {
-    TileCopy<C, D * (int)sizeof(E)> wq;     // -W and Q~ (same shape)
-    TileCopy<D, C * (int)sizeof(E)> kt;     // K^T
-    TileCopy<C, C * (int)sizeof(E)> p;      // P
-    TileCopy<C, BV * (int)sizeof(E)> u;     // this slice of U~
-    __device__ __forceinline__ void init(int wave, int lane) {
-        constexpr int ES = (int)sizeof(E);
-        wq.init(D * ES, wave, lane);
-        kt.init(C * ES, wave, lane);
-        p.init(C * ES, wave, lane);
-        u.init(D * ES, wave, lane);
-    }
-};
-
-template <typename E, int D, int C, int BV>
-__device__ __forceinline__ void state_fetch(const StateArgs& a, const StateCopies<E, D, C, BV>& cp,
-                                            int64_t rec, int slice, E* buf, int wave, int lane)
+__device__ __forceinline__ void state_fetch(const StateArgs& a, int64_t rec, int slice, unsigned char* buf,
+                                            int wave, int lane)
 {
     typedef StateShape<E, D, C, BV> S;
-    constexpr int ES = S::ES;
-    unsigned char* l = reinterpret_cast<unsigned char*>(buf);
-    cp.wq.issue((const unsigned char*)((const E*)a.Wn + rec * C * D), l + S::OFF_W * ES, wave);
-    cp.wq.issue((const unsigned char*)((const E*)a.Qt + rec * C * D), l + S::OFF_Q * ES, wave);
-    cp.kt.issue((const unsigned char*)((const E*)a.Kh + rec * C * D), l + S::OFF_KT * ES, wave);
-    cp.p.issue((const unsigned char*)((const E*)a.P + rec * C * C), l + S::OFF_P * ES, wave);
-    cp.u.issue((const unsigned char*)((const E*)a.Ut + rec * C * D + slice * BV), l + S::OFF_U * ES, wave);
-    // gamma: D floats, one unpadded row
-    if (wave == 0 && lane < D / 4)
-        __builtin_amdgcn_global_load_lds(a.gam + rec * D + lane * 4, (lds_void*)(l + S::OFF_G * ES), 16, 0, 0);
+    typedef Frags<E, D, C> F;
+    copy_linear<F::W_BYTES>((const unsigned char*)a.Wn + rec * F::W_BYTES, buf + S::OFF_W, wave, lane);
+    copy_linear<F::W_BYTES>((const unsigned char*)a.Qt + rec * F::W_BYTES, buf + S::OFF_Q, wave, lane);
+    copy_linear<F::K_BYTES>((const unsigned char*)a.Kh + rec * F::K_BYTES, buf + S::OFF_KT, wave, lane);
+    copy_linear<F::P_BYTES>((const unsigned char*)a.P + rec * F::P_BYTES, buf + S::OFF_P, wave, lane);
+    copy_linear<S::U_SLICE>((const unsigned char*)a.Ut + rec * F::U_BYTES + slice * S::U_SLICE, buf + S::OFF_U,
+                            wave, lane);
+    // gamma: D floats
+    if (wave == (NT / 64) - 1 && lane < D / 4)
+        __builtin_amdgcn_global_load_lds(a.gam + rec * D + lane * 4, (lds_void*)(buf + S::OFF_G), 16, 0, 0);
 }
 
 // Scheduling hint for a phase of N MFMAs fed from LDS: issue the first
@@ -838,54 +1148,49 @@ __device__ __forceinline__ void sched_pipeline()
     }
 }
 
-// s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed.
-__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// One chunk from buffer `buf`: Delta = U~ - W S, O = Q~ S + P Delta,
-// S <- diag(gamma) S + K^T Delta; O goes out through the wave's staging rows.
 template <typename E, int D, int C, int BV>
 __device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
                                              int slice, int64_t n, int lane, int wave);
 
+// One chunk from buffer `buf`: Delta = U~ - W S, O = Q~ S + P Delta,
+// S <- diag(gamma) S + K^T Delta; O goes out through the wave's staging rows.
 template <typename E, int D, int C, int BV>
-__device__ __forceinline__ void state_compute(const StateArgs& a, const E* buf, E* sOw, f32x4* St,
+__device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned char* buf, E* sOw, f32x4* St,
                                               int64_t b, int64_t h, int slice, int64_t n,
                                               int lane, int wave)
 {
     typedef StateShape<E, D, C, BV> S;
+    typedef Frags<E, D, C> F;
     typedef Mma<E> MM;
-    constexpr int NB = S::NB, VEC = S::VEC, LDA = S::LDA, LDT = S::LDT, LDU = S::LDU, LDO = S::LDO;
-    constexpr int NKS = D / MM::KB;      // MFMA steps over the state rows
-    constexpr int NKC = C / MM::KB;      // MFMA steps over the chunk's tokens
+    typedef typename MM::Frag Frag;
+    constexpr int NB = S::NB, LDO = S::LDO, KT = F::KT, NKS = F::NKS, NKC = F::NKC;
     constexpr int KTS = D / 16;
     const int gq = lane >> 4, cl = lane & 15;
-    const E* sW = buf + S::OFF_W;
-    const E* sQ = buf + S::OFF_Q;
-    const E* sKT = buf + S::OFF_KT;
-    const E* sP = buf + S::OFF_P;
-    const E* sU = buf + S::OFF_U;
+    const unsigned char* fl = buf + lane * 16;
+    auto frag = [&](size_t off, int i) -> Frag { return *reinterpret_cast<const Frag*>(fl + off + i * F::FRAG); };
     const float* sGam = reinterpret_cast<const float*>(buf + S::OFF_G);
 
-    typename MM::Frag SB[NKS];
+    Frag SB[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-        SB[ks] = MM::from_acc(&St[ks * MM::KT]);
+        SB[ks] = MM::from_acc(&St[ks * KT]);
 
     // Delta = U~ - W S  (W is stored negated).  Each phase reads all of its
     // A fragments before its MFMAs so LDS latency overlaps.
     f32x4 dl[NB];
     {
-        typename MM::Frag aw[NB][NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-                aw[mt][ks] = MM::load_perm(sW + 16 * mt * LDA + ks * MM::KB, LDA, lane);
+        Frag aw[NB][NKS];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dl[mt][i] = to_f32(sU[(16 * mt + 4 * gq + i) * LDU + 16 * wave + cl]);
+            for (int ks = 0; ks < NKS; ++ks)
+                aw[mt][ks] = frag(S::OFF_W, mt * NKS + ks);
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) {
+            const E* u = reinterpret_cast<const E*>(buf + S::OFF_U + (wave * NB + mt) * F::TILE_U) + lane * 4;
+            dl[mt] = f32x4{to_f32(u[0]), to_f32(u[1]), to_f32(u[2]), to_f32(u[3])};
+        }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -893,29 +1198,26 @@ __device__ __forceinline__ void state_compute(const StateArgs& a, const E* buf, 
                 dl[mt] = MM::mma(aw[mt][ks], SB[ks], dl[mt]);
         sched_pipeline<NB * NKS>();
     }
-    typename MM::Frag DB[NKC];
+    Frag DB[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
-        DB[kc] = MM::from_acc(&dl[kc * MM::KT]);
+        DB[kc] = MM::from_acc(&dl[kc * KT]);
     // the previous chunk's outputs leave while this one computes
     if (n > 0)
         state_store_o<E, D, C, BV>(a, sOw, b, h, slice, n - 1, lane, wave);
 
-    // O = Q~ S + P Delta  (P is lower triangular: skip all-zero steps).
+    // O = Q~ S + P Delta  (P is lower triangular: only stored steps).
     f32x4 ot[NB];
     {
-        typename MM::Frag aq[NB][NKS], ap[NB][NKC];
+        Frag aq[NB][NKS], ap[F::NP];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+        for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-                aq[mt][ks] = MM::load_perm(sQ + 16 * mt * LDA + ks * MM::KB, LDA, lane);
+            for (int ks = 0; ks < NKS; ++ks)
+                aq[mt][ks] = frag(S::OFF_Q, mt * NKS + ks);
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-                if (kc * MM::KT <= mt)
-                    ap[mt][kc] = MM::load_perm(sP + 16 * mt * LDT + kc * MM::KB, LDT, lane);
+        for (int i = 0; i < F::NP; ++i)
+            ap[i] = frag(S::OFF_P, i);
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt)
             ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -925,22 +1227,21 @@ __device__ __forceinline__ void state_compute(const StateArgs& a, const E* buf, 
             for (int mt = 0; mt < NB; ++mt)
                 ot[mt] = MM::mma(aq[mt][ks], SB[ks], ot[mt]);
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+        for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-                if (kc * MM::KT <= mt)
-                    ot[mt] = MM::mma(ap[mt][kc], DB[kc], ot[mt]);
+            for (int kc = 0; kc <= mt / KT; ++kc)
+                ot[mt] = MM::mma(ap[F::p_offset(mt) + kc], DB[kc], ot[mt]);
         sched_pipeline<NB * NKS>();
     }
 
     // S <- diag(gamma) S + K^T Delta.
     {
-        typename MM::Frag ak[KTS][NKC];
+        Frag ak[KTS][NKC];
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+        for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < KTS; ++kt)
-                ak[kt][kc] = MM::load_perm(sKT + 16 * kt * LDT + kc * MM::KB, LDT, lane);
+            for (int kc = 0; kc < NKC; ++kc)
+                ak[kt][kc] = frag(S::OFF_KT, kt * NKC + kc);
 #pragma unroll
         for (int kt = 0; kt < KTS; ++kt)
             St[kt] = St[kt] * *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * gq);
@@ -984,8 +1285,8 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
 {
     typedef StateShape<E, D, C, BV> S;
     constexpr int KTS = D / 16;
-    __shared__ __align__(16) E buf0[S::BUF];
-    __shared__ __align__(16) E buf1[S::NBUF == 2 ? S::BUF : 1];
+    __shared__ __align__(16) unsigned char buf0[S::BUF];
+    __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
     __shared__ __align__(16) E sO[(NT / 64) * C * S::LDO];
 
     // Workgroup -> (sequence*head, column slice).  The NS slices of one
@@ -1013,22 +1314,20 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
                 St[kt][i] = s0 ? s0[(16 * kt + 4 * gq + i) * D + col] : 0.f;
     }
 
-    StateCopies<E, D, C, BV> cp;
-    cp.init(wave, lane);
-    state_fetch<E, D, C, BV>(a, cp, rec0, slice, buf0, wave, lane);
+    state_fetch<E, D, C, BV>(a, rec0, slice, buf0, wave, lane);
     if (S::NBUF == 2) {
         for (int64_t n = 0; n < a.NC; n += 2) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
             if (n + 1 < a.NC)
-                state_fetch<E, D, C, BV>(a, cp, rec0 + n + 1, slice, buf1, wave, lane);
+                state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf1, wave, lane);
             state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
             if (n + 1 >= a.NC)
                 break;
             wait_copies();
             __syncthreads();          // chunk n + 1 is in buf1; everyone is done with buf0
             if (n + 2 < a.NC)
-                state_fetch<E, D, C, BV>(a, cp, rec0 + n + 2, slice, buf0, wave, lane);
+                state_fetch<E, D, C, BV>(a, rec0 + n + 2, slice, buf0, wave, lane);
             state_compute<E, D, C, BV>(a, buf1, sOw, St, b, h, slice, n + 1, lane, wave);
         }
     } else {
@@ -1038,7 +1337,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
             state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
             __syncthreads();          // everyone is done with buf0
             if (n + 1 < a.NC)
-                state_fetch<E, D, C, BV>(a, cp, rec0 + n + 1, slice, buf0, wave, lane);
+                state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf0, wave, lane);
         }
     }
 
@@ -1097,13 +1396,10 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     static const hipError_t attr1g = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&chunk_prep_kernel<false, E, D, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
-    static const hipError_t attr2 = hipSuccess;
     if (attr1 != hipSuccess)
         return attr1;
     if (attr1g != hipSuccess)
         return attr1g;
-    if (attr2 != hipSuccess)
-        return attr2;
 
     if (a.stage != GDR2_STAGE_STATE) {
         const int64_t grid1 = std::min<int64_t>(L.nrec, (int64_t)cu_count());

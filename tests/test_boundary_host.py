@@ -142,15 +142,19 @@ def test_forward_workspace_required(lib):
 
 
 def test_workspace_size_formula(lib):
-    # per chunk record: -W, U~, K^, Q~ ([C][D] each), P [C][C] in the input
-    # dtype, gamma [D] fp32; each array padded to 256 bytes.
+    # per chunk record: -W, U~, K^T, Q~ (C*D elements each) in the input
+    # dtype, the nonzero 1 KB fragments of P (16-token row block T holds
+    # T // KT + 1 of them, KT = 2 for bf16, 1 for fp32), gamma [D] fp32;
+    # each array padded to 256 bytes.
     def al(x):
         return (x + 255) // 256 * 256
     for (B, T, H, D, C, dt, es) in [(2, 100, 3, 128, 64, gdr2.BF16, 2), (1, 256, 1, 64, 32, gdr2.F32, 4),
-                                    (8, 4096, 16, 128, 64, gdr2.BF16, 2)]:
+                                    (8, 4096, 16, 128, 64, gdr2.BF16, 2), (1, 70, 2, 64, 64, gdr2.F32, 4)]:
         a = good_fwd(B=B, T=T, H=H, D=D, chunk=C, dtype=dt)
         nrec = B * H * -(-T // C)
-        want = 4 * al(nrec * C * D * es) + al(nrec * C * C * es) + al(nrec * D * 4)
+        kt = 2 if es == 2 else 1
+        n_p = sum(t // kt + 1 for t in range(C // 16))
+        want = 4 * al(nrec * C * D * es) + al(nrec * n_p * 1024) + al(nrec * D * 4)
         assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == want
     a = good_fwd(D=96)
     assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == 0
