@@ -1305,13 +1305,17 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
     E* sOw = sO + wave * C * S::LDO;
 
     f32x4 St[KTS];
-    {
-        const float* s0 = a.S0 ? a.S0 + bh * D * D : nullptr;
+    if (a.S0) {
+        const float* s0 = a.S0 + bh * D * D;
 #pragma unroll
         for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                St[kt][i] = s0 ? s0[(16 * kt + 4 * gq + i) * D + col] : 0.f;
+                St[kt][i] = s0[(16 * kt + 4 * gq + i) * D + col];
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+            St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     state_fetch<E, D, C, BV>(a, rec0, slice, buf0, wave, lane);
