@@ -167,16 +167,31 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
         return fail(GDR2_ERR_UNSUPPORTED, "too many chunks for one launch");
     if (!mul_ok(bh, a->Dk * a->Dv * 4, state_bytes))
         return fail(GDR2_ERR_INVALID_ARG, "state size overflows int64");
+    int64_t ck_bytes;
+    if (!mul_ok(*state_bytes, nchunks, &ck_bytes))
+        return fail(GDR2_ERR_INVALID_ARG, "S_chunks size overflows int64");
     Range S0 = range("S0", a->S0, *state_bytes), So = range("S_out", a->S_out, *state_bytes);
+    Range Sc = range("S_chunks", a->S_chunks, ck_bytes);
+    if (a->S_chunks) {
+        if (!aligned16(a->S_chunks))
+            return fail(GDR2_ERR_INVALID_ARG, "S_chunks must be 16-byte aligned");
+        if (overlaps(Sc, S0) || overlaps(Sc, So))
+            return fail(GDR2_ERR_INVALID_ARG, "S_chunks overlaps S0 / S_out");
+    }
     if ((a->S0 && !aligned16(a->S0)) || (a->S_out && !aligned16(a->S_out)))
         return fail(GDR2_ERR_INVALID_ARG, "S0 / S_out must be 16-byte aligned");
     if (a->S0 && a->S_out && a->S0 != a->S_out && overlaps(S0, So))
         return fail(GDR2_ERR_INVALID_ARG, "S_out partially overlaps S0 (only exact aliasing is allowed)");
     if (rows > 0) {
         TokenTensors t{a->q, a->k, a->v, a->b, a->w, a->g, a->o};
-        Range outs[1] = {So};
+        Range outs[2];
+        int n_outs = 0;
+        if (a->S_out)
+            outs[n_outs++] = So;
+        if (a->S_chunks)
+            outs[n_outs++] = Sc;
         s = check_token_ptrs(t, rows, a->Dk, a->Dv, a->dtype, a->b_width, a->w_width, a->g_width,
-                             outs, a->S_out ? 1 : 0);
+                             outs, n_outs);
         if (s != GDR2_OK)
             return s;
         // S0 is an input as well: o must not overlap it.
@@ -194,7 +209,7 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
             const Range others[] = {range("q", a->q, rows * a->Dk * e), range("k", a->k, rows * a->Dk * e),
                                     range("v", a->v, rows * a->Dv * e), range("b", a->b, rows * a->b_width * e),
                                     range("w", a->w, rows * a->w_width * e), range("g", a->g, rows * a->g_width * 4),
-                                    S0, So, range("o", a->o, rows * a->Dv * e)};
+                                    S0, So, Sc, range("o", a->o, rows * a->Dv * e)};
             for (const auto& r : others)
                 if (overlaps(ws, r))
                     return fail(GDR2_ERR_INVALID_ARG, "workspace overlaps %s", r.name);

@@ -152,6 +152,7 @@ struct StateArgs {
     const float* gam;
     const float* S0;
     float* S_out;
+    float* S_chunks;          // optional: the state at the start of every chunk
     void* o;
     int64_t T, H, NC, nbh;
 };
@@ -1153,6 +1154,21 @@ template <typename E, int D, int C, int BV>
 __device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
                                              int slice, int64_t n, int lane, int wave);
 
+// The state at the start of chunk n (this lane's column, its 4 rows per
+// tile) into the checkpoint output.
+template <int D>
+__device__ __forceinline__ void state_emit(const StateArgs& a, const f32x4* St, int64_t bh, int64_t n,
+                                           int gq, int col)
+{
+    constexpr int KTS = D / 16;
+    float* dst = a.S_chunks + (bh * a.NC + n) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dst[(16 * kt + 4 * gq + i) * D + col] = St[kt][i];
+}
+
 // One chunk from buffer `buf`: Delta = U~ - W S, O = Q~ S + P Delta,
 // S <- diag(gamma) S + K^T Delta; O goes out through the wave's staging rows.
 template <typename E, int D, int C, int BV>
@@ -1325,6 +1341,8 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
             if (n + 1 < a.NC)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf1, wave, lane);
+            if (a.S_chunks)
+                state_emit<D>(a, St, bh, n, gq, col);
             state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
             if (n + 1 >= a.NC)
                 break;
@@ -1332,12 +1350,16 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
             __syncthreads();          // chunk n + 1 is in buf1; everyone is done with buf0
             if (n + 2 < a.NC)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 2, slice, buf0, wave, lane);
+            if (a.S_chunks)
+                state_emit<D>(a, St, bh, n + 1, gq, col);
             state_compute<E, D, C, BV>(a, buf1, sOw, St, b, h, slice, n + 1, lane, wave);
         }
     } else {
         for (int64_t n = 0; n < a.NC; ++n) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0
+            if (a.S_chunks)
+                state_emit<D>(a, St, bh, n, gq, col);
             state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
             __syncthreads();          // everyone is done with buf0
             if (n + 1 < a.NC)
@@ -1419,7 +1441,7 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
 
     StateArgs sa;
     sa.Wn = pa.Wn; sa.Ut = pa.Ut; sa.Kh = pa.Kh; sa.Qt = pa.Qt; sa.P = pa.P; sa.gam = pa.gam;
-    sa.S0 = a.S0; sa.S_out = a.S_out; sa.o = a.o;
+    sa.S0 = a.S0; sa.S_out = a.S_out; sa.S_chunks = a.S_chunks; sa.o = a.o;
     sa.T = a.T; sa.H = a.H; sa.NC = pa.NC; sa.nbh = a.B * a.H;
     const int64_t grid2 = ceil_div(sa.nbh, 8) * 8 * SS::NS;
     hipLaunchKernelGGL((chunk_state_kernel<E, D, C, BV>), dim3((unsigned)grid2), dim3(NT), 0, stream, sa);

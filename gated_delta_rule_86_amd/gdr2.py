@@ -33,7 +33,7 @@ class FwdArgs(ctypes.Structure):
                 ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("reserved", _c_i32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp),
                 ("g", _vp), ("S0", _vp), ("o", _vp), ("S_out", _vp),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("S_chunks", _vp)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -46,7 +46,7 @@ class DecodeArgs(ctypes.Structure):
 # Every symbol include/gdr2.h declares (checked by the tests).
 EXPORTS = ("gdr2_forward_workspace_size", "gdr2_forward_chunked", "gdr2_decode_step",
            "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class Gdr2Error(RuntimeError):
@@ -114,14 +114,14 @@ def _req(t: torch.Tensor, name: str, dtype=None):
 
 
 def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
-             algo: str = "auto", workspace=None, stage: str = "all") -> FwdArgs:
+             algo: str = "auto", workspace=None, stage: str = "all", S_chunks=None) -> FwdArgs:
     B, T, H, Dk = q.shape
     a = FwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, v.shape[-1]
     a.chunk, a.dtype, a.algo, a.stage = chunk, _dtype_code(q), ALGOS[algo], STAGES[stage]
     a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
     a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
-    a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
+    a.S0, a.o, a.S_out, a.S_chunks = _ptr(S0), _ptr(o), _ptr(S_out), _ptr(S_chunks)
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a
@@ -129,10 +129,12 @@ def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
 
 def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
             out=None, S_out=None, workspace=None, final_state: bool = True,
-            stage: str = "all"):
+            stage: str = "all", chunk_states=None):
     """Chunked forward.  q,k [B,T,H,Dk]; v [B,T,H,Dv]; b [B,T,H,1|Dk];
     w [B,T,H,1|Dv] (all float32 or bfloat16); g float32 [B,T,H,1|Dk];
-    S0 float32 [B,H,Dk,Dv] or None.  Returns (o, S_final).
+    S0 float32 [B,H,Dk,Dv] or None.  Returns (o, S_final), or
+    (o, S_final, S_chunks) when chunk_states is True or a float32 tensor
+    [B,H,ceil(T/chunk),Dk,Dv]: the state at the start of every chunk.
     stage='prep' / 'state' runs one kernel of the staged algorithm (pass the
     same workspace, out and S_out to both calls)."""
     lib = load_library()
@@ -147,7 +149,14 @@ def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
         out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
     if S_out is None and final_state:
         S_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, stage=stage)
+    ck = None
+    if chunk_states is not None and chunk_states is not False:
+        if chunk_states is True:
+            ck = torch.empty((B, H, -(-T // chunk), Dk, Dv), dtype=torch.float32, device=q.device)
+        else:
+            ck = chunk_states
+            _req(ck, "chunk_states", torch.float32)
+    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, stage=stage, S_chunks=ck)
     need = lib.gdr2_forward_workspace_size(ctypes.byref(a))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -155,7 +164,7 @@ def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib, lib.gdr2_forward_chunked(ctypes.byref(a), stream))
-    return out, S_out
+    return (out, S_out) if ck is None else (out, S_out, ck)
 
 
 def workspace_size(q, k, v, b, w, g, chunk: int = 64, algo: str = "auto") -> int:

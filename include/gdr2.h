@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 1
+#define GDR2_ABI_VERSION 2
 
 typedef enum gdr2_status {
     GDR2_OK = 0,
@@ -110,6 +110,16 @@ typedef enum gdr2_stage {
  *   S_out  [B, H, Dk, Dv]       fp32, written, may be NULL; may be the same
  *                               pointer as S0 (in-place continuation), must
  *                               not otherwise overlap anything
+ *   S_chunks [B, H, NC, Dk, Dv] fp32, NC = ceil(T / chunk), may be NULL:
+ *                               written with the state at the start of every
+ *                               chunk (S_chunks[b, h, n] = the state before
+ *                               token n*chunk; n = 0 gives S0 or zeros), the
+ *                               segment-boundary memory checkpoints of the
+ *                               page "Memory Caching(MC): 길이에 따라
+ *                               메모리가 커지는 RNN에 대한 연구", section
+ *                               "체크포인트를 캐싱할까, 독립 압축기를
+ *                               쓸까?".  Written by the STATE stage; must
+ *                               not overlap anything else.
  *   o must not overlap any input.
  * Supported set: Dk == Dv in {64, 128}; chunk in {32, 64}; dtype F32 or BF16,
  * with Dk * chunk <= 4096 for F32; B, T, H >= 0 (T need not be a multiple of
@@ -131,6 +141,7 @@ typedef struct gdr2_fwd_args {
     float *S_out;
     void *workspace;      /* device memory, >= gdr2_forward_workspace_size() bytes */
     size_t workspace_bytes;
+    float *S_chunks;      /* optional chunk-start states (see above) */
 } gdr2_fwd_args;
 
 /*

@@ -63,6 +63,9 @@ def _bind(lib):
     lib.gdr2_oracle_forward.restype = ctypes.c_int
     lib.gdr2_oracle_forward.argtypes = [_L, _L, _L, _L, _L, _D, _D, _D, _D, _L, _D, _L,
                                         _D, _L, _D, _D, _D, ctypes.c_int]
+    lib.gdr2_oracle_forward_ckpt.restype = ctypes.c_int
+    lib.gdr2_oracle_forward_ckpt.argtypes = [_L, _L, _L, _L, _L, _D, _D, _D, _D, _L, _D, _L,
+                                             _D, _L, _D, _D, _D, _L, _D, ctypes.c_int]
     lib.gdr2_oracle_decode.restype = ctypes.c_int
     lib.gdr2_oracle_decode.argtypes = [_L, _L, _L, _L, _D, _D, _D, _D, _L, _D, _L, _D, _L,
                                        _D, _D, ctypes.c_int]
@@ -112,6 +115,30 @@ def forward(q, k, v, b, w, g, S0=None, threads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError(f"gdr2_oracle_forward failed ({rc})")
     return o, S
+
+
+def forward_checkpoints(q, k, v, b, w, g, every: int, S0=None, threads: int = 0, lib=None):
+    """Sequential fp64 forward that also records the state before every
+    `every`-th token (a checkpoint at each segment boundary).
+
+    Returns (o, S_final, S_ckpt [B,H,ceil(T/every),dk,dv]) as float64 arrays;
+    S_ckpt[:, :, n] is the state before token n*every (S_ckpt[:, :, 0] = S0).
+    """
+    lib = lib or load()
+    q, k, v, b, w, g = (_f64(x) for x in (q, k, v, b, w, g))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bw, ww, gw = _width(b, dk, "b"), _width(w, dv, "w"), _width(g, dk, "g")
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    S = np.zeros((B, H, dk, dv), dtype=np.float64)
+    ck = np.zeros((B, H, -(-T // every), dk, dv), dtype=np.float64)
+    rc = lib.gdr2_oracle_forward_ckpt(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(b), bw,
+                                      _ptr(w), ww, _ptr(g), gw, _ptr(s0), _ptr(o), _ptr(S),
+                                      int(every), _ptr(ck), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"gdr2_oracle_forward_ckpt failed ({rc})")
+    return o, S, ck
 
 
 def decode_step(state, q, k, v, b, w, g, threads: int = 0, lib=None):

@@ -93,14 +93,18 @@ static void gdr2_token(long dk, long dv, double *S, double *r,
 }
 
 /*
+ * The forward.  every > 0 and S_ckpt non-NULL also record checkpoints
+ * ([MC], section "체크포인트를 캐싱할까, 독립 압축기를 쓸까?": the memory
+ * at segment boundaries): S_ckpt [B, H, ceil(T/every), d_k, d_v] receives
+ * the state before token n*every, for every n (entry 0 is the initial state).
  * Returns 0 on success, -1 on bad arguments, -2 when memory runs out.
  * threads <= 0 keeps the OpenMP default.
  */
-int gdr2_oracle_forward(long B, long T, long H, long dk, long dv,
+static int forward_impl(long B, long T, long H, long dk, long dv,
                         const double *q, const double *k, const double *v,
                         const double *b, long bw, const double *w, long ww,
                         const double *g, long gw, const double *S0,
-                        double *o, double *S_out, int threads)
+                        double *o, double *S_out, long every, double *S_ckpt, int threads)
 {
     long bh, n_bh = B * H;
     int failed = 0;
@@ -134,6 +138,10 @@ int gdr2_oracle_forward(long B, long T, long H, long dk, long dv,
             memset(S, 0, sizeof(double) * (size_t)(dk * dv));
         for (t = 0; t < T; ++t) {
             long row = (bi * T + t) * H + h; /* token row in [B, T, H, .] */
+            if (S_ckpt && t % every == 0) {
+                long nck = (T + every - 1) / every;
+                memcpy(S_ckpt + (bh * nck + t / every) * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
+            }
             gdr2_token(dk, dv, S, r,
                        q + row * dk, k + row * dk, v + row * dv,
                        b + row * bw, bw, w + row * ww, ww,
@@ -145,6 +153,26 @@ int gdr2_oracle_forward(long B, long T, long H, long dk, long dv,
         free(r);
     }
     return failed ? -2 : 0;
+}
+
+int gdr2_oracle_forward(long B, long T, long H, long dk, long dv,
+                        const double *q, const double *k, const double *v,
+                        const double *b, long bw, const double *w, long ww,
+                        const double *g, long gw, const double *S0,
+                        double *o, double *S_out, int threads)
+{
+    return forward_impl(B, T, H, dk, dv, q, k, v, b, bw, w, ww, g, gw, S0, o, S_out, 0, NULL, threads);
+}
+
+int gdr2_oracle_forward_ckpt(long B, long T, long H, long dk, long dv,
+                             const double *q, const double *k, const double *v,
+                             const double *b, long bw, const double *w, long ww,
+                             const double *g, long gw, const double *S0,
+                             double *o, double *S_out, long every, double *S_ckpt, int threads)
+{
+    if (every <= 0 || !S_ckpt)
+        return -1;
+    return forward_impl(B, T, H, dk, dv, q, k, v, b, bw, w, ww, g, gw, S0, o, S_out, every, S_ckpt, threads);
 }
 
 /*

@@ -298,6 +298,25 @@ def pin_decode_is_one_token(lib, seed=11):
     return worst
 
 
+def pin_checkpoints_are_prefix_states(lib, seed=12):
+    """[MC] The checkpoint at segment boundary n is the state a run over the
+    first n*every tokens ends in (bit for bit), checkpoint 0 is S0, and the
+    run's own outputs are unchanged by recording checkpoints."""
+    rng = np.random.default_rng(seed)
+    p = rand_problem(rng, B=2, T=13, H=2)
+    S0 = rng.standard_normal((2, 2, 6, 5))
+    o, S = oracle.forward(**p, S0=S0, lib=lib)
+    worst = 0.0
+    for every in (1, 4, 13, 20):
+        oc, Sc, ck = oracle.forward_checkpoints(**p, every=every, S0=S0, lib=lib)
+        assert ck.shape[2] == -(-13 // every)
+        worst = max(worst, np.abs(oc - o).max(), np.abs(Sc - S).max(), np.abs(ck[:, :, 0] - S0).max())
+        for n in range(ck.shape[2]):
+            _, Sn = oracle.forward(**{m: a[:, :n * every] for m, a in p.items()}, S0=S0, lib=lib)
+            worst = max(worst, np.abs(ck[:, :, n] - Sn).max())
+    return worst
+
+
 ALL_PINS = {
     "retrieval_identity": pin_retrieval_identity,
     "one_step_all_gates": pin_one_step_all_gates,
@@ -311,9 +330,11 @@ ALL_PINS = {
     "segment_chaining": pin_segment_chaining,
     "hand_example": pin_hand_example,
     "decode_is_one_token": pin_decode_is_one_token,
+    "checkpoints_are_prefix_states": pin_checkpoints_are_prefix_states,
 }
 
 # Residual bounds: fp64 arithmetic on O(1) values over a few tokens.
 TOL = {name: 1e-12 for name in ALL_PINS}
 TOL["segment_chaining"] = 0.0           # identical operations in identical order
+TOL["checkpoints_are_prefix_states"] = 0.0
 TOL["hand_example"] = 1e-14

@@ -113,6 +113,12 @@ FWD_CASES = [
     ("S_out_overlaps_g", _mod(S_out=fake(5, 256)), gdr2.ERR_INVALID_ARG),
     ("S_out_partial_S0", _mod(S_out=fake(6, 4096)), gdr2.ERR_INVALID_ARG),
     ("workspace_overlaps_q", _mod(workspace=fake(0, 4096)), gdr2.ERR_INVALID_ARG),
+    ("misaligned_S_chunks", _mod(S_chunks=fake(10, 8)), gdr2.ERR_INVALID_ARG),
+    ("S_chunks_overlaps_o", _mod(S_chunks=fake(7, 512)), gdr2.ERR_INVALID_ARG),
+    ("S_chunks_overlaps_k", _mod(S_chunks=fake(1, 1024)), gdr2.ERR_INVALID_ARG),
+    ("S_chunks_overlaps_S_out", _mod(S_chunks=fake(8, 64)), gdr2.ERR_INVALID_ARG),
+    ("S_chunks_overlaps_S0", _mod(S_chunks=fake(6, 0)), gdr2.ERR_INVALID_ARG),
+    ("workspace_overlaps_S_chunks", _mod(S_chunks=fake(10), workspace=fake(10, 4096)), gdr2.ERR_INVALID_ARG),
 ]
 
 

@@ -1,0 +1,67 @@
+"""GPU parity of the chunk-boundary state output (S_chunks of the C ABI):
+the state at the start of every chunk, against the fp64 oracle's checkpoints
+at the same token positions, normwise per (batch, head, chunk) slice with
+the dtype's tolerance.  Recording the checkpoints must not change o or the
+final state (bit for bit), and checkpoint 0 is S0 exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_86_amd import gdr2
+from gated_delta_rule_86_amd.inputs import Workload, draw, to_f64
+from tests.parity import TOL, normwise, to_dev
+
+pytestmark = pytest.mark.gpu
+NAMES = ("q", "k", "v", "b", "w", "g")
+
+CASES = [
+    # name, B, T, H, D, dtype, chunk, S0 std
+    ("f32_d64_c32", 1, 100, 2, 64, "f32", 32, 0.05),
+    ("f32_d64_c64", 2, 130, 1, 64, "f32", 64, 0.0),
+    ("bf16_d128_c64_ragged", 2, 150, 2, 128, "bf16", 64, 0.05),
+    ("bf16_d128_c32", 1, 96, 3, 128, "bf16", 32, 0.02),
+    ("bf16_d64_c64", 1, 64, 2, 64, "bf16", 64, 0.05),
+]
+
+
+@pytest.mark.parametrize("name,B,T,H,D,dtype,chunk,s0", CASES, ids=[c[0] for c in CASES])
+def test_chunk_states_match_oracle_checkpoints(name, B, T, H, D, dtype, chunk, s0):
+    inp = draw(Workload(name, "forward", B, T, H, D, dtype, "full", s0, chunk, 401))
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    o, S, ck = gdr2.forward(*args, S0=d["S0"], chunk=chunk, chunk_states=True)
+    o0, S0f = gdr2.forward(*args, S0=d["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    NC = -(-T // chunk)
+    assert ck.shape == (B, H, NC, D, D)
+    assert torch.equal(o, o0) and torch.equal(S, S0f)
+    if d["S0"] is not None:
+        assert torch.equal(ck[:, :, 0], d["S0"])
+    else:
+        assert not ck[:, :, 0].any()
+    _, _, ck_ref = oracle.forward_checkpoints(*(to_f64(inp[n]) for n in NAMES), every=chunk,
+                                              S0=to_f64(inp.get("S0")))
+    got = to_f64(ck).reshape(B, H * NC, D, D)
+    err = normwise(got, ck_ref.reshape(B, H * NC, D, D), "state")
+    print(f"{name}: chunk states {err:.2e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= TOL[dtype], f"{name}: chunk-state error {err:.3e}"
+
+
+def test_chunk_states_written_by_the_state_stage():
+    """PREP then STATE with a checkpoint buffer gives the one-call result."""
+    inp = draw(Workload("ck_stages", "forward", 1, 200, 2, 128, "bf16", "full", 0.05, 64, 402))
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    o1, S1, ck1 = gdr2.forward(*args, S0=d["S0"], chunk=64, chunk_states=True)
+    ws = torch.empty(gdr2.workspace_size(*args, chunk=64), dtype=torch.uint8, device="cuda")
+    o2, S2 = torch.empty_like(o1), torch.empty_like(S1)
+    ck2 = torch.full_like(ck1, float("nan"))
+    gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="prep",
+                 chunk_states=ck2)
+    assert torch.isnan(ck2).all()          # PREP does not touch the checkpoints
+    gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="state",
+                 chunk_states=ck2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(ck1, ck2)
