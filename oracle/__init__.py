@@ -66,6 +66,9 @@ def _bind(lib):
     lib.gdr2_oracle_forward_ckpt.restype = ctypes.c_int
     lib.gdr2_oracle_forward_ckpt.argtypes = [_L, _L, _L, _L, _L, _D, _D, _D, _D, _L, _D, _L,
                                              _D, _L, _D, _D, _D, _L, _D, ctypes.c_int]
+    lib.gdr2_oracle_backward.restype = ctypes.c_int
+    lib.gdr2_oracle_backward.argtypes = [_L, _L, _L, _L, _L, _D, _D, _D, _D, _L, _D, _L, _D, _L,
+                                         _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_int]
     lib.gdr2_oracle_decode.restype = ctypes.c_int
     lib.gdr2_oracle_decode.argtypes = [_L, _L, _L, _L, _D, _D, _D, _D, _L, _D, _L, _D, _L,
                                        _D, _D, ctypes.c_int]
@@ -139,6 +142,33 @@ def forward_checkpoints(q, k, v, b, w, g, every: int, S0=None, threads: int = 0,
     if rc != 0:
         raise RuntimeError(f"gdr2_oracle_forward_ckpt failed ({rc})")
     return o, S, ck
+
+
+def backward(q, k, v, b, w, g, dO, S0=None, dS_final=None, threads: int = 0, lib=None):
+    """Sequential fp64 gradients of a loss through the forward.
+
+    dO: dL/do [B,T,H,dv]; dS_final: dL/dS_final [B,H,dk,dv] or None (zero).
+    Returns a dict with dq, dk, dv, db, dw, dg (shaped like the inputs; a
+    width-1 gate's gradient is summed over its channels) and dS0.
+    """
+    lib = lib or load()
+    q, k, v, b, w, g, dO = (_f64(x) for x in (q, k, v, b, w, g, dO))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bw, ww, gw = _width(b, dk, "b"), _width(w, dv, "w"), _width(g, dk, "g")
+    assert dO.shape == (B, T, H, dv)
+    s0 = None if S0 is None else _f64(S0)
+    dsf = None if dS_final is None else _f64(dS_final)
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "db": np.zeros_like(b), "dw": np.zeros_like(w), "dg": np.zeros_like(g),
+           "dS0": np.zeros((B, H, dk, dv), dtype=np.float64)}
+    rc = lib.gdr2_oracle_backward(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(b), bw,
+                                  _ptr(w), ww, _ptr(g), gw, _ptr(s0), _ptr(dO), _ptr(dsf),
+                                  *(_ptr(out[n]) for n in ("dq", "dk", "dv", "db", "dw", "dg", "dS0")),
+                                  int(threads))
+    if rc != 0:
+        raise RuntimeError(f"gdr2_oracle_backward failed ({rc})")
+    return out
 
 
 def decode_step(state, q, k, v, b, w, g, threads: int = 0, lib=None):

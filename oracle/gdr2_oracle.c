@@ -176,6 +176,182 @@ int gdr2_oracle_forward_ckpt(long B, long T, long H, long dk, long dv,
 }
 
 /*
+ * Gradients of a scalar loss L through the forward, given dO = dL/do
+ * [B, T, H, d_v] and dS_final = dL/dS_T [B, H, d_k, d_v] (NULL: zero).
+ * Outputs dq, dk [B,T,H,d_k], dv [B,T,H,d_v], db [B,T,H,bw], dw [B,T,H,ww],
+ * dg [B,T,H,gw] and dS0 [B,H,d_k,d_v] (dS0 may be NULL).  A width-1 gate's
+ * gradient is the sum over the channels it is broadcast to.
+ *
+ * The reverse sweep walks the same per-token steps as gdr2_token backwards
+ * (chain rule, one step at a time), with Lam = dL/dS_t:
+ *   o_t = S_t^T q_t              ->  dq_t = S_t dO_t,  Lam += q_t dO_t^T
+ *   S_t = S' + k_t (u - r)^T     ->  c = Lam^T k_t (= dL/du = -dL/dr),
+ *                                    dk_t += Lam (u - r),  dS' = Lam
+ *   u = w_t . v_t                ->  dw = c . v_t,  dv = c . w_t
+ *   r = S'^T e,  e = b_t . k_t   ->  de = -S' c,  dS' += -e c^T
+ *                                    db = de . k_t,  dk_t += de . b_t
+ *   S' = D_t S_{t-1}             ->  dg_t[i] = sum_j dS'[i,j] S'[i,j],
+ *                                    Lam_{t-1} = D_t dS'
+ * S_{t-1} for the sweep comes from a stored copy of every state.
+ * Returns 0, -1 (bad arguments) or -2 (out of memory).
+ */
+int gdr2_oracle_backward(long B, long T, long H, long dk, long dv,
+                         const double *q, const double *k, const double *v,
+                         const double *b, long bw, const double *w, long ww,
+                         const double *g, long gw, const double *S0,
+                         const double *dO, const double *dS_final,
+                         double *dq, double *dk_out, double *dv_out, double *db,
+                         double *dw, double *dg, double *dS0, int threads)
+{
+    long bh, n_bh = B * H;
+    int failed = 0;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (!(bw == 1 || bw == dk) || !(ww == 1 || ww == dv) || !(gw == 1 || gw == dk))
+        return -1;
+    if (T > 0 && (!q || !k || !v || !b || !w || !g || !dO || !dq || !dk_out || !dv_out || !db ||
+                  !dw || !dg))
+        return -1;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(|| : failed)
+    for (bh = 0; bh < n_bh; ++bh) {
+        long bi = bh / H, h = bh % H, t, i, j;
+        const size_t ss = (size_t)(dk * dv);
+        double *St = (double *)malloc(sizeof(double) * ss * (size_t)(T + 1)); /* S_0 .. S_T */
+        double *Lam = (double *)malloc(sizeof(double) * ss);
+        double *Sp = (double *)malloc(sizeof(double) * ss);
+        double *r = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *c = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *de = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *ot = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!St || !Lam || !Sp || !r || !c || !de || !ot) {
+            free(St); free(Lam); free(Sp); free(r); free(c); free(de); free(ot);
+            failed = 1;
+            continue;
+        }
+        /* forward, keeping every state */
+        if (S0)
+            memcpy(St, S0 + bh * ss, sizeof(double) * ss);
+        else
+            memset(St, 0, sizeof(double) * ss);
+        for (t = 0; t < T; ++t) {
+            long row = (bi * T + t) * H + h;
+            memcpy(St + (t + 1) * ss, St + t * ss, sizeof(double) * ss);
+            gdr2_token(dk, dv, St + (t + 1) * ss, r, q + row * dk, k + row * dk, v + row * dv,
+                       b + row * bw, bw, w + row * ww, ww, g + row * gw, gw, ot);
+        }
+        /* reverse sweep */
+        if (dS_final)
+            memcpy(Lam, dS_final + bh * ss, sizeof(double) * ss);
+        else
+            memset(Lam, 0, sizeof(double) * ss);
+        for (t = T - 1; t >= 0; --t) {
+            long row = (bi * T + t) * H + h;
+            const double *qt = q + row * dk, *kt = k + row * dk, *vt = v + row * dv;
+            const double *bt = b + row * bw, *wt = w + row * ww, *gt = g + row * gw;
+            const double *dot = dO + row * dv;
+            const double *Sn = St + (t + 1) * ss, *Sprev = St + t * ss;
+            double *dqt = dq + row * dk, *dkt = dk_out + row * dk, *dvt = dv_out + row * dv;
+            double *dbt = db + row * bw, *dwt = dw + row * ww, *dgt = dg + row * gw;
+            /* readout */
+            for (i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (j = 0; j < dv; ++j)
+                    acc += Sn[i * dv + j] * dot[j];
+                dqt[i] = acc;
+                for (j = 0; j < dv; ++j)
+                    Lam[i * dv + j] += qt[i] * dot[j];
+            }
+            /* recompute S' = D_t S_{t-1} and r = S'^T e */
+            for (i = 0; i < dk; ++i) {
+                double d = exp(gw == 1 ? gt[0] : gt[i]);
+                for (j = 0; j < dv; ++j)
+                    Sp[i * dv + j] = d * Sprev[i * dv + j];
+            }
+            for (j = 0; j < dv; ++j)
+                r[j] = 0.0;
+            for (i = 0; i < dk; ++i) {
+                double e = (bw == 1 ? bt[0] : bt[i]) * kt[i];
+                for (j = 0; j < dv; ++j)
+                    r[j] += e * Sp[i * dv + j];
+            }
+            /* write term: c = Lam^T k, dk = Lam (u - r) */
+            for (j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (i = 0; i < dk; ++i)
+                    acc += Lam[i * dv + j] * kt[i];
+                c[j] = acc;
+            }
+            for (i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (j = 0; j < dv; ++j) {
+                    double u = (ww == 1 ? wt[0] : wt[j]) * vt[j];
+                    acc += Lam[i * dv + j] * (u - r[j]);
+                }
+                dkt[i] = acc;
+            }
+            /* u = w . v */
+            if (ww == 1) {
+                double acc = 0.0;
+                for (j = 0; j < dv; ++j)
+                    acc += c[j] * vt[j];
+                dwt[0] = acc;
+            } else {
+                for (j = 0; j < dv; ++j)
+                    dwt[j] = c[j] * vt[j];
+            }
+            for (j = 0; j < dv; ++j)
+                dvt[j] = c[j] * (ww == 1 ? wt[0] : wt[j]);
+            /* erase read: de = -S' c; e = b . k */
+            for (i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (j = 0; j < dv; ++j)
+                    acc += Sp[i * dv + j] * c[j];
+                de[i] = -acc;
+            }
+            if (bw == 1) {
+                double acc = 0.0;
+                for (i = 0; i < dk; ++i)
+                    acc += de[i] * kt[i];
+                dbt[0] = acc;
+            } else {
+                for (i = 0; i < dk; ++i)
+                    dbt[i] = de[i] * kt[i];
+            }
+            for (i = 0; i < dk; ++i)
+                dkt[i] += de[i] * (bw == 1 ? bt[0] : bt[i]);
+            /* dS' = Lam - e c^T; dg; Lam_{t-1} = D dS' */
+            if (gw == 1)
+                dgt[0] = 0.0;
+            for (i = 0; i < dk; ++i) {
+                double e = (bw == 1 ? bt[0] : bt[i]) * kt[i];
+                double d = exp(gw == 1 ? gt[0] : gt[i]);
+                double acc = 0.0;
+                for (j = 0; j < dv; ++j) {
+                    double dsp = Lam[i * dv + j] - e * c[j];
+                    acc += dsp * Sp[i * dv + j];
+                    Lam[i * dv + j] = d * dsp;
+                }
+                if (gw == 1)
+                    dgt[0] += acc;
+                else
+                    dgt[i] = acc;
+            }
+        }
+        if (dS0)
+            memcpy(dS0 + bh * ss, Lam, sizeof(double) * ss);
+        free(St); free(Lam); free(Sp); free(r); free(c); free(de); free(ot);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
  * One decode step for N independent sequences x H heads: the same token
  * update applied once per state, in place on state [N, H, d_k, d_v].
  * Token inputs are [N, H, .] (one token each); o is [N, H, d_v].

@@ -317,6 +317,71 @@ def pin_checkpoints_are_prefix_states(lib, seed=12):
     return worst
 
 
+def _loss(p, S0, dO, dSf, lib):
+    o, S = oracle.forward(**p, S0=S0, lib=lib)
+    return float((o * dO).sum() + (S * dSf).sum())
+
+
+def pin_backward_finite_differences(lib, seed=13):
+    """The backward against central finite differences of the loss
+    L = <dO, o> + <dS_final, S_final> through the oracle forward, for every
+    input (q, k, v, b, w, g, S0) and every gate width: an independent check
+    of the chain rule (a dropped term, a wrong sign or a transposed operand
+    in the backward changes some derivative by O(1))."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for bw, ww, gw in ((None, None, None), (1, 1, 1), (None, 1, None), (1, None, 1)):
+        p = rand_problem(rng, B=1, T=6, H=2, dk=4, dv=3, bw=bw, ww=ww, gw=gw)
+        S0 = rng.standard_normal((1, 2, 4, 3))
+        dO = rng.standard_normal((1, 6, 2, 3))
+        dSf = rng.standard_normal((1, 2, 4, 3))
+        gr = oracle.backward(**p, dO=dO, S0=S0, dS_final=dSf, lib=lib)
+        grads = {"q": gr["dq"], "k": gr["dk"], "v": gr["dv"], "b": gr["db"], "w": gr["dw"],
+                 "g": gr["dg"], "S0": gr["dS0"]}
+        h = 1e-6
+        for name, an in grads.items():
+            base = S0 if name == "S0" else p[name]
+            fd = np.zeros_like(base)
+            for idx in np.ndindex(base.shape):
+                x = base.copy()
+                x[idx] += h
+                lp = _loss(p if name == "S0" else {**p, name: x}, x if name == "S0" else S0, dO, dSf, lib)
+                x[idx] -= 2 * h
+                lm = _loss(p if name == "S0" else {**p, name: x}, x if name == "S0" else S0, dO, dSf, lib)
+                fd[idx] = (lp - lm) / (2 * h)
+            worst = max(worst, float(np.abs(fd - an).max() / max(np.abs(fd).max(), 1.0)))
+    return worst
+
+
+def pin_backward_linear_attention(lib, seed=14):
+    """b = 0, w = 1, g = 0 (plain linear attention, o_t = S0^T q_t +
+    sum_{s<=t} (q_t . k_s) v_s): the closed-form gradients
+    dq_t = S0 dO_t + sum_{s<=t} k_s (v_s . dO_t), dv_s = sum_{t>=s} (q_t . k_s) dO_t,
+    dk_s = sum_{t>=s} q_t (v_s . dO_t), dS0 = sum_t q_t dO_t^T."""
+    rng = np.random.default_rng(seed)
+    p = rand_problem(rng, B=2, T=7, H=2, dk=5, dv=4)
+    p["b"] = np.zeros_like(p["b"])
+    p["w"] = np.ones_like(p["w"])
+    p["g"] = np.zeros_like(p["g"])
+    S0 = rng.standard_normal((2, 2, 5, 4))
+    dO = rng.standard_normal((2, 7, 2, 4))
+    gr = oracle.backward(**p, dO=dO, S0=S0, lib=lib)
+    q, k, v = p["q"], p["k"], p["v"]
+    worst = 0.0
+    for bi in range(2):
+        for h in range(2):
+            Q, K, V, G = q[bi, :, h], k[bi, :, h], v[bi, :, h], dO[bi, :, h]
+            Lt = np.tril(np.ones((7, 7)))
+            A = (Q @ K.T) * Lt                  # A[t,s] = q_t . k_s, s <= t
+            dq = G @ S0[bi, h].T + ((G @ V.T) * Lt) @ K
+            dv = A.T @ G
+            dk = ((G @ V.T) * Lt).T @ Q
+            dS0 = Q.T @ G
+            worst = max(worst, np.abs(gr["dq"][bi, :, h] - dq).max(), np.abs(gr["dv"][bi, :, h] - dv).max(),
+                        np.abs(gr["dk"][bi, :, h] - dk).max(), np.abs(gr["dS0"][bi, h] - dS0).max())
+    return worst
+
+
 ALL_PINS = {
     "retrieval_identity": pin_retrieval_identity,
     "one_step_all_gates": pin_one_step_all_gates,
@@ -331,10 +396,13 @@ ALL_PINS = {
     "hand_example": pin_hand_example,
     "decode_is_one_token": pin_decode_is_one_token,
     "checkpoints_are_prefix_states": pin_checkpoints_are_prefix_states,
+    "backward_finite_differences": pin_backward_finite_differences,
+    "backward_linear_attention": pin_backward_linear_attention,
 }
 
 # Residual bounds: fp64 arithmetic on O(1) values over a few tokens.
 TOL = {name: 1e-12 for name in ALL_PINS}
 TOL["segment_chaining"] = 0.0           # identical operations in identical order
 TOL["checkpoints_are_prefix_states"] = 0.0
+TOL["backward_finite_differences"] = 1e-7   # central differences, h = 1e-6, in fp64
 TOL["hand_example"] = 1e-14

@@ -37,6 +37,21 @@ MUTANTS = [
      "o[j] += q[i] * S[i * dv + j];", "o[j] += k[i] * S[i * dv + j];"),
     ("readout_transposed",
      "o[j] += q[i] * S[i * dv + j];", "o[j] += q[j < dk ? j : 0] * S[i * dv + (i < dv ? i : 0)];"),
+    # the backward sweep
+    ("bwd_readout_uses_old_state",
+     "acc += Sn[i * dv + j] * dot[j];", "acc += Sprev[i * dv + j] * dot[j];"),
+    ("bwd_erase_read_sign", "de[i] = -acc;", "de[i] = acc;"),
+    ("bwd_erase_outer_sign",
+     "double dsp = Lam[i * dv + j] - e * c[j];", "double dsp = Lam[i * dv + j] + e * c[j];"),
+    ("bwd_erase_outer_dropped",
+     "double dsp = Lam[i * dv + j] - e * c[j];", "double dsp = Lam[i * dv + j];"),
+    ("bwd_decay_not_propagated", "Lam[i * dv + j] = d * dsp;", "Lam[i * dv + j] = dsp;"),
+    ("bwd_dg_uses_undecayed", "acc += dsp * Sp[i * dv + j];", "acc += dsp * Sprev[i * dv + j];"),
+    ("bwd_dk_drops_read",
+     "acc += Lam[i * dv + j] * (u - r[j]);", "acc += Lam[i * dv + j] * u;"),
+    ("bwd_dv_drops_gate",
+     "dvt[j] = c[j] * (ww == 1 ? wt[0] : wt[j]);", "dvt[j] = c[j];"),
+    ("bwd_db_drops_key", "dbt[i] = de[i] * kt[i];", "dbt[i] = de[i];"),
 ]
 
 
