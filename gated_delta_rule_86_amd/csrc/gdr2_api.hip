@@ -218,6 +218,90 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
     return GDR2_OK;
 }
 
+// The chunked backward: every check of the forward's inputs plus the
+// gradient buffers.  Outputs may overlap nothing, except that dS0 may be the
+// same pointer as dS_final.
+gdr2_status validate_backward(const gdr2_bwd_args* a)
+{
+    if (!a)
+        return fail(GDR2_ERR_INVALID_ARG, "args is NULL");
+    if (a->B < 0 || a->T < 0 || a->H < 0)
+        return fail(GDR2_ERR_INVALID_ARG, "B, T, H must be >= 0");
+    int64_t bh, rows;
+    if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->T, &rows))
+        return fail(GDR2_ERR_INVALID_ARG, "B*T*H overflows int64");
+    gdr2_status s = check_common(rows, a->Dk, a->Dv, a->dtype, a->b_width, a->w_width, a->g_width);
+    if (s != GDR2_OK)
+        return s;
+    if (a->reserved != 0)
+        return fail(GDR2_ERR_INVALID_ARG, "reserved field must be 0");
+    if (a->chunk != 64)
+        return fail(GDR2_ERR_UNSUPPORTED, "the backward supports chunk 64 only (got %d)", a->chunk);
+    const int64_t nchunks = (a->T + 63) / 64;
+    int64_t nrec, state_bytes, ck_bytes;
+    // the widest launch has two workgroups per chunk record
+    if (!mul_ok(bh, nchunks, &nrec) || nrec > (int64_t)INT32_MAX / 2)
+        return fail(GDR2_ERR_UNSUPPORTED, "too many chunks for one launch");
+    if (!mul_ok(bh, a->Dk * a->Dv * 4, &state_bytes) || !mul_ok(state_bytes, nchunks, &ck_bytes))
+        return fail(GDR2_ERR_INVALID_ARG, "state size overflows int64");
+    if (bh == 0)
+        return GDR2_OK;
+    const int64_t e = elt_bytes(a->dtype);
+    int64_t tmp;
+    if (!mul_ok(rows, a->Dk * 4, &tmp) || !mul_ok(rows, a->Dv * 4, &tmp))
+        return fail(GDR2_ERR_INVALID_ARG, "tensor size overflows int64");
+    const int64_t nk = rows * a->Dk, nv = rows * a->Dv;
+    const Range ins[] = {range("q", a->q, nk * e), range("k", a->k, nk * e), range("v", a->v, nv * e),
+                         range("b", a->b, rows * a->b_width * e), range("w", a->w, rows * a->w_width * e),
+                         range("g", a->g, rows * a->g_width * 4), range("S_chunks", a->S_chunks, ck_bytes),
+                         range("dO", a->dO, nv * e), range("dS_final", a->dS_final, state_bytes)};
+    const Range outs[] = {range("dq", a->dq, nk * 4), range("dk", a->dk, nk * 4), range("dv", a->dv, nv * 4),
+                          range("db", a->db, rows * a->b_width * 4), range("dw", a->dw, rows * a->w_width * 4),
+                          range("dg", a->dg, rows * a->g_width * 4), range("dS0", a->dS0, state_bytes)};
+    const int n_ins = 9, n_outs = 7;
+    const bool need_tokens = rows > 0;
+    for (int i = 0; i < n_ins; ++i) {
+        const bool optional = i == 8 || (!need_tokens && i < 8);
+        if (!ins[i].lo && !optional)
+            return fail(GDR2_ERR_INVALID_ARG, "%s is NULL", ins[i].name);
+        if (ins[i].lo && (ins[i].lo & 15u))
+            return fail(GDR2_ERR_INVALID_ARG, "%s is not 16-byte aligned", ins[i].name);
+    }
+    for (int i = 0; i < n_outs; ++i) {
+        const bool optional = i == 6 || !need_tokens;
+        if (!outs[i].lo && !optional)
+            return fail(GDR2_ERR_INVALID_ARG, "%s is NULL", outs[i].name);
+        if (outs[i].lo && (outs[i].lo & 15u))
+            return fail(GDR2_ERR_INVALID_ARG, "%s is not 16-byte aligned", outs[i].name);
+    }
+    for (int i = 0; i < n_outs; ++i) {
+        for (int j = 0; j < n_ins; ++j) {
+            const bool alias = i == 6 && j == 8 && outs[i].lo == ins[j].lo;
+            if (!alias && overlaps(outs[i], ins[j]))
+                return fail(GDR2_ERR_INVALID_ARG, "%s overlaps input %s", outs[i].name, ins[j].name);
+        }
+        for (int j = i + 1; j < n_outs; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(GDR2_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    const size_t need = gdr2::backward_workspace_bytes(*a);
+    if (need > 0) {
+        if (!a->workspace || a->workspace_bytes < need)
+            return fail(GDR2_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                        a->workspace ? a->workspace_bytes : (size_t)0);
+        if (!aligned16(a->workspace))
+            return fail(GDR2_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+        const Range ws = range("workspace", a->workspace, (int64_t)need);
+        for (const auto& r : ins)
+            if (overlaps(ws, r))
+                return fail(GDR2_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+        for (const auto& r : outs)
+            if (overlaps(ws, r))
+                return fail(GDR2_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+    }
+    return GDR2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +336,30 @@ gdr2_status gdr2_forward_chunked(const gdr2_fwd_args* a, void* stream_)
                          "state copy");
     }
     return hip_check(gdr2::launch_forward_staged(*a, stream), stream, "chunked forward");
+}
+
+size_t gdr2_backward_workspace_size(const gdr2_bwd_args* a)
+{
+    if (!a || a->B < 0 || a->T < 0 || a->H < 0)
+        return 0;
+    int64_t bh, rows;
+    if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->T, &rows) || rows == 0)
+        return 0;
+    if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128) || a->chunk != 64 ||
+        (a->dtype != GDR2_F32 && a->dtype != GDR2_BF16))
+        return 0;
+    return gdr2::backward_workspace_bytes(*a);
+}
+
+gdr2_status gdr2_backward_chunked(const gdr2_bwd_args* a, void* stream_)
+{
+    gdr2_status s = validate_backward(a);
+    if (s != GDR2_OK)
+        return s;
+    if (a->B * a->H == 0)
+        return GDR2_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    return hip_check(gdr2::launch_backward(*a, stream), stream, "chunked backward");
 }
 
 gdr2_status gdr2_decode_step(const gdr2_decode_args* a, void* stream_)

@@ -43,10 +43,22 @@ class DecodeArgs(ctypes.Structure):
                 ("g", _vp), ("state", _vp), ("o", _vp)]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("B", _c_i64), ("T", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
+                ("chunk", _c_i32), ("dtype", _c_i32),
+                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("reserved", _c_i32),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp), ("g", _vp),
+                ("S_chunks", _vp), ("dO", _vp), ("dS_final", _vp),
+                ("dq", _vp), ("dk", _vp), ("dv", _vp), ("db", _vp), ("dw", _vp), ("dg", _vp),
+                ("dS0", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
 # Every symbol include/gdr2.h declares (checked by the tests).
 EXPORTS = ("gdr2_forward_workspace_size", "gdr2_forward_chunked", "gdr2_decode_step",
+           "gdr2_backward_workspace_size", "gdr2_backward_chunked",
            "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version")
-ABI_VERSION = 2
+ABI_VERSION = 3
+BWD_CHUNK = 64
 
 
 class Gdr2Error(RuntimeError):
@@ -75,6 +87,10 @@ def load_library(path: str = LIB_PATH):
         lib.gdr2_forward_chunked.argtypes = [ctypes.POINTER(FwdArgs), _vp]
         lib.gdr2_decode_step.restype = ctypes.c_int
         lib.gdr2_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        lib.gdr2_backward_workspace_size.restype = ctypes.c_size_t
+        lib.gdr2_backward_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+        lib.gdr2_backward_chunked.restype = ctypes.c_int
+        lib.gdr2_backward_chunked.argtypes = [ctypes.POINTER(BwdArgs), _vp]
         lib.gdr2_status_string.restype = ctypes.c_char_p
         lib.gdr2_status_string.argtypes = [ctypes.c_int]
         lib.gdr2_last_error.restype = ctypes.c_char_p
@@ -199,3 +215,57 @@ def decode_step(state, q, k, v, b, w, g, out=None):
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib, lib.gdr2_decode_step(ctypes.byref(a), stream))
     return out
+
+
+def bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final=None, grads=None, dS0=None,
+             workspace=None, chunk: int = BWD_CHUNK) -> BwdArgs:
+    """grads: (dq, dk, dv, db, dw, dg) or None."""
+    B, T, H, Dk = q.shape
+    a = BwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, v.shape[-1]
+    a.chunk, a.dtype = chunk, _dtype_code(q)
+    a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
+    a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
+    a.S_chunks, a.dO, a.dS_final, a.dS0 = _ptr(S_chunks), _ptr(dO), _ptr(dS_final), _ptr(dS0)
+    if grads is not None:
+        a.dq, a.dk, a.dv, a.db, a.dw, a.dg = (_ptr(x) for x in grads)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def backward_workspace_size(q, k, v, b, w, g) -> int:
+    lib = load_library()
+    return int(lib.gdr2_backward_workspace_size(ctypes.byref(bwd_args(q, k, v, b, w, g, None, None))))
+
+
+def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grads=None,
+             dS0=None, want_dS0: bool = True):
+    """Chunked backward (chunk 64).  Inputs as for ``forward``; S_chunks is
+    the float32 [B,H,ceil(T/64),Dk,Dv] chunk-start states of a chunk-64
+    forward; dO [B,T,H,Dv] in the inputs' dtype; dS_final float32
+    [B,H,Dk,Dv] or None.  Returns a dict of float32 gradients dq, dk, dv,
+    db, dw, dg (shaped like their inputs) and dS0 (None unless want_dS0 or
+    given)."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w), ("dO", dO)):
+        _req(t, n, q.dtype)
+    _req(g, "g", torch.float32)
+    _req(S_chunks, "S_chunks", torch.float32)
+    if dS_final is not None:
+        _req(dS_final, "dS_final", torch.float32)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if grads is None:
+        grads = tuple(torch.empty(x.shape, dtype=torch.float32, device=q.device) for x in (q, k, v, b, w, g))
+    if dS0 is None and want_dS0:
+        dS0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    a = bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final, grads, dS0)
+    need = lib.gdr2_backward_workspace_size(ctypes.byref(a))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib, lib.gdr2_backward_chunked(ctypes.byref(a), stream))
+    return dict(zip(("dq", "dk", "dv", "db", "dw", "dg"), grads), dS0=dS0)

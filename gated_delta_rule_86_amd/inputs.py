@@ -113,6 +113,19 @@ def draw_decode_tokens(wl: Workload, step: int) -> dict:
     return draw(wl.with_(s0_std=0.0), seed=wl.seed + 1000 * (step + 1))
 
 
+def draw_cotangents(wl: Workload, dS_std: float = 1.0, seed: int | None = None) -> dict:
+    """Seeded loss cotangents for the backward: dO ~ N(0,1) [B,T,H,D] in the
+    workload dtype, dS_final ~ N(0, dS_std^2) float32 [B,H,D,D] (None when
+    dS_std == 0).  Seed wl.seed + 500_000 unless given."""
+    rng = np.random.default_rng(wl.seed + 500_000 if seed is None else seed)
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    dO = torch.from_numpy(rng.standard_normal((B, T, H, D))).to(TORCH_DTYPES[wl.dtype])
+    dS = None
+    if dS_std > 0:
+        dS = torch.from_numpy(rng.standard_normal((B, H, D, D)) * dS_std).to(torch.float32)
+    return {"dO": dO, "dS_final": dS}
+
+
 def select_heads(inp: dict, pairs) -> dict:
     """Restrict forward inputs to the given (b, h) pairs, each as its own
     batch row of one head: every (b, h) recurrence is independent."""
@@ -121,6 +134,10 @@ def select_heads(inp: dict, pairs) -> dict:
         out[n] = torch.stack([inp[n][b, :, h:h + 1] for b, h in pairs])
     S0 = inp.get("S0")
     out["S0"] = None if S0 is None else torch.stack([S0[b, h:h + 1] for b, h in pairs])
+    for n in ("dO", "dS_final"):      # cotangents, when present
+        t = inp.get(n)
+        if t is not None:
+            out[n] = torch.stack([t[b, :, h:h + 1] if n == "dO" else t[b, h:h + 1] for b, h in pairs])
     return out
 
 

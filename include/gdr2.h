@@ -1,5 +1,5 @@
 /*
- * gdr2.h -- C ABI of the Gated DeltaNet-2 forward library for AMD MI355X
+ * gdr2.h -- C ABI of the Gated DeltaNet-2 library for AMD MI355X
  * (gfx950).  Plain C: no C++ or HIP types.  Streams are passed as void*
  * holding a hipStream_t (NULL = the default stream).
  *
@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 2
+#define GDR2_ABI_VERSION 3
 
 typedef enum gdr2_status {
     GDR2_OK = 0,
@@ -163,6 +163,47 @@ typedef struct gdr2_decode_args {
     void *o;
 } gdr2_decode_args;
 
+/*
+ * Arguments of the chunked backward: the gradients of a loss L with respect
+ * to every input of the chunked forward, given dL/do and dL/dS_final.  The
+ * derivatives are those of the update and readout above (page "Gated
+ * DeltaNet-2 ...", section "Gated Delta Rule-2 업데이트 수식"), taken
+ * through the chunked WY form of section "효율적 구현"; the state at every
+ * chunk start comes from the forward (S_chunks), so no state is recomputed.
+ *   q, k, v, b, w, g   the forward's inputs, same shapes, dtype and widths
+ *   S_chunks [B, H, NC, Dk, Dv] fp32, NC = ceil(T / 64): the chunk-start
+ *                      states the forward wrote with chunk = 64 (any exact
+ *                      source of the states before tokens 0, 64, 128, ...
+ *                      serves); S_chunks[:, :, 0] is the forward's S0
+ *   dO       [B, T, H, Dv]  dtype  dL/do
+ *   dS_final [B, H, Dk, Dv] fp32   dL/dS_final, may be NULL (zero)
+ * Outputs, all fp32, written in full (no accumulation into them):
+ *   dq, dk   [B, T, H, Dk]     dv [B, T, H, Dv]
+ *   db       [B, T, H, b_width]   dw [B, T, H, w_width]   dg [B, T, H, g_width]
+ *            (a width-1 gate gets the sum over the channels it broadcasts to)
+ *   dS0      [B, H, Dk, Dv], may be NULL: dL/dS0
+ * No output may overlap any input, another output or the workspace.
+ * Supported set: Dk == Dv in {64, 128}; chunk == 64; dtype F32 or BF16;
+ * B, T, H >= 0 (T == 0 writes dS_final, or zeros, to dS0).  Anything else
+ * returns GDR2_ERR_UNSUPPORTED.  All arithmetic is fp32.
+ */
+typedef struct gdr2_bwd_args {
+    int64_t B, T, H, Dk, Dv;
+    int32_t chunk;        /* must be 64 */
+    int32_t dtype;        /* gdr2_dtype of q, k, v, b, w, dO */
+    int32_t b_width, w_width, g_width;
+    int32_t reserved;     /* must be 0 */
+    const void *q, *k, *v, *b, *w;
+    const float *g;
+    const float *S_chunks;
+    const void *dO;
+    const float *dS_final;
+    float *dq, *dk, *dv, *db, *dw, *dg;
+    float *dS0;
+    void *workspace;      /* device memory, >= gdr2_backward_workspace_size() bytes */
+    size_t workspace_bytes;
+} gdr2_bwd_args;
+
 /* Bytes of device workspace gdr2_forward_chunked needs for these arguments
  * (pointers are not read).  0 when none is needed or the arguments are
  * invalid or unsupported. */
@@ -170,6 +211,14 @@ size_t gdr2_forward_workspace_size(const gdr2_fwd_args *args);
 
 /* Chunked forward: o for every token and the final state S_out. */
 gdr2_status gdr2_forward_chunked(const gdr2_fwd_args *args, void *stream);
+
+/* Bytes of device workspace gdr2_backward_chunked needs for these
+ * arguments (pointers are not read).  0 when none is needed or the arguments
+ * are invalid or unsupported. */
+size_t gdr2_backward_workspace_size(const gdr2_bwd_args *args);
+
+/* Chunked backward: every input gradient and dS0. */
+gdr2_status gdr2_backward_chunked(const gdr2_bwd_args *args, void *stream);
 
 /* One recurrent decode step for every (sequence, head) state. */
 gdr2_status gdr2_decode_step(const gdr2_decode_args *args, void *stream);

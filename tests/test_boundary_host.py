@@ -234,3 +234,105 @@ def test_python_wrappers_refuse_host_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         gdr2.forward(x, x, x, x, x, x)
+
+
+def good_bwd(B=2, T=100, H=3, D=128, dtype=gdr2.BF16, widths=None):
+    a = gdr2.BwdArgs()
+    a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, D, D
+    a.chunk, a.dtype = 64, dtype
+    a.b_width, a.w_width, a.g_width = widths or (D, D, D)
+    a.q, a.k, a.v, a.b, a.w, a.g = (fake(i) for i in range(6))
+    a.S_chunks, a.dO, a.dS_final = fake(6), fake(7), fake(8)
+    a.dq, a.dk, a.dv, a.db, a.dw, a.dg = (fake(i) for i in range(9, 15))
+    a.dS0, a.workspace = fake(15), fake(16)
+    return a
+
+
+def call_bwd(lib, a, ws_ok=True):
+    if ws_ok:
+        a.workspace_bytes = lib.gdr2_backward_workspace_size(ctypes.byref(a))
+    return lib.gdr2_backward_chunked(ctypes.byref(a), None)
+
+
+BWD_CASES = [
+    ("negative_H", _mod(H=-1), gdr2.ERR_INVALID_ARG),
+    ("head_dim_96", _mod(Dk=96, Dv=96, b_width=96, w_width=96, g_width=96), gdr2.ERR_UNSUPPORTED),
+    ("chunk_32", _mod(chunk=32), gdr2.ERR_UNSUPPORTED),
+    ("bad_dtype", _mod(dtype=2), gdr2.ERR_INVALID_ARG),
+    ("reserved_set", _mod(reserved=1), gdr2.ERR_INVALID_ARG),
+    ("bad_w_width", _mod(w_width=2), gdr2.ERR_INVALID_ARG),
+    ("null_S_chunks", _mod(S_chunks=None), gdr2.ERR_INVALID_ARG),
+    ("null_dO", _mod(dO=None), gdr2.ERR_INVALID_ARG),
+    ("null_dg", _mod(dg=None), gdr2.ERR_INVALID_ARG),
+    ("null_dq", _mod(dq=None), gdr2.ERR_INVALID_ARG),
+    ("misaligned_dO", _mod(dO=fake(7, 2)), gdr2.ERR_INVALID_ARG),
+    ("misaligned_dS0", _mod(dS0=fake(15, 4)), gdr2.ERR_INVALID_ARG),
+    ("misaligned_dS_final", _mod(dS_final=fake(8, 8)), gdr2.ERR_INVALID_ARG),
+    ("dq_overlaps_q", _mod(dq=fake(0, 256)), gdr2.ERR_INVALID_ARG),
+    ("dk_overlaps_dq", _mod(dk=fake(9, 1024)), gdr2.ERR_INVALID_ARG),
+    ("dg_overlaps_S_chunks", _mod(dg=fake(6, 4096)), gdr2.ERR_INVALID_ARG),
+    ("dS0_overlaps_dO", _mod(dS0=fake(7, 16)), gdr2.ERR_INVALID_ARG),
+    ("dS0_partial_dS_final", _mod(dS0=fake(8, 4096)), gdr2.ERR_INVALID_ARG),
+    ("workspace_overlaps_dw", _mod(workspace=fake(13, 4096)), gdr2.ERR_INVALID_ARG),
+    ("workspace_overlaps_S_chunks", _mod(workspace=fake(6, 65536)), gdr2.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mod,status", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_rejects(lib, name, mod, status):
+    a = good_bwd()
+    mod(a)
+    got = call_bwd(lib, a)
+    assert got == status, (name, got, lib.gdr2_last_error())
+    assert lib.gdr2_last_error()
+
+
+def test_backward_null_args_and_workspace(lib):
+    assert lib.gdr2_backward_chunked(None, None) == gdr2.ERR_INVALID_ARG
+    assert lib.gdr2_backward_workspace_size(None) == 0
+    a = good_bwd()
+    need = lib.gdr2_backward_workspace_size(ctypes.byref(a))
+    assert need > 0
+    a.workspace_bytes = need - 1
+    assert lib.gdr2_backward_chunked(ctypes.byref(a), None) == gdr2.ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = None, need
+    assert lib.gdr2_backward_chunked(ctypes.byref(a), None) == gdr2.ERR_WORKSPACE
+
+
+def test_backward_workspace_size_formula(lib):
+    # per chunk record, fp32, each array padded to 256 bytes: 16 arrays of
+    # [C][D] (G, E, U, E~, Q~, K^, W, U~, Delta, dDelta, dQ~, dK^, dW, dU,
+    # dE~, dO), 6 of [C][C] (P, X, dP, dX, a product, dM), gamma [D] and the
+    # chunk-end state gradient [D][D]
+    def al(x):
+        return (x + 255) // 256 * 256
+    for (B, T, H, D) in [(2, 100, 3, 128), (1, 64, 1, 64), (8, 4096, 16, 128)]:
+        a = good_bwd(B=B, T=T, H=H, D=D)
+        nrec = B * H * -(-T // 64)
+        want = 16 * al(nrec * 64 * D * 4) + 6 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * D * D * 4)
+        assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == want
+    assert lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(T=0))) == 0
+    a = good_bwd()
+    a.chunk = 32
+    assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_backward_empty_is_a_noop(lib):
+    for kw in (dict(B=0), dict(H=0)):
+        assert call_bwd(lib, good_bwd(**kw)) == gdr2.OK
+    a = good_bwd(T=0)
+    a.dS0 = a.dS_final             # in place with no tokens: nothing to write
+    assert call_bwd(lib, a) == gdr2.OK
+    a = good_bwd(T=0)
+    a.dS0 = None
+    assert call_bwd(lib, a) == gdr2.OK
+
+
+def test_backward_accepts_inplace_state_gradient(lib):
+    # dS0 == dS_final is allowed; fail later on purpose (missing dv) to show
+    # validation got past the aliasing rule without launching
+    a = good_bwd()
+    a.dS0 = a.dS_final
+    a.dv = None
+    assert call_bwd(lib, a) == gdr2.ERR_INVALID_ARG
+    assert b"dv is NULL" in lib.gdr2_last_error()
