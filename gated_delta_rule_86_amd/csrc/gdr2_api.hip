@@ -239,8 +239,8 @@ gdr2_status validate_backward(const gdr2_bwd_args* a)
         return fail(GDR2_ERR_UNSUPPORTED, "the backward supports chunk 64 only (got %d)", a->chunk);
     const int64_t nchunks = (a->T + 63) / 64;
     int64_t nrec, state_bytes, ck_bytes;
-    // the widest launch has two workgroups per chunk record
-    if (!mul_ok(bh, nchunks, &nrec) || nrec > (int64_t)INT32_MAX / 2)
+    // the widest launch has four workgroups per chunk record
+    if (!mul_ok(bh, nchunks, &nrec) || nrec > (int64_t)INT32_MAX / 4)
         return fail(GDR2_ERR_UNSUPPORTED, "too many chunks for one launch");
     if (!mul_ok(bh, a->Dk * a->Dv * 4, &state_bytes) || !mul_ok(state_bytes, nchunks, &ck_bytes))
         return fail(GDR2_ERR_INVALID_ARG, "state size overflows int64");

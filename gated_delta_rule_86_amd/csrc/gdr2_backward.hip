@@ -57,10 +57,12 @@ struct BwdLayout {
     size_t gam;
     // [D][D] per record: state gradient at every chunk end
     size_t Lam;
+    // scan operand fragments (ScanFrags), rec_bytes per record
+    size_t SF;
     size_t total;
 };
 
-BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D)
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes)
 {
     BwdLayout L;
     L.nrec = B * H * cdiv(T, BC);
@@ -82,6 +84,8 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D)
     o += d1;
     L.Lam = o;
     o += dd;
+    L.SF = o;
+    o += a64((size_t)L.nrec * rec_bytes / 4);
     L.total = o * sizeof(float);
     return L;
 }
@@ -94,7 +98,7 @@ struct BwdArgs {
     const float* dS_final;
     float *dq, *dk, *dv, *db, *dw, *dg, *dS0;
     int bw, ww, gw;
-    int64_t T, H, NC, nrec;
+    int64_t T, H, NC, nrec, nbh;
     float* ws;           // workspace base (fp32)
     BwdLayout L;
 };
@@ -248,84 +252,259 @@ __global__ __launch_bounds__(NTB) void bwd_dout_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_scan: state gradient through the chunks in reverse, per (sequence,
-// head, 32 value columns).  Lam [D][32] lives in LDS.
+// Operands of the reverse scan, in MFMA fragment order and the input
+// precision E.  A 1 KB fragment holds 16 rows x KB contraction indices: lane
+// l keeps row l%16 and, inside the KB block, k = 4(l/16)..+3 (bf16: also
+// 16+4(l/16)..+3), 16 contiguous bytes per lane -- what Mma<E>::load reads
+// from a row-major matrix, so an accumulator tile is directly a B operand.
+// Per chunk record:
+//   K   K^      rows s (C/16 tiles)           x k = key channel (D/KB steps)
+//   P   P^T     rows s                        x k = token (C/KB steps; the
+//               part below the diagonal is stored as zeros)
+//   Q   Q~^T    rows = key channel (D/16)     x k = token
+//   W   -W^T    same
+//   O   dO^T    rows = value column (D/16)    x k = token
 // ---------------------------------------------------------------------------
-constexpr int SV = 32;   // value columns per workgroup
+template <typename E, int D>
+struct ScanFrags {
+    static constexpr int KB = Mma<E>::KB, KT = KB / 16, NB = BC / 16;
+    static constexpr int NKS = D / KB, NKC = BC / KB, DT = D / 16;
+    static constexpr size_t FRAG = 1024;
+    static constexpr size_t K_BYTES = (size_t)NB * NKS * FRAG;    // C*D*sizeof(E)
+    static constexpr size_t P_BYTES = (size_t)NB * NKC * FRAG;    // C*C*sizeof(E)
+    static constexpr size_t T_BYTES = (size_t)DT * NKC * FRAG;    // C*D*sizeof(E)
+    static constexpr size_t OFF_K = 0, OFF_P = K_BYTES, OFF_Q = OFF_P + P_BYTES, OFF_W = OFF_Q + T_BYTES,
+                            OFF_O = OFF_W + T_BYTES, REC = OFF_O + T_BYTES;
+    static constexpr int NFRAG = (int)(REC / FRAG);
+    static_assert(K_BYTES == (size_t)BC * D * sizeof(E), "fragment size");
+    static_assert(REC == (size_t)(4 * BC * D + BC * BC) * sizeof(E), "record size used for the workspace");
+};
 
-template <int D>
+// Contraction index held in slot j (0 .. 16/sizeof(E)-1) by lane group gq.
+template <typename E> __device__ __forceinline__ int slot_k(int gq, int j);
+template <> __device__ __forceinline__ int slot_k<bf16>(int gq, int j) { return (j < 4 ? 0 : 12) + 4 * gq + j; }
+template <> __device__ __forceinline__ int slot_k<float>(int gq, int j) { return 4 * gq + j; }
+
+// One workgroup per chunk record: the fp32 rows the prep kernel and the dO
+// copy wrote, re-laid into fragments.  Item (fragment, lane) -> 16 bytes.
+template <typename E, int D>
+__global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
+{
+    typedef ScanFrags<E, D> F;
+    constexpr int C = BC, NV = 16 / (int)sizeof(E);
+    const int64_t r = blockIdx.x;
+    const float* ws = a.ws;
+    const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
+    unsigned char* out = reinterpret_cast<unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC;
+    for (int it = threadIdx.x; it < F::NFRAG * 64; it += NTB) {
+        const int f = it / 64, lane = it % 64, gq = lane / 16, rl = lane % 16;
+        const float* src;
+        int row, m;
+        int64_t rs, ks;            // element (row, k) at src[row * rs + k * ks]
+        float sign = 1.f;
+        if (f < F::NB * F::NKS) {                       // K^ [s][i]
+            row = 16 * (f / F::NKS) + rl; m = f % F::NKS;
+            src = ws + a.L.Kh + cdo; rs = D; ks = 1;
+        } else if (f < F::NB * (F::NKS + F::NKC)) {     // P^T [s][t] = P[t][s]
+            const int g = f - F::NB * F::NKS;
+            row = 16 * (g / F::NKC) + rl; m = g % F::NKC;
+            src = ws + a.L.P + cco; rs = 1; ks = C;
+        } else {                                        // Q~^T, -W^T, dO^T: [i][t] = X[t][i]
+            const int g = f - F::NB * (F::NKS + F::NKC), which = g / (F::DT * F::NKC), h = g % (F::DT * F::NKC);
+            row = 16 * (h / F::NKC) + rl; m = h % F::NKC;
+            src = ws + cdo + (which == 0 ? a.L.Qt : which == 1 ? a.L.W : a.L.dO);
+            sign = which == 1 ? -1.f : 1.f;
+            rs = 1; ks = D;
+        }
+        float x[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            x[j] = sign * src[row * rs + (int64_t)(m * F::KB + slot_k<E>(gq, j)) * ks];
+        unsigned char* dst = out + (size_t)f * F::FRAG + lane * 16;
+        if constexpr (sizeof(E) == 2) {
+            *reinterpret_cast<bf16x8*>(dst) = Mma<bf16>::pack(f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]});
+        } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_scan: the state gradient through the chunks in reverse, per (sequence,
+// head) and BV value columns (16 per wave; columns evolve independently).
+// Lam (the gradient at the current chunk end) stays in MFMA accumulators;
+// per chunk:
+//   dDelta = K^ Lam + P^T dO,   Lam <- diag(gamma) Lam + Q~^T dO - W^T dDelta
+// and Lam (before the update) and dDelta go to the workspace in fp32.  A
+// chunk's fragments are copied global -> LDS with global_load_lds (no
+// register staging), double buffered when two buffers fit.
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+struct ScanShape {
+    typedef ScanFrags<E, D> F;
+    static constexpr int BV = 64, NS = D / BV;
+    static constexpr size_t O_SLICE = (size_t)(BV / 16) * F::NKC * F::FRAG;
+    static constexpr size_t OFF_O = F::OFF_O, OFF_G = OFF_O + O_SLICE, BUF = OFF_G + (size_t)D * 4;
+    static constexpr int NBUF = 2 * BUF <= 160 * 1024 ? 2 : 1;
+    static_assert(F::OFF_O % 1024 == 0 && O_SLICE % 1024 == 0, "whole fragments");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// BYTES (a multiple of 1 KB) global -> LDS, 16 bytes per lane per
+// instruction; instruction j belongs to wave j % 4.
+template <size_t BYTES>
+__device__ __forceinline__ void copy_frags(const unsigned char* g, unsigned char* l, int wave, int lane)
+{
+    constexpr int NINST = (int)(BYTES / 1024);
+#pragma unroll
+    for (int j = wave; j < NINST; j += NTB / 64)
+        __builtin_amdgcn_global_load_lds(g + j * 1024 + lane * 16, (lds_void*)(l + j * 1024), 16, 0, 0);
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void scan_fetch(const BwdArgs& a, int64_t r, int slice, unsigned char* buf, int wave,
+                                           int lane)
+{
+    typedef ScanShape<E, D> S;
+    typedef ScanFrags<E, D> F;
+    const unsigned char* rec = reinterpret_cast<const unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC;
+    copy_frags<F::OFF_O>(rec, buf, wave, lane);
+    copy_frags<S::O_SLICE>(rec + F::OFF_O + slice * S::O_SLICE, buf + S::OFF_O, wave, lane);
+    if (wave == NTB / 64 - 1 && lane < D / 4)
+        __builtin_amdgcn_global_load_lds(a.ws + a.L.gam + (size_t)r * D + lane * 4, (lds_void*)(buf + S::OFF_G), 16,
+                                         0, 0);
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char* buf, f32x4* lam, int64_t r,
+                                           int col, int lane, int wave)
+{
+    typedef ScanShape<E, D> S;
+    typedef ScanFrags<E, D> F;
+    typedef Mma<E> MM;
+    typedef typename MM::Frag Frag;
+    constexpr int NB = F::NB, NKS = F::NKS, NKC = F::NKC, KT = F::KT, DT = F::DT;
+    const int gq = lane >> 4;
+    const unsigned char* fl = buf + lane * 16;
+    auto frag = [&](size_t off, int i) -> Frag { return *reinterpret_cast<const Frag*>(fl + off + (size_t)i * 1024); };
+    const float* sGam = reinterpret_cast<const float*>(buf + S::OFF_G);
+
+    // the gradient at this chunk's end, for the per-chunk products
+    float* lo = a.ws + a.L.Lam + (size_t)r * D * D;
+#pragma unroll
+    for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lo[(16 * kt + 4 * gq + i) * D + col] = lam[kt][i];
+
+    Frag LB[NKS], OB[NKC];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        LB[ks] = MM::from_acc(&lam[ks * KT]);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        OB[kc] = frag(S::OFF_O, wave * NKC + kc);
+
+    // dDelta = K^ Lam + P^T dO  (P^T is upper triangular: k-steps from the diagonal)
+    f32x4 dd[NB];
+#pragma unroll
+    for (int st = 0; st < NB; ++st)
+        dd[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int st = 0; st < NB; ++st)
+            dd[st] = MM::mma(frag(F::OFF_K, st * NKS + ks), LB[ks], dd[st]);
+#pragma unroll
+    for (int st = 0; st < NB; ++st)
+#pragma unroll
+        for (int kc = st / KT; kc < NKC; ++kc)
+            dd[st] = MM::mma(frag(F::OFF_P, st * NKC + kc), OB[kc], dd[st]);
+    float* dq = a.ws + a.L.dDel + (size_t)r * BC * D;
+#pragma unroll
+    for (int st = 0; st < NB; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dq[(16 * st + 4 * gq + i) * D + col] = dd[st][i];
+
+    // Lam <- diag(gamma) Lam + Q~^T dO - W^T dDelta  (the W fragments hold -W^T)
+    Frag DB[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        DB[kc] = MM::from_acc(&dd[kc * KT]);
+#pragma unroll
+    for (int kt = 0; kt < DT; ++kt)
+        lam[kt] = lam[kt] * *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * gq);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt) {
+            lam[kt] = MM::mma(frag(F::OFF_Q, kt * NKC + kc), OB[kc], lam[kt]);
+            lam[kt] = MM::mma(frag(F::OFF_W, kt * NKC + kc), DB[kc], lam[kt]);
+        }
+}
+
+template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
 {
-    constexpr int C = BC;
-    extern __shared__ __align__(16) float sm[];
-    float* sLam = sm;                // [D][SV]
-    float* sdO = sLam + D * SV;      // [C][SV]
-    float* sdD = sdO + C * SV;       // [C][SV]
-    float* sP = sdD + C * SV;        // [C][C]
-    float* sKh = sP + C * C;         // [C][D]
-    float* sQt = sKh + C * D;        // [C][D]
-    float* sW = sQt + C * D;         // [C][D]
-    float* sGam = sW + C * D;        // [D]
-    const int NS = D / SV;
-    const int64_t bh = blockIdx.x / NS;
-    const int c0 = (int)(blockIdx.x % NS) * SV;
-    const int tid = threadIdx.x;
-    float* ws = a.ws;
+    typedef ScanShape<E, D> S;
+    constexpr int DT = D / 16;
+    __shared__ __align__(16) unsigned char buf0[S::BUF];
+    __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
+    // workgroup -> ((b,h), column slice); the slices of one (b,h) share
+    // blockIdx % 8, i.e. one XCD and its L2
+    const int64_t bx = blockIdx.x, grp = bx / (8 * S::NS);
+    const int within = (int)(bx % (8 * S::NS)), slice = within / 8;
+    const int64_t bh = grp * 8 + within % 8;
+    if (bh >= a.nbh)
+        return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4;
+    const int col = slice * S::BV + 16 * wave + (lane & 15);
+    const int64_t rec0 = bh * a.NC;
 
-    for (int e = tid; e < D * SV; e += NTB) {
-        const int i = e / SV, j = e % SV;
-        sLam[e] = a.dS_final ? a.dS_final[(bh * D + i) * D + c0 + j] : 0.f;
-    }
-    for (int64_t n = a.NC - 1; n >= 0; --n) {
-        const int64_t r = bh * a.NC + n;
-        const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
-        __syncthreads();
-        for (int e = tid; e < C * SV; e += NTB)
-            sdO[e] = ws[a.L.dO + cdo + (e / SV) * D + c0 + e % SV];
-        for (int e = tid; e < C * C; e += NTB)
-            sP[e] = ws[a.L.P + cco + e];
-        for (int e = tid; e < C * D; e += NTB) {
-            sKh[e] = ws[a.L.Kh + cdo + e];
-            sQt[e] = ws[a.L.Qt + cdo + e];
-            sW[e] = ws[a.L.W + cdo + e];
-        }
-        for (int e = tid; e < D; e += NTB)
-            sGam[e] = ws[a.L.gam + (size_t)r * D + e];
-        __syncthreads();
-        // the state gradient at this chunk's end
-        for (int e = tid; e < D * SV; e += NTB)
-            ws[a.L.Lam + (size_t)r * D * D + (e / SV) * D + c0 + e % SV] = sLam[e];
-        // dDelta = P^T dO + K^ Lam
-        for (int e = tid; e < C * SV; e += NTB) {
-            const int s = e / SV, j = e % SV;
-            float acc = 0.f;
-            for (int t = s; t < C; ++t)
-                acc += sP[t * C + s] * sdO[t * SV + j];
-            for (int i = 0; i < D; ++i)
-                acc += sKh[s * D + i] * sLam[i * SV + j];
-            sdD[e] = acc;
-            ws[a.L.dDel + cdo + s * D + c0 + j] = acc;
-        }
-        __syncthreads();
-        // Lam_start = Q~^T dO + gamma Lam - W^T dDelta
-        float nl[D * SV / NTB];
+    f32x4 lam[DT];
 #pragma unroll
-        for (int u = 0; u < D * SV / NTB; ++u) {
-            const int e = u * NTB + tid, i = e / SV, j = e % SV;
-            float acc = sGam[i] * sLam[e];
-            for (int t = 0; t < C; ++t)
-                acc += sQt[t * D + i] * sdO[t * SV + j] - sW[t * D + i] * sdD[t * SV + j];
-            nl[u] = acc;
-        }
-        __syncthreads();
+    for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
-        for (int u = 0; u < D * SV / NTB; ++u)
-            sLam[u * NTB + tid] = nl[u];
+        for (int i = 0; i < 4; ++i)
+            lam[kt][i] = a.dS_final ? a.dS_final[(bh * D + 16 * kt + 4 * gq + i) * D + col] : 0.f;
+
+    scan_fetch<E, D>(a, rec0 + a.NC - 1, slice, buf0, wave, lane);
+    if constexpr (S::NBUF == 2) {
+        for (int64_t n = a.NC - 1; n >= 0; n -= 2) {
+            wait_copies();
+            __syncthreads();          // chunk n is in buf0; everyone is done with buf1
+            if (n >= 1)
+                scan_fetch<E, D>(a, rec0 + n - 1, slice, buf1, wave, lane);
+            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave);
+            if (n == 0)
+                break;
+            wait_copies();
+            __syncthreads();          // chunk n - 1 is in buf1; everyone is done with buf0
+            if (n >= 2)
+                scan_fetch<E, D>(a, rec0 + n - 2, slice, buf0, wave, lane);
+            scan_chunk<E, D>(a, buf1, lam, rec0 + n - 1, col, lane, wave);
+        }
+    } else {
+        for (int64_t n = a.NC - 1; n >= 0; --n) {
+            wait_copies();
+            __syncthreads();          // chunk n is in buf0
+            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave);
+            __syncthreads();          // everyone is done with buf0
+            if (n >= 1)
+                scan_fetch<E, D>(a, rec0 + n - 1, slice, buf0, wave, lane);
+        }
     }
-    __syncthreads();
-    if (a.dS0)
-        for (int e = tid; e < D * SV; e += NTB)
-            a.dS0[(bh * D + e / SV) * D + c0 + e % SV] = sLam[e];
+    if (a.dS0) {
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.dS0[(bh * D + 16 * kt + 4 * gq + i) * D + col] = lam[kt][i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -406,21 +585,31 @@ __global__ __launch_bounds__(NTB) void bgemm_kernel(int M, int N, int K, GemmOp 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_decay: per chunk, the decay-weighted sums and the input gradients.
+// bwd_decay: per chunk and block of DC key channels, the decay-weighted sums
+// and the input gradients.  Every channel is independent here, so one
+// workgroup takes DC channels of one chunk; thread (row group, channel) owns
+// the rows t = rg + 8m of its channel.
 // ---------------------------------------------------------------------------
+constexpr int DC = 32;                 // channels per decay workgroup
+constexpr int LC = DC + 1;             // padded LDS row
+
 template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
 {
-    constexpr int C = BC;
+    constexpr int C = BC, NRG = NTB / DC, RPT = C / NRG;
     extern __shared__ __align__(16) float sm[];
-    float* sG = sm;                 // [C][D]
-    float* sE = sG + C * D;         // [C][D] e
-    float* sK = sE + C * D;         // [C][D] k
-    float* sQ = sK + C * D;         // [C][D] q, later dG
-    float* sGL = sQ + C * D;        // [D] dG_L
-    const int64_t r = blockIdx.x;
+    float* sG = sm;                 // [C][LC] cumulative log-decay
+    float* sE = sG + C * LC;        // [C][LC] e = b*k
+    float* sK = sE + C * LC;        // [C][LC] k
+    float* sQ = sK + C * LC;        // [C][LC] q
+    float* sdG = sQ + C * LC;       // [C][LC] dG, then dg
+    float* sdM = sdG + C * LC;      // [C][C]
+    float* sdP = sdM + C * C;       // [C][C]
+    float* sGL = sdP + C * C;       // [DC] dG_L
+    const int64_t r = blockIdx.x / (D / DC);
+    const int i0 = (int)(blockIdx.x % (D / DC)) * DC;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, il = tid % DC, rg = tid / DC, i = i0 + il;
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
@@ -428,24 +617,27 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     const E* w = (const E*)a.w;
     const float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
-    const float* dM = ws + a.L.dM + cco;
-    const float* dP = ws + a.L.dP + cco;
 
-    for (int e = tid; e < C * D; e += NTB) {
-        const int t = e / D;
+    for (int e = tid; e < C * DC; e += NTB) {
+        const int t = e / DC, c = e % DC, l = t * LC + c;
+        const size_t x = cdo + (size_t)t * D + i0 + c;
         float kv = 0.f, qv = 0.f;
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H;
-            kv = ldf(k, row * D + e % D);
-            qv = ldf(q, row * D + e % D);
+            kv = ldf(k, row * D + i0 + c);
+            qv = ldf(q, row * D + i0 + c);
         }
-        sG[e] = ws[a.L.G + cdo + e];
-        sE[e] = ws[a.L.E + cdo + e];
-        sK[e] = kv;
-        sQ[e] = qv;
+        sG[l] = ws[a.L.G + x];
+        sE[l] = ws[a.L.E + x];
+        sK[l] = kv;
+        sQ[l] = qv;
+    }
+    for (int e = tid; e < C * C; e += NTB) {
+        sdM[e] = ws[a.L.dM + cco + e];
+        sdP[e] = ws[a.L.dP + cco + e];
     }
     // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam)
-    for (int i = tid; i < D; i += NTB) {
+    if (tid < DC) {
         const float* S = a.S_chunks + (size_t)r * D * D + (size_t)i * D;
         const float* Lam = ws + a.L.Lam + (size_t)r * D * D + (size_t)i * D;
         float dgam = 0.f;
@@ -454,82 +646,73 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         float acc = dgam * ws[a.L.gam + (size_t)r * D + i];
         for (int s = 0; s < C; ++s)
             acc += ws[a.L.dKh + cdo + s * D + i] * ws[a.L.Kh + cdo + s * D + i];
-        sGL[i] = acc;
+        sGL[il] = acc;
     }
     __syncthreads();
-    // per (row, channel): the four decay-weighted sums
-    constexpr int PER = C * D / NTB;
-    float dEm[PER], dqp[PER], dkm[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = u * NTB + tid, t = e / D, i = e % D;
-        const float Gt = sG[e];
-        float a1 = 0.f, a2 = 0.f, b1 = 0.f;
-        for (int s = 0; s <= t; ++s) {           // as the later token t
-            const float f = expf(Gt - sG[s * D + i]) * sK[s * D + i];
-            a1 += (s < t ? dM[t * C + s] : 0.f) * f;
-            a2 += dP[t * C + s] * f;
+    for (int m = 0; m < RPT; ++m) {
+        const int t = rg + NRG * m, l = t * LC + il;
+        const float Gt = sG[l];
+        // as the later token t: sum over s <= t
+        float dEm = 0.f, dqp = 0.f;
+        for (int s = 0; s <= t; ++s) {
+            const float f = expf(Gt - sG[s * LC + il]) * sK[s * LC + il];
+            dEm += sdM[t * C + s] * f;       // dM is strictly lower: dM[t][t] = 0
+            dqp += sdP[t * C + s] * f;
         }
-        for (int t2 = t; t2 < C; ++t2) {          // as the earlier token (s = t)
-            const float f = expf(sG[t2 * D + i] - Gt);
-            b1 += ((t2 > t ? dM[t2 * C + t] * sE[t2 * D + i] : 0.f) + dP[t2 * C + t] * sQ[t2 * D + i]) * f;
+        // as the earlier token: sum over t2 >= t
+        float dkm = 0.f;
+        for (int t2 = t; t2 < C; ++t2) {
+            const float f = expf(sG[t2 * LC + il] - Gt);
+            dkm += (sdM[t2 * C + t] * sE[t2 * LC + il] + sdP[t2 * C + t] * sQ[t2 * LC + il]) * f;
         }
-        dEm[u] = a1;
-        dqp[u] = a2;
-        dkm[u] = b1;
-    }
-    __syncthreads();
-    // dG into sQ (q is read again from the inputs below)
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = u * NTB + tid, t = e / D, i = e % D;
-        const float kv = sK[e];
-        const int64_t row = rc.row0 + (int64_t)t * a.H;
-        const float qv = t < rc.L ? ldf(q, row * D + i) : 0.f;
-        float dG = sE[e] * dEm[u] + qv * dqp[u] - kv * dkm[u];
-        dG += ws[a.L.dEt + cdo + e] * ws[a.L.Et + cdo + e] + ws[a.L.dQt + cdo + e] * ws[a.L.Qt + cdo + e] -
-              ws[a.L.dKh + cdo + e] * ws[a.L.Kh + cdo + e];
+        const size_t x = cdo + (size_t)t * D + i;
+        const float eg = expf(Gt), dEt = ws[a.L.dEt + x], dQt = ws[a.L.dQt + x];
+        const float dKh = ws[a.L.dKh + x], Kh = ws[a.L.Kh + x];
+        float dG = sE[l] * dEm + sQ[l] * dqp - sK[l] * dkm + dEt * ws[a.L.Et + x] + dQt * ws[a.L.Qt + x] -
+                   dKh * Kh;
         if (t == rc.L - 1)
-            dG += sGL[i];
-        sQ[e] = dG;
+            dG += sGL[il];
+        sdG[l] = dG;
+        if (t < rc.L) {
+            const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i;
+            const float GL = sG[(C - 1) * LC + il];
+            const float bv = ldf(b, a.bw == 1 ? row : off);
+            const float dE = dEm + dEt * eg;
+            const float dU = ws[a.L.dU + x];
+            a.dq[off] = dqp + dQt * eg;
+            a.dk[off] = dkm + dKh * expf(GL - Gt) + dE * bv;
+            a.dv[off] = dU * ldf(w, a.ww == 1 ? row : off);
+            const float dbv = dE * sK[l], dwv = dU * ldf(v, off);
+            if (a.bw == 1)
+                atomicAdd(a.db + row, dbv);
+            else
+                a.db[off] = dbv;
+            if (a.ww == 1)
+                atomicAdd(a.dw + row, dwv);
+            else
+                a.dw[off] = dwv;
+        }
     }
     __syncthreads();
     // dg: reverse cumulative sum over the chunk, per channel
-    for (int i = tid; i < D; i += NTB) {
+    if (tid < DC) {
         float acc = 0.f;
         for (int t = C - 1; t >= 0; --t) {
-            acc += sQ[t * D + i];
-            sQ[t * D + i] = acc;
+            acc += sdG[t * LC + tid];
+            sdG[t * LC + tid] = acc;
         }
     }
     __syncthreads();
-    // input gradients for valid rows; width-1 gates sum over channels
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = u * NTB + tid, t = e / D, i = e % D;
+    for (int m = 0; m < RPT; ++m) {
+        const int t = rg + NRG * m;
         if (t >= rc.L)
             continue;
-        const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i;
-        const float G = sG[e], GL = sG[(C - 1) * D + i], eg = expf(G);
-        const float bv = ldf(b, a.bw == 1 ? row : off);
-        const float dE = dEm[u] + ws[a.L.dEt + cdo + e] * eg;
-        const float dU = ws[a.L.dU + cdo + e];
-        a.dq[off] = dqp[u] + ws[a.L.dQt + cdo + e] * eg;
-        a.dk[off] = dkm[u] + ws[a.L.dKh + cdo + e] * expf(GL - G) + dE * bv;
-        a.dv[off] = dU * ldf(w, a.ww == 1 ? row : off);
-        const float dbv = dE * sK[e], dwv = dU * ldf(v, off), dgv = sQ[e];
-        if (a.bw == 1)
-            atomicAdd(a.db + row, dbv);
-        else
-            a.db[off] = dbv;
-        if (a.ww == 1)
-            atomicAdd(a.dw + row, dwv);
-        else
-            a.dw[off] = dwv;
+        const int64_t row = rc.row0 + (int64_t)t * a.H;
+        const float dgv = sdG[t * LC + il];
         if (a.gw == 1)
             atomicAdd(a.dg + row, dgv);
         else
-            a.dg[off] = dgv;
+            a.dg[row * D + i] = dgv;
     }
 }
 
@@ -568,7 +751,8 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     a.dq = x.dq; a.dk = x.dk; a.dv = x.dv; a.db = x.db; a.dw = x.dw; a.dg = x.dg; a.dS0 = x.dS0;
     a.bw = x.b_width; a.ww = x.w_width; a.gw = x.g_width;
     a.T = x.T; a.H = x.H; a.NC = cdiv(x.T, C);
-    a.L = bwd_layout(x.B, x.H, x.T, D);
+    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC);
+    a.nbh = x.B * x.H;
     a.nrec = a.L.nrec;
     a.ws = static_cast<float*>(x.workspace);
     const int64_t nrec = a.nrec, rows = x.B * x.T * x.H;
@@ -579,13 +763,10 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     if (a.gw == 1 && (e = zero_fill(a.dg, rows, s)) != hipSuccess) return e;
 
     const size_t lds_prep = (size_t)(4 * C * (D + 1) + C * C) * 4;
-    const size_t lds_scan = (size_t)(D * SV + 2 * C * SV + C * C + 3 * C * D + D) * 4;
-    const size_t lds_decay = (size_t)(4 * C * D + D) * 4;
+    const size_t lds_decay = (size_t)(5 * C * LC + 2 * C * C + DC) * 4;
     // more than 64 KiB of dynamic LDS must be requested per kernel
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_prep_kernel<E, D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_prep)) != hipSuccess ||
-        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_scan_kernel<D>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_scan)) != hipSuccess ||
         (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_decay_kernel<E, D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_decay)) != hipSuccess)
         return e;
@@ -594,7 +775,12 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dout_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)(x.B * x.H * (D / SV))), dim3(NTB), lds_scan, s, a);
+    hipLaunchKernelGGL((bwd_frag_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        const int64_t groups = cdiv(a.nbh, 8) * 8 * ScanShape<E, D>::NS;
+        hipLaunchKernelGGL((bwd_scan_kernel<E, D>), dim3((unsigned)groups), dim3(NTB), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     float* ws = a.ws;
@@ -621,7 +807,7 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     if ((e = gemm(s, nrec, C, C, C, op(L.dX, CC, C, 0), op(L.X, CC, C, 1), ws + L.T1, CC, C, 1.f)) != hipSuccess) return e;
     if ((e = gemm(s, nrec, C, C, C, op(L.X, CC, C, 1), op(L.T1, CC, C, 0), ws + L.dM, CC, C, -1.f, 0.f, nullptr, 0, 2)) != hipSuccess) return e;
 
-    hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), lds_decay, s, a);
+    hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(nrec * (D / DC))), dim3(NTB), lds_decay, s, a);
     return hipGetLastError();
 }
 
@@ -631,7 +817,9 @@ size_t backward_workspace_bytes(const gdr2_bwd_args& a)
 {
     if (a.B * a.H * a.T == 0)
         return 0;
-    return bwd_layout(a.B, a.H, a.T, (int)a.Dk).total;
+    const size_t esz = a.dtype == GDR2_BF16 ? 2 : 4;
+    const size_t rec = (size_t)(4 * BC * a.Dk + BC * BC) * esz;   // ScanFrags<E, D>::REC
+    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec).total;
 }
 
 hipError_t launch_backward(const gdr2_bwd_args& a, hipStream_t stream)
