@@ -123,20 +123,82 @@ __device__ __forceinline__ Rec rec_of(int64_t r, int64_t NC, int64_t T, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_prep: one workgroup per chunk record.
+// bwd_prep: one workgroup (NTP threads) per chunk record.
+//   1. raw rows into LDS, 4 channels per item; G = cumulative log-decay;
+//      E~, Q~, K^, gamma, E, U written out (fp32)
+//   2. M (strictly lower) and P (lower) pair by pair: the 4x4 token block
+//      (tb, sb), sb <= tb, is owned by two threads, one per half of the
+//      channels; the halves' partial sums meet in LDS.  Every factor is
+//      exp(G_t - G_s) for s <= t (no overflow for decays)
+//   3. X = (I + M)^-1 by 16x16 blocks: diagonal blocks by substitution, the
+//      rest by X_ij = -X_ii sum_{k=j}^{i-1} M_ik X_kj, one block diagonal at
+//      a time
+//   4. W = X E~, U~ = X U, register-blocked (2 tokens x D/16 channels per
+//      thread)
 // ---------------------------------------------------------------------------
-template <typename E, int D>
-__global__ __launch_bounds__(NTB) void bwd_prep_kernel(BwdArgs a)
+constexpr int NTP = 512;         // threads of the prep kernel
+
+template <int D>
+struct BwdPrepShape {
+    static constexpr int C = BC, LD = D + 4, LDM = C + 4;
+    static constexpr int OFF_G = 0, OFF_E = C * LD, OFF_K = 2 * C * LD, OFF_Q = 3 * C * LD, OFF_M = 4 * C * LD;
+    static constexpr int FLOATS = OFF_M + C * LDM;
+    static constexpr size_t SMEM = (size_t)FLOATS * 4;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(C * LDM <= C * LD && 3 * 256 <= C * LD && C * C <= C * LD,
+                  "X fits in the q area; the block products and the partial P in the k area");
+};
+
+// Y_ij (16x16, into sY) = sum_{k=j}^{i-1} M_ik X_kj  for the blocks (i, i-d)
+// of block diagonal d; then X_ij = -X_ii Y_ij.
+__device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float* sY, int d, int tid)
 {
-    // Rows of the [C][D] tiles are padded to LD floats so that lanes walking
-    // down a column hit distinct LDS banks in the pairwise loops.
-    constexpr int C = BC, LD = D + 1;
+    constexpr int LDM = BC + 4;
+    const int nblk = 4 - d;
+    for (int e = tid; e < nblk * 256; e += NTP) {
+        const int bi = e / 256, rr = (e / 16) % 16, cc = e % 16, i = bi + d, j = bi;
+        float acc = 0.f;
+        for (int kb = j; kb < i; ++kb)
+            for (int c = 0; c < 16; ++c)
+                acc += sM[(16 * i + rr) * LDM + 16 * kb + c] * sX[(16 * kb + c) * LDM + 16 * j + cc];
+        sY[e] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < nblk * 256; e += NTP) {
+        const int bi = e / 256, rr = (e / 16) % 16, cc = e % 16, i = bi + d, j = bi;
+        float acc = 0.f;
+        for (int c = 0; c <= rr; ++c)
+            acc += sX[(16 * i + rr) * LDM + 16 * i + c] * sY[bi * 256 + c * 16 + cc];
+        sX[(16 * i + rr) * LDM + 16 * j + cc] = -acc;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4s(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// Four consecutive channels of a gate of width 1 or D at element row `row`.
+template <typename T>
+__device__ __forceinline__ f32x4 gate4(const T* p, int width, int64_t row, int i)
+{
+    if (width == 1) {
+        const float x = to_f32(p[row]);
+        return f32x4{x, x, x, x};
+    }
+    return load4(p + row * (int64_t)width + i);
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
+{
+    typedef BwdPrepShape<D> PS;
+    constexpr int C = BC, LD = PS::LD, LDM = PS::LDM, CPT = D / 16, Q4 = D / 4;
     extern __shared__ __align__(16) float sm[];
-    float* sG = sm;                 // [C][LD] cumulative log-decay
-    float* sE = sG + C * LD;        // [C][LD] e = b*k, later u
-    float* sK = sE + C * LD;        // [C][LD] k, later E~
-    float* sQ = sK + C * LD;        // [C][LD] q, later X [C][C]
-    float* sM = sQ + C * LD;        // [C][C] M
+    float* sG = sm + PS::OFF_G;     // [C][LD] cumulative log-decay (natural units)
+    float* sE = sm + PS::OFF_E;     // [C][LD] e = b*k, later E~
+    float* sK = sm + PS::OFF_K;     // [C][LD] k, later partial P, block products and u
+    float* sQ = sm + PS::OFF_Q;     // [C][LD] q, later X [C][LDM]
+    float* sM = sm + PS::OFF_M;     // [C][LDM] M
     const int64_t r = blockIdx.x;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
     const int tid = threadIdx.x;
@@ -148,28 +210,28 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BwdArgs a)
     float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
 
-    // raw rows (zero past the chunk's valid length)
-    for (int e = tid; e < C * D; e += NTB) {
-        const int t = e / D, i = e % D, l = t * LD + i;
-        float gv = 0.f, kv = 0.f, qv = 0.f, bv = 0.f, uv = 0.f;
+    // 1. raw rows (zero past the chunk's valid length), 4 channels per item
+    for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
+        const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+        const size_t x = cdo + (size_t)t * D + i;
+        f32x4 gv = {0.f, 0.f, 0.f, 0.f}, kv = gv, qv = gv, ev = gv, uv = gv;
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H;
-            gv = a.g[a.gw == 1 ? row : row * D + i];
-            kv = ldf(k, row * D + i);
-            qv = ldf(q, row * D + i);
-            bv = ldf(b, a.bw == 1 ? row : row * D + i);
-            uv = ldf(w, a.ww == 1 ? row : row * D + i) * ldf(v, row * D + i);
+            gv = gate4(a.g, a.gw, row, i);
+            kv = load4(k + row * D + i);
+            qv = load4(q + row * D + i);
+            ev = gate4(b, a.bw, row, i) * kv;
+            uv = gate4(w, a.ww, row, i) * load4(v + row * D + i);
         }
-        sG[l] = gv;
-        sK[l] = kv;
-        sQ[l] = qv;
-        sE[l] = bv * kv;
-        ws[a.L.E + cdo + e] = bv * kv;
-        ws[a.L.U + cdo + e] = uv;
+        st4s(sG + l, gv);
+        st4s(sK + l, kv);
+        st4s(sQ + l, qv);
+        st4s(sE + l, ev);
+        st4s(ws + a.L.E + x, ev);
+        st4s(ws + a.L.U + x, uv);
     }
     __syncthreads();
-    // cumulative sum over the chunk, per channel
-    for (int i = tid; i < D; i += NTB) {
+    for (int i = tid; i < D; i += NTP) {
         float acc = 0.f;
         for (int t = 0; t < C; ++t) {
             acc += sG[t * LD + i];
@@ -177,63 +239,153 @@ __global__ __launch_bounds__(NTB) void bwd_prep_kernel(BwdArgs a)
         }
     }
     __syncthreads();
-    for (int e = tid; e < C * D; e += NTB) {
-        const int t = e / D, i = e % D, l = t * LD + i;
-        const float G = sG[l], GL = sG[(C - 1) * LD + i], eg = expf(G);
-        ws[a.L.G + cdo + e] = G;
-        ws[a.L.Et + cdo + e] = sE[l] * eg;
-        ws[a.L.Qt + cdo + e] = sQ[l] * eg;
-        ws[a.L.Kh + cdo + e] = sK[l] * expf(GL - G);
-        if (t == 0)
-            ws[a.L.gam + (size_t)r * D + i] = expf(GL);
-    }
-    // M (strictly lower) and P (lower), pair by pair; every exponent is
-    // G_t - G_s with s <= t
-    for (int e = tid; e < C * C; e += NTB) {
-        const int t = e / C, s = e % C;
-        float m = 0.f, p = 0.f;
-        if (s <= t) {
-            for (int i = 0; i < D; ++i) {
-                const float f = expf(sG[t * LD + i] - sG[s * LD + i]) * sK[s * LD + i];
-                m += sE[t * LD + i] * f;
-                p += sQ[t * LD + i] * f;
-            }
+    for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
+        const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+        const size_t x = cdo + (size_t)t * D + i;
+        const f32x4 G = ld4s(sG + l), GL = ld4s(sG + (C - 1) * LD + i);
+        f32x4 eg, kd;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            eg[j] = expf(G[j]);
+            kd[j] = expf(GL[j] - G[j]);
         }
-        sM[e] = s < t ? m : 0.f;
-        ws[a.L.P + cco + e] = p;
+        st4s(ws + a.L.G + x, G);
+        st4s(ws + a.L.Et + x, ld4s(sE + l) * eg);
+        st4s(ws + a.L.Qt + x, ld4s(sQ + l) * eg);
+        st4s(ws + a.L.Kh + x, ld4s(sK + l) * kd);
+        if (t == 0) {
+            f32x4 gm;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                gm[j] = expf(GL[j]);
+            st4s(ws + a.L.gam + (size_t)r * D + i, gm);
+        }
+    }
+
+    // 2. M and P, 4x4 token blocks on and below the diagonal; two threads
+    // (channel halves) per block
+    float m[4][4] = {}, p[4][4] = {};
+    const int half = tid / 136, bid = tid % 136;
+    int tb = 0;
+    while ((tb + 1) * (tb + 2) / 2 <= bid)
+        ++tb;
+    const int sb = bid - tb * (tb + 1) / 2, t0 = 4 * tb, s0 = 4 * sb;
+    if (tid < 272) {
+        for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
+            float gt[4], et[4], qt[4], gs[4], ks[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                gt[x] = sG[(t0 + x) * LD + i];
+                et[x] = sE[(t0 + x) * LD + i];
+                qt[x] = sQ[(t0 + x) * LD + i];
+                gs[x] = sG[(s0 + x) * LD + i];
+                ks[x] = sK[(s0 + x) * LD + i];
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const float f = __expf(gt[x] - gs[y]) * ks[y];
+                    m[x][y] += et[x] * f;
+                    p[x][y] += qt[x] * f;
+                }
+        }
+    }
+    __syncthreads();                  // q and k rows are no longer read
+    float* sPp = sK;                  // [C][C] partial P of the second half
+    if (tid >= 136 && tid < 272) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                sM[(t0 + x) * LDM + s0 + y] = m[x][y];
+                sPp[(t0 + x) * C + s0 + y] = p[x][y];
+            }
     }
     __syncthreads();
-    // X = (I + M)^-1 by forward substitution, one column per thread (into sQ)
+    if (tid < 136) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int t = t0 + x, s_ = s0 + y;
+                const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
+                sM[t * LDM + s_] = s_ < t ? mm : 0.f;
+                ws[a.L.P + cco + t * C + s_] = s_ <= t ? pp : 0.f;
+            }
+        if (sb != tb) {               // the mirrored block above the diagonal is zero
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    sM[(s0 + y) * LDM + t0 + x] = 0.f;
+                    ws[a.L.P + cco + (s0 + y) * C + t0 + x] = 0.f;
+                }
+        }
+    }
+    __syncthreads();
+
+    // 3. X = (I + M)^-1 into the q area; first the diagonal 16x16 blocks, one
+    // column per thread, then the block diagonals below
     float* sX = sQ;
+    float* sY = sK;
+    for (int e = tid; e < C * C; e += NTP)
+        sX[(e / C) * LDM + e % C] = 0.f;
+    __syncthreads();
     if (tid < C) {
-        const int j = tid;
-        for (int rr = 0; rr < C; ++rr) {
+        const int bk = tid / 16, j = tid % 16, o = 16 * bk;
+        for (int rr = j; rr < 16; ++rr) {
             float acc = rr == j ? 1.f : 0.f;
             for (int c = j; c < rr; ++c)
-                acc -= sM[rr * C + c] * sX[c * C + j];
-            sX[rr * C + j] = acc;
+                acc -= sM[(o + rr) * LDM + o + c] * sX[(o + c) * LDM + o + j];
+            sX[(o + rr) * LDM + o + j] = acc;
         }
-    }
-    // E~ into sK, u into sE
-    for (int e = tid; e < C * D; e += NTB) {
-        const int l = (e / D) * LD + e % D;
-        sK[l] = sE[l] * expf(sG[l]);
-        sE[l] = ws[a.L.U + cdo + e];
     }
     __syncthreads();
-    for (int e = tid; e < C * C; e += NTB)
-        ws[a.L.X + cco + e] = sX[e];
-    // W = X E~, U~ = X u (X is lower triangular)
-    for (int e = tid; e < C * D; e += NTB) {
-        const int t = e / D, i = e % D;
-        float wv = 0.f, uv = 0.f;
-        for (int s = 0; s <= t; ++s) {
-            const float x = sX[t * C + s];
-            wv += x * sK[s * LD + i];
-            uv += x * sE[s * LD + i];
+    xinv_diagonal(sM, sX, sY, 1, tid);
+    xinv_diagonal(sM, sX, sY, 2, tid);
+    xinv_diagonal(sM, sX, sY, 3, tid);
+    for (int e = tid; e < C * C; e += NTP)
+        ws[a.L.X + cco + e] = sX[(e / C) * LDM + e % C];
+
+    // 4. E~ in place, u into the k area; W = X E~, U~ = X u
+    float* sU = sK;
+    for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
+        const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+        f32x4 ev = ld4s(sE + l);
+        const f32x4 G = ld4s(sG + l);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ev[j] *= expf(G[j]);
+        st4s(sE + l, ev);
+        st4s(sU + l, ld4s(ws + a.L.U + cdo + (size_t)t * D + i));
+    }
+    __syncthreads();
+    {
+        const int tr = tid / 16, cg = tid % 16, r0 = 2 * tr, c0 = CPT * cg;
+        float wv[2][CPT] = {}, uv[2][CPT] = {};
+        for (int s_ = 0; s_ <= r0 + 1; ++s_) {
+            const float x0 = sX[r0 * LDM + s_], x1 = sX[(r0 + 1) * LDM + s_];
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                const f32x4 e4 = ld4s(sE + s_ * LD + c0 + c), u4 = ld4s(sU + s_ * LD + c0 + c);
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    wv[0][c + y] += x0 * e4[y];
+                    wv[1][c + y] += x1 * e4[y];
+                    uv[0][c + y] += x0 * u4[y];
+                    uv[1][c + y] += x1 * u4[y];
+                }
+            }
         }
-        ws[a.L.W + cdo + e] = wv;
-        ws[a.L.Ut + cdo + e] = uv;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                const size_t o = cdo + (size_t)(r0 + x) * D + c0 + c;
+                st4s(ws + a.L.W + o, f32x4{wv[x][c], wv[x][c + 1], wv[x][c + 2], wv[x][c + 3]});
+                st4s(ws + a.L.Ut + o, f32x4{uv[x][c], uv[x][c + 1], uv[x][c + 2], uv[x][c + 3]});
+            }
     }
 }
 
@@ -523,93 +675,116 @@ __global__ __launch_bounds__(NTB) void bgemm_kernel(int M, int N, int K, GemmOp 
                                                     int64_t cbs, int ldc, float alpha, float beta,
                                                     const float* C0, int64_t c0bs, int mask)
 {
-    __shared__ float sA[16][64 + 4];   // [k][m]
-    __shared__ float sB[16][64 + 4];   // [k][n]
+    // 64x64 output tile; wave (wm, wn) owns a 32x32 quarter = 2x2 MFMA tiles.
+    // Each 16-deep k slab is staged as sA[m][k] and sB[n][k] (rows padded to
+    // 20 floats), the layout Mma<float>::load reads.
+    constexpr int LS = 20;
+    __shared__ __align__(16) float sA[64 * LS];
+    __shared__ __align__(16) float sB[64 * LS];
     const int tiles_n = N / 64, tiles = (M / 64) * tiles_n;
     const int64_t z = blockIdx.x / tiles;
     const int tile = (int)(blockIdx.x - z * tiles);
     const int m0 = (tile / tiles_n) * 64, n0 = (tile % tiles_n) * 64;
-    const int tid = threadIdx.x, tm = tid / 16, tn = tid % 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
     const float* Ap = A.p + z * A.bs;
     const float* Bp = B.p + z * B.bs;
-    float acc[4][4] = {};
+    // this thread's float4 of the slab: along k (row-major operand) or along m / n
+    const int ra = tid / 4, ka = 4 * (tid % 4);      // 64 rows x 4 float4 along k
+    const int kb = tid / 16, ca = 4 * (tid % 16);    // 16 k-rows x 16 float4 along m / n
+    auto fetch = [&](const GemmOp& X, const float* Xp, int r0, int k0) -> f32x4 {
+        return X.trans == 0 ? *reinterpret_cast<const f32x4*>(Xp + (int64_t)(r0 + ra) * X.ld + k0 + ka)
+                            : *reinterpret_cast<const f32x4*>(Xp + (int64_t)(k0 + kb) * X.ld + r0 + ca);
+    };
+    // op(A)(m, k): A[m][k] (trans 0) or A[k][m]; op(B)(k, n): B[k][n] (trans 0) or B[n][k]
+    GemmOp Bk = B;
+    Bk.trans = B.trans ? 0 : 1;      // as a [n][k] source, B^T row-major is "k along rows"
+    auto stage = [&](float* sX, const GemmOp& X, f32x4 v) {
+        if (X.trans == 0) {
+            *reinterpret_cast<f32x4*>(sX + ra * LS + ka) = v;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sX[(ca + j) * LS + kb] = v[j];
+        }
+    };
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 va = fetch(A, Ap, m0, 0), vb = fetch(Bk, Bp, n0, 0);
     for (int k0 = 0; k0 < K; k0 += 16) {
-        for (int e = tid; e < 16 * 64; e += NTB) {
-            int kk, mm;
-            if (A.trans) {             // op(A)(m, k) = A[k][m]: read rows of A
-                kk = e / 64; mm = e % 64;
-                sA[kk][mm] = Ap[(int64_t)(k0 + kk) * A.ld + m0 + mm];
-            } else {                   // A[m][k]
-                mm = e / 16; kk = e % 16;
-                sA[kk][mm] = Ap[(int64_t)(m0 + mm) * A.ld + k0 + kk];
-            }
-            int nn;
-            if (B.trans) {             // op(B)(k, n) = B[n][k]
-                nn = e / 16; kk = e % 16;
-                sB[kk][nn] = Bp[(int64_t)(n0 + nn) * B.ld + k0 + kk];
-            } else {                   // B[k][n]
-                kk = e / 64; nn = e % 64;
-                sB[kk][nn] = Bp[(int64_t)(k0 + kk) * B.ld + n0 + nn];
-            }
-        }
         __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[i] = sA[kk][tm * 4 + i];
-                bv[i] = sB[kk][tn * 4 + i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] += av[i] * bv[j];
-        }
+        stage(sA, A, va);
+        stage(sB, Bk, vb);
         __syncthreads();
+        if (k0 + 16 < K) {
+            va = fetch(A, Ap, m0, k0 + 16);
+            vb = fetch(Bk, Bp, n0, k0 + 16);
+        }
+        f32x4 fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            fa[i] = Mma<float>::load(sA + (wm + 16 * i) * LS, LS, lane);
+            fb[i] = Mma<float>::load(sB + (wn + 16 * i) * LS, LS, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = Mma<float>::mma(fa[i], fb[j], acc[i][j]);
     }
     float* Cz = Cp + z * cbs;
+    const int gq = lane >> 4, cl = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + tm * 4 + i, n = n0 + tn * 4 + j;
-            float val = alpha * acc[i][j];
-            if (C0)
-                val += beta * C0[z * c0bs + (int64_t)m * ldc + n];
-            if ((mask == 1 && n > m) || (mask == 2 && n >= m))
-                val = 0.f;
-            Cz[(int64_t)m * ldc + n] = val;
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int m = m0 + wm + 16 * i + 4 * gq + x, n = n0 + wn + 16 * j + cl;
+                float val = alpha * acc[i][j][x];
+                if (C0)
+                    val += beta * C0[z * c0bs + (int64_t)m * ldc + n];
+                if ((mask == 1 && n > m) || (mask == 2 && n >= m))
+                    val = 0.f;
+                Cz[(int64_t)m * ldc + n] = val;
+            }
 }
 
 // ---------------------------------------------------------------------------
 // bwd_decay: per chunk and block of DC key channels, the decay-weighted sums
 // and the input gradients.  Every channel is independent here, so one
-// workgroup takes DC channels of one chunk; thread (row group, channel) owns
-// the rows t = rg + 8m of its channel.
+// workgroup takes DC channels of one chunk; thread (row group rg, channel)
+// owns the RPT consecutive tokens t = RPT*rg + m of its channel.  One pass
+// over the partner token u serves both sums of every owned token:
+//   u <= t:  f = e^{G_t - G_u};  dE_M[t] += dM[t,u] k_u f,  dq_P[t] += dP[t,u] k_u f
+//   u >= t:  f = e^{G_u - G_t};  dk[t]   += (dM[u,t] e_u + dP[u,t] q_u) f
+// (dM is strictly lower, so the u == t terms of dM vanish.)
 // ---------------------------------------------------------------------------
 constexpr int DC = 32;                 // channels per decay workgroup
-constexpr int LC = DC + 1;             // padded LDS row
+constexpr int LC = DC + 1;             // padded LDS row of the per-channel arrays
+constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte aligned)
 
 template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
 {
     constexpr int C = BC, NRG = NTB / DC, RPT = C / NRG;
+    static_assert(RPT == 8, "two 16-byte reads cover a thread's tokens");
     extern __shared__ __align__(16) float sm[];
-    float* sG = sm;                 // [C][LC] cumulative log-decay
+    float* sdM = sm;                // [C][LPC]
+    float* sdP = sdM + C * LPC;     // [C][LPC]
+    float* sG = sdP + C * LPC;      // [C][LC] cumulative log-decay
     float* sE = sG + C * LC;        // [C][LC] e = b*k
     float* sK = sE + C * LC;        // [C][LC] k
     float* sQ = sK + C * LC;        // [C][LC] q
     float* sdG = sQ + C * LC;       // [C][LC] dG, then dg
-    float* sdM = sdG + C * LC;      // [C][C]
-    float* sdP = sdM + C * C;       // [C][C]
-    float* sGL = sdP + C * C;       // [DC] dG_L
+    float* sGL = sdG + C * LC;      // [DC] dG_L
     const int64_t r = blockIdx.x / (D / DC);
     const int i0 = (int)(blockIdx.x % (D / DC)) * DC;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
-    const int tid = threadIdx.x, il = tid % DC, rg = tid / DC, i = i0 + il;
+    const int tid = threadIdx.x, il = tid % DC, rg = tid / DC, i = i0 + il, t0 = RPT * rg;
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
@@ -632,43 +807,85 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         sK[l] = kv;
         sQ[l] = qv;
     }
-    for (int e = tid; e < C * C; e += NTB) {
-        sdM[e] = ws[a.L.dM + cco + e];
-        sdP[e] = ws[a.L.dP + cco + e];
+    for (int e = tid; e < C * C / 4; e += NTB) {
+        const int t = e / (C / 4), c = 4 * (e % (C / 4));
+        *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
+        *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
     }
-    // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam)
-    if (tid < DC) {
-        const float* S = a.S_chunks + (size_t)r * D * D + (size_t)i * D;
-        const float* Lam = ws + a.L.Lam + (size_t)r * D * D + (size_t)i * D;
-        float dgam = 0.f;
-        for (int j = 0; j < D; ++j)
-            dgam += S[j] * Lam[j];
-        float acc = dgam * ws[a.L.gam + (size_t)r * D + i];
-        for (int s = 0; s < C; ++s)
-            acc += ws[a.L.dKh + cdo + s * D + i] * ws[a.L.Kh + cdo + s * D + i];
-        sGL[il] = acc;
+    // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam):
+    // every thread sums its share (D / NRG state columns, RPT tokens) of its
+    // channel, then the NRG partial sums of a channel are added up
+    {
+        constexpr int JPT = D / NRG;
+        const float* S = a.S_chunks + (size_t)r * D * D + (size_t)i * D + rg * JPT;
+        const float* Lam = ws + a.L.Lam + (size_t)r * D * D + (size_t)i * D + rg * JPT;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < JPT; j += 4) {
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + j), l4 = *reinterpret_cast<const f32x4*>(Lam + j);
+            acc += s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
+        }
+        acc *= ws[a.L.gam + (size_t)r * D + i];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const size_t x = cdo + (size_t)(t0 + m) * D + i;
+            acc += ws[a.L.dKh + x] * ws[a.L.Kh + x];
+        }
+        sdG[rg * LC + il] = acc;        // sdG is free until the main loop
     }
     __syncthreads();
+    if (tid < DC) {
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < NRG; ++g)
+            acc += sdG[g * LC + tid];
+        sGL[tid] = acc;
+    }
+
+    float Gt[RPT], dEm[RPT], dqp[RPT], dkm[RPT];
+#pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const int t = rg + NRG * m, l = t * LC + il;
-        const float Gt = sG[l];
-        // as the later token t: sum over s <= t
-        float dEm = 0.f, dqp = 0.f;
-        for (int s = 0; s <= t; ++s) {
-            const float f = expf(Gt - sG[s * LC + il]) * sK[s * LC + il];
-            dEm += sdM[t * C + s] * f;       // dM is strictly lower: dM[t][t] = 0
-            dqp += sdP[t * C + s] * f;
+        Gt[m] = sG[(t0 + m) * LC + il];
+        dEm[m] = dqp[m] = dkm[m] = 0.f;
+    }
+    for (int u0 = 0; u0 < C; u0 += 4) {
+        f32x4 rM[RPT], rP[RPT];          // dM[t, u0..u0+3], dP[t, u0..u0+3]
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            rM[m] = *reinterpret_cast<const f32x4*>(sdM + (t0 + m) * LPC + u0);
+            rP[m] = *reinterpret_cast<const f32x4*>(sdP + (t0 + m) * LPC + u0);
         }
-        // as the earlier token: sum over t2 >= t
-        float dkm = 0.f;
-        for (int t2 = t; t2 < C; ++t2) {
-            const float f = expf(sG[t2 * LC + il] - Gt);
-            dkm += (sdM[t2 * C + t] * sE[t2 * LC + il] + sdP[t2 * C + t] * sQ[t2 * LC + il]) * f;
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+            const int u = u0 + uu;
+            const float Gu = sG[u * LC + il], ku = sK[u * LC + il], eu = sE[u * LC + il], qu = sQ[u * LC + il];
+            // dM[u, t0..t0+7], dP[u, t0..t0+7]
+            const f32x4 cM0 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0);
+            const f32x4 cM1 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0 + 4);
+            const f32x4 cP0 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0);
+            const f32x4 cP1 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0 + 4);
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int t = t0 + m;
+                const float d = Gt[m] - Gu;
+                const float f = __expf(u <= t ? d : -d);
+                const float w1 = u <= t ? f * ku : 0.f, w2 = u >= t ? f : 0.f;
+                dEm[m] += rM[m][uu] * w1;
+                dqp[m] += rP[m][uu] * w1;
+                const float cm = m < 4 ? cM0[m & 3] : cM1[m & 3], cp = m < 4 ? cP0[m & 3] : cP1[m & 3];
+                dkm[m] += (cm * eu + cp * qu) * w2;
+            }
         }
+    }
+    __syncthreads();                     // sGL ready; sdG partial sums consumed
+
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int t = t0 + m, l = t * LC + il;
         const size_t x = cdo + (size_t)t * D + i;
-        const float eg = expf(Gt), dEt = ws[a.L.dEt + x], dQt = ws[a.L.dQt + x];
+        const float eg = expf(Gt[m]), dEt = ws[a.L.dEt + x], dQt = ws[a.L.dQt + x];
         const float dKh = ws[a.L.dKh + x], Kh = ws[a.L.Kh + x];
-        float dG = sE[l] * dEm + sQ[l] * dqp - sK[l] * dkm + dEt * ws[a.L.Et + x] + dQt * ws[a.L.Qt + x] -
+        float dG = sE[l] * dEm[m] + sQ[l] * dqp[m] - sK[l] * dkm[m] + dEt * ws[a.L.Et + x] + dQt * ws[a.L.Qt + x] -
                    dKh * Kh;
         if (t == rc.L - 1)
             dG += sGL[il];
@@ -677,10 +894,10 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i;
             const float GL = sG[(C - 1) * LC + il];
             const float bv = ldf(b, a.bw == 1 ? row : off);
-            const float dE = dEm + dEt * eg;
+            const float dE = dEm[m] + dEt * eg;
             const float dU = ws[a.L.dU + x];
-            a.dq[off] = dqp + dQt * eg;
-            a.dk[off] = dkm + dKh * expf(GL - Gt) + dE * bv;
+            a.dq[off] = dqp[m] + dQt * eg;
+            a.dk[off] = dkm[m] + dKh * expf(GL - Gt[m]) + dE * bv;
             a.dv[off] = dU * ldf(w, a.ww == 1 ? row : off);
             const float dbv = dE * sK[l], dwv = dU * ldf(v, off);
             if (a.bw == 1)
@@ -703,8 +920,9 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
     }
     __syncthreads();
+#pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const int t = rg + NRG * m;
+        const int t = t0 + m;
         if (t >= rc.L)
             continue;
         const int64_t row = rc.row0 + (int64_t)t * a.H;
@@ -762,8 +980,8 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     if (a.ww == 1 && (e = zero_fill(a.dw, rows, s)) != hipSuccess) return e;
     if (a.gw == 1 && (e = zero_fill(a.dg, rows, s)) != hipSuccess) return e;
 
-    const size_t lds_prep = (size_t)(4 * C * (D + 1) + C * C) * 4;
-    const size_t lds_decay = (size_t)(5 * C * LC + 2 * C * C + DC) * 4;
+    const size_t lds_prep = BwdPrepShape<D>::SMEM;
+    const size_t lds_decay = (size_t)(2 * C * LPC + 5 * C * LC + DC) * 4;
     // more than 64 KiB of dynamic LDS must be requested per kernel
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_prep_kernel<E, D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_prep)) != hipSuccess ||
@@ -771,7 +989,7 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_decay)) != hipSuccess)
         return e;
 
-    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), lds_prep, s, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)nrec), dim3(NTP), lds_prep, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dout_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
