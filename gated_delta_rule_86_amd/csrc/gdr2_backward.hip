@@ -793,19 +793,24 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     const float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
 
-    for (int e = tid; e < C * DC; e += NTB) {
-        const int t = e / DC, c = e % DC, l = t * LC + c;
+    for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
+        const int t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
         const size_t x = cdo + (size_t)t * D + i0 + c;
-        float kv = 0.f, qv = 0.f;
+        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H;
-            kv = ldf(k, row * D + i0 + c);
-            qv = ldf(q, row * D + i0 + c);
+            kv = load4(k + row * D + i0 + c);
+            qv = load4(q + row * D + i0 + c);
         }
-        sG[l] = ws[a.L.G + x];
-        sE[l] = ws[a.L.E + x];
-        sK[l] = kv;
-        sQ[l] = qv;
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(ws + a.L.G + x);
+        const f32x4 ev = *reinterpret_cast<const f32x4*>(ws + a.L.E + x);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sG[l + j] = gv[j];
+            sE[l + j] = ev[j];
+            sK[l + j] = kv[j];
+            sQ[l + j] = qv[j];
+        }
     }
     for (int e = tid; e < C * C / 4; e += NTB) {
         const int t = e / (C / 4), c = 4 * (e % (C / 4));
@@ -877,37 +882,59 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             }
         }
     }
-    __syncthreads();                     // sGL ready; sdG partial sums consumed
-
+    __syncthreads();                     // sGL ready; dM and dP no longer read
+    // the three sums into LDS (the dM / dP area), then the gradients with
+    // four channels per item
+    float* sEm = sdM;                    // [C][LC] dE_M
+    float* sQp = sEm + C * LC;           // [C][LC] dq_P
+    float* sKm = sQp + C * LC;           // [C][LC] dk_M + dk_P
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const int t = t0 + m, l = t * LC + il;
-        const size_t x = cdo + (size_t)t * D + i;
-        const float eg = expf(Gt[m]), dEt = ws[a.L.dEt + x], dQt = ws[a.L.dQt + x];
-        const float dKh = ws[a.L.dKh + x], Kh = ws[a.L.Kh + x];
-        float dG = sE[l] * dEm[m] + sQ[l] * dqp[m] - sK[l] * dkm[m] + dEt * ws[a.L.Et + x] + dQt * ws[a.L.Qt + x] -
-                   dKh * Kh;
-        if (t == rc.L - 1)
-            dG += sGL[il];
-        sdG[l] = dG;
+        const int l = (t0 + m) * LC + il;
+        sEm[l] = dEm[m];
+        sQp[l] = dqp[m];
+        sKm[l] = dkm[m];
+    }
+    __syncthreads();
+    for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
+        const int t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
+        const size_t x = cdo + (size_t)t * D + i0 + c;
+        const f32x4 dEt = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
+        const f32x4 dQt = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
+        const f32x4 dKh = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
+        const f32x4 Kh = *reinterpret_cast<const f32x4*>(ws + a.L.Kh + x);
+        const f32x4 Et = *reinterpret_cast<const f32x4*>(ws + a.L.Et + x);
+        const f32x4 Qt = *reinterpret_cast<const f32x4*>(ws + a.L.Qt + x);
+        const f32x4 dU = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+        f32x4 dq, dk, dE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float G = sG[l + j], eg = expf(G);
+            float dG = sE[l + j] * sEm[l + j] + sQ[l + j] * sQp[l + j] - sK[l + j] * sKm[l + j] + dEt[j] * Et[j] +
+                       dQt[j] * Qt[j] - dKh[j] * Kh[j];
+            if (t == rc.L - 1)
+                dG += sGL[c + j];
+            sdG[l + j] = dG;
+            dE[j] = sEm[l + j] + dEt[j] * eg;
+            dq[j] = sQp[l + j] + dQt[j] * eg;
+            dk[j] = sKm[l + j] + dKh[j] * expf(sG[(C - 1) * LC + c + j] - G);
+        }
         if (t < rc.L) {
-            const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i;
-            const float GL = sG[(C - 1) * LC + il];
-            const float bv = ldf(b, a.bw == 1 ? row : off);
-            const float dE = dEm[m] + dEt * eg;
-            const float dU = ws[a.L.dU + x];
-            a.dq[off] = dqp[m] + dQt * eg;
-            a.dk[off] = dkm[m] + dKh * expf(GL - Gt[m]) + dE * bv;
-            a.dv[off] = dU * ldf(w, a.ww == 1 ? row : off);
-            const float dbv = dE * sK[l], dwv = dU * ldf(v, off);
+            const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i0 + c;
+            const f32x4 bv = gate4(b, a.bw, row, i0 + c), wv = gate4(w, a.ww, row, i0 + c);
+            const f32x4 vv = load4(v + off), kv = f32x4{sK[l], sK[l + 1], sK[l + 2], sK[l + 3]};
+            *reinterpret_cast<f32x4*>(a.dq + off) = dq;
+            *reinterpret_cast<f32x4*>(a.dk + off) = dk + dE * bv;
+            *reinterpret_cast<f32x4*>(a.dv + off) = dU * wv;
+            const f32x4 dbv = dE * kv, dwv = dU * vv;
             if (a.bw == 1)
-                atomicAdd(a.db + row, dbv);
+                atomicAdd(a.db + row, dbv[0] + dbv[1] + dbv[2] + dbv[3]);
             else
-                a.db[off] = dbv;
+                *reinterpret_cast<f32x4*>(a.db + off) = dbv;
             if (a.ww == 1)
-                atomicAdd(a.dw + row, dwv);
+                atomicAdd(a.dw + row, dwv[0] + dwv[1] + dwv[2] + dwv[3]);
             else
-                a.dw[off] = dwv;
+                *reinterpret_cast<f32x4*>(a.dw + off) = dwv;
         }
     }
     __syncthreads();
