@@ -10,8 +10,8 @@ resident in device memory when the timed region starts.
 Prints one JSON line: tokens/s (B*T per step time), the roofline of the
 dominant kernel (HIP events on the launch stream, algorithmic bytes per
 launch), the fp64 CPU oracle on the host cores, and in "extra" the per-kernel
-split, the MFMA fraction and the batched decode step (256 x 16 states,
-1000 steps) in GB/s.
+split, the MFMA fraction, the batched decode step (256 x 16 states,
+1000 steps) in GB/s and the chunked backward over the same batch.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -56,6 +56,77 @@ def staged_bytes(B, T, H, D, C, esz, bw, ww, gw, s0: bool, s_out: bool):
     st = factors + rows * D * esz + (state if s0 else 0) + (state if s_out else 0)
     minimum = inputs + rows * D * esz + (state if s0 else 0) + (state if s_out else 0)
     return prep, st, minimum
+
+
+def backward_flops_per_chunk(C: int, D: int) -> int:
+    """Dense contractions of the chunked backward per (b, h, chunk), with the
+    triangular structure exploited.  Recomputed forward factors: gated Gram
+    and scores, WY solve, Delta = U~ - W S.  Reverse scan: K^ Lam, P^T dO,
+    Q~^T dO, W^T dDelta.  Chunk-local gradients: dO S^T, dDelta S^T,
+    Delta Lam^T, dO Delta^T, dDelta U^T + dW E~^T, X^T dDelta, X^T dW,
+    X^T dX X^T, and the four decay-weighted sums of dM and dP."""
+    tri = C * (C + 1) * D                 # one lower-triangular C x C x D product
+    dense = 2 * C * D * D                 # one C x D x D product
+    recompute = C * (C - 1) * D + tri + C * (C - 1) * (D + D) + dense
+    scan = 3 * dense + tri
+    grads = 3 * dense + tri + 2 * tri + 2 * tri + 2 * C * C * C * 2 // 3 + 4 * tri
+    return recompute + scan + grads
+
+
+def backward_min_bytes(B, T, H, D, esz) -> int:
+    """Fewest HBM bytes the backward can move: the forward's inputs, dO and
+    the chunk-start states read once, the fp32 gradients written once."""
+    rows = B * T * H
+    nck = -(-T // 64)
+    return rows * (5 * D * esz + D * 4 + D * esz + 6 * D * 4) + B * H * nck * D * D * 4
+
+
+def bench_backward(torch, gdr2, lib, wl, d, steps: int, warmup: int):
+    """The chunked backward over the same batch: a forward that records the
+    chunk-start states (untimed), then `steps` backward calls."""
+    from gated_delta_rule_86_amd.inputs import draw_cotangents
+
+    cot = {n: t.cuda() for n, t in draw_cotangents(wl, 1.0).items()}
+    x = [d[n] for n in NAMES]
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    _, _, ck = gdr2.forward(*x, S0=d["S0"], chunk=64, chunk_states=True)
+    grads = tuple(torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in x)
+    dS0 = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdr2.backward_workspace_size(*x), dtype=torch.uint8, device="cuda")
+    a = gdr2.bwd_args(*x, ck, cot["dO"], cot["dS_final"], grads, dS0, workspace=ws)
+    # the forward as a training step runs it: o, S_final and the chunk-start states
+    o = torch.empty_like(d["v"])
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    fws = torch.empty(gdr2.workspace_size(*x, chunk=64), dtype=torch.uint8, device="cuda")
+    f = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=64, workspace=fws, S_chunks=ck)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        assert lib.gdr2_forward_chunked(ctypes.byref(f), stream) == 0, lib.gdr2_last_error()
+        assert lib.gdr2_backward_chunked(ctypes.byref(a), stream) == 0, lib.gdr2_last_error()
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(steps):
+        lib.gdr2_forward_chunked(ctypes.byref(f), stream)
+    e1.record()
+    for _ in range(steps):
+        lib.gdr2_backward_chunked(ctypes.byref(a), stream)
+    e2.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    ms = e1.elapsed_time(e2) / steps
+    flops = backward_flops_per_chunk(64, D) * B * H * -(-T // 64)
+    mb = backward_min_bytes(B, T, H, D, 2)
+    out = {"workload": "train_4k backward: dq, dk, dv, db, dw, dg, dS0 from dO and dS_final, "
+                       "chunk-start states from the forward", "steps": steps, "ms": round(ms, 4),
+           "tokens_per_s": round(B * T / (ms * 1e-3), 1), "workspace_bytes": ws.numel(),
+           "algorithmic_flops": flops,
+           "mfma_frac_bf16_dense": round(flops / (ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+           "min_bytes": mb, "hbm_frac_of_min_bytes": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "forward_with_chunk_states_ms": round(fwd_ms, 4),
+           "train_step_tokens_per_s": round(B * T / ((fwd_ms + ms) * 1e-3), 1)}
+    del ws, fws, grads, dS0, ck, cot, o, S_out
+    return out
 
 
 def cpu_baseline(inp, wl):
@@ -139,6 +210,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy bandwidth reference")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -223,6 +295,10 @@ def main():
     }
     if not args.no_decode:
         extra["decode"] = bench_decode(torch, gdr2, lib, args.decode_steps, 20)
+    if not args.no_backward:
+        # one training step of the layer: the forward that also records the
+        # chunk-start states, then the backward
+        extra["backward"] = bench_backward(torch, gdr2, lib, wl, d, max(1, K // 2), 2)
     if measured:
         extra["hbm_traffic_bytes_per_launch"] = measured
 
