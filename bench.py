@@ -11,7 +11,8 @@ Prints one JSON line: tokens/s (B*T per step time), the roofline of the
 dominant kernel (HIP events on the launch stream, algorithmic bytes per
 launch), the fp64 CPU oracle on the host cores, and in "extra" the per-kernel
 split, the MFMA fraction, the batched decode step (256 x 16 states,
-1000 steps) in GB/s and the chunked backward over the same batch.
+1000 steps) in GB/s, the forward for each gate-width mix and the chunked
+backward over the same batch.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -129,6 +130,43 @@ def bench_backward(torch, gdr2, lib, wl, d, steps: int, warmup: int):
     return out
 
 
+def bench_gate_widths(torch, gdr2, lib, d, steps: int):
+    """The forward at the same shape for each gate-width mix: per-channel
+    (GDN-2), KDA (scalar erase and write gate, per-channel decay), GDN (all
+    scalar), the two ablation variants (one scalar gate) and scalar decay
+    with per-channel gates.  Width-1 gates are channel 0 of the same draw."""
+    x = {n: d[n] for n in NAMES}
+    mixes = [("gdn2_per_channel", False, False, False), ("kda_scalar_b_w", True, True, False),
+             ("gdn_all_scalar", True, True, True), ("scalar_write", False, True, False),
+             ("scalar_erase", True, False, False), ("scalar_decay", False, False, True)]
+    B, T, H, D = x["q"].shape
+    o = torch.empty_like(x["v"])
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+    for name, nb, nw, ng in mixes:
+        b = x["b"][..., :1].contiguous() if nb else x["b"]
+        w = x["w"][..., :1].contiguous() if nw else x["w"]
+        g = x["g"][..., :1].contiguous() if ng else x["g"]
+        args = (x["q"], x["k"], x["v"], b, w, g)
+        ws = torch.empty(gdr2.workspace_size(*args, chunk=64), dtype=torch.uint8, device="cuda")
+        a = gdr2.fwd_args(*args, S0=d["S0"], o=o, S_out=S_out, chunk=64, workspace=ws)
+        for _ in range(3):
+            lib.gdr2_forward_chunked(ctypes.byref(a), stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            lib.gdr2_forward_chunked(ctypes.byref(a), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out.append({"gates": name, "widths_b_w_g": [b.shape[-1], w.shape[-1], g.shape[-1]],
+                    "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1)})
+        del ws
+    return out
+
+
 def cpu_baseline(inp, wl):
     """The fp64 oracle (as it stands) on the host cores over the whole
     workload batch: every (b, h) recurrence, OpenMP over them."""
@@ -211,6 +249,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-gate-widths", action="store_true", help="skip the gate-width sweep")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy bandwidth reference")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -295,6 +334,8 @@ def main():
     }
     if not args.no_decode:
         extra["decode"] = bench_decode(torch, gdr2, lib, args.decode_steps, 20)
+    if not args.no_gate_widths:
+        extra["gate_widths"] = bench_gate_widths(torch, gdr2, lib, d, K)
     if not args.no_backward:
         # one training step of the layer: the forward that also records the
         # chunk-start states, then the backward

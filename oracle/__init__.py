@@ -27,6 +27,8 @@ import threading
 
 import numpy as np
 
+from . import prologue as _pro
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdr2_oracle.c")
 _LIB = os.path.join(_HERE, "libgdr2_oracle.so")
@@ -93,14 +95,16 @@ def _width(gate, full, name):
     return wdt
 
 
-def forward(q, k, v, b, w, g, S0=None, threads: int = 0, lib=None):
+def forward(q, k, v, b, w, g, S0=None, threads: int = 0, lib=None, prologue: int = 0):
     """Sequential fp64 forward.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; b: [B,T,H,1|dk]; w: [B,T,H,1|dv];
     g: [B,T,H,1|dk] (log-decay); S0: [B,H,dk,dv] or None (zeros).
+    prologue: bits of oracle.prologue applied to the raw q, k, b, w, g first.
     Returns (o [B,T,H,dv], S_final [B,H,dk,dv]) as float64 arrays.
     """
     lib = lib or load()
+    q, k, b, w, g = _pro.apply(q, k, b, w, g, prologue)
     q, k, v, b, w, g = (_f64(x) for x in (q, k, v, b, w, g))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -120,7 +124,8 @@ def forward(q, k, v, b, w, g, S0=None, threads: int = 0, lib=None):
     return o, S
 
 
-def forward_checkpoints(q, k, v, b, w, g, every: int, S0=None, threads: int = 0, lib=None):
+def forward_checkpoints(q, k, v, b, w, g, every: int, S0=None, threads: int = 0, lib=None,
+                        prologue: int = 0):
     """Sequential fp64 forward that also records the state before every
     `every`-th token (a checkpoint at each segment boundary).
 
@@ -128,6 +133,7 @@ def forward_checkpoints(q, k, v, b, w, g, every: int, S0=None, threads: int = 0,
     S_ckpt[:, :, n] is the state before token n*every (S_ckpt[:, :, 0] = S0).
     """
     lib = lib or load()
+    q, k, b, w, g = _pro.apply(q, k, b, w, g, prologue)
     q, k, v, b, w, g = (_f64(x) for x in (q, k, v, b, w, g))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -144,13 +150,21 @@ def forward_checkpoints(q, k, v, b, w, g, every: int, S0=None, threads: int = 0,
     return o, S, ck
 
 
-def backward(q, k, v, b, w, g, dO, S0=None, dS_final=None, threads: int = 0, lib=None):
+def backward(q, k, v, b, w, g, dO, S0=None, dS_final=None, threads: int = 0, lib=None,
+             prologue: int = 0):
     """Sequential fp64 gradients of a loss through the forward.
 
     dO: dL/do [B,T,H,dv]; dS_final: dL/dS_final [B,H,dk,dv] or None (zero).
+    prologue: bits of oracle.prologue; the gradients are then with respect
+    to the raw inputs (the prologue's chain rule is applied last).
     Returns a dict with dq, dk, dv, db, dw, dg (shaped like the inputs; a
     width-1 gate's gradient is summed over its channels) and dS0.
     """
+    if prologue:
+        raw = (q, k, b, w, g)
+        pq, pk, pb, pw, pg = _pro.apply(*raw, prologue)
+        grads = backward(pq, pk, v, pb, pw, pg, dO, S0=S0, dS_final=dS_final, threads=threads, lib=lib)
+        return _pro.backward(*raw, prologue, grads)
     lib = lib or load()
     q, k, v, b, w, g, dO = (_f64(x) for x in (q, k, v, b, w, g, dO))
     B, T, H, dk = q.shape
@@ -171,13 +185,15 @@ def backward(q, k, v, b, w, g, dO, S0=None, dS_final=None, threads: int = 0, lib
     return out
 
 
-def decode_step(state, q, k, v, b, w, g, threads: int = 0, lib=None):
+def decode_step(state, q, k, v, b, w, g, threads: int = 0, lib=None, prologue: int = 0):
     """One decode step, in place on ``state`` [N,H,dk,dv] (float64, contiguous).
 
     q, k: [N,H,dk]; v: [N,H,dv]; b: [N,H,1|dk]; w: [N,H,1|dv]; g: [N,H,1|dk].
+    prologue: bits of oracle.prologue applied to the raw token inputs first.
     Returns o [N,H,dv].
     """
     lib = lib or load()
+    q, k, b, w, g = _pro.apply(q, k, b, w, g, prologue)
     if not (isinstance(state, np.ndarray) and state.dtype == np.float64
             and state.flags["C_CONTIGUOUS"]):
         raise TypeError("state must be a C-contiguous float64 array (updated in place)")

@@ -382,6 +382,94 @@ def pin_backward_linear_attention(lib, seed=14):
     return worst
 
 
+def pin_prologue_normalised_retrieval(lib, seed=15):
+    """[GDN2] takes the key L2-normalised.  With the prologue's NORM_QK bit a
+    raw key of any length behaves as the unit key: b = 1 makes the erase
+    remove exactly what the key reads, so S_t^T k^_t = w_t * v_t (up to the
+    epsilon's relative 1e-6 / |k|^2), and the readout of q equals that of
+    q / |q|.  Without the bit the identity fails for |k| != 1."""
+    from oracle import prologue as pro
+    rng = np.random.default_rng(seed)
+    p = rand_problem(rng, B=2, T=5, H=2, unit_k=False)
+    p["k"] *= 3.0                     # |k| ~ 3 * sqrt(dk): far from unit length
+    p["b"] = np.ones_like(p["b"])
+    S0 = rng.standard_normal((2, 2, 6, 5))
+    worst = 0.0
+    for T in range(1, 6):
+        sub = {m: a[:, :T] for m, a in p.items()}
+        o, S = oracle.forward(**sub, S0=S0, lib=lib, prologue=pro.NORM_QK)
+        kT = sub["k"][:, T - 1]
+        kn = kT / np.sqrt((kT * kT).sum(-1, keepdims=True) + pro.NORM_EPS)
+        lhs = np.einsum("bhij,bhi->bhj", S, kn)
+        rhs = sub["w"][:, T - 1] * sub["v"][:, T - 1]
+        worst = max(worst, np.abs(lhs - rhs).max() / 1e-6)      # scaled: a 1e-6 residual is the epsilon
+        # readout of the raw q equals the readout through the normalised q
+        qT = sub["q"][:, T - 1]
+        qn = qT / np.sqrt((qT * qT).sum(-1, keepdims=True) + pro.NORM_EPS)
+        worst = max(worst, np.abs(o[:, T - 1] - np.einsum("bhij,bhi->bhj", S, qn)).max() / 1e-12)
+    _, S = oracle.forward(**p, S0=S0, lib=lib)                 # without the bit: no identity
+    lhs = np.einsum("bhij,bhi->bhj", S, p["k"][:, -1] / np.linalg.norm(p["k"][:, -1], axis=-1, keepdims=True))
+    assert np.abs(lhs - p["w"][:, -1] * p["v"][:, -1]).max() > 1e-3
+    return worst
+
+
+def pin_prologue_gate_values(lib, seed=16):
+    """The GATES bit at points where the activations have closed forms:
+    pre-activations 0 give b = w = 1/2 and decay exp(-ln 2) = 1/2; b, w
+    pre-activations of -40 give gates of ~4e-18 and a decay pre-activation
+    of -40 gives no decay (g ~ -4e-18).  Compared with the plain recurrence
+    on those gate values."""
+    from oracle import prologue as pro
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for bv, wv, gv, b_eff, w_eff, g_eff in ((0.0, 0.0, 0.0, 0.5, 0.5, -np.log(2.0)),
+                                             (-40.0, 0.0, -40.0, 0.0, 0.5, 0.0),
+                                             (0.0, -40.0, 0.0, 0.5, 0.0, -np.log(2.0))):
+        p = rand_problem(rng, B=1, T=6, H=2)
+        S0 = rng.standard_normal((1, 2, 6, 5))
+        raw = {**p, "b": np.full_like(p["b"], bv), "w": np.full_like(p["w"], wv), "g": np.full_like(p["g"], gv)}
+        eff = {**p, "b": np.full_like(p["b"], b_eff), "w": np.full_like(p["w"], w_eff),
+               "g": np.full_like(p["g"], g_eff)}
+        o1, S1 = oracle.forward(**raw, S0=S0, lib=lib, prologue=pro.GATES)
+        o2, S2 = oracle.forward(**eff, S0=S0, lib=lib)
+        worst = max(worst, np.abs(o1 - o2).max(), np.abs(S1 - S2).max())
+    return worst
+
+
+def pin_prologue_finite_differences(lib, seed=17):
+    """The backward with the prologue (both bits, every gate width) against
+    central finite differences of L = <dO, o> + <dS_final, S_final> through
+    the prologue and the forward, in the raw inputs."""
+    from oracle import prologue as pro
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for bw, ww, gw in ((None, None, None), (1, 1, 1), (1, None, 1)):
+        p = rand_problem(rng, B=1, T=5, H=1, dk=4, dv=3, bw=bw, ww=ww, gw=gw, unit_k=False)
+        p["b"] = rng.standard_normal(p["b"].shape)       # pre-activations
+        p["w"] = rng.standard_normal(p["w"].shape)
+        p["g"] = rng.standard_normal(p["g"].shape)
+        S0 = rng.standard_normal((1, 1, 4, 3))
+        dO = rng.standard_normal((1, 5, 1, 3))
+        dSf = rng.standard_normal((1, 1, 4, 3))
+        gr = oracle.backward(**p, dO=dO, S0=S0, dS_final=dSf, lib=lib, prologue=pro.ALL)
+
+        def loss(pp):
+            o, S = oracle.forward(**pp, S0=S0, lib=lib, prologue=pro.ALL)
+            return float((o * dO).sum() + (S * dSf).sum())
+        h = 1e-6
+        for name in ("q", "k", "v", "b", "w", "g"):
+            fd = np.zeros_like(p[name])
+            for idx in np.ndindex(p[name].shape):
+                x = p[name].copy()
+                x[idx] += h
+                lp = loss({**p, name: x})
+                x[idx] -= 2 * h
+                lm = loss({**p, name: x})
+                fd[idx] = (lp - lm) / (2 * h)
+            worst = max(worst, float(np.abs(fd - gr["d" + name]).max() / max(np.abs(fd).max(), 1.0)))
+    return worst
+
+
 ALL_PINS = {
     "retrieval_identity": pin_retrieval_identity,
     "one_step_all_gates": pin_one_step_all_gates,
@@ -398,6 +486,9 @@ ALL_PINS = {
     "checkpoints_are_prefix_states": pin_checkpoints_are_prefix_states,
     "backward_finite_differences": pin_backward_finite_differences,
     "backward_linear_attention": pin_backward_linear_attention,
+    "prologue_normalised_retrieval": pin_prologue_normalised_retrieval,
+    "prologue_gate_values": pin_prologue_gate_values,
+    "prologue_finite_differences": pin_prologue_finite_differences,
 }
 
 # Residual bounds: fp64 arithmetic on O(1) values over a few tokens.
@@ -405,4 +496,7 @@ TOL = {name: 1e-12 for name in ALL_PINS}
 TOL["segment_chaining"] = 0.0           # identical operations in identical order
 TOL["checkpoints_are_prefix_states"] = 0.0
 TOL["backward_finite_differences"] = 1e-7   # central differences, h = 1e-6, in fp64
+TOL["prologue_finite_differences"] = 1e-7
+TOL["prologue_normalised_retrieval"] = 1.0   # residuals scaled: epsilon-sized and rounding-sized
+TOL["prologue_gate_values"] = 1e-12
 TOL["hand_example"] = 1e-14

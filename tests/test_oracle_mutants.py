@@ -4,6 +4,7 @@ part of the recurrence (decay, erase, write, readout, gate broadcasting)."""
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -105,3 +106,65 @@ def test_readout_before_update_is_caught(tmp_path):
 def test_mutant_is_caught(tmp_path, name, old, new):
     lib = _build_mutant(tmp_path, name, old, new)
     assert _caught(lib), f"mutant {name} passes every pin"   # NaN residuals count as caught
+
+
+# Mistakes planted in the prologue (oracle/prologue.py), each of which must
+# fail a prologue pin.
+def _mut_norm_axis(q, k, b, w, g, flags):
+    from oracle import prologue as pro
+    q, k, b, w, g = (np.asarray(x, np.float64) for x in (q, k, b, w, g))
+    if flags & pro.NORM_QK:                                   # over heads instead of channels
+        q = q / np.sqrt((q * q).sum(-2, keepdims=True) + pro.NORM_EPS)
+        k = k / np.sqrt((k * k).sum(-2, keepdims=True) + pro.NORM_EPS)
+    if flags & pro.GATES:
+        b, w, g = pro._sigmoid(b), pro._sigmoid(w), -pro._softplus(g)
+    return q, k, b, w, g
+
+
+def _mut_decay_sign(q, k, b, w, g, flags):
+    from oracle import prologue as pro
+    q, k, b, w, g = _ORIG_APPLY(q, k, b, w, g, flags & pro.NORM_QK)
+    if flags & pro.GATES:
+        b, w, g = pro._sigmoid(b), pro._sigmoid(w), pro._softplus(g)
+    return q, k, b, w, g
+
+
+def _mut_sigmoid_grad(q, k, b, w, g, flags, grads):
+    out = _ORIG_BACKWARD(q, k, b, w, g, flags, grads)
+    from oracle import prologue as pro
+    if flags & pro.GATES:
+        out["db"] = np.asarray(grads["db"]) * pro._sigmoid(np.asarray(b))
+    return out
+
+
+def _mut_norm_grad(q, k, b, w, g, flags, grads):
+    out = _ORIG_BACKWARD(q, k, b, w, g, flags, grads)
+    from oracle import prologue as pro
+    if flags & pro.NORM_QK:                                   # Jacobian without the projection
+        kk = np.asarray(k, np.float64)
+        out["dk"] = np.asarray(grads["dk"]) / np.sqrt((kk * kk).sum(-1, keepdims=True) + pro.NORM_EPS)
+    return out
+
+
+from oracle import prologue as _prologue_mod  # noqa: E402
+
+_ORIG_APPLY = _prologue_mod.apply
+_ORIG_BACKWARD = _prologue_mod.backward
+PROLOGUE_MUTANTS = [("norm_over_heads", "apply", _mut_norm_axis), ("decay_sign", "apply", _mut_decay_sign),
+                    ("sigmoid_derivative", "backward", _mut_sigmoid_grad),
+                    ("norm_jacobian_no_projection", "backward", _mut_norm_grad)]
+
+
+@pytest.mark.parametrize("name,attr,fn", PROLOGUE_MUTANTS, ids=[m[0] for m in PROLOGUE_MUTANTS])
+def test_prologue_mutant_is_caught(monkeypatch, name, attr, fn):
+    monkeypatch.setattr(_prologue_mod, attr, fn)
+    lib = oracle.load()
+    failed = []
+    for pin in ("prologue_normalised_retrieval", "prologue_gate_values", "prologue_finite_differences"):
+        try:
+            res = pins.ALL_PINS[pin](lib)
+            if not res <= pins.TOL[pin]:
+                failed.append(pin)
+        except AssertionError:
+            failed.append(pin)
+    assert failed, f"prologue mutant {name} survived every prologue pin"
