@@ -155,8 +155,8 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
         return fail(GDR2_ERR_INVALID_ARG, "unknown algo %d", a->algo);
     if (a->stage != GDR2_STAGE_ALL && a->stage != GDR2_STAGE_PREP && a->stage != GDR2_STAGE_STATE)
         return fail(GDR2_ERR_INVALID_ARG, "unknown stage %d", a->stage);
-    if (a->reserved != 0)
-        return fail(GDR2_ERR_INVALID_ARG, "reserved field must be 0");
+    if (a->prologue & ~(GDR2_PROLOGUE_NORM_QK | GDR2_PROLOGUE_GATES))
+        return fail(GDR2_ERR_INVALID_ARG, "unknown prologue bits 0x%x", a->prologue);
     if (a->chunk != 32 && a->chunk != 64)
         return fail(GDR2_ERR_UNSUPPORTED, "supported chunk sizes: 32, 64 (got %d)", a->chunk);
     if (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096)
@@ -233,8 +233,8 @@ gdr2_status validate_backward(const gdr2_bwd_args* a)
     gdr2_status s = check_common(rows, a->Dk, a->Dv, a->dtype, a->b_width, a->w_width, a->g_width);
     if (s != GDR2_OK)
         return s;
-    if (a->reserved != 0)
-        return fail(GDR2_ERR_INVALID_ARG, "reserved field must be 0");
+    if (a->prologue & ~(GDR2_PROLOGUE_NORM_QK | GDR2_PROLOGUE_GATES))
+        return fail(GDR2_ERR_INVALID_ARG, "unknown prologue bits 0x%x", a->prologue);
     if (a->chunk != 64)
         return fail(GDR2_ERR_UNSUPPORTED, "the backward supports chunk 64 only (got %d)", a->chunk);
     const int64_t nchunks = (a->T + 63) / 64;
@@ -374,6 +374,10 @@ gdr2_status gdr2_decode_step(const gdr2_decode_args* a, void* stream_)
     gdr2_status s = check_common(rows, a->Dk, a->Dv, a->dtype, a->b_width, a->w_width, a->g_width);
     if (s != GDR2_OK)
         return s;
+    if (a->prologue & ~(GDR2_PROLOGUE_NORM_QK | GDR2_PROLOGUE_GATES))
+        return fail(GDR2_ERR_INVALID_ARG, "unknown prologue bits 0x%x", a->prologue);
+    if (a->reserved != 0)
+        return fail(GDR2_ERR_INVALID_ARG, "reserved field must be 0");
     if (rows > (int64_t)INT32_MAX)
         return fail(GDR2_ERR_UNSUPPORTED, "too many states for one launch");
     if (!mul_ok(rows, a->Dk * a->Dv * 4, &state_bytes))

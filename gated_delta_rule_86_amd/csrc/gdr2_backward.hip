@@ -55,6 +55,8 @@ struct BwdLayout {
     size_t P, X, dP, dX, T1, dM;
     // [D] per record
     size_t gam;
+    // [2][C] per record: prologue 1/|k|, 1/|q| of every token
+    size_t RN;
     // [D][D] per record: state gradient at every chunk end
     size_t Lam;
     // scan operand fragments (ScanFrags), rec_bytes per record
@@ -82,6 +84,8 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes)
     }
     L.gam = o;
     o += d1;
+    L.RN = o;
+    o += a64((size_t)L.nrec * 2 * BC);
     L.Lam = o;
     o += dd;
     L.SF = o;
@@ -98,6 +102,7 @@ struct BwdArgs {
     const float* dS_final;
     float *dq, *dk, *dv, *db, *dw, *dg, *dS0;
     int bw, ww, gw;
+    int pro;             // prologue bits
     int64_t T, H, NC, nrec, nbh;
     float* ws;           // workspace base (fp32)
     BwdLayout L;
@@ -175,6 +180,12 @@ __device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float*
 }
 
 __device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
+__device__ __forceinline__ float bsigm(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float bneg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))); }
+__device__ __forceinline__ f32x4 bsigm4(f32x4 x) { return f32x4{bsigm(x[0]), bsigm(x[1]), bsigm(x[2]), bsigm(x[3])}; }
+constexpr float kNormEps = 1e-6f;
 __device__ __forceinline__ void st4s(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
 // Four consecutive channels of a gate of width 1 or D at element row `row`.
@@ -220,9 +231,35 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             gv = gate4(a.g, a.gw, row, i);
             kv = load4(k + row * D + i);
             qv = load4(q + row * D + i);
-            ev = gate4(b, a.bw, row, i) * kv;
-            uv = gate4(w, a.ww, row, i) * load4(v + row * D + i);
+            f32x4 bv = gate4(b, a.bw, row, i), wv = gate4(w, a.ww, row, i);
+            if (a.pro & GDR2_PROLOGUE_GATES) {
+                bv = bsigm4(bv);
+                wv = bsigm4(wv);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    gv[j] = bneg_softplus(gv[j]);
+            }
+            ev = bv;
+            uv = wv * load4(v + row * D + i);
         }
+        if (a.pro & GDR2_PROLOGUE_NORM_QK) {
+            // unit L2 norm per token: the Q4 items of a row are Q4 consecutive lanes
+            float sk = kv[0] * kv[0] + kv[1] * kv[1] + kv[2] * kv[2] + kv[3] * kv[3];
+            float sq = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
+#pragma unroll
+            for (int m = 1; m < Q4; m <<= 1) {
+                sk += __shfl_xor(sk, m);
+                sq += __shfl_xor(sq, m);
+            }
+            const float rk = rsqrtf(sk + kNormEps), rq = rsqrtf(sq + kNormEps);
+            kv = kv * rk;
+            qv = qv * rq;
+            if (i == 0) {
+                ws[a.L.RN + (size_t)r * 2 * C + t] = rk;
+                ws[a.L.RN + (size_t)r * 2 * C + C + t] = rq;
+            }
+        }
+        ev = ev * kv;
         st4s(sG + l, gv);
         st4s(sK + l, kv);
         st4s(sQ + l, qv);
@@ -801,6 +838,10 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             const int64_t row = rc.row0 + (int64_t)t * a.H;
             kv = load4(k + row * D + i0 + c);
             qv = load4(q + row * D + i0 + c);
+            if (a.pro & GDR2_PROLOGUE_NORM_QK) {
+                kv = kv * ws[a.L.RN + (size_t)r * 2 * C + t];
+                qv = qv * ws[a.L.RN + (size_t)r * 2 * C + C + t];
+            }
         }
         const f32x4 gv = *reinterpret_cast<const f32x4*>(ws + a.L.G + x);
         const f32x4 ev = *reinterpret_cast<const f32x4*>(ws + a.L.E + x);
@@ -921,12 +962,20 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i0 + c;
-            const f32x4 bv = gate4(b, a.bw, row, i0 + c), wv = gate4(w, a.ww, row, i0 + c);
+            f32x4 bv = gate4(b, a.bw, row, i0 + c), wv = gate4(w, a.ww, row, i0 + c);
+            // prologue gates: the activated values, and d(activation)/d(raw)
+            f32x4 bd = {1.f, 1.f, 1.f, 1.f}, wd = bd;
+            if (a.pro & GDR2_PROLOGUE_GATES) {
+                bv = bsigm4(bv);
+                wv = bsigm4(wv);
+                bd = bv * (f32x4{1.f, 1.f, 1.f, 1.f} - bv);
+                wd = wv * (f32x4{1.f, 1.f, 1.f, 1.f} - wv);
+            }
             const f32x4 vv = load4(v + off), kv = f32x4{sK[l], sK[l + 1], sK[l + 2], sK[l + 3]};
             *reinterpret_cast<f32x4*>(a.dq + off) = dq;
             *reinterpret_cast<f32x4*>(a.dk + off) = dk + dE * bv;
             *reinterpret_cast<f32x4*>(a.dv + off) = dU * wv;
-            const f32x4 dbv = dE * kv, dwv = dU * vv;
+            const f32x4 dbv = dE * kv * bd, dwv = dU * vv * wd;
             if (a.bw == 1)
                 atomicAdd(a.db + row, dbv[0] + dbv[1] + dbv[2] + dbv[3]);
             else
@@ -953,11 +1002,47 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         if (t >= rc.L)
             continue;
         const int64_t row = rc.row0 + (int64_t)t * a.H;
-        const float dgv = sdG[t * LC + il];
+        float dgv = sdG[t * LC + il];
+        if (a.pro & GDR2_PROLOGUE_GATES)      // d/dx[-softplus(x)] = -sigmoid(x)
+            dgv *= -bsigm(a.g[a.gw == 1 ? row : row * D + i]);
         if (a.gw == 1)
             atomicAdd(a.dg + row, dgv);
         else
             a.dg[row * D + i] = dgv;
+    }
+}
+
+// The prologue's normalisation, backwards: with y = x r, r = (|x|^2 + eps)^-1/2,
+// dx = r (dy - y (y . dy)), in place on dq and dk.  A row (token, head) of D
+// channels is D/4 consecutive threads, 4 channels each.
+template <typename E, int D>
+__global__ __launch_bounds__(NTB) void bwd_norm_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                       float* __restrict__ dq, float* __restrict__ dk,
+                                                       int64_t rows)
+{
+    constexpr int TPR = D / 4, RPB = NTB / TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = 4 * (threadIdx.x % TPR);
+    const bool ok = row < rows;
+    const int64_t off = (ok ? row : 0) * D + c;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const E* x = which == 0 ? q : k;
+        float* dx = which == 0 ? dq : dk;
+        const f32x4 xv = load4(x + off);
+        const f32x4 dy = ok ? *reinterpret_cast<const f32x4*>(dx + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        float ss = xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1)
+            ss += __shfl_xor(ss, m);
+        const float rn = rsqrtf(ss + kNormEps);
+        const f32x4 y = xv * rn;
+        float yd = y[0] * dy[0] + y[1] * dy[1] + y[2] * dy[2] + y[3] * dy[3];
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1)
+            yd += __shfl_xor(yd, m);
+        if (ok)
+            *reinterpret_cast<f32x4*>(dx + off) = rn * (dy - y * yd);
     }
 }
 
@@ -994,7 +1079,7 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     a.q = x.q; a.k = x.k; a.v = x.v; a.b = x.b; a.w = x.w; a.g = x.g; a.dO = x.dO;
     a.S_chunks = x.S_chunks; a.dS_final = x.dS_final;
     a.dq = x.dq; a.dk = x.dk; a.dv = x.dv; a.db = x.db; a.dw = x.dw; a.dg = x.dg; a.dS0 = x.dS0;
-    a.bw = x.b_width; a.ww = x.w_width; a.gw = x.g_width;
+    a.bw = x.b_width; a.ww = x.w_width; a.gw = x.g_width; a.pro = x.prologue;
     a.T = x.T; a.H = x.H; a.NC = cdiv(x.T, C);
     a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC);
     a.nbh = x.B * x.H;
@@ -1053,6 +1138,12 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     if ((e = gemm(s, nrec, C, C, C, op(L.X, CC, C, 1), op(L.T1, CC, C, 0), ws + L.dM, CC, C, -1.f, 0.f, nullptr, 0, 2)) != hipSuccess) return e;
 
     hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(nrec * (D / DC))), dim3(NTB), lds_decay, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.pro & GDR2_PROLOGUE_NORM_QK) {
+        constexpr int RPB = NTB / (D / 4);
+        hipLaunchKernelGGL((bwd_norm_kernel<E, D>), dim3((unsigned)cdiv(rows, RPB)), dim3(NTB), 0, s,
+                           (const E*)x.q, (const E*)x.k, x.dq, x.dk, rows);
+    }
     return hipGetLastError();
 }
 

@@ -142,6 +142,7 @@ struct PrepArgs {
     const void *q, *k, *v, *b, *w;
     const float* g;
     int bw, ww, gw;
+    int pro;                  // prologue bits (normalise q, k; activate gates)
     int64_t T, H, NC, nrec;
     void *Wn, *Ut, *Kh, *Qt, *P;
     float* gam;
@@ -226,6 +227,11 @@ template <> __device__ __forceinline__ int kpos<float>(int col) { return col; }
 
 // s_waitcnt lgkmcnt(0) with a compiler barrier: LDS writes of this wave are
 // complete before any later LDS read of it (lanes exchange data this way).
+// Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
+__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))); }
+constexpr float kNormEps = 1e-6f;
+
 __device__ __forceinline__ void lds_fence_wave()
 {
     __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -356,7 +362,8 @@ struct PrepShape {
     static constexpr size_t OFF_X = al256(OFF_XC + (size_t)NB * 16 * LDX * 4);  // X [C][LDXP] in fragment k order
     static constexpr size_t OFF_TOT = al256(OFF_X + (size_t)C * LDXP * ES);     // wave totals [NWB][D]
     static constexpr size_t OFF_FK = OFF_TOT + (size_t)NWB * D * 4;             // 2^(G_L - Gh) [NH][D]
-    static constexpr size_t OFF_FLAG = OFF_FK + (size_t)NH * D * 4;
+    static constexpr size_t OFF_RN = OFF_FK + (size_t)NH * D * 4;               // prologue: 1/|k|, 1/|q| [2][C]
+    static constexpr size_t OFF_FLAG = OFF_RN + (size_t)2 * C * 4;
     static constexpr size_t SMEM = OFF_FLAG + 16;                               // dynamic LDS
     // raw g [C][D] (exact path: G) lives in its own static LDS object, so the
     // compiler knows the asynchronous copies into it touch nothing else
@@ -441,10 +448,10 @@ __device__ __forceinline__ void prep_copy_g(const PrepArgs& a, const ChunkPos& c
 
 // Phase B for one lane: decay-referenced operands of its tokens into LDS.
 // VALID: every token of the chunk is valid (no zeroing needed).
-template <bool VALID, bool SECOND, typename E, int D, int C>
+template <bool VALID, bool SECOND, bool PRO, typename E, int D, int C>
 __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const float (*G)[16 / sizeof(E)],
                                                const float* gh, int bw, int ww, int L, int t0, int c0,
-                                               unsigned char* smem)
+                                               unsigned char* smem, int pro)
 {
     typedef PrepShape<E, D, C> S;
     constexpr int VEC = S::VEC;
@@ -476,6 +483,25 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
             mx = fmaxf(mx, fmaxf(fabsf(d[x]), g));
         }
         unpack<E>(R.k[j], kk);
+        if constexpr (PRO) {
+            // prologue: unit L2 norm per token over the row, whose channel
+            // groups sit in the lanes lane % LPC + LPC * m
+            if (pro & GDR2_PROLOGUE_NORM_QK) {
+                float ss = 0.f;
+#pragma unroll
+                for (int x = 0; x < VEC; ++x)
+                    ss += kk[x] * kk[x];
+#pragma unroll
+                for (int m = S::LPC; m < 64; m <<= 1)
+                    ss += __shfl_xor(ss, m);
+                const float rk = rsqrtf(ss + kNormEps);
+#pragma unroll
+                for (int x = 0; x < VEC; ++x)
+                    kk[x] *= rk;
+                if (c0 == 0)
+                    reinterpret_cast<float*>(smem + S::OFF_RN)[t] = rk;
+            }
+        }
 #pragma unroll
         for (int x = 0; x < VEC; ++x) {
             kk[x] = valid ? kk[x] : 0.f;
@@ -487,7 +513,15 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
         {
             float bb[VEC];
             unpack<E>(R.b[j], bb);
-            const float bs = scalar0<E>(R.b[j]);
+            float bs = scalar0<E>(R.b[j]);
+            if constexpr (PRO) {
+                if (pro & GDR2_PROLOGUE_GATES) {
+                    bs = sigm(bs);
+#pragma unroll
+                    for (int x = 0; x < VEC; ++x)
+                        bb[x] = sigm(bb[x]);
+                }
+            }
 #pragma unroll
             for (int x = 0; x < VEC; ++x) {
                 tmp[x] = (bw == 1 ? bs : bb[x]) * kk[x] * eh[x];
@@ -502,6 +536,23 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
         {
             float qq[VEC];
             unpack<E>(R.q[j], qq);
+            if constexpr (PRO) {
+                if (pro & GDR2_PROLOGUE_NORM_QK) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int x = 0; x < VEC; ++x)
+                        ss += qq[x] * qq[x];
+#pragma unroll
+                    for (int m = S::LPC; m < 64; m <<= 1)
+                        ss += __shfl_xor(ss, m);
+                    const float rq = rsqrtf(ss + kNormEps);
+#pragma unroll
+                    for (int x = 0; x < VEC; ++x)
+                        qq[x] *= rq;
+                    if (c0 == 0)
+                        reinterpret_cast<float*>(smem + S::OFF_RN)[C + t] = rq;
+                }
+            }
 #pragma unroll
             for (int x = 0; x < VEC; ++x) {
                 tmp[x] = (valid ? qq[x] : 0.f) * eh[x];
@@ -517,7 +568,15 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
             float vv[VEC], wv[VEC];
             unpack<E>(R.v[j], vv);
             unpack<E>(R.w[j], wv);
-            const float ws = scalar0<E>(R.w[j]);
+            float ws = scalar0<E>(R.w[j]);
+            if constexpr (PRO) {
+                if (pro & GDR2_PROLOGUE_GATES) {
+                    ws = sigm(ws);
+#pragma unroll
+                    for (int x = 0; x < VEC; ++x)
+                        wv[x] = sigm(wv[x]);
+                }
+            }
 #pragma unroll
             for (int x = 0; x < VEC; ++x)
                 tmp[x] = (valid ? (ww == 1 ? ws : wv[x]) : 0.f) * vv[x];
@@ -544,7 +603,7 @@ __device__ __forceinline__ typename Mma16<E>::Frag row4(const E* base, int r, in
     return Mma16<E>::load(base + swz<E, D>(r, col));
 }
 
-template <bool FULL, typename E, int D, int C>
+template <bool FULL, bool PRO, typename E, int D, int C>
 __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 {
     typedef PrepShape<E, D, C> S;
@@ -643,15 +702,23 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 #pragma unroll
             for (int j = 0; j < S::TPL; ++j) {
                 const bool valid = full_chunk || t0 + j < cp.L;
+                const bool act = PRO && (a.pro & GDR2_PROLOGUE_GATES);
                 if (gw == 1) {
-                    const float gv = sG[t0 + j];
+                    float gv = sG[t0 + j];
+                    if (act)
+                        gv = neg_softplus(gv);
 #pragma unroll
                     for (int x = 0; x < VEC; ++x)
                         G[j][x] = valid ? gv * kLog2e : 0.f;
                 } else {
 #pragma unroll
                     for (int x4 = 0; x4 < VEC / 4; ++x4) {
-                        const f32x4 gv = *reinterpret_cast<const f32x4*>(sG + (t0 + j) * D + c0 + 4 * x4);
+                        f32x4 gv = *reinterpret_cast<const f32x4*>(sG + (t0 + j) * D + c0 + 4 * x4);
+                        if (act) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                gv[i] = neg_softplus(gv[i]);
+                        }
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             G[j][4 * x4 + i] = valid ? gv[i] * kLog2e : 0.f;
@@ -754,11 +821,11 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             }
             float mx;
             if (second)
-                mx = full_chunk ? prep_operands<true, true, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem)
-                                : prep_operands<false, true, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem);
+                mx = full_chunk ? prep_operands<true, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro)
+                                : prep_operands<false, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro);
             else
-                mx = full_chunk ? prep_operands<true, false, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem)
-                                : prep_operands<false, false, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem);
+                mx = full_chunk ? prep_operands<true, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro)
+                                : prep_operands<false, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro);
             if (mx > kSpanMax)
                 *sFlag = 1;
             if (pre)
@@ -846,6 +913,9 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             const E* q = (const E*)a.q;
             const E* k = (const E*)a.k;
             const E* b = (const E*)a.b;
+            // prologue: per-token 1/|k|, 1/|q| from phase B, sigmoid on b
+            const float* sRn = reinterpret_cast<const float*>(smem + S::OFF_RN);
+            const bool pn = PRO && (a.pro & GDR2_PROLOGUE_NORM_QK), pg = PRO && (a.pro & GDR2_PROLOGUE_GATES);
             // M, every pair s < t
             for (int e = tid; e < C * C; e += NTP) {
                 const int t = e / C, s = e % C;
@@ -855,10 +925,14 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
                 if (t < cp.L) {
                     const int64_t xr = cp.row0 + (int64_t)t * a.H, xs = cp.row0 + (int64_t)s * a.H;
                     for (int i = 0; i < D; ++i) {
-                        const float br = to_f32(bw == 1 ? b[xr] : b[xr * D + i]);
+                        float br = to_f32(bw == 1 ? b[xr] : b[xr * D + i]);
+                        if (pg)
+                            br = sigm(br);
                         m += br * to_f32(k[xr * D + i]) * to_f32(k[xs * D + i]) *
                              fast_exp2(sG[t * D + i] - sG[s * D + i]);
                     }
+                    if (pn)
+                        m *= sRn[t] * sRn[s];
                 }
                 if ((t >> 4) == (s >> 4))
                     sMd[t * LDX + (s & 15)] = m;
@@ -878,6 +952,8 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
                     const int64_t xr = cp.row0 + (int64_t)t * a.H, xs = cp.row0 + (int64_t)s * a.H;
                     for (int i = 0; i < D; ++i)
                         p += to_f32(q[xr * D + i]) * to_f32(k[xs * D + i]) * fast_exp2(sG[t * D + i] - sG[s * D + i]);
+                    if (pn)
+                        p *= sRn[C + t] * sRn[s];
                 }
                 // lane (g, r) holds k = 4g..4g+3 of each 16-block of the fragment
                 const int k16 = kk & 15, slot = 4 * (kk >> 4) + (k16 & 3);
@@ -888,7 +964,8 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
                 const int t = e / D, i = e % D;
                 float kh = 0.f;
                 if (t < cp.L)
-                    kh = to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) * fast_exp2(sG[(C - 1) * D + i] - sG[t * D + i]);
+                    kh = to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) * fast_exp2(sG[(C - 1) * D + i] - sG[t * D + i]) *
+                         (pn ? sRn[t] : 1.f);
                 sKr[swz<E, D>(t, i)] = from_f32<E>(kh);
             }
             __syncthreads();   // every read of G is done
@@ -1411,29 +1488,39 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
 
     PrepArgs pa;
     pa.q = a.q; pa.k = a.k; pa.v = a.v; pa.b = a.b; pa.w = a.w; pa.g = a.g;
-    pa.bw = a.b_width; pa.ww = a.w_width; pa.gw = a.g_width;
+    pa.bw = a.b_width; pa.ww = a.w_width; pa.gw = a.g_width; pa.pro = a.prologue;
     pa.T = a.T; pa.H = a.H; pa.NC = ceil_div(a.T, C); pa.nrec = L.nrec;
     pa.Wn = ws + L.wn; pa.Ut = ws + L.ut; pa.Kh = ws + L.kh; pa.Qt = ws + L.qt; pa.P = ws + L.p;
     pa.gam = reinterpret_cast<float*>(ws + L.gam);
 
     static const hipError_t attr1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<true, E, D, C>),
+        reinterpret_cast<const void*>(&chunk_prep_kernel<true, false, E, D, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
     static const hipError_t attr1g = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<false, E, D, C>),
+        reinterpret_cast<const void*>(&chunk_prep_kernel<false, false, E, D, C>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
+    static const hipError_t attr1p = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&chunk_prep_kernel<false, true, E, D, C>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
     if (attr1 != hipSuccess)
         return attr1;
     if (attr1g != hipSuccess)
         return attr1g;
+    if (attr1p != hipSuccess)
+        return attr1p;
 
     if (a.stage != GDR2_STAGE_STATE) {
         const int64_t grid1 = std::min<int64_t>(L.nrec, (int64_t)cu_count());
         const bool full = a.b_width == D && a.w_width == D && a.g_width == D;
-        if (full)
-            hipLaunchKernelGGL((chunk_prep_kernel<true, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM, stream, pa);
+        if (a.prologue != 0)      // one variant, every gate width
+            hipLaunchKernelGGL((chunk_prep_kernel<false, true, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM,
+                               stream, pa);
+        else if (full)
+            hipLaunchKernelGGL((chunk_prep_kernel<true, false, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM,
+                               stream, pa);
         else
-            hipLaunchKernelGGL((chunk_prep_kernel<false, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM, stream, pa);
+            hipLaunchKernelGGL((chunk_prep_kernel<false, false, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM,
+                               stream, pa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.stage == GDR2_STAGE_PREP)
             return e;

@@ -20,11 +20,17 @@
 
 namespace gdr2 {
 
-template <int D, typename T>
+// Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
+__device__ __forceinline__ float dec_sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float dec_neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))); }
+
+// PRO: the input prologue (gdr2_prologue bits in `pro`) is applied to the
+// token vectors before the update.
+template <int D, typename T, bool PRO>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ b, const T* __restrict__ w, const float* __restrict__ g,
-    int bw, int ww, int gw, float* __restrict__ state, T* __restrict__ o)
+    int bw, int ww, int gw, float* __restrict__ state, T* __restrict__ o, int pro)
 {
     constexpr int CG = D / 4;       // column groups (4 fp32 each)
     constexpr int RG = 256 / CG;    // row groups
@@ -49,19 +55,56 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __shared__ float s_qk[NW];
     __shared__ f32x4 s_red_r[NW][CG], s_red_a[NW][CG];
     float qk = 0.f;
+    float rk = 1.f, rq = 1.f;                 // prologue: 1/|k|, 1/|q|
+    if constexpr (PRO) {
+        if (pro & GDR2_PROLOGUE_NORM_QK) {
+            __shared__ float s_ss[2][NW];
+            float sk = 0.f, sq = 0.f;
+            if (tid < D) {
+                const float ki = to_f32(k[s * D + tid]), qi = to_f32(q[s * D + tid]);
+                sk = ki * ki;
+                sq = qi * qi;
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                sk += __shfl_xor(sk, off);
+                sq += __shfl_xor(sq, off);
+            }
+            if ((tid & 63) == 0) {
+                s_ss[0][tid >> 6] = sk;
+                s_ss[1][tid >> 6] = sq;
+            }
+            __syncthreads();
+            sk = sq = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                sk += s_ss[0][wv];
+                sq += s_ss[1][wv];
+            }
+            rk = rsqrtf(sk + 1e-6f);
+            rq = rsqrtf(sq + 1e-6f);
+        }
+    }
     if (tid < D) {
         const int i = tid;
-        const float gi = g[s * gw + (gw == 1 ? 0 : i)];
+        float gi = g[s * gw + (gw == 1 ? 0 : i)];
+        float bi = to_f32(b[s * bw + (bw == 1 ? 0 : i)]);
+        float wi = to_f32(w[s * ww + (ww == 1 ? 0 : i)]);
+        if constexpr (PRO) {
+            if (pro & GDR2_PROLOGUE_GATES) {
+                gi = dec_neg_softplus(gi);
+                bi = dec_sigm(bi);
+                wi = dec_sigm(wi);
+            }
+        }
         const float di = fast_exp2(gi * kLog2e);
-        const float ki = to_f32(k[s * D + i]);
-        const float qi = to_f32(q[s * D + i]);
-        const float bi = to_f32(b[s * bw + (bw == 1 ? 0 : i)]);
+        const float ki = to_f32(k[s * D + i]) * rk;
+        const float qi = to_f32(q[s * D + i]) * rq;
         s_d[i] = di;
         s_de[i] = di * bi * ki;
         s_dq[i] = di * qi;
         s_k[i] = ki;
         const float vi = to_f32(v[s * D + i]);
-        const float wi = to_f32(w[s * ww + (ww == 1 ? 0 : i)]);
         s_u[i] = wi * vi;
         qk = qi * ki;
     }
@@ -130,10 +173,16 @@ template <int D, typename T>
 static hipError_t launch_decode_t(const gdr2_decode_args& a, hipStream_t stream)
 {
     const int64_t n = a.N * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<D, T>), dim3((unsigned)n), dim3(256), 0, stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.b,
-                       (const T*)a.w, a.g, a.b_width, a.w_width, a.g_width, a.state,
-                       (T*)a.o);
+    if (a.prologue != 0)
+        hipLaunchKernelGGL((decode_step_kernel<D, T, true>), dim3((unsigned)n), dim3(256), 0, stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.b,
+                           (const T*)a.w, a.g, a.b_width, a.w_width, a.g_width, a.state,
+                           (T*)a.o, a.prologue);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<D, T, false>), dim3((unsigned)n), dim3(256), 0, stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.b,
+                           (const T*)a.w, a.g, a.b_width, a.w_width, a.g_width, a.state,
+                           (T*)a.o, 0);
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libgdr2.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
+PROLOGUE_NORM_QK, PROLOGUE_GATES = 1, 2
 ALGO_AUTO, ALGO_STAGED = 0, 1
 ALGOS = {"auto": ALGO_AUTO, "staged": ALGO_STAGED}
 STAGES = {"all": 0, "prep": 1, "state": 2}
@@ -30,7 +31,7 @@ _vp = ctypes.c_void_p
 class FwdArgs(ctypes.Structure):
     _fields_ = [("B", _c_i64), ("T", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
                 ("chunk", _c_i32), ("dtype", _c_i32), ("algo", _c_i32), ("stage", _c_i32),
-                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("reserved", _c_i32),
+                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("prologue", _c_i32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp),
                 ("g", _vp), ("S0", _vp), ("o", _vp), ("S_out", _vp),
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("S_chunks", _vp)]
@@ -40,13 +41,13 @@ class DecodeArgs(ctypes.Structure):
     _fields_ = [("N", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
                 ("dtype", _c_i32), ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp),
-                ("g", _vp), ("state", _vp), ("o", _vp)]
+                ("g", _vp), ("state", _vp), ("o", _vp), ("prologue", _c_i32), ("reserved", _c_i32)]
 
 
 class BwdArgs(ctypes.Structure):
     _fields_ = [("B", _c_i64), ("T", _c_i64), ("H", _c_i64), ("Dk", _c_i64), ("Dv", _c_i64),
                 ("chunk", _c_i32), ("dtype", _c_i32),
-                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("reserved", _c_i32),
+                ("b_width", _c_i32), ("w_width", _c_i32), ("g_width", _c_i32), ("prologue", _c_i32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp), ("g", _vp),
                 ("S_chunks", _vp), ("dO", _vp), ("dS_final", _vp),
                 ("dq", _vp), ("dk", _vp), ("dv", _vp), ("db", _vp), ("dw", _vp), ("dg", _vp),
@@ -57,7 +58,7 @@ class BwdArgs(ctypes.Structure):
 EXPORTS = ("gdr2_forward_workspace_size", "gdr2_forward_chunked", "gdr2_decode_step",
            "gdr2_backward_workspace_size", "gdr2_backward_chunked",
            "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version")
-ABI_VERSION = 3
+ABI_VERSION = 4
 BWD_CHUNK = 64
 
 
@@ -130,7 +131,8 @@ def _req(t: torch.Tensor, name: str, dtype=None):
 
 
 def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
-             algo: str = "auto", workspace=None, stage: str = "all", S_chunks=None) -> FwdArgs:
+             algo: str = "auto", workspace=None, stage: str = "all", S_chunks=None,
+             prologue: int = 0) -> FwdArgs:
     B, T, H, Dk = q.shape
     a = FwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, Dk, v.shape[-1]
@@ -138,6 +140,7 @@ def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
     a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
     a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
     a.S0, a.o, a.S_out, a.S_chunks = _ptr(S0), _ptr(o), _ptr(S_out), _ptr(S_chunks)
+    a.prologue = prologue
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a
@@ -145,14 +148,15 @@ def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
 
 def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
             out=None, S_out=None, workspace=None, final_state: bool = True,
-            stage: str = "all", chunk_states=None):
+            stage: str = "all", chunk_states=None, prologue: int = 0):
     """Chunked forward.  q,k [B,T,H,Dk]; v [B,T,H,Dv]; b [B,T,H,1|Dk];
     w [B,T,H,1|Dv] (all float32 or bfloat16); g float32 [B,T,H,1|Dk];
     S0 float32 [B,H,Dk,Dv] or None.  Returns (o, S_final), or
     (o, S_final, S_chunks) when chunk_states is True or a float32 tensor
     [B,H,ceil(T/chunk),Dk,Dv]: the state at the start of every chunk.
     stage='prep' / 'state' runs one kernel of the staged algorithm (pass the
-    same workspace, out and S_out to both calls)."""
+    same workspace, out and S_out to both calls).  prologue: PROLOGUE_* bits
+    (raw q, k normalised and raw gates activated inside the kernels)."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w)):
         _req(t, n, q.dtype)
@@ -172,7 +176,7 @@ def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
         else:
             ck = chunk_states
             _req(ck, "chunk_states", torch.float32)
-    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, stage=stage, S_chunks=ck)
+    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, stage=stage, S_chunks=ck, prologue=prologue)
     need = lib.gdr2_forward_workspace_size(ctypes.byref(a))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -188,7 +192,7 @@ def workspace_size(q, k, v, b, w, g, chunk: int = 64, algo: str = "auto") -> int
     return int(lib.gdr2_forward_workspace_size(ctypes.byref(fwd_args(q, k, v, b, w, g, chunk=chunk, algo=algo))))
 
 
-def decode_args(state, q, k, v, b, w, g, o) -> DecodeArgs:
+def decode_args(state, q, k, v, b, w, g, o, prologue: int = 0) -> DecodeArgs:
     N, H, Dk, Dv = state.shape
     a = DecodeArgs()
     a.N, a.H, a.Dk, a.Dv = N, H, Dk, Dv
@@ -196,10 +200,11 @@ def decode_args(state, q, k, v, b, w, g, o) -> DecodeArgs:
     a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
     a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
     a.state, a.o = _ptr(state), _ptr(o)
+    a.prologue = prologue
     return a
 
 
-def decode_step(state, q, k, v, b, w, g, out=None):
+def decode_step(state, q, k, v, b, w, g, out=None, prologue: int = 0):
     """One decode step, in place on ``state`` float32 [N,H,Dk,Dv].
     q,k [N,H,Dk]; v [N,H,Dv]; b [N,H,1|Dk]; w [N,H,1|Dv]; g float32 [N,H,1|Dk].
     Returns o [N,H,Dv]."""
@@ -211,14 +216,14 @@ def decode_step(state, q, k, v, b, w, g, out=None):
     N, H, Dk, Dv = state.shape
     if out is None:
         out = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
-    a = decode_args(state, q, k, v, b, w, g, out)
+    a = decode_args(state, q, k, v, b, w, g, out, prologue)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib, lib.gdr2_decode_step(ctypes.byref(a), stream))
     return out
 
 
 def bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final=None, grads=None, dS0=None,
-             workspace=None, chunk: int = BWD_CHUNK) -> BwdArgs:
+             workspace=None, chunk: int = BWD_CHUNK, prologue: int = 0) -> BwdArgs:
     """grads: (dq, dk, dv, db, dw, dg) or None."""
     B, T, H, Dk = q.shape
     a = BwdArgs()
@@ -227,6 +232,7 @@ def bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final=None, grads=None, dS0=None
     a.b_width, a.w_width, a.g_width = b.shape[-1], w.shape[-1], g.shape[-1]
     a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
     a.S_chunks, a.dO, a.dS_final, a.dS0 = _ptr(S_chunks), _ptr(dO), _ptr(dS_final), _ptr(dS0)
+    a.prologue = prologue
     if grads is not None:
         a.dq, a.dk, a.dv, a.db, a.dw, a.dg = (_ptr(x) for x in grads)
     if workspace is not None:
@@ -240,7 +246,7 @@ def backward_workspace_size(q, k, v, b, w, g) -> int:
 
 
 def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grads=None,
-             dS0=None, want_dS0: bool = True):
+             dS0=None, want_dS0: bool = True, prologue: int = 0):
     """Chunked backward (chunk 64).  Inputs as for ``forward``; S_chunks is
     the float32 [B,H,ceil(T/64),Dk,Dv] chunk-start states of a chunk-64
     forward; dO [B,T,H,Dv] in the inputs' dtype; dS_final float32
@@ -260,7 +266,7 @@ def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grad
         grads = tuple(torch.empty(x.shape, dtype=torch.float32, device=q.device) for x in (q, k, v, b, w, g))
     if dS0 is None and want_dS0:
         dS0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    a = bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final, grads, dS0)
+    a = bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final, grads, dS0, prologue=prologue)
     need = lib.gdr2_backward_workspace_size(ctypes.byref(a))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

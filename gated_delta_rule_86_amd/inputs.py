@@ -113,6 +113,35 @@ def draw_decode_tokens(wl: Workload, step: int) -> dict:
     return draw(wl.with_(s0_std=0.0), seed=wl.seed + 1000 * (step + 1))
 
 
+def draw_raw(wl: Workload, seed: int | None = None) -> dict:
+    """Raw projections for the input prologue: q, k ~ N(0, 1) scaled per
+    token by U(0.5, 3) (not normalised), erase / write gate and decay
+    pre-activations ~ N(0, 1) (width 1 when wl.gates == "scalar"), cast like
+    `draw`; S0 ~ N(0, s0_std^2).  Seed wl.seed + 700_000 unless given."""
+    rng = np.random.default_rng(wl.seed + 700_000 if seed is None else seed)
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    shp = (B, T, H, D)
+    q = rng.standard_normal(shp) * rng.uniform(0.5, 3.0, (B, T, H, 1))
+    k = rng.standard_normal(shp) * rng.uniform(0.5, 3.0, (B, T, H, 1))
+    v = rng.standard_normal(shp)
+    gshape = shp if wl.gates == "full" else (B, T, H, 1)
+    b = rng.standard_normal(gshape)
+    w = rng.standard_normal(gshape)
+    x = rng.standard_normal(gshape)
+    if wl.g_const is not None:
+        x = np.full_like(x, wl.g_const)
+    S0 = rng.standard_normal((B, H, D, D)) * wl.s0_std if wl.s0_std > 0 else None
+    dt = TORCH_DTYPES[wl.dtype]
+    out = {n: torch.from_numpy(a).to(dt) for n, a in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w))}
+    out["g"] = torch.from_numpy(x).to(torch.float32)
+    out["S0"] = None if S0 is None else torch.from_numpy(S0).to(torch.float32)
+    if wl.kind == "decode":
+        for n in ("q", "k", "v", "b", "w", "g"):
+            out[n] = out[n][:, 0].contiguous()
+        out["state"] = out.pop("S0")
+    return out
+
+
 def draw_cotangents(wl: Workload, dS_std: float = 1.0, seed: int | None = None) -> dict:
     """Seeded loss cotangents for the backward: dO ~ N(0,1) [B,T,H,D] in the
     workload dtype, dS_final ~ N(0, dS_std^2) float32 [B,H,D,D] (None when

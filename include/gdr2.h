@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 3
+#define GDR2_ABI_VERSION 4
 
 typedef enum gdr2_status {
     GDR2_OK = 0,
@@ -78,6 +78,26 @@ typedef enum gdr2_dtype {
     GDR2_F32 = 0,
     GDR2_BF16 = 1  /* bfloat16; o is rounded to nearest-even once, at store */
 } gdr2_dtype;
+
+/*
+ * Optional input prologue, fused into the kernels (bit flags; 0 = inputs are
+ * used as given).  The page "Gated DeltaNet-2 ..." (section "Gated Delta
+ * Rule-2 업데이트 수식", symbol table) takes the key L2-normalised, the
+ * erase and write gates in [0, 1] and the decay in (0, 1); these bits let a
+ * caller pass raw projections instead of normalising and activating them in
+ * a separate pass over HBM.  The pages name no activation function: the
+ * logistic sigmoid and the log-sigmoid decay below are this library's choice.
+ *   NORM_QK  q and k are scaled per token and head to unit L2 norm over the
+ *            d_k channels: x <- x (sum x_i^2 + 1e-6)^(-1/2)
+ *   GATES    b <- sigmoid(b), w <- sigmoid(w) (applied to the scalar of a
+ *            width-1 gate), and g carries a pre-activation x whose log-decay
+ *            is -softplus(x) = log sigmoid(-x)
+ * The backward's gradients are then with respect to the raw inputs.
+ */
+typedef enum gdr2_prologue {
+    GDR2_PROLOGUE_NORM_QK = 1,
+    GDR2_PROLOGUE_GATES = 2
+} gdr2_prologue;
 
 /* Algorithm of the chunked forward. */
 typedef enum gdr2_algo {
@@ -133,7 +153,7 @@ typedef struct gdr2_fwd_args {
     int32_t algo;         /* gdr2_algo */
     int32_t stage;        /* gdr2_stage */
     int32_t b_width, w_width, g_width;
-    int32_t reserved;     /* must be 0 */
+    int32_t prologue;     /* gdr2_prologue bits */
     const void *q, *k, *v, *b, *w;
     const float *g;
     const float *S0;
@@ -161,6 +181,8 @@ typedef struct gdr2_decode_args {
     const float *g;
     float *state;
     void *o;
+    int32_t prologue;     /* gdr2_prologue bits */
+    int32_t reserved;     /* must be 0 */
 } gdr2_decode_args;
 
 /*
@@ -192,7 +214,7 @@ typedef struct gdr2_bwd_args {
     int32_t chunk;        /* must be 64 */
     int32_t dtype;        /* gdr2_dtype of q, k, v, b, w, dO */
     int32_t b_width, w_width, g_width;
-    int32_t reserved;     /* must be 0 */
+    int32_t prologue;     /* gdr2_prologue bits, as given to the forward */
     const void *q, *k, *v, *b, *w;
     const float *g;
     const float *S_chunks;

@@ -99,7 +99,7 @@ FWD_CASES = [
     ("bad_dtype", _mod(dtype=7), gdr2.ERR_INVALID_ARG),
     ("bad_algo", _mod(algo=9), gdr2.ERR_INVALID_ARG),
     ("bad_stage", _mod(stage=3), gdr2.ERR_INVALID_ARG),
-    ("reserved_set", _mod(reserved=1), gdr2.ERR_INVALID_ARG),
+    ("bad_prologue", _mod(prologue=4), gdr2.ERR_INVALID_ARG),
     ("bad_b_width", _mod(b_width=3), gdr2.ERR_INVALID_ARG),
     ("bad_w_width", _mod(w_width=64), gdr2.ERR_INVALID_ARG),
     ("bad_g_width", _mod(g_width=2), gdr2.ERR_INVALID_ARG),
@@ -212,6 +212,8 @@ DEC_CASES = [
     ("o_overlaps_state", _mod(o=fake(6, 512)), gdr2.ERR_INVALID_ARG),
     ("state_overlaps_k", _mod(state=fake(1, 0)), gdr2.ERR_INVALID_ARG),
     ("bad_g_width", _mod(g_width=5), gdr2.ERR_INVALID_ARG),
+    ("bad_prologue", _mod(prologue=-1), gdr2.ERR_INVALID_ARG),
+    ("reserved_set", _mod(reserved=1), gdr2.ERR_INVALID_ARG),
 ]
 
 
@@ -259,7 +261,7 @@ BWD_CASES = [
     ("head_dim_96", _mod(Dk=96, Dv=96, b_width=96, w_width=96, g_width=96), gdr2.ERR_UNSUPPORTED),
     ("chunk_32", _mod(chunk=32), gdr2.ERR_UNSUPPORTED),
     ("bad_dtype", _mod(dtype=2), gdr2.ERR_INVALID_ARG),
-    ("reserved_set", _mod(reserved=1), gdr2.ERR_INVALID_ARG),
+    ("bad_prologue", _mod(prologue=8), gdr2.ERR_INVALID_ARG),
     ("bad_w_width", _mod(w_width=2), gdr2.ERR_INVALID_ARG),
     ("null_S_chunks", _mod(S_chunks=None), gdr2.ERR_INVALID_ARG),
     ("null_dO", _mod(dO=None), gdr2.ERR_INVALID_ARG),
@@ -303,7 +305,8 @@ def test_backward_workspace_size_formula(lib):
     # per chunk record, fp32, each array padded to 256 bytes: 16 arrays of
     # [C][D] (G, E, U, E~, Q~, K^, W, U~, Delta, dDelta, dQ~, dK^, dW, dU,
     # dE~, dO), 6 of [C][C] (P, X, dP, dX, a product, dM), gamma [D], the
-    # chunk-end state gradient [D][D]; then the scan's operand fragments in
+    # prologue's per-token 1/|k|, 1/|q| [2][C], the chunk-end state gradient
+    # [D][D]; then the scan's operand fragments in
     # the input dtype: K^, Q~^T, -W^T, dO^T (C*D each) and P^T (C*C)
     def al(x):
         return (x + 255) // 256 * 256
@@ -311,8 +314,8 @@ def test_backward_workspace_size_formula(lib):
                                  (8, 4096, 16, 128, gdr2.BF16, 2), (1, 200, 2, 128, gdr2.F32, 4)]:
         a = good_bwd(B=B, T=T, H=H, D=D, dtype=dt)
         nrec = B * H * -(-T // 64)
-        want = (16 * al(nrec * 64 * D * 4) + 6 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * D * D * 4)
-                + al(nrec * (4 * 64 * D + 64 * 64) * es))
+        want = (16 * al(nrec * 64 * D * 4) + 6 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
+                + al(nrec * D * D * 4) + al(nrec * (4 * 64 * D + 64 * 64) * es))
         assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == want
     assert lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(T=0))) == 0
     a = good_bwd()
