@@ -182,8 +182,8 @@ __device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float*
 __device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
-__device__ __forceinline__ float bsigm(float x) { return 1.f / (1.f + __expf(-x)); }
-__device__ __forceinline__ float bneg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))); }
+__device__ __forceinline__ float bsigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float bneg_softplus(float x) { return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))); }
 __device__ __forceinline__ f32x4 bsigm4(f32x4 x) { return f32x4{bsigm(x[0]), bsigm(x[1]), bsigm(x[2]), bsigm(x[3])}; }
 constexpr float kNormEps = 1e-6f;
 __device__ __forceinline__ void st4s(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }

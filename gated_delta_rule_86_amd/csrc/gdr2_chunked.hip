@@ -228,8 +228,10 @@ template <> __device__ __forceinline__ int kpos<float>(int col) { return col; }
 // s_waitcnt lgkmcnt(0) with a compiler barrier: LDS writes of this wave are
 // complete before any later LDS read of it (lanes exchange data this way).
 // Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
-__device__ __forceinline__ float neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))); }
+// (v_exp, v_log, v_rcp: about 1 ulp each; log(1 + e) loses e < 6e-8 absolute,
+// far below the decay's own rounding)
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float neg_softplus(float x) { return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))); }
 constexpr float kNormEps = 1e-6f;
 
 __device__ __forceinline__ void lds_fence_wave()
@@ -396,7 +398,7 @@ struct PrepRegs {
 // and are zeroed where they are used, so no load sits under a per-lane branch.
 // PART: 0 = k, 1 = q, 2 = v, 3 = b, 4 = w (issued at different points of
 // the previous chunk, so no wave stalls on a full memory queue).
-template <int PART, bool FULL, typename E, int D, int C>
+template <int PART, int WB, int WW, typename E, int D, int C>
 __device__ __forceinline__ void prep_load(const PrepArgs& a, const ChunkPos& cp, PrepRegs<E, D, C>& R,
                                           int t0, int c0)
 {
@@ -412,13 +414,13 @@ __device__ __forceinline__ void prep_load(const PrepArgs& a, const ChunkPos& cp,
         if (PART == 2)
             R.v[j] = ldg16((const E*)a.v + off);
         if (PART == 3) {
-            if (FULL || a.bw != 1)
+            if (WB == 0 ? a.bw != 1 : WB != 1)
                 R.b[j] = ldg16((const E*)a.b + off);
             else
                 R.b[j][0] = ld_bits<E>((const E*)a.b + row);
         }
         if (PART == 4) {
-            if (FULL || a.ww != 1)
+            if (WW == 0 ? a.ww != 1 : WW != 1)
                 R.w[j] = ldg16((const E*)a.w + off);
             else
                 R.w[j][0] = ld_bits<E>((const E*)a.w + row);
@@ -429,12 +431,12 @@ __device__ __forceinline__ void prep_load(const PrepArgs& a, const ChunkPos& cp,
 // Copy one chunk's log-decay rows straight into LDS (global_load_lds, no
 // registers): [C][D] fp32, or C floats for a width-1 gate.  Rows past the
 // valid length repeat the last valid row and are zeroed by the reader.
-template <bool FULL, typename E, int D, int C>
+template <int WG, typename E, int D, int C>
 __device__ __forceinline__ void prep_copy_g(const PrepArgs& a, const ChunkPos& cp, unsigned char* sGraw,
                                             int wave, int lane)
 {
     typedef __attribute__((address_space(3))) void lds_t;
-    if (FULL || a.gw != 1) {
+    if (WG == 0 ? a.gw != 1 : WG != 1) {
         constexpr int NI = C * D * 4 / 1024;
         for (int j = wave; j < NI; j += NWP) {
             const int byte = j * 1024 + lane * 16, t = min(byte / (D * 4), cp.L - 1), col = (byte % (D * 4)) / 4;
@@ -603,7 +605,9 @@ __device__ __forceinline__ typename Mma16<E>::Frag row4(const E* base, int r, in
     return Mma16<E>::load(base + swz<E, D>(r, col));
 }
 
-template <bool FULL, bool PRO, typename E, int D, int C>
+// Gate widths WB, WW, WG: 1 or D fixed at compile time, 0 = read from the
+// arguments (one variant serves every mix).
+template <int WB, int WW, int WG, bool PRO, typename E, int D, int C>
 __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 {
     typedef PrepShape<E, D, C> S;
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
     const int wave = threadIdx.x >> 6;
     const bool ab = wave < S::NWB;              // waves of phases A and B
     const bool second = NH == 2 && wave >= S::NWB / 2;
-    const int bw = FULL ? D : a.bw, ww = FULL ? D : a.ww, gw = FULL ? D : a.gw;
+    const int bw = WB ? WB : a.bw, ww = WW ? WW : a.ww, gw = WG ? WG : a.gw;
 
     // X: the blocks above the diagonal that fragments cover stay zero
     for (int e = threadIdx.x; e < C * LDXP; e += NTP)
@@ -652,13 +656,13 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         const int lane = threadIdx.x & 63;
         const ChunkPos cp0 = walk.pos(a.NC, a.T, a.H, C);
         const int t0 = wave * S::TW + (lane % S::LPC) * S::TPL, c0 = (lane / S::LPC) * VEC;
-        prep_copy_g<FULL, E, D, C>(a, cp0, reinterpret_cast<unsigned char*>(sG), wave, lane);
+        prep_copy_g<WG, E, D, C>(a, cp0, reinterpret_cast<unsigned char*>(sG), wave, lane);
         if (ab) {
-            prep_load<0, FULL>(a, cp0, Rn, t0, c0);
-            prep_load<1, FULL>(a, cp0, Rn, t0, c0);
-            prep_load<2, FULL>(a, cp0, Rn, t0, c0);
-            prep_load<3, FULL>(a, cp0, Rn, t0, c0);
-            prep_load<4, FULL>(a, cp0, Rn, t0, c0);
+            prep_load<0, WB, WW>(a, cp0, Rn, t0, c0);
+            prep_load<1, WB, WW>(a, cp0, Rn, t0, c0);
+            prep_load<2, WB, WW>(a, cp0, Rn, t0, c0);
+            prep_load<3, WB, WW>(a, cp0, Rn, t0, c0);
+            prep_load<4, WB, WW>(a, cp0, Rn, t0, c0);
         }
     }
 
@@ -680,8 +684,8 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         const bool pre = ab && next < a.nrec;   // this lane prefetches tokens
         const ChunkPos np = walk.pos(a.NC, a.T, a.H, C);
         if (pre) {
-            prep_load<0, FULL>(a, np, Rn, t0, c0);
-            prep_load<1, FULL>(a, np, Rn, t0, c0);
+            prep_load<0, WB, WW>(a, np, Rn, t0, c0);
+            prep_load<1, WB, WW>(a, np, Rn, t0, c0);
         }
         // identity B operand of the transposes: element (k = 4gq + i, n = cl)
         typename M16::Frag ident;
@@ -769,7 +773,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             *sFlag = 0;
         lds_barrier();   // B1: wave totals; the previous chunk is done with LDS
         if (pre)
-            prep_load<2, FULL>(a, np, Rn, t0, c0);
+            prep_load<2, WB, WW>(a, np, Rn, t0, c0);
 
         // ---- B: decay-referenced operands ----------------------------------
         float gh[VEC];
@@ -829,17 +833,17 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             if (mx > kSpanMax)
                 *sFlag = 1;
             if (pre)
-                prep_load<3, FULL>(a, np, Rn, t0, c0);
+                prep_load<3, WB, WW>(a, np, Rn, t0, c0);
         }
         lds_barrier();   // B2: operands in LDS
 
         E* gP = (E*)a.P + rec * (F::P_BYTES / sizeof(E));
         if (pre)
-            prep_load<4, FULL>(a, np, Rn, t0, c0);
+            prep_load<4, WB, WW>(a, np, Rn, t0, c0);
         const bool guard = *sFlag != 0;
         if (!guard) {
             if (next < a.nrec)
-                prep_copy_g<FULL, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
+                prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
             // ---- C1: M tiles (waves 0-3) and P fragments (waves 4-7) -------
             if (wave < NWP / 2) {
                 constexpr int NTM = NB * (NB + 1) / 2;
@@ -970,7 +974,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             }
             __syncthreads();   // every read of G is done
             if (next < a.nrec)
-                prep_copy_g<FULL, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
+                prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
         }
         lds_barrier();   // B3: M in LDS
 
@@ -1477,6 +1481,21 @@ int cu_count()
     return counts[dev];
 }
 
+template <int WB, int WW, int WG, bool PRO, typename E, int D, int C>
+hipError_t launch_prep(const PrepArgs& pa, int64_t grid, hipStream_t stream)
+{
+    typedef PrepShape<E, D, C> PS;
+    // more than 64 KiB of dynamic LDS: requested once per variant
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&chunk_prep_kernel<WB, WW, WG, PRO, E, D, C>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((chunk_prep_kernel<WB, WW, WG, PRO, E, D, C>), dim3((unsigned)grid), dim3(NTP), PS::SMEM,
+                       stream, pa);
+    return hipSuccess;
+}
+
 template <typename E, int D, int C>
 hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
 {
@@ -1493,34 +1512,30 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     pa.Wn = ws + L.wn; pa.Ut = ws + L.ut; pa.Kh = ws + L.kh; pa.Qt = ws + L.qt; pa.P = ws + L.p;
     pa.gam = reinterpret_cast<float*>(ws + L.gam);
 
-    static const hipError_t attr1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<true, false, E, D, C>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
-    static const hipError_t attr1g = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<false, false, E, D, C>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
-    static const hipError_t attr1p = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<false, true, E, D, C>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
-    if (attr1 != hipSuccess)
-        return attr1;
-    if (attr1g != hipSuccess)
-        return attr1g;
-    if (attr1p != hipSuccess)
-        return attr1p;
-
     if (a.stage != GDR2_STAGE_STATE) {
         const int64_t grid1 = std::min<int64_t>(L.nrec, (int64_t)cu_count());
-        const bool full = a.b_width == D && a.w_width == D && a.g_width == D;
-        if (a.prologue != 0)      // one variant, every gate width
-            hipLaunchKernelGGL((chunk_prep_kernel<false, true, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM,
-                               stream, pa);
-        else if (full)
-            hipLaunchKernelGGL((chunk_prep_kernel<true, false, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM,
-                               stream, pa);
-        else
-            hipLaunchKernelGGL((chunk_prep_kernel<false, false, E, D, C>), dim3((unsigned)grid1), dim3(NTP), PS::SMEM,
-                               stream, pa);
+        // one compile-time variant per gate-width mix; with the prologue, the
+        // per-channel mix has its own variant and the others share the one
+        // that reads the widths at run time
+        const int code = (a.b_width == 1 ? 4 : 0) | (a.w_width == 1 ? 2 : 0) | (a.g_width == 1 ? 1 : 0);
+        hipError_t e0 = hipSuccess;
+        if (a.prologue != 0) {
+            e0 = code == 0 ? launch_prep<D, D, D, true, E, D, C>(pa, grid1, stream)
+                           : launch_prep<0, 0, 0, true, E, D, C>(pa, grid1, stream);
+        } else {
+            switch (code) {
+            case 0: e0 = launch_prep<D, D, D, false, E, D, C>(pa, grid1, stream); break;
+            case 1: e0 = launch_prep<D, D, 1, false, E, D, C>(pa, grid1, stream); break;
+            case 2: e0 = launch_prep<D, 1, D, false, E, D, C>(pa, grid1, stream); break;
+            case 3: e0 = launch_prep<D, 1, 1, false, E, D, C>(pa, grid1, stream); break;
+            case 4: e0 = launch_prep<1, D, D, false, E, D, C>(pa, grid1, stream); break;
+            case 5: e0 = launch_prep<1, D, 1, false, E, D, C>(pa, grid1, stream); break;
+            case 6: e0 = launch_prep<1, 1, D, false, E, D, C>(pa, grid1, stream); break;
+            default: e0 = launch_prep<1, 1, 1, false, E, D, C>(pa, grid1, stream); break;
+            }
+        }
+        if (e0 != hipSuccess)
+            return e0;
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.stage == GDR2_STAGE_PREP)
             return e;

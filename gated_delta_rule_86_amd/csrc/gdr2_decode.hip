@@ -21,8 +21,8 @@
 namespace gdr2 {
 
 // Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
-__device__ __forceinline__ float dec_sigm(float x) { return 1.f / (1.f + __expf(-x)); }
-__device__ __forceinline__ float dec_neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))); }
+__device__ __forceinline__ float dec_sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float dec_neg_softplus(float x) { return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))); }
 
 // PRO: the input prologue (gdr2_prologue bits in `pro`) is applied to the
 // token vectors before the update.

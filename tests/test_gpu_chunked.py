@@ -52,19 +52,23 @@ def test_ragged_lengths(dtype, D, C, T):
     check(draw(wl), C, dtype, f"{dtype} D={D} C={C} T={T}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("widths", [(1, 1, 1), (64, 1, 64), (1, 64, 1), (64, 64, 1)],
-                         ids=["gdn", "scalar_write", "scalar_erase_decay", "scalar_decay"])
-def test_gate_widths(dtype, widths):
-    """Scalar gates broadcast: (b, w, g) widths from {1, d}; the result must
+WIDTH_CFGS = [("bf16", 128, 64), ("f32", 64, 32), ("bf16", 64, 32)]
+WIDTH_MIXES = [(nb, nw, ng) for nb in (0, 1) for nw in (0, 1) for ng in (0, 1)]
+
+
+@pytest.mark.parametrize("dtype,D,C", WIDTH_CFGS, ids=[f"{a}-d{b}-c{c}" for a, b, c in WIDTH_CFGS])
+@pytest.mark.parametrize("mix", WIDTH_MIXES, ids=["b%s_w%s_g%s" % tuple("1" if x else "d" for x in m)
+                                                  for m in WIDTH_MIXES])
+def test_gate_widths(dtype, D, C, mix):
+    """Every gate-width mix (b, w, g each of width 1 or d; each mix has its
+    own compiled prep kernel): scalar gates broadcast, and the result must
     equal the oracle on the same (width-1) inputs."""
-    wl = Workload("widths", "forward", 2, 100, 2, 64, dtype, "full", 0.05, 32, 55)
+    wl = Workload("widths", "forward", 2, 100, 2, D, dtype, "full", 0.05, C, 55 + D + C)
     inp = draw(wl)
-    bw, ww, gw = widths
-    inp["b"] = inp["b"][..., :bw].contiguous()
-    inp["w"] = inp["w"][..., :ww].contiguous()
-    inp["g"] = inp["g"][..., :gw].contiguous()
-    check(inp, 32, dtype, f"widths {widths} {dtype}")
+    for n, narrow in zip(("b", "w", "g"), mix):
+        if narrow:
+            inp[n] = inp[n][..., :1].contiguous()
+    check(inp, C, dtype, f"widths {mix} {dtype} D={D} C={C}")
 
 
 @pytest.mark.parametrize("g_const,g_scale", [(0.0, 1.0), (-80.0, 1.0), (None, 0.01), (-1e-4, 1.0)],
