@@ -355,7 +355,7 @@ def main():
     esz = 2
     prep_b, state_b, min_b = staged_bytes(B, T, H, D, C, esz, D, D, D, d["S0"] is not None, True)
     flops = algorithmic_flops_per_chunk(C, D) * B * H * (T // C)
-    kernels = {"gdr2_chunk_prep": (prep_ms, prep_b), "gdr2_chunk_state": (state_ms, state_b)}
+    kernels = {"gdr2_chunk_prep[b,w,g=d,d,d]": (prep_ms, prep_b), "gdr2_chunk_state": (state_ms, state_b)}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_b = kernels[dom]
     achieved = dom_b / (dom_ms * 1e-3) / 1e9

@@ -43,9 +43,20 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+_PREP_VARIANT = re.compile(r"chunk_prep_kernel(?:ILi(\d+)ELi(\d+)ELi(\d+)ELb(\d)|<(\d+), (\d+), (\d+), (true|false))")
+
+
 def short_name(kernel: str) -> str | None:
     for frag, name in KERNELS:
         if frag in kernel:
+            if name == "gdr2_chunk_prep":
+                # one prep kernel per gate-width mix (0 = widths read at run time)
+                m = _PREP_VARIANT.search(kernel)
+                if m:
+                    g = m.groups()
+                    wb, ww, wg, pro = g[0:4] if g[0] is not None else g[4:8]
+                    tag = ",".join("x" if x == "0" else ("1" if x == "1" else "d") for x in (wb, ww, wg))
+                    name += f"[b,w,g={tag}" + (",prologue]" if pro in ("1", "true") else "]")
             return name
     return None
 
@@ -83,18 +94,20 @@ def _counter_per_kernel(path, counter):
         name = short_name(r["Kernel_Name"])
         if name:
             vals.setdefault(name, []).append(float(r["Counter_Value"]))
-    return {k: statistics.median(v) for k, v in vals.items()}
+    return {k: statistics.median(v) for k, v in vals.items()}, {k: max(v) for k, v in vals.items()}
 
 
 def traffic(args):
     copy_bytes = args.copy_bytes
-    fetch = _counter_per_kernel(args.fetch_dir, "FETCH_SIZE")
-    write = _counter_per_kernel(args.write_dir, "WRITE_SIZE")
+    fetch, fetch_max = _counter_per_kernel(args.fetch_dir, "FETCH_SIZE")
+    write, write_max = _counter_per_kernel(args.write_dir, "WRITE_SIZE")
+    fetch["plain_copy"], write["plain_copy"] = fetch_max["plain_copy"], write_max["plain_copy"]
     if "plain_copy" not in fetch or "plain_copy" not in write:
         raise SystemExit("the plain copy kernel is missing from the counter runs")
-    # a copy of N bytes reads N and writes N bytes
-    kf = copy_bytes / fetch["plain_copy"]
-    kw = copy_bytes / write["plain_copy"]
+    # a copy of N bytes reads N and writes N bytes; the calibration copy is
+    # the largest copy dispatch of the run
+    kf = copy_bytes / fetch_max["plain_copy"]
+    kw = copy_bytes / write_max["plain_copy"]
     out = [f"# HBM traffic per launch (rocprofv3 --pmc): {args.title}", "",
            "Commands (from the repository root on the GPU box), one counter per run:", "",
            f"    {args.command_fetch}", f"    {args.command_write}", "",
