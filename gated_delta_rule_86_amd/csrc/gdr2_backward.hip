@@ -147,7 +147,8 @@ template <int D>
 struct BwdPrepShape {
     static constexpr int C = BC, LD = D + 4, LDM = C + 4;
     static constexpr int OFF_G = 0, OFF_E = C * LD, OFF_K = 2 * C * LD, OFF_Q = 3 * C * LD, OFF_M = 4 * C * LD;
-    static constexpr int FLOATS = OFF_M + C * LDM;
+    static constexpr int OFF_CF = OFF_M + C * LDM;           // cross-block decay factors [6][D]
+    static constexpr int FLOATS = OFF_CF + 6 * D;
     static constexpr size_t SMEM = (size_t)FLOATS * 4;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert(C * LDM <= C * LD && 3 * 256 <= C * LD && C * C <= C * LD,
@@ -222,6 +223,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
 
     // 1. raw rows (zero past the chunk's valid length), 4 channels per item
+    int growth = 0;                  // a log-decay > 0 somewhere in the chunk
     for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
         const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
         const size_t x = cdo + (size_t)t * D + i;
@@ -241,6 +243,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             }
             ev = bv;
             uv = wv * load4(v + row * D + i);
+            growth |= (gv[0] > 0.f) | (gv[1] > 0.f) | (gv[2] > 0.f) | (gv[3] > 0.f);
         }
         if (a.pro & GDR2_PROLOGUE_NORM_QK) {
             // unit L2 norm per token: the Q4 items of a row are Q4 consecutive lanes
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         st4s(ws + a.L.E + x, ev);
         st4s(ws + a.L.U + x, uv);
     }
-    __syncthreads();
+    growth = __syncthreads_or(growth);
     for (int i = tid; i < D; i += NTP) {
         float acc = 0.f;
         for (int t = 0; t < C; ++t) {
@@ -299,68 +302,143 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         }
     }
 
-    // 2. M and P, 4x4 token blocks on and below the diagonal; two threads
-    // (channel halves) per block
-    float m[4][4] = {}, p[4][4] = {};
-    const int half = tid / 136, bid = tid % 136;
-    int tb = 0;
-    while ((tb + 1) * (tb + 2) / 2 <= bid)
-        ++tb;
-    const int sb = bid - tb * (tb + 1) / 2, t0 = 4 * tb, s0 = 4 * sb;
-    if (tid < 272) {
-        for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
-            float gt[4], et[4], qt[4], gs[4], ks[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                gt[x] = sG[(t0 + x) * LD + i];
-                et[x] = sE[(t0 + x) * LD + i];
-                qt[x] = sQ[(t0 + x) * LD + i];
-                gs[x] = sG[(s0 + x) * LD + i];
-                ks[x] = sK[(s0 + x) * LD + i];
+    // 2. M (strictly lower) and P (lower).
+    if (!growth) {
+        // Decays only: 2a the diagonal 16x16 blocks pair by pair; 2b the
+        // rows re-referenced to their block in place,
+        //   E^ = e e^{G - G_16T},  Q^ = q e^{G - G_16T},  K- = k e^{G_16T+15 - G},
+        // and c_TS = e^{G_16T - G_16S+15} for S < T (every factor <= 1);
+        // 2c the blocks below the diagonal as M_TS = (E^_T c_TS) K-_S^T.
+        float* sCf = sm + PS::OFF_CF;
+        for (int e = tid; e < 4 * 136; e += NTP) {
+            const int blk = e / 136, pr = e % 136;
+            int rr = 0;
+            while ((rr + 1) * (rr + 2) / 2 <= pr)
+                ++rr;
+            const int cc = pr - rr * (rr + 1) / 2, t = 16 * blk + rr, s_ = 16 * blk + cc;
+            float m = 0.f, p = 0.f;
+            for (int i = 0; i < D; ++i) {
+                const float f = __expf(sG[t * LD + i] - sG[s_ * LD + i]) * sK[s_ * LD + i];
+                m += sE[t * LD + i] * f;
+                p += sQ[t * LD + i] * f;
             }
+            sM[t * LDM + s_] = cc < rr ? m : 0.f;
+            ws[a.L.P + cco + t * C + s_] = p;
+            if (cc < rr) {
+                sM[s_ * LDM + t] = 0.f;
+                ws[a.L.P + cco + s_ * C + t] = 0.f;
+            }
+        }
+        __syncthreads();
+        for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
+            const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i, T = t / 16;
+            const f32x4 G = ld4s(sG + l), G0 = ld4s(sG + 16 * T * LD + i), G1 = ld4s(sG + (16 * T + 15) * LD + i);
+            f32x4 fa, fb;
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int j = 0; j < 4; ++j) {
+                fa[j] = __expf(G[j] - G0[j]);
+                fb[j] = __expf(G1[j] - G[j]);
+            }
+            st4s(sE + l, ld4s(sE + l) * fa);
+            st4s(sQ + l, ld4s(sQ + l) * fa);
+            st4s(sK + l, ld4s(sK + l) * fb);
+        }
+        for (int e = tid; e < 6 * D; e += NTP) {
+            const int pi = e / D, i = e % D;
+            const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
+            sCf[e] = __expf(sG[16 * T * LD + i] - sG[(16 * S + 15) * LD + i]);
+        }
+        __syncthreads();
+        for (int e = tid; e < 6 * 64; e += NTP) {
+            const int pi = e / 64, rr = (e / 4) % 16, cg = e % 4;
+            const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
+            const int t = 16 * T + rr, s0 = 16 * S + 4 * cg;
+            const float* cf = sCf + pi * D;
+            float m[4] = {}, p[4] = {};
+            for (int i = 0; i < D; ++i) {
+                const float c = cf[i], am = sE[t * LD + i] * c, ap = sQ[t * LD + i] * c;
 #pragma unroll
                 for (int y = 0; y < 4; ++y) {
-                    const float f = __expf(gt[x] - gs[y]) * ks[y];
-                    m[x][y] += et[x] * f;
-                    p[x][y] += qt[x] * f;
+                    const float kb = sK[(s0 + y) * LD + i];
+                    m[y] += am * kb;
+                    p[y] += ap * kb;
                 }
+            }
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                sM[t * LDM + s0 + y] = m[y];
+                ws[a.L.P + cco + t * C + s0 + y] = p[y];
+                sM[(s0 + y) * LDM + t] = 0.f;
+                ws[a.L.P + cco + (s0 + y) * C + t] = 0.f;
+            }
         }
-    }
-    __syncthreads();                  // q and k rows are no longer read
-    float* sPp = sK;                  // [C][C] partial P of the second half
-    if (tid >= 136 && tid < 272) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                sM[(t0 + x) * LDM + s0 + y] = m[x][y];
-                sPp[(t0 + x) * C + s0 + y] = p[x][y];
+        __syncthreads();
+    } else {
+        // Some log-decay > 0 (growth): factors could exceed 1, so every
+        // pair takes its own exponential.  4x4 token blocks on and below the
+        // diagonal; two threads (channel halves) per block.
+        float m[4][4] = {}, p[4][4] = {};
+        const int half = tid / 136, bid = tid % 136;
+        int tb = 0;
+        while ((tb + 1) * (tb + 2) / 2 <= bid)
+            ++tb;
+        const int sb = bid - tb * (tb + 1) / 2, t0 = 4 * tb, s0 = 4 * sb;
+        if (tid < 272) {
+            for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
+                float gt[4], et[4], qt[4], gs[4], ks[4];
+    #pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    gt[x] = sG[(t0 + x) * LD + i];
+                    et[x] = sE[(t0 + x) * LD + i];
+                    qt[x] = sQ[(t0 + x) * LD + i];
+                    gs[x] = sG[(s0 + x) * LD + i];
+                    ks[x] = sK[(s0 + x) * LD + i];
+                }
+    #pragma unroll
+                for (int x = 0; x < 4; ++x)
+    #pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        const float f = __expf(gt[x] - gs[y]) * ks[y];
+                        m[x][y] += et[x] * f;
+                        p[x][y] += qt[x] * f;
+                    }
             }
-    }
-    __syncthreads();
-    if (tid < 136) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                const int t = t0 + x, s_ = s0 + y;
-                const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
-                sM[t * LDM + s_] = s_ < t ? mm : 0.f;
-                ws[a.L.P + cco + t * C + s_] = s_ <= t ? pp : 0.f;
-            }
-        if (sb != tb) {               // the mirrored block above the diagonal is zero
-#pragma unroll
+        }
+        __syncthreads();                  // q and k rows are no longer read
+        float* sPp = sK;                  // [C][C] partial P of the second half
+        if (tid >= 136 && tid < 272) {
+    #pragma unroll
             for (int x = 0; x < 4; ++x)
-#pragma unroll
+    #pragma unroll
                 for (int y = 0; y < 4; ++y) {
-                    sM[(s0 + y) * LDM + t0 + x] = 0.f;
-                    ws[a.L.P + cco + (s0 + y) * C + t0 + x] = 0.f;
+                    sM[(t0 + x) * LDM + s0 + y] = m[x][y];
+                    sPp[(t0 + x) * C + s0 + y] = p[x][y];
                 }
         }
+        __syncthreads();
+        if (tid < 136) {
+    #pragma unroll
+            for (int x = 0; x < 4; ++x)
+    #pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int t = t0 + x, s_ = s0 + y;
+                    const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
+                    sM[t * LDM + s_] = s_ < t ? mm : 0.f;
+                    ws[a.L.P + cco + t * C + s_] = s_ <= t ? pp : 0.f;
+                }
+            if (sb != tb) {               // the mirrored block above the diagonal is zero
+    #pragma unroll
+                for (int x = 0; x < 4; ++x)
+    #pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        sM[(s0 + y) * LDM + t0 + x] = 0.f;
+                        ws[a.L.P + cco + (s0 + y) * C + t0 + x] = 0.f;
+                    }
+            }
+        }
+        __syncthreads();
+
     }
-    __syncthreads();
 
     // 3. X = (I + M)^-1 into the q area; first the diagonal 16x16 blocks, one
     // column per thread, then the block diagonals below
@@ -389,7 +467,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     float* sU = sK;
     for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
         const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        f32x4 ev = ld4s(sE + l);
+        f32x4 ev = ld4s(ws + a.L.E + cdo + (size_t)t * D + i);   // sE holds the re-referenced rows
         const f32x4 G = ld4s(sG + l);
 #pragma unroll
         for (int j = 0; j < 4; ++j)

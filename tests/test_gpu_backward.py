@@ -84,6 +84,19 @@ def test_backward_matches_oracle(name, B, T, H, D, dtype, gates, s0, ds, widths)
     _compare(name, got, _oracle_backward(inp), TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_backward_with_growth(dtype, D):
+    """A positive log-decay (g = +0.01, the state grows): the prep kernel's
+    re-referenced factors could exceed 1 there, so such chunks take the
+    pair-by-pair path."""
+    wl = Workload("growth", "forward", 1, 150, 2, D, dtype, "full", 0.05, 64, 603, g_const=0.01)
+    inp = draw(wl)
+    inp.update(draw_cotangents(wl, 1.0))
+    got = _gpu_backward(to_dev(inp))
+    torch.cuda.synchronize()
+    _compare(f"growth_{dtype}", got, _oracle_backward(inp), TOL[dtype])
+
+
 def test_state_gradient_only():
     """dO = 0: every gradient flows from dS_final through the chunk-level
     recurrence alone.  The decay is weakened (g scaled by 0.02) so that dS0
