@@ -966,13 +966,25 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         sGL[tid] = acc;
     }
 
+    // growth (some G_t > G_t-1, i.e. a log-decay > 0) anywhere in these
+    // channels: every pair takes its own exponential
+    int grow = 0;
+    for (int e = tid; e < (C - 1) * DC; e += NTB) {
+        const int t = e / DC + 1, c = e % DC;
+        grow |= sG[t * LC + c] > sG[(t - 1) * LC + c];
+    }
+    grow = __syncthreads_or(grow);
+
     float Gt[RPT], dEm[RPT], dqp[RPT], dkm[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         Gt[m] = sG[(t0 + m) * LC + il];
         dEm[m] = dqp[m] = dkm[m] = 0.f;
     }
-    for (int u0 = 0; u0 < C; u0 += 4) {
+    // the partner tokens u of the pair-by-pair pass: all of them (growth), or
+    // only the 16-token block of the thread's rows
+    const int u_lo = grow ? 0 : (t0 / 16) * 16, u_hi = grow ? C : u_lo + 16;
+    for (int u0 = u_lo; u0 < u_hi; u0 += 4) {
         f32x4 rM[RPT], rP[RPT];          // dM[t, u0..u0+3], dP[t, u0..u0+3]
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
@@ -1001,6 +1013,83 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             }
         }
     }
+    if (!grow) {
+        // Decays only: pairs in different 16-token blocks T > S through
+        // factors that are all <= 1 (per channel):
+        //   e^{G_t - G_s} = e^{G_t - G_16T} c_TS e^{G_16S+15 - G_s},  c_TS = e^{G_16T - G_16S+15}
+        // The rows are re-referenced in place (E^ = e e^{G - G_16T},
+        // Q^ = q e^{G - G_16T}, K- = k e^{G_16S+15 - G}); the epilogue reads
+        // the raw rows again from memory.
+        float* sCf = sdG;                // [6][DC] c_TS; sdG is not needed until the epilogue
+        __syncthreads();                 // the pass above is done with the raw rows
+        for (int e = tid; e < C * DC; e += NTB) {
+            const int t = e / DC, c = e % DC, l = t * LC + c, T = t / 16;
+            const float G = sG[l];
+            const float fa = __expf(G - sG[16 * T * LC + c]), fb = __expf(sG[(16 * T + 15) * LC + c] - G);
+            sE[l] *= fa;
+            sQ[l] *= fa;
+            sK[l] *= fb;
+        }
+        for (int e = tid; e < 6 * DC; e += NTB) {
+            const int pi = e / DC, c = e % DC;
+            const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
+            sCf[e] = __expf(sG[16 * T * LC + c] - sG[(16 * S + 15) * LC + c]);
+        }
+        __syncthreads();
+        const int Tb = t0 / 16;          // the 16-token block of this thread's rows
+        float fa[RPT], fb[RPT];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            fa[m] = __expf(Gt[m] - sG[16 * Tb * LC + il]);
+            fb[m] = __expf(sG[(16 * Tb + 15) * LC + il] - Gt[m]);
+        }
+        // as the later token: blocks S < Tb
+        for (int S = 0; S < Tb; ++S) {
+            const float c = sCf[(Tb * (Tb - 1) / 2 + S) * DC + il];
+            float am[RPT] = {}, ap[RPT] = {};
+            for (int s0 = 16 * S; s0 < 16 * S + 16; s0 += 4) {
+                float kb[4];
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+                    kb[y] = sK[(s0 + y) * LC + il];
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const f32x4 rm = *reinterpret_cast<const f32x4*>(sdM + (t0 + m) * LPC + s0);
+                    const f32x4 rp = *reinterpret_cast<const f32x4*>(sdP + (t0 + m) * LPC + s0);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        am[m] += rm[y] * kb[y];
+                        ap[m] += rp[y] * kb[y];
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                dEm[m] += fa[m] * c * am[m];
+                dqp[m] += fa[m] * c * ap[m];
+            }
+        }
+        // as the earlier token: blocks T > Tb
+        for (int T = Tb + 1; T < C / 16; ++T) {
+            const float c = sCf[(T * (T - 1) / 2 + Tb) * DC + il];
+            float ak[RPT] = {};
+            for (int u = 16 * T; u < 16 * T + 16; ++u) {
+                const float eu = sE[u * LC + il], qu = sQ[u * LC + il];
+                const f32x4 cM0 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0);
+                const f32x4 cM1 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0 + 4);
+                const f32x4 cP0 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0);
+                const f32x4 cP1 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0 + 4);
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float cm = m < 4 ? cM0[m & 3] : cM1[m & 3], cp = m < 4 ? cP0[m & 3] : cP1[m & 3];
+                    ak[m] += cm * eu + cp * qu;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < RPT; ++m)
+                dkm[m] += fb[m] * c * ak[m];
+        }
+    }
     __syncthreads();                     // sGL ready; dM and dP no longer read
     // the three sums into LDS (the dM / dP area), then the gradients with
     // four channels per item
@@ -1025,11 +1114,24 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         const f32x4 Et = *reinterpret_cast<const f32x4*>(ws + a.L.Et + x);
         const f32x4 Qt = *reinterpret_cast<const f32x4*>(ws + a.L.Qt + x);
         const f32x4 dU = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+        // raw rows (LDS may hold the re-referenced ones): e from the
+        // workspace, k and q from the inputs (normalised under the prologue)
+        const f32x4 ev = *reinterpret_cast<const f32x4*>(ws + a.L.E + x);
+        f32x4 kr = {0.f, 0.f, 0.f, 0.f}, qr = kr;
+        if (t < rc.L) {
+            const int64_t row = rc.row0 + (int64_t)t * a.H;
+            kr = load4(k + row * D + i0 + c);
+            qr = load4(q + row * D + i0 + c);
+            if (a.pro & GDR2_PROLOGUE_NORM_QK) {
+                kr = kr * ws[a.L.RN + (size_t)r * 2 * C + t];
+                qr = qr * ws[a.L.RN + (size_t)r * 2 * C + C + t];
+            }
+        }
         f32x4 dq, dk, dE;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float G = sG[l + j], eg = expf(G);
-            float dG = sE[l + j] * sEm[l + j] + sQ[l + j] * sQp[l + j] - sK[l + j] * sKm[l + j] + dEt[j] * Et[j] +
+            float dG = ev[j] * sEm[l + j] + qr[j] * sQp[l + j] - kr[j] * sKm[l + j] + dEt[j] * Et[j] +
                        dQt[j] * Qt[j] - dKh[j] * Kh[j];
             if (t == rc.L - 1)
                 dG += sGL[c + j];
@@ -1049,7 +1151,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
                 bd = bv * (f32x4{1.f, 1.f, 1.f, 1.f} - bv);
                 wd = wv * (f32x4{1.f, 1.f, 1.f, 1.f} - wv);
             }
-            const f32x4 vv = load4(v + off), kv = f32x4{sK[l], sK[l + 1], sK[l + 2], sK[l + 3]};
+            const f32x4 vv = load4(v + off), kv = kr;
             *reinterpret_cast<f32x4*>(a.dq + off) = dq;
             *reinterpret_cast<f32x4*>(a.dk + off) = dk + dE * bv;
             *reinterpret_cast<f32x4*>(a.dv + off) = dU * wv;
