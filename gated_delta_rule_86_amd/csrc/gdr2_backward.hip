@@ -21,16 +21,19 @@
 // Kernels (all fp32 arithmetic; intermediates in a fp32 workspace, one
 // record per (sequence, head, chunk)):
 //   bwd_prep   one workgroup per chunk: G, E, U, E~, Q~, K^, gamma; M and P
-//              pair by pair (every exponent is G_t - G_s for s <= t, so no
-//              factor exceeds 1 for decays); X by substitution; W, U~.
+//              (pair by pair inside 16-token blocks, through block-referenced
+//              factors <= 1 across them); X by blocks; W, U~.
 //   bwd_dout   dO rows of every chunk into the workspace (zero past T).
-//   bwd_scan   per (sequence, head, 32 value columns): the state gradient
+//   bwd_frag   the scan's operands in MFMA fragment order.
+//   bwd_scan   per (sequence, head, 64 value columns): the state gradient
 //              through the chunks in reverse (columns evolve independently),
 //              recording Lam at every chunk end and dDelta.
-//   bgemm      batched C = alpha op(A) op(B) + beta C0 over all chunks (LDS
-//              tiles, 64x64 per workgroup) for the products above.
-//   bwd_decay  per chunk: the decay-weighted sums, dG, dg and the input
-//              gradients.
+//   bwd_sgrad, bwd_xgrad  per chunk: the state and WY-factor products above
+//              as chained 64x64 MFMA tiles in one workgroup (operands stay
+//              in cache between the products).
+//   bwd_decay  per chunk and 32 channels: the decay-weighted sums, dG, dg
+//              and the input gradients.
+//   bwd_norm   the prologue's normalisation, backwards (when asked for).
 #include "gdr2_device.h"
 #include "gdr2_internal.h"
 
@@ -775,46 +778,40 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bgemm: Cz = alpha * op(Az) * op(Bz) + beta * C0z for every record z.
-// op(X) is X or X^T of a row-major matrix with leading dimension ld.  M, N,
-// K are multiples of 64 / 16.  mask: 0 none, 1 keep n <= m, 2 keep n < m.
+// Tile products of the chunk-local gradient (fp32 MFMA).  op(X) is X or X^T
+// of a row-major matrix; every dimension is a multiple of 64 (M, N) or 16 (K).
 // ---------------------------------------------------------------------------
-struct GemmOp {
+// One row-major matrix operand of a tile product, already offset to its
+// record: element (r, c) at p[r * ld + c]; trans = 1 reads it as X^T.
+struct Mat {
     const float* p;
-    int64_t bs;      // elements between records
     int ld;
     int trans;
 };
 
-__global__ __launch_bounds__(NTB) void bgemm_kernel(int M, int N, int K, GemmOp A, GemmOp B, float* Cp,
-                                                    int64_t cbs, int ldc, float alpha, float beta,
-                                                    const float* C0, int64_t c0bs, int mask)
+// One 64x64 tile of C = alpha (op(A1) op(B1) + op(A2) op(B2)) + beta C0 at
+// rows m0.., columns n0.. of the record (the second product is skipped when
+// K2 == 0).  All NTB threads take part: wave (wm, wn) owns a 32x32 quarter
+// = 2x2 MFMA tiles, and each 16-deep k slab is staged as sA[m][k] and
+// sB[n][k] (rows padded to 20 floats), the layout Mma<float>::load reads.
+// mask: 0 none, 1 keep n <= m, 2 keep n < m.
+__device__ __forceinline__ void gemm_tile(float* sA, float* sB, int m0, int n0, int K1, Mat A1, Mat B1, int K2,
+                                          Mat A2, Mat B2, float* Cz, int ldc, float alpha, float beta,
+                                          const float* C0z, int mask)
 {
-    // 64x64 output tile; wave (wm, wn) owns a 32x32 quarter = 2x2 MFMA tiles.
-    // Each 16-deep k slab is staged as sA[m][k] and sB[n][k] (rows padded to
-    // 20 floats), the layout Mma<float>::load reads.
     constexpr int LS = 20;
-    __shared__ __align__(16) float sA[64 * LS];
-    __shared__ __align__(16) float sB[64 * LS];
-    const int tiles_n = N / 64, tiles = (M / 64) * tiles_n;
-    const int64_t z = blockIdx.x / tiles;
-    const int tile = (int)(blockIdx.x - z * tiles);
-    const int m0 = (tile / tiles_n) * 64, n0 = (tile % tiles_n) * 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    const float* Ap = A.p + z * A.bs;
-    const float* Bp = B.p + z * B.bs;
-    // this thread's float4 of the slab: along k (row-major operand) or along m / n
+    // this thread's float4 of a slab: along k (row-major operand) or along m / n
     const int ra = tid / 4, ka = 4 * (tid % 4);      // 64 rows x 4 float4 along k
     const int kb = tid / 16, ca = 4 * (tid % 16);    // 16 k-rows x 16 float4 along m / n
-    auto fetch = [&](const GemmOp& X, const float* Xp, int r0, int k0) -> f32x4 {
-        return X.trans == 0 ? *reinterpret_cast<const f32x4*>(Xp + (int64_t)(r0 + ra) * X.ld + k0 + ka)
-                            : *reinterpret_cast<const f32x4*>(Xp + (int64_t)(k0 + kb) * X.ld + r0 + ca);
+    // as a [row][k] source: A is "k along columns" when not transposed; B is
+    // when transposed (op(B)(k, n) = B[n][k])
+    auto fetch = [&](const float* p, int ld, bool k_cols, int r0, int k0) -> f32x4 {
+        return k_cols ? *reinterpret_cast<const f32x4*>(p + (int64_t)(r0 + ra) * ld + k0 + ka)
+                      : *reinterpret_cast<const f32x4*>(p + (int64_t)(k0 + kb) * ld + r0 + ca);
     };
-    // op(A)(m, k): A[m][k] (trans 0) or A[k][m]; op(B)(k, n): B[k][n] (trans 0) or B[n][k]
-    GemmOp Bk = B;
-    Bk.trans = B.trans ? 0 : 1;      // as a [n][k] source, B^T row-major is "k along rows"
-    auto stage = [&](float* sX, const GemmOp& X, f32x4 v) {
-        if (X.trans == 0) {
+    auto stage = [&](float* sX, bool k_cols, f32x4 v) {
+        if (k_cols) {
             *reinterpret_cast<f32x4*>(sX + ra * LS + ka) = v;
         } else {
 #pragma unroll
@@ -828,29 +825,35 @@ __global__ __launch_bounds__(NTB) void bgemm_kernel(int M, int N, int K, GemmOp 
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 va = fetch(A, Ap, m0, 0), vb = fetch(Bk, Bp, n0, 0);
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        __syncthreads();
-        stage(sA, A, va);
-        stage(sB, Bk, vb);
-        __syncthreads();
-        if (k0 + 16 < K) {
-            va = fetch(A, Ap, m0, k0 + 16);
-            vb = fetch(Bk, Bp, n0, k0 + 16);
+    for (int seg = 0; seg < 2; ++seg) {
+        const int K = seg == 0 ? K1 : K2;
+        if (K == 0)
+            break;
+        const Mat A = seg == 0 ? A1 : A2, B = seg == 0 ? B1 : B2;
+        const bool ak = A.trans == 0, bk = B.trans != 0;
+        f32x4 va = fetch(A.p, A.ld, ak, m0, 0), vb = fetch(B.p, B.ld, bk, n0, 0);
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            __syncthreads();
+            stage(sA, ak, va);
+            stage(sB, bk, vb);
+            __syncthreads();
+            if (k0 + 16 < K) {
+                va = fetch(A.p, A.ld, ak, m0, k0 + 16);
+                vb = fetch(B.p, B.ld, bk, n0, k0 + 16);
+            }
+            f32x4 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i] = Mma<float>::load(sA + (wm + 16 * i) * LS, LS, lane);
+                fb[i] = Mma<float>::load(sB + (wn + 16 * i) * LS, LS, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = Mma<float>::mma(fa[i], fb[j], acc[i][j]);
         }
-        f32x4 fa[2], fb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            fa[i] = Mma<float>::load(sA + (wm + 16 * i) * LS, LS, lane);
-            fb[i] = Mma<float>::load(sB + (wn + 16 * i) * LS, LS, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = Mma<float>::mma(fa[i], fb[j], acc[i][j]);
     }
-    float* Cz = Cp + z * cbs;
     const int gq = lane >> 4, cl = lane & 15;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -860,12 +863,74 @@ __global__ __launch_bounds__(NTB) void bgemm_kernel(int M, int N, int K, GemmOp 
             for (int x = 0; x < 4; ++x) {
                 const int m = m0 + wm + 16 * i + 4 * gq + x, n = n0 + wn + 16 * j + cl;
                 float val = alpha * acc[i][j][x];
-                if (C0)
-                    val += beta * C0[z * c0bs + (int64_t)m * ldc + n];
+                if (C0z)
+                    val += beta * C0z[(int64_t)m * ldc + n];
                 if ((mask == 1 && n > m) || (mask == 2 && n >= m))
                     val = 0.f;
                 Cz[(int64_t)m * ldc + n] = val;
             }
+}
+
+// Results of one tile product are read by the next one in the same
+// workgroup: complete the stores and meet at a barrier.
+__device__ __forceinline__ void tile_done()
+{
+    __threadfence_block();
+    __syncthreads();
+}
+
+// The products of the chunk-local gradient that involve the states, one
+// workgroup per chunk record (S = the chunk-start state, Lam = dL/dS at its
+// end):  Delta = U~ - W S,  dQ~ = dO S^T,  dW = -dDelta S^T,
+// dK^ = Delta Lam^T,  dP = tril(dO Delta^T).
+template <int D>
+__global__ __launch_bounds__(NTB) void bwd_sgrad_kernel(BwdArgs a)
+{
+    constexpr int C = BC, NT = D / 64;
+    __shared__ __align__(16) float sA[64 * 20];
+    __shared__ __align__(16) float sB[64 * 20];
+    const int64_t r = blockIdx.x;
+    float* ws = a.ws;
+    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C, dd = (size_t)r * D * D;
+    const Mat S{a.S_chunks + dd, D, 0}, St{a.S_chunks + dd, D, 1}, Lt{ws + a.L.Lam + dd, D, 1};
+    const Mat W{ws + a.L.W + cd, D, 0}, dO{ws + a.L.dO + cd, D, 0}, dDel{ws + a.L.dDel + cd, D, 0};
+    const Mat Del{ws + a.L.Del + cd, D, 0}, Delt{ws + a.L.Del + cd, D, 1}, none{nullptr, 0, 0};
+    for (int nt = 0; nt < NT; ++nt)
+        gemm_tile(sA, sB, 0, 64 * nt, D, W, S, 0, none, none, ws + a.L.Del + cd, D, -1.f, 1.f, ws + a.L.Ut + cd, 0);
+    for (int nt = 0; nt < NT; ++nt) {
+        gemm_tile(sA, sB, 0, 64 * nt, D, dO, St, 0, none, none, ws + a.L.dQt + cd, D, 1.f, 0.f, nullptr, 0);
+        gemm_tile(sA, sB, 0, 64 * nt, D, dDel, St, 0, none, none, ws + a.L.dW + cd, D, -1.f, 0.f, nullptr, 0);
+    }
+    tile_done();                        // Delta complete
+    for (int nt = 0; nt < NT; ++nt)
+        gemm_tile(sA, sB, 0, 64 * nt, D, Del, Lt, 0, none, none, ws + a.L.dKh + cd, D, 1.f, 0.f, nullptr, 0);
+    gemm_tile(sA, sB, 0, 0, D, dO, Delt, 0, none, none, ws + a.L.dP + cc, C, 1.f, 0.f, nullptr, 1);
+}
+
+// The products through the WY factor X = (I + M)^-1, one workgroup per
+// chunk record:  dX = dDelta U^T + dW E~^T,  dM = strict_tril(-X^T dX X^T),
+// dU = X^T dDelta,  dE~ = X^T dW.
+template <int D>
+__global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
+{
+    constexpr int C = BC, NT = D / 64;
+    __shared__ __align__(16) float sA[64 * 20];
+    __shared__ __align__(16) float sB[64 * 20];
+    const int64_t r = blockIdx.x;
+    float* ws = a.ws;
+    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
+    const Mat dDel{ws + a.L.dDel + cd, D, 0}, dW{ws + a.L.dW + cd, D, 0};
+    const Mat Ut{ws + a.L.U + cd, D, 1}, Ett{ws + a.L.Et + cd, D, 1};
+    const Mat Xt{ws + a.L.X + cc, C, 1}, dX{ws + a.L.dX + cc, C, 0}, T1{ws + a.L.T1 + cc, C, 0}, none{nullptr, 0, 0};
+    gemm_tile(sA, sB, 0, 0, D, dDel, Ut, D, dW, Ett, ws + a.L.dX + cc, C, 1.f, 0.f, nullptr, 0);
+    for (int nt = 0; nt < NT; ++nt) {
+        gemm_tile(sA, sB, 0, 64 * nt, C, Xt, dDel, 0, none, none, ws + a.L.dU + cd, D, 1.f, 0.f, nullptr, 0);
+        gemm_tile(sA, sB, 0, 64 * nt, C, Xt, dW, 0, none, none, ws + a.L.dEt + cd, D, 1.f, 0.f, nullptr, 0);
+    }
+    tile_done();                        // dX complete
+    gemm_tile(sA, sB, 0, 0, C, dX, Xt, 0, none, none, ws + a.L.T1 + cc, C, 1.f, 0.f, nullptr, 0);
+    tile_done();                        // T1 complete
+    gemm_tile(sA, sB, 0, 0, C, Xt, T1, 0, none, none, ws + a.L.dM + cc, C, -1.f, 0.f, nullptr, 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -1241,16 +1306,6 @@ hipError_t zero_fill(float* p, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t gemm(hipStream_t s, int64_t nrec, int M, int N, int K, GemmOp A, GemmOp B, float* Cp,
-                int64_t cbs, int ldc, float alpha, float beta = 0.f, const float* C0 = nullptr,
-                int64_t c0bs = 0, int mask = 0)
-{
-    const int64_t blocks = nrec * (M / 64) * (N / 64);
-    hipLaunchKernelGGL(bgemm_kernel, dim3((unsigned)blocks), dim3(NTB), 0, s, M, N, K, A, B, Cp,
-                       cbs, ldc, alpha, beta, C0, c0bs, mask);
-    return hipGetLastError();
-}
-
 template <typename E, int D>
 hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
 {
@@ -1293,29 +1348,10 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    float* ws = a.ws;
-    const BwdLayout& L = a.L;
-    const int64_t CD = (int64_t)C * D, CC = (int64_t)C * C, DD = (int64_t)D * D;
-    auto op = [&](size_t off, int64_t bs, int ld, int tr) { return GemmOp{ws + off, bs, ld, tr}; };
-    const GemmOp Sop{x.S_chunks, DD, D, 0}, SopT{x.S_chunks, DD, D, 1};
-    // Delta = U~ - W S
-    if ((e = gemm(s, nrec, C, D, D, op(L.W, CD, D, 0), Sop, ws + L.Del, CD, D, -1.f, 1.f, ws + L.Ut, CD)) != hipSuccess) return e;
-    // dQ~ = dO S^T, dW = -dDelta S^T
-    if ((e = gemm(s, nrec, C, D, D, op(L.dO, CD, D, 0), SopT, ws + L.dQt, CD, D, 1.f)) != hipSuccess) return e;
-    if ((e = gemm(s, nrec, C, D, D, op(L.dDel, CD, D, 0), SopT, ws + L.dW, CD, D, -1.f)) != hipSuccess) return e;
-    // dK^ = Delta Lam^T
-    if ((e = gemm(s, nrec, C, D, D, op(L.Del, CD, D, 0), op(L.Lam, DD, D, 1), ws + L.dKh, CD, D, 1.f)) != hipSuccess) return e;
-    // dP = tril(dO Delta^T)
-    if ((e = gemm(s, nrec, C, C, D, op(L.dO, CD, D, 0), op(L.Del, CD, D, 1), ws + L.dP, CC, C, 1.f, 0.f, nullptr, 0, 1)) != hipSuccess) return e;
-    // dX = dDelta U^T + dW E~^T
-    if ((e = gemm(s, nrec, C, C, D, op(L.dDel, CD, D, 0), op(L.U, CD, D, 1), ws + L.dX, CC, C, 1.f)) != hipSuccess) return e;
-    if ((e = gemm(s, nrec, C, C, D, op(L.dW, CD, D, 0), op(L.Et, CD, D, 1), ws + L.dX, CC, C, 1.f, 1.f, ws + L.dX, CC)) != hipSuccess) return e;
-    // dU = X^T dDelta, dE~ = X^T dW
-    if ((e = gemm(s, nrec, C, D, C, op(L.X, CC, C, 1), op(L.dDel, CD, D, 0), ws + L.dU, CD, D, 1.f)) != hipSuccess) return e;
-    if ((e = gemm(s, nrec, C, D, C, op(L.X, CC, C, 1), op(L.dW, CD, D, 0), ws + L.dEt, CD, D, 1.f)) != hipSuccess) return e;
-    // dM = strict_tril(-X^T dX X^T)
-    if ((e = gemm(s, nrec, C, C, C, op(L.dX, CC, C, 0), op(L.X, CC, C, 1), ws + L.T1, CC, C, 1.f)) != hipSuccess) return e;
-    if ((e = gemm(s, nrec, C, C, C, op(L.X, CC, C, 1), op(L.T1, CC, C, 0), ws + L.dM, CC, C, -1.f, 0.f, nullptr, 0, 2)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_sgrad_kernel<D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_xgrad_kernel<D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
 
     hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(nrec * (D / DC))), dim3(NTB), lds_decay, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
