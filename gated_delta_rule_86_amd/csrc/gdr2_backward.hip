@@ -792,31 +792,34 @@ struct Mat {
 // One 64x64 tile of C = alpha (op(A1) op(B1) + op(A2) op(B2)) + beta C0 at
 // rows m0.., columns n0.. of the record (the second product is skipped when
 // K2 == 0).  All NTB threads take part: wave (wm, wn) owns a 32x32 quarter
-// = 2x2 MFMA tiles, and each 16-deep k slab is staged as sA[m][k] and
-// sB[n][k] (rows padded to 20 floats), the layout Mma<float>::load reads.
-// mask: 0 none, 1 keep n <= m, 2 keep n < m.
+// = 2x2 MFMA tiles, and each KB-deep k slab is staged in fp32 as sA[m][k]
+// and sB[n][k] (rows padded to KB + 4 floats), the layout MM::load reads;
+// with MM = Mma<bf16> the operands are rounded to bf16 as they are loaded
+// into the MFMA (fp32 accumulation).  mask: 0 none, 1 keep n <= m, 2 keep
+// n < m.
+template <typename MM>
 __device__ __forceinline__ void gemm_tile(float* sA, float* sB, int m0, int n0, int K1, Mat A1, Mat B1, int K2,
                                           Mat A2, Mat B2, float* Cz, int ldc, float alpha, float beta,
                                           const float* C0z, int mask)
 {
-    constexpr int LS = 20;
+    constexpr int KB = MM::KB, LS = KB + 4, NV = KB / 16;     // float4 per thread per operand slab
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    // this thread's float4 of a slab: along k (row-major operand) or along m / n
-    const int ra = tid / 4, ka = 4 * (tid % 4);      // 64 rows x 4 float4 along k
+    // this thread's float4s of a slab: along k (row-major operand) or along m / n
+    const int ra = tid / 4, ka = 4 * (tid % 4);      // 64 rows x 4 float4 along k, per 16 of k
     const int kb = tid / 16, ca = 4 * (tid % 16);    // 16 k-rows x 16 float4 along m / n
     // as a [row][k] source: A is "k along columns" when not transposed; B is
     // when transposed (op(B)(k, n) = B[n][k])
-    auto fetch = [&](const float* p, int ld, bool k_cols, int r0, int k0) -> f32x4 {
-        return k_cols ? *reinterpret_cast<const f32x4*>(p + (int64_t)(r0 + ra) * ld + k0 + ka)
-                      : *reinterpret_cast<const f32x4*>(p + (int64_t)(k0 + kb) * ld + r0 + ca);
+    auto fetch = [&](const float* p, int ld, bool k_cols, int r0, int k0, int v) -> f32x4 {
+        return k_cols ? *reinterpret_cast<const f32x4*>(p + (int64_t)(r0 + ra) * ld + k0 + 16 * v + ka)
+                      : *reinterpret_cast<const f32x4*>(p + (int64_t)(k0 + 16 * v + kb) * ld + r0 + ca);
     };
-    auto stage = [&](float* sX, bool k_cols, f32x4 v) {
+    auto stage = [&](float* sX, bool k_cols, f32x4 x, int v) {
         if (k_cols) {
-            *reinterpret_cast<f32x4*>(sX + ra * LS + ka) = v;
+            *reinterpret_cast<f32x4*>(sX + ra * LS + 16 * v + ka) = x;
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                sX[(ca + j) * LS + kb] = v[j];
+                sX[(ca + j) * LS + 16 * v + kb] = x[j];
         }
     };
     f32x4 acc[2][2];
@@ -831,27 +834,38 @@ __device__ __forceinline__ void gemm_tile(float* sA, float* sB, int m0, int n0, 
             break;
         const Mat A = seg == 0 ? A1 : A2, B = seg == 0 ? B1 : B2;
         const bool ak = A.trans == 0, bk = B.trans != 0;
-        f32x4 va = fetch(A.p, A.ld, ak, m0, 0), vb = fetch(B.p, B.ld, bk, n0, 0);
-        for (int k0 = 0; k0 < K; k0 += 16) {
+        f32x4 va[NV], vb[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            va[v] = fetch(A.p, A.ld, ak, m0, 0, v);
+            vb[v] = fetch(B.p, B.ld, bk, n0, 0, v);
+        }
+        for (int k0 = 0; k0 < K; k0 += KB) {
             __syncthreads();
-            stage(sA, ak, va);
-            stage(sB, bk, vb);
-            __syncthreads();
-            if (k0 + 16 < K) {
-                va = fetch(A.p, A.ld, ak, m0, k0 + 16);
-                vb = fetch(B.p, B.ld, bk, n0, k0 + 16);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                stage(sA, ak, va[v], v);
+                stage(sB, bk, vb[v], v);
             }
-            f32x4 fa[2], fb[2];
+            __syncthreads();
+            if (k0 + KB < K) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    va[v] = fetch(A.p, A.ld, ak, m0, k0 + KB, v);
+                    vb[v] = fetch(B.p, B.ld, bk, n0, k0 + KB, v);
+                }
+            }
+            typename MM::Frag fa[2], fb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                fa[i] = Mma<float>::load(sA + (wm + 16 * i) * LS, LS, lane);
-                fb[i] = Mma<float>::load(sB + (wn + 16 * i) * LS, LS, lane);
+                fa[i] = MM::load(sA + (wm + 16 * i) * LS, LS, lane);
+                fb[i] = MM::load(sB + (wn + 16 * i) * LS, LS, lane);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = Mma<float>::mma(fa[i], fb[j], acc[i][j]);
+                    acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
         }
     }
     const int gq = lane >> 4, cl = lane & 15;
@@ -883,12 +897,12 @@ __device__ __forceinline__ void tile_done()
 // workgroup per chunk record (S = the chunk-start state, Lam = dL/dS at its
 // end):  Delta = U~ - W S,  dQ~ = dO S^T,  dW = -dDelta S^T,
 // dK^ = Delta Lam^T,  dP = tril(dO Delta^T).
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_sgrad_kernel(BwdArgs a)
 {
-    constexpr int C = BC, NT = D / 64;
-    __shared__ __align__(16) float sA[64 * 20];
-    __shared__ __align__(16) float sB[64 * 20];
+    constexpr int C = BC, NT = D / 64, LS = Mma<E>::KB + 4;
+    __shared__ __align__(16) float sA[64 * LS];
+    __shared__ __align__(16) float sB[64 * LS];
     const int64_t r = blockIdx.x;
     float* ws = a.ws;
     const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C, dd = (size_t)r * D * D;
@@ -896,41 +910,41 @@ __global__ __launch_bounds__(NTB) void bwd_sgrad_kernel(BwdArgs a)
     const Mat W{ws + a.L.W + cd, D, 0}, dO{ws + a.L.dO + cd, D, 0}, dDel{ws + a.L.dDel + cd, D, 0};
     const Mat Del{ws + a.L.Del + cd, D, 0}, Delt{ws + a.L.Del + cd, D, 1}, none{nullptr, 0, 0};
     for (int nt = 0; nt < NT; ++nt)
-        gemm_tile(sA, sB, 0, 64 * nt, D, W, S, 0, none, none, ws + a.L.Del + cd, D, -1.f, 1.f, ws + a.L.Ut + cd, 0);
+        gemm_tile<Mma<E>>(sA, sB, 0, 64 * nt, D, W, S, 0, none, none, ws + a.L.Del + cd, D, -1.f, 1.f, ws + a.L.Ut + cd, 0);
     for (int nt = 0; nt < NT; ++nt) {
-        gemm_tile(sA, sB, 0, 64 * nt, D, dO, St, 0, none, none, ws + a.L.dQt + cd, D, 1.f, 0.f, nullptr, 0);
-        gemm_tile(sA, sB, 0, 64 * nt, D, dDel, St, 0, none, none, ws + a.L.dW + cd, D, -1.f, 0.f, nullptr, 0);
+        gemm_tile<Mma<E>>(sA, sB, 0, 64 * nt, D, dO, St, 0, none, none, ws + a.L.dQt + cd, D, 1.f, 0.f, nullptr, 0);
+        gemm_tile<Mma<E>>(sA, sB, 0, 64 * nt, D, dDel, St, 0, none, none, ws + a.L.dW + cd, D, -1.f, 0.f, nullptr, 0);
     }
     tile_done();                        // Delta complete
     for (int nt = 0; nt < NT; ++nt)
-        gemm_tile(sA, sB, 0, 64 * nt, D, Del, Lt, 0, none, none, ws + a.L.dKh + cd, D, 1.f, 0.f, nullptr, 0);
-    gemm_tile(sA, sB, 0, 0, D, dO, Delt, 0, none, none, ws + a.L.dP + cc, C, 1.f, 0.f, nullptr, 1);
+        gemm_tile<Mma<E>>(sA, sB, 0, 64 * nt, D, Del, Lt, 0, none, none, ws + a.L.dKh + cd, D, 1.f, 0.f, nullptr, 0);
+    gemm_tile<Mma<E>>(sA, sB, 0, 0, D, dO, Delt, 0, none, none, ws + a.L.dP + cc, C, 1.f, 0.f, nullptr, 1);
 }
 
 // The products through the WY factor X = (I + M)^-1, one workgroup per
 // chunk record:  dX = dDelta U^T + dW E~^T,  dM = strict_tril(-X^T dX X^T),
 // dU = X^T dDelta,  dE~ = X^T dW.
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
 {
-    constexpr int C = BC, NT = D / 64;
-    __shared__ __align__(16) float sA[64 * 20];
-    __shared__ __align__(16) float sB[64 * 20];
+    constexpr int C = BC, NT = D / 64, LS = Mma<E>::KB + 4;
+    __shared__ __align__(16) float sA[64 * LS];
+    __shared__ __align__(16) float sB[64 * LS];
     const int64_t r = blockIdx.x;
     float* ws = a.ws;
     const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
     const Mat dDel{ws + a.L.dDel + cd, D, 0}, dW{ws + a.L.dW + cd, D, 0};
     const Mat Ut{ws + a.L.U + cd, D, 1}, Ett{ws + a.L.Et + cd, D, 1};
     const Mat Xt{ws + a.L.X + cc, C, 1}, dX{ws + a.L.dX + cc, C, 0}, T1{ws + a.L.T1 + cc, C, 0}, none{nullptr, 0, 0};
-    gemm_tile(sA, sB, 0, 0, D, dDel, Ut, D, dW, Ett, ws + a.L.dX + cc, C, 1.f, 0.f, nullptr, 0);
+    gemm_tile<Mma<E>>(sA, sB, 0, 0, D, dDel, Ut, D, dW, Ett, ws + a.L.dX + cc, C, 1.f, 0.f, nullptr, 0);
     for (int nt = 0; nt < NT; ++nt) {
-        gemm_tile(sA, sB, 0, 64 * nt, C, Xt, dDel, 0, none, none, ws + a.L.dU + cd, D, 1.f, 0.f, nullptr, 0);
-        gemm_tile(sA, sB, 0, 64 * nt, C, Xt, dW, 0, none, none, ws + a.L.dEt + cd, D, 1.f, 0.f, nullptr, 0);
+        gemm_tile<Mma<E>>(sA, sB, 0, 64 * nt, C, Xt, dDel, 0, none, none, ws + a.L.dU + cd, D, 1.f, 0.f, nullptr, 0);
+        gemm_tile<Mma<E>>(sA, sB, 0, 64 * nt, C, Xt, dW, 0, none, none, ws + a.L.dEt + cd, D, 1.f, 0.f, nullptr, 0);
     }
     tile_done();                        // dX complete
-    gemm_tile(sA, sB, 0, 0, C, dX, Xt, 0, none, none, ws + a.L.T1 + cc, C, 1.f, 0.f, nullptr, 0);
+    gemm_tile<Mma<E>>(sA, sB, 0, 0, C, dX, Xt, 0, none, none, ws + a.L.T1 + cc, C, 1.f, 0.f, nullptr, 0);
     tile_done();                        // T1 complete
-    gemm_tile(sA, sB, 0, 0, C, Xt, T1, 0, none, none, ws + a.L.dM + cc, C, -1.f, 0.f, nullptr, 2);
+    gemm_tile<Mma<E>>(sA, sB, 0, 0, C, Xt, T1, 0, none, none, ws + a.L.dM + cc, C, -1.f, 0.f, nullptr, 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -1348,9 +1362,9 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    hipLaunchKernelGGL((bwd_sgrad_kernel<D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    hipLaunchKernelGGL((bwd_sgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_xgrad_kernel<D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    hipLaunchKernelGGL((bwd_xgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(nrec * (D / DC))), dim3(NTB), lds_decay, s, a);
