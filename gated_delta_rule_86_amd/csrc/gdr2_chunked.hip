@@ -180,10 +180,10 @@ __device__ __forceinline__ void unpack<float>(const u32x4& r, float* out)
         out[i] = __uint_as_float(r[i]);
 }
 
-// The scalar held in element 0 of a width-1 gate's raw bits.
-template <typename E> __device__ __forceinline__ float scalar0(const u32x4& r);
-template <> __device__ __forceinline__ float scalar0<bf16>(const u32x4& r) { return __uint_as_float(r[0] << 16); }
-template <> __device__ __forceinline__ float scalar0<float>(const u32x4& r) { return __uint_as_float(r[0]); }
+// A width-1 gate's value from its raw bits, zero-extended to 32 bits.
+template <typename E> __device__ __forceinline__ float gate_bits(unsigned int u);
+template <> __device__ __forceinline__ float gate_bits<bf16>(unsigned int u) { return __uint_as_float(u << 16); }
+template <> __device__ __forceinline__ float gate_bits<float>(unsigned int u) { return __uint_as_float(u); }
 
 template <typename E> __device__ __forceinline__ u32x4 pack_vec(const float* x);
 template <>
@@ -207,14 +207,6 @@ __device__ __forceinline__ u32x4 ldg16(const void* p)
 }
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void sts16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-
-// Bits of one element, for width-1 gates.
-template <typename E> __device__ __forceinline__ unsigned int ld_bits(const E* p);
-template <> __device__ __forceinline__ unsigned int ld_bits<bf16>(const bf16* p)
-{
-    return *reinterpret_cast<const unsigned short*>(p);
-}
-template <> __device__ __forceinline__ unsigned int ld_bits<float>(const float* p) { return __float_as_uint(*p); }
 
 // Position of logical k index `col` inside its fragment row (see Frags).
 template <typename E> __device__ __forceinline__ int kpos(int col);
@@ -370,7 +362,7 @@ struct PrepShape {
     // raw g [C][D] (exact path: G) lives in its own static LDS object, so the
     // compiler knows the asynchronous copies into it touch nothing else
     static constexpr size_t SZ_G = (size_t)C * D * 4;
-    static_assert(SMEM + SZ_G <= 160 * 1024, "LDS budget");
+    static_assert(SMEM + SZ_G + 2 * C * 4 <= 160 * 1024, "LDS budget");   // + width-1 b, w
     static_assert(C == 32 || C == 64, "chunk");
     static_assert(64 % NCG == 0 && NCG >= 8 && TPL >= 1 && TW == LPC * TPL, "lane mapping");
     static_assert(NWB == NWP || NH == 1, "halves need every wave in phase B");
@@ -385,8 +377,8 @@ __device__ __forceinline__ int swz(int r, int col)
     return r * D + (((col / VEC) ^ (r & 7)) * VEC) + (col % VEC);
 }
 
-// Raw inputs of one lane's TPL tokens (bit patterns; width-1 gates keep their
-// scalar in element 0 and are broadcast when used).
+// Raw inputs of one lane's TPL tokens (bit patterns; width-1 gates are not
+// held here but copied to LDS by prep_copy_bw).
 template <typename E, int D, int C>
 struct PrepRegs {
     typedef PrepShape<E, D, C> S;
@@ -413,18 +405,10 @@ __device__ __forceinline__ void prep_load(const PrepArgs& a, const ChunkPos& cp,
             R.q[j] = ldg16((const E*)a.q + off);
         if (PART == 2)
             R.v[j] = ldg16((const E*)a.v + off);
-        if (PART == 3) {
-            if (WB == 0 ? a.bw != 1 : WB != 1)
-                R.b[j] = ldg16((const E*)a.b + off);
-            else
-                R.b[j][0] = ld_bits<E>((const E*)a.b + row);
-        }
-        if (PART == 4) {
-            if (WW == 0 ? a.ww != 1 : WW != 1)
-                R.w[j] = ldg16((const E*)a.w + off);
-            else
-                R.w[j][0] = ld_bits<E>((const E*)a.w + row);
-        }
+        if (PART == 3 && (WB == 0 ? a.bw != 1 : WB != 1))
+            R.b[j] = ldg16((const E*)a.b + off);
+        if (PART == 4 && (WW == 0 ? a.ww != 1 : WW != 1))
+            R.w[j] = ldg16((const E*)a.w + off);
     }
 }
 
@@ -448,12 +432,47 @@ __device__ __forceinline__ void prep_copy_g(const PrepArgs& a, const ChunkPos& c
     }
 }
 
+// One element per lane from global memory into the 32-bit LDS word `lane` of
+// dst (zero-extended), without a register.
+template <typename E> __device__ __forceinline__ void copy_elem_lds(const E* src, unsigned int* dst);
+template <>
+__device__ __forceinline__ void copy_elem_lds<bf16>(const bf16* src, unsigned int* dst)
+{
+    typedef __attribute__((address_space(3))) void lds_t;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)dst, 2, 0, 0);
+}
+template <>
+__device__ __forceinline__ void copy_elem_lds<float>(const float* src, unsigned int* dst)
+{
+    typedef __attribute__((address_space(3))) void lds_t;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)dst, 4, 0, 0);
+}
+
+// Copy one chunk's width-1 erase and write gates straight into LDS
+// (global_load_lds, one element per lane): token t's bits land
+// zero-extended in 32-bit word t of sBW (b) and of sBW + C (w), so no lane
+// spends a register load on a scalar that 16 lanes share.  Rows past the
+// valid length repeat the last valid row.
+template <int WB, int WW, typename E, int D, int C>
+__device__ __forceinline__ void prep_copy_bw(const PrepArgs& a, const ChunkPos& cp, unsigned int* sBW,
+                                             int wave, int lane)
+{
+    const bool nb = WB == 0 ? a.bw == 1 : WB == 1, nw = WW == 0 ? a.ww == 1 : WW == 1;
+    if (lane < C) {
+        const int64_t row = cp.row0 + (int64_t)min(lane, cp.L - 1) * a.H;
+        if (nb && wave == 1)
+            copy_elem_lds<E>((const E*)a.b + row, sBW);
+        if (nw && wave == 2)
+            copy_elem_lds<E>((const E*)a.w + row, sBW + C);
+    }
+}
+
 // Phase B for one lane: decay-referenced operands of its tokens into LDS.
 // VALID: every token of the chunk is valid (no zeroing needed).
 template <bool VALID, bool SECOND, bool PRO, typename E, int D, int C>
 __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const float (*G)[16 / sizeof(E)],
                                                const float* gh, int bw, int ww, int L, int t0, int c0,
-                                               unsigned char* smem, int pro)
+                                               unsigned char* smem, const unsigned int* sBW, int pro)
 {
     typedef PrepShape<E, D, C> S;
     constexpr int VEC = S::VEC;
@@ -515,7 +534,7 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
         {
             float bb[VEC];
             unpack<E>(R.b[j], bb);
-            float bs = scalar0<E>(R.b[j]);
+            float bs = bw == 1 ? gate_bits<E>(sBW[t]) : 0.f;
             if constexpr (PRO) {
                 if (pro & GDR2_PROLOGUE_GATES) {
                     bs = sigm(bs);
@@ -570,7 +589,7 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
             float vv[VEC], wv[VEC];
             unpack<E>(R.v[j], vv);
             unpack<E>(R.w[j], wv);
-            float ws = scalar0<E>(R.w[j]);
+            float ws = ww == 1 ? gate_bits<E>(sBW[C + t]) : 0.f;
             if constexpr (PRO) {
                 if (pro & GDR2_PROLOGUE_GATES) {
                     ws = sigm(ws);
@@ -632,6 +651,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
     float* sFk = reinterpret_cast<float*>(smem + S::OFF_FK);
     int* sFlag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
     __shared__ __align__(16) float sG[C * D];
+    __shared__ __align__(16) unsigned int sBW[2 * C];   // width-1 b and w of the chunk
 
     const int wave = threadIdx.x >> 6;
     const bool ab = wave < S::NWB;              // waves of phases A and B
@@ -657,6 +677,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         const ChunkPos cp0 = walk.pos(a.NC, a.T, a.H, C);
         const int t0 = wave * S::TW + (lane % S::LPC) * S::TPL, c0 = (lane / S::LPC) * VEC;
         prep_copy_g<WG, E, D, C>(a, cp0, reinterpret_cast<unsigned char*>(sG), wave, lane);
+        prep_copy_bw<WB, WW, E, D, C>(a, cp0, sBW, wave, lane);
         if (ab) {
             prep_load<0, WB, WW>(a, cp0, Rn, t0, c0);
             prep_load<1, WB, WW>(a, cp0, Rn, t0, c0);
@@ -825,17 +846,19 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             }
             float mx;
             if (second)
-                mx = full_chunk ? prep_operands<true, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro)
-                                : prep_operands<false, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro);
+                mx = full_chunk ? prep_operands<true, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro)
+                                : prep_operands<false, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro);
             else
-                mx = full_chunk ? prep_operands<true, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro)
-                                : prep_operands<false, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, a.pro);
+                mx = full_chunk ? prep_operands<true, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro)
+                                : prep_operands<false, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro);
             if (mx > kSpanMax)
                 *sFlag = 1;
             if (pre)
                 prep_load<3, WB, WW>(a, np, Rn, t0, c0);
         }
         lds_barrier();   // B2: operands in LDS
+        if (next < a.nrec)   // phase B has read this chunk's width-1 gates
+            prep_copy_bw<WB, WW, E, D, C>(a, np, sBW, wave, lane);
 
         E* gP = (E*)a.P + rec * (F::P_BYTES / sizeof(E));
         if (pre)
