@@ -368,13 +368,23 @@ struct PrepShape {
     static_assert(NWB == NWP || NH == 1, "halves need every wave in phase B");
 };
 
-// Element offset of element `col` of row `r` in a swizzled [rows][D] array:
-// 16-byte chunk j of row r sits at chunk j ^ (r & 7).
+// Row swizzle of the [rows][D] operand arrays: 16-byte chunk j of row r
+// sits at chunk j ^ (r & SWZ_MASK), with the mask as wide as the row allows
+// up to 15, so the 16 rows that one 16-lane group of a fragment read touches
+// land on distinct banks.
+template <typename E, int D>
+constexpr int swz_mask()
+{
+    constexpr int NCG = D * (int)sizeof(E) / 16;   // 16-byte chunks per row
+    return (NCG < 16 ? NCG : 16) - 1;
+}
+
+// Element offset of element `col` of row `r` in a swizzled [rows][D] array.
 template <typename E, int D>
 __device__ __forceinline__ int swz(int r, int col)
 {
     constexpr int VEC = 16 / (int)sizeof(E);
-    return r * D + (((col / VEC) ^ (r & 7)) * VEC) + (col % VEC);
+    return r * D + (((col / VEC) ^ (r & swz_mask<E, D>())) * VEC) + (col % VEC);
 }
 
 // Raw inputs of one lane's TPL tokens (bit patterns; width-1 gates are not
@@ -614,7 +624,7 @@ template <typename E, int D>
 __device__ __forceinline__ typename Mma<E>::Frag row_frag(const E* base, int r, int ch)
 {
     constexpr int VEC = 16 / (int)sizeof(E);
-    return *reinterpret_cast<const typename Mma<E>::Frag*>(base + r * D + ((ch ^ (r & 7)) * VEC));
+    return *reinterpret_cast<const typename Mma<E>::Frag*>(base + r * D + ((ch ^ (r & swz_mask<E, D>())) * VEC));
 }
 
 // Four consecutive elements (col a multiple of 4) of a swizzled row array.
