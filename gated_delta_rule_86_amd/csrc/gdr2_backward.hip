@@ -958,6 +958,10 @@ __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
 // (dM is strictly lower, so the u == t terms of dM vanish.)
 // ---------------------------------------------------------------------------
 constexpr int DC = 32;                 // channels per decay workgroup
+// Largest decay span (natural log units) over one 16-token block for which
+// the diagonal block's pairs go through the block-referenced rows: every
+// factor then stays within e^{+-kDiagSpan}, far inside fp32's range.
+constexpr float kDiagSpan = 60.f;
 constexpr int LC = DC + 1;             // padded LDS row of the per-channel arrays
 constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte aligned)
 
@@ -1015,9 +1019,11 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
         *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
     }
-    // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam):
-    // every thread sums its share (D / NRG state columns, RPT tokens) of its
-    // channel, then the NRG partial sums of a channel are added up
+    __syncthreads();
+    // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam) and
+    // K^ = k e^{G_L - G} recomputed from the rows in LDS: every thread sums
+    // its share (D / NRG state columns, RPT tokens) of its channel, then the
+    // NRG partial sums of a channel are added up
     {
         constexpr int JPT = D / NRG;
         const float* S = a.S_chunks + (size_t)r * D * D + (size_t)i * D + rg * JPT;
@@ -1029,10 +1035,11 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             acc += s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
         }
         acc *= ws[a.L.gam + (size_t)r * D + i];
+        const float GL = sG[(C - 1) * LC + il];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const size_t x = cdo + (size_t)(t0 + m) * D + i;
-            acc += ws[a.L.dKh + x] * ws[a.L.Kh + x];
+            const int l = (t0 + m) * LC + il;
+            acc += ws[a.L.dKh + cdo + (size_t)(t0 + m) * D + i] * (sK[l] * expf(GL - sG[l]));
         }
         sdG[rg * LC + il] = acc;        // sdG is free until the main loop
     }
@@ -1054,6 +1061,16 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     }
     grow = __syncthreads_or(grow);
 
+    // a 16-token block whose decay spans more than kDiagSpan in some channel:
+    // the diagonal blocks take the pair-by-pair pass below
+    int steep = 0;
+    for (int e = tid; e < (C / 16) * DC; e += NTB) {
+        const int T = e / DC, c = e % DC;
+        steep |= sG[16 * T * LC + c] - sG[(16 * T + 15) * LC + c] > kDiagSpan;
+    }
+    steep = __syncthreads_or(steep);
+    const bool pairwise = grow || steep;
+
     float Gt[RPT], dEm[RPT], dqp[RPT], dkm[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
@@ -1061,8 +1078,8 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         dEm[m] = dqp[m] = dkm[m] = 0.f;
     }
     // the partner tokens u of the pair-by-pair pass: all of them (growth), or
-    // only the 16-token block of the thread's rows
-    const int u_lo = grow ? 0 : (t0 / 16) * 16, u_hi = grow ? C : u_lo + 16;
+    // only the 16-token block of the thread's rows (steep blocks)
+    const int u_lo = grow ? 0 : (t0 / 16) * 16, u_hi = !pairwise ? u_lo : grow ? C : u_lo + 16;
     for (int u0 = u_lo; u0 < u_hi; u0 += 4) {
         f32x4 rM[RPT], rP[RPT];          // dM[t, u0..u0+3], dP[t, u0..u0+3]
 #pragma unroll
@@ -1121,6 +1138,47 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         for (int m = 0; m < RPT; ++m) {
             fa[m] = __expf(Gt[m] - sG[16 * Tb * LC + il]);
             fb[m] = __expf(sG[(16 * Tb + 15) * LC + il] - Gt[m]);
+        }
+        if (!pairwise) {
+            // the diagonal block through the same rows (span <= kDiagSpan):
+            //   e^{G_t - G_s} = e^{G_t - G_16T+15} (k_s e^{G_16T+15 - G_s}) / k_s
+            //                 = e^{G_16T - G_s} (e_t e^{G_t - G_16T}) / e_t
+            // so the sums as the later token scale by e^{G_t - G_16T+15} >= 1
+            // and those as the earlier token by e^{G_16T - G_t} >= 1
+            float am[RPT] = {}, ap[RPT] = {}, ak[RPT] = {};
+            for (int u0 = 16 * Tb; u0 < 16 * Tb + 16; u0 += 4) {
+                f32x4 rM[RPT], rP[RPT];      // dM[t, u0..u0+3], dP[t, u0..u0+3]
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    rM[m] = *reinterpret_cast<const f32x4*>(sdM + (t0 + m) * LPC + u0);
+                    rP[m] = *reinterpret_cast<const f32x4*>(sdP + (t0 + m) * LPC + u0);
+                }
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu) {
+                    const int u = u0 + uu;
+                    const float kb = sK[u * LC + il], eh = sE[u * LC + il], qh = sQ[u * LC + il];
+                    const f32x4 cM0 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0);
+                    const f32x4 cM1 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0 + 4);
+                    const f32x4 cP0 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0);
+                    const f32x4 cP1 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0 + 4);
+#pragma unroll
+                    for (int m = 0; m < RPT; ++m) {
+                        const int t = t0 + m;
+                        const float cm = m < 4 ? cM0[m & 3] : cM1[m & 3], cp = m < 4 ? cP0[m & 3] : cP1[m & 3];
+                        am[m] += (u <= t ? rM[m][uu] : 0.f) * kb;
+                        ap[m] += (u <= t ? rP[m][uu] : 0.f) * kb;
+                        ak[m] += u >= t ? cm * eh + cp * qh : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const float up = __expf(Gt[m] - sG[(16 * Tb + 15) * LC + il]);
+                const float dn = __expf(sG[16 * Tb * LC + il] - Gt[m]);
+                dEm[m] += up * am[m];
+                dqp[m] += up * ap[m];
+                dkm[m] += dn * ak[m];
+            }
         }
         // as the later token: blocks S < Tb
         for (int S = 0; S < Tb; ++S) {
@@ -1189,9 +1247,6 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         const f32x4 dEt = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
         const f32x4 dQt = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
         const f32x4 dKh = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
-        const f32x4 Kh = *reinterpret_cast<const f32x4*>(ws + a.L.Kh + x);
-        const f32x4 Et = *reinterpret_cast<const f32x4*>(ws + a.L.Et + x);
-        const f32x4 Qt = *reinterpret_cast<const f32x4*>(ws + a.L.Qt + x);
         const f32x4 dU = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
         // raw rows (LDS may hold the re-referenced ones): e from the
         // workspace, k and q from the inputs (normalised under the prologue)
@@ -1209,15 +1264,17 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         f32x4 dq, dk, dE;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float G = sG[l + j], eg = expf(G);
-            float dG = ev[j] * sEm[l + j] + qr[j] * sQp[l + j] - kr[j] * sKm[l + j] + dEt[j] * Et[j] +
-                       dQt[j] * Qt[j] - dKh[j] * Kh[j];
+            // E~ = E e^G, Q~ = q e^G, K^ = k e^{G_L - G}, recomputed exactly as
+            // bwd_prep forms them
+            const float G = sG[l + j], eg = expf(G), kd = expf(sG[(C - 1) * LC + c + j] - G);
+            float dG = ev[j] * sEm[l + j] + qr[j] * sQp[l + j] - kr[j] * sKm[l + j] + dEt[j] * (ev[j] * eg) +
+                       dQt[j] * (qr[j] * eg) - dKh[j] * (kr[j] * kd);
             if (t == rc.L - 1)
                 dG += sGL[c + j];
             sdG[l + j] = dG;
             dE[j] = sEm[l + j] + dEt[j] * eg;
             dq[j] = sQp[l + j] + dQt[j] * eg;
-            dk[j] = sKm[l + j] + dKh[j] * expf(sG[(C - 1) * LC + c + j] - G);
+            dk[j] = sKm[l + j] + dKh[j] * kd;
         }
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i0 + c;

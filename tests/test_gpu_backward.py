@@ -97,6 +97,21 @@ def test_backward_with_growth(dtype, D):
     _compare(f"growth_{dtype}", got, _oracle_backward(inp), TOL[dtype])
 
 
+@pytest.mark.parametrize("g_const", [-3.5, -5.0])
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_backward_steep_decay(dtype, D, g_const):
+    """A constant log-decay of -3.5 (a 16-token block spans 52.5 < 60 nats:
+    the decay kernel's diagonal blocks go through block-referenced rows with
+    factors up to e^52) and of -5 (75 nats: they take the pair-by-pair
+    pass)."""
+    wl = Workload("steep", "forward", 1, 100, 2, D, dtype, "full", 0.05, 64, 604, g_const=g_const)
+    inp = draw(wl)
+    inp.update(draw_cotangents(wl, 1.0))
+    got = _gpu_backward(to_dev(inp))
+    torch.cuda.synchronize()
+    _compare(f"steep_{dtype}_{g_const}", got, _oracle_backward(inp), TOL[dtype])
+
+
 def test_state_gradient_only():
     """dO = 0: every gradient flows from dS_final through the chunk-level
     recurrence alone.  The decay is weakened (g scaled by 0.02) so that dS0
