@@ -21,8 +21,8 @@
 // Kernels (all fp32 arithmetic; intermediates in a fp32 workspace, one
 // record per (sequence, head, chunk)):
 //   bwd_prep   one workgroup per chunk: G, E, U, E~, Q~, K^, gamma; M and P
-//              (pair by pair inside 16-token blocks, through block-referenced
-//              factors <= 1 across them); X by blocks; W, U~.
+//              as 16x16 blocks through block-referenced rows (fp32 MFMA);
+//              X by blocks; W, U~ (fp32 MFMA).
 //   bwd_dout   dO rows of every chunk into the workspace (zero past T).
 //   bwd_frag   the scan's operands in MFMA fragment order.
 //   bwd_scan   per (sequence, head, 64 value columns): the state gradient
@@ -134,24 +134,27 @@ __device__ __forceinline__ Rec rec_of(int64_t r, int64_t NC, int64_t T, int64_t 
 // bwd_prep: one workgroup (NTP threads) per chunk record.
 //   1. raw rows into LDS, 4 channels per item; G = cumulative log-decay;
 //      E~, Q~, K^, gamma, E, U written out (fp32)
-//   2. M (strictly lower) and P (lower) pair by pair: the 4x4 token block
-//      (tb, sb), sb <= tb, is owned by two threads, one per half of the
-//      channels; the halves' partial sums meet in LDS.  Every factor is
-//      exp(G_t - G_s) for s <= t (no overflow for decays)
+//   2. M (strictly lower) and P (lower) by 16x16 token blocks on fp32 MFMA,
+//      through rows re-referenced to their block (every factor <= 1 below
+//      the diagonal, <= e^kDiagSpan on it); steeper diagonal blocks pair by
+//      pair, and every pair by its own exponential under growth
 //   3. X = (I + M)^-1 by 16x16 blocks: diagonal blocks by substitution, the
 //      rest by X_ij = -X_ii sum_{k=j}^{i-1} M_ik X_kj, one block diagonal at
 //      a time
-//   4. W = X E~, U~ = X U, register-blocked (2 tokens x D/16 channels per
-//      thread)
+//   4. W = X E~, U~ = X U as 16x16 fp32 MFMA tiles, one wave per tile
 // ---------------------------------------------------------------------------
 constexpr int NTP = 512;         // threads of the prep kernel
+// Largest decay span (natural log units) over one 16-token block for which
+// the pairs inside the block go through block-referenced rows: every factor
+// then stays within e^{+-kDiagSpan}, far inside fp32's range.
+constexpr float kDiagSpan = 60.f;
 
 template <int D>
 struct BwdPrepShape {
     static constexpr int C = BC, LD = D + 4, LDM = C + 4;
     static constexpr int OFF_G = 0, OFF_E = C * LD, OFF_K = 2 * C * LD, OFF_Q = 3 * C * LD, OFF_M = 4 * C * LD;
-    static constexpr int OFF_CF = OFF_M + C * LDM;           // cross-block decay factors [6][D]
-    static constexpr int FLOATS = OFF_CF + 6 * D;
+    static constexpr int OFF_CF = OFF_M + C * LDM;           // block-pair decay factors [10][D]
+    static constexpr int FLOATS = OFF_CF + 10 * D;
     static constexpr size_t SMEM = (size_t)FLOATS * 4;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert(C * LDM <= C * LD && 3 * 256 <= C * LD && C * C <= C * LD,
@@ -207,7 +210,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 {
     typedef BwdPrepShape<D> PS;
-    constexpr int C = BC, LD = PS::LD, LDM = PS::LDM, CPT = D / 16, Q4 = D / 4;
+    constexpr int C = BC, LD = PS::LD, LDM = PS::LDM, Q4 = D / 4;
     extern __shared__ __align__(16) float sm[];
     float* sG = sm + PS::OFF_G;     // [C][LD] cumulative log-decay (natural units)
     float* sE = sm + PS::OFF_E;     // [C][LD] e = b*k, later E~
@@ -307,13 +310,21 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 
     // 2. M (strictly lower) and P (lower).
     if (!growth) {
-        // Decays only: 2a the diagonal 16x16 blocks pair by pair; 2b the
-        // rows re-referenced to their block in place,
-        //   E^ = e e^{G - G_16T},  Q^ = q e^{G - G_16T},  K- = k e^{G_16T+15 - G},
-        // and c_TS = e^{G_16T - G_16S+15} for S < T (every factor <= 1);
-        // 2c the blocks below the diagonal as M_TS = (E^_T c_TS) K-_S^T.
+        // Decays only.  The rows are re-referenced to their 16-token block in
+        // place,  E^ = e e^{G - G_16T},  Q^ = q e^{G - G_16T},  K- = k e^{G_16T+15 - G},
+        // so the block (T, S), S <= T, is  M_TS = (E^_T c_TS) K-_S^T  (and P
+        // with Q^), c_TS = e^{G_16T - G_16S+15}: <= 1 below the diagonal,
+        // e^{span of block T} on it.  A block whose span exceeds kDiagSpan in
+        // some channel sends the diagonal blocks pair by pair (2a) instead.
         float* sCf = sm + PS::OFF_CF;
-        for (int e = tid; e < 4 * 136; e += NTP) {
+        int steep = 0;
+        for (int e = tid; e < (C / 16) * D; e += NTP) {
+            const int T = e / D, i = e % D;
+            steep |= sG[16 * T * LD + i] - sG[(16 * T + 15) * LD + i] > kDiagSpan;
+        }
+        steep = __syncthreads_or(steep);
+        // 2a. (steep) the diagonal 16x16 blocks pair by pair, from the raw rows
+        for (int e = steep ? tid : 4 * 136; e < 4 * 136; e += NTP) {
             const int blk = e / 136, pr = e % 136;
             int rr = 0;
             while ((rr + 1) * (rr + 2) / 2 <= pr)
@@ -333,6 +344,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             }
         }
         __syncthreads();
+        // 2b. re-referenced rows, and c_TS (pairs 0..5 below the diagonal in
+        // the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); 6 + T on it)
         for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
             const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i, T = t / 16;
             const f32x4 G = ld4s(sG + l), G0 = ld4s(sG + 16 * T * LD + i), G1 = ld4s(sG + (16 * T + 15) * LD + i);
@@ -346,33 +359,41 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             st4s(sQ + l, ld4s(sQ + l) * fa);
             st4s(sK + l, ld4s(sK + l) * fb);
         }
-        for (int e = tid; e < 6 * D; e += NTP) {
+        for (int e = tid; e < 10 * D; e += NTP) {
             const int pi = e / D, i = e % D;
-            const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
+            const int T = pi < 1 ? 1 : pi < 3 ? 2 : pi < 6 ? 3 : pi - 6;
+            const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
             sCf[e] = __expf(sG[16 * T * LD + i] - sG[(16 * S + 15) * LD + i]);
         }
         __syncthreads();
-        for (int e = tid; e < 6 * 64; e += NTP) {
-            const int pi = e / 64, rr = (e / 4) % 16, cg = e % 4;
-            const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
-            const int t = 16 * T + rr, s0 = 16 * S + 4 * cg;
-            const float* cf = sCf + pi * D;
-            float m[4] = {}, p[4] = {};
-            for (int i = 0; i < D; ++i) {
-                const float c = cf[i], am = sE[t * LD + i] * c, ap = sQ[t * LD + i] * c;
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const float kb = sK[(s0 + y) * LD + i];
-                    m[y] += am * kb;
-                    p[y] += ap * kb;
+        // 2c. the block products on fp32 MFMA, one wave per block pair (M and
+        // P share the K- fragments); each wave also clears the mirrored block
+        // above the diagonal
+        {
+            typedef Mma<float> MF;
+            const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+            for (int pi = wave; pi < (steep ? 6 : 10); pi += NTP / 64) {
+                const int T = pi < 1 ? 1 : pi < 3 ? 2 : pi < 6 ? 3 : pi - 6;
+                const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
+                const float* cf = sCf + pi * D;
+                f32x4 m = {0.f, 0.f, 0.f, 0.f}, p = m;
+#pragma unroll 4
+                for (int k0 = 0; k0 < D; k0 += MF::KB) {
+                    const MF::Frag kb = MF::load(sK + 16 * S * LD + k0, LD, lane);
+                    m = MF::mma(MF::load_scaled(sE + 16 * T * LD + k0, LD, cf + k0, lane), kb, m);
+                    p = MF::mma(MF::load_scaled(sQ + 16 * T * LD + k0, LD, cf + k0, lane), kb, p);
                 }
-            }
 #pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                sM[t * LDM + s0 + y] = m[y];
-                ws[a.L.P + cco + t * C + s0 + y] = p[y];
-                sM[(s0 + y) * LDM + t] = 0.f;
-                ws[a.L.P + cco + (s0 + y) * C + t] = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * T + 4 * gq + i, s_ = 16 * S + cl;
+                    sM[t * LDM + s_] = s_ < t ? m[i] : 0.f;
+                    ws[a.L.P + cco + t * C + s_] = s_ <= t ? p[i] : 0.f;
+                    if (S < T) {
+                        const int ta = 16 * S + 4 * gq + i, sa = 16 * T + cl;   // the block (S, T)
+                        sM[ta * LDM + sa] = 0.f;
+                        ws[a.L.P + cco + ta * C + sa] = 0.f;
+                    }
+                }
             }
         }
         __syncthreads();
@@ -480,30 +501,24 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     }
     __syncthreads();
     {
-        const int tr = tid / 16, cg = tid % 16, r0 = 2 * tr, c0 = CPT * cg;
-        float wv[2][CPT] = {}, uv[2][CPT] = {};
-        for (int s_ = 0; s_ <= r0 + 1; ++s_) {
-            const float x0 = sX[r0 * LDM + s_], x1 = sX[(r0 + 1) * LDM + s_];
+        // 16x16 output tiles on fp32 MFMA, one wave per tile: A = rows of X
+        // (lower triangular, so tile row T needs k-tiles 0..T), B = the
+        // columns of E~ or u
+        typedef Mma<float> MF;
+        const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+        constexpr int NTD = D / 16, NPER = (C / 16) * NTD;
+        for (int tile = wave; tile < 2 * NPER; tile += NTP / 64) {
+            const int which = tile / NPER, T = (tile % NPER) / NTD, c = tile % NTD;
+            const float* src = which == 0 ? sE : sU;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk <= T; ++kk)
+                acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
+                              MF::load_kn(src + 16 * kk * LD + 16 * c, LD, lane), acc);
+            float* dst = ws + (which == 0 ? a.L.W : a.L.Ut) + cdo + (size_t)(16 * T + 4 * gq) * D + 16 * c + cl;
 #pragma unroll
-            for (int c = 0; c < CPT; c += 4) {
-                const f32x4 e4 = ld4s(sE + s_ * LD + c0 + c), u4 = ld4s(sU + s_ * LD + c0 + c);
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    wv[0][c + y] += x0 * e4[y];
-                    wv[1][c + y] += x1 * e4[y];
-                    uv[0][c + y] += x0 * u4[y];
-                    uv[1][c + y] += x1 * u4[y];
-                }
-            }
+            for (int i = 0; i < 4; ++i)
+                dst[(size_t)i * D] = acc[i];
         }
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int c = 0; c < CPT; c += 4) {
-                const size_t o = cdo + (size_t)(r0 + x) * D + c0 + c;
-                st4s(ws + a.L.W + o, f32x4{wv[x][c], wv[x][c + 1], wv[x][c + 2], wv[x][c + 3]});
-                st4s(ws + a.L.Ut + o, f32x4{uv[x][c], uv[x][c + 1], uv[x][c + 2], uv[x][c + 3]});
-            }
     }
 }
 
@@ -958,10 +973,6 @@ __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
 // (dM is strictly lower, so the u == t terms of dM vanish.)
 // ---------------------------------------------------------------------------
 constexpr int DC = 32;                 // channels per decay workgroup
-// Largest decay span (natural log units) over one 16-token block for which
-// the diagonal block's pairs go through the block-referenced rows: every
-// factor then stays within e^{+-kDiagSpan}, far inside fp32's range.
-constexpr float kDiagSpan = 60.f;
 constexpr int LC = DC + 1;             // padded LDS row of the per-channel arrays
 constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte aligned)
 
