@@ -161,6 +161,27 @@ struct BwdPrepShape {
                   "X fits in the q area; the block products and the partial P in the k area");
 };
 
+// s_barrier once this wave's LDS accesses have completed.  Unlike
+// __syncthreads() it does not wait for the wave's outstanding global stores,
+// so a workgroup that only exchanges data through LDS lets them drain.
+__device__ __forceinline__ void lds_barrier() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup-wide OR of v through one LDS word per wave (slots[NW], used by
+// one call site only), with lds_barrier.
+template <int NW>
+__device__ __forceinline__ int lds_barrier_or(int v, int* slots)
+{
+    const int any = __ballot(v) != 0;
+    if ((threadIdx.x & 63) == 0)
+        slots[threadIdx.x >> 6] = any;
+    lds_barrier();
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        r |= slots[w];
+    return r;
+}
+
 // Y_ij (16x16, into sY) = sum_{k=j}^{i-1} M_ik X_kj  for the blocks (i, i-d)
 // of block diagonal d; then X_ij = -X_ii Y_ij.
 __device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float* sY, int d, int tid)
@@ -175,7 +196,7 @@ __device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float*
                 acc += sM[(16 * i + rr) * LDM + 16 * kb + c] * sX[(16 * kb + c) * LDM + 16 * j + cc];
         sY[e] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < nblk * 256; e += NTP) {
         const int bi = e / 256, rr = (e / 16) % 16, cc = e % 16, i = bi + d, j = bi;
         float acc = 0.f;
@@ -183,10 +204,11 @@ __device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float*
             acc += sX[(16 * i + rr) * LDM + 16 * i + c] * sY[bi * 256 + c * 16 + cc];
         sX[(16 * i + rr) * LDM + 16 * j + cc] = -acc;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 __device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
 
 // Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
 __device__ __forceinline__ float bsigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
@@ -217,6 +239,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     float* sK = sm + PS::OFF_K;     // [C][LD] k, later partial P, block products and u
     float* sQ = sm + PS::OFF_Q;     // [C][LD] q, later X [C][LDM]
     float* sM = sm + PS::OFF_M;     // [C][LDM] M
+    __shared__ int sOr[2 * (NTP / 64)];
     const int64_t r = blockIdx.x;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
     const int tid = threadIdx.x;
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         st4s(ws + a.L.E + x, ev);
         st4s(ws + a.L.U + x, uv);
     }
-    growth = __syncthreads_or(growth);
+    growth = lds_barrier_or<NTP / 64>(growth, sOr);
     for (int i = tid; i < D; i += NTP) {
         float acc = 0.f;
         for (int t = 0; t < C; ++t) {
@@ -284,7 +307,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             sG[t * LD + i] = acc;
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
         const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
         const size_t x = cdo + (size_t)t * D + i;
@@ -322,7 +345,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             const int T = e / D, i = e % D;
             steep |= sG[16 * T * LD + i] - sG[(16 * T + 15) * LD + i] > kDiagSpan;
         }
-        steep = __syncthreads_or(steep);
+        steep = lds_barrier_or<NTP / 64>(steep, sOr + NTP / 64);
         // 2a. (steep) the diagonal 16x16 blocks pair by pair, from the raw rows
         for (int e = steep ? tid : 4 * 136; e < 4 * 136; e += NTP) {
             const int blk = e / 136, pr = e % 136;
@@ -343,7 +366,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 ws[a.L.P + cco + s_ * C + t] = 0.f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // 2b. re-referenced rows, and c_TS (pairs 0..5 below the diagonal in
         // the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); 6 + T on it)
         for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
@@ -365,7 +388,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
             sCf[e] = __expf(sG[16 * T * LD + i] - sG[(16 * S + 15) * LD + i]);
         }
-        __syncthreads();
+        lds_barrier();
         // 2c. the block products on fp32 MFMA, one wave per block pair (M and
         // P share the K- fragments); each wave also clears the mirrored block
         // above the diagonal
@@ -396,7 +419,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     } else {
         // Some log-decay > 0 (growth): factors could exceed 1, so every
         // pair takes its own exponential.  4x4 token blocks on and below the
@@ -428,7 +451,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     }
             }
         }
-        __syncthreads();                  // q and k rows are no longer read
+        lds_barrier();                  // q and k rows are no longer read
         float* sPp = sK;                  // [C][C] partial P of the second half
         if (tid >= 136 && tid < 272) {
     #pragma unroll
@@ -439,7 +462,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     sPp[(t0 + x) * C + s0 + y] = p[x][y];
                 }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < 136) {
     #pragma unroll
             for (int x = 0; x < 4; ++x)
@@ -460,7 +483,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
     }
 
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     float* sY = sK;
     for (int e = tid; e < C * C; e += NTP)
         sX[(e / C) * LDM + e % C] = 0.f;
-    __syncthreads();
+    lds_barrier();
     if (tid < C) {
         const int bk = tid / 16, j = tid % 16, o = 16 * bk;
         for (int rr = j; rr < 16; ++rr) {
@@ -480,7 +503,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             sX[(o + rr) * LDM + o + j] = acc;
         }
     }
-    __syncthreads();
+    lds_barrier();
     xinv_diagonal(sM, sX, sY, 1, tid);
     xinv_diagonal(sM, sX, sY, 2, tid);
     xinv_diagonal(sM, sX, sY, 3, tid);
@@ -491,7 +514,10 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     float* sU = sK;
     for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
         const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        f32x4 ev = ld4s(ws + a.L.E + cdo + (size_t)t * D + i);   // sE holds the re-referenced rows
+        // sE holds the re-referenced rows; each thread re-reads the E and u
+        // elements it wrote itself in step 1 (same item mapping), so no
+        // barrier has to wait for those stores
+        f32x4 ev = ld4s(ws + a.L.E + cdo + (size_t)t * D + i);
         const f32x4 G = ld4s(sG + l);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -499,7 +525,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         st4s(sE + l, ev);
         st4s(sU + l, ld4s(ws + a.L.U + cdo + (size_t)t * D + i));
     }
-    __syncthreads();
+    lds_barrier();
     {
         // 16x16 output tiles on fp32 MFMA, one wave per tile: A = rows of X
         // (lower triangular, so tile row T needs k-tiles 0..T), B = the
@@ -990,6 +1016,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     float* sQ = sK + C * LC;        // [C][LC] q
     float* sdG = sQ + C * LC;       // [C][LC] dG, then dg
     float* sGL = sdG + C * LC;      // [DC] dG_L
+    __shared__ int sOr[2 * (NTB / 64)];
     const int64_t r = blockIdx.x / (D / DC);
     const int i0 = (int)(blockIdx.x % (D / DC)) * DC;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
@@ -1030,7 +1057,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
         *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
     }
-    __syncthreads();
+    lds_barrier();
     // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam) and
     // K^ = k e^{G_L - G} recomputed from the rows in LDS: every thread sums
     // its share (D / NRG state columns, RPT tokens) of its channel, then the
@@ -1054,7 +1081,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
         sdG[rg * LC + il] = acc;        // sdG is free until the main loop
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < DC) {
         float acc = 0.f;
 #pragma unroll
@@ -1070,7 +1097,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         const int t = e / DC + 1, c = e % DC;
         grow |= sG[t * LC + c] > sG[(t - 1) * LC + c];
     }
-    grow = __syncthreads_or(grow);
+    grow = lds_barrier_or<NTB / 64>(grow, sOr);
 
     // a 16-token block whose decay spans more than kDiagSpan in some channel:
     // the diagonal blocks take the pair-by-pair pass below
@@ -1079,7 +1106,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         const int T = e / DC, c = e % DC;
         steep |= sG[16 * T * LC + c] - sG[(16 * T + 15) * LC + c] > kDiagSpan;
     }
-    steep = __syncthreads_or(steep);
+    steep = lds_barrier_or<NTB / 64>(steep, sOr + NTB / 64);
     const bool pairwise = grow || steep;
 
     float Gt[RPT], dEm[RPT], dqp[RPT], dkm[RPT];
@@ -1128,7 +1155,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         // Q^ = q e^{G - G_16T}, K- = k e^{G_16S+15 - G}); the epilogue reads
         // the raw rows again from memory.
         float* sCf = sdG;                // [6][DC] c_TS; sdG is not needed until the epilogue
-        __syncthreads();                 // the pass above is done with the raw rows
+        lds_barrier();                 // the pass above is done with the raw rows
         for (int e = tid; e < C * DC; e += NTB) {
             const int t = e / DC, c = e % DC, l = t * LC + c, T = t / 16;
             const float G = sG[l];
@@ -1142,7 +1169,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
             sCf[e] = __expf(sG[16 * T * LC + c] - sG[(16 * S + 15) * LC + c]);
         }
-        __syncthreads();
+        lds_barrier();
         const int Tb = t0 / 16;          // the 16-token block of this thread's rows
         float fa[RPT], fb[RPT];
 #pragma unroll
@@ -1238,7 +1265,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
                 dkm[m] += fb[m] * c * ak[m];
         }
     }
-    __syncthreads();                     // sGL ready; dM and dP no longer read
+    lds_barrier();                     // sGL ready; dM and dP no longer read
     // the three sums into LDS (the dM / dP area), then the gradients with
     // four channels per item
     float* sEm = sdM;                    // [C][LC] dE_M
@@ -1251,7 +1278,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         sQp[l] = dqp[m];
         sKm[l] = dkm[m];
     }
-    __syncthreads();
+    lds_barrier();
     for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
         const int t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
         const size_t x = cdo + (size_t)t * D + i0 + c;
@@ -1313,7 +1340,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
                 *reinterpret_cast<f32x4*>(a.dw + off) = dwv;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dg: reverse cumulative sum over the chunk, per channel
     if (tid < DC) {
         float acc = 0.f;
@@ -1322,7 +1349,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             sdG[t * LC + tid] = acc;
         }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int t = t0 + m;
