@@ -151,7 +151,7 @@ def bench_gate_widths(torch, gdr2, lib, d, steps: int):
         args = (x["q"], x["k"], x["v"], b, w, g)
         ws = torch.empty(gdr2.workspace_size(*args, chunk=64), dtype=torch.uint8, device="cuda")
         a = gdr2.fwd_args(*args, S0=d["S0"], o=o, S_out=S_out, chunk=64, workspace=ws)
-        for _ in range(3):
+        for _ in range(20):       # each mix warms up on its own workspace (3 calls read ~10% slow)
             lib.gdr2_forward_chunked(ctypes.byref(a), stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -180,7 +180,7 @@ def bench_prologue(torch, gdr2, lib, d, steps: int):
     res = {}
     for name, bits in (("plain", 0), ("prologue_all", gdr2.PROLOGUE_NORM_QK | gdr2.PROLOGUE_GATES)):
         a = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=64, workspace=ws, prologue=bits)
-        for _ in range(3):
+        for _ in range(20):
             lib.gdr2_forward_chunked(ctypes.byref(a), stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
