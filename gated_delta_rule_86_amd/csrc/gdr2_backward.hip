@@ -962,6 +962,162 @@ __global__ __launch_bounds__(NTB) void bwd_sgrad_kernel(BwdArgs a)
     gemm_tile<Mma<E>>(sA, sB, 0, 0, D, dO, Delt, 0, none, none, ws + a.L.dP + cc, C, 1.f, 0.f, nullptr, 1);
 }
 
+// bf16 inputs: the same state products with every operand read from memory
+// once (the tile version above re-reads S, W, dO and Delta from memory for
+// each product, since a chunk's operands do not stay in cache).  CG waves per
+// 16 token rows: wave w owns the rows 16 (w % 4).. and a 1/CG share of the
+// output columns of every product; its row operands W, dO and dDelta come straight from memory
+// as A fragments; S (as S and S^T), Lam and Delta are staged in LDS in bf16,
+// the precision of every MFMA operand here.  Delta never leaves the
+// workgroup.
+template <int D>
+struct SgradShape {
+    static constexpr int C = BC, LDB = D + 8;   // bf16 rows padded by 16 bytes: conflict-free fragment reads
+    static constexpr size_t S_OFF = 0, ST_OFF = S_OFF + (size_t)D * LDB, L_OFF = ST_OFF + (size_t)D * LDB,
+                            DEL_OFF = L_OFF + (size_t)D * LDB, ELEMS = DEL_OFF + (size_t)C * LDB;
+    static constexpr size_t SMEM = ELEMS * 2;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static constexpr int CG = 2;                     // waves (column groups) per 16 token rows
+    static constexpr int NTH = CG * 64 * (C / 16);   // threads
+    static_assert((D / 16) % CG == 0 && (C / 16) % CG == 0, "whole tiles per column group");
+};
+
+template <int D>
+__global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdArgs a)
+{
+    typedef SgradShape<D> SH;
+    typedef Mma<bf16> MM;
+    typedef MM::Frag Frag;
+    constexpr int C = BC, LDB = SH::LDB, NKS = D / MM::KB, NT = D / 16, NTH = SH::NTH, NH = NT / SH::CG;
+    extern __shared__ __align__(16) bf16 sb[];
+    bf16* sS = sb + SH::S_OFF;       // S[i][j]
+    bf16* sSt = sb + SH::ST_OFF;     // S^T[j][i]
+    bf16* sL = sb + SH::L_OFF;       // Lam[i][j]
+    bf16* sDel = sb + SH::DEL_OFF;   // Delta[t][j]
+    const int64_t r = blockIdx.x;
+    float* ws = a.ws;
+    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C, dd = (size_t)r * D * D;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int rw = wave & 3, t0 = 16 * rw, n0 = (wave >> 2) * NH;   // row block; first of its NH column tiles
+
+    const float* S = a.S_chunks + dd;
+    const float* Lam = ws + a.L.Lam + dd;
+    for (int e = tid; e < D * D / 4; e += NTH) {
+        const int i = e / (D / 4), j = 4 * (e % (D / 4));
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
+        bf16x4 sv, lv;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            sv[x] = (bf16)s4[x];
+            lv[x] = (bf16)l4[x];
+            sSt[(j + x) * LDB + i] = sv[x];
+        }
+        *reinterpret_cast<bf16x4*>(sS + i * LDB + j) = sv;
+        *reinterpret_cast<bf16x4*>(sL + i * LDB + j) = lv;
+    }
+    __syncthreads();
+
+    const float* W = ws + a.L.W + cd + (size_t)t0 * D;
+    const float* dO = ws + a.L.dO + cd + (size_t)t0 * D;
+    const float* dDel = ws + a.L.dDel + cd + (size_t)t0 * D;
+    const size_t orow = cd + (size_t)(t0 + 4 * gq) * D + cl;   // output element (row 4gq, column cl) of the wave
+
+    // Delta = U~ - W S   (k = i: B fragments from S^T)
+    {
+        f32x4 p[NH];
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+            p[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const Frag aw = MM::load(W + ks * MM::KB, D, lane);
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt)
+                p[nt] = MM::mma(aw, MM::load(sSt + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), p[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float dl = ws[a.L.Ut + orow + (size_t)x * D + 16 * (n0 + nt)] - p[nt][x];
+                sDel[(t0 + 4 * gq + x) * LDB + 16 * (n0 + nt) + cl] = (bf16)dl;
+            }
+    }
+    // dQ~ = dO S^T,  dW = -dDelta S^T   (k = j: B fragments from S)
+    {
+        f32x4 q[NH], w[NH];
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+            q[nt] = w[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const Frag ao = MM::load(dO + ks * MM::KB, D, lane), ad = MM::load(dDel + ks * MM::KB, D, lane);
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt) {
+                const Frag bs = MM::load(sS + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane);
+                q[nt] = MM::mma(ao, bs, q[nt]);
+                w[nt] = MM::mma(ad, bs, w[nt]);
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                ws[a.L.dQt + orow + (size_t)x * D + 16 * (n0 + nt)] = q[nt][x];
+                ws[a.L.dW + orow + (size_t)x * D + 16 * (n0 + nt)] = -w[nt][x];
+            }
+    }
+    __syncthreads();                 // every wave's Delta rows are in LDS
+    // dK^ = Delta Lam^T   (A: this wave's Delta rows; k = j: B fragments from Lam)
+    {
+        f32x4 k[NH];
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+            k[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const Frag ad = MM::load(sDel + t0 * LDB + ks * MM::KB, LDB, lane);
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt)
+                k[nt] = MM::mma(ad, MM::load(sL + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), k[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                ws[a.L.dKh + orow + (size_t)x * D + 16 * (n0 + nt)] = k[nt][x];
+    }
+    // dP = tril(dO Delta^T)   (k = j: B fragments from the Delta rows s);
+    // blocks above the diagonal are zero
+    {
+        constexpr int SBH = C / 16 / SH::CG;   // token blocks per column group
+        const int s0 = (wave >> 2) * SBH;
+        f32x4 pp[SBH];
+#pragma unroll
+        for (int sbk = 0; sbk < SBH; ++sbk)
+            pp[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s0 <= rw) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const Frag ao = MM::load(dO + ks * MM::KB, D, lane);
+#pragma unroll
+                for (int sbk = 0; sbk < SBH; ++sbk)
+                    if (s0 + sbk <= rw)
+                        pp[sbk] = MM::mma(ao, MM::load(sDel + 16 * (s0 + sbk) * LDB + ks * MM::KB, LDB, lane),
+                                          pp[sbk]);
+            }
+        }
+#pragma unroll
+        for (int sbk = 0; sbk < SBH; ++sbk)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int t = t0 + 4 * gq + x, s_ = 16 * (s0 + sbk) + cl;
+                ws[a.L.dP + cc + (size_t)t * C + s_] = s_ <= t ? pp[sbk][x] : 0.f;
+            }
+    }
+}
+
 // The products through the WY factor X = (I + M)^-1, one workgroup per
 // chunk record:  dX = dDelta U^T + dW E~^T,  dM = strict_tril(-X^T dX X^T),
 // dU = X^T dDelta,  dE~ = X^T dW.
@@ -1444,6 +1600,12 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
         (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_decay_kernel<E, D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_decay)) != hipSuccess)
         return e;
+    if constexpr (sizeof(E) == 2) {
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_sgrad_bf16_kernel<D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)SgradShape<D>::SMEM)) !=
+            hipSuccess)
+            return e;
+    }
 
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)nrec), dim3(NTP), lds_prep, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1457,7 +1619,12 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    hipLaunchKernelGGL((bwd_sgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    if constexpr (sizeof(E) == 2) {
+        hipLaunchKernelGGL((bwd_sgrad_bf16_kernel<D>), dim3((unsigned)nrec), dim3(SgradShape<D>::NTH),
+                           SgradShape<D>::SMEM, s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_sgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_xgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
