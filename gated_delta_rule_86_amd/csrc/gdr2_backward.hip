@@ -973,9 +973,10 @@ __global__ __launch_bounds__(NTB) void bwd_sgrad_kernel(BwdArgs a)
 template <int D>
 struct SgradShape {
     static constexpr int C = BC, LDB = D + 8;   // bf16 rows padded by 16 bytes: conflict-free fragment reads
+    static constexpr int LDG = D / 4 + 1;         // fp32 row of the dgamma partial sums
     static constexpr size_t S_OFF = 0, ST_OFF = S_OFF + (size_t)D * LDB, L_OFF = ST_OFF + (size_t)D * LDB,
                             DEL_OFF = L_OFF + (size_t)D * LDB, ELEMS = DEL_OFF + (size_t)C * LDB;
-    static constexpr size_t SMEM = ELEMS * 2;
+    static constexpr size_t SMEM = ELEMS * 2 + (size_t)D * LDG * 4;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static constexpr int CG = 2;                     // waves (column groups) per 16 token rows
     static constexpr int NTH = CG * 64 * (C / 16);   // threads
@@ -994,6 +995,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     bf16* sSt = sb + SH::ST_OFF;     // S^T[j][i]
     bf16* sL = sb + SH::L_OFF;       // Lam[i][j]
     bf16* sDel = sb + SH::DEL_OFF;   // Delta[t][j]
+    float* sPg = reinterpret_cast<float*>(sb + SH::ELEMS);   // [D][LDG] partial sums of dgamma
     const int64_t r = blockIdx.x;
     float* ws = a.ws;
     const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C, dd = (size_t)r * D * D;
@@ -1002,6 +1004,10 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
 
     const float* S = a.S_chunks + dd;
     const float* Lam = ws + a.L.Lam + dd;
+    // staging also forms dgamma_i = sum_j S[i][j] Lam[i][j] in fp32 (partial
+    // sums of 4 through LDS); gamma becomes gamma * dgamma, the chunk-end term
+    // of dG_L that bwd_decay adds (the scan has used gamma)
+    const float gam_i = tid < D ? ws[a.L.gam + (size_t)r * D + tid] : 0.f;
     for (int e = tid; e < D * D / 4; e += NTH) {
         const int i = e / (D / 4), j = 4 * (e % (D / 4));
         const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
@@ -1015,8 +1021,16 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         }
         *reinterpret_cast<bf16x4*>(sS + i * LDB + j) = sv;
         *reinterpret_cast<bf16x4*>(sL + i * LDB + j) = lv;
+        sPg[i * SH::LDG + j / 4] = s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
     }
     __syncthreads();
+    if (tid < D) {
+        float dg = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < D / 4; ++c)
+            dg += sPg[tid * SH::LDG + c];
+        ws[a.L.gam + (size_t)r * D + tid] = gam_i * dg;
+    }
 
     const float* W = ws + a.L.W + cd + (size_t)t0 * D;
     const float* dO = ws + a.L.dO + cd + (size_t)t0 * D;
@@ -1188,7 +1202,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
         const int t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
         const size_t x = cdo + (size_t)t * D + i0 + c;
-        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
+        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv, ev = kv;
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H;
             kv = load4(k + row * D + i0 + c);
@@ -1197,9 +1211,13 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
                 kv = kv * ws[a.L.RN + (size_t)r * 2 * C + t];
                 qv = qv * ws[a.L.RN + (size_t)r * 2 * C + C + t];
             }
+            // e = b k, formed as bwd_prep forms it
+            f32x4 bv = gate4(b, a.bw, row, i0 + c);
+            if (a.pro & GDR2_PROLOGUE_GATES)
+                bv = bsigm4(bv);
+            ev = bv * kv;
         }
         const f32x4 gv = *reinterpret_cast<const f32x4*>(ws + a.L.G + x);
-        const f32x4 ev = *reinterpret_cast<const f32x4*>(ws + a.L.E + x);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             sG[l + j] = gv[j];
@@ -1219,16 +1237,21 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     // its share (D / NRG state columns, RPT tokens) of its channel, then the
     // NRG partial sums of a channel are added up
     {
-        constexpr int JPT = D / NRG;
-        const float* S = a.S_chunks + (size_t)r * D * D + (size_t)i * D + rg * JPT;
-        const float* Lam = ws + a.L.Lam + (size_t)r * D * D + (size_t)i * D + rg * JPT;
         float acc = 0.f;
+        if constexpr (sizeof(E) == 2) {
+            // bf16 inputs: bwd_sgrad_bf16 left gamma * dgamma in gam
+            acc = rg == 0 ? ws[a.L.gam + (size_t)r * D + i] : 0.f;
+        } else {
+            constexpr int JPT = D / NRG;
+            const float* S = a.S_chunks + (size_t)r * D * D + (size_t)i * D + rg * JPT;
+            const float* Lam = ws + a.L.Lam + (size_t)r * D * D + (size_t)i * D + rg * JPT;
 #pragma unroll
-        for (int j = 0; j < JPT; j += 4) {
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + j), l4 = *reinterpret_cast<const f32x4*>(Lam + j);
-            acc += s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
+            for (int j = 0; j < JPT; j += 4) {
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + j), l4 = *reinterpret_cast<const f32x4*>(Lam + j);
+                acc += s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
+            }
+            acc *= ws[a.L.gam + (size_t)r * D + i];
         }
-        acc *= ws[a.L.gam + (size_t)r * D + i];
         const float GL = sG[(C - 1) * LC + il];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
@@ -1442,10 +1465,9 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         const f32x4 dQt = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
         const f32x4 dKh = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
         const f32x4 dU = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
-        // raw rows (LDS may hold the re-referenced ones): e from the
-        // workspace, k and q from the inputs (normalised under the prologue)
-        const f32x4 ev = *reinterpret_cast<const f32x4*>(ws + a.L.E + x);
-        f32x4 kr = {0.f, 0.f, 0.f, 0.f}, qr = kr;
+        // raw rows (LDS may hold the re-referenced ones) from the inputs:
+        // k and q normalised and b activated under the prologue, e = b k
+        f32x4 kr = {0.f, 0.f, 0.f, 0.f}, qr = kr, bv = kr, bd = {1.f, 1.f, 1.f, 1.f};
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H;
             kr = load4(k + row * D + i0 + c);
@@ -1454,7 +1476,13 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
                 kr = kr * ws[a.L.RN + (size_t)r * 2 * C + t];
                 qr = qr * ws[a.L.RN + (size_t)r * 2 * C + C + t];
             }
+            bv = gate4(b, a.bw, row, i0 + c);
+            if (a.pro & GDR2_PROLOGUE_GATES) {
+                bv = bsigm4(bv);
+                bd = bv * (f32x4{1.f, 1.f, 1.f, 1.f} - bv);   // d(activation)/d(raw)
+            }
         }
+        const f32x4 ev = bv * kr;
         f32x4 dq, dk, dE;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1472,13 +1500,10 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i0 + c;
-            f32x4 bv = gate4(b, a.bw, row, i0 + c), wv = gate4(w, a.ww, row, i0 + c);
+            f32x4 wv = gate4(w, a.ww, row, i0 + c), wd = {1.f, 1.f, 1.f, 1.f};
             // prologue gates: the activated values, and d(activation)/d(raw)
-            f32x4 bd = {1.f, 1.f, 1.f, 1.f}, wd = bd;
             if (a.pro & GDR2_PROLOGUE_GATES) {
-                bv = bsigm4(bv);
                 wv = bsigm4(wv);
-                bd = bv * (f32x4{1.f, 1.f, 1.f, 1.f} - bv);
                 wd = wv * (f32x4{1.f, 1.f, 1.f, 1.f} - wv);
             }
             const f32x4 vv = load4(v + off), kv = kr;
