@@ -1177,6 +1177,7 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
 {
     constexpr int C = BC, NRG = NTB / DC, RPT = C / NRG;
     static_assert(RPT == 8, "two 16-byte reads cover a thread's tokens");
+    static_assert(NTB / 64 == C / 16, "one wave per 16-token block in the block sums");
     extern __shared__ __align__(16) float sm[];
     float* sdM = sm;                // [C][LPC]
     float* sdP = sdM + C * LPC;     // [C][LPC]
@@ -1326,15 +1327,23 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             }
         }
     }
+    // the three sums go to LDS (the dM / dP area) for the epilogue, which
+    // takes four channels per item
+    float* sEm = sdM;                    // [C][LC] dE_M
+    float* sQp = sEm + C * LC;           // [C][LC] dq_P
+    float* sKm = sQp + C * LC;           // [C][LC] dk_M + dk_P
     if (!grow) {
-        // Decays only: pairs in different 16-token blocks T > S through
-        // factors that are all <= 1 (per channel):
-        //   e^{G_t - G_s} = e^{G_t - G_16T} c_TS e^{G_16S+15 - G_s},  c_TS = e^{G_16T - G_16S+15}
-        // The rows are re-referenced in place (E^ = e e^{G - G_16T},
-        // Q^ = q e^{G - G_16T}, K- = k e^{G_16S+15 - G}); the epilogue reads
-        // the raw rows again from memory.
-        float* sCf = sdG;                // [6][DC] c_TS; sdG is not needed until the epilogue
-        lds_barrier();                 // the pass above is done with the raw rows
+        // Decays only.  The rows are re-referenced in place to their 16-token
+        // block,  E^ = e e^{G - G_16T},  Q^ = q e^{G - G_16T},  K- = k e^{G_16T+15 - G},
+        // so with c_TS = e^{G_16T - G_16S+15} (<= 1 below the diagonal,
+        // e^{span of block T} <= e^kDiagSpan on it), for blocks S <= T:
+        //   dE_M[t] = e^{G_t - G_16T} sum_S c_TS sum_{s in S} dM[t,s] K-_s     (dq_P with dP)
+        //   dk[s]   = e^{G_16S+15 - G_s} sum_T c_TS sum_{t in T} (dM[t,s] E^_t + dP[t,s] Q^_t)
+        // block by block on fp32 MFMA; wave w takes token block w, as the
+        // later token and as the earlier one.  Steep diagonal blocks came
+        // from the pass above.  The epilogue reads the raw rows again.
+        float* sCf = sdG;                // [10][DC] c_TS: the pairs S < T, then the diagonal
+        lds_barrier();                   // the pass above is done with the raw rows
         for (int e = tid; e < C * DC; e += NTB) {
             const int t = e / DC, c = e % DC, l = t * LC + c, T = t / 16;
             const float G = sG[l];
@@ -1343,119 +1352,80 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
             sQ[l] *= fa;
             sK[l] *= fb;
         }
-        for (int e = tid; e < 6 * DC; e += NTB) {
+        for (int e = tid; e < 10 * DC; e += NTB) {
             const int pi = e / DC, c = e % DC;
-            const int T = pi < 1 ? 1 : pi < 3 ? 2 : 3, S = pi - (T * (T - 1)) / 2;
+            const int T = pi < 1 ? 1 : pi < 3 ? 2 : pi < 6 ? 3 : pi - 6;
+            const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
             sCf[e] = __expf(sG[16 * T * LC + c] - sG[(16 * S + 15) * LC + c]);
         }
         lds_barrier();
-        const int Tb = t0 / 16;          // the 16-token block of this thread's rows
-        float fa[RPT], fb[RPT];
+        typedef Mma<float> MF;
+        constexpr int NCT = DC / 16;
+        const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 aE[NCT], aQ[NCT], aK[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            aE[ct] = aQ[ct] = aK[ct] = zero;
+        for (int S = 0; S <= wave; ++S) {            // as the later token (T = wave)
+            if (S == wave && steep)
+                continue;
+            const int pi = S < wave ? wave * (wave - 1) / 2 + S : 6 + wave;
+            const MF::Frag am = MF::load(sdM + 16 * wave * LPC + 16 * S, LPC, lane);
+            const MF::Frag ap = MF::load(sdP + 16 * wave * LPC + 16 * S, LPC, lane);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const MF::Frag kb = MF::load_kn(sK + 16 * S * LC + 16 * ct, LC, lane);
+                const float c = sCf[pi * DC + 16 * ct + cl];
+                aE[ct] += c * MF::mma(am, kb, zero);
+                aQ[ct] += c * MF::mma(ap, kb, zero);
+            }
+        }
+        for (int T = wave; T < C / 16; ++T) {        // as the earlier token (S = wave)
+            if (T == wave && steep)
+                continue;
+            const int pi = wave < T ? T * (T - 1) / 2 + wave : 6 + T;
+            // dM[t][s], dP[t][s] with s as the row: rows s of block S, k = t of block T
+            const MF::Frag am = MF::load_kn(sdM + 16 * T * LPC + 16 * wave, LPC, lane);
+            const MF::Frag ap = MF::load_kn(sdP + 16 * T * LPC + 16 * wave, LPC, lane);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 z = MF::mma(am, MF::load_kn(sE + 16 * T * LC + 16 * ct, LC, lane), zero);
+                z = MF::mma(ap, MF::load_kn(sQ + 16 * T * LC + 16 * ct, LC, lane), z);
+                aK[ct] += sCf[pi * DC + 16 * ct + cl] * z;
+            }
+        }
+        lds_barrier();                   // dM and dP no longer read
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int t = 16 * wave + 4 * gq + x, c = 16 * ct + cl, l = t * LC + c;
+                const float G = sG[l];
+                const float fa = __expf(G - sG[16 * wave * LC + c]), fb = __expf(sG[(16 * wave + 15) * LC + c] - G);
+                sEm[l] = fa * aE[ct][x];
+                sQp[l] = fa * aQ[ct][x];
+                sKm[l] = fb * aK[ct][x];
+            }
+        if (steep) {
+            lds_barrier();
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int l = (t0 + m) * LC + il;
+                sEm[l] += dEm[m];
+                sQp[l] += dqp[m];
+                sKm[l] += dkm[m];
+            }
+        }
+    } else {
+        lds_barrier();                   // dM and dP no longer read
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            fa[m] = __expf(Gt[m] - sG[16 * Tb * LC + il]);
-            fb[m] = __expf(sG[(16 * Tb + 15) * LC + il] - Gt[m]);
+            const int l = (t0 + m) * LC + il;
+            sEm[l] = dEm[m];
+            sQp[l] = dqp[m];
+            sKm[l] = dkm[m];
         }
-        if (!pairwise) {
-            // the diagonal block through the same rows (span <= kDiagSpan):
-            //   e^{G_t - G_s} = e^{G_t - G_16T+15} (k_s e^{G_16T+15 - G_s}) / k_s
-            //                 = e^{G_16T - G_s} (e_t e^{G_t - G_16T}) / e_t
-            // so the sums as the later token scale by e^{G_t - G_16T+15} >= 1
-            // and those as the earlier token by e^{G_16T - G_t} >= 1
-            float am[RPT] = {}, ap[RPT] = {}, ak[RPT] = {};
-            for (int u0 = 16 * Tb; u0 < 16 * Tb + 16; u0 += 4) {
-                f32x4 rM[RPT], rP[RPT];      // dM[t, u0..u0+3], dP[t, u0..u0+3]
-#pragma unroll
-                for (int m = 0; m < RPT; ++m) {
-                    rM[m] = *reinterpret_cast<const f32x4*>(sdM + (t0 + m) * LPC + u0);
-                    rP[m] = *reinterpret_cast<const f32x4*>(sdP + (t0 + m) * LPC + u0);
-                }
-#pragma unroll
-                for (int uu = 0; uu < 4; ++uu) {
-                    const int u = u0 + uu;
-                    const float kb = sK[u * LC + il], eh = sE[u * LC + il], qh = sQ[u * LC + il];
-                    const f32x4 cM0 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0);
-                    const f32x4 cM1 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0 + 4);
-                    const f32x4 cP0 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0);
-                    const f32x4 cP1 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0 + 4);
-#pragma unroll
-                    for (int m = 0; m < RPT; ++m) {
-                        const int t = t0 + m;
-                        const float cm = m < 4 ? cM0[m & 3] : cM1[m & 3], cp = m < 4 ? cP0[m & 3] : cP1[m & 3];
-                        am[m] += (u <= t ? rM[m][uu] : 0.f) * kb;
-                        ap[m] += (u <= t ? rP[m][uu] : 0.f) * kb;
-                        ak[m] += u >= t ? cm * eh + cp * qh : 0.f;
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const float up = __expf(Gt[m] - sG[(16 * Tb + 15) * LC + il]);
-                const float dn = __expf(sG[16 * Tb * LC + il] - Gt[m]);
-                dEm[m] += up * am[m];
-                dqp[m] += up * ap[m];
-                dkm[m] += dn * ak[m];
-            }
-        }
-        // as the later token: blocks S < Tb
-        for (int S = 0; S < Tb; ++S) {
-            const float c = sCf[(Tb * (Tb - 1) / 2 + S) * DC + il];
-            float am[RPT] = {}, ap[RPT] = {};
-            for (int s0 = 16 * S; s0 < 16 * S + 16; s0 += 4) {
-                float kb[4];
-#pragma unroll
-                for (int y = 0; y < 4; ++y)
-                    kb[y] = sK[(s0 + y) * LC + il];
-#pragma unroll
-                for (int m = 0; m < RPT; ++m) {
-                    const f32x4 rm = *reinterpret_cast<const f32x4*>(sdM + (t0 + m) * LPC + s0);
-                    const f32x4 rp = *reinterpret_cast<const f32x4*>(sdP + (t0 + m) * LPC + s0);
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        am[m] += rm[y] * kb[y];
-                        ap[m] += rp[y] * kb[y];
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                dEm[m] += fa[m] * c * am[m];
-                dqp[m] += fa[m] * c * ap[m];
-            }
-        }
-        // as the earlier token: blocks T > Tb
-        for (int T = Tb + 1; T < C / 16; ++T) {
-            const float c = sCf[(T * (T - 1) / 2 + Tb) * DC + il];
-            float ak[RPT] = {};
-            for (int u = 16 * T; u < 16 * T + 16; ++u) {
-                const float eu = sE[u * LC + il], qu = sQ[u * LC + il];
-                const f32x4 cM0 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0);
-                const f32x4 cM1 = *reinterpret_cast<const f32x4*>(sdM + u * LPC + t0 + 4);
-                const f32x4 cP0 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0);
-                const f32x4 cP1 = *reinterpret_cast<const f32x4*>(sdP + u * LPC + t0 + 4);
-#pragma unroll
-                for (int m = 0; m < RPT; ++m) {
-                    const float cm = m < 4 ? cM0[m & 3] : cM1[m & 3], cp = m < 4 ? cP0[m & 3] : cP1[m & 3];
-                    ak[m] += cm * eu + cp * qu;
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < RPT; ++m)
-                dkm[m] += fb[m] * c * ak[m];
-        }
-    }
-    lds_barrier();                     // sGL ready; dM and dP no longer read
-    // the three sums into LDS (the dM / dP area), then the gradients with
-    // four channels per item
-    float* sEm = sdM;                    // [C][LC] dE_M
-    float* sQp = sEm + C * LC;           // [C][LC] dq_P
-    float* sKm = sQp + C * LC;           // [C][LC] dk_M + dk_P
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int l = (t0 + m) * LC + il;
-        sEm[l] = dEm[m];
-        sQp[l] = dqp[m];
-        sKm[l] = dkm[m];
     }
     lds_barrier();
     for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
