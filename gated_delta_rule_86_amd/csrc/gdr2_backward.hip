@@ -1158,6 +1158,164 @@ __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
     gemm_tile<Mma<E>>(sA, sB, 0, 0, C, Xt, T1, 0, none, none, ws + a.L.dM + cc, C, -1.f, 0.f, nullptr, 2);
 }
 
+// bf16 inputs: the WY-factor products of one chunk with every operand read
+// from memory once and dX, T1 kept on chip.  Eight waves: wave w owns the
+// rows 16 (w % 4).. and half the output columns of every product.  Staged in
+// LDS in bf16 (the precision of every MFMA operand here): X and X^T, dDelta^T
+// and dW^T, U and E~, then dX and T1^T.
+template <int D>
+struct XgradShape {
+    static constexpr int C = BC, LC = C + 8, LDd = D + 8;   // bf16 rows padded by 16 bytes
+    static constexpr size_t X_OFF = 0, XT_OFF = X_OFF + (size_t)C * LC, DDT_OFF = XT_OFF + (size_t)C * LC,
+                            DWT_OFF = DDT_OFF + (size_t)D * LC, U_OFF = DWT_OFF + (size_t)D * LC,
+                            ET_OFF = U_OFF + (size_t)C * LDd, DX_OFF = ET_OFF + (size_t)C * LDd,
+                            T1T_OFF = DX_OFF + (size_t)C * LC, ELEMS = T1T_OFF + (size_t)C * LC;
+    static constexpr size_t SMEM = ELEMS * 2;
+    static constexpr int NTH = 2 * 64 * (C / 16);
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+};
+
+template <int D>
+__global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdArgs a)
+{
+    typedef XgradShape<D> SH;
+    typedef Mma<bf16> MM;
+    typedef MM::Frag Frag;
+    constexpr int C = BC, LC = SH::LC, LDd = SH::LDd, KB = MM::KB, NTH = SH::NTH;
+    extern __shared__ __align__(16) bf16 sx[];
+    bf16* sX = sx + SH::X_OFF;       // X[t][s]
+    bf16* sXt = sx + SH::XT_OFF;     // X^T[s][t]
+    bf16* sDdT = sx + SH::DDT_OFF;   // dDelta^T[j][t]
+    bf16* sDwT = sx + SH::DWT_OFF;   // dW^T[i][t]
+    bf16* sU = sx + SH::U_OFF;       // U[s][j]
+    bf16* sEt = sx + SH::ET_OFF;     // E~[s][i]
+    bf16* sdX = sx + SH::DX_OFF;     // dX[t][u]
+    bf16* sT1t = sx + SH::T1T_OFF;   // T1^T[s][u]
+    const int64_t r = blockIdx.x;
+    float* ws = a.ws;
+    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int rw = wave & 3, hf = wave >> 2, t0 = 16 * rw;
+    const float* Xg = ws + a.L.X + cc;
+    const float* dDel = ws + a.L.dDel + cd;
+    const float* dW = ws + a.L.dW + cd;
+
+    for (int e = tid; e < C * C / 4; e += NTH) {
+        const int t = e / (C / 4), c = 4 * (e % (C / 4));
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(Xg + t * C + c);
+        bf16x4 xv;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            xv[y] = (bf16)x4[y];
+            sXt[(c + y) * LC + t] = xv[y];
+        }
+        *reinterpret_cast<bf16x4*>(sX + t * LC + c) = xv;
+    }
+    for (int e = tid; e < C * D / 4; e += NTH) {
+        const int t = e / (D / 4), j = 4 * (e % (D / 4));
+        const size_t o = cd + (size_t)t * D + j;
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ws + a.L.dDel + o);
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(ws + a.L.dW + o);
+        const f32x4 u4 = *reinterpret_cast<const f32x4*>(ws + a.L.U + o);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(ws + a.L.Et + o);
+        bf16x4 uv, ev;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            sDdT[(j + y) * LC + t] = (bf16)d4[y];
+            sDwT[(j + y) * LC + t] = (bf16)w4[y];
+            uv[y] = (bf16)u4[y];
+            ev[y] = (bf16)e4[y];
+        }
+        *reinterpret_cast<bf16x4*>(sU + t * LDd + j) = uv;
+        *reinterpret_cast<bf16x4*>(sEt + t * LDd + j) = ev;
+    }
+    __syncthreads();
+
+    // dX = dDelta U^T + dW E~^T   (rows t, this wave's two column blocks s)
+    {
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < D / KB; ++ks) {
+            const Frag ad = MM::load(dDel + (size_t)t0 * D + ks * KB, D, lane);
+            const Frag aw = MM::load(dW + (size_t)t0 * D + ks * KB, D, lane);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int sb = 2 * hf + n;
+                acc[n] = MM::mma(ad, MM::load(sU + 16 * sb * LDd + ks * KB, LDd, lane), acc[n]);
+                acc[n] = MM::mma(aw, MM::load(sEt + 16 * sb * LDd + ks * KB, LDd, lane), acc[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                sdX[(t0 + 4 * gq + x) * LC + 16 * (2 * hf + n) + cl] = (bf16)acc[n][x];
+    }
+    // dU = X^T dDelta,  dE~ = X^T dW   (rows s = 16 rw.., this wave's half of the columns)
+    {
+        constexpr int NH = D / 32;
+        f32x4 du[NH], de[NH];
+#pragma unroll
+        for (int n = 0; n < NH; ++n)
+            du[n] = de[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C / KB; ++ks) {
+            const Frag ax = MM::load(sXt + t0 * LC + ks * KB, LC, lane);
+#pragma unroll
+            for (int n = 0; n < NH; ++n) {
+                const int jb = hf * NH + n;
+                du[n] = MM::mma(ax, MM::load(sDdT + 16 * jb * LC + ks * KB, LC, lane), du[n]);
+                de[n] = MM::mma(ax, MM::load(sDwT + 16 * jb * LC + ks * KB, LC, lane), de[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NH; ++n)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const size_t o = cd + (size_t)(t0 + 4 * gq + x) * D + 16 * (hf * NH + n) + cl;
+                ws[a.L.dU + o] = du[n][x];
+                ws[a.L.dEt + o] = de[n][x];
+            }
+    }
+    __syncthreads();                 // dX complete
+    // T1 = dX X^T   (rows t, this wave's two column blocks s), stored transposed
+    {
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < C / KB; ++ks) {
+            const Frag ad = MM::load(sdX + t0 * LC + ks * KB, LC, lane);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                acc[n] = MM::mma(ad, MM::load(sX + 16 * (2 * hf + n) * LC + ks * KB, LC, lane), acc[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                sT1t[(16 * (2 * hf + n) + cl) * LC + t0 + 4 * gq + x] = (bf16)acc[n][x];
+    }
+    __syncthreads();                 // T1 complete
+    // dM = strict_tril(-X^T T1)   (rows t, this wave's two column blocks s)
+    {
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < C / KB; ++ks) {
+            const Frag ax = MM::load(sXt + t0 * LC + ks * KB, LC, lane);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                if (2 * hf + n <= rw)
+                    acc[n] = MM::mma(ax, MM::load(sT1t + 16 * (2 * hf + n) * LC + ks * KB, LC, lane), acc[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int t = t0 + 4 * gq + x, s_ = 16 * (2 * hf + n) + cl;
+                ws[a.L.dM + cc + (size_t)t * C + s_] = s_ < t ? -acc[n][x] : 0.f;
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bwd_decay: per chunk and block of DC key channels, the decay-weighted sums
 // and the input gradients.  Every channel is independent here, so one
@@ -1600,6 +1758,10 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)SgradShape<D>::SMEM)) !=
             hipSuccess)
             return e;
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_xgrad_bf16_kernel<D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)XgradShape<D>::SMEM)) !=
+            hipSuccess)
+            return e;
     }
 
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)nrec), dim3(NTP), lds_prep, s, a);
@@ -1621,7 +1783,12 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
         hipLaunchKernelGGL((bwd_sgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_xgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    if constexpr (sizeof(E) == 2) {
+        hipLaunchKernelGGL((bwd_xgrad_bf16_kernel<D>), dim3((unsigned)nrec), dim3(XgradShape<D>::NTH),
+                           XgradShape<D>::SMEM, s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_xgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(nrec * (D / DC))), dim3(NTB), lds_decay, s, a);
