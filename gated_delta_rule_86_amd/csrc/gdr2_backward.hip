@@ -23,14 +23,16 @@
 //   bwd_prep   one workgroup per chunk: G, E, U, E~, Q~, K^, gamma; M and P
 //              as 16x16 blocks through block-referenced rows (fp32 MFMA);
 //              X by blocks; W, U~ (fp32 MFMA).
-//   bwd_dout   dO rows of every chunk into the workspace (zero past T).
+//   bwd_dout   (fp32 inputs) dO rows of every chunk into the workspace (zero
+//              past T); the other kernels read dO from the input.
 //   bwd_frag   the scan's operands in MFMA fragment order.
 //   bwd_scan   per (sequence, head, 64 value columns): the state gradient
 //              through the chunks in reverse (columns evolve independently),
 //              recording Lam at every chunk end and dDelta.
-//   bwd_sgrad, bwd_xgrad  per chunk: the state and WY-factor products above
-//              as chained 64x64 MFMA tiles in one workgroup (operands stay
-//              in cache between the products).
+//   bwd_sgrad, bwd_xgrad  per chunk: the state and WY-factor products
+//              above.  bf16 inputs: every operand read once, staged in LDS
+//              in bf16, intermediates (Delta, dX, T1) kept on chip; fp32
+//              inputs: chained 64x64 fp32 MFMA tiles through memory.
 //   bwd_decay  per chunk and 32 channels: the decay-weighted sums, dG, dg
 //              and the input gradients.
 //   bwd_norm   the prologue's normalisation, backwards (when asked for).
@@ -606,6 +608,8 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
     const int64_t r = blockIdx.x;
     const float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
+    const Rec rc = rec_of(r, a.NC, a.T, a.H);
+    const E* dOin = (const E*)a.dO;
     unsigned char* out = reinterpret_cast<unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC;
     for (int it = threadIdx.x; it < F::NFRAG * 64; it += NTB) {
         const int f = it / 64, lane = it % 64, gq = lane / 16, rl = lane % 16;
@@ -613,6 +617,7 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
         int row, m;
         int64_t rs, ks;            // element (row, k) at src[row * rs + k * ks]
         float sign = 1.f;
+        bool dout = false;         // dO^T, read from the input rows (zero past the valid length)
         if (f < F::NB * F::NKS) {                       // K^ [s][i]
             row = 16 * (f / F::NKS) + rl; m = f % F::NKS;
             src = ws + a.L.Kh + cdo; rs = D; ks = 1;
@@ -623,14 +628,23 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
         } else {                                        // Q~^T, -W^T, dO^T: [i][t] = X[t][i]
             const int g = f - F::NB * (F::NKS + F::NKC), which = g / (F::DT * F::NKC), h = g % (F::DT * F::NKC);
             row = 16 * (h / F::NKC) + rl; m = h % F::NKC;
-            src = ws + cdo + (which == 0 ? a.L.Qt : which == 1 ? a.L.W : a.L.dO);
+            src = ws + cdo + (which == 0 ? a.L.Qt : a.L.W);
             sign = which == 1 ? -1.f : 1.f;
             rs = 1; ks = D;
+            dout = which == 2;
         }
         float x[NV];
+        if (dout) {
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
-            x[j] = sign * src[row * rs + (int64_t)(m * F::KB + slot_k<E>(gq, j)) * ks];
+            for (int j = 0; j < NV; ++j) {
+                const int t = m * F::KB + slot_k<E>(gq, j);
+                x[j] = t < rc.L ? to_f32(dOin[(rc.row0 + (int64_t)t * a.H) * D + row]) : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                x[j] = sign * src[row * rs + (int64_t)(m * F::KB + slot_k<E>(gq, j)) * ks];
+        }
         unsigned char* dst = out + (size_t)f * F::FRAG + lane * 16;
         if constexpr (sizeof(E) == 2) {
             *reinterpret_cast<bf16x8*>(dst) = Mma<bf16>::pack(f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]});
@@ -1033,8 +1047,22 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     }
 
     const float* W = ws + a.L.W + cd + (size_t)t0 * D;
-    const float* dO = ws + a.L.dO + cd + (size_t)t0 * D;
     const float* dDel = ws + a.L.dDel + cd + (size_t)t0 * D;
+    // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
+    // valid length)
+    const Rec rc = rec_of(r, a.NC, a.T, a.H);
+    const bool dorow = t0 + cl < rc.L;
+    const bf16* dOr = (const bf16*)a.dO + (rc.row0 + (int64_t)(dorow ? t0 + cl : 0) * a.H) * D + 4 * gq;
+    auto load_dO = [&](int ks) -> Frag {
+        Frag f = {};
+        if (dorow) {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB + 16);
+            f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+            f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+        }
+        return f;
+    };
     const size_t orow = cd + (size_t)(t0 + 4 * gq) * D + cl;   // output element (row 4gq, column cl) of the wave
 
     // Delta = U~ - W S   (k = i: B fragments from S^T)
@@ -1066,7 +1094,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
             q[nt] = w[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const Frag ao = MM::load(dO + ks * MM::KB, D, lane), ad = MM::load(dDel + ks * MM::KB, D, lane);
+            const Frag ao = load_dO(ks), ad = MM::load(dDel + ks * MM::KB, D, lane);
 #pragma unroll
             for (int nt = 0; nt < NH; ++nt) {
                 const Frag bs = MM::load(sS + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane);
@@ -1114,7 +1142,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         if (s0 <= rw) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const Frag ao = MM::load(dO + ks * MM::KB, D, lane);
+                const Frag ao = load_dO(ks);
 #pragma unroll
                 for (int sbk = 0; sbk < SBH; ++sbk)
                     if (s0 + sbk <= rw)
@@ -1766,8 +1794,10 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
 
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)nrec), dim3(NTP), lds_prep, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dout_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (sizeof(E) == 4) {   // the fp32 state products read dO as zero-padded records
+        hipLaunchKernelGGL((bwd_dout_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_frag_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
