@@ -20,7 +20,7 @@
 //
 // Kernels (all fp32 arithmetic; intermediates in a fp32 workspace, one
 // record per (sequence, head, chunk)):
-//   bwd_prep   one workgroup per chunk: G, E, U, E~, Q~, K^, gamma; M and P
+//   bwd_prep   one workgroup per chunk: G, U, E~, Q~, K^, gamma; M and P
 //              as 16x16 blocks through block-referenced rows (fp32 MFMA);
 //              X by blocks; W, U~ (fp32 MFMA).
 //   bwd_dout   (fp32 inputs) dO rows of every chunk into the workspace (zero
@@ -55,7 +55,7 @@ size_t a64(size_t x) { return (x + 63) & ~size_t(63); }
 struct BwdLayout {
     int64_t nrec;
     // [C][D] per record
-    size_t G, E, U, Et, Qt, Kh, W, Ut, Del, dDel, dQt, dKh, dW, dU, dEt, dO;
+    size_t G, U, Et, Qt, Kh, W, Ut, Del, dDel, dQt, dKh, dW, dU, dEt, dO;
     // [C][C] per record
     size_t P, X, dP, dX, T1, dM;
     // [D] per record
@@ -76,7 +76,7 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes)
     const size_t cd = a64((size_t)L.nrec * BC * D), cc = a64((size_t)L.nrec * BC * BC);
     const size_t dd = a64((size_t)L.nrec * D * D), d1 = a64((size_t)L.nrec * D);
     size_t o = 0;
-    size_t* cds[] = {&L.G, &L.E, &L.U, &L.Et, &L.Qt, &L.Kh, &L.W, &L.Ut, &L.Del, &L.dDel, &L.dQt, &L.dKh,
+    size_t* cds[] = {&L.G, &L.U, &L.Et, &L.Qt, &L.Kh, &L.W, &L.Ut, &L.Del, &L.dDel, &L.dQt, &L.dKh,
                      &L.dW, &L.dU, &L.dEt, &L.dO};
     for (size_t* p : cds) {
         *p = o;
@@ -135,14 +135,15 @@ __device__ __forceinline__ Rec rec_of(int64_t r, int64_t NC, int64_t T, int64_t 
 // ---------------------------------------------------------------------------
 // bwd_prep: one workgroup (NTP threads) per chunk record.
 //   1. raw rows into LDS, 4 channels per item; G = cumulative log-decay;
-//      E~, Q~, K^, gamma, E, U written out (fp32)
+//      E~, Q~, K^, gamma, U written out (fp32)
 //   2. M (strictly lower) and P (lower) by 16x16 token blocks on fp32 MFMA,
 //      through rows re-referenced to their block (every factor <= 1 below
 //      the diagonal, <= e^kDiagSpan on it); steeper diagonal blocks pair by
 //      pair, and every pair by its own exponential under growth
-//   3. X = (I + M)^-1 by 16x16 blocks: diagonal blocks by substitution, the
-//      rest by X_ij = -X_ii sum_{k=j}^{i-1} M_ik X_kj, one block diagonal at
-//      a time
+//   3. X = (I + M)^-1 by 16x16 blocks in one wave: diagonal blocks by
+//      substitution (a column per lane), the rest by
+//      X_ij = -X_ii sum_{k=j}^{i-1} M_ik X_kj on fp32 MFMA, one block diagonal
+//      at a time; meanwhile the other waves stage E~ and U for step 4
 //   4. W = X E~, U~ = X U as 16x16 fp32 MFMA tiles, one wave per tile
 // ---------------------------------------------------------------------------
 constexpr int NTP = 512;         // threads of the prep kernel
@@ -163,6 +164,9 @@ struct BwdPrepShape {
                   "X fits in the q area; the block products and the partial P in the k area");
 };
 
+// This wave's LDS accesses have completed (a wave-local LDS fence).
+__device__ __forceinline__ void lds_fence_wave() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // s_barrier once this wave's LDS accesses have completed.  Unlike
 // __syncthreads() it does not wait for the wave's outstanding global stores,
 // so a workgroup that only exchanges data through LDS lets them drain.
@@ -182,31 +186,6 @@ __device__ __forceinline__ int lds_barrier_or(int v, int* slots)
     for (int w = 0; w < NW; ++w)
         r |= slots[w];
     return r;
-}
-
-// Y_ij (16x16, into sY) = sum_{k=j}^{i-1} M_ik X_kj  for the blocks (i, i-d)
-// of block diagonal d; then X_ij = -X_ii Y_ij.
-__device__ __forceinline__ void xinv_diagonal(const float* sM, float* sX, float* sY, int d, int tid)
-{
-    constexpr int LDM = BC + 4;
-    const int nblk = 4 - d;
-    for (int e = tid; e < nblk * 256; e += NTP) {
-        const int bi = e / 256, rr = (e / 16) % 16, cc = e % 16, i = bi + d, j = bi;
-        float acc = 0.f;
-        for (int kb = j; kb < i; ++kb)
-            for (int c = 0; c < 16; ++c)
-                acc += sM[(16 * i + rr) * LDM + 16 * kb + c] * sX[(16 * kb + c) * LDM + 16 * j + cc];
-        sY[e] = acc;
-    }
-    lds_barrier();
-    for (int e = tid; e < nblk * 256; e += NTP) {
-        const int bi = e / 256, rr = (e / 16) % 16, cc = e % 16, i = bi + d, j = bi;
-        float acc = 0.f;
-        for (int c = 0; c <= rr; ++c)
-            acc += sX[(16 * i + rr) * LDM + 16 * i + c] * sY[bi * 256 + c * 16 + cc];
-        sX[(16 * i + rr) * LDM + 16 * j + cc] = -acc;
-    }
-    lds_barrier();
 }
 
 __device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
@@ -242,6 +221,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     float* sQ = sm + PS::OFF_Q;     // [C][LD] q, later X [C][LDM]
     float* sM = sm + PS::OFF_M;     // [C][LDM] M
     __shared__ int sOr[2 * (NTP / 64)];
+    __shared__ float sRN[2 * C];    // prologue: 1/|k|, 1/|q| per token
     const int64_t r = blockIdx.x;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
     const int tid = threadIdx.x;
@@ -291,6 +271,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             if (i == 0) {
                 ws[a.L.RN + (size_t)r * 2 * C + t] = rk;
                 ws[a.L.RN + (size_t)r * 2 * C + C + t] = rq;
+                sRN[t] = rk;
             }
         }
         ev = ev * kv;
@@ -298,7 +279,6 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         st4s(sK + l, kv);
         st4s(sQ + l, qv);
         st4s(sE + l, ev);
-        st4s(ws + a.L.E + x, ev);
         st4s(ws + a.L.U + x, uv);
     }
     growth = lds_barrier_or<NTP / 64>(growth, sOr);
@@ -489,45 +469,80 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 
     }
 
-    // 3. X = (I + M)^-1 into the q area; first the diagonal 16x16 blocks, one
-    // column per thread, then the block diagonals below
+    // 3. X = (I + M)^-1 into the q area (wave 0), while the other waves stage
+    // E~ and u for step 4 (recomputed from the inputs: the k area and the
+    // E area hold re-referenced rows)
     float* sX = sQ;
-    float* sY = sK;
-    for (int e = tid; e < C * C; e += NTP)
-        sX[(e / C) * LDM + e % C] = 0.f;
-    lds_barrier();
-    if (tid < C) {
-        const int bk = tid / 16, j = tid % 16, o = 16 * bk;
-        for (int rr = j; rr < 16; ++rr) {
-            float acc = rr == j ? 1.f : 0.f;
-            for (int c = j; c < rr; ++c)
-                acc -= sM[(o + rr) * LDM + o + c] * sX[(o + c) * LDM + o + j];
-            sX[(o + rr) * LDM + o + j] = acc;
+    float* sU = sK;
+    if (tid < 64) {
+        typedef Mma<float> MF;
+        const int lane = tid, gq = lane >> 4, cl = lane & 15;
+        {
+            // column cl of the diagonal block X_gq,gq by forward substitution
+            // (unit diagonal), then zeros for the blocks right of it
+            const float* m = sM + 16 * gq * LDM + 16 * gq;
+            float x[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float acc = rr == cl ? 1.f : 0.f;
+#pragma unroll
+                for (int c = 0; c < rr; ++c)
+                    acc -= m[rr * LDM + c] * x[c];
+                x[rr] = acc;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                sX[(16 * gq + rr) * LDM + 16 * gq + cl] = x[rr];
+                for (int J = gq + 1; J < C / 16; ++J)
+                    sX[(16 * gq + rr) * LDM + 16 * J + cl] = 0.f;
+            }
+        }
+        // X_IJ = -X_II sum_{K=J}^{I-1} M_IK X_KJ, one block diagonal at a time
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        for (int dg = 1; dg < C / 16; ++dg) {
+            lds_fence_wave();
+            for (int I = dg; I < C / 16; ++I) {
+                const int J = I - dg;
+                f32x4 y = zero;
+                for (int K = J; K < I; ++K)
+                    y = MF::mma(MF::load(sM + 16 * I * LDM + 16 * K, LDM, lane),
+                                MF::load_kn(sX + 16 * K * LDM + 16 * J, LDM, lane), y);
+                const f32x4 xi = MF::mma(MF::load(sX + 16 * I * LDM + 16 * I, LDM, lane), MF::from_acc(&y), zero);
+#pragma unroll
+                for (int x4 = 0; x4 < 4; ++x4)
+                    sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = -xi[x4];
+            }
+        }
+    } else {
+        for (int e4 = tid - 64; e4 < C * Q4; e4 += NTP - 64) {
+            const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+            f32x4 ev = {0.f, 0.f, 0.f, 0.f}, uv = ev;
+            if (t < rc.L) {
+                // e = b k and u = w v as step 1 forms them
+                const int64_t row = rc.row0 + (int64_t)t * a.H;
+                f32x4 kv = load4(k + row * D + i), bv = gate4(b, a.bw, row, i), wv = gate4(w, a.ww, row, i);
+                if (a.pro & GDR2_PROLOGUE_GATES) {
+                    bv = bsigm4(bv);
+                    wv = bsigm4(wv);
+                }
+                if (a.pro & GDR2_PROLOGUE_NORM_QK)
+                    kv = kv * sRN[t];
+                ev = bv * kv;
+                uv = wv * load4(v + row * D + i);
+            }
+            const f32x4 G = ld4s(sG + l);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ev[j] *= expf(G[j]);
+            st4s(sE + l, ev);
+            st4s(sU + l, uv);
         }
     }
     lds_barrier();
-    xinv_diagonal(sM, sX, sY, 1, tid);
-    xinv_diagonal(sM, sX, sY, 2, tid);
-    xinv_diagonal(sM, sX, sY, 3, tid);
     for (int e = tid; e < C * C; e += NTP)
         ws[a.L.X + cco + e] = sX[(e / C) * LDM + e % C];
 
-    // 4. E~ in place, u into the k area; W = X E~, U~ = X u
-    float* sU = sK;
-    for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
-        const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        // sE holds the re-referenced rows; each thread re-reads the E and u
-        // elements it wrote itself in step 1 (same item mapping), so no
-        // barrier has to wait for those stores
-        f32x4 ev = ld4s(ws + a.L.E + cdo + (size_t)t * D + i);
-        const f32x4 G = ld4s(sG + l);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ev[j] *= expf(G[j]);
-        st4s(sE + l, ev);
-        st4s(sU + l, ld4s(ws + a.L.U + cdo + (size_t)t * D + i));
-    }
-    lds_barrier();
+    // 4. W = X E~, U~ = X u
     {
         // 16x16 output tiles on fp32 MFMA, one wave per tile: A = rows of X
         // (lower triangular, so tile row T needs k-tiles 0..T), B = the

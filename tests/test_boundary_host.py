@@ -314,7 +314,7 @@ def test_backward_workspace_size_formula(lib):
                                  (8, 4096, 16, 128, gdr2.BF16, 2), (1, 200, 2, 128, gdr2.F32, 4)]:
         a = good_bwd(B=B, T=T, H=H, D=D, dtype=dt)
         nrec = B * H * -(-T // 64)
-        want = (16 * al(nrec * 64 * D * 4) + 6 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
+        want = (15 * al(nrec * 64 * D * 4) + 6 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
                 + al(nrec * D * D * 4) + al(nrec * (4 * 64 * D + 64 * 64) * es))
         assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == want
     assert lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(T=0))) == 0
