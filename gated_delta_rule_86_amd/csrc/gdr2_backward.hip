@@ -232,6 +232,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     const E* w = (const E*)a.w;
     float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
+    E* wP = reinterpret_cast<E*>(ws + a.L.P) + cco;   // P, in the input dtype
 
     // 1. raw rows (zero past the chunk's valid length), 4 channels per item
     int growth = 0;                  // a log-decay > 0 somewhere in the chunk
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         st4s(sK + l, kv);
         st4s(sQ + l, qv);
         st4s(sE + l, ev);
-        st4s(ws + a.L.U + x, uv);
+        store4(reinterpret_cast<E*>(ws + a.L.U) + x, uv);
     }
     growth = lds_barrier_or<NTP / 64>(growth, sOr);
     for (int i = tid; i < D; i += NTP) {
@@ -301,9 +302,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             kd[j] = expf(GL[j] - G[j]);
         }
         st4s(ws + a.L.G + x, G);
-        st4s(ws + a.L.Et + x, ld4s(sE + l) * eg);
-        st4s(ws + a.L.Qt + x, ld4s(sQ + l) * eg);
-        st4s(ws + a.L.Kh + x, ld4s(sK + l) * kd);
+        store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ld4s(sE + l) * eg);
+        store4(reinterpret_cast<E*>(ws + a.L.Qt) + x, ld4s(sQ + l) * eg);
+        store4(reinterpret_cast<E*>(ws + a.L.Kh) + x, ld4s(sK + l) * kd);
         if (t == 0) {
             f32x4 gm;
 #pragma unroll
@@ -342,10 +343,10 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 p += sQ[t * LD + i] * f;
             }
             sM[t * LDM + s_] = cc < rr ? m : 0.f;
-            ws[a.L.P + cco + t * C + s_] = p;
+            wP[t * C + s_] = from_f32<E>(p);
             if (cc < rr) {
                 sM[s_ * LDM + t] = 0.f;
-                ws[a.L.P + cco + s_ * C + t] = 0.f;
+                wP[s_ * C + t] = from_f32<E>(0.f);
             }
         }
         lds_barrier();
@@ -392,11 +393,11 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * T + 4 * gq + i, s_ = 16 * S + cl;
                     sM[t * LDM + s_] = s_ < t ? m[i] : 0.f;
-                    ws[a.L.P + cco + t * C + s_] = s_ <= t ? p[i] : 0.f;
+                    wP[t * C + s_] = from_f32<E>(s_ <= t ? p[i] : 0.f);
                     if (S < T) {
                         const int ta = 16 * S + 4 * gq + i, sa = 16 * T + cl;   // the block (S, T)
                         sM[ta * LDM + sa] = 0.f;
-                        ws[a.L.P + cco + ta * C + sa] = 0.f;
+                        wP[ta * C + sa] = from_f32<E>(0.f);
                     }
                 }
             }
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     const int t = t0 + x, s_ = s0 + y;
                     const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
                     sM[t * LDM + s_] = s_ < t ? mm : 0.f;
-                    ws[a.L.P + cco + t * C + s_] = s_ <= t ? pp : 0.f;
+                    wP[t * C + s_] = from_f32<E>(s_ <= t ? pp : 0.f);
                 }
             if (sb != tb) {               // the mirrored block above the diagonal is zero
     #pragma unroll
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     #pragma unroll
                     for (int y = 0; y < 4; ++y) {
                         sM[(s0 + y) * LDM + t0 + x] = 0.f;
-                        ws[a.L.P + cco + (s0 + y) * C + t0 + x] = 0.f;
+                        wP[(s0 + y) * C + t0 + x] = from_f32<E>(0.f);
                     }
             }
         }
@@ -557,10 +558,16 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             for (int kk = 0; kk <= T; ++kk)
                 acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
                               MF::load_kn(src + 16 * kk * LD + 16 * c, LD, lane), acc);
-            float* dst = ws + (which == 0 ? a.L.W : a.L.Ut) + cdo + (size_t)(16 * T + 4 * gq) * D + 16 * c + cl;
+            const size_t o = cdo + (size_t)(16 * T + 4 * gq) * D + 16 * c + cl;
+            if (which == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dst[(size_t)i * D] = acc[i];
+                for (int i = 0; i < 4; ++i)
+                    reinterpret_cast<E*>(ws + a.L.W)[o + (size_t)i * D] = from_f32<E>(acc[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ws[a.L.Ut + o + (size_t)i * D] = acc[i];
+            }
         }
     }
 }
@@ -628,22 +635,22 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
     unsigned char* out = reinterpret_cast<unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC;
     for (int it = threadIdx.x; it < F::NFRAG * 64; it += NTB) {
         const int f = it / 64, lane = it % 64, gq = lane / 16, rl = lane % 16;
-        const float* src;
+        const E* src;
         int row, m;
         int64_t rs, ks;            // element (row, k) at src[row * rs + k * ks]
         float sign = 1.f;
         bool dout = false;         // dO^T, read from the input rows (zero past the valid length)
         if (f < F::NB * F::NKS) {                       // K^ [s][i]
             row = 16 * (f / F::NKS) + rl; m = f % F::NKS;
-            src = ws + a.L.Kh + cdo; rs = D; ks = 1;
+            src = reinterpret_cast<const E*>(ws + a.L.Kh) + cdo; rs = D; ks = 1;
         } else if (f < F::NB * (F::NKS + F::NKC)) {     // P^T [s][t] = P[t][s]
             const int g = f - F::NB * F::NKS;
             row = 16 * (g / F::NKC) + rl; m = g % F::NKC;
-            src = ws + a.L.P + cco; rs = 1; ks = C;
+            src = reinterpret_cast<const E*>(ws + a.L.P) + cco; rs = 1; ks = C;
         } else {                                        // Q~^T, -W^T, dO^T: [i][t] = X[t][i]
             const int g = f - F::NB * (F::NKS + F::NKC), which = g / (F::DT * F::NKC), h = g % (F::DT * F::NKC);
             row = 16 * (h / F::NKC) + rl; m = h % F::NKC;
-            src = ws + cdo + (which == 0 ? a.L.Qt : a.L.W);
+            src = reinterpret_cast<const E*>(ws + (which == 0 ? a.L.Qt : a.L.W)) + cdo;
             sign = which == 1 ? -1.f : 1.f;
             rs = 1; ks = D;
             dout = which == 2;
@@ -658,7 +665,7 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
         } else {
 #pragma unroll
             for (int j = 0; j < NV; ++j)
-                x[j] = sign * src[row * rs + (int64_t)(m * F::KB + slot_k<E>(gq, j)) * ks];
+                x[j] = sign * to_f32(src[row * rs + (int64_t)(m * F::KB + slot_k<E>(gq, j)) * ks]);
         }
         unsigned char* dst = out + (size_t)f * F::FRAG + lane * 16;
         if constexpr (sizeof(E) == 2) {
@@ -1061,7 +1068,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         ws[a.L.gam + (size_t)r * D + tid] = gam_i * dg;
     }
 
-    const float* W = ws + a.L.W + cd + (size_t)t0 * D;
+    const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
     const float* dDel = ws + a.L.dDel + cd + (size_t)t0 * D;
     // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
     // valid length)
@@ -1259,18 +1266,13 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
         const size_t o = cd + (size_t)t * D + j;
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(ws + a.L.dDel + o);
         const f32x4 w4 = *reinterpret_cast<const f32x4*>(ws + a.L.dW + o);
-        const f32x4 u4 = *reinterpret_cast<const f32x4*>(ws + a.L.U + o);
-        const f32x4 e4 = *reinterpret_cast<const f32x4*>(ws + a.L.Et + o);
-        bf16x4 uv, ev;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
             sDdT[(j + y) * LC + t] = (bf16)d4[y];
             sDwT[(j + y) * LC + t] = (bf16)w4[y];
-            uv[y] = (bf16)u4[y];
-            ev[y] = (bf16)e4[y];
         }
-        *reinterpret_cast<bf16x4*>(sU + t * LDd + j) = uv;
-        *reinterpret_cast<bf16x4*>(sEt + t * LDd + j) = ev;
+        *reinterpret_cast<bf16x4*>(sU + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.U) + o / 4);
+        *reinterpret_cast<bf16x4*>(sEt + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.Et) + o / 4);
     }
     __syncthreads();
 
