@@ -770,12 +770,12 @@ __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char
 #pragma unroll
         for (int kc = st / KT; kc < NKC; ++kc)
             dd[st] = MM::mma(frag(F::OFF_P, st * NKC + kc), OB[kc], dd[st]);
-    float* dq = a.ws + a.L.dDel + (size_t)r * BC * D;
+    E* dq = reinterpret_cast<E*>(a.ws + a.L.dDel) + (size_t)r * BC * D;   // in the input dtype
 #pragma unroll
     for (int st = 0; st < NB; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dq[(16 * st + 4 * gq + i) * D + col] = dd[st][i];
+            dq[(16 * st + 4 * gq + i) * D + col] = from_f32<E>(dd[st][i]);
 
     // Lam <- diag(gamma) Lam + Q~^T dO - W^T dDelta  (the W fragments hold -W^T)
     Frag DB[NKC];
@@ -1069,7 +1069,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     }
 
     const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
-    const float* dDel = ws + a.L.dDel + cd + (size_t)t0 * D;
+    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd + (size_t)t0 * D;
     // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
     // valid length)
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 ws[a.L.dQt + orow + (size_t)x * D + 16 * (n0 + nt)] = q[nt][x];
-                ws[a.L.dW + orow + (size_t)x * D + 16 * (n0 + nt)] = -w[nt][x];
+                reinterpret_cast<bf16*>(ws + a.L.dW)[orow + (size_t)x * D + 16 * (n0 + nt)] = (bf16)(-w[nt][x]);
             }
     }
     __syncthreads();                 // every wave's Delta rows are in LDS
@@ -1247,8 +1247,8 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
     const int rw = wave & 3, hf = wave >> 2, t0 = 16 * rw;
     const float* Xg = ws + a.L.X + cc;
-    const float* dDel = ws + a.L.dDel + cd;
-    const float* dW = ws + a.L.dW + cd;
+    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd;
+    const bf16* dW = reinterpret_cast<const bf16*>(ws + a.L.dW) + cd;
 
     for (int e = tid; e < C * C / 4; e += NTH) {
         const int t = e / (C / 4), c = 4 * (e % (C / 4));
@@ -1264,12 +1264,12 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
     for (int e = tid; e < C * D / 4; e += NTH) {
         const int t = e / (D / 4), j = 4 * (e % (D / 4));
         const size_t o = cd + (size_t)t * D + j;
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ws + a.L.dDel + o);
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(ws + a.L.dW + o);
+        const bf16x4 d4 = *(reinterpret_cast<const bf16x4*>(ws + a.L.dDel) + o / 4);
+        const bf16x4 w4 = *(reinterpret_cast<const bf16x4*>(ws + a.L.dW) + o / 4);
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            sDdT[(j + y) * LC + t] = (bf16)d4[y];
-            sDwT[(j + y) * LC + t] = (bf16)w4[y];
+            sDdT[(j + y) * LC + t] = d4[y];
+            sDwT[(j + y) * LC + t] = w4[y];
         }
         *reinterpret_cast<bf16x4*>(sU + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.U) + o / 4);
         *reinterpret_cast<bf16x4*>(sEt + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.Et) + o / 4);
