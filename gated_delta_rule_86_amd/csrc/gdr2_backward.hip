@@ -283,12 +283,29 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         store4(reinterpret_cast<E*>(ws + a.L.U) + x, uv);
     }
     growth = lds_barrier_or<NTP / 64>(growth, sOr);
-    for (int i = tid; i < D; i += NTP) {
-        float acc = 0.f;
-        for (int t = 0; t < C; ++t) {
-            acc += sG[t * LD + i];
-            sG[t * LD + i] = acc;
-        }
+    {
+        // cumulative sum over the chunk per channel: thread (group gi, channel
+        // i) scans its TPG consecutive tokens, then adds the earlier groups'
+        // totals (through the M area, free until step 2)
+        constexpr int NG = NTP / D, TPG = C / NG;
+        static_assert(NTP % D == 0 && C % NG == 0, "whole token groups");
+        const int i = tid % D, gi = tid / D;
+        float* sTot = sM;
+        float v[TPG];
+#pragma unroll
+        for (int m = 0; m < TPG; ++m)
+            v[m] = sG[(gi * TPG + m) * LD + i];
+#pragma unroll
+        for (int m = 1; m < TPG; ++m)
+            v[m] += v[m - 1];
+        sTot[gi * D + i] = v[TPG - 1];
+        lds_barrier();
+        float off = 0.f;
+        for (int g2 = 0; g2 < gi; ++g2)
+            off += sTot[g2 * D + i];
+#pragma unroll
+        for (int m = 0; m < TPG; ++m)
+            sG[(gi * TPG + m) * LD + i] = v[m] + off;
     }
     lds_barrier();
     for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
@@ -1695,22 +1712,33 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
     }
     lds_barrier();
-    // dg: reverse cumulative sum over the chunk, per channel
-    if (tid < DC) {
-        float acc = 0.f;
-        for (int t = C - 1; t >= 0; --t) {
-            acc += sdG[t * LC + tid];
-            sdG[t * LC + tid] = acc;
-        }
-    }
+    // dg: reverse cumulative sum over the chunk, per channel: each thread
+    // scans its RPT tokens, then adds the later row groups' totals
+    float vg[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        vg[m] = sdG[(t0 + m) * LC + il];
+#pragma unroll
+    for (int m = RPT - 2; m >= 0; --m)
+        vg[m] += vg[m + 1];
+    lds_barrier();                       // every thread has its dG rows
+    sdG[rg * LC + il] = vg[0];
     lds_barrier();
+    {
+        float off = 0.f;
+        for (int g2 = rg + 1; g2 < NRG; ++g2)
+            off += sdG[g2 * LC + il];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            vg[m] += off;
+    }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int t = t0 + m;
         if (t >= rc.L)
             continue;
         const int64_t row = rc.row0 + (int64_t)t * a.H;
-        float dgv = sdG[t * LC + il];
+        float dgv = vg[m];
         if (a.pro & GDR2_PROLOGUE_GATES)      // d/dx[-softplus(x)] = -sigmoid(x)
             dgv *= -bsigm(a.g[a.gw == 1 ? row : row * D + i]);
         if (a.gw == 1)
