@@ -28,8 +28,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KERNELS = (("chunk_prep_kernel", "gdr2_chunk_prep"), ("chunk_state_kernel", "gdr2_chunk_state"),
            ("decode_step_kernel", "gdr2_decode_step"), ("bwd_prep_kernel", "gdr2_bwd_prep"),
            ("bwd_dout_kernel", "gdr2_bwd_dout"), ("bwd_frag_kernel", "gdr2_bwd_frag"),
-           ("bwd_scan_kernel", "gdr2_bwd_scan"), ("bwd_sgrad_kernel", "gdr2_bwd_sgrad"),
-           ("bwd_xgrad_kernel", "gdr2_bwd_xgrad"), ("bwd_norm_kernel", "gdr2_bwd_norm"),
+           ("bwd_scan_kernel", "gdr2_bwd_scan"), ("bwd_sgrad", "gdr2_bwd_sgrad"),
+           ("bwd_xgrad", "gdr2_bwd_xgrad"), ("bwd_norm_kernel", "gdr2_bwd_norm"),
            ("bwd_decay_kernel", "gdr2_bwd_decay"), ("zero_kernel", "gdr2_zero_fill"), ("copy", "plain_copy"))
 COPY_BYTES_MARK = "calibration copy bytes:"
 
