@@ -1393,7 +1393,7 @@ constexpr int LC = DC + 1;             // padded LDS row of the per-channel arra
 constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte aligned)
 
 template <typename E, int D>
-__global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
+__global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
 {
     constexpr int C = BC, NRG = NTB / DC, RPT = C / NRG;
     static_assert(RPT == 8, "two 16-byte reads cover a thread's tokens");
@@ -1420,31 +1420,54 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
     const float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
 
-    for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
-        const int t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
+    // This thread's items (token t, 4 channels) of the row arrays: every
+    // global operand of the staging and of the epilogue is loaded here, up
+    // front, so those loads overlap everything up to the epilogue.
+    constexpr int NIT = C * DC / 4 / NTB;
+    static_assert(NIT * NTB == C * DC / 4, "whole items per thread");
+    f32x4 xk[NIT], xq[NIT], xb[NIT], xw[NIT], xv[NIT], xdEt[NIT], xdQt[NIT], xdKh[NIT], xdU[NIT];
+    float xrk[NIT], xrq[NIT];
+#pragma unroll
+    for (int p = 0; p < NIT; ++p) {
+        const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4));
         const size_t x = cdo + (size_t)t * D + i0 + c;
-        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv, ev = kv;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        xk[p] = xq[p] = xb[p] = xw[p] = xv[p] = z;
+        xrk[p] = xrq[p] = 1.f;
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H;
-            kv = load4(k + row * D + i0 + c);
-            qv = load4(q + row * D + i0 + c);
+            xk[p] = load4(k + row * D + i0 + c);
+            xq[p] = load4(q + row * D + i0 + c);
+            xv[p] = load4(v + row * D + i0 + c);
+            xb[p] = gate4(b, a.bw, row, i0 + c);
+            xw[p] = gate4(w, a.ww, row, i0 + c);
             if (a.pro & GDR2_PROLOGUE_NORM_QK) {
-                kv = kv * ws[a.L.RN + (size_t)r * 2 * C + t];
-                qv = qv * ws[a.L.RN + (size_t)r * 2 * C + C + t];
+                xrk[p] = ws[a.L.RN + (size_t)r * 2 * C + t];
+                xrq[p] = ws[a.L.RN + (size_t)r * 2 * C + C + t];
             }
-            // e = b k, formed as bwd_prep forms it
-            f32x4 bv = gate4(b, a.bw, row, i0 + c);
-            if (a.pro & GDR2_PROLOGUE_GATES)
-                bv = bsigm4(bv);
-            ev = bv * kv;
         }
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(ws + a.L.G + x);
+        xdEt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
+        xdQt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
+        xdKh[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
+        xdU[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+    }
+#pragma unroll
+    for (int p = 0; p < NIT; ++p) {
+        // k, q normalised and b activated under the prologue; e = b k as
+        // bwd_prep forms it
+        xk[p] = xk[p] * xrk[p];
+        xq[p] = xq[p] * xrq[p];
+        if (a.pro & GDR2_PROLOGUE_GATES)
+            xb[p] = bsigm4(xb[p]);
+        const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(ws + a.L.G + cdo + (size_t)t * D + i0 + c);
+        const f32x4 ev = xb[p] * xk[p];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             sG[l + j] = gv[j];
             sE[l + j] = ev[j];
-            sK[l + j] = kv[j];
-            sQ[l + j] = qv[j];
+            sK[l + j] = xk[p][j];
+            sQ[l + j] = xq[p][j];
         }
     }
     for (int e = tid; e < C * C / 4; e += NTB) {
@@ -1648,30 +1671,15 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
     }
     lds_barrier();
-    for (int e4 = tid; e4 < C * DC / 4; e4 += NTB) {
-        const int t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
-        const size_t x = cdo + (size_t)t * D + i0 + c;
-        const f32x4 dEt = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
-        const f32x4 dQt = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
-        const f32x4 dKh = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
-        const f32x4 dU = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
-        // raw rows (LDS may hold the re-referenced ones) from the inputs:
-        // k and q normalised and b activated under the prologue, e = b k
-        f32x4 kr = {0.f, 0.f, 0.f, 0.f}, qr = kr, bv = kr, bd = {1.f, 1.f, 1.f, 1.f};
-        if (t < rc.L) {
-            const int64_t row = rc.row0 + (int64_t)t * a.H;
-            kr = load4(k + row * D + i0 + c);
-            qr = load4(q + row * D + i0 + c);
-            if (a.pro & GDR2_PROLOGUE_NORM_QK) {
-                kr = kr * ws[a.L.RN + (size_t)r * 2 * C + t];
-                qr = qr * ws[a.L.RN + (size_t)r * 2 * C + C + t];
-            }
-            bv = gate4(b, a.bw, row, i0 + c);
-            if (a.pro & GDR2_PROLOGUE_GATES) {
-                bv = bsigm4(bv);
-                bd = bv * (f32x4{1.f, 1.f, 1.f, 1.f} - bv);   // d(activation)/d(raw)
-            }
-        }
+#pragma unroll
+    for (int p = 0; p < NIT; ++p) {
+        const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
+        const f32x4 dEt = xdEt[p], dQt = xdQt[p], dKh = xdKh[p], dU = xdU[p];
+        // raw rows (LDS may hold the re-referenced ones), held since the
+        // start: k and q normalised and b activated under the prologue, e = b k
+        const f32x4 kr = xk[p], qr = xq[p], bv = xb[p];
+        const f32x4 bd = (a.pro & GDR2_PROLOGUE_GATES) ? bv * (f32x4{1.f, 1.f, 1.f, 1.f} - bv)
+                                                       : f32x4{1.f, 1.f, 1.f, 1.f};   // d(activation)/d(raw)
         const f32x4 ev = bv * kr;
         f32x4 dq, dk, dE;
 #pragma unroll
@@ -1690,13 +1698,13 @@ __global__ __launch_bounds__(NTB) void bwd_decay_kernel(BwdArgs a)
         }
         if (t < rc.L) {
             const int64_t row = rc.row0 + (int64_t)t * a.H, off = row * D + i0 + c;
-            f32x4 wv = gate4(w, a.ww, row, i0 + c), wd = {1.f, 1.f, 1.f, 1.f};
+            f32x4 wv = xw[p], wd = {1.f, 1.f, 1.f, 1.f};
             // prologue gates: the activated values, and d(activation)/d(raw)
             if (a.pro & GDR2_PROLOGUE_GATES) {
                 wv = bsigm4(wv);
                 wd = wv * (f32x4{1.f, 1.f, 1.f, 1.f} - wv);
             }
-            const f32x4 vv = load4(v + off), kv = kr;
+            const f32x4 vv = xv[p], kv = kr;
             *reinterpret_cast<f32x4*>(a.dq + off) = dq;
             *reinterpret_cast<f32x4*>(a.dk + off) = dk + dE * bv;
             *reinterpret_cast<f32x4*>(a.dv + off) = dU * wv;
