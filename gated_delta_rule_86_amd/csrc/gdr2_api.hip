@@ -151,7 +151,7 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
     gdr2_status s = check_common(rows, a->Dk, a->Dv, a->dtype, a->b_width, a->w_width, a->g_width);
     if (s != GDR2_OK)
         return s;
-    if (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED)
+    if (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED && a->algo != GDR2_ALGO_SEGMENTED)
         return fail(GDR2_ERR_INVALID_ARG, "unknown algo %d", a->algo);
     if (a->stage != GDR2_STAGE_ALL && a->stage != GDR2_STAGE_PREP && a->stage != GDR2_STAGE_STATE)
         return fail(GDR2_ERR_INVALID_ARG, "unknown stage %d", a->stage);

@@ -109,7 +109,7 @@ struct Frags {
 // arrays -W, U~, K^T, Q~ (C*D elements each), P (NP fragments), gamma (D fp32).
 struct Layout {
     int64_t nrec;
-    size_t wn, ut, kh, qt, p, gam, total;
+    size_t wn, ut, kh, qt, p, gam, span, total;
 };
 
 int p_frags(int C, int es)
@@ -121,7 +121,10 @@ int p_frags(int C, int es)
     return n;
 }
 
-Layout staged_layout(int64_t B, int64_t H, int64_t T, int D, int C, int esz)
+// nseg > 1 adds the segment area of the two-level scan: per (sequence, head)
+// and per segment but the last, two D x D fp32 matrices (the segment's chunk
+// product, then its local state).
+Layout staged_layout(int64_t B, int64_t H, int64_t T, int D, int C, int esz, int64_t nseg)
 {
     Layout L;
     L.nrec = B * H * ceil_div(T, C);
@@ -134,7 +137,8 @@ Layout staged_layout(int64_t B, int64_t H, int64_t T, int D, int C, int esz)
     L.qt = 3 * mat;
     L.p = 4 * mat;
     L.gam = 4 * mat + pm;
-    L.total = 4 * mat + pm + gm;
+    L.span = 4 * mat + pm + gm;
+    L.total = L.span + (nseg > 1 ? al256((size_t)(B * H) * (nseg - 1) * 2 * D * D * 4) : 0);
     return L;
 }
 
@@ -156,6 +160,8 @@ struct StateArgs {
     float* S_chunks;          // optional: the state at the start of every chunk
     void* o;
     int64_t T, H, NC, nbh;
+    int64_t nseg, seg_len;    // chunk segments of the two-level scan (1, NC: one pass)
+    float* span;              // segment area (nseg > 1)
 };
 
 // ---------------------------------------------------------------------------
@@ -1287,7 +1293,7 @@ __device__ __forceinline__ void state_emit(const StateArgs& a, const f32x4* St, 
 // S <- diag(gamma) S + K^T Delta; O goes out through the wave's staging rows.
 template <typename E, int D, int C, int BV>
 __device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned char* buf, E* sOw, f32x4* St,
-                                              int64_t b, int64_t h, int slice, int64_t n,
+                                              int64_t b, int64_t h, int slice, int64_t n, bool store_prev,
                                               int lane, int wave)
 {
     typedef StateShape<E, D, C, BV> S;
@@ -1333,7 +1339,7 @@ __device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned
     for (int kc = 0; kc < NKC; ++kc)
         DB[kc] = MM::from_acc(&dl[kc * KT]);
     // the previous chunk's outputs leave while this one computes
-    if (n > 0)
+    if (store_prev)
         state_store_o<E, D, C, BV>(a, sOw, b, h, slice, n - 1, lane, wave);
 
     // O = Q~ S + P Delta  (P is lower triangular: only stored steps).
@@ -1419,24 +1425,29 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
     __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
     __shared__ __align__(16) E sO[(NT / 64) * C * S::LDO];
 
-    // Workgroup -> (sequence*head, column slice).  The NS slices of one
-    // (b,h) read the same chunk records: give them the same blockIdx % 8 so
-    // they land on the same XCD and share its L2.
+    // Workgroup -> (sequence*head, chunk segment, column slice).  The NS
+    // slices of one segment read the same chunk records: give them the same
+    // blockIdx % 8 so they land on the same XCD and share its L2.
     const int64_t bx = blockIdx.x;
     const int64_t grp = bx / (8 * S::NS);
     const int within = (int)(bx % (8 * S::NS));
     const int slice = within / 8;
-    const int64_t bh = grp * 8 + within % 8;
-    if (bh >= a.nbh)
+    const int64_t unit = grp * 8 + within % 8;       // (b*H + h) * nseg + segment
+    if (unit >= a.nbh * a.nseg)
         return;
+    const int64_t bh = unit / a.nseg, seg = unit - bh * a.nseg;
     const int64_t b = bh / a.H, h = bh - b * a.H, rec0 = bh * a.NC;
+    const int64_t n0 = seg * a.seg_len, n1 = min(a.NC, n0 + a.seg_len);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
     const int col = slice * BV + 16 * wave + cl;     // this lane's state column
     E* sOw = sO + wave * C * S::LDO;
 
+    // start state: S0 (or zero) for the first segment, else the one the
+    // segment fold left in the local-state half of the previous segment
+    const float* s0 = seg == 0 ? (a.S0 ? a.S0 + bh * D * D : nullptr)
+                               : a.span + ((bh * (a.nseg - 1) + seg - 1) * 2 + 1) * D * D;
     f32x4 St[KTS];
-    if (a.S0) {
-        const float* s0 = a.S0 + bh * D * D;
+    if (s0) {
 #pragma unroll
         for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
@@ -1448,48 +1459,290 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
             St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    state_fetch<E, D, C, BV>(a, rec0, slice, buf0, wave, lane);
+    state_fetch<E, D, C, BV>(a, rec0 + n0, slice, buf0, wave, lane);
     if (S::NBUF == 2) {
-        for (int64_t n = 0; n < a.NC; n += 2) {
+        for (int64_t n = n0; n < n1; n += 2) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
-            if (n + 1 < a.NC)
+            if (n + 1 < n1)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf1, wave, lane);
             if (a.S_chunks)
                 state_emit<D>(a, St, bh, n, gq, col);
-            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
-            if (n + 1 >= a.NC)
+            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, n > n0, lane, wave);
+            if (n + 1 >= n1)
                 break;
             wait_copies();
             __syncthreads();          // chunk n + 1 is in buf1; everyone is done with buf0
-            if (n + 2 < a.NC)
+            if (n + 2 < n1)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 2, slice, buf0, wave, lane);
             if (a.S_chunks)
                 state_emit<D>(a, St, bh, n + 1, gq, col);
-            state_compute<E, D, C, BV>(a, buf1, sOw, St, b, h, slice, n + 1, lane, wave);
+            state_compute<E, D, C, BV>(a, buf1, sOw, St, b, h, slice, n + 1, true, lane, wave);
         }
     } else {
-        for (int64_t n = 0; n < a.NC; ++n) {
+        for (int64_t n = n0; n < n1; ++n) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0
             if (a.S_chunks)
                 state_emit<D>(a, St, bh, n, gq, col);
-            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, lane, wave);
+            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, n > n0, lane, wave);
             __syncthreads();          // everyone is done with buf0
-            if (n + 1 < a.NC)
+            if (n + 1 < n1)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf0, wave, lane);
         }
     }
 
-    state_store_o<E, D, C, BV>(a, sOw, b, h, slice, a.NC - 1, lane, wave);
+    state_store_o<E, D, C, BV>(a, sOw, b, h, slice, n1 - 1, lane, wave);
 
-    if (a.S_out) {
+    if (a.S_out && n1 == a.NC) {
         float* so = a.S_out + bh * D * D;
 #pragma unroll
         for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 so[(16 * kt + 4 * gq + i) * D + col] = St[kt][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-level scan over the chunks, for few (sequence, head) pairs and many
+// chunks, where one pass over the chunks would leave most CUs idle.  A chunk
+// step is affine in the state: S_next = A S + B with A = diag(gamma) - K^T W
+// and B = K^T U~.  The chunks of a sequence are cut into nseg segments of
+// seg_len chunks (the last may be shorter):
+//   span  every segment but the last, in parallel: the product of its
+//         chunks' A (carried from the identity, as D more state columns)
+//         and its local state (carried from zero; from S0 for segment 0,
+//         which then holds the true state at the start of segment 1);
+//   fold  per (sequence, head), over the segments in order: start of
+//         segment j+1 = (product of segment j) (start of segment j) + (local
+//         state of segment j), in fp32, written over the local state;
+//   state the chunk pass above, every segment in parallel from its start.
+// The span pass runs the same chunk step as the state pass without the
+// outputs, so it needs only -W, K^T, gamma (and U~ for local-state columns).
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C>
+struct SpanShape {
+    typedef Frags<E, D, C> F;
+    static constexpr size_t OFF_W = 0;
+    static constexpr size_t OFF_KT = OFF_W + F::W_BYTES;
+    static constexpr size_t OFF_G = OFF_KT + F::K_BYTES;
+    static constexpr size_t BUF = OFF_G + (size_t)D * 4;
+    static_assert(2 * BUF <= 80 * 1024, "two workgroups per CU");
+};
+
+// Four U~ values of one accumulator tile, held raw until they are used so
+// that the load of the next chunk's values stays in flight.
+template <typename E> struct Quad;
+template <> struct Quad<bf16> {
+    typedef u32x2 Raw;
+    static __device__ __forceinline__ Raw load(const bf16* p) { return *reinterpret_cast<const u32x2*>(p); }
+    static __device__ __forceinline__ f32x4 cvt(Raw r) {
+        return f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                     __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
+    }
+};
+template <> struct Quad<float> {
+    typedef f32x4 Raw;
+    static __device__ __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    static __device__ __forceinline__ f32x4 cvt(Raw r) { return r; }
+};
+
+template <typename E, int D, int C>
+__device__ __forceinline__ void span_fetch(const StateArgs& a, int64_t rec, unsigned char* buf, int wave, int lane)
+{
+    typedef SpanShape<E, D, C> S;
+    typedef Frags<E, D, C> F;
+    copy_linear<F::W_BYTES>((const unsigned char*)a.Wn + rec * F::W_BYTES, buf + S::OFF_W, wave, lane);
+    copy_linear<F::K_BYTES>((const unsigned char*)a.Kh + rec * F::K_BYTES, buf + S::OFF_KT, wave, lane);
+    if (wave == (NT / 64) - 1 && lane < D / 4)
+        __builtin_amdgcn_global_load_lds(a.gam + rec * D + lane * 4, (lds_void*)(buf + S::OFF_G), 16, 0, 0);
+}
+
+// One chunk step without outputs: Delta = U~ - W X, X <- diag(gamma) X + K^T Delta.
+template <typename E, int D, int C>
+__device__ __forceinline__ void span_compute(const unsigned char* buf, const f32x4* uc, f32x4* St, int lane)
+{
+    typedef SpanShape<E, D, C> S;
+    typedef Frags<E, D, C> F;
+    typedef Mma<E> MM;
+    typedef typename MM::Frag Frag;
+    constexpr int NB = F::NB, KT = F::KT, NKS = F::NKS, NKC = F::NKC, KTS = D / 16;
+    const int gq = lane >> 4;
+    const unsigned char* fl = buf + lane * 16;
+    auto frag = [&](size_t off, int i) -> Frag { return *reinterpret_cast<const Frag*>(fl + off + i * F::FRAG); };
+    const float* sGam = reinterpret_cast<const float*>(buf + S::OFF_G);
+
+    Frag SB[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        SB[ks] = MM::from_acc(&St[ks * KT]);
+    f32x4 dl[NB];
+    {
+        Frag aw[NB][NKS];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                aw[mt][ks] = frag(S::OFF_W, mt * NKS + ks);
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            dl[mt] = uc[mt];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+                dl[mt] = MM::mma(aw[mt][ks], SB[ks], dl[mt]);
+        sched_pipeline<NB * NKS>();
+    }
+    Frag DB[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        DB[kc] = MM::from_acc(&dl[kc * KT]);
+    {
+        Frag ak[KTS][NKC];
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+                ak[kt][kc] = frag(S::OFF_KT, kt * NKC + kc);
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+            St[kt] = St[kt] * *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * gq);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int kt = 0; kt < KTS; ++kt)
+                St[kt] = MM::mma(ak[kt][kc], DB[kc], St[kt]);
+        sched_pipeline<KTS * NKC>();
+    }
+}
+
+// Workgroup -> (sequence*head, segment j < nseg - 1, column slice): slices
+// 0 .. NS-1 carry the chunk product's columns, NS .. 2NS-1 the local state's.
+template <typename E, int D, int C, int BV>
+__global__ __launch_bounds__(NT, 2) void chunk_span_kernel(StateArgs a)
+{
+    typedef SpanShape<E, D, C> S;
+    typedef Frags<E, D, C> F;
+    typedef Quad<E> Q;
+    constexpr int NS = D / BV, NB = F::NB, KTS = D / 16;
+    constexpr size_t U_SLICE = (size_t)(BV / 16) * NB * F::TILE_U;
+    __shared__ __align__(16) unsigned char buf[2][S::BUF];
+
+    const int64_t bx = blockIdx.x;
+    const int64_t grp = bx / (8 * 2 * NS);
+    const int within = (int)(bx % (8 * 2 * NS));
+    const int slice = within / 8;
+    const int64_t unit = grp * 8 + within % 8;       // (b*H + h) * (nseg - 1) + j
+    const int64_t nspan = a.nseg - 1;
+    if (unit >= a.nbh * nspan)
+        return;
+    const int64_t bh = unit / nspan, j = unit - bh * nspan;
+    const bool local = slice >= NS;
+    if (j == 0 && !local)
+        return;                                      // segment 0 needs no product
+    const int vs = local ? slice - NS : slice;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int col = vs * BV + 16 * wave + cl;
+
+    f32x4 St[KTS];
+    const float* s0 = (local && j == 0 && a.S0) ? a.S0 + bh * D * D : nullptr;
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * kt + 4 * gq + i;
+            St[kt][i] = s0 ? s0[row * D + col] : (!local && row == col ? 1.f : 0.f);
+        }
+
+    const int64_t rec0 = bh * a.NC + j * a.seg_len;
+    // this lane's U~ values: value tile (vs, wave), row tiles 0 .. NB-1
+    const E* ub = reinterpret_cast<const E*>((const unsigned char*)a.Ut + vs * U_SLICE +
+                                             (size_t)wave * NB * F::TILE_U) + lane * 4;
+    typename Q::Raw ur[NB];
+    span_fetch<E, D, C>(a, rec0, buf[0], wave, lane);
+    if (local) {
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            ur[mt] = Q::load(ub + rec0 * (F::U_BYTES / sizeof(E)) + mt * (F::TILE_U / sizeof(E)));
+    }
+    for (int64_t i = 0; i < a.seg_len; ++i) {
+        wait_copies();
+        __syncthreads();              // chunk i is in buf[i&1]; everyone is done with the other
+        f32x4 uc[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            uc[mt] = local ? Q::cvt(ur[mt]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (i + 1 < a.seg_len) {
+            const int64_t rec = rec0 + i + 1;
+            span_fetch<E, D, C>(a, rec, buf[(i + 1) & 1], wave, lane);
+            if (local) {
+#pragma unroll
+                for (int mt = 0; mt < NB; ++mt)
+                    ur[mt] = Q::load(ub + rec * (F::U_BYTES / sizeof(E)) + mt * (F::TILE_U / sizeof(E)));
+            }
+        }
+        span_compute<E, D, C>(buf[i & 1], uc, St, lane);
+    }
+
+    float* dst = a.span + ((bh * nspan + j) * 2 + (local ? 1 : 0)) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dst[(16 * kt + 4 * gq + i) * D + col] = St[kt][i];
+}
+
+// Start states of segments 2 .. nseg-1, in order: for j = 1 .. nseg-2,
+// X <- Pi_j X + L_j (X starts as the true state at the start of segment 1,
+// which the span pass left in L_0), written over L_j.  Workgroup ->
+// (sequence*head, 16 state columns); fp32 throughout.
+template <int D>
+__global__ __launch_bounds__(256) void span_fold_kernel(float* span, int64_t nbh, int64_t nseg)
+{
+    constexpr int TPR = 256 / D, CPT = 16 / TPR;     // threads per row, columns per thread
+    __shared__ __align__(16) float sX[D * 16];
+    const int64_t bh = blockIdx.x / (D / 16);
+    const int cb = (int)(blockIdx.x % (D / 16));
+    if (bh >= nbh)
+        return;
+    const int t = threadIdx.x, r = t / TPR, c0 = (t % TPR) * CPT;
+    const int64_t nspan = nseg - 1;
+    float* base = span + bh * nspan * 2 * D * D;
+    const int64_t off = (int64_t)r * D + cb * 16 + c0;   // this thread's outputs in a D x D matrix
+
+    float x[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+        x[c] = base[D * D + off + c];
+    for (int64_t j = 1; j < nspan; ++j) {
+        __syncthreads();              // the previous fold's reads of sX are done
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+            sX[r * 16 + c0 + c] = x[c];
+        __syncthreads();
+        const float* Pi = base + j * 2 * D * D;
+        float* L = base + (j * 2 + 1) * D * D;
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+            acc[c] = L[off + c];
+        const f32x4* prow = reinterpret_cast<const f32x4*>(Pi + (int64_t)r * D);
+#pragma unroll 4
+        for (int k4 = 0; k4 < D / 4; ++k4) {
+            const f32x4 p = prow[k4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    acc[c] = fmaf(p[kk], sX[(4 * k4 + kk) * 16 + c0 + c], acc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            L[off + c] = acc[c];
+            x[c] = acc[c];
+        }
     }
 }
 
@@ -1529,13 +1782,44 @@ hipError_t launch_prep(const PrepArgs& pa, int64_t grid, hipStream_t stream)
     return hipSuccess;
 }
 
+// Segments of the two-level scan.  One pass runs B*H*D/64 workgroups for NC
+// chunk steps each; nseg segments run about twice the chunk steps in all but
+// only ~2*NC/nseg in sequence, so they pay when the one pass fills less than
+// a quarter of the CUs.  AUTO cuts the chunks into as many segments as one
+// wave of state workgroups fills the CUs with (at least 4 chunks each);
+// SEGMENTED always uses at least two.
+struct SegPlan {
+    int64_t nseg, len;
+};
+
+SegPlan seg_plan(const gdr2_fwd_args& a)
+{
+    const int64_t NC = ceil_div(a.T, a.chunk), wgs = a.B * a.H * (a.Dk / 64);
+    SegPlan p{1, NC};
+    if (a.algo == GDR2_ALGO_STAGED || NC < 2 || wgs == 0)
+        return p;
+    const int64_t fill = (int64_t)cu_count() / wgs;
+    int64_t n;
+    if (a.algo == GDR2_ALGO_SEGMENTED) {
+        n = std::max<int64_t>(2, std::min(fill, NC));
+    } else {
+        n = std::min(fill, NC / 4);
+        if (n < 4)
+            return p;
+    }
+    p.len = ceil_div(NC, n);
+    p.nseg = ceil_div(NC, p.len);
+    return p;
+}
+
 template <typename E, int D, int C>
 hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
 {
     constexpr int BV = 64;
     typedef PrepShape<E, D, C> PS;
     typedef StateShape<E, D, C, BV> SS;
-    const Layout L = staged_layout(a.B, a.H, a.T, D, C, (int)sizeof(E));
+    const SegPlan sp = seg_plan(a);
+    const Layout L = staged_layout(a.B, a.H, a.T, D, C, (int)sizeof(E), sp.nseg);
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
 
     PrepArgs pa;
@@ -1578,7 +1862,16 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     sa.Wn = pa.Wn; sa.Ut = pa.Ut; sa.Kh = pa.Kh; sa.Qt = pa.Qt; sa.P = pa.P; sa.gam = pa.gam;
     sa.S0 = a.S0; sa.S_out = a.S_out; sa.S_chunks = a.S_chunks; sa.o = a.o;
     sa.T = a.T; sa.H = a.H; sa.NC = pa.NC; sa.nbh = a.B * a.H;
-    const int64_t grid2 = ceil_div(sa.nbh, 8) * 8 * SS::NS;
+    sa.nseg = sp.nseg; sa.seg_len = sp.len;
+    sa.span = sp.nseg > 1 ? reinterpret_cast<float*>(ws + L.span) : nullptr;
+    if (sp.nseg > 1) {
+        const int64_t gs = ceil_div(sa.nbh * (sp.nseg - 1), 8) * 8 * 2 * SS::NS;
+        hipLaunchKernelGGL((chunk_span_kernel<E, D, C, BV>), dim3((unsigned)gs), dim3(NT), 0, stream, sa);
+        if (sp.nseg > 2)
+            hipLaunchKernelGGL((span_fold_kernel<D>), dim3((unsigned)(sa.nbh * (D / 16))), dim3(256), 0, stream,
+                               sa.span, sa.nbh, sp.nseg);
+    }
+    const int64_t grid2 = ceil_div(sa.nbh * sp.nseg, 8) * 8 * SS::NS;
     hipLaunchKernelGGL((chunk_state_kernel<E, D, C, BV>), dim3((unsigned)grid2), dim3(NT), 0, stream, sa);
     return hipGetLastError();
 }
@@ -1589,7 +1882,7 @@ size_t staged_workspace_bytes(const gdr2_fwd_args& a)
 {
     if (a.B * a.H * a.T == 0)
         return 0;
-    return staged_layout(a.B, a.H, a.T, (int)a.Dk, a.chunk, a.dtype == GDR2_BF16 ? 2 : 4).total;
+    return staged_layout(a.B, a.H, a.T, (int)a.Dk, a.chunk, a.dtype == GDR2_BF16 ? 2 : 4, seg_plan(a).nseg).total;
 }
 
 hipError_t launch_forward_staged(const gdr2_fwd_args& a, hipStream_t stream)

@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libgdr2.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 PROLOGUE_NORM_QK, PROLOGUE_GATES = 1, 2
-ALGO_AUTO, ALGO_STAGED = 0, 1
-ALGOS = {"auto": ALGO_AUTO, "staged": ALGO_STAGED}
+ALGO_AUTO, ALGO_STAGED, ALGO_SEGMENTED = 0, 1, 2
+ALGOS = {"auto": ALGO_AUTO, "staged": ALGO_STAGED, "segmented": ALGO_SEGMENTED}
 STAGES = {"all": 0, "prep": 1, "state": 2}
 
 _c_i64 = ctypes.c_int64

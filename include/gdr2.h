@@ -102,9 +102,19 @@ typedef enum gdr2_prologue {
 /* Algorithm of the chunked forward. */
 typedef enum gdr2_algo {
     GDR2_ALGO_AUTO = 0,    /* the library picks */
-    GDR2_ALGO_STAGED = 1   /* intra-chunk kernel writes per-chunk factors to the
+    GDR2_ALGO_STAGED = 1,  /* intra-chunk kernel writes per-chunk factors to the
                               workspace; a propagation kernel carries the state
                               through the chunks and writes o */
+    GDR2_ALGO_SEGMENTED = 2 /* STAGED with the chunks of each sequence cut into
+                              segments that run in parallel: a span kernel
+                              forms each segment's chunk product and local
+                              state, a fold kernel chains the segments' start
+                              states, and the propagation kernel runs every
+                              segment from its start (a two-level scan of the
+                              chunk recurrence, for few sequences x heads and
+                              many chunks).  AUTO takes it when one pass would
+                              leave most of the GPU idle.  Same results as
+                              STAGED up to rounding order. */
 } gdr2_algo;
 
 /* Which kernels of GDR2_ALGO_STAGED one call runs.  Two calls on the same

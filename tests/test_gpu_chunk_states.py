@@ -16,22 +16,25 @@ pytestmark = pytest.mark.gpu
 NAMES = ("q", "k", "v", "b", "w", "g")
 
 CASES = [
-    # name, B, T, H, D, dtype, chunk, S0 std
-    ("f32_d64_c32", 1, 100, 2, 64, "f32", 32, 0.05),
-    ("f32_d64_c64", 2, 130, 1, 64, "f32", 64, 0.0),
-    ("bf16_d128_c64_ragged", 2, 150, 2, 128, "bf16", 64, 0.05),
-    ("bf16_d128_c32", 1, 96, 3, 128, "bf16", 32, 0.02),
-    ("bf16_d64_c64", 1, 64, 2, 64, "bf16", 64, 0.05),
+    # name, B, T, H, D, dtype, chunk, S0 std, algo
+    ("f32_d64_c32", 1, 100, 2, 64, "f32", 32, 0.05, "auto"),
+    ("f32_d64_c64", 2, 130, 1, 64, "f32", 64, 0.0, "auto"),
+    ("bf16_d128_c64_ragged", 2, 150, 2, 128, "bf16", 64, 0.05, "auto"),
+    ("bf16_d128_c32", 1, 96, 3, 128, "bf16", 32, 0.02, "auto"),
+    ("bf16_d64_c64", 1, 64, 2, 64, "bf16", 64, 0.05, "auto"),
+    # two-level scan: every segment emits its own chunks' starts
+    ("bf16_d128_c64_segmented", 2, 700, 2, 128, "bf16", 64, 0.05, "segmented"),
+    ("f32_d64_c32_segmented", 1, 300, 2, 64, "f32", 32, 0.0, "segmented"),
 ]
 
 
-@pytest.mark.parametrize("name,B,T,H,D,dtype,chunk,s0", CASES, ids=[c[0] for c in CASES])
-def test_chunk_states_match_oracle_checkpoints(name, B, T, H, D, dtype, chunk, s0):
+@pytest.mark.parametrize("name,B,T,H,D,dtype,chunk,s0,algo", CASES, ids=[c[0] for c in CASES])
+def test_chunk_states_match_oracle_checkpoints(name, B, T, H, D, dtype, chunk, s0, algo):
     inp = draw(Workload(name, "forward", B, T, H, D, dtype, "full", s0, chunk, 401))
     d = to_dev(inp)
     args = [d[n] for n in NAMES]
-    o, S, ck = gdr2.forward(*args, S0=d["S0"], chunk=chunk, chunk_states=True)
-    o0, S0f = gdr2.forward(*args, S0=d["S0"], chunk=chunk)
+    o, S, ck = gdr2.forward(*args, S0=d["S0"], chunk=chunk, chunk_states=True, algo=algo)
+    o0, S0f = gdr2.forward(*args, S0=d["S0"], chunk=chunk, algo=algo)
     torch.cuda.synchronize()
     NC = -(-T // chunk)
     assert ck.shape == (B, H, NC, D, D)

@@ -175,11 +175,60 @@ def test_long_64k_workload_sampled_heads():
           [float(per_chunk[:, i * q:(i + 1) * q].max()) for i in range(4)], flush=True)
 
 
-def test_weak_decay_long_sequence():
+@pytest.mark.parametrize("algo", ["staged", "auto"])
+def test_weak_decay_long_sequence(algo):
     """g scaled by 0.01: memory spans thousands of tokens, so the state carries
-    the accumulated chunk updates; the error must not grow past tolerance."""
+    the accumulated chunk updates; the error must not grow past tolerance.
+    With 2 heads and 128 chunks, AUTO takes the two-level scan (on 256 CUs:
+    32 segments of 4 chunks), whose segment products are far from zero here."""
     wl = Workload("weak", "forward", 1, 8192, 2, 128, "bf16", "full", 0.02, 64, 4321, g_scale=0.01)
-    check(draw(wl), 64, "bf16", "weak decay T=8192")
+    check(draw(wl), 64, "bf16", f"weak decay T=8192 {algo}", algo=algo)
+
+
+# Two-level scan forced on small shapes.  Segment plans on 256 CUs:
+# 4 segments of 3 chunks (the last of 2), one chunk per segment, 2 per
+# segment with a 1-chunk tail, and so on.
+SEG_CASES = [
+    # name, B, T, H, D, dtype, chunk, S0 std, gates
+    ("bf16_d128_c64_len3", 4, 647, 8, 128, "bf16", 64, 0.05, "full"),
+    ("f32_d64_c32_len1", 1, 333, 2, 64, "f32", 32, 0.05, "full"),
+    ("bf16_d64_c32_len2", 2, 2000, 3, 64, "bf16", 32, 0.02, "full"),
+    ("f32_d128_c32_len1", 1, 500, 1, 128, "f32", 32, 0.0, "full"),
+    ("bf16_d128_c32_len2", 1, 1500, 4, 128, "bf16", 32, 0.05, "scalar"),
+    ("f32_d64_c64_len1", 1, 700, 3, 64, "f32", 64, 0.05, "full"),
+    ("bf16_d128_c64_two_chunks", 1, 100, 1, 128, "bf16", 64, 0.05, "full"),
+]
+
+
+@pytest.mark.parametrize("name,B,T,H,D,dtype,chunk,s0,gates", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_segmented_matches_oracle(name, B, T, H, D, dtype, chunk, s0, gates):
+    wl = Workload(name, "forward", B, T, H, D, dtype, gates, s0, chunk, 5000 + T)
+    check(draw(wl), chunk, dtype, f"segmented {name}", algo="segmented")
+
+
+def test_segmented_weak_decay_products():
+    """g scaled by 0.005 over 40 chunks in 40 one-chunk segments: every segment
+    start is a fold of many nearly undecayed chunk products."""
+    wl = Workload("weak_seg", "forward", 1, 2560, 1, 64, "f32", "full", 0.05, 64, 4322, g_scale=0.005)
+    check(draw(wl), 64, "f32", "segmented weak decay", algo="segmented")
+
+
+def test_segmented_stage_split_and_determinism():
+    """PREP then STATE equals one call bit for bit on the segmented path, and
+    two calls agree bit for bit."""
+    wl = Workload("seg_stages", "forward", 1, 1000, 2, 128, "bf16", "full", 0.05, 64, 13)
+    d = to_dev(draw(wl))
+    args = [d[n] for n in NAMES]
+    o1, S1 = gdr2.forward(*args, S0=d["S0"], chunk=64, algo="segmented")
+    o3, S3 = gdr2.forward(*args, S0=d["S0"], chunk=64, algo="segmented")
+    ws = torch.empty(gdr2.workspace_size(*args, chunk=64, algo="segmented"), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    S2 = torch.empty_like(S1)
+    gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="prep", algo="segmented")
+    gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="state", algo="segmented")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o1, o3) and torch.equal(S1, S3)
 
 
 def test_stage_split_equals_one_call():
