@@ -11,8 +11,9 @@ Prints one JSON line: tokens/s (B*T per step time), the roofline of the
 dominant kernel (HIP events on the launch stream, algorithmic bytes per
 launch), the fp64 CPU oracle on the host cores, and in "extra" the per-kernel
 split, the MFMA fraction, the batched decode step (256 x 16 states,
-1000 steps) in GB/s, the forward for each gate-width mix and the chunked
-backward over the same batch.
+1000 steps) in GB/s, the forward for each gate-width mix, the chunked
+backward over the same batch and the long-context forward (one sequence of
+65536 tokens, two-level scan beside one pass).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -247,6 +248,45 @@ def bench_decode(torch, gdr2, lib, steps: int, warmup: int):
             "GBps": byts / (us * 1e-6) / 1e9, "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_long(torch, gdr2, lib, steps: int, warmup: int, algos=("auto", "staged"), stages=("all", "state")):
+    """The long-context forward: one sequence of 65536 tokens, 16 heads,
+    d = 128, bf16, S0 ~ N(0, 0.02^2).  One pass over the 1024 chunks runs only
+    32 state workgroups; the library's default here is the two-level scan over
+    chunk segments.  Both are timed, with the state stage alone."""
+    from gated_delta_rule_86_amd.inputs import WORKLOADS, draw
+
+    wl = WORKLOADS["long_64k"]
+    inp = draw(wl)
+    d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    x = [d[n] for n in NAMES]
+    o = torch.empty_like(d["v"])
+    S_out = torch.empty((wl.B, wl.H, wl.D, wl.D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"workload": "long_64k: B=1 H=16 T=65536 d=128 bf16, per-channel gates, chunk 64, S0"}
+    for algo in algos:
+        ws = torch.empty(gdr2.workspace_size(*x, chunk=64, algo=algo), dtype=torch.uint8, device="cuda")
+        for stage in stages:
+            a = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=64, workspace=ws, stage=stage, algo=algo)
+            for _ in range(warmup):
+                assert lib.gdr2_forward_chunked(ctypes.byref(a), stream) == 0
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                lib.gdr2_forward_chunked(ctypes.byref(a), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            key = ("segmented" if algo == "auto" else "one_pass") + ("" if stage == "all" else "_state_stage")
+            res[key + "_ms"] = round(ms, 4)
+            if stage == "all":
+                res[key + "_tokens_per_s"] = round(wl.B * wl.T / (ms * 1e-3), 1)
+        del ws
+    del d, x, o, S_out
+    torch.cuda.empty_cache()
+    return res
+
+
 COPY_BYTES = 1 << 30
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_train_4k.md")
 
@@ -282,6 +322,10 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-gate-widths", action="store_true", help="skip the gate-width sweep")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy bandwidth reference")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context forward")
+    ap.add_argument("--long-only", action="store_true",
+                    help="time only the long-context forward and print its JSON object (for a profile of "
+                         "those kernels alone)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -298,6 +342,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lib = gdr2.load_library()
+    if args.long_only:
+        # the library's default algorithm only, whole calls: one kernel of each kind per call
+        res = bench_long(torch, gdr2, lib, args.steps, args.warmup, algos=("auto",), stages=("all",))
+        print(json.dumps({"long_context": res}), flush=True)
+        return
     wl = WORKLOADS["train_4k"]
     inp = draw(wl)
     d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
@@ -392,6 +441,8 @@ def main():
 
     del d, x, o, S_out, ws
     torch.cuda.empty_cache()
+    if not args.no_long:
+        extra["long_context"] = bench_long(torch, gdr2, lib, max(1, K // 2), 5)
     if not args.no_copy:
         extra["plain_copy"] = plain_copy(torch)
         pc = extra["plain_copy"]["GBps"]

@@ -1647,14 +1647,21 @@ __global__ __launch_bounds__(NT, 2) void chunk_span_kernel(StateArgs a)
     const int col = vs * BV + 16 * wave + cl;
 
     f32x4 St[KTS];
-    const float* s0 = (local && j == 0 && a.S0) ? a.S0 + bh * D * D : nullptr;
+    if (local && j == 0 && a.S0) {
+        const float* s0 = a.S0 + bh * D * D;
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt)
+        for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * kt + 4 * gq + i;
-            St[kt][i] = s0 ? s0[row * D + col] : (!local && row == col ? 1.f : 0.f);
-        }
+            for (int i = 0; i < 4; ++i)
+                St[kt][i] = s0[(16 * kt + 4 * gq + i) * D + col];
+    } else {
+        const float one = local ? 0.f : 1.f;    // identity for the product, zero for the local state
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                St[kt][i] = 16 * kt + 4 * gq + i == col ? one : 0.f;
+    }
 
     const int64_t rec0 = bh * a.NC + j * a.seg_len;
     // this lane's U~ values: value tile (vs, wave), row tiles 0 .. NB-1
@@ -1697,52 +1704,109 @@ __global__ __launch_bounds__(NT, 2) void chunk_span_kernel(StateArgs a)
 // Start states of segments 2 .. nseg-1, in order: for j = 1 .. nseg-2,
 // X <- Pi_j X + L_j (X starts as the true state at the start of segment 1,
 // which the span pass left in L_0), written over L_j.  Workgroup ->
-// (sequence*head, 16 state columns); fp32 throughout.
+// (sequence*head, 16 state columns); the D/16 workgroups of one (b,h) share
+// blockIdx % 8 (one XCD, one L2 for the products they all read).  fp32 MFMA:
+// wave w computes row tiles NRT*w .. NRT*w+NRT-1 of Pi_j X with X's column
+// tiles as B operands straight from accumulator layout; the new X goes
+// round through LDS so that every wave holds all of it.  The operands of
+// the next two folds are in flight while one fold computes.
+template <int D>
+struct FoldOps {
+    static constexpr int KTS = D / 16, NRT = KTS / 4;
+    f32x4 A[NRT][KTS];      // rows of Pi_j: (row tile, 16-wide k block)
+    f32x4 L[NRT];           // L_j at this lane's output positions
+};
+
+template <int D>
+__device__ __forceinline__ void fold_load(FoldOps<D>& op, const float* base, int64_t j, int wave, int lane, int col)
+{
+    typedef Mma<float> MM;
+    constexpr int KTS = FoldOps<D>::KTS, NRT = FoldOps<D>::NRT;
+    const float* Pi = base + j * 2 * D * D;
+    const float* L = Pi + D * D;
+    const int gq = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) {
+        const int mt = wave * NRT + r;
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+            op.A[r][kt] = MM::load(Pi + 16 * mt * D + 16 * kt, D, lane);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            op.L[r][x] = L[(16 * mt + 4 * gq + x) * D + col];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void fold_step(const FoldOps<D>& op, f32x4* X, f32x4 (*sX)[64], float* base, int64_t j,
+                                          int wave, int lane, int col)
+{
+    typedef Mma<float> MM;
+    constexpr int KTS = FoldOps<D>::KTS, NRT = FoldOps<D>::NRT;
+    const int gq = lane >> 4;
+    f32x4 acc[NRT];
+#pragma unroll
+    for (int r = 0; r < NRT; ++r)
+        acc[r] = op.L[r];
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+            acc[r] = MM::mma(op.A[r][kt], MM::from_acc(&X[kt]), acc[r]);
+    float* L = base + (j * 2 + 1) * D * D;
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) {
+        const int mt = wave * NRT + r;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            L[(16 * mt + 4 * gq + x) * D + col] = acc[r][x];
+        sX[mt][lane] = acc[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt)
+        X[kt] = sX[kt][lane];
+    __syncthreads();              // sX is rewritten by the next fold
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void span_fold_kernel(float* span, int64_t nbh, int64_t nseg)
 {
-    constexpr int TPR = 256 / D, CPT = 16 / TPR;     // threads per row, columns per thread
-    __shared__ __align__(16) float sX[D * 16];
-    const int64_t bh = blockIdx.x / (D / 16);
-    const int cb = (int)(blockIdx.x % (D / 16));
+    constexpr int KTS = D / 16, NCB = D / 16;
+    static_assert(KTS % 4 == 0, "row tiles split over 4 waves");
+    __shared__ __align__(16) f32x4 sX[KTS][64];
+    const int64_t bx = blockIdx.x;
+    const int64_t grp = bx / (8 * NCB);
+    const int within = (int)(bx % (8 * NCB));
+    const int cb = within / 8;
+    const int64_t bh = grp * 8 + within % 8;
     if (bh >= nbh)
         return;
-    const int t = threadIdx.x, r = t / TPR, c0 = (t % TPR) * CPT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, gq = lane >> 4, cl = lane & 15;
+    const int col = cb * 16 + cl;
     const int64_t nspan = nseg - 1;
     float* base = span + bh * nspan * 2 * D * D;
-    const int64_t off = (int64_t)r * D + cb * 16 + c0;   // this thread's outputs in a D x D matrix
 
-    float x[CPT];
+    f32x4 X[KTS];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-        x[c] = base[D * D + off + c];
-    for (int64_t j = 1; j < nspan; ++j) {
-        __syncthreads();              // the previous fold's reads of sX are done
+    for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c)
-            sX[r * 16 + c0 + c] = x[c];
-        __syncthreads();
-        const float* Pi = base + j * 2 * D * D;
-        float* L = base + (j * 2 + 1) * D * D;
-        float acc[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c)
-            acc[c] = L[off + c];
-        const f32x4* prow = reinterpret_cast<const f32x4*>(Pi + (int64_t)r * D);
-#pragma unroll 4
-        for (int k4 = 0; k4 < D / 4; ++k4) {
-            const f32x4 p = prow[k4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int c = 0; c < CPT; ++c)
-                    acc[c] = fmaf(p[kk], sX[(4 * k4 + kk) * 16 + c0 + c], acc[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            L[off + c] = acc[c];
-            x[c] = acc[c];
-        }
+        for (int x = 0; x < 4; ++x)
+            X[kt][x] = base[D * D + (16 * kt + 4 * gq + x) * D + col];
+    FoldOps<D> op0, op1;
+    if (nspan > 1)
+        fold_load<D>(op0, base, 1, wave, lane, col);
+    if (nspan > 2)
+        fold_load<D>(op1, base, 2, wave, lane, col);
+    for (int64_t j = 1; j < nspan; j += 2) {
+        fold_step<D>(op0, X, sX, base, j, wave, lane, col);
+        if (j + 2 < nspan)
+            fold_load<D>(op0, base, j + 2, wave, lane, col);
+        if (j + 1 >= nspan)
+            break;
+        fold_step<D>(op1, X, sX, base, j + 1, wave, lane, col);
+        if (j + 3 < nspan)
+            fold_load<D>(op1, base, j + 3, wave, lane, col);
     }
 }
 
@@ -1868,8 +1932,8 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
         const int64_t gs = ceil_div(sa.nbh * (sp.nseg - 1), 8) * 8 * 2 * SS::NS;
         hipLaunchKernelGGL((chunk_span_kernel<E, D, C, BV>), dim3((unsigned)gs), dim3(NT), 0, stream, sa);
         if (sp.nseg > 2)
-            hipLaunchKernelGGL((span_fold_kernel<D>), dim3((unsigned)(sa.nbh * (D / 16))), dim3(256), 0, stream,
-                               sa.span, sa.nbh, sp.nseg);
+            hipLaunchKernelGGL((span_fold_kernel<D>), dim3((unsigned)(ceil_div(sa.nbh, 8) * 8 * (D / 16))), dim3(256),
+                               0, stream, sa.span, sa.nbh, sp.nseg);
     }
     const int64_t grid2 = ceil_div(sa.nbh * sp.nseg, 8) * 8 * SS::NS;
     hipLaunchKernelGGL((chunk_state_kernel<E, D, C, BV>), dim3((unsigned)grid2), dim3(NT), 0, stream, sa);

@@ -26,6 +26,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 # Kernel-name fragments -> short names used in the summaries and bench.py.
 KERNELS = (("chunk_prep_kernel", "gdr2_chunk_prep"), ("chunk_state_kernel", "gdr2_chunk_state"),
+           ("chunk_span_kernel", "gdr2_chunk_span"), ("span_fold_kernel", "gdr2_span_fold"),
            ("decode_step_kernel", "gdr2_decode_step"), ("bwd_prep_kernel", "gdr2_bwd_prep"),
            ("bwd_dout_kernel", "gdr2_bwd_dout"), ("bwd_frag_kernel", "gdr2_bwd_frag"),
            ("bwd_scan_kernel", "gdr2_bwd_scan"), ("bwd_sgrad", "gdr2_bwd_sgrad"),

@@ -168,6 +168,37 @@ def test_workspace_size_formula(lib):
     assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == 0
 
 
+def test_segmented_workspace_size(lib):
+    """The two-level scan adds two D x D fp32 matrices per (b, h) and per
+    segment but the last.  Plans on a 256-CU device (the host without a GPU
+    counts 256): one (b, h) at d = 128 runs 2 state workgroups per pass, so
+    AUTO cuts 100 chunks into 25 segments of 4 (at least 4 chunks each),
+    SEGMENTED into 100 of 1; STAGED never segments.  Few chunks or many
+    sequences x heads keep AUTO on one pass."""
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def size(algo, **kw):
+        a = good_fwd(**kw)
+        a.algo = algo
+        return lib.gdr2_forward_workspace_size(ctypes.byref(a))
+
+    shape = dict(B=1, T=6400, H=1, D=128)
+    base = size(gdr2.ALGO_STAGED, **shape)
+    assert size(gdr2.ALGO_AUTO, **shape) == base + al(24 * 2 * 128 * 128 * 4)
+    assert size(gdr2.ALGO_SEGMENTED, **shape) == base + al(99 * 2 * 128 * 128 * 4)
+    # 4 (b, h) at d = 64: 4 workgroups per pass; AUTO 25 segments of 4, SEGMENTED asks for 64
+    # and gets 50 of 2 chunks
+    shape = dict(B=2, T=6400, H=2, D=64)
+    base = size(gdr2.ALGO_STAGED, **shape)
+    assert size(gdr2.ALGO_AUTO, **shape) == base + al(4 * 24 * 2 * 64 * 64 * 4)
+    assert size(gdr2.ALGO_SEGMENTED, **shape) == base + al(4 * 49 * 2 * 64 * 64 * 4)
+    for kw in (dict(B=1, T=12 * 64, H=1, D=128),        # 12 chunks: 3 segments < 4
+               dict(B=8, T=4096, H=16, D=128)):         # 256 workgroups already
+        assert size(gdr2.ALGO_AUTO, **kw) == size(gdr2.ALGO_STAGED, **kw)
+    assert size(gdr2.ALGO_SEGMENTED, B=1, T=64, H=1, D=128) == size(gdr2.ALGO_STAGED, B=1, T=64, H=1, D=128)
+
+
 def test_forward_empty_is_a_noop(lib):
     # nothing to compute and no state to write: OK without any launch
     for kw in (dict(B=0), dict(H=0)):
