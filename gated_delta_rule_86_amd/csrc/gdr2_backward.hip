@@ -209,6 +209,118 @@ __device__ __forceinline__ f32x4 gate4(const T* p, int width, int64_t row, int i
     return load4(p + row * (int64_t)width + i);
 }
 
+// Four consecutive elements in their storage type, converted at use.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+    typedef f32x4 V;
+    static __device__ __forceinline__ f32x4 cvt(V v) { return v; }
+};
+template <> struct Raw4<bf16> {
+    typedef bf16x4 V;
+    static __device__ __forceinline__ f32x4 cvt(V v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
+};
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::V ld_raw4(const T* p) { return *reinterpret_cast<const typename Raw4<T>::V*>(p); }
+__device__ __forceinline__ f32x4 bcast4(float x) { return f32x4{x, x, x, x}; }
+
+// bwd_prep step 1 for one gate-width mix (B1, W1, G1: b, w, g of width 1):
+// the chunk's raw rows into LDS (G, k, q, e = b*k) and U = w*v to the
+// workspace, 4 channels per item.  Every item's loads are issued before
+// any is used; rows past the valid length re-read the last valid row and
+// are zeroed at use.  Returns whether a valid log-decay is positive.
+template <bool B1, bool W1, bool G1, typename E, int D>
+__device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_t r, int tid, float* sm, float* sRN)
+{
+    typedef BwdPrepShape<D> PS;
+    typedef Raw4<E> R;
+    constexpr int C = BC, LD = PS::LD, Q4 = D / 4, NIT = C * Q4 / NTP;
+    static_assert(C * Q4 % NTP == 0, "whole items per thread");
+    const E* q = (const E*)a.q;
+    const E* k = (const E*)a.k;
+    const E* v = (const E*)a.v;
+    const E* b = (const E*)a.b;
+    const E* w = (const E*)a.w;
+    float* ws = a.ws;
+    const size_t cdo = (size_t)r * C * D;
+
+    typename R::V rk[NIT], rq[NIT], rv[NIT], rb[NIT], rw[NIT];
+    f32x4 rg[NIT];
+    E sb[NIT], sw[NIT];
+    float sg[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4);
+        const int64_t row = rc.row0 + (int64_t)min(t, rc.L - 1) * a.H;
+        rk[it] = ld_raw4(k + row * D + i);
+        rq[it] = ld_raw4(q + row * D + i);
+        rv[it] = ld_raw4(v + row * D + i);
+        if (B1)
+            sb[it] = b[row];
+        else
+            rb[it] = ld_raw4(b + row * D + i);
+        if (W1)
+            sw[it] = w[row];
+        else
+            rw[it] = ld_raw4(w + row * D + i);
+        if (G1)
+            sg[it] = a.g[row];
+        else
+            rg[it] = load4(a.g + row * D + i);
+    }
+    int growth = 0;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+        const size_t x = cdo + (size_t)t * D + i;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 gv = G1 ? bcast4(sg[it]) : rg[it];
+        f32x4 kv = R::cvt(rk[it]), qv = R::cvt(rq[it]);
+        f32x4 bv = B1 ? bcast4(to_f32(sb[it])) : R::cvt(rb[it]);
+        f32x4 wv = W1 ? bcast4(to_f32(sw[it])) : R::cvt(rw[it]);
+        if (a.pro & GDR2_PROLOGUE_GATES) {
+            bv = bsigm4(bv);
+            wv = bsigm4(wv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                gv[j] = bneg_softplus(gv[j]);
+        }
+        f32x4 ev = bv, uv = wv * R::cvt(rv[it]);
+        if (t >= rc.L) {
+            gv = zero;
+            kv = zero;
+            qv = zero;
+            ev = zero;
+            uv = zero;
+        }
+        growth |= (gv[0] > 0.f) | (gv[1] > 0.f) | (gv[2] > 0.f) | (gv[3] > 0.f);
+        if (a.pro & GDR2_PROLOGUE_NORM_QK) {
+            // unit L2 norm per token: the Q4 items of a row are Q4 consecutive lanes
+            float sk = kv[0] * kv[0] + kv[1] * kv[1] + kv[2] * kv[2] + kv[3] * kv[3];
+            float sq = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
+#pragma unroll
+            for (int m = 1; m < Q4; m <<= 1) {
+                sk += __shfl_xor(sk, m);
+                sq += __shfl_xor(sq, m);
+            }
+            const float rkn = rsqrtf(sk + kNormEps), rqn = rsqrtf(sq + kNormEps);
+            kv = kv * rkn;
+            qv = qv * rqn;
+            if (i == 0) {
+                ws[a.L.RN + (size_t)r * 2 * C + t] = rkn;
+                ws[a.L.RN + (size_t)r * 2 * C + C + t] = rqn;
+                sRN[t] = rkn;
+            }
+        }
+        ev = ev * kv;
+        st4s(sm + PS::OFF_G + l, gv);
+        st4s(sm + PS::OFF_K + l, kv);
+        st4s(sm + PS::OFF_Q + l, qv);
+        st4s(sm + PS::OFF_E + l, ev);
+        store4(reinterpret_cast<E*>(ws + a.L.U) + x, uv);
+    }
+    return growth;
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 {
@@ -235,52 +347,16 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     E* wP = reinterpret_cast<E*>(ws + a.L.P) + cco;   // P, in the input dtype
 
     // 1. raw rows (zero past the chunk's valid length), 4 channels per item
-    int growth = 0;                  // a log-decay > 0 somewhere in the chunk
-    for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
-        const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        const size_t x = cdo + (size_t)t * D + i;
-        f32x4 gv = {0.f, 0.f, 0.f, 0.f}, kv = gv, qv = gv, ev = gv, uv = gv;
-        if (t < rc.L) {
-            const int64_t row = rc.row0 + (int64_t)t * a.H;
-            gv = gate4(a.g, a.gw, row, i);
-            kv = load4(k + row * D + i);
-            qv = load4(q + row * D + i);
-            f32x4 bv = gate4(b, a.bw, row, i), wv = gate4(w, a.ww, row, i);
-            if (a.pro & GDR2_PROLOGUE_GATES) {
-                bv = bsigm4(bv);
-                wv = bsigm4(wv);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    gv[j] = bneg_softplus(gv[j]);
-            }
-            ev = bv;
-            uv = wv * load4(v + row * D + i);
-            growth |= (gv[0] > 0.f) | (gv[1] > 0.f) | (gv[2] > 0.f) | (gv[3] > 0.f);
-        }
-        if (a.pro & GDR2_PROLOGUE_NORM_QK) {
-            // unit L2 norm per token: the Q4 items of a row are Q4 consecutive lanes
-            float sk = kv[0] * kv[0] + kv[1] * kv[1] + kv[2] * kv[2] + kv[3] * kv[3];
-            float sq = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
-#pragma unroll
-            for (int m = 1; m < Q4; m <<= 1) {
-                sk += __shfl_xor(sk, m);
-                sq += __shfl_xor(sq, m);
-            }
-            const float rk = rsqrtf(sk + kNormEps), rq = rsqrtf(sq + kNormEps);
-            kv = kv * rk;
-            qv = qv * rq;
-            if (i == 0) {
-                ws[a.L.RN + (size_t)r * 2 * C + t] = rk;
-                ws[a.L.RN + (size_t)r * 2 * C + C + t] = rq;
-                sRN[t] = rk;
-            }
-        }
-        ev = ev * kv;
-        st4s(sG + l, gv);
-        st4s(sK + l, kv);
-        st4s(sQ + l, qv);
-        st4s(sE + l, ev);
-        store4(reinterpret_cast<E*>(ws + a.L.U) + x, uv);
+    int growth;
+    switch ((a.bw == 1 ? 4 : 0) | (a.ww == 1 ? 2 : 0) | (a.gw == 1 ? 1 : 0)) {
+    case 0: growth = prep_rows<false, false, false, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 1: growth = prep_rows<false, false, true, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 2: growth = prep_rows<false, true, false, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 3: growth = prep_rows<false, true, true, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 4: growth = prep_rows<true, false, false, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 5: growth = prep_rows<true, false, true, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 6: growth = prep_rows<true, true, false, E, D>(a, rc, r, tid, sm, sRN); break;
+    default: growth = prep_rows<true, true, true, E, D>(a, rc, r, tid, sm, sRN); break;
     }
     growth = lds_barrier_or<NTP / 64>(growth, sOr);
     {
@@ -829,12 +905,19 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
     const int col = slice * S::BV + 16 * wave + (lane & 15);
     const int64_t rec0 = bh * a.NC;
 
+    // the null test outside the loads, so that they are all in flight at once
     f32x4 lam[DT];
+    if (a.dS_final) {
 #pragma unroll
-    for (int kt = 0; kt < DT; ++kt)
+        for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lam[kt][i] = a.dS_final ? a.dS_final[(bh * D + 16 * kt + 4 * gq + i) * D + col] : 0.f;
+            for (int i = 0; i < 4; ++i)
+                lam[kt][i] = a.dS_final[(bh * D + 16 * kt + 4 * gq + i) * D + col];
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt)
+            lam[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     scan_fetch<E, D>(a, rec0 + a.NC - 1, slice, buf0, wave, lane);
     if constexpr (S::NBUF == 2) {
@@ -1061,10 +1144,20 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     // sums of 4 through LDS); gamma becomes gamma * dgamma, the chunk-end term
     // of dG_L that bwd_decay adds (the scan has used gamma)
     const float gam_i = tid < D ? ws[a.L.gam + (size_t)r * D + tid] : 0.f;
-    for (int e = tid; e < D * D / 4; e += NTH) {
-        const int i = e / (D / 4), j = 4 * (e % (D / 4));
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
+    // every item's loads first (all in flight together), then the conversions
+    constexpr int NIT = D * D / 4 / NTH;
+    static_assert(D * D / 4 % NTH == 0, "whole items per thread");
+    f32x4 s4r[NIT], l4r[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+        s4r[it] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
+        l4r[it] = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+        const f32x4 s4 = s4r[it], l4 = l4r[it];
         bf16x4 sv, lv;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -1392,6 +1485,67 @@ constexpr int DC = 32;                 // channels per decay workgroup
 constexpr int LC = DC + 1;             // padded LDS row of the per-channel arrays
 constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte aligned)
 
+// bwd_decay's up-front loads for one gate-width mix (B1, W1: b, w of width
+// 1): this thread's items (token t, 4 channels from i0) of the input rows
+// and of dE~, dQ~, dK^, dU.  Every load is issued before any is used; rows
+// past the valid length re-read the last valid row and are zeroed here.
+template <bool B1, bool W1, typename E, int D, int NIT>
+__device__ __forceinline__ void decay_loads(const BwdArgs& a, const Rec& rc, int64_t r, int tid, int i0, f32x4* xk,
+                                            f32x4* xq, f32x4* xb, f32x4* xw, f32x4* xv, f32x4* xdEt, f32x4* xdQt,
+                                            f32x4* xdKh, f32x4* xdU, float* xrk, float* xrq)
+{
+    typedef Raw4<E> R;
+    constexpr int C = BC;
+    const E* q = (const E*)a.q;
+    const E* k = (const E*)a.k;
+    const E* v = (const E*)a.v;
+    const E* b = (const E*)a.b;
+    const E* w = (const E*)a.w;
+    const float* ws = a.ws;
+    const size_t cdo = (size_t)r * C * D;
+    typename R::V rk[NIT], rq[NIT], rv[NIT], rb[NIT], rw[NIT];
+    E sb[NIT], sw[NIT];
+#pragma unroll
+    for (int p = 0; p < NIT; ++p) {
+        const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4));
+        const size_t x = cdo + (size_t)t * D + i0 + c;
+        const int64_t row = rc.row0 + (int64_t)min(t, rc.L - 1) * a.H;
+        rk[p] = ld_raw4(k + row * D + i0 + c);
+        rq[p] = ld_raw4(q + row * D + i0 + c);
+        rv[p] = ld_raw4(v + row * D + i0 + c);
+        if (B1)
+            sb[p] = b[row];
+        else
+            rb[p] = ld_raw4(b + row * D + i0 + c);
+        if (W1)
+            sw[p] = w[row];
+        else
+            rw[p] = ld_raw4(w + row * D + i0 + c);
+        xrk[p] = xrq[p] = 1.f;
+        if (a.pro & GDR2_PROLOGUE_NORM_QK) {
+            xrk[p] = ws[a.L.RN + (size_t)r * 2 * C + t];
+            xrq[p] = ws[a.L.RN + (size_t)r * 2 * C + C + t];
+        }
+        xdEt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
+        xdQt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
+        xdKh[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
+        xdU[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+    }
+#pragma unroll
+    for (int p = 0; p < NIT; ++p) {
+        const int t = (tid + p * NTB) / (DC / 4);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const bool valid = t < rc.L;
+        xk[p] = valid ? R::cvt(rk[p]) : z;
+        xq[p] = valid ? R::cvt(rq[p]) : z;
+        xv[p] = valid ? R::cvt(rv[p]) : z;
+        xb[p] = valid ? (B1 ? bcast4(to_f32(sb[p])) : R::cvt(rb[p])) : z;
+        xw[p] = valid ? (W1 ? bcast4(to_f32(sw[p])) : R::cvt(rw[p])) : z;
+        if (!valid)
+            xrk[p] = xrq[p] = 1.f;
+    }
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
 {
@@ -1427,29 +1581,11 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
     static_assert(NIT * NTB == C * DC / 4, "whole items per thread");
     f32x4 xk[NIT], xq[NIT], xb[NIT], xw[NIT], xv[NIT], xdEt[NIT], xdQt[NIT], xdKh[NIT], xdU[NIT];
     float xrk[NIT], xrq[NIT];
-#pragma unroll
-    for (int p = 0; p < NIT; ++p) {
-        const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4));
-        const size_t x = cdo + (size_t)t * D + i0 + c;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        xk[p] = xq[p] = xb[p] = xw[p] = xv[p] = z;
-        xrk[p] = xrq[p] = 1.f;
-        if (t < rc.L) {
-            const int64_t row = rc.row0 + (int64_t)t * a.H;
-            xk[p] = load4(k + row * D + i0 + c);
-            xq[p] = load4(q + row * D + i0 + c);
-            xv[p] = load4(v + row * D + i0 + c);
-            xb[p] = gate4(b, a.bw, row, i0 + c);
-            xw[p] = gate4(w, a.ww, row, i0 + c);
-            if (a.pro & GDR2_PROLOGUE_NORM_QK) {
-                xrk[p] = ws[a.L.RN + (size_t)r * 2 * C + t];
-                xrq[p] = ws[a.L.RN + (size_t)r * 2 * C + C + t];
-            }
-        }
-        xdEt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
-        xdQt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
-        xdKh[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
-        xdU[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+    switch ((a.bw == 1 ? 2 : 0) | (a.ww == 1 ? 1 : 0)) {
+    case 0: decay_loads<false, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
+    case 1: decay_loads<false, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
+    case 2: decay_loads<true, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
+    default: decay_loads<true, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
     }
 #pragma unroll
     for (int p = 0; p < NIT; ++p) {
