@@ -1492,7 +1492,7 @@ constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte a
 template <bool B1, bool W1, typename E, int D, int NIT>
 __device__ __forceinline__ void decay_loads(const BwdArgs& a, const Rec& rc, int64_t r, int tid, int i0, f32x4* xk,
                                             f32x4* xq, f32x4* xb, f32x4* xw, f32x4* xv, f32x4* xdEt, f32x4* xdQt,
-                                            f32x4* xdKh, f32x4* xdU, float* xrk, float* xrq)
+                                            f32x4* xdKh, f32x4* xdU, float* xrk, float* xrq, f32x4* xG)
 {
     typedef Raw4<E> R;
     constexpr int C = BC;
@@ -1530,6 +1530,7 @@ __device__ __forceinline__ void decay_loads(const BwdArgs& a, const Rec& rc, int
         xdQt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
         xdKh[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
         xdU[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+        xG[p] = *reinterpret_cast<const f32x4*>(ws + a.L.G + x);
     }
 #pragma unroll
     for (int p = 0; p < NIT; ++p) {
@@ -1581,11 +1582,12 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
     static_assert(NIT * NTB == C * DC / 4, "whole items per thread");
     f32x4 xk[NIT], xq[NIT], xb[NIT], xw[NIT], xv[NIT], xdEt[NIT], xdQt[NIT], xdKh[NIT], xdU[NIT];
     float xrk[NIT], xrq[NIT];
+    f32x4 xG[NIT];
     switch ((a.bw == 1 ? 2 : 0) | (a.ww == 1 ? 1 : 0)) {
-    case 0: decay_loads<false, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
-    case 1: decay_loads<false, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
-    case 2: decay_loads<true, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
-    default: decay_loads<true, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq); break;
+    case 0: decay_loads<false, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq, xG); break;
+    case 1: decay_loads<false, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq, xG); break;
+    case 2: decay_loads<true, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq, xG); break;
+    default: decay_loads<true, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq, xG); break;
     }
 #pragma unroll
     for (int p = 0; p < NIT; ++p) {
@@ -1596,7 +1598,7 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
         if (a.pro & GDR2_PROLOGUE_GATES)
             xb[p] = bsigm4(xb[p]);
         const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(ws + a.L.G + cdo + (size_t)t * D + i0 + c);
+        const f32x4 gv = xG[p];
         const f32x4 ev = xb[p] * xk[p];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1604,12 +1606,26 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
             sE[l + j] = ev[j];
             sK[l + j] = xk[p][j];
             sQ[l + j] = xq[p][j];
+            sdG[l + j] = xdKh[p][j];     // for dG_L below (sdG is free until the main loop)
         }
     }
-    for (int e = tid; e < C * C / 4; e += NTB) {
-        const int t = e / (C / 4), c = 4 * (e % (C / 4));
-        *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
-        *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
+    {
+        // dM, dP: every load in flight before the first LDS write
+        constexpr int NMP = C * C / 4 / NTB;
+        static_assert(C * C / 4 % NTB == 0, "whole items per thread");
+        f32x4 rM[NMP], rP[NMP];
+#pragma unroll
+        for (int it = 0; it < NMP; ++it) {
+            const int e = tid + it * NTB, t = e / (C / 4), c = 4 * (e % (C / 4));
+            rM[it] = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
+            rP[it] = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
+        }
+#pragma unroll
+        for (int it = 0; it < NMP; ++it) {
+            const int e = tid + it * NTB, t = e / (C / 4), c = 4 * (e % (C / 4));
+            *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = rM[it];
+            *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = rP[it];
+        }
     }
     lds_barrier();
     // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam) and
@@ -1636,8 +1652,9 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int l = (t0 + m) * LC + il;
-            acc += ws[a.L.dKh + cdo + (size_t)(t0 + m) * D + i] * (sK[l] * expf(GL - sG[l]));
+            acc += sdG[l] * (sK[l] * expf(GL - sG[l]));     // dK^ staged above
         }
+        lds_barrier();                  // every thread has read its dK^ rows
         sdG[rg * LC + il] = acc;        // sdG is free until the main loop
     }
     lds_barrier();
