@@ -227,9 +227,11 @@ __device__ __forceinline__ f32x4 bcast4(float x) { return f32x4{x, x, x, x}; }
 // the chunk's raw rows into LDS (G, k, q, e = b*k) and U = w*v to the
 // workspace, 4 channels per item.  Every item's loads are issued before
 // any is used; rows past the valid length re-read the last valid row and
-// are zeroed at use.  Returns whether a valid log-decay is positive.
+// are zeroed at use.  e and u of every item stay in keepE, keepU for step 3.
+// Returns whether a valid log-decay is positive.
 template <bool B1, bool W1, bool G1, typename E, int D>
-__device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_t r, int tid, float* sm, float* sRN)
+__device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_t r, int tid, float* sm, float* sRN,
+                                         f32x4* keepE, f32x4* keepU)
 {
     typedef BwdPrepShape<D> PS;
     typedef Raw4<E> R;
@@ -317,6 +319,8 @@ __device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_
         st4s(sm + PS::OFF_Q + l, qv);
         st4s(sm + PS::OFF_E + l, ev);
         store4(reinterpret_cast<E*>(ws + a.L.U) + x, uv);
+        keepE[it] = ev;
+        keepU[it] = uv;
     }
     return growth;
 }
@@ -347,16 +351,18 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     E* wP = reinterpret_cast<E*>(ws + a.L.P) + cco;   // P, in the input dtype
 
     // 1. raw rows (zero past the chunk's valid length), 4 channels per item
+    constexpr int NIT1 = C * Q4 / NTP;
+    f32x4 keepE[NIT1], keepU[NIT1];  // e = b k and u = w v of this thread's items, for step 3
     int growth;
     switch ((a.bw == 1 ? 4 : 0) | (a.ww == 1 ? 2 : 0) | (a.gw == 1 ? 1 : 0)) {
-    case 0: growth = prep_rows<false, false, false, E, D>(a, rc, r, tid, sm, sRN); break;
-    case 1: growth = prep_rows<false, false, true, E, D>(a, rc, r, tid, sm, sRN); break;
-    case 2: growth = prep_rows<false, true, false, E, D>(a, rc, r, tid, sm, sRN); break;
-    case 3: growth = prep_rows<false, true, true, E, D>(a, rc, r, tid, sm, sRN); break;
-    case 4: growth = prep_rows<true, false, false, E, D>(a, rc, r, tid, sm, sRN); break;
-    case 5: growth = prep_rows<true, false, true, E, D>(a, rc, r, tid, sm, sRN); break;
-    case 6: growth = prep_rows<true, true, false, E, D>(a, rc, r, tid, sm, sRN); break;
-    default: growth = prep_rows<true, true, true, E, D>(a, rc, r, tid, sm, sRN); break;
+    case 0: growth = prep_rows<false, false, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    case 1: growth = prep_rows<false, false, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    case 2: growth = prep_rows<false, true, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    case 3: growth = prep_rows<false, true, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    case 4: growth = prep_rows<true, false, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    case 5: growth = prep_rows<true, false, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    case 6: growth = prep_rows<true, true, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
+    default: growth = prep_rows<true, true, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
     }
     growth = lds_barrier_or<NTP / 64>(growth, sOr);
     {
@@ -563,11 +569,22 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 
     }
 
-    // 3. X = (I + M)^-1 into the q area (wave 0), while the other waves stage
-    // E~ and u for step 4 (recomputed from the inputs: the k area and the
-    // E area hold re-referenced rows)
+    // 3. X = (I + M)^-1 into the q area (wave 0), after every thread has
+    // staged E~ = e e^G and u of its step-1 items for step 4 (the k and E
+    // areas held re-referenced rows until now)
     float* sX = sQ;
     float* sU = sK;
+#pragma unroll
+    for (int it = 0; it < NIT1; ++it) {
+        const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+        const f32x4 G = ld4s(sG + l);
+        f32x4 ev = keepE[it];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ev[j] *= expf(G[j]);
+        st4s(sE + l, ev);
+        st4s(sU + l, keepU[it]);
+    }
     if (tid < 64) {
         typedef Mma<float> MF;
         const int lane = tid, gq = lane >> 4, cl = lane & 15;
@@ -606,30 +623,6 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 for (int x4 = 0; x4 < 4; ++x4)
                     sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = -xi[x4];
             }
-        }
-    } else {
-        for (int e4 = tid - 64; e4 < C * Q4; e4 += NTP - 64) {
-            const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-            f32x4 ev = {0.f, 0.f, 0.f, 0.f}, uv = ev;
-            if (t < rc.L) {
-                // e = b k and u = w v as step 1 forms them
-                const int64_t row = rc.row0 + (int64_t)t * a.H;
-                f32x4 kv = load4(k + row * D + i), bv = gate4(b, a.bw, row, i), wv = gate4(w, a.ww, row, i);
-                if (a.pro & GDR2_PROLOGUE_GATES) {
-                    bv = bsigm4(bv);
-                    wv = bsigm4(wv);
-                }
-                if (a.pro & GDR2_PROLOGUE_NORM_QK)
-                    kv = kv * sRN[t];
-                ev = bv * kv;
-                uv = wv * load4(v + row * D + i);
-            }
-            const f32x4 G = ld4s(sG + l);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ev[j] *= expf(G[j]);
-            st4s(sE + l, ev);
-            st4s(sU + l, uv);
         }
     }
     lds_barrier();
