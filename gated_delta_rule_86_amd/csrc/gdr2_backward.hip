@@ -1133,6 +1133,39 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
 
     const float* S = a.S_chunks + dd;
     const float* Lam = ws + a.L.Lam + dd;
+    const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
+    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd + (size_t)t0 * D;
+    // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
+    // valid length)
+    const Rec rc = rec_of(r, a.NC, a.T, a.H);
+    const bool dorow = t0 + cl < rc.L;
+    const bf16* dOr = (const bf16*)a.dO + (rc.row0 + (int64_t)(dorow ? t0 + cl : 0) * a.H) * D + 4 * gq;
+    auto load_dO = [&](int ks) -> Frag {
+        Frag f = {};
+        if (dorow) {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB + 16);
+            f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+            f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+        }
+        return f;
+    };
+    const size_t orow = cd + (size_t)(t0 + 4 * gq) * D + cl;   // output element (row 4gq, column cl) of the wave
+    // this wave's global operands of the products below, loaded first so
+    // that they arrive while S and Lam are staged
+    Frag pW[NKS], pD[NKS], pO[NKS];
+    float pU[NH][4];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        pW[ks] = MM::load(W + ks * MM::KB, D, lane);
+        pD[ks] = MM::load(dDel + ks * MM::KB, D, lane);
+        pO[ks] = load_dO(ks);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            pU[nt][x] = ws[a.L.Ut + orow + (size_t)x * D + 16 * (n0 + nt)];
     // staging also forms dgamma_i = sum_j S[i][j] Lam[i][j] in fp32 (partial
     // sums of 4 through LDS); gamma becomes gamma * dgamma, the chunk-end term
     // of dG_L that bwd_decay adds (the scan has used gamma)
@@ -1171,24 +1204,6 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         ws[a.L.gam + (size_t)r * D + tid] = gam_i * dg;
     }
 
-    const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
-    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd + (size_t)t0 * D;
-    // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
-    // valid length)
-    const Rec rc = rec_of(r, a.NC, a.T, a.H);
-    const bool dorow = t0 + cl < rc.L;
-    const bf16* dOr = (const bf16*)a.dO + (rc.row0 + (int64_t)(dorow ? t0 + cl : 0) * a.H) * D + 4 * gq;
-    auto load_dO = [&](int ks) -> Frag {
-        Frag f = {};
-        if (dorow) {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB + 16);
-            f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-            f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-        }
-        return f;
-    };
-    const size_t orow = cd + (size_t)(t0 + 4 * gq) * D + cl;   // output element (row 4gq, column cl) of the wave
 
     // Delta = U~ - W S   (k = i: B fragments from S^T)
     {
@@ -1198,16 +1213,15 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
             p[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const Frag aw = MM::load(W + ks * MM::KB, D, lane);
 #pragma unroll
             for (int nt = 0; nt < NH; ++nt)
-                p[nt] = MM::mma(aw, MM::load(sSt + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), p[nt]);
+                p[nt] = MM::mma(pW[ks], MM::load(sSt + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), p[nt]);
         }
 #pragma unroll
         for (int nt = 0; nt < NH; ++nt)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const float dl = ws[a.L.Ut + orow + (size_t)x * D + 16 * (n0 + nt)] - p[nt][x];
+                const float dl = pU[nt][x] - p[nt][x];
                 sDel[(t0 + 4 * gq + x) * LDB + 16 * (n0 + nt) + cl] = (bf16)dl;
             }
     }
@@ -1219,12 +1233,11 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
             q[nt] = w[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const Frag ao = load_dO(ks), ad = MM::load(dDel + ks * MM::KB, D, lane);
 #pragma unroll
             for (int nt = 0; nt < NH; ++nt) {
                 const Frag bs = MM::load(sS + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane);
-                q[nt] = MM::mma(ao, bs, q[nt]);
-                w[nt] = MM::mma(ad, bs, w[nt]);
+                q[nt] = MM::mma(pO[ks], bs, q[nt]);
+                w[nt] = MM::mma(pD[ks], bs, w[nt]);
             }
         }
 #pragma unroll
@@ -1267,11 +1280,10 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         if (s0 <= rw) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const Frag ao = load_dO(ks);
 #pragma unroll
                 for (int sbk = 0; sbk < SBH; ++sbk)
                     if (s0 + sbk <= rw)
-                        pp[sbk] = MM::mma(ao, MM::load(sDel + 16 * (s0 + sbk) * LDB + ks * MM::KB, LDB, lane),
+                        pp[sbk] = MM::mma(pO[ks], MM::load(sDel + 16 * (s0 + sbk) * LDB + ks * MM::KB, LDB, lane),
                                           pp[sbk]);
             }
         }
