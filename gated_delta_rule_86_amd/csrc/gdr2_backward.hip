@@ -1568,8 +1568,16 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
     float* sdG = sQ + C * LC;       // [C][LC] dG, then dg
     float* sGL = sdG + C * LC;      // [DC] dG_L
     __shared__ int sOr[2 * (NTB / 64)];
-    const int64_t r = blockIdx.x / (D / DC);
-    const int i0 = (int)(blockIdx.x % (D / DC)) * DC;
+    // workgroup -> (chunk record, channel group): the D/DC groups of a
+    // record share blockIdx % 8, i.e. one XCD, so the dM and dP they all
+    // stage come from HBM once and from that XCD's L2 after
+    constexpr int NCG = D / DC;
+    const int64_t bx = blockIdx.x, grp = bx / (8 * NCG);
+    const int within = (int)(bx % (8 * NCG));
+    const int64_t r = grp * 8 + within % 8;
+    if (r >= a.nrec)
+        return;
+    const int i0 = (within / 8) * DC;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
     const int tid = threadIdx.x, il = tid % DC, rg = tid / DC, i = i0 + il, t0 = RPT * rg;
     const E* q = (const E*)a.q;
@@ -2032,7 +2040,8 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(nrec * (D / DC))), dim3(NTB), lds_decay, s, a);
+    hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(cdiv(nrec, 8) * 8 * (D / DC))), dim3(NTB), lds_decay, s,
+                       a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.pro & GDR2_PROLOGUE_NORM_QK) {
         constexpr int RPB = NTB / (D / 4);
