@@ -55,9 +55,9 @@ size_t a64(size_t x) { return (x + 63) & ~size_t(63); }
 struct BwdLayout {
     int64_t nrec;
     // [C][D] per record
-    size_t G, U, Et, Qt, Kh, W, Ut, Del, dDel, dQt, dKh, dW, dU, dEt, dO;
+    size_t G, U, Et, W, Ut, Del, dDel, dQt, dKh, dW, dU, dEt, dO;
     // [C][C] per record
-    size_t P, X, dP, dX, T1, dM;
+    size_t X, dP, dX, T1, dM;
     // [D] per record
     size_t gam;
     // [2][C] per record: prologue 1/|k|, 1/|q| of every token
@@ -76,13 +76,12 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes)
     const size_t cd = a64((size_t)L.nrec * BC * D), cc = a64((size_t)L.nrec * BC * BC);
     const size_t dd = a64((size_t)L.nrec * D * D), d1 = a64((size_t)L.nrec * D);
     size_t o = 0;
-    size_t* cds[] = {&L.G, &L.U, &L.Et, &L.Qt, &L.Kh, &L.W, &L.Ut, &L.Del, &L.dDel, &L.dQt, &L.dKh,
-                     &L.dW, &L.dU, &L.dEt, &L.dO};
+    size_t* cds[] = {&L.G, &L.U, &L.Et, &L.W, &L.Ut, &L.Del, &L.dDel, &L.dQt, &L.dKh, &L.dW, &L.dU, &L.dEt, &L.dO};
     for (size_t* p : cds) {
         *p = o;
         o += cd;
     }
-    size_t* ccs[] = {&L.P, &L.X, &L.dP, &L.dX, &L.T1, &L.dM};
+    size_t* ccs[] = {&L.X, &L.dP, &L.dX, &L.T1, &L.dM};
     for (size_t* p : ccs) {
         *p = o;
         o += cc;
@@ -130,6 +129,47 @@ __device__ __forceinline__ Rec rec_of(int64_t r, int64_t NC, int64_t T, int64_t 
     x.row0 = (b * T + t0) * H + h;
     x.L = (int)min((int64_t)BC, T - t0);
     return x;
+}
+
+// ---------------------------------------------------------------------------
+// Operands of the reverse scan, in MFMA fragment order and the input
+// precision E.  A 1 KB fragment holds 16 rows x KB contraction indices: lane
+// l keeps row l%16 and, inside the KB block, k = 4(l/16)..+3 (bf16: also
+// 16+4(l/16)..+3), 16 contiguous bytes per lane -- what Mma<E>::load reads
+// from a row-major matrix, so an accumulator tile is directly a B operand.
+// Per chunk record:
+//   K   K^      rows s (C/16 tiles)           x k = key channel (D/KB steps)
+//   P   P^T     rows s                        x k = token (C/KB steps; the
+//               part below the diagonal is stored as zeros)
+//   Q   Q~^T    rows = key channel (D/16)     x k = token
+//   W   -W^T    same
+//   O   dO^T    rows = value column (D/16)    x k = token
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+struct ScanFrags {
+    static constexpr int KB = Mma<E>::KB, KT = KB / 16, NB = BC / 16;
+    static constexpr int NKS = D / KB, NKC = BC / KB, DT = D / 16;
+    static constexpr size_t FRAG = 1024;
+    static constexpr size_t K_BYTES = (size_t)NB * NKS * FRAG;    // C*D*sizeof(E)
+    static constexpr size_t P_BYTES = (size_t)NB * NKC * FRAG;    // C*C*sizeof(E)
+    static constexpr size_t T_BYTES = (size_t)DT * NKC * FRAG;    // C*D*sizeof(E)
+    static constexpr size_t OFF_K = 0, OFF_P = K_BYTES, OFF_Q = OFF_P + P_BYTES, OFF_W = OFF_Q + T_BYTES,
+                            OFF_O = OFF_W + T_BYTES, REC = OFF_O + T_BYTES;
+    static constexpr int NFRAG = (int)(REC / FRAG);
+    static_assert(K_BYTES == (size_t)BC * D * sizeof(E), "fragment size");
+    static_assert(REC == (size_t)(4 * BC * D + BC * BC) * sizeof(E), "record size used for the workspace");
+};
+
+// Byte offset of element (row, k) in an array of such fragments whose
+// 16-row blocks hold nk fragments each (KB k-values per fragment).  Four
+// consecutive k from a multiple of 4 are contiguous.
+template <typename E>
+__device__ __forceinline__ size_t frag_at(int row, int k, int nk)
+{
+    constexpr int KB = Mma<E>::KB;
+    const int f = (row >> 4) * nk + k / KB, lane = (row & 15) + 16 * ((k & 15) >> 2);
+    const int j = (k & 3) + 4 * ((k % KB) >> 4);
+    return (size_t)f * 1024 + (size_t)lane * 16 + (size_t)j * sizeof(E);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,7 +388,13 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     const E* w = (const E*)a.w;
     float* ws = a.ws;
     const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
-    E* wP = reinterpret_cast<E*>(ws + a.L.P) + cco;   // P, in the input dtype
+    // the scan's operand fragments of this record (K^, P^T, Q~^T, -W^T; the
+    // frag pass adds dO^T), in the input dtype
+    typedef ScanFrags<E, D> SF;
+    unsigned char* sfr = reinterpret_cast<unsigned char*>(ws + a.L.SF) + (size_t)r * SF::REC;
+    auto pT = [&](int s_, int t) -> E* {            // P^T[s][t] = P[t][s]
+        return reinterpret_cast<E*>(sfr + SF::OFF_P + frag_at<E>(s_, t, SF::NKC));
+    };
 
     // 1. raw rows (zero past the chunk's valid length), 4 channels per item
     constexpr int NIT1 = C * Q4 / NTP;
@@ -402,8 +448,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         }
         st4s(ws + a.L.G + x, G);
         store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ld4s(sE + l) * eg);
-        store4(reinterpret_cast<E*>(ws + a.L.Qt) + x, ld4s(sQ + l) * eg);
-        store4(reinterpret_cast<E*>(ws + a.L.Kh) + x, ld4s(sK + l) * kd);
+        // K^ straight into the scan's fragments (row = token, k = channel)
+        store4(reinterpret_cast<E*>(sfr + SF::OFF_K + frag_at<E>(t, i, SF::NKS)), ld4s(sK + l) * kd);
         if (t == 0) {
             f32x4 gm;
 #pragma unroll
@@ -411,6 +457,17 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 gm[j] = expf(GL[j]);
             st4s(ws + a.L.gam + (size_t)r * D + i, gm);
         }
+    }
+    // Q~ = q e^G into the scan's Q~^T fragments (row = channel, k = token):
+    // an item is one channel at 4 consecutive tokens, read from the raw
+    // rows before step 2 re-references them
+    for (int e = tid; e < D * (C / 4); e += NTP) {
+        const int i = e % D, t0 = 4 * (e / D);
+        f32x4 qv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qv[j] = sQ[(t0 + j) * LD + i] * expf(sG[(t0 + j) * LD + i]);
+        store4(reinterpret_cast<E*>(sfr + SF::OFF_Q + frag_at<E>(i, t0, SF::NKC)), qv);
     }
 
     // 2. M (strictly lower) and P (lower).
@@ -442,10 +499,10 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 p += sQ[t * LD + i] * f;
             }
             sM[t * LDM + s_] = cc < rr ? m : 0.f;
-            wP[t * C + s_] = from_f32<E>(p);
+            *pT(s_, t) = from_f32<E>(p);
             if (cc < rr) {
                 sM[s_ * LDM + t] = 0.f;
-                wP[s_ * C + t] = from_f32<E>(0.f);
+                *pT(t, s_) = from_f32<E>(0.f);
             }
         }
         lds_barrier();
@@ -488,17 +545,21 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     m = MF::mma(MF::load_scaled(sE + 16 * T * LD + k0, LD, cf + k0, lane), kb, m);
                     p = MF::mma(MF::load_scaled(sQ + 16 * T * LD + k0, LD, cf + k0, lane), kb, p);
                 }
+                f32x4 pv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * T + 4 * gq + i, s_ = 16 * S + cl;
                     sM[t * LDM + s_] = s_ < t ? m[i] : 0.f;
-                    wP[t * C + s_] = from_f32<E>(s_ <= t ? p[i] : 0.f);
+                    pv[i] = s_ <= t ? p[i] : 0.f;
                     if (S < T) {
                         const int ta = 16 * S + 4 * gq + i, sa = 16 * T + cl;   // the block (S, T)
                         sM[ta * LDM + sa] = 0.f;
-                        wP[ta * C + sa] = from_f32<E>(0.f);
                     }
                 }
+                // the accumulator column is a P^T fragment row: 4 consecutive tokens
+                store4(pT(16 * S + cl, 16 * T + 4 * gq), pv);
+                if (S < T)
+                    store4(pT(16 * T + cl, 16 * S + 4 * gq), f32x4{0.f, 0.f, 0.f, 0.f});
             }
         }
         lds_barrier();
@@ -546,6 +607,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         }
         lds_barrier();
         if (tid < 136) {
+            f32x4 pv[4];                  // pv[y][x] = P[t0 + x][s0 + y]
     #pragma unroll
             for (int x = 0; x < 4; ++x)
     #pragma unroll
@@ -553,16 +615,19 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     const int t = t0 + x, s_ = s0 + y;
                     const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
                     sM[t * LDM + s_] = s_ < t ? mm : 0.f;
-                    wP[t * C + s_] = from_f32<E>(s_ <= t ? pp : 0.f);
+                    pv[y][x] = s_ <= t ? pp : 0.f;
                 }
+    #pragma unroll
+            for (int y = 0; y < 4; ++y)
+                store4(pT(s0 + y, t0), pv[y]);
             if (sb != tb) {               // the mirrored block above the diagonal is zero
     #pragma unroll
-                for (int x = 0; x < 4; ++x)
+                for (int x = 0; x < 4; ++x) {
     #pragma unroll
-                    for (int y = 0; y < 4; ++y) {
+                    for (int y = 0; y < 4; ++y)
                         sM[(s0 + y) * LDM + t0 + x] = 0.f;
-                        wP[(s0 + y) * C + t0 + x] = from_f32<E>(0.f);
-                    }
+                    store4(pT(t0 + x, s0), f32x4{0.f, 0.f, 0.f, 0.f});
+                }
             }
         }
         lds_barrier();
@@ -649,6 +714,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     reinterpret_cast<E*>(ws + a.L.W)[o + (size_t)i * D] = from_f32<E>(acc[i]);
+                // and -W^T for the scan: the accumulator column is a fragment row
+                store4(reinterpret_cast<E*>(sfr + SF::OFF_W + frag_at<E>(16 * c + cl, 16 * T + 4 * gq, SF::NKC)), -acc);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -672,86 +739,33 @@ __global__ __launch_bounds__(NTB) void bwd_dout_kernel(BwdArgs a)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Operands of the reverse scan, in MFMA fragment order and the input
-// precision E.  A 1 KB fragment holds 16 rows x KB contraction indices: lane
-// l keeps row l%16 and, inside the KB block, k = 4(l/16)..+3 (bf16: also
-// 16+4(l/16)..+3), 16 contiguous bytes per lane -- what Mma<E>::load reads
-// from a row-major matrix, so an accumulator tile is directly a B operand.
-// Per chunk record:
-//   K   K^      rows s (C/16 tiles)           x k = key channel (D/KB steps)
-//   P   P^T     rows s                        x k = token (C/KB steps; the
-//               part below the diagonal is stored as zeros)
-//   Q   Q~^T    rows = key channel (D/16)     x k = token
-//   W   -W^T    same
-//   O   dO^T    rows = value column (D/16)    x k = token
-// ---------------------------------------------------------------------------
-template <typename E, int D>
-struct ScanFrags {
-    static constexpr int KB = Mma<E>::KB, KT = KB / 16, NB = BC / 16;
-    static constexpr int NKS = D / KB, NKC = BC / KB, DT = D / 16;
-    static constexpr size_t FRAG = 1024;
-    static constexpr size_t K_BYTES = (size_t)NB * NKS * FRAG;    // C*D*sizeof(E)
-    static constexpr size_t P_BYTES = (size_t)NB * NKC * FRAG;    // C*C*sizeof(E)
-    static constexpr size_t T_BYTES = (size_t)DT * NKC * FRAG;    // C*D*sizeof(E)
-    static constexpr size_t OFF_K = 0, OFF_P = K_BYTES, OFF_Q = OFF_P + P_BYTES, OFF_W = OFF_Q + T_BYTES,
-                            OFF_O = OFF_W + T_BYTES, REC = OFF_O + T_BYTES;
-    static constexpr int NFRAG = (int)(REC / FRAG);
-    static_assert(K_BYTES == (size_t)BC * D * sizeof(E), "fragment size");
-    static_assert(REC == (size_t)(4 * BC * D + BC * BC) * sizeof(E), "record size used for the workspace");
-};
 
 // Contraction index held in slot j (0 .. 16/sizeof(E)-1) by lane group gq.
 template <typename E> __device__ __forceinline__ int slot_k(int gq, int j);
 template <> __device__ __forceinline__ int slot_k<bf16>(int gq, int j) { return (j < 4 ? 0 : 12) + 4 * gq + j; }
 template <> __device__ __forceinline__ int slot_k<float>(int gq, int j) { return 4 * gq + j; }
 
-// One workgroup per chunk record: the fp32 rows the prep kernel and the dO
-// copy wrote, re-laid into fragments.  Item (fragment, lane) -> 16 bytes.
+// One workgroup per chunk record: the dO^T fragments of the scan (rows =
+// value columns, k = tokens), read from the input rows, zero past the valid
+// length.  bwd_prep writes the record's other fragments.  Item (fragment,
+// lane) -> 16 bytes.
 template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
 {
     typedef ScanFrags<E, D> F;
-    constexpr int C = BC, NV = 16 / (int)sizeof(E);
+    constexpr int NV = 16 / (int)sizeof(E), NOF = F::DT * F::NKC;
     const int64_t r = blockIdx.x;
-    const float* ws = a.ws;
-    const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
     const Rec rc = rec_of(r, a.NC, a.T, a.H);
     const E* dOin = (const E*)a.dO;
-    unsigned char* out = reinterpret_cast<unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC;
-    for (int it = threadIdx.x; it < F::NFRAG * 64; it += NTB) {
-        const int f = it / 64, lane = it % 64, gq = lane / 16, rl = lane % 16;
-        const E* src;
-        int row, m;
-        int64_t rs, ks;            // element (row, k) at src[row * rs + k * ks]
-        float sign = 1.f;
-        bool dout = false;         // dO^T, read from the input rows (zero past the valid length)
-        if (f < F::NB * F::NKS) {                       // K^ [s][i]
-            row = 16 * (f / F::NKS) + rl; m = f % F::NKS;
-            src = reinterpret_cast<const E*>(ws + a.L.Kh) + cdo; rs = D; ks = 1;
-        } else if (f < F::NB * (F::NKS + F::NKC)) {     // P^T [s][t] = P[t][s]
-            const int g = f - F::NB * F::NKS;
-            row = 16 * (g / F::NKC) + rl; m = g % F::NKC;
-            src = reinterpret_cast<const E*>(ws + a.L.P) + cco; rs = 1; ks = C;
-        } else {                                        // Q~^T, -W^T, dO^T: [i][t] = X[t][i]
-            const int g = f - F::NB * (F::NKS + F::NKC), which = g / (F::DT * F::NKC), h = g % (F::DT * F::NKC);
-            row = 16 * (h / F::NKC) + rl; m = h % F::NKC;
-            src = reinterpret_cast<const E*>(ws + (which == 0 ? a.L.Qt : a.L.W)) + cdo;
-            sign = which == 1 ? -1.f : 1.f;
-            rs = 1; ks = D;
-            dout = which == 2;
-        }
+    unsigned char* out = reinterpret_cast<unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC + F::OFF_O;
+    for (int it = threadIdx.x; it < NOF * 64; it += NTB) {
+        const int f = it / 64, lane = it % 64, gq = lane / 16;
+        const int row = 16 * (f / F::NKC) + lane % 16, m = f % F::NKC;
         float x[NV];
-        if (dout) {
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const int t = m * F::KB + slot_k<E>(gq, j);
-                x[j] = t < rc.L ? to_f32(dOin[(rc.row0 + (int64_t)t * a.H) * D + row]) : 0.f;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NV; ++j)
-                x[j] = sign * to_f32(src[row * rs + (int64_t)(m * F::KB + slot_k<E>(gq, j)) * ks]);
+        for (int j = 0; j < NV; ++j) {
+            const int t = m * F::KB + slot_k<E>(gq, j);
+            x[j] = t < rc.L ? to_f32(dOin[(rc.row0 + (int64_t)min(t, rc.L - 1) * a.H) * D + row]) : 0.f;
         }
         unsigned char* dst = out + (size_t)f * F::FRAG + lane * 16;
         if constexpr (sizeof(E) == 2) {

@@ -333,19 +333,19 @@ def test_backward_null_args_and_workspace(lib):
 
 
 def test_backward_workspace_size_formula(lib):
-    # per chunk record, fp32, each array padded to 256 bytes: 16 arrays of
-    # [C][D] (G, E, U, E~, Q~, K^, W, U~, Delta, dDelta, dQ~, dK^, dW, dU,
-    # dE~, dO), 6 of [C][C] (P, X, dP, dX, a product, dM), gamma [D], the
-    # prologue's per-token 1/|k|, 1/|q| [2][C], the chunk-end state gradient
-    # [D][D]; then the scan's operand fragments in
-    # the input dtype: K^, Q~^T, -W^T, dO^T (C*D each) and P^T (C*C)
+    # per chunk record, fp32, each array padded to 256 bytes: 13 arrays of
+    # [C][D] (G, U, E~, W, U~, Delta, dDelta, dQ~, dK^, dW, dU, dE~, dO),
+    # 5 of [C][C] (X, dP, dX, a product, dM), gamma [D], the prologue's
+    # per-token 1/|k|, 1/|q| [2][C], the chunk-end state gradient [D][D];
+    # then the scan's operand fragments in the input dtype: K^, Q~^T, -W^T,
+    # dO^T (C*D each) and P^T (C*C)
     def al(x):
         return (x + 255) // 256 * 256
     for (B, T, H, D, dt, es) in [(2, 100, 3, 128, gdr2.BF16, 2), (1, 64, 1, 64, gdr2.F32, 4),
                                  (8, 4096, 16, 128, gdr2.BF16, 2), (1, 200, 2, 128, gdr2.F32, 4)]:
         a = good_bwd(B=B, T=T, H=H, D=D, dtype=dt)
         nrec = B * H * -(-T // 64)
-        want = (15 * al(nrec * 64 * D * 4) + 6 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
+        want = (13 * al(nrec * 64 * D * 4) + 5 * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
                 + al(nrec * D * D * 4) + al(nrec * (4 * 64 * D + 64 * 64) * es))
         assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == want
     assert lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(T=0))) == 0
