@@ -31,9 +31,9 @@ def _narrow(inp, widths):
     return out
 
 
-def _gpu_backward(d, fwd_chunk=64):
+def _gpu_backward(d, fwd_chunk=64, fwd_algo="auto"):
     args = [d[n] for n in NAMES]
-    _, _, ck = gdr2.forward(*args, S0=d["S0"], chunk=fwd_chunk, chunk_states=True)
+    _, _, ck = gdr2.forward(*args, S0=d["S0"], chunk=fwd_chunk, chunk_states=True, algo=fwd_algo)
     if fwd_chunk != 64:                     # chunk-64 starts are every other chunk-32 start
         ck = ck[:, :, ::64 // fwd_chunk].contiguous()
     return gdr2.backward(*args, S_chunks=ck, dO=d["dO"], dS_final=d["dS_final"])
@@ -110,6 +110,19 @@ def test_backward_steep_decay(dtype, D, g_const):
     got = _gpu_backward(to_dev(inp))
     torch.cuda.synchronize()
     _compare(f"steep_{dtype}_{g_const}", got, _oracle_backward(inp), TOL[dtype])
+
+
+def test_backward_from_two_level_forward():
+    """Chunk-start states from the forward's two-level scan (2 heads, 32
+    chunks: segments of 4 on 256 CUs) with a weak decay (g scaled by 0.05),
+    so every segment's start state carries the earlier segments' updates
+    into the backward."""
+    wl = Workload("seg_bwd", "forward", 1, 2048, 2, 128, "bf16", "full", 0.05, 64, 611, g_scale=0.05)
+    inp = draw(wl)
+    inp.update(draw_cotangents(wl, 1.0))
+    got = _gpu_backward(to_dev(inp), fwd_algo="segmented")
+    torch.cuda.synchronize()
+    _compare("seg_bwd", got, _oracle_backward(inp), TOL["bf16"])
 
 
 def test_state_gradient_only():

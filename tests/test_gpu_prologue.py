@@ -44,10 +44,11 @@ def _inputs(wl, bits):
     return inp
 
 
-def _fwd_check(name, wl, bits, chunk):
+def _fwd_check(name, wl, bits, chunk, algo="auto"):
     inp = _inputs(wl, bits)
     d = to_dev(inp)
-    o, S, ck = gdr2.forward(*(d[n] for n in NAMES), S0=d["S0"], chunk=chunk, chunk_states=True, prologue=bits)
+    o, S, ck = gdr2.forward(*(d[n] for n in NAMES), S0=d["S0"], chunk=chunk, chunk_states=True, prologue=bits,
+                            algo=algo)
     torch.cuda.synchronize()
     raw = [to_f64(inp[n]) for n in NAMES]
     o_ref, S_ref, ck_ref = oracle.forward_checkpoints(*raw, every=chunk, S0=to_f64(inp["S0"]), prologue=bits)
@@ -62,6 +63,15 @@ def _fwd_check(name, wl, bits, chunk):
 @pytest.mark.parametrize("name,B,T,H,D,dtype,gates,s0,chunk,bits", FWD_CASES, ids=[c[0] for c in FWD_CASES])
 def test_forward_prologue_matches_oracle(name, B, T, H, D, dtype, gates, s0, chunk, bits):
     _fwd_check(name, Workload(name, "forward", B, T, H, D, dtype, gates, s0, chunk, 801), bits, chunk)
+
+
+@pytest.mark.parametrize("dtype,D,chunk", [("bf16", 128, 64), ("f32", 64, 32)])
+def test_forward_prologue_two_level_scan(dtype, D, chunk):
+    """The prologue under the two-level scan over chunk segments (the span
+    pass reads the factors the prologue-fused prep kernel wrote)."""
+    name = f"{dtype}_d{D}_c{chunk}_all_segmented"
+    _fwd_check(name, Workload(name, "forward", 1, 700, 2, D, dtype, "full", 0.05, chunk, 802), pro.ALL, chunk,
+               algo="segmented")
 
 
 def test_forward_prologue_steep_decay_exact_path():
