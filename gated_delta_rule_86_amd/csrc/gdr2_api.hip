@@ -237,6 +237,10 @@ gdr2_status validate_backward(const gdr2_bwd_args* a)
         return fail(GDR2_ERR_INVALID_ARG, "unknown prologue bits 0x%x", a->prologue);
     if (a->chunk != 64)
         return fail(GDR2_ERR_UNSUPPORTED, "the backward supports chunk 64 only (got %d)", a->chunk);
+    if (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED && a->algo != GDR2_ALGO_SEGMENTED)
+        return fail(GDR2_ERR_INVALID_ARG, "unknown algo %d", a->algo);
+    if (a->reserved != 0)
+        return fail(GDR2_ERR_INVALID_ARG, "reserved must be 0");
     const int64_t nchunks = (a->T + 63) / 64;
     int64_t nrec, state_bytes, ck_bytes;
     // the widest launch has four workgroups per chunk record

@@ -66,10 +66,13 @@ struct BwdLayout {
     size_t Lam;
     // scan operand fragments (ScanFrags), rec_bytes per record
     size_t SF;
+    // two-level scan (nseg > 1): per (b,h) and segment but the first, a
+    // chunk product and a local gradient, D x D fp32 each
+    size_t span;
     size_t total;
 };
 
-BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes)
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, int64_t nseg)
 {
     BwdLayout L;
     L.nrec = B * H * cdiv(T, BC);
@@ -94,6 +97,9 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes)
     o += dd;
     L.SF = o;
     o += a64((size_t)L.nrec * rec_bytes / 4);
+    L.span = o;
+    if (nseg > 1)
+        o += a64((size_t)(B * H) * (nseg - 1) * 2 * D * D);
     L.total = o * sizeof(float);
     return L;
 }
@@ -108,6 +114,7 @@ struct BwdArgs {
     int bw, ww, gw;
     int pro;             // prologue bits
     int64_t T, H, NC, nrec, nbh;
+    int64_t nseg, seg_len;   // chunk segments of the reverse scan (1, NC: one pass)
     float* ws;           // workspace base (fp32)
     BwdLayout L;
 };
@@ -901,64 +908,227 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
     constexpr int DT = D / 16;
     __shared__ __align__(16) unsigned char buf0[S::BUF];
     __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
-    // workgroup -> ((b,h), column slice); the slices of one (b,h) share
-    // blockIdx % 8, i.e. one XCD and its L2
+    // workgroup -> ((b,h), chunk segment, column slice); the slices of one
+    // segment share blockIdx % 8, i.e. one XCD and its L2
     const int64_t bx = blockIdx.x, grp = bx / (8 * S::NS);
     const int within = (int)(bx % (8 * S::NS)), slice = within / 8;
-    const int64_t bh = grp * 8 + within % 8;
-    if (bh >= a.nbh)
+    const int64_t unit = grp * 8 + within % 8;       // (b*H + h) * nseg + segment
+    if (unit >= a.nbh * a.nseg)
         return;
+    const int64_t bh = unit / a.nseg, seg = unit - bh * a.nseg;
+    const int64_t n0 = seg * a.seg_len, n1 = min(a.NC, n0 + a.seg_len);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4;
     const int col = slice * S::BV + 16 * wave + (lane & 15);
     const int64_t rec0 = bh * a.NC;
 
-    // the null test outside the loads, so that they are all in flight at once
+    // the gradient at the segment's end: dS_final (or zero) for the last
+    // segment, else what the segment fold left for it (the null test
+    // outside the loads, so that they are all in flight at once)
+    const float* l0 = seg == a.nseg - 1
+                          ? (a.dS_final ? a.dS_final + bh * D * D : nullptr)
+                          : a.ws + a.L.span + ((bh * (a.nseg - 1) + (a.nseg - 2 - seg)) * 2 + 1) * D * D;
     f32x4 lam[DT];
-    if (a.dS_final) {
+    if (l0) {
 #pragma unroll
         for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                lam[kt][i] = a.dS_final[(bh * D + 16 * kt + 4 * gq + i) * D + col];
+                lam[kt][i] = l0[(16 * kt + 4 * gq + i) * D + col];
     } else {
 #pragma unroll
         for (int kt = 0; kt < DT; ++kt)
             lam[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    scan_fetch<E, D>(a, rec0 + a.NC - 1, slice, buf0, wave, lane);
+    scan_fetch<E, D>(a, rec0 + n1 - 1, slice, buf0, wave, lane);
     if constexpr (S::NBUF == 2) {
-        for (int64_t n = a.NC - 1; n >= 0; n -= 2) {
+        for (int64_t n = n1 - 1; n >= n0; n -= 2) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
-            if (n >= 1)
+            if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf1, wave, lane);
             scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave);
-            if (n == 0)
+            if (n == n0)
                 break;
             wait_copies();
             __syncthreads();          // chunk n - 1 is in buf1; everyone is done with buf0
-            if (n >= 2)
+            if (n - 2 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 2, slice, buf0, wave, lane);
             scan_chunk<E, D>(a, buf1, lam, rec0 + n - 1, col, lane, wave);
         }
     } else {
-        for (int64_t n = a.NC - 1; n >= 0; --n) {
+        for (int64_t n = n1 - 1; n >= n0; --n) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0
             scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave);
             __syncthreads();          // everyone is done with buf0
-            if (n >= 1)
+            if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf0, wave, lane);
         }
     }
-    if (a.dS0) {
+    if (a.dS0 && seg == 0) {
 #pragma unroll
         for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 a.dS0[(bh * D + 16 * kt + 4 * gq + i) * D + col] = lam[kt][i];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Two-level reverse scan, the mirror of the forward's: in reverse the chunk
+// step is affine in the gradient,
+//   Lam_prev = (diag(gamma) - W^T K^) Lam + (Q~^T - W^T P^T) dO,
+// and the chunks are cut into nseg segments of seg_len chunks.
+// bwd_span_kernel runs every segment but the first, in parallel, from its
+// end: the product of its chunks' transitions (carried from the identity as
+// D more columns) and its local gradient (from zero; the last segment from
+// dS_final, so that one is the true gradient at its start).  Entry e holds
+// segment nseg-1-e, so the segment fold (X = L_0, X <- Pi_e X + L_e) leaves
+// in the local half of entry e the gradient at the end of segment nseg-2-e,
+// where bwd_scan_kernel starts that segment.
+// ---------------------------------------------------------------------------
+template <bool LOCAL, typename E, int D>
+__device__ __forceinline__ void span_scan_chunk(const unsigned char* buf, f32x4* lam, int lane, int wave)
+{
+    typedef ScanShape<E, D> S;
+    typedef ScanFrags<E, D> F;
+    typedef Mma<E> MM;
+    typedef typename MM::Frag Frag;
+    constexpr int NB = F::NB, NKS = F::NKS, NKC = F::NKC, KT = F::KT, DT = F::DT;
+    const int gq = lane >> 4;
+    const unsigned char* fl = buf + lane * 16;
+    auto frag = [&](size_t off, int i) -> Frag { return *reinterpret_cast<const Frag*>(fl + off + (size_t)i * 1024); };
+    const float* sGam = reinterpret_cast<const float*>(buf + S::OFF_G);
+
+    Frag LB[NKS], OB[NKC];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        LB[ks] = MM::from_acc(&lam[ks * KT]);
+    if (LOCAL) {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+            OB[kc] = frag(S::OFF_O, wave * NKC + kc);
+    }
+    // dDelta = K^ X (+ P^T dO for the local columns)
+    f32x4 dd[NB];
+#pragma unroll
+    for (int st = 0; st < NB; ++st)
+        dd[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int st = 0; st < NB; ++st)
+            dd[st] = MM::mma(frag(F::OFF_K, st * NKS + ks), LB[ks], dd[st]);
+    if (LOCAL) {
+#pragma unroll
+        for (int st = 0; st < NB; ++st)
+#pragma unroll
+            for (int kc = st / KT; kc < NKC; ++kc)
+                dd[st] = MM::mma(frag(F::OFF_P, st * NKC + kc), OB[kc], dd[st]);
+    }
+    // X <- diag(gamma) X (+ Q~^T dO) - W^T dDelta
+    Frag DB[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        DB[kc] = MM::from_acc(&dd[kc * KT]);
+#pragma unroll
+    for (int kt = 0; kt < DT; ++kt)
+        lam[kt] = lam[kt] * *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * gq);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt) {
+            if (LOCAL)
+                lam[kt] = MM::mma(frag(F::OFF_Q, kt * NKC + kc), OB[kc], lam[kt]);
+            lam[kt] = MM::mma(frag(F::OFF_W, kt * NKC + kc), DB[kc], lam[kt]);
+        }
+}
+
+template <bool LOCAL, typename E, int D>
+__device__ __forceinline__ void span_scan_run(const BwdArgs& a, unsigned char* buf0, unsigned char* buf1, f32x4* lam,
+                                              int64_t rec0, int64_t n0, int64_t n1, int slice, int lane, int wave)
+{
+    typedef ScanShape<E, D> S;
+    scan_fetch<E, D>(a, rec0 + n1 - 1, slice, buf0, wave, lane);
+    if constexpr (S::NBUF == 2) {
+        for (int64_t n = n1 - 1; n >= n0; n -= 2) {
+            wait_copies();
+            __syncthreads();          // chunk n is in buf0; everyone is done with buf1
+            if (n - 1 >= n0)
+                scan_fetch<E, D>(a, rec0 + n - 1, slice, buf1, wave, lane);
+            span_scan_chunk<LOCAL, E, D>(buf0, lam, lane, wave);
+            if (n == n0)
+                break;
+            wait_copies();
+            __syncthreads();          // chunk n - 1 is in buf1; everyone is done with buf0
+            if (n - 2 >= n0)
+                scan_fetch<E, D>(a, rec0 + n - 2, slice, buf0, wave, lane);
+            span_scan_chunk<LOCAL, E, D>(buf1, lam, lane, wave);
+        }
+    } else {
+        for (int64_t n = n1 - 1; n >= n0; --n) {
+            wait_copies();
+            __syncthreads();          // chunk n is in buf0
+            span_scan_chunk<LOCAL, E, D>(buf0, lam, lane, wave);
+            __syncthreads();          // everyone is done with buf0
+            if (n - 1 >= n0)
+                scan_fetch<E, D>(a, rec0 + n - 1, slice, buf0, wave, lane);
+        }
+    }
+}
+
+// Workgroup -> ((b,h), entry e < nseg - 1, column slice): slices 0 .. NS-1
+// carry the product's columns, NS .. 2NS-1 the local gradient's.
+template <typename E, int D>
+__global__ __launch_bounds__(NTB) void bwd_span_kernel(BwdArgs a)
+{
+    typedef ScanShape<E, D> S;
+    constexpr int DT = D / 16, NS = S::NS;
+    __shared__ __align__(16) unsigned char buf0[S::BUF];
+    __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
+    const int64_t bx = blockIdx.x, grp = bx / (8 * 2 * NS);
+    const int within = (int)(bx % (8 * 2 * NS)), slice = within / 8;
+    const int64_t unit = grp * 8 + within % 8;       // (b*H + h) * (nseg - 1) + e
+    const int64_t nspan = a.nseg - 1;
+    if (unit >= a.nbh * nspan)
+        return;
+    const int64_t bh = unit / nspan, e = unit - bh * nspan, seg = a.nseg - 1 - e;
+    const bool local = slice >= NS;
+    if (e == 0 && !local)
+        return;                                      // the last segment needs no product
+    const int vs = local ? slice - NS : slice;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4;
+    const int col = vs * S::BV + 16 * wave + (lane & 15);
+    const int64_t n0 = seg * a.seg_len, n1 = min(a.NC, n0 + a.seg_len), rec0 = bh * a.NC;
+
+    f32x4 lam[DT];
+    if (local && e == 0 && a.dS_final) {
+        const float* l0 = a.dS_final + bh * D * D;
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lam[kt][i] = l0[(16 * kt + 4 * gq + i) * D + col];
+    } else {
+        const float one = local ? 0.f : 1.f;    // identity for the product, zero for the local gradient
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lam[kt][i] = 16 * kt + 4 * gq + i == col ? one : 0.f;
+    }
+    if (local)
+        span_scan_run<true, E, D>(a, buf0, buf1, lam, rec0, n0, n1, vs, lane, wave);
+    else
+        span_scan_run<false, E, D>(a, buf0, buf1, lam, rec0, n0, n1, vs, lane, wave);
+
+    float* dst = a.ws + a.L.span + ((bh * nspan + e) * 2 + (local ? 1 : 0)) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dst[(16 * kt + 4 * gq + i) * D + col] = lam[kt][i];
 }
 
 // ---------------------------------------------------------------------------
@@ -1995,8 +2165,9 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     a.dq = x.dq; a.dk = x.dk; a.dv = x.dv; a.db = x.db; a.dw = x.dw; a.dg = x.dg; a.dS0 = x.dS0;
     a.bw = x.b_width; a.ww = x.w_width; a.gw = x.g_width; a.pro = x.prologue;
     a.T = x.T; a.H = x.H; a.NC = cdiv(x.T, C);
-    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC);
     a.nbh = x.B * x.H;
+    segment_plan(x.algo, a.NC, a.nbh * ScanShape<E, D>::NS, &a.nseg, &a.seg_len);
+    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC, a.nseg);
     a.nrec = a.L.nrec;
     a.ws = static_cast<float*>(x.workspace);
     const int64_t nrec = a.nrec, rows = x.B * x.T * x.H;
@@ -2033,8 +2204,14 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     }
     hipLaunchKernelGGL((bwd_frag_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.nseg > 1) {
+        const int64_t groups = cdiv(a.nbh * (a.nseg - 1), 8) * 8 * 2 * ScanShape<E, D>::NS;
+        hipLaunchKernelGGL((bwd_span_kernel<E, D>), dim3((unsigned)groups), dim3(NTB), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (a.nseg > 2 && (e = launch_span_fold(a.ws + a.L.span, a.nbh, a.nseg, D, s)) != hipSuccess) return e;
+    }
     {
-        const int64_t groups = cdiv(a.nbh, 8) * 8 * ScanShape<E, D>::NS;
+        const int64_t groups = cdiv(a.nbh * a.nseg, 8) * 8 * ScanShape<E, D>::NS;
         hipLaunchKernelGGL((bwd_scan_kernel<E, D>), dim3((unsigned)groups), dim3(NTB), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2073,7 +2250,9 @@ size_t backward_workspace_bytes(const gdr2_bwd_args& a)
         return 0;
     const size_t esz = a.dtype == GDR2_BF16 ? 2 : 4;
     const size_t rec = (size_t)(4 * BC * a.Dk + BC * BC) * esz;   // ScanFrags<E, D>::REC
-    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec).total;
+    int64_t nseg, len;
+    segment_plan(a.algo, cdiv(a.T, BC), a.B * a.H * (a.Dk / 64), &nseg, &len);
+    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec, nseg).total;
 }
 
 hipError_t launch_backward(const gdr2_bwd_args& a, hipStream_t stream)

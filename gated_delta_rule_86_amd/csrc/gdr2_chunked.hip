@@ -1858,21 +1858,8 @@ struct SegPlan {
 
 SegPlan seg_plan(const gdr2_fwd_args& a)
 {
-    const int64_t NC = ceil_div(a.T, a.chunk), wgs = a.B * a.H * (a.Dk / 64);
-    SegPlan p{1, NC};
-    if (a.algo == GDR2_ALGO_STAGED || NC < 2 || wgs == 0)
-        return p;
-    const int64_t fill = (int64_t)cu_count() / wgs;
-    int64_t n;
-    if (a.algo == GDR2_ALGO_SEGMENTED) {
-        n = std::max<int64_t>(2, std::min(fill, NC));
-    } else {
-        n = std::min(fill, NC / 4);
-        if (n < 4)
-            return p;
-    }
-    p.len = ceil_div(NC, n);
-    p.nseg = ceil_div(NC, p.len);
+    SegPlan p;
+    segment_plan(a.algo, ceil_div(a.T, a.chunk), a.B * a.H * (a.Dk / 64), &p.nseg, &p.len);
     return p;
 }
 
@@ -1934,6 +1921,8 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
         if (sp.nseg > 2)
             hipLaunchKernelGGL((span_fold_kernel<D>), dim3((unsigned)(ceil_div(sa.nbh, 8) * 8 * (D / 16))), dim3(256),
                                0, stream, sa.span, sa.nbh, sp.nseg);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return e;
     }
     const int64_t grid2 = ceil_div(sa.nbh * sp.nseg, 8) * 8 * SS::NS;
     hipLaunchKernelGGL((chunk_state_kernel<E, D, C, BV>), dim3((unsigned)grid2), dim3(NT), 0, stream, sa);
@@ -1941,6 +1930,37 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
 }
 
 }  // namespace
+
+int device_cu_count() { return cu_count(); }
+
+void segment_plan(int algo, int64_t NC, int64_t wgs, int64_t* nseg, int64_t* len)
+{
+    *nseg = 1;
+    *len = NC;
+    if (algo == GDR2_ALGO_STAGED || NC < 2 || wgs <= 0)
+        return;
+    const int64_t fill = (int64_t)cu_count() / wgs;
+    int64_t n;
+    if (algo == GDR2_ALGO_SEGMENTED) {
+        n = std::max<int64_t>(2, std::min(fill, NC));
+    } else {
+        n = std::min(fill, NC / 4);
+        if (n < 4)
+            return;
+    }
+    *len = ceil_div(NC, n);
+    *nseg = ceil_div(NC, *len);
+}
+
+hipError_t launch_span_fold(float* span, int64_t nbh, int64_t nseg, int D, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)(ceil_div(nbh, 8) * 8 * (D / 16));
+    if (D == 128)
+        hipLaunchKernelGGL((span_fold_kernel<128>), dim3(grid), dim3(256), 0, stream, span, nbh, nseg);
+    else
+        hipLaunchKernelGGL((span_fold_kernel<64>), dim3(grid), dim3(256), 0, stream, span, nbh, nseg);
+    return hipGetLastError();
+}
 
 size_t staged_workspace_bytes(const gdr2_fwd_args& a)
 {

@@ -21,4 +21,18 @@ size_t staged_workspace_bytes(const gdr2_fwd_args& a);
 // Workspace of the chunked backward, in bytes (0 if nothing to do).
 size_t backward_workspace_bytes(const gdr2_bwd_args& a);
 
+// Compute units of the current device (256 when it cannot be queried).
+int device_cu_count();
+
+// Segments of a two-level scan over NC chunks run by `wgs` workgroups per
+// pass (gdr2_algo `algo`): *nseg segments of *len chunks (the last may be
+// shorter); nseg == 1 is one pass.
+void segment_plan(int algo, int64_t NC, int64_t wgs, int64_t* nseg, int64_t* len);
+
+// The segment fold of a two-level scan over `span` (per (b,h), nseg - 1
+// entries of two D x D fp32 matrices: a product Pi and a local part L):
+// X = L of entry 0, then X <- Pi_e X + L_e for e = 1 .. nseg-2, each X
+// written over L_e.  Launched only for nseg > 2.
+hipError_t launch_span_fold(float* span, int64_t nbh, int64_t nseg, int D, hipStream_t stream);
+
 }  // namespace gdr2

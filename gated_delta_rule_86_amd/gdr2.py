@@ -51,14 +51,15 @@ class BwdArgs(ctypes.Structure):
                 ("q", _vp), ("k", _vp), ("v", _vp), ("b", _vp), ("w", _vp), ("g", _vp),
                 ("S_chunks", _vp), ("dO", _vp), ("dS_final", _vp),
                 ("dq", _vp), ("dk", _vp), ("dv", _vp), ("db", _vp), ("dw", _vp), ("dg", _vp),
-                ("dS0", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("dS0", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("algo", _c_i32), ("reserved", _c_i32)]
 
 
 # Every symbol include/gdr2.h declares (checked by the tests).
 EXPORTS = ("gdr2_forward_workspace_size", "gdr2_forward_chunked", "gdr2_decode_step",
            "gdr2_backward_workspace_size", "gdr2_backward_chunked",
            "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version")
-ABI_VERSION = 4
+ABI_VERSION = 5
 BWD_CHUNK = 64
 
 
@@ -223,7 +224,7 @@ def decode_step(state, q, k, v, b, w, g, out=None, prologue: int = 0):
 
 
 def bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final=None, grads=None, dS0=None,
-             workspace=None, chunk: int = BWD_CHUNK, prologue: int = 0) -> BwdArgs:
+             workspace=None, chunk: int = BWD_CHUNK, prologue: int = 0, algo: str = "auto") -> BwdArgs:
     """grads: (dq, dk, dv, db, dw, dg) or None."""
     B, T, H, Dk = q.shape
     a = BwdArgs()
@@ -233,6 +234,7 @@ def bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final=None, grads=None, dS0=None
     a.q, a.k, a.v, a.b, a.w, a.g = (_ptr(x) for x in (q, k, v, b, w, g))
     a.S_chunks, a.dO, a.dS_final, a.dS0 = _ptr(S_chunks), _ptr(dO), _ptr(dS_final), _ptr(dS0)
     a.prologue = prologue
+    a.algo = ALGOS[algo]
     if grads is not None:
         a.dq, a.dk, a.dv, a.db, a.dw, a.dg = (_ptr(x) for x in grads)
     if workspace is not None:
@@ -240,19 +242,20 @@ def bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final=None, grads=None, dS0=None
     return a
 
 
-def backward_workspace_size(q, k, v, b, w, g) -> int:
+def backward_workspace_size(q, k, v, b, w, g, algo: str = "auto") -> int:
     lib = load_library()
-    return int(lib.gdr2_backward_workspace_size(ctypes.byref(bwd_args(q, k, v, b, w, g, None, None))))
+    return int(lib.gdr2_backward_workspace_size(ctypes.byref(bwd_args(q, k, v, b, w, g, None, None, algo=algo))))
 
 
 def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grads=None,
-             dS0=None, want_dS0: bool = True, prologue: int = 0):
+             dS0=None, want_dS0: bool = True, prologue: int = 0, algo: str = "auto"):
     """Chunked backward (chunk 64).  Inputs as for ``forward``; S_chunks is
     the float32 [B,H,ceil(T/64),Dk,Dv] chunk-start states of a chunk-64
     forward; dO [B,T,H,Dv] in the inputs' dtype; dS_final float32
     [B,H,Dk,Dv] or None.  Returns a dict of float32 gradients dq, dk, dv,
     db, dw, dg (shaped like their inputs) and dS0 (None unless want_dS0 or
-    given)."""
+    given).  algo: 'staged' (one reverse pass over the chunks per (b, h)),
+    'segmented' (the two-level scan over chunk segments) or 'auto'."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w), ("dO", dO)):
         _req(t, n, q.dtype)
@@ -266,7 +269,7 @@ def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grad
         grads = tuple(torch.empty(x.shape, dtype=torch.float32, device=q.device) for x in (q, k, v, b, w, g))
     if dS0 is None and want_dS0:
         dS0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    a = bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final, grads, dS0, prologue=prologue)
+    a = bwd_args(q, k, v, b, w, g, S_chunks, dO, dS_final, grads, dS0, prologue=prologue, algo=algo)
     need = lib.gdr2_backward_workspace_size(ctypes.byref(a))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

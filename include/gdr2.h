@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 4
+#define GDR2_ABI_VERSION 5
 
 typedef enum gdr2_status {
     GDR2_OK = 0,
@@ -234,6 +234,14 @@ typedef struct gdr2_bwd_args {
     float *dS0;
     void *workspace;      /* device memory, >= gdr2_backward_workspace_size() bytes */
     size_t workspace_bytes;
+    int32_t algo;         /* gdr2_algo of the reverse scan over the chunks:
+                             STAGED one pass per (b, h), SEGMENTED the
+                             two-level scan over chunk segments (a span
+                             kernel, the segment fold and the scan per
+                             segment, as in the forward), AUTO the library
+                             picks (the two-level scan when one pass would
+                             leave most of the GPU idle) */
+    int32_t reserved;     /* must be 0 */
 } gdr2_bwd_args;
 
 /* Bytes of device workspace gdr2_forward_chunked needs for these arguments

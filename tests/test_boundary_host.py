@@ -293,6 +293,8 @@ BWD_CASES = [
     ("chunk_32", _mod(chunk=32), gdr2.ERR_UNSUPPORTED),
     ("bad_dtype", _mod(dtype=2), gdr2.ERR_INVALID_ARG),
     ("bad_prologue", _mod(prologue=8), gdr2.ERR_INVALID_ARG),
+    ("bad_algo", _mod(algo=3), gdr2.ERR_INVALID_ARG),
+    ("reserved_set", _mod(reserved=1), gdr2.ERR_INVALID_ARG),
     ("bad_w_width", _mod(w_width=2), gdr2.ERR_INVALID_ARG),
     ("null_S_chunks", _mod(S_chunks=None), gdr2.ERR_INVALID_ARG),
     ("null_dO", _mod(dO=None), gdr2.ERR_INVALID_ARG),
@@ -352,6 +354,28 @@ def test_backward_workspace_size_formula(lib):
     a = good_bwd()
     a.chunk = 32
     assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_backward_segmented_workspace_size(lib):
+    """The backward's two-level reverse scan adds, per (b, h) and per segment
+    but the first, a chunk product and a local gradient (D x D fp32 each),
+    with the forward's segment plan (on 256 CUs, which the host without a
+    GPU counts): one (b, h) at d = 128 runs 2 scan workgroups per pass, so
+    AUTO cuts 100 chunks into 25 segments of 4 and SEGMENTED into 100 of 1."""
+    def al(x):
+        return (x + 63) // 64 * 64
+
+    def size(algo, **kw):
+        a = good_bwd(**kw)
+        a.algo = algo
+        return lib.gdr2_backward_workspace_size(ctypes.byref(a))
+
+    shape = dict(B=1, T=6400, H=1, D=128)
+    base = size(gdr2.ALGO_STAGED, **shape)
+    assert size(gdr2.ALGO_AUTO, **shape) == base + 4 * al(24 * 2 * 128 * 128)
+    assert size(gdr2.ALGO_SEGMENTED, **shape) == base + 4 * al(99 * 2 * 128 * 128)
+    big = dict(B=8, T=4096, H=16, D=128)       # 256 workgroups already: one pass
+    assert size(gdr2.ALGO_AUTO, **big) == size(gdr2.ALGO_STAGED, **big)
 
 
 def test_backward_empty_is_a_noop(lib):

@@ -31,12 +31,12 @@ def _narrow(inp, widths):
     return out
 
 
-def _gpu_backward(d, fwd_chunk=64, fwd_algo="auto"):
+def _gpu_backward(d, fwd_chunk=64, fwd_algo="auto", bwd_algo="auto"):
     args = [d[n] for n in NAMES]
     _, _, ck = gdr2.forward(*args, S0=d["S0"], chunk=fwd_chunk, chunk_states=True, algo=fwd_algo)
     if fwd_chunk != 64:                     # chunk-64 starts are every other chunk-32 start
         ck = ck[:, :, ::64 // fwd_chunk].contiguous()
-    return gdr2.backward(*args, S_chunks=ck, dO=d["dO"], dS_final=d["dS_final"])
+    return gdr2.backward(*args, S_chunks=ck, dO=d["dO"], dS_final=d["dS_final"], algo=bwd_algo)
 
 
 def _oracle_backward(inp):
@@ -123,6 +123,30 @@ def test_backward_from_two_level_forward():
     got = _gpu_backward(to_dev(inp), fwd_algo="segmented")
     torch.cuda.synchronize()
     _compare("seg_bwd", got, _oracle_backward(inp), TOL["bf16"])
+
+
+# The two-level reverse scan forced on small shapes; plans on 256 CUs in
+# the ids (segments x chunks each).  g is scaled down in some cases so the
+# segment products carry weight.
+SEG_CASES = [
+    # name, B, T, H, D, dtype, g_scale, dS_final std, backward algo
+    ("bf16_d128_32x1_weak", 1, 2048, 2, 128, "bf16", 0.05, 1.0, "segmented"),
+    ("bf16_d64_16x1", 2, 1000, 1, 64, "bf16", 1.0, 1.0, "segmented"),
+    ("bf16_d128_4x3_ragged", 4, 700, 8, 128, "bf16", 1.0, 0.5, "segmented"),
+    ("f32_d64_8x1_weak", 1, 500, 2, 64, "f32", 0.05, 1.0, "segmented"),
+    ("f32_d128_5x1", 1, 300, 1, 128, "f32", 1.0, 1.0, "segmented"),
+    ("bf16_d128_auto_16x4_weak", 1, 4096, 2, 128, "bf16", 0.02, 1.0, "auto"),
+]
+
+
+@pytest.mark.parametrize("name,B,T,H,D,dtype,gs,ds,algo", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_backward_two_level_scan(name, B, T, H, D, dtype, gs, ds, algo):
+    wl = Workload(name, "forward", B, T, H, D, dtype, "full", 0.05, 64, 612, g_scale=gs)
+    inp = draw(wl)
+    inp.update(draw_cotangents(wl, ds))
+    got = _gpu_backward(to_dev(inp), fwd_chunk=32 if (dtype == "f32" and D == 128) else 64, bwd_algo=algo)
+    torch.cuda.synchronize()
+    _compare(name, got, _oracle_backward(inp), TOL[dtype])
 
 
 def test_state_gradient_only():
