@@ -248,11 +248,13 @@ def bench_decode(torch, gdr2, lib, steps: int, warmup: int):
             "GBps": byts / (us * 1e-6) / 1e9, "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
-def bench_long(torch, gdr2, lib, steps: int, warmup: int, algos=("auto", "staged"), stages=("all", "state")):
+def bench_long(torch, gdr2, lib, steps: int, warmup: int, algos=("auto", "staged"), stages=("all", "state"),
+               backward: bool = True):
     """The long-context forward: one sequence of 65536 tokens, 16 heads,
     d = 128, bf16, S0 ~ N(0, 0.02^2).  One pass over the 1024 chunks runs only
     32 state workgroups; the library's default here is the two-level scan over
-    chunk segments.  Both are timed, with the state stage alone."""
+    chunk segments.  Both are timed, with the state stage alone, and the
+    backward over the same sequence with its reverse scan either way."""
     from gated_delta_rule_86_amd.inputs import WORKLOADS, draw
 
     wl = WORKLOADS["long_64k"]
@@ -282,6 +284,33 @@ def bench_long(torch, gdr2, lib, steps: int, warmup: int, algos=("auto", "staged
             if stage == "all":
                 res[key + "_tokens_per_s"] = round(wl.B * wl.T / (ms * 1e-3), 1)
         del ws
+    if backward:
+        # the backward over the same sequence (chunk-start states from the
+        # forward): one reverse pass, and the two-level reverse scan
+        from gated_delta_rule_86_amd.inputs import draw_cotangents
+        cot = {n: t.cuda() for n, t in draw_cotangents(wl, 1.0).items() if t is not None}
+        _, _, ck = gdr2.forward(*x, S0=d["S0"], chunk=64, chunk_states=True)
+        for algo in algos:
+            ws = torch.empty(gdr2.backward_workspace_size(*x, algo=algo), dtype=torch.uint8, device="cuda")
+            grads = tuple(torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in x)
+            dS0 = torch.empty_like(S_out)
+            run = lambda: gdr2.backward(*x, S_chunks=ck, dO=cot["dO"], dS_final=cot["dS_final"], workspace=ws,
+                                        grads=grads, dS0=dS0, algo=algo)
+            for _ in range(2):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            key = "backward_" + ("segmented" if algo == "auto" else "one_pass")
+            res[key + "_ms"] = round(ms, 4)
+            res[key + "_tokens_per_s"] = round(wl.B * wl.T / (ms * 1e-3), 1)
+            del ws, grads, dS0
+        del ck, cot
     del d, x, o, S_out
     torch.cuda.empty_cache()
     return res
@@ -344,7 +373,7 @@ def main():
     lib = gdr2.load_library()
     if args.long_only:
         # the library's default algorithm only, whole calls: one kernel of each kind per call
-        res = bench_long(torch, gdr2, lib, args.steps, args.warmup, algos=("auto",), stages=("all",))
+        res = bench_long(torch, gdr2, lib, args.steps, args.warmup, algos=("auto",), stages=("all",), backward=False)
         print(json.dumps({"long_context": res}), flush=True)
         return
     wl = WORKLOADS["train_4k"]
