@@ -20,15 +20,19 @@
 //
 // Kernels (all fp32 arithmetic; intermediates in a fp32 workspace, one
 // record per (sequence, head, chunk)):
-//   bwd_prep   one workgroup per chunk: G, U, E~, Q~, K^, gamma; M and P
-//              as 16x16 blocks through block-referenced rows (fp32 MFMA);
-//              X by blocks; W, U~ (fp32 MFMA).
+//   bwd_prep   one workgroup per chunk: G, U, E~, gamma; M and P as 16x16
+//              blocks through block-referenced rows (fp32 MFMA); X by
+//              blocks; W, U~ (fp32 MFMA); and the scan's K^, P^T, Q~^T,
+//              -W^T operands in MFMA fragment order.
 //   bwd_dout   (fp32 inputs) dO rows of every chunk into the workspace (zero
 //              past T); the other kernels read dO from the input.
-//   bwd_frag   the scan's operands in MFMA fragment order.
-//   bwd_scan   per (sequence, head, 64 value columns): the state gradient
-//              through the chunks in reverse (columns evolve independently),
-//              recording Lam at every chunk end and dDelta.
+//   bwd_frag   the scan's dO^T fragments.
+//   bwd_span   (few sequences x heads, many chunks) per chunk segment: the
+//              segment's transition product and local gradient, for the
+//              two-level reverse scan.
+//   bwd_scan   per (sequence, head, chunk segment, 64 value columns): the
+//              state gradient through the chunks in reverse (columns evolve
+//              independently), recording Lam at every chunk end and dDelta.
 //   bwd_sgrad, bwd_xgrad  per chunk: the state and WY-factor products
 //              above.  bf16 inputs: every operand read once, staged in LDS
 //              in bf16, intermediates (Delta, dX, T1) kept on chip; fp32
