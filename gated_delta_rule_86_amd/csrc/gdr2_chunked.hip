@@ -20,6 +20,9 @@
 //               value columns of S evolve independently, so they split
 //               exactly) walks the chunks in order with the fp32 state in
 //               MFMA accumulators.
+// With few sequences x heads and many chunks, a two-level scan over chunk
+// segments replaces the one pass (chunk_span, span_fold, then chunk_state
+// per segment; see the section on it below).
 //
 // The workspace holds every factor in MFMA operand order.  A "fragment" is
 // one A operand tile of the state kernel -- 16 rows x KB k-values (KB = 32
