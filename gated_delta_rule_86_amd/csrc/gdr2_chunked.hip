@@ -1838,12 +1838,19 @@ template <int WB, int WW, int WG, bool PRO, typename E, int D, int C>
 hipError_t launch_prep(const PrepArgs& pa, int64_t grid, hipStream_t stream)
 {
     typedef PrepShape<E, D, C> PS;
-    // more than 64 KiB of dynamic LDS: requested once per variant
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prep_kernel<WB, WW, WG, PRO, E, D, C>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
-    if (attr != hipSuccess)
-        return attr;
+    // more than 64 KiB of dynamic LDS: requested once per variant and device
+    // (the attribute belongs to the device current at the call)
+    static int done[64] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || !done[dev]) {
+        const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&chunk_prep_kernel<WB, WW, WG, PRO, E, D, C>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)PS::SMEM);
+        if (attr != hipSuccess)
+            return attr;
+        if (dev >= 0 && dev < 64)
+            done[dev] = 1;
+    }
     hipLaunchKernelGGL((chunk_prep_kernel<WB, WW, WG, PRO, E, D, C>), dim3((unsigned)grid), dim3(NTP), PS::SMEM,
                        stream, pa);
     return hipSuccess;
