@@ -928,9 +928,12 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
     // the gradient at the segment's end: dS_final (or zero) for the last
     // segment, else what the segment fold left for it (the null test
     // outside the loads, so that they are all in flight at once)
-    const float* l0 = seg == a.nseg - 1
-                          ? (a.dS_final ? a.dS_final + bh * D * D : nullptr)
-                          : a.ws + a.L.span + ((bh * (a.nseg - 1) + (a.nseg - 2 - seg)) * 2 + 1) * D * D;
+    // (with segments, the last one starts from the span pass's copy of
+    // dS_final, as dS0 may be dS_final)
+    const float* l0 = seg < a.nseg - 1 ? a.ws + a.L.span + ((bh * (a.nseg - 1) + (a.nseg - 2 - seg)) * 2 + 1) * D * D
+                      : !a.dS_final    ? nullptr
+                      : a.nseg > 1     ? a.ws + a.L.span + bh * (a.nseg - 1) * 2 * D * D
+                                       : a.dS_final + bh * D * D;
     f32x4 lam[DT];
     if (l0) {
 #pragma unroll
@@ -1114,6 +1117,15 @@ __global__ __launch_bounds__(NTB) void bwd_span_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 lam[kt][i] = l0[(16 * kt + 4 * gq + i) * D + col];
+        // a copy of dS_final in entry 0's product half (the last segment has
+        // no product): the scan starts the last segment from it, since dS0
+        // may be dS_final and segment 0 writes dS0 in that same pass
+        float* c0 = a.ws + a.L.span + bh * nspan * 2 * D * D;
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                c0[(16 * kt + 4 * gq + i) * D + col] = lam[kt][i];
     } else {
         const float one = local ? 0.f : 1.f;    // identity for the product, zero for the local gradient
 #pragma unroll

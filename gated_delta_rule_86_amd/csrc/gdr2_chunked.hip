@@ -1445,10 +1445,13 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
     const int col = slice * BV + 16 * wave + cl;     // this lane's state column
     E* sOw = sO + wave * C * S::LDO;
 
-    // start state: S0 (or zero) for the first segment, else the one the
-    // segment fold left in the local-state half of the previous segment
-    const float* s0 = seg == 0 ? (a.S0 ? a.S0 + bh * D * D : nullptr)
-                               : a.span + ((bh * (a.nseg - 1) + seg - 1) * 2 + 1) * D * D;
+    // start state: S0 (or zero) for the first segment -- with segments, the
+    // span pass's copy of it, as S_out may be S0 -- else the one the segment
+    // fold left in the local-state half of the previous segment
+    const float* s0 = seg > 0   ? a.span + ((bh * (a.nseg - 1) + seg - 1) * 2 + 1) * D * D
+                      : !a.S0   ? nullptr
+                      : a.nseg > 1 ? a.span + bh * (a.nseg - 1) * 2 * D * D
+                                   : a.S0 + bh * D * D;
     f32x4 St[KTS];
     if (s0) {
 #pragma unroll
@@ -1657,6 +1660,15 @@ __global__ __launch_bounds__(NT, 2) void chunk_span_kernel(StateArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 St[kt][i] = s0[(16 * kt + 4 * gq + i) * D + col];
+        // a copy of S0 in entry 0's product half (segment 0 has no product):
+        // the state pass starts segment 0 from it, since S_out may be S0 and
+        // the last segment writes S_out in that same pass
+        float* c0 = a.span + bh * nspan * 2 * D * D;
+#pragma unroll
+        for (int kt = 0; kt < KTS; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                c0[(16 * kt + 4 * gq + i) * D + col] = St[kt][i];
     } else {
         const float one = local ? 0.f : 1.f;    // identity for the product, zero for the local state
 #pragma unroll

@@ -149,6 +149,25 @@ def test_backward_two_level_scan(name, B, T, H, D, dtype, gs, ds, algo):
     _compare(name, got, _oracle_backward(inp), TOL[dtype])
 
 
+def test_backward_inplace_state_gradient_two_level():
+    """dS0 aliasing dS_final under the two-level reverse scan: the last
+    segment starts from the span pass's copy of dS_final while segment 0
+    writes dS0 in the same pass; equal bit for bit to the out-of-place call."""
+    wl = Workload("inplace_bwd", "forward", 1, 1024, 2, 128, "bf16", "full", 0.05, 64, 613, g_scale=0.05)
+    inp = draw(wl)
+    inp.update(draw_cotangents(wl, 1.0))
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    _, _, ck = gdr2.forward(*args, S0=d["S0"], chunk=64, chunk_states=True)
+    g1 = gdr2.backward(*args, S_chunks=ck, dO=d["dO"], dS_final=d["dS_final"], algo="segmented")
+    dS = d["dS_final"].clone()
+    g2 = gdr2.backward(*args, S_chunks=ck, dO=d["dO"], dS_final=dS, dS0=dS, algo="segmented")
+    torch.cuda.synchronize()
+    assert g2["dS0"].data_ptr() == dS.data_ptr()
+    for n in GRADS + ("dS0",):
+        assert torch.equal(g1[n], g2[n]), n
+
+
 def test_state_gradient_only():
     """dO = 0: every gradient flows from dS_final through the chunk-level
     recurrence alone.  The decay is weakened (g scaled by 0.02) so that dS0

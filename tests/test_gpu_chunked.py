@@ -106,6 +106,21 @@ def test_inplace_state_and_chaining():
     assert normwise(to_f64(o_all), o_ref) <= TOL["bf16"]
 
 
+def test_inplace_state_two_level_scan():
+    """S_out aliasing S0 under the two-level scan: segment 0 starts from the
+    span pass's copy of S0 while the last segment writes S_out in the same
+    pass, so the result equals the out-of-place call bit for bit."""
+    wl = Workload("inplace_seg", "forward", 1, 2000, 2, 128, "bf16", "full", 0.05, 64, 32, g_scale=0.05)
+    d = to_dev(draw(wl))
+    args = [d[n] for n in NAMES]
+    o1, S1 = gdr2.forward(*args, S0=d["S0"], chunk=64, algo="segmented")
+    S = d["S0"].clone()
+    o2, S2 = gdr2.forward(*args, S0=S, S_out=S, chunk=64, algo="segmented")
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S)
+
+
 def test_zero_length_copies_state():
     wl = Workload("t0", "forward", 2, 0, 3, 64, "bf16", "full", 0.05, 64, 5)
     inp = draw(wl)
