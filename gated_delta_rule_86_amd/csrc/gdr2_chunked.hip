@@ -150,7 +150,7 @@ struct PrepArgs {
     const float* g;
     int bw, ww, gw;
     int pro;                  // prologue bits (normalise q, k; activate gates)
-    int64_t T, H, NC, nrec;
+    int64_t B, T, H, NC, nrec;
     void *Wn, *Ut, *Kh, *Qt, *P;
     float* gam;
 };
@@ -269,34 +269,37 @@ struct ChunkPos {
     int L;            // valid tokens (>= 1)
 };
 
-// Walks the items blockIdx.x, blockIdx.x + gridDim.x, ... as (b, n, h) with
-// carries, so the loop divides only once.
+// Walks the items blockIdx.x, blockIdx.x + gridDim.x, ... with carries, so
+// the loop divides only once.  Item i is (m, b, h) with the head fastest and
+// m = NC - 1 - n slowest: the chunks are visited last to first, so the
+// records written last -- the ones the memory-side cache still holds when
+// the state pass starts -- are the early chunks that pass reads first.
 struct ItemWalk {
-    int64_t b, n, h;          // current item
-    int64_t db, dn, dh;       // one step of gridDim.x items
-    __device__ __forceinline__ void init(int64_t i, int64_t step, int64_t NC, int64_t H)
+    int64_t m, b, h;          // current item, m = NC - 1 - n
+    int64_t dm, db, dh;       // one step of gridDim.x items
+    __device__ __forceinline__ void init(int64_t i, int64_t step, int64_t B, int64_t H)
     {
-        const int64_t bn = i / H, sn = step / H;
-        h = i - bn * H;
-        n = bn % NC;
-        b = bn / NC;
-        dh = step - sn * H;
-        dn = sn % NC;
-        db = sn / NC;
+        const int64_t mb = i / H, sm = step / H;
+        h = i - mb * H;
+        b = mb % B;
+        m = mb / B;
+        dh = step - sm * H;
+        db = sm % B;
+        dm = sm / B;
     }
-    __device__ __forceinline__ void advance(int64_t NC, int64_t H)
+    __device__ __forceinline__ void advance(int64_t B, int64_t H)
     {
         h += dh;
         const int64_t ch = h >= H;
         h -= ch * H;
-        n += dn + ch;
-        const int64_t cn = n >= NC;
-        n -= cn * NC;
-        b += db + cn;
+        b += db + ch;
+        const int64_t cb = b >= B;
+        b -= cb * B;
+        m += dm + cb;
     }
     __device__ __forceinline__ ChunkPos pos(int64_t NC, int64_t T, int64_t H, int C) const
     {
-        const int64_t t0 = n * C;
+        const int64_t n = NC - 1 - m, t0 = n * C;
         ChunkPos p;
         p.rec = (b * H + h) * NC + n;
         p.row0 = (b * T + t0) * H + h;
@@ -690,7 +693,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
     if (it >= a.nrec)
         return;
     ItemWalk walk;
-    walk.init(it, gridDim.x, a.NC, a.H);
+    walk.init(it, gridDim.x, a.B, a.H);
     {
         const int lane = threadIdx.x & 63;
         const ChunkPos cp0 = walk.pos(a.NC, a.T, a.H, C);
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         __syncthreads();   // B0: this chunk's g rows are in LDS, its tokens in Rn
         R = Rn;
         const ChunkPos cp = walk.pos(a.NC, a.T, a.H, C);
-        walk.advance(a.NC, a.H);
+        walk.advance(a.B, a.H);
         const int64_t next = it + gridDim.x;
         const bool pre = ab && next < a.nrec;   // this lane prefetches tokens
         const ChunkPos np = walk.pos(a.NC, a.T, a.H, C);
@@ -1898,7 +1901,7 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     PrepArgs pa;
     pa.q = a.q; pa.k = a.k; pa.v = a.v; pa.b = a.b; pa.w = a.w; pa.g = a.g;
     pa.bw = a.b_width; pa.ww = a.w_width; pa.gw = a.g_width; pa.pro = a.prologue;
-    pa.T = a.T; pa.H = a.H; pa.NC = ceil_div(a.T, C); pa.nrec = L.nrec;
+    pa.B = a.B; pa.T = a.T; pa.H = a.H; pa.NC = ceil_div(a.T, C); pa.nrec = L.nrec;
     pa.Wn = ws + L.wn; pa.Ut = ws + L.ut; pa.Kh = ws + L.kh; pa.Qt = ws + L.qt; pa.P = ws + L.p;
     pa.gam = reinterpret_cast<float*>(ws + L.gam);
 
