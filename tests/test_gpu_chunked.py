@@ -52,6 +52,24 @@ def test_ragged_lengths(dtype, D, C, T):
     check(draw(wl), C, dtype, f"{dtype} D={D} C={C} T={T}")
 
 
+# The prep pass is persistent (one workgroup per CU, items visited with a
+# stride of the grid size, last chunk first): head counts above the grid
+# size, item counts that are not a multiple of it, and several chunks per
+# sequence exercise every carry of that walk.
+WALK_CASES = [
+    # B, T, H
+    (1, 64, 300),
+    (2, 130, 200),
+    (3, 100, 7),
+]
+
+
+@pytest.mark.parametrize("B,T,H", WALK_CASES, ids=[f"B{b}_T{t}_H{h}" for b, t, h in WALK_CASES])
+def test_prep_item_walk(B, T, H):
+    wl = Workload("walk", "forward", B, T, H, 64, "bf16", "full", 0.05, 64, 17 * H + T + B)
+    check(draw(wl), 64, "bf16", f"walk B={B} T={T} H={H}")
+
+
 WIDTH_CFGS = [("bf16", 128, 64), ("f32", 64, 32), ("bf16", 64, 32)]
 WIDTH_MIXES = [(nb, nw, ng) for nb in (0, 1) for nw in (0, 1) for ng in (0, 1)]
 
