@@ -198,52 +198,97 @@ def bench_prologue(torch, gdr2, lib, d, steps: int):
     return res
 
 
+def host_cpu_info() -> dict:
+    """The host this process runs on: the CPU model, how many cores the OS
+    shows, how many this process may use, and OMP_NUM_THREADS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc_online": os.cpu_count(), "affinity_cores": affinity,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(inp, wl):
     """The fp64 oracle (as it stands) on the host cores over the whole
-    workload batch: every (b, h) recurrence, OpenMP over them."""
+    workload batch: every (b, h) recurrence, OpenMP over them, with as many
+    threads as this process is granted (OMP_NUM_THREADS when it is set --
+    the share of the host that goes with one GPU -- else every core of the
+    affinity set).  Also one recurrence on one thread, the per-core rate.
+    Returns the baseline record and the oracle's (o, S_final)."""
     import oracle
-    from gated_delta_rule_86_amd.inputs import to_f64
+    from gated_delta_rule_86_amd.inputs import select_heads, to_f64
 
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    threads = max(1, min(ncpu, 16, wl.B * wl.H))
+    host = host_cpu_info()
+    omp = host["OMP_NUM_THREADS"]
+    granted = int(omp) if omp and omp.isdigit() and int(omp) > 0 else host["affinity_cores"]
+    threads = max(1, min(granted, wl.B * wl.H))
     args = [to_f64(inp[n]) for n in NAMES]
     t0 = time.perf_counter()
-    oracle.forward(*args, S0=to_f64(inp["S0"]), threads=threads)
+    o_ref, S_ref = oracle.forward(*args, S0=to_f64(inp["S0"]), threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
-            "sample": f"the whole batch: {wl.B * wl.H} (b,h) recurrences x T={wl.T}, "
-                      f"fp64, {threads} OpenMP threads"}
+    one = select_heads(inp, [(0, 0)])
+    a1 = [to_f64(one[n]) for n in NAMES]
+    t1 = time.perf_counter()
+    oracle.forward(*a1, S0=to_f64(one["S0"]), threads=1)
+    dt1 = time.perf_counter() - t1
+    rec = {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "seconds": dt,
+           "sample": f"the whole batch: {wl.B * wl.H} (b,h) recurrences x T={wl.T}, fp64, "
+                     f"{threads} OpenMP threads (OpenMP over the independent recurrences)",
+           "single_thread": {"recurrence_tokens": wl.T, "seconds": dt1,
+                             "token_heads_per_s": wl.T / dt1},
+           **host}
+    return rec, o_ref, S_ref
 
 
-def bench_decode(torch, gdr2, lib, steps: int, warmup: int):
+def bench_decode(torch, gdr2, lib, steps: int, warmup: int, sets: int = 1):
+    """`steps` batched decode steps (256 sequences x 16 heads, one token
+    each).  With sets > 1, that many independent state sets take turns (step
+    i updates set i % sets), so the working set is sets x 268 MB: two or
+    more exceed the 256 MB memory-side cache, and the state then streams
+    from HBM.  Every call's status is checked."""
     from gated_delta_rule_86_amd.inputs import WORKLOADS, draw, draw_decode_tokens
 
     wl = WORKLOADS["decode"]
-    state = draw(wl)["state"].cuda()
+    base = draw(wl)["state"]
+    states = [base.cuda() for _ in range(sets)]
     ring = []
     for s in range(8):                         # 8 token sets reused cyclically
         tok = {n: t.cuda() for n, t in draw_decode_tokens(wl, s).items() if t is not None}
         o = torch.empty((wl.B, wl.H, wl.D), dtype=tok["q"].dtype, device="cuda")
-        ring.append(gdr2.decode_args(state, *(tok[n] for n in NAMES), o))
-        ring[-1]._keep = (tok, o)
+        ring.append([gdr2.decode_args(st, *(tok[n] for n in NAMES), o) for st in states])
+        for a in ring[-1]:
+            a._keep = (tok, o)
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
-        assert lib.gdr2_decode_step(ctypes.byref(ring[i % 8]), stream) == 0
+        assert lib.gdr2_decode_step(ctypes.byref(ring[i % 8][i % sets]), stream) == 0
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bad = 0
     e0.record()
     for i in range(steps):
-        lib.gdr2_decode_step(ctypes.byref(ring[i % 8]), stream)
+        bad |= lib.gdr2_decode_step(ctypes.byref(ring[i % 8][i % sets]), stream)
     e1.record()
     torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError("gdr2_decode_step failed: " + lib.gdr2_last_error().decode())
     us = e0.elapsed_time(e1) * 1e3 / steps
     nstate = wl.B * wl.H
     byts = nstate * (2 * wl.D * wl.D * 4 + (5 * wl.D) * 2 + wl.D * 4 + wl.D * 2)
+    del states, ring
+    torch.cuda.empty_cache()
     return {"workload": "decode: 256 sequences x 16 heads, d=128, bf16 tokens, fp32 state",
+            "state_sets": sets, "working_set_bytes": sets * nstate * wl.D * wl.D * 4,
             "steps": steps, "us_per_step": us, "algorithmic_bytes_per_step": byts,
             "GBps": byts / (us * 1e-6) / 1e9, "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
@@ -339,12 +384,32 @@ def plain_copy(torch, reps: int = 3):
             "GBps": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}
 
 
+def parity_errors(o, S, o_ref, S_ref) -> dict:
+    """Normwise error per (b, h) slice, max over the slices: max |x - y| over
+    the slice / max |y| over the slice, for o and for S_final."""
+    import numpy as np
+
+    def nw(x, y, btd):
+        x = np.asarray(x, np.float64)
+        y = np.asarray(y, np.float64)
+        if btd:
+            x, y = np.moveaxis(x, 2, 1), np.moveaxis(y, 2, 1)
+        x = x.reshape(x.shape[0] * x.shape[1], -1)
+        y = y.reshape(y.shape[0] * y.shape[1], -1)
+        den = np.abs(y).max(axis=1)
+        return float((np.abs(x - y).max(axis=1) / np.where(den == 0, 1.0, den)).max())
+
+    return {"o": nw(o, o_ref, True), "S_final": nw(S, S_ref, False), "tolerance": 2e-2,
+            "slices": int(o_ref.shape[0] * o_ref.shape[2]),
+            "metric": "max over (b,h) slices of max|gpu - oracle| / max|oracle|, oracle fp64 on the same "
+                      "bf16 inputs"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first (the clocks settle within ~25 ms of load)")
+    ap.add_argument("--warmup", type=int, default=50, help="untimed steps right before the timed ones")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -362,6 +427,8 @@ def main():
               "no multi-GPU run is part of this build)", file=sys.stderr)
         sys.exit(2)
 
+    import statistics
+
     import torch
 
     from gated_delta_rule_86_amd import gdr2
@@ -376,6 +443,21 @@ def main():
         res = bench_long(torch, gdr2, lib, args.steps, args.warmup, algos=("auto",), stages=("all",), backward=False)
         print(json.dumps({"long_context": res}), flush=True)
         return
+    K = args.steps
+    extra = {}
+    # Legs other than the headline run first: they are timed on their own,
+    # and by the time the headline loop starts the GPU has been busy for
+    # a while (its clocks have settled).  Their GPU time is reported.
+    t_legs = time.perf_counter()
+    if not args.no_decode:
+        extra["decode"] = bench_decode(torch, gdr2, lib, args.decode_steps, 20, sets=1)
+        # two and four independent state sets (537 MB, 1.07 GB): more than the
+        # 256 MB memory-side cache holds, so the state streams from HBM
+        extra["decode_hbm_working_set"] = [bench_decode(torch, gdr2, lib, args.decode_steps, 20, sets=n)
+                                           for n in (2, 4)]
+    if not args.no_long:
+        extra["long_context"] = bench_long(torch, gdr2, lib, max(1, K // 2), 5)
+
     wl = WORKLOADS["train_4k"]
     inp = draw(wl)
     d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
@@ -383,6 +465,16 @@ def main():
     o = torch.empty((B, T, H, D), dtype=d["q"].dtype, device="cuda")
     S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     x = [d[n] for n in NAMES]
+    if not args.no_gate_widths:
+        extra["gate_widths"] = bench_gate_widths(torch, gdr2, lib, d, K)
+        extra["prologue"] = bench_prologue(torch, gdr2, lib, d, K)
+    if not args.no_backward:
+        # one training step of the layer: the forward that also records the
+        # chunk-start states, then the backward
+        extra["backward"] = bench_backward(torch, gdr2, lib, wl, d, max(1, K // 2), 2)
+    torch.cuda.synchronize()
+    legs_s = time.perf_counter() - t_legs
+
     need = gdr2.workspace_size(*x, chunk=C)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     a_all = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=C, workspace=ws)
@@ -398,9 +490,8 @@ def main():
     for _ in range(args.warmup):
         call(a_all)
     torch.cuda.synchronize()
-    K = args.steps
-    # The step: K whole forward calls (both kernels, one API call each),
-    # events only at the ends of the timed region.
+    # The step: K whole forward calls (every kernel of the path, one API
+    # call each), events only at the ends of the timed region.
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -411,10 +502,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = e_start.elapsed_time(e_end) / K
-    # The per-kernel split for the roofline: the same K steps, each kernel
-    # bracketed by events on the launch stream (a stage call per kernel).
-    # The events between kernels cost a little, so these durations sum to
-    # slightly more than the step.
+    o_gpu, S_gpu = o.float().cpu(), S_out.cpu()
+    # The same K steps with an event between consecutive steps: the spread
+    # of single steps (min, median).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(K):
+        call(a_all)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+    # The per-kernel split: the same K steps, each kernel bracketed by
+    # events on the launch stream (a stage call per kernel).  The events
+    # between kernels cost a little, so these durations sum to slightly
+    # more than the step.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
@@ -433,52 +535,62 @@ def main():
     esz = 2
     prep_b, state_b, min_b = staged_bytes(B, T, H, D, C, esz, D, D, D, d["S0"] is not None, True)
     flops = algorithmic_flops_per_chunk(C, D) * B * H * (T // C)
-    kernels = {"gdr2_chunk_prep[b,w,g=d,d,d]": (prep_ms, prep_b), "gdr2_chunk_state": (state_ms, state_b)}
-    dom = max(kernels, key=lambda n: kernels[n][0])
-    dom_ms, dom_b = kernels[dom]
-    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    kernels = {"gdr2_chunk_prep[b,w,g=d,d,d]": prep_ms, "gdr2_chunk_state": state_ms}
+    own_bytes = {"gdr2_chunk_prep[b,w,g=d,d,d]": prep_b, "gdr2_chunk_state": state_b}
+    dom = max(kernels, key=lambda n: kernels[n])
+    dom_ms = kernels[dom]
+    # Algorithmic bytes of the path: the minimum a single fused pass moves
+    # (q, k, v, b, w in bf16 and g in fp32 read once, o in bf16 written once:
+    # 2048 B per token-head at d = 128, plus S_final), charged to the
+    # dominant kernel's launch -- the kernels' own workspace traffic is not
+    # algorithmic.
+    achieved = min_b / (dom_ms * 1e-3) / 1e9
     from gated_delta_rule_86_amd.rocprof_summary import read_traffic
     measured = read_traffic(TRAFFIC_SUMMARY) or {}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured.get(dom), "kernel": dom,
-                "algorithmic_bytes_per_launch": dom_b}
-
-    extra = {
+                "kernel_avg_us": round(dom_ms * 1e3, 2),
+                "algorithmic_bytes_per_launch": min_b,
+                "algorithmic_bytes_basis": "2048 B per token-head (q,k,v,b,w bf16 and g fp32 read once, "
+                                           "o bf16 written once) x 524288 token-heads + S_final",
+                "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE of these kernel sources, "
+                                   "profiles/hbm_traffic_train_4k.md") if measured.get(dom) else None}
+    t_mem_min = min_b / (HBM_PEAK_GBS * 1e9)
+    t_mfma_min = flops / (BF16_DENSE_PEAK_TFLOPS * 1e12)
+    extra.update({
         "step_ms": round(step_ms, 4), "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "step_ms_min": round(min(per_step), 4), "step_ms_median": round(statistics.median(per_step), 4),
+        "host_seconds_of_gpu_work_before_timed_loop": round(legs_s, 2),
         "prep_ms": round(prep_ms, 4), "state_ms": round(state_ms, 4),
         "split_step_ms_with_events_between_kernels": round(split_step_ms, 4),
-        "prep_GBps": round(prep_b / (prep_ms * 1e-3) / 1e9, 1),
-        "state_GBps": round(state_b / (state_ms * 1e-3) / 1e9, 1),
         "path_min_bytes": min_b,
+        "path_roofline_frac": round(max(t_mem_min, t_mfma_min) / (step_ms * 1e-3), 4),
         "path_hbm_frac_of_min_bytes": round(min_b / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_own_bytes": {n: {"bytes": own_bytes[n], "GBps": round(own_bytes[n] / (kernels[n] * 1e-3) / 1e9, 1),
+                                 "note": "the kernel's own reads and writes, workspace included"}
+                             for n in kernels},
         "algorithmic_flops": flops,
         "mfma_frac_bf16_dense": round(flops / (step_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
         "pages_context": "38.0 Kt/s (2K) and 36.1 Kt/s (8K): whole-model GDN-2 training "
                          "throughput on unstated hardware; not comparable",
-    }
-    if not args.no_decode:
-        extra["decode"] = bench_decode(torch, gdr2, lib, args.decode_steps, 20)
-    if not args.no_gate_widths:
-        extra["gate_widths"] = bench_gate_widths(torch, gdr2, lib, d, K)
-        extra["prologue"] = bench_prologue(torch, gdr2, lib, d, K)
-    if not args.no_backward:
-        # one training step of the layer: the forward that also records the
-        # chunk-start states, then the backward
-        extra["backward"] = bench_backward(torch, gdr2, lib, wl, d, max(1, K // 2), 2)
+    })
     if measured:
         extra["hbm_traffic_bytes_per_launch"] = measured
+        fwd_traffic = sum(measured.get(n, 0) for n in kernels)
+        if all(n in measured for n in kernels):
+            extra["path_counter_traffic_bytes"] = fwd_traffic
+            extra["path_counter_traffic_over_min_bytes"] = round(fwd_traffic / min_b, 3)
 
     del d, x, o, S_out, ws
     torch.cuda.empty_cache()
-    if not args.no_long:
-        extra["long_context"] = bench_long(torch, gdr2, lib, max(1, K // 2), 5)
     if not args.no_copy:
         extra["plain_copy"] = plain_copy(torch)
         pc = extra["plain_copy"]["GBps"]
         extra["step_frac_of_plain_copy_bw"] = round(min_b / (step_ms * 1e-3) / 1e9 / pc, 4)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, wl)
+        cpu, o_ref, S_ref = cpu_baseline(inp, wl)
+        extra["parity"] = parity_errors(o_gpu.numpy(), S_gpu.numpy(), o_ref, S_ref)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

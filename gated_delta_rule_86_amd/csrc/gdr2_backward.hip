@@ -73,10 +73,16 @@ struct BwdLayout {
     // two-level scan (nseg > 1): per (b,h) and segment but the first, a
     // chunk product and a local gradient, D x D fp32 each
     size_t span;
+    // width-1 gates (narrow): per record, token and key-channel group of the
+    // decay kernel, that group's partial sums of db, dw and dg
+    // ([3][nrec*C][D/DC]); bwd_gate_sum adds the groups in order
+    size_t GP;
     size_t total;
 };
 
-BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, int64_t nseg)
+constexpr int DC = 32;                 // channels per decay workgroup
+
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, int64_t nseg, bool narrow)
 {
     BwdLayout L;
     L.nrec = B * H * cdiv(T, BC);
@@ -104,6 +110,9 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, i
     L.span = o;
     if (nseg > 1)
         o += a64((size_t)(B * H) * (nseg - 1) * 2 * D * D);
+    L.GP = o;
+    if (narrow)
+        o += a64((size_t)3 * L.nrec * BC * (D / DC));
     L.total = o * sizeof(float);
     return L;
 }
@@ -1686,7 +1695,6 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
 //   u >= t:  f = e^{G_u - G_t};  dk[t]   += (dM[u,t] e_u + dP[u,t] q_u) f
 // (dM is strictly lower, so the u == t terms of dM vanish.)
 // ---------------------------------------------------------------------------
-constexpr int DC = 32;                 // channels per decay workgroup
 constexpr int LC = DC + 1;             // padded LDS row of the per-channel arrays
 constexpr int LPC = BC + 4;            // padded LDS row of dM and dP (16-byte aligned)
 
@@ -1767,6 +1775,12 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
     float* sQ = sK + C * LC;        // [C][LC] q
     float* sdG = sQ + C * LC;       // [C][LC] dG, then dg
     float* sGL = sdG + C * LC;      // [DC] dG_L
+    // width-1 gates, in the epilogue (e, k and q rows are no longer read
+    // then): per-thread partials of db and dw [C][DC/4], per-channel dg [C][DC]
+    float* sRb = sE;
+    float* sRw = sRb + C * (DC / 4);
+    float* sRg = sRw + C * (DC / 4);
+    static_assert(2 * C * (DC / 4) + C * DC <= 3 * C * LC, "partials fit the e, k, q rows");
     __shared__ int sOr[2 * (NTB / 64)];
     // workgroup -> (chunk record, channel group): the D/DC groups of a
     // record share blockIdx % 8, i.e. one XCD, so the dM and dP they all
@@ -2076,16 +2090,34 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
             *reinterpret_cast<f32x4*>(a.dv + off) = dU * wv;
             const f32x4 dbv = dE * kv * bd, dwv = dU * vv * wd;
             if (a.bw == 1)
-                atomicAdd(a.db + row, dbv[0] + dbv[1] + dbv[2] + dbv[3]);
+                sRb[e4] = (dbv[0] + dbv[1]) + (dbv[2] + dbv[3]);
             else
                 *reinterpret_cast<f32x4*>(a.db + off) = dbv;
             if (a.ww == 1)
-                atomicAdd(a.dw + row, dwv[0] + dwv[1] + dwv[2] + dwv[3]);
+                sRw[e4] = (dwv[0] + dwv[1]) + (dwv[2] + dwv[3]);
             else
                 *reinterpret_cast<f32x4*>(a.dw + off) = dwv;
         }
     }
     lds_barrier();
+    // width-1 erase / write gate: this group's DC channels summed per token
+    // in channel order (the groups are added in order by bwd_gate_sum, so
+    // the result does not depend on scheduling)
+    if ((a.bw == 1 || a.ww == 1) && tid < rc.L) {
+        constexpr int NP4 = DC / 4;
+        float sb = 0.f, sw = 0.f;
+#pragma unroll
+        for (int j = 0; j < NP4; ++j) {
+            sb += sRb[tid * NP4 + j];
+            sw += sRw[tid * NP4 + j];
+        }
+        const size_t gi = ((size_t)r * C + tid) * (D / DC) + i0 / DC;
+        const size_t np = (size_t)a.nrec * C * (D / DC);
+        if (a.bw == 1)
+            a.ws[a.L.GP + gi] = sb;
+        if (a.ww == 1)
+            a.ws[a.L.GP + np + gi] = sw;
+    }
     // dg: reverse cumulative sum over the chunk, per channel: each thread
     // scans its RPT tokens, then adds the later row groups' totals
     float vg[RPT];
@@ -2116,9 +2148,50 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
         if (a.pro & GDR2_PROLOGUE_GATES)      // d/dx[-softplus(x)] = -sigmoid(x)
             dgv *= -bsigm(a.g[a.gw == 1 ? row : row * D + i]);
         if (a.gw == 1)
-            atomicAdd(a.dg + row, dgv);
+            sRg[t * DC + il] = dgv;
         else
             a.dg[row * D + i] = dgv;
+    }
+    if (a.gw == 1) {
+        // width-1 decay: this group's channels summed per token in order
+        lds_barrier();
+        if (tid < rc.L) {
+            float sg = 0.f;
+            for (int j = 0; j < DC; ++j)
+                sg += sRg[tid * DC + j];
+            const size_t np = (size_t)a.nrec * C * (D / DC);
+            a.ws[a.L.GP + 2 * np + ((size_t)r * C + tid) * (D / DC) + i0 / DC] = sg;
+        }
+    }
+}
+
+// Width-1 gate gradients: the partial sums the D/DC decay workgroups of a
+// chunk left per token, added in group order (one thread per token).
+template <int D>
+__global__ __launch_bounds__(NTB) void bwd_gate_sum_kernel(BwdArgs a)
+{
+    constexpr int C = BC, NG = D / DC;
+    const int64_t e = (int64_t)blockIdx.x * NTB + threadIdx.x;
+    const int64_t r = e / C;
+    const int t = (int)(e - r * C);
+    if (r >= a.nrec)
+        return;
+    const Rec rc = rec_of(r, a.NC, a.T, a.H);
+    if (t >= rc.L)
+        return;
+    const int64_t row = rc.row0 + (int64_t)t * a.H;
+    const size_t np = (size_t)a.nrec * C * NG;
+    const float* gp = a.ws + a.L.GP + (size_t)e * NG;
+    float* outs[3] = {a.bw == 1 ? a.db : nullptr, a.ww == 1 ? a.dw : nullptr, a.gw == 1 ? a.dg : nullptr};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        if (!outs[x])
+            continue;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+            s += gp[x * np + j];
+        outs[x][row] = s;
     }
 }
 
@@ -2183,15 +2256,12 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     a.T = x.T; a.H = x.H; a.NC = cdiv(x.T, C);
     a.nbh = x.B * x.H;
     segment_plan(x.algo, a.NC, a.nbh * ScanShape<E, D>::NS, &a.nseg, &a.seg_len);
-    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC, a.nseg);
+    const bool narrow = a.bw == 1 || a.ww == 1 || a.gw == 1;
+    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC, a.nseg, narrow);
     a.nrec = a.L.nrec;
     a.ws = static_cast<float*>(x.workspace);
     const int64_t nrec = a.nrec, rows = x.B * x.T * x.H;
     hipError_t e;
-    // width-1 gate gradients accumulate over channels
-    if (a.bw == 1 && (e = zero_fill(a.db, rows, s)) != hipSuccess) return e;
-    if (a.ww == 1 && (e = zero_fill(a.dw, rows, s)) != hipSuccess) return e;
-    if (a.gw == 1 && (e = zero_fill(a.dg, rows, s)) != hipSuccess) return e;
 
     const size_t lds_prep = BwdPrepShape<D>::SMEM;
     const size_t lds_decay = (size_t)(2 * C * LPC + 5 * C * LC + DC) * 4;
@@ -2250,6 +2320,10 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(cdiv(nrec, 8) * 8 * (D / DC))), dim3(NTB), lds_decay, s,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (narrow) {
+        hipLaunchKernelGGL((bwd_gate_sum_kernel<D>), dim3((unsigned)cdiv(nrec * C, NTB)), dim3(NTB), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.pro & GDR2_PROLOGUE_NORM_QK) {
         constexpr int RPB = NTB / (D / 4);
         hipLaunchKernelGGL((bwd_norm_kernel<E, D>), dim3((unsigned)cdiv(rows, RPB)), dim3(NTB), 0, s,
@@ -2268,7 +2342,8 @@ size_t backward_workspace_bytes(const gdr2_bwd_args& a)
     const size_t rec = (size_t)(4 * BC * a.Dk + BC * BC) * esz;   // ScanFrags<E, D>::REC
     int64_t nseg, len;
     segment_plan(a.algo, cdiv(a.T, BC), a.B * a.H * (a.Dk / 64), &nseg, &len);
-    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec, nseg).total;
+    const bool narrow = a.b_width == 1 || a.w_width == 1 || a.g_width == 1;
+    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec, nseg, narrow).total;
 }
 
 hipError_t launch_backward(const gdr2_bwd_args& a, hipStream_t stream)

@@ -258,11 +258,13 @@ __device__ __forceinline__ float dpp_shr(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + d, 0xF, 0xF, true));
 }
 
-// Work item -> chunk.  Items run in (sequence, chunk, head) order, so the
-// workgroups in flight together read whole token rows: the H heads of a
-// token are one contiguous run of H*D elements of the [B,T,H,.] inputs.
-// Token row r of the chunk is element offset ((b*T + t0 + r)*H + h); the
-// chunk's record in the workspace is (b*H + h)*NC + n.
+// Work item -> chunk.  The persistent prep kernel visits items in the order
+// (chunk taken last to first, sequence, head) with the head fastest (see
+// ItemWalk), so the workgroups in flight together read whole token rows: the
+// H heads of a token are one contiguous run of H*D elements of the
+// [B,T,H,.] inputs.  Token row r of the chunk is element offset
+// ((b*T + t0 + r)*H + h); the chunk's record in the workspace is
+// (b*H + h)*NC + n.
 struct ChunkPos {
     int64_t rec;      // workspace record
     int64_t row0;     // (b*T + t0)*H + h

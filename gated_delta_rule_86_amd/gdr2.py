@@ -122,13 +122,82 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _req(t: torch.Tensor, name: str, dtype=None):
+def _req(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    """Dtype, exact shape (when given), then device and contiguity of one
+    tensor argument.  The library takes every size from q (or the state)
+    and the chunk, so a tensor of another shape would be read or written out
+    of bounds: it is refused here, before any launch."""
+    _req_shape(t, name, dtype, shape)
+    _req_dev(t, name, device)
+
+
+def _req_shape(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _req_dev(t: torch.Tensor, name: str, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _gate_shape(t: torch.Tensor, name: str, lead, full: int):
+    """Shape of a gate: lead + (1,) or lead + (full,), by its last dim."""
+    if t.dim() != len(lead) + 1 or t.shape[-1] not in (1, full):
+        raise ValueError(f"{name} must have shape {tuple(lead) + (1,)} or {tuple(lead) + (full,)}, "
+                         f"got {tuple(t.shape)}")
+    return tuple(lead) + (t.shape[-1],)
+
+
+def check_forward_shapes(q, k, v, b, w, g, S0=None):
+    """Dtypes and shapes of the forward's (and backward's) inputs against
+    q [B,T,H,Dk] and v [B,T,H,Dv]; returns (B, T, H, Dk, Dv).  Raises
+    ValueError / TypeError on a mismatch (no device is touched)."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"q and v must be [B,T,H,D], got {tuple(q.shape)} and {tuple(v.shape)}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported dtype {q.dtype} (float32 or bfloat16)")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    lead = (B, T, H)
+    _req_shape(k, "k", q.dtype, (B, T, H, Dk))
+    _req_shape(v, "v", q.dtype, (B, T, H, Dv))
+    _req_shape(b, "b", q.dtype, _gate_shape(b, "b", lead, Dk))
+    _req_shape(w, "w", q.dtype, _gate_shape(w, "w", lead, Dv))
+    _req_shape(g, "g", torch.float32, _gate_shape(g, "g", lead, Dk))
+    if S0 is not None:
+        _req_shape(S0, "S0", torch.float32, (B, H, Dk, Dv))
+    return B, T, H, Dk, Dv
+
+
+def check_decode_shapes(state, q, k, v, b, w, g):
+    """Dtypes and shapes of one decode step's arguments against state
+    [N,H,Dk,Dv]; returns (N, H, Dk, Dv)."""
+    _req_shape(state, "state", torch.float32)
+    if state.dim() != 4:
+        raise ValueError(f"state must be [N,H,Dk,Dv], got {tuple(state.shape)}")
+    N, H, Dk, Dv = state.shape
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported dtype {q.dtype} (float32 or bfloat16)")
+    _req_shape(q, "q", None, (N, H, Dk))
+    _req_shape(k, "k", q.dtype, (N, H, Dk))
+    _req_shape(v, "v", q.dtype, (N, H, Dv))
+    _req_shape(b, "b", q.dtype, _gate_shape(b, "b", (N, H), Dk))
+    _req_shape(w, "w", q.dtype, _gate_shape(w, "w", (N, H), Dv))
+    _req_shape(g, "g", torch.float32, _gate_shape(g, "g", (N, H), Dk))
+    return N, H, Dk, Dv
+
+
+def _on_device(dev, **tensors):
+    for n, t in tensors.items():
+        if t is not None:
+            _req_dev(t, n, dev)
 
 
 def fwd_args(q, k, v, b, w, g, S0=None, o=None, S_out=None, chunk: int = 64,
@@ -158,31 +227,32 @@ def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
     stage='prep' / 'state' runs one kernel of the staged algorithm (pass the
     same workspace, out and S_out to both calls).  prologue: PROLOGUE_* bits
     (raw q, k normalised and raw gates activated inside the kernels)."""
+    B, T, H, Dk, Dv = check_forward_shapes(q, k, v, b, w, g, S0)
+    if chunk <= 0:
+        raise ValueError(f"chunk must be positive, got {chunk}")
+    if out is not None:
+        _req_shape(out, "out", q.dtype, (B, T, H, Dv))
+    if S_out is not None:
+        _req_shape(S_out, "S_out", torch.float32, (B, H, Dk, Dv))
+    ckt = chunk_states if isinstance(chunk_states, torch.Tensor) else None
+    if ckt is not None:
+        _req_shape(ckt, "chunk_states", torch.float32, (B, H, -(-T // chunk), Dk, Dv))
+    _on_device(q.device, q=q, k=k, v=v, b=b, w=w, g=g, S0=S0, out=out, S_out=S_out, chunk_states=ckt,
+               workspace=workspace)
     lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w)):
-        _req(t, n, q.dtype)
-    _req(g, "g", torch.float32)
-    if S0 is not None:
-        _req(S0, "S0", torch.float32)
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
     if out is None:
         out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
     if S_out is None and final_state:
         S_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    ck = None
-    if chunk_states is not None and chunk_states is not False:
-        if chunk_states is True:
-            ck = torch.empty((B, H, -(-T // chunk), Dk, Dv), dtype=torch.float32, device=q.device)
-        else:
-            ck = chunk_states
-            _req(ck, "chunk_states", torch.float32)
+    ck = ckt
+    if chunk_states is True:
+        ck = torch.empty((B, H, -(-T // chunk), Dk, Dv), dtype=torch.float32, device=q.device)
     a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, stage=stage, S_chunks=ck, prologue=prologue)
     need = lib.gdr2_forward_workspace_size(ctypes.byref(a))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib, lib.gdr2_forward_chunked(ctypes.byref(a), stream))
     return (out, S_out) if ck is None else (out, S_out, ck)
@@ -209,12 +279,11 @@ def decode_step(state, q, k, v, b, w, g, out=None, prologue: int = 0):
     """One decode step, in place on ``state`` float32 [N,H,Dk,Dv].
     q,k [N,H,Dk]; v [N,H,Dv]; b [N,H,1|Dk]; w [N,H,1|Dv]; g float32 [N,H,1|Dk].
     Returns o [N,H,Dv]."""
+    N, H, Dk, Dv = check_decode_shapes(state, q, k, v, b, w, g)
+    if out is not None:
+        _req_shape(out, "out", q.dtype, (N, H, Dv))
+    _on_device(state.device, state=state, q=q, k=k, v=v, b=b, w=w, g=g, out=out)
     lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w)):
-        _req(t, n, q.dtype)
-    _req(g, "g", torch.float32)
-    _req(state, "state", torch.float32)
-    N, H, Dk, Dv = state.shape
     if out is None:
         out = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
     a = decode_args(state, q, k, v, b, w, g, out, prologue)
@@ -256,15 +325,22 @@ def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grad
     db, dw, dg (shaped like their inputs) and dS0 (None unless want_dS0 or
     given).  algo: 'staged' (one reverse pass over the chunks per (b, h)),
     'segmented' (the two-level scan over chunk segments) or 'auto'."""
-    lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("b", b), ("w", w), ("dO", dO)):
-        _req(t, n, q.dtype)
-    _req(g, "g", torch.float32)
-    _req(S_chunks, "S_chunks", torch.float32)
+    B, T, H, Dk, Dv = check_forward_shapes(q, k, v, b, w, g)
+    dev = q.device
+    _req_shape(dO, "dO", q.dtype, (B, T, H, Dv))
+    _req_shape(S_chunks, "S_chunks", torch.float32, (B, H, -(-T // BWD_CHUNK), Dk, Dv))
     if dS_final is not None:
-        _req(dS_final, "dS_final", torch.float32)
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
+        _req_shape(dS_final, "dS_final", torch.float32, (B, H, Dk, Dv))
+    if grads is not None:
+        if len(grads) != 6:
+            raise ValueError("grads must be (dq, dk, dv, db, dw, dg)")
+        for n, gt, x in zip(("dq", "dk", "dv", "db", "dw", "dg"), grads, (q, k, v, b, w, g)):
+            _req_shape(gt, n, torch.float32, tuple(x.shape))
+    if dS0 is not None:
+        _req_shape(dS0, "dS0", torch.float32, (B, H, Dk, Dv))
+    _on_device(dev, q=q, k=k, v=v, b=b, w=w, g=g, dO=dO, S_chunks=S_chunks, dS_final=dS_final, dS0=dS0,
+               workspace=workspace, **({} if grads is None else dict(zip(("dq", "dk", "dv", "db", "dw", "dg"), grads))))
+    lib = load_library()
     if grads is None:
         grads = tuple(torch.empty(x.shape, dtype=torch.float32, device=q.device) for x in (q, k, v, b, w, g))
     if dS0 is None and want_dS0:
@@ -274,7 +350,7 @@ def backward(q, k, v, b, w, g, S_chunks, dO, dS_final=None, workspace=None, grad
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib, lib.gdr2_backward_chunked(ctypes.byref(a), stream))
     return dict(zip(("dq", "dk", "dv", "db", "dw", "dg"), grads), dS0=dS0)

@@ -354,6 +354,14 @@ def test_backward_workspace_size_formula(lib):
     a = good_bwd()
     a.chunk = 32
     assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == 0
+    # any width-1 gate adds the decay workgroups' partial sums of db, dw, dg
+    # per token and 32-channel group, [3][nrec*C][D/32] fp32, which a last
+    # kernel adds in group order (no atomics)
+    for widths in ((1, 128, 128), (128, 1, 128), (128, 128, 1), (1, 1, 1)):
+        full = lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd()))
+        nrec = 2 * 3 * 2
+        got = lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(widths=widths)))
+        assert got == full + al(3 * nrec * 64 * (128 // 32) * 4), widths
 
 
 def test_backward_segmented_workspace_size(lib):
@@ -397,3 +405,79 @@ def test_backward_accepts_inplace_state_gradient(lib):
     a.dv = None
     assert call_bwd(lib, a) == gdr2.ERR_INVALID_ARG
     assert b"dv is NULL" in lib.gdr2_last_error()
+
+
+def _shape_case(mod):
+    """Forward inputs of one consistent shape on the host, with `mod`
+    replacing some of them (the binding checks shapes before devices)."""
+    import torch
+    B, T, H, D = 2, 70, 3, 64
+    t = {n: torch.zeros(B, T, H, D) for n in ("q", "k", "v", "b", "w", "g")}
+    t["S0"] = torch.zeros(B, H, D, D)
+    t.update(mod(t))
+    return t
+
+
+SHAPE_CASES = [
+    ("k_short_T", lambda t: {"k": t["k"][:, :69]}),
+    ("v_wrong_heads", lambda t: {"v": t["v"][:, :, :2]}),
+    ("b_width_2", lambda t: {"b": t["b"][..., :2]}),
+    ("w_missing_dim", lambda t: {"w": t["w"][..., 0]}),
+    ("g_wrong_batch", lambda t: {"g": t["g"][:1]}),
+    ("S0_wrong_dv", lambda t: {"S0": t["S0"][..., :32]}),
+]
+
+
+@pytest.mark.parametrize("name,mod", SHAPE_CASES, ids=[c[0] for c in SHAPE_CASES])
+def test_python_forward_refuses_mismatched_shapes(name, mod):
+    """A tensor whose shape disagrees with q is refused before any device
+    check or launch: the library would take its size from q."""
+    t = _shape_case(mod)
+    with pytest.raises(ValueError, match="shape"):
+        gdr2.forward(*(t[n] for n in ("q", "k", "v", "b", "w", "g")), S0=t["S0"])
+
+
+def test_python_forward_refuses_mismatched_outputs():
+    import torch
+    t = _shape_case(lambda t: {})
+    args = [t[n] for n in ("q", "k", "v", "b", "w", "g")]
+    with pytest.raises(ValueError, match="shape"):
+        gdr2.forward(*args, out=torch.zeros(2, 70, 3, 32))
+    with pytest.raises(ValueError, match="shape"):
+        gdr2.forward(*args, S_out=torch.zeros(2, 3, 64, 32))
+    # chunk states made for another chunk size
+    with pytest.raises(ValueError, match="shape"):
+        gdr2.forward(*args, chunk=64, chunk_states=torch.zeros(2, 3, 3, 64, 64))
+    with pytest.raises(TypeError):
+        gdr2.forward(*args, out=torch.zeros(2, 70, 3, 64, dtype=torch.bfloat16))
+
+
+def test_python_decode_refuses_mismatched_shapes():
+    import torch
+    N, H, D = 4, 2, 64
+    st = torch.zeros(N, H, D, D)
+    tok = {n: torch.zeros(N, H, D) for n in ("q", "k", "v", "b", "w", "g")}
+    for n, bad in (("q", torch.zeros(N, H, 32)), ("v", torch.zeros(N, 1, D)), ("b", torch.zeros(N, H, 3)),
+                   ("g", torch.zeros(N + 1, H, D))):
+        x = dict(tok, **{n: bad})
+        with pytest.raises(ValueError, match="shape"):
+            gdr2.decode_step(st, *(x[m] for m in ("q", "k", "v", "b", "w", "g")))
+    with pytest.raises(ValueError, match="shape"):
+        gdr2.decode_step(st, *(tok[m] for m in ("q", "k", "v", "b", "w", "g")), out=torch.zeros(N, H, 32))
+
+
+def test_python_backward_refuses_mismatched_shapes():
+    import torch
+    t = _shape_case(lambda t: {})
+    args = [t[n] for n in ("q", "k", "v", "b", "w", "g")]
+    B, T, H, D = t["q"].shape
+    ck = torch.zeros(B, H, 2, D, D)
+    dO = torch.zeros(B, T, H, D)
+    good = dict(S_chunks=ck, dO=dO)
+    for kw in (dict(good, S_chunks=torch.zeros(B, H, 3, D, D)),     # chunk-32 states
+               dict(good, dO=torch.zeros(B, T - 1, H, D)),
+               dict(good, dS_final=torch.zeros(B, H, D, 1)),
+               dict(good, dS0=torch.zeros(B, 1, D, D)),
+               dict(good, grads=tuple(torch.zeros(B, T, H, D) for _ in range(5)) + (torch.zeros(B, T, H, 2),))):
+        with pytest.raises(ValueError, match="shape"):
+            gdr2.backward(*args, **kw)
