@@ -139,7 +139,7 @@ gdr2_status check_token_ptrs(const TokenTensors& t, int64_t rows, int64_t Dk, in
     return GDR2_OK;
 }
 
-gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
+gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes, bool with_workspace = true)
 {
     if (!a)
         return fail(GDR2_ERR_INVALID_ARG, "args is NULL");
@@ -197,7 +197,7 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes)
         // S0 is an input as well: o must not overlap it.
         if (overlaps(range("o", a->o, rows * a->Dv * elt_bytes(a->dtype)), S0))
             return fail(GDR2_ERR_INVALID_ARG, "o overlaps input S0");
-        size_t need = gdr2::staged_workspace_bytes(*a);
+        size_t need = with_workspace ? gdr2::staged_workspace_bytes(*a) : 0;
         if (need > 0) {
             if (!a->workspace || a->workspace_bytes < need)
                 return fail(GDR2_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
@@ -307,6 +307,25 @@ gdr2_status validate_backward(const gdr2_bwd_args* a)
 }
 
 }  // namespace
+
+namespace gdr2 {
+
+gdr2_status check_forward_args(const gdr2_fwd_args* a)
+{
+    int64_t state_bytes = 0;
+    return validate_forward(a, &state_bytes, false);
+}
+
+gdr2_status set_error(gdr2_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(tl_error, sizeof(tl_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+}  // namespace gdr2
 
 extern "C" {
 

@@ -21,6 +21,12 @@ size_t staged_workspace_bytes(const gdr2_fwd_args& a);
 // Workspace of the chunked backward, in bytes (0 if nothing to do).
 size_t backward_workspace_bytes(const gdr2_bwd_args& a);
 
+// Every check of gdr2_forward_chunked except the workspace's (host only).
+gdr2_status check_forward_args(const gdr2_fwd_args* a);
+
+// Records a message for gdr2_last_error() in the calling thread; returns s.
+gdr2_status set_error(gdr2_status s, const char* fmt, ...);
+
 // Compute units of the current device (256 when it cannot be queried).
 int device_cu_count();
 

@@ -58,8 +58,9 @@ class BwdArgs(ctypes.Structure):
 # Every symbol include/gdr2.h declares (checked by the tests).
 EXPORTS = ("gdr2_forward_workspace_size", "gdr2_forward_chunked", "gdr2_decode_step",
            "gdr2_backward_workspace_size", "gdr2_backward_chunked",
-           "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version")
-ABI_VERSION = 5
+           "gdr2_status_string", "gdr2_last_error", "gdr2_abi_version", "gdr2_forward_chunked_noalloc")
+ABI_VERSION = 6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 BWD_CHUNK = 64
 
 
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH):
         lib.gdr2_forward_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
         lib.gdr2_forward_chunked.restype = ctypes.c_int
         lib.gdr2_forward_chunked.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+        lib.gdr2_forward_chunked_noalloc.restype = ctypes.c_int
+        lib.gdr2_forward_chunked_noalloc.argtypes = [ctypes.POINTER(FwdArgs), _vp]
         lib.gdr2_decode_step.restype = ctypes.c_int
         lib.gdr2_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         lib.gdr2_backward_workspace_size.restype = ctypes.c_size_t
@@ -256,6 +259,32 @@ def forward(q, k, v, b, w, g, S0=None, chunk: int = 64, algo: str = "auto",
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib, lib.gdr2_forward_chunked(ctypes.byref(a), stream))
     return (out, S_out) if ck is None else (out, S_out, ck)
+
+
+def forward_noalloc(q, k, v, b, w, g, S0=None, out=None, S_out=None, chunk: int = 64, algo: str = "auto",
+                    chunk_states=None, prologue: int = 0):
+    """The chunked forward through gdr2_forward_chunked_noalloc: the
+    workspace is the library's static device scratch (NOALLOC_SCRATCH_BYTES
+    per device), so the library allocates nothing.  Pass `out` and `S_out`
+    (and chunk_states) preallocated to allocate nothing here either.  Calls
+    that overlap in time on one device share that scratch and race."""
+    B, T, H, Dk, Dv = check_forward_shapes(q, k, v, b, w, g, S0)
+    if out is not None:
+        _req_shape(out, "out", q.dtype, (B, T, H, Dv))
+    if S_out is not None:
+        _req_shape(S_out, "S_out", torch.float32, (B, H, Dk, Dv))
+    if chunk_states is not None:
+        _req_shape(chunk_states, "chunk_states", torch.float32, (B, H, -(-T // chunk), Dk, Dv))
+    _on_device(q.device, q=q, k=k, v=v, b=b, w=w, g=g, S0=S0, out=out, S_out=S_out, chunk_states=chunk_states)
+    lib = load_library()
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if S_out is None:
+        S_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    a = fwd_args(q, k, v, b, w, g, S0, out, S_out, chunk, algo, S_chunks=chunk_states, prologue=prologue)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib, lib.gdr2_forward_chunked_noalloc(ctypes.byref(a), stream))
+    return out, S_out
 
 
 def workspace_size(q, k, v, b, w, g, chunk: int = 64, algo: str = "auto") -> int:

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDR2_ABI_VERSION 5
+#define GDR2_ABI_VERSION 6
 
 typedef enum gdr2_status {
     GDR2_OK = 0,
@@ -262,6 +262,26 @@ gdr2_status gdr2_backward_chunked(const gdr2_bwd_args *args, void *stream);
 
 /* One recurrent decode step for every (sequence, head) state. */
 gdr2_status gdr2_decode_step(const gdr2_decode_args *args, void *stream);
+
+/* Bytes of the library's static device scratch used by
+ * gdr2_forward_chunked_noalloc (one copy per device, held until the process
+ * ends). */
+#define GDR2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* The chunked forward for callers that cannot allocate device memory: code
+ * under HIP stream/graph capture, tight serving loops, hosts that forbid
+ * hipMalloc.  Same arguments, results and checks as gdr2_forward_chunked,
+ * except that args->workspace and args->workspace_bytes are ignored: the
+ * workspace is the library's static device scratch of
+ * GDR2_NOALLOC_SCRATCH_BYTES bytes.  The call allocates nothing (no
+ * hipMalloc, no hipFree).  Arguments whose workspace
+ * (gdr2_forward_workspace_size) exceeds the scratch return
+ * GDR2_ERR_WORKSPACE and launch nothing.  Every call on one device shares
+ * that device's scratch: calls that may overlap in time on one device (other
+ * streams, other threads) race and must be serialised by the caller.  The
+ * scratch's address is looked up on the first call on each device (a HIP
+ * error then returns GDR2_ERR_HIP). */
+gdr2_status gdr2_forward_chunked_noalloc(const gdr2_fwd_args *args, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *gdr2_status_string(gdr2_status status);

@@ -481,3 +481,21 @@ def test_python_backward_refuses_mismatched_shapes():
                dict(good, grads=tuple(torch.zeros(B, T, H, D) for _ in range(5)) + (torch.zeros(B, T, H, 2),))):
         with pytest.raises(ValueError, match="shape"):
             gdr2.backward(*args, **kw)
+
+
+def test_noalloc_refuses_before_touching_a_device(lib):
+    """gdr2_forward_chunked_noalloc checks its arguments on the host: a call
+    needing more workspace than the static scratch holds is refused with
+    GDR2_ERR_WORKSPACE (the caller's workspace fields are ignored), and
+    invalid arguments as by gdr2_forward_chunked."""
+    a = good_fwd(B=8, T=4096, H=16)
+    assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) > gdr2.NOALLOC_SCRATCH_BYTES
+    a.workspace_bytes = 1 << 40
+    assert lib.gdr2_forward_chunked_noalloc(ctypes.byref(a), None) == gdr2.ERR_WORKSPACE
+    assert b"static scratch" in lib.gdr2_last_error()
+    assert lib.gdr2_forward_chunked_noalloc(None, None) == gdr2.ERR_INVALID_ARG
+    b = good_fwd(T=10)
+    b.q = None
+    assert lib.gdr2_forward_chunked_noalloc(ctypes.byref(b), None) == gdr2.ERR_INVALID_ARG
+    c = good_fwd(T=10, D=96)
+    assert lib.gdr2_forward_chunked_noalloc(ctypes.byref(c), None) == gdr2.ERR_UNSUPPORTED
