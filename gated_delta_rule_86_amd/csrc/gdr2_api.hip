@@ -151,7 +151,8 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes, bool 
     gdr2_status s = check_common(rows, a->Dk, a->Dv, a->dtype, a->b_width, a->w_width, a->g_width);
     if (s != GDR2_OK)
         return s;
-    if (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED && a->algo != GDR2_ALGO_SEGMENTED)
+    if (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED && a->algo != GDR2_ALGO_SEGMENTED &&
+        a->algo != GDR2_ALGO_FUSED)
         return fail(GDR2_ERR_INVALID_ARG, "unknown algo %d", a->algo);
     if (a->stage != GDR2_STAGE_ALL && a->stage != GDR2_STAGE_PREP && a->stage != GDR2_STAGE_STATE)
         return fail(GDR2_ERR_INVALID_ARG, "unknown stage %d", a->stage);
@@ -162,6 +163,10 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes, bool 
     if (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096)
         return fail(GDR2_ERR_UNSUPPORTED, "fp32 needs Dk * chunk <= 4096 (got %lld * %d)",
                     (long long)a->Dk, a->chunk);
+    if (a->algo == GDR2_ALGO_FUSED && !gdr2::fused_supported(*a))
+        return fail(GDR2_ERR_UNSUPPORTED, "GDR2_ALGO_FUSED supports bf16 inputs only");
+    if (a->algo == GDR2_ALGO_FUSED && a->stage != GDR2_STAGE_ALL)
+        return fail(GDR2_ERR_UNSUPPORTED, "GDR2_ALGO_FUSED has no stages (stage must be GDR2_STAGE_ALL)");
     int64_t nchunks = (a->T + a->chunk - 1) / a->chunk, groups;
     if (!mul_ok(bh, nchunks, &groups) || groups > (int64_t)INT32_MAX)
         return fail(GDR2_ERR_UNSUPPORTED, "too many chunks for one launch");
@@ -338,7 +343,9 @@ size_t gdr2_forward_workspace_size(const gdr2_fwd_args* a)
         return 0;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128) || (a->chunk != 32 && a->chunk != 64) ||
         (a->dtype != GDR2_F32 && a->dtype != GDR2_BF16) ||
-        (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096))
+        (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096) ||
+        (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED && a->algo != GDR2_ALGO_SEGMENTED &&
+         a->algo != GDR2_ALGO_FUSED))
         return 0;
     return gdr2::staged_workspace_bytes(*a);
 }
@@ -358,6 +365,8 @@ gdr2_status gdr2_forward_chunked(const gdr2_fwd_args* a, void* stream_)
         return hip_check(gdr2::launch_state_copy(a->S0, a->S_out, state_bytes / 4, stream), stream,
                          "state copy");
     }
+    if (gdr2::forward_algo(*a) == GDR2_ALGO_FUSED)
+        return hip_check(gdr2::launch_forward_fused(*a, stream), stream, "chunked forward (fused)");
     return hip_check(gdr2::launch_forward_staged(*a, stream), stream, "chunked forward");
 }
 

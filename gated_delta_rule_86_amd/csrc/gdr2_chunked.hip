@@ -31,8 +31,7 @@
 // each fragment in registers and writes it with one coalesced 16-byte store
 // per lane; the state kernel copies a chunk's fragments into LDS linearly and
 // reads each one with a single conflict-free 16-byte LDS read per lane.
-#include "gdr2_device.h"
-#include "gdr2_internal.h"
+#include "gdr2_chunk_common.h"
 
 #include <algorithm>
 
@@ -40,73 +39,6 @@ namespace gdr2 {
 namespace {
 
 constexpr int NT = 256;            // threads of the state kernel (4 waves)
-constexpr float kSpanMax = 80.f;   // largest decay exponent (log2) a factor may carry
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// ---------------------------------------------------------------------------
-// 16x16x16 products in the accumulator-compatible k order: lane l holds
-// k = 4*(l/16) .. 4*(l/16)+3 of a 16-deep contraction, for A (row l%16) and
-// B (column l%16) alike -- an accumulator tile is directly a B operand.
-// bf16: v_mfma_f32_16x16x16_bf16; fp32: four v_mfma_f32_16x16x4f32.
-// ---------------------------------------------------------------------------
-template <typename E> struct Mma16;
-template <> struct Mma16<bf16> {
-    typedef bf16x4 Frag;
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    static __device__ __forceinline__ Frag pack(f32x4 x) {
-        Frag f;
-        f[0] = (bf16)x[0]; f[1] = (bf16)x[1]; f[2] = (bf16)x[2]; f[3] = (bf16)x[3];
-        return f;
-    }
-    static __device__ __forceinline__ Frag load(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                         __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-    }
-};
-template <> struct Mma16<float> {
-    typedef f32x4 Frag;
-    static __device__ __forceinline__ Frag pack(f32x4 x) { return x; }
-    static __device__ __forceinline__ Frag load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) { return Mma<float>::mma(a, b, c); }
-};
-
-// A full-width fragment (KT 16-blocks along k) from KT accumulator tiles.
-template <typename E> __device__ __forceinline__ typename Mma<E>::Frag frag_of(const f32x4* t);
-template <> __device__ __forceinline__ Mma<bf16>::Frag frag_of<bf16>(const f32x4* t) { return Mma<bf16>::pack(t[0], t[1]); }
-template <> __device__ __forceinline__ Mma<float>::Frag frag_of<float>(const f32x4* t) { return t[0]; }
-
-// ---------------------------------------------------------------------------
-// Fragment geometry of one chunk record.
-//   -W  [T][m]: rows t = 16T + l%16, k = key channels (m-th KB block)
-//   Q~  [T][m]: same
-//   K^T [c][m]: rows = key channels 16c + l%16, k = tokens (m-th KB block)
-//   P   [T][m] for m*KT <= T only (the rest of P is zero above the diagonal)
-//   U~  [n][T]: accumulator tiles, rows = tokens 16T.., columns 16n..
-// Within a KB block, lane group g = l/16 holds k = 4g..4g+3 (and, for bf16,
-// 16+4g..16+4g+3 in its upper four slots).
-// ---------------------------------------------------------------------------
-template <typename E, int D, int C>
-struct Frags {
-    static constexpr int KB = Mma<E>::KB, KT = KB / 16;
-    static constexpr int NB = C / 16;
-    static constexpr int NKS = D / KB;               // k-steps over key channels
-    static constexpr int NKC = C / KB;               // k-steps over tokens
-    static constexpr int FRAG = 1024;
-    static constexpr int TILE_U = 64 * 4 * (int)sizeof(E);
-    static constexpr int p_count(int T) { return T / KT + 1; }
-    static constexpr int p_offset(int T) { return T == 0 ? 0 : p_offset(T - 1) + p_count(T - 1); }
-    static constexpr int NP = p_offset(NB);
-    static constexpr size_t W_BYTES = (size_t)NB * NKS * FRAG;       // = C*D*sizeof(E)
-    static constexpr size_t K_BYTES = (size_t)(D / 16) * NKC * FRAG;  // = C*D*sizeof(E)
-    static constexpr size_t P_BYTES = (size_t)NP * FRAG;
-    static constexpr size_t U_BYTES = (size_t)NB * (D / 16) * TILE_U; // = C*D*sizeof(E)
-    static_assert(W_BYTES == (size_t)C * D * sizeof(E) && K_BYTES == W_BYTES && U_BYTES == W_BYTES, "sizes");
-};
 
 // Workspace: per record (sequence, head, chunk) in the order (b*H + h)*NC + n,
 // arrays -W, U~, K^T, Q~ (C*D elements each), P (NP fragments), gamma (D fp32).
@@ -145,12 +77,9 @@ Layout staged_layout(int64_t B, int64_t H, int64_t T, int D, int C, int esz, int
     return L;
 }
 
-struct PrepArgs {
-    const void *q, *k, *v, *b, *w;
-    const float* g;
-    int bw, ww, gw;
-    int pro;                  // prologue bits (normalise q, k; activate gates)
-    int64_t B, T, H, NC, nrec;
+
+struct PrepArgs : PrepIn {
+    int64_t nrec;
     void *Wn, *Ut, *Kh, *Qt, *P;
     float* gam;
 };
@@ -167,111 +96,6 @@ struct StateArgs {
     float* span;              // segment area (nseg > 1)
 };
 
-// ---------------------------------------------------------------------------
-// Small element helpers.
-// ---------------------------------------------------------------------------
-template <typename E>
-__device__ __forceinline__ void unpack(const u32x4& r, float* out);
-template <>
-__device__ __forceinline__ void unpack<bf16>(const u32x4& r, float* out)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        out[2 * i] = __uint_as_float(r[i] << 16);
-        out[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
-    }
-}
-template <>
-__device__ __forceinline__ void unpack<float>(const u32x4& r, float* out)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        out[i] = __uint_as_float(r[i]);
-}
-
-// A width-1 gate's value from its raw bits, zero-extended to 32 bits.
-template <typename E> __device__ __forceinline__ float gate_bits(unsigned int u);
-template <> __device__ __forceinline__ float gate_bits<bf16>(unsigned int u) { return __uint_as_float(u << 16); }
-template <> __device__ __forceinline__ float gate_bits<float>(unsigned int u) { return __uint_as_float(u); }
-
-template <typename E> __device__ __forceinline__ u32x4 pack_vec(const float* x);
-template <>
-__device__ __forceinline__ u32x4 pack_vec<bf16>(const float* x)
-{
-    bf16x8 v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        v[i] = (bf16)x[i];
-    return __builtin_bit_cast(u32x4, v);
-}
-template <>
-__device__ __forceinline__ u32x4 pack_vec<float>(const float* x)
-{
-    return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-}
-
-__device__ __forceinline__ u32x4 ldg16(const void* p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-__device__ __forceinline__ void sts16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-
-// Position of logical k index `col` inside its fragment row (see Frags).
-template <typename E> __device__ __forceinline__ int kpos(int col);
-template <> __device__ __forceinline__ int kpos<bf16>(int col)
-{
-    const int c = col & 31;
-    return (col & ~31) + 8 * ((c & 15) >> 2) + (c & 3) + 4 * (c >> 4);
-}
-template <> __device__ __forceinline__ int kpos<float>(int col) { return col; }
-
-// s_waitcnt lgkmcnt(0) with a compiler barrier: LDS writes of this wave are
-// complete before any later LDS read of it (lanes exchange data this way).
-// Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
-// (v_exp, v_log, v_rcp: about 1 ulp each; log(1 + e) loses e < 6e-8 absolute,
-// far below the decay's own rounding)
-__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
-__device__ __forceinline__ float neg_softplus(float x) { return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))); }
-constexpr float kNormEps = 1e-6f;
-
-__device__ __forceinline__ void lds_fence_wave()
-{
-    __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
-// Workgroup barrier that orders LDS data only: this wave's LDS operations
-// have completed, then s_barrier.  (__syncthreads() also waits for every
-// outstanding global access, including loads still being prefetched.)
-__device__ __forceinline__ void lds_barrier()
-{
-    __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// s_waitcnt vmcnt(0): every global->LDS copy this wave issued has landed.
-__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Inclusive-scan step: the value of the lane `d` below within the 16-lane row.
-template <int d>
-__device__ __forceinline__ float dpp_shr(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + d, 0xF, 0xF, true));
-}
-
-// Work item -> chunk.  The persistent prep kernel visits items in the order
-// (chunk taken last to first, sequence, head) with the head fastest (see
-// ItemWalk), so the workgroups in flight together read whole token rows: the
-// H heads of a token are one contiguous run of H*D elements of the
-// [B,T,H,.] inputs.  Token row r of the chunk is element offset
-// ((b*T + t0 + r)*H + h); the chunk's record in the workspace is
-// (b*H + h)*NC + n.
-struct ChunkPos {
-    int64_t rec;      // workspace record
-    int64_t row0;     // (b*T + t0)*H + h
-    int L;            // valid tokens (>= 1)
-};
-
-// Walks the items blockIdx.x, blockIdx.x + gridDim.x, ... with carries, so
 // the loop divides only once.  Item i is (m, b, h) with the head fastest and
 // m = NC - 1 - n slowest: the chunks are visited last to first, so the
 // records written last -- the ones the memory-side cache still holds when
@@ -339,314 +163,28 @@ struct ItemWalk {
 //  D  W^T = E~^T X^T gives the -W fragments in registers; U~ = X u gives the
 //     U~ accumulator tiles.  Both go straight to the workspace.
 // ---------------------------------------------------------------------------
-constexpr int NTP = 512;           // threads of the prep kernel
-constexpr int NWP = NTP / 64;      // its waves
-
 template <typename E, int D, int C>
-struct PrepShape {
-    typedef Frags<E, D, C> F;
-    static constexpr int ES = (int)sizeof(E);
-    static constexpr int VEC = 16 / ES;                      // elements per 16-byte access
-    static constexpr int NB = C / 16, NH = C / 32;
-    static constexpr int NCG = D / VEC;                      // 16-byte chunks per row
-    static constexpr int NWB0 = C * D / VEC / 64;
-    static constexpr int NWB = NWB0 < NWP ? NWB0 : NWP;      // waves of phases A and B
-    static constexpr int TW = C / NWB;                       // tokens per wave
-    static constexpr int LPC = 64 / NCG;                     // lanes sharing a channel group
-    static constexpr int TPL = TW / LPC;                     // tokens per lane
-    static constexpr int LDM = C + 4;                        // rows of M (elements)
-    static constexpr int LDXP = C + VEC;                     // rows of X (elements)
-    static constexpr int LDX = 20;                           // rows of fp32 16x16 blocks
-    static constexpr size_t ROWB = (size_t)D * ES;
-    static constexpr size_t OFF_EH = 0;                              // E^ [C][D]
-    static constexpr size_t OFF_QH = OFF_EH + C * ROWB;              // Q^ [C][D]
-    static constexpr size_t OFF_KR = OFF_QH + C * ROWB;              // Kr [C][D] (exact path: K^)
-    static constexpr size_t OFF_U = OFF_KR + C * ROWB;               // u  [C][D]
-    static constexpr size_t OFF_E2 = OFF_U + C * ROWB;               // E~ [C-32][D] second half
-    static constexpr size_t OFF_Q2 = OFF_E2 + (NH - 1) * 32 * ROWB;  // Q~ [C-32][D] second half
-    static constexpr size_t OFF_M = al256(OFF_Q2 + (NH - 1) * 32 * ROWB);       // M [C][LDM], blocks below the diagonal
-    static constexpr size_t OFF_MD = al256(OFF_M + (size_t)C * LDM * ES);       // M_II fp32 [NB][16][LDX]
-    static constexpr size_t OFF_XC = OFF_MD + (size_t)NB * 16 * LDX * 4;        // X_II fp32, column j as row j
-    static constexpr size_t OFF_X = al256(OFF_XC + (size_t)NB * 16 * LDX * 4);  // X [C][LDXP] in fragment k order
-    static constexpr size_t OFF_TOT = al256(OFF_X + (size_t)C * LDXP * ES);     // wave totals [NWB][D]
-    static constexpr size_t OFF_FK = OFF_TOT + (size_t)NWB * D * 4;             // 2^(G_L - Gh) [NH][D]
-    static constexpr size_t OFF_RN = OFF_FK + (size_t)NH * D * 4;               // prologue: 1/|k|, 1/|q| [2][C]
-    static constexpr size_t OFF_FLAG = OFF_RN + (size_t)2 * C * 4;
-    static constexpr size_t SMEM = OFF_FLAG + 16;                               // dynamic LDS
+struct PrepShape : PrepGeom<E, D, C> {
+    typedef PrepGeom<E, D, C> G;
+    static constexpr size_t OFF_EH = 0;                                   // E^ [C][D]
+    static constexpr size_t OFF_QH = OFF_EH + G::SZ_ROWS;                 // Q^ [C][D]
+    static constexpr size_t OFF_KR = OFF_QH + G::SZ_ROWS;                 // Kr [C][D] (exact path: K^)
+    static constexpr size_t OFF_U = OFF_KR + G::SZ_ROWS;                  // u  [C][D]
+    static constexpr size_t OFF_E2 = OFF_U + G::SZ_ROWS;                  // E~ [C-32][D] second half
+    static constexpr size_t OFF_Q2 = OFF_E2 + G::SZ_HALF;                 // Q~ [C-32][D] second half
+    static constexpr size_t OFF_M = al256(OFF_Q2 + G::SZ_HALF);           // M [C][LDM], blocks below the diagonal
+    static constexpr size_t OFF_MD = al256(OFF_M + G::SZ_M);              // M_II fp32 [NB][16][LDX]
+    static constexpr size_t OFF_XC = OFF_MD + G::SZ_MD;                   // X_II fp32, column j as row j
+    static constexpr size_t OFF_X = al256(OFF_XC + G::SZ_MD);             // X [C][LDXP] in fragment k order
+    static constexpr size_t OFF_TOT = al256(OFF_X + G::SZ_X);             // wave totals [NWB][D]
+    static constexpr size_t OFF_FK = OFF_TOT + G::SZ_TOT;                 // 2^(G_L - Gh) [NH][D]
+    static constexpr size_t OFF_RN = OFF_FK + G::SZ_FK;                   // prologue: 1/|k|, 1/|q| [2][C]
+    static constexpr size_t OFF_FLAG = OFF_RN + G::SZ_RN;
+    static constexpr size_t SMEM = OFF_FLAG + 16;                         // dynamic LDS
     // raw g [C][D] (exact path: G) lives in its own static LDS object, so the
     // compiler knows the asynchronous copies into it touch nothing else
-    static constexpr size_t SZ_G = (size_t)C * D * 4;
-    static_assert(SMEM + SZ_G + 2 * C * 4 <= 160 * 1024, "LDS budget");   // + width-1 b, w
-    static_assert(C == 32 || C == 64, "chunk");
-    static_assert(64 % NCG == 0 && NCG >= 8 && TPL >= 1 && TW == LPC * TPL, "lane mapping");
-    static_assert(NWB == NWP || NH == 1, "halves need every wave in phase B");
+    static_assert(SMEM + G::SZ_G + 2 * C * 4 <= 160 * 1024, "LDS budget");   // + width-1 b, w
 };
-
-// Row swizzle of the [rows][D] operand arrays: 16-byte chunk j of row r
-// sits at chunk j ^ (r & SWZ_MASK), with the mask as wide as the row allows
-// up to 15, so the 16 rows that one 16-lane group of a fragment read touches
-// land on distinct banks.
-template <typename E, int D>
-constexpr int swz_mask()
-{
-    constexpr int NCG = D * (int)sizeof(E) / 16;   // 16-byte chunks per row
-    return (NCG < 16 ? NCG : 16) - 1;
-}
-
-// Element offset of element `col` of row `r` in a swizzled [rows][D] array.
-template <typename E, int D>
-__device__ __forceinline__ int swz(int r, int col)
-{
-    constexpr int VEC = 16 / (int)sizeof(E);
-    return r * D + (((col / VEC) ^ (r & swz_mask<E, D>())) * VEC) + (col % VEC);
-}
-
-// Raw inputs of one lane's TPL tokens (bit patterns; width-1 gates are not
-// held here but copied to LDS by prep_copy_bw).
-template <typename E, int D, int C>
-struct PrepRegs {
-    typedef PrepShape<E, D, C> S;
-    u32x4 k[S::TPL], q[S::TPL], v[S::TPL], b[S::TPL], w[S::TPL];
-};
-
-// Issue the token loads of one chunk for tokens t0.. of this lane, channels
-// c0...  Rows past the valid length re-read the last valid row (in bounds)
-// and are zeroed where they are used, so no load sits under a per-lane branch.
-// PART: 0 = k, 1 = q, 2 = v, 3 = b, 4 = w (issued at different points of
-// the previous chunk, so no wave stalls on a full memory queue).
-template <int PART, int WB, int WW, typename E, int D, int C>
-__device__ __forceinline__ void prep_load(const PrepArgs& a, const ChunkPos& cp, PrepRegs<E, D, C>& R,
-                                          int t0, int c0)
-{
-    typedef PrepShape<E, D, C> S;
-#pragma unroll
-    for (int j = 0; j < S::TPL; ++j) {
-        const int t = min(t0 + j, cp.L - 1);
-        const int64_t row = cp.row0 + (int64_t)t * a.H, off = row * D + c0;
-        if (PART == 0)
-            R.k[j] = ldg16((const E*)a.k + off);
-        if (PART == 1)
-            R.q[j] = ldg16((const E*)a.q + off);
-        if (PART == 2)
-            R.v[j] = ldg16((const E*)a.v + off);
-        if (PART == 3 && (WB == 0 ? a.bw != 1 : WB != 1))
-            R.b[j] = ldg16((const E*)a.b + off);
-        if (PART == 4 && (WW == 0 ? a.ww != 1 : WW != 1))
-            R.w[j] = ldg16((const E*)a.w + off);
-    }
-}
-
-// Copy one chunk's log-decay rows straight into LDS (global_load_lds, no
-// registers): [C][D] fp32, or C floats for a width-1 gate.  Rows past the
-// valid length repeat the last valid row and are zeroed by the reader.
-template <int WG, typename E, int D, int C>
-__device__ __forceinline__ void prep_copy_g(const PrepArgs& a, const ChunkPos& cp, unsigned char* sGraw,
-                                            int wave, int lane)
-{
-    typedef __attribute__((address_space(3))) void lds_t;
-    if (WG == 0 ? a.gw != 1 : WG != 1) {
-        constexpr int NI = C * D * 4 / 1024;
-        for (int j = wave; j < NI; j += NWP) {
-            const int byte = j * 1024 + lane * 16, t = min(byte / (D * 4), cp.L - 1), col = (byte % (D * 4)) / 4;
-            __builtin_amdgcn_global_load_lds(a.g + (cp.row0 + (int64_t)t * a.H) * D + col,
-                                             (lds_t*)(sGraw + j * 1024), 16, 0, 0);
-        }
-    } else if (wave == 0 && lane < C) {
-        __builtin_amdgcn_global_load_lds(a.g + cp.row0 + (int64_t)min(lane, cp.L - 1) * a.H, (lds_t*)sGraw, 4, 0, 0);
-    }
-}
-
-// One element per lane from global memory into the 32-bit LDS word `lane` of
-// dst (zero-extended), without a register.
-template <typename E> __device__ __forceinline__ void copy_elem_lds(const E* src, unsigned int* dst);
-template <>
-__device__ __forceinline__ void copy_elem_lds<bf16>(const bf16* src, unsigned int* dst)
-{
-    typedef __attribute__((address_space(3))) void lds_t;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)dst, 2, 0, 0);
-}
-template <>
-__device__ __forceinline__ void copy_elem_lds<float>(const float* src, unsigned int* dst)
-{
-    typedef __attribute__((address_space(3))) void lds_t;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_t*)dst, 4, 0, 0);
-}
-
-// Copy one chunk's width-1 erase and write gates straight into LDS
-// (global_load_lds, one element per lane): token t's bits land
-// zero-extended in 32-bit word t of sBW (b) and of sBW + C (w), so no lane
-// spends a register load on a scalar that 16 lanes share.  Rows past the
-// valid length repeat the last valid row.
-template <int WB, int WW, typename E, int D, int C>
-__device__ __forceinline__ void prep_copy_bw(const PrepArgs& a, const ChunkPos& cp, unsigned int* sBW,
-                                             int wave, int lane)
-{
-    const bool nb = WB == 0 ? a.bw == 1 : WB == 1, nw = WW == 0 ? a.ww == 1 : WW == 1;
-    if (lane < C) {
-        const int64_t row = cp.row0 + (int64_t)min(lane, cp.L - 1) * a.H;
-        if (nb && wave == 1)
-            copy_elem_lds<E>((const E*)a.b + row, sBW);
-        if (nw && wave == 2)
-            copy_elem_lds<E>((const E*)a.w + row, sBW + C);
-    }
-}
-
-// Phase B for one lane: decay-referenced operands of its tokens into LDS.
-// VALID: every token of the chunk is valid (no zeroing needed).
-template <bool VALID, bool SECOND, bool PRO, typename E, int D, int C>
-__device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const float (*G)[16 / sizeof(E)],
-                                               const float* gh, int bw, int ww, int L, int t0, int c0,
-                                               unsigned char* smem, const unsigned int* sBW, int pro)
-{
-    typedef PrepShape<E, D, C> S;
-    constexpr int VEC = S::VEC;
-    E* sEh = reinterpret_cast<E*>(smem + S::OFF_EH);
-    E* sQh = reinterpret_cast<E*>(smem + S::OFF_QH);
-    E* sKr = reinterpret_cast<E*>(smem + S::OFF_KR);
-    E* sU = reinterpret_cast<E*>(smem + S::OFF_U);
-    E* sE2 = reinterpret_cast<E*>(smem + S::OFF_E2);
-    E* sQ2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
-    float fh[VEC];
-    if (SECOND) {
-#pragma unroll
-        for (int x = 0; x < VEC; ++x)
-            fh[x] = fast_exp2(gh[x]);
-    }
-    float mx = 0.f;
-#pragma unroll
-    for (int j = 0; j < S::TPL; ++j) {
-        // one output array at a time keeps few values live
-        const int t = t0 + j;
-        const bool valid = VALID || t < L;
-        const int o = swz<E, D>(t, c0);
-        const int o2 = SECOND ? swz<E, D>(t - 32, c0) : 0;
-        float eh[VEC], d[VEC], kk[VEC], tmp[VEC], tmp2[VEC];
-#pragma unroll
-        for (int x = 0; x < VEC; ++x) {
-            const float g = G[j][x];
-            d[x] = SECOND ? g - gh[x] : g;
-            mx = fmaxf(mx, fmaxf(fabsf(d[x]), g));
-        }
-        unpack<E>(R.k[j], kk);
-        if constexpr (PRO) {
-            // prologue: unit L2 norm per token over the row, whose channel
-            // groups sit in the lanes lane % LPC + LPC * m
-            if (pro & GDR2_PROLOGUE_NORM_QK) {
-                float ss = 0.f;
-#pragma unroll
-                for (int x = 0; x < VEC; ++x)
-                    ss += kk[x] * kk[x];
-#pragma unroll
-                for (int m = S::LPC; m < 64; m <<= 1)
-                    ss += __shfl_xor(ss, m);
-                const float rk = rsqrtf(ss + kNormEps);
-#pragma unroll
-                for (int x = 0; x < VEC; ++x)
-                    kk[x] *= rk;
-                if (c0 == 0)
-                    reinterpret_cast<float*>(smem + S::OFF_RN)[t] = rk;
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < VEC; ++x) {
-            kk[x] = valid ? kk[x] : 0.f;
-            tmp[x] = kk[x] * fast_exp2(-d[x]);
-            eh[x] = fast_exp2(d[x]);
-        }
-        sts16(sKr + o, pack_vec<E>(tmp));
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            float bb[VEC];
-            unpack<E>(R.b[j], bb);
-            float bs = bw == 1 ? gate_bits<E>(sBW[t]) : 0.f;
-            if constexpr (PRO) {
-                if (pro & GDR2_PROLOGUE_GATES) {
-                    bs = sigm(bs);
-#pragma unroll
-                    for (int x = 0; x < VEC; ++x)
-                        bb[x] = sigm(bb[x]);
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < VEC; ++x) {
-                tmp[x] = (bw == 1 ? bs : bb[x]) * kk[x] * eh[x];
-                if (SECOND)
-                    tmp2[x] = tmp[x] * fh[x];
-            }
-        }
-        sts16(sEh + o, pack_vec<E>(tmp));
-        if (SECOND)
-            sts16(sE2 + o2, pack_vec<E>(tmp2));
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            float qq[VEC];
-            unpack<E>(R.q[j], qq);
-            if constexpr (PRO) {
-                if (pro & GDR2_PROLOGUE_NORM_QK) {
-                    float ss = 0.f;
-#pragma unroll
-                    for (int x = 0; x < VEC; ++x)
-                        ss += qq[x] * qq[x];
-#pragma unroll
-                    for (int m = S::LPC; m < 64; m <<= 1)
-                        ss += __shfl_xor(ss, m);
-                    const float rq = rsqrtf(ss + kNormEps);
-#pragma unroll
-                    for (int x = 0; x < VEC; ++x)
-                        qq[x] *= rq;
-                    if (c0 == 0)
-                        reinterpret_cast<float*>(smem + S::OFF_RN)[C + t] = rq;
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < VEC; ++x) {
-                tmp[x] = (valid ? qq[x] : 0.f) * eh[x];
-                if (SECOND)
-                    tmp2[x] = tmp[x] * fh[x];
-            }
-        }
-        sts16(sQh + o, pack_vec<E>(tmp));
-        if (SECOND)
-            sts16(sQ2 + o2, pack_vec<E>(tmp2));
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            float vv[VEC], wv[VEC];
-            unpack<E>(R.v[j], vv);
-            unpack<E>(R.w[j], wv);
-            float ws = ww == 1 ? gate_bits<E>(sBW[C + t]) : 0.f;
-            if constexpr (PRO) {
-                if (pro & GDR2_PROLOGUE_GATES) {
-                    ws = sigm(ws);
-#pragma unroll
-                    for (int x = 0; x < VEC; ++x)
-                        wv[x] = sigm(wv[x]);
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < VEC; ++x)
-                tmp[x] = (valid ? (ww == 1 ? ws : wv[x]) : 0.f) * vv[x];
-        }
-        sts16(sU + o, pack_vec<E>(tmp));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    return mx;
-}
-
-// 16 bytes of a swizzled row array as a full-width fragment: logical chunk
-// ch (k-values VEC*ch ..) of row r.
-template <typename E, int D>
-__device__ __forceinline__ typename Mma<E>::Frag row_frag(const E* base, int r, int ch)
-{
-    constexpr int VEC = 16 / (int)sizeof(E);
-    return *reinterpret_cast<const typename Mma<E>::Frag*>(base + r * D + ((ch ^ (r & swz_mask<E, D>())) * VEC));
-}
-
-// Four consecutive elements (col a multiple of 4) of a swizzled row array.
-template <typename E, int D>
-__device__ __forceinline__ typename Mma16<E>::Frag row4(const E* base, int r, int col)
-{
-    return Mma16<E>::load(base + swz<E, D>(r, col));
-}
 
 // Gate widths WB, WW, WG: 1 or D fixed at compile time, 0 = read from the
 // arguments (one variant serves every mix).
@@ -657,34 +195,38 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
     typedef Frags<E, D, C> F;
     typedef Mma<E> MM;
     typedef Mma16<E> M16;
-    constexpr int NB = S::NB, NH = S::NH, VEC = S::VEC, LDM = S::LDM, LDXP = S::LDXP, LDX = S::LDX;
-    constexpr int KB = F::KB, KT = F::KT, NKS = F::NKS, NKC = F::NKC, NP = F::NP;
+    constexpr int NB = S::NB, NH = S::NH, VEC = S::VEC, LDXP = S::LDXP;
+    constexpr int KB = F::KB, NKS = F::NKS, NKC = F::NKC, NP = F::NP;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    E* sEh = reinterpret_cast<E*>(smem + S::OFF_EH);
-    E* sQh = reinterpret_cast<E*>(smem + S::OFF_QH);
-    E* sKr = reinterpret_cast<E*>(smem + S::OFF_KR);
-    E* sU = reinterpret_cast<E*>(smem + S::OFF_U);
-    E* sE2 = reinterpret_cast<E*>(smem + S::OFF_E2);
-    E* sQ2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
-    E* sM = reinterpret_cast<E*>(smem + S::OFF_M);
-    float* sMd = reinterpret_cast<float*>(smem + S::OFF_MD);
-    float* sXc = reinterpret_cast<float*>(smem + S::OFF_XC);
-    E* sX = reinterpret_cast<E*>(smem + S::OFF_X);
-    float* sTot = reinterpret_cast<float*>(smem + S::OFF_TOT);
-    float* sFk = reinterpret_cast<float*>(smem + S::OFF_FK);
-    int* sFlag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
     __shared__ __align__(16) float sG[C * D];
     __shared__ __align__(16) unsigned int sBW[2 * C];   // width-1 b and w of the chunk
+    PrepLds<E> s;
+    s.Eh = reinterpret_cast<E*>(smem + S::OFF_EH);
+    s.Qh = reinterpret_cast<E*>(smem + S::OFF_QH);
+    s.Kr = reinterpret_cast<E*>(smem + S::OFF_KR);
+    s.U = reinterpret_cast<E*>(smem + S::OFF_U);
+    s.E2 = reinterpret_cast<E*>(smem + S::OFF_E2);
+    s.Q2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
+    s.M = reinterpret_cast<E*>(smem + S::OFF_M);
+    s.X = reinterpret_cast<E*>(smem + S::OFF_X);
+    s.Md = reinterpret_cast<float*>(smem + S::OFF_MD);
+    s.Xc = reinterpret_cast<float*>(smem + S::OFF_XC);
+    s.Tot = reinterpret_cast<float*>(smem + S::OFF_TOT);
+    s.Fk = reinterpret_cast<float*>(smem + S::OFF_FK);
+    s.Rn = reinterpret_cast<float*>(smem + S::OFF_RN);
+    s.Flag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
+    s.G = sG;
+    s.BW = sBW;
 
     const int wave = threadIdx.x >> 6;
     const bool ab = wave < S::NWB;              // waves of phases A and B
     const bool second = NH == 2 && wave >= S::NWB / 2;
-    const int bw = WB ? WB : a.bw, ww = WW ? WW : a.ww, gw = WG ? WG : a.gw;
+    const int bw = WB ? WB : a.bw, ww = WW ? WW : a.ww;
 
     // X: the blocks above the diagonal that fragments cover stay zero
     for (int e = threadIdx.x; e < C * LDXP; e += NTP)
-        sX[e] = from_f32<E>(0.f);
+        s.X[e] = from_f32<E>(0.f);
 
     // Token inputs: two register sets, Rn receives chunk n+1 while chunk n
     // computes from R, so every token load is issued a whole chunk ahead of
@@ -732,151 +274,24 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
             prep_load<0, WB, WW>(a, np, Rn, t0, c0);
             prep_load<1, WB, WW>(a, np, Rn, t0, c0);
         }
-        // identity B operand of the transposes: element (k = 4gq + i, n = cl)
-        typename M16::Frag ident;
-        {
-            f32x4 id;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                id[i] = (4 * gq + i == cl) ? 1.f : 0.f;
-            ident = M16::pack(id);
-        }
+        const typename M16::Frag ident = identity16<E>(gq, cl);
         const int64_t rec = cp.rec;
-        const bool full_chunk = cp.L == C;
 
         // ---- A: cumulative log2-decay in registers -------------------------
         float G[S::TPL][VEC];
         float excl[VEC];
-        if (ab) {
-#pragma unroll
-            for (int j = 0; j < S::TPL; ++j) {
-                const bool valid = full_chunk || t0 + j < cp.L;
-                const bool act = PRO && (a.pro & GDR2_PROLOGUE_GATES);
-                if (gw == 1) {
-                    float gv = sG[t0 + j];
-                    if (act)
-                        gv = neg_softplus(gv);
-#pragma unroll
-                    for (int x = 0; x < VEC; ++x)
-                        G[j][x] = valid ? gv * kLog2e : 0.f;
-                } else {
-#pragma unroll
-                    for (int x4 = 0; x4 < VEC / 4; ++x4) {
-                        f32x4 gv = *reinterpret_cast<const f32x4*>(sG + (t0 + j) * D + c0 + 4 * x4);
-                        if (act) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                gv[i] = neg_softplus(gv[i]);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            G[j][4 * x4 + i] = valid ? gv[i] * kLog2e : 0.f;
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 1; j < S::TPL; ++j)
-#pragma unroll
-                for (int x = 0; x < VEC; ++x)
-                    G[j][x] += G[j - 1][x];
-            float inc[VEC];
-#pragma unroll
-            for (int x = 0; x < VEC; ++x)
-                inc[x] = G[S::TPL - 1][x];
-            if (S::LPC > 1) {
-#pragma unroll
-                for (int x = 0; x < VEC; ++x) {
-                    const float y = dpp_shr<1>(inc[x]);
-                    inc[x] += lpc >= 1 ? y : 0.f;
-                }
-            }
-            if (S::LPC > 2) {
-#pragma unroll
-                for (int x = 0; x < VEC; ++x) {
-                    const float y = dpp_shr<2>(inc[x]);
-                    inc[x] += lpc >= 2 ? y : 0.f;
-                }
-            }
-            if (S::LPC > 4) {
-#pragma unroll
-                for (int x = 0; x < VEC; ++x) {
-                    const float y = dpp_shr<4>(inc[x]);
-                    inc[x] += lpc >= 4 ? y : 0.f;
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < VEC; ++x)
-                excl[x] = inc[x] - G[S::TPL - 1][x];
-            if (lpc == S::LPC - 1) {
-#pragma unroll
-                for (int x4 = 0; x4 < VEC / 4; ++x4)
-                    *reinterpret_cast<f32x4*>(sTot + wave * D + c0 + 4 * x4) =
-                        f32x4{inc[4 * x4], inc[4 * x4 + 1], inc[4 * x4 + 2], inc[4 * x4 + 3]};
-            }
-        }
+        if (ab)
+            prep_cumsum<WG, PRO, E, D, C>(a, s, cp.L, t0, c0, lpc, wave, G, excl);
         if (tid == 0)
-            *sFlag = 0;
+            *s.Flag = 0;
         lds_barrier();   // B1: wave totals; the previous chunk is done with LDS
         if (pre)
             prep_load<2, WB, WW>(a, np, Rn, t0, c0);
 
         // ---- B: decay-referenced operands ----------------------------------
-        float gh[VEC];
         if (ab) {
-            float off[VEC];
-#pragma unroll
-            for (int x = 0; x < VEC; ++x)
-                off[x] = gh[x] = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < S::NWB - 1; ++w2) {
-                if (w2 < wave) {
-#pragma unroll
-                    for (int x4 = 0; x4 < VEC / 4; ++x4) {
-                        const f32x4 tv = *reinterpret_cast<const f32x4*>(sTot + w2 * D + c0 + 4 * x4);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            off[4 * x4 + i] += tv[i];
-                    }
-                }
-                if (NH == 2 && w2 == S::NWB / 2 - 1) {
-#pragma unroll
-                    for (int x = 0; x < VEC; ++x)
-                        gh[x] = off[x];
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < S::TPL; ++j)
-#pragma unroll
-                for (int x = 0; x < VEC; ++x)
-                    G[j][x] += off[x] + excl[x];
-            if (wave == S::NWB - 1 && lpc == S::LPC - 1) {
-                // the chunk's last token: gamma and the K^ factors per half
-                float f0[VEC], f1[VEC];
-#pragma unroll
-                for (int x = 0; x < VEC; ++x) {
-                    const float gl = G[S::TPL - 1][x];
-                    f0[x] = fast_exp2(gl);
-                    f1[x] = fast_exp2(gl - gh[x]);
-                }
-#pragma unroll
-                for (int x4 = 0; x4 < VEC / 4; ++x4) {
-                    const f32x4 v0 = f32x4{f0[4 * x4], f0[4 * x4 + 1], f0[4 * x4 + 2], f0[4 * x4 + 3]};
-                    *reinterpret_cast<f32x4*>(sFk + c0 + 4 * x4) = v0;
-                    *reinterpret_cast<f32x4*>(a.gam + rec * D + c0 + 4 * x4) = v0;
-                    if (NH == 2)
-                        *reinterpret_cast<f32x4*>(sFk + D + c0 + 4 * x4) =
-                            f32x4{f1[4 * x4], f1[4 * x4 + 1], f1[4 * x4 + 2], f1[4 * x4 + 3]};
-                }
-            }
-            float mx;
-            if (second)
-                mx = full_chunk ? prep_operands<true, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro)
-                                : prep_operands<false, true, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro);
-            else
-                mx = full_chunk ? prep_operands<true, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro)
-                                : prep_operands<false, false, PRO, E, D, C>(R, G, gh, bw, ww, cp.L, t0, c0, smem, sBW, a.pro);
-            if (mx > kSpanMax)
-                *sFlag = 1;
+            prep_offsets_operands<PRO, D, E, D, C>(a, R, s, cp.L, t0, c0, lpc, wave, second, G, excl,
+                                                   a.gam + rec * D, 0, bw, ww);
             if (pre)
                 prep_load<3, WB, WW>(a, np, Rn, t0, c0);
         }
@@ -884,142 +299,18 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         if (next < a.nrec)   // phase B has read this chunk's width-1 gates
             prep_copy_bw<WB, WW, E, D, C>(a, np, sBW, wave, lane);
 
-        E* gP = (E*)a.P + rec * (F::P_BYTES / sizeof(E));
+        unsigned char* gP = (unsigned char*)a.P + rec * F::P_BYTES;
         if (pre)
             prep_load<4, WB, WW>(a, np, Rn, t0, c0);
-        const bool guard = *sFlag != 0;
+        const bool guard = *s.Flag != 0;
         if (!guard) {
             if (next < a.nrec)
                 prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
             // ---- C1: M tiles (waves 0-3) and P fragments (waves 4-7) -------
-            if (wave < NWP / 2) {
-                constexpr int NTM = NB * (NB + 1) / 2;
-                for (int tile = wave; tile < NTM; tile += NWP / 2) {
-                    int I = 0;
-                    while ((I + 1) * (I + 2) / 2 <= tile)
-                        ++I;
-                    const int J = tile - I * (I + 1) / 2;
-                    const bool same = NH == 1 || (I >> 1) == (J >> 1);
-                    const E* Bs = same ? sEh : sE2;
-                    const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks)
-                        acc = MM::mma(row_frag<E, D>(sKr, 16 * J + cl, 4 * ks + gq),
-                                      row_frag<E, D>(Bs, rb, 4 * ks + gq), acc);
-                    // lane: M[16I + cl][16J + 4gq + i]
-                    if (J < I) {
-                        *reinterpret_cast<typename M16::Frag*>(sM + (16 * I + cl) * LDM + 16 * J + 4 * gq) =
-                            M16::pack(acc);
-                    } else {
-                        f32x4 m;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            m[i] = 4 * gq + i < cl ? acc[i] : 0.f;
-                        *reinterpret_cast<f32x4*>(sMd + (16 * I + cl) * LDX + 4 * gq) = m;
-                    }
-                }
-            } else {
-                for (int f = wave - NWP / 2; f < NP; f += NWP / 2) {
-                    int I = 0;
-                    while (I + 1 < NB && F::p_offset(I + 1) <= f)
-                        ++I;
-                    const int m = f - F::p_offset(I);
-                    f32x4 acc[KT];
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) {
-                        const int J = KT * m + kt;
-                        acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (J > I)
-                            continue;
-                        const bool same = NH == 1 || (I >> 1) == (J >> 1);
-                        const E* Bs = same ? sQh : sQ2;
-                        const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
-#pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks)
-                            acc[kt] = MM::mma(row_frag<E, D>(sKr, 16 * J + cl, 4 * ks + gq),
-                                              row_frag<E, D>(Bs, rb, 4 * ks + gq), acc[kt]);
-                        if (J == I) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                acc[kt][i] = 4 * gq + i <= cl ? acc[kt][i] : 0.f;
-                        }
-                    }
-                    stg16(reinterpret_cast<unsigned char*>(gP) + f * F::FRAG + lane * 16,
-                          __builtin_bit_cast(u32x4, frag_of<E>(acc)));
-                }
-            }
+            prep_gram<E, D, C>(s, gP, wave, lane);
         } else {
             // ---- exact path for a chunk with steep decay -------------------
-            // G over the raw rows in sG (phase A has read them all)
-            if (ab) {
-#pragma unroll
-                for (int j = 0; j < S::TPL; ++j)
-#pragma unroll
-                    for (int x4 = 0; x4 < VEC / 4; ++x4)
-                        *reinterpret_cast<f32x4*>(sG + (t0 + j) * D + c0 + 4 * x4) =
-                            f32x4{G[j][4 * x4], G[j][4 * x4 + 1], G[j][4 * x4 + 2], G[j][4 * x4 + 3]};
-            }
-            __syncthreads();
-            const E* q = (const E*)a.q;
-            const E* k = (const E*)a.k;
-            const E* b = (const E*)a.b;
-            // prologue: per-token 1/|k|, 1/|q| from phase B, sigmoid on b
-            const float* sRn = reinterpret_cast<const float*>(smem + S::OFF_RN);
-            const bool pn = PRO && (a.pro & GDR2_PROLOGUE_NORM_QK), pg = PRO && (a.pro & GDR2_PROLOGUE_GATES);
-            // M, every pair s < t
-            for (int e = tid; e < C * C; e += NTP) {
-                const int t = e / C, s = e % C;
-                if (s >= t)
-                    continue;
-                float m = 0.f;
-                if (t < cp.L) {
-                    const int64_t xr = cp.row0 + (int64_t)t * a.H, xs = cp.row0 + (int64_t)s * a.H;
-                    for (int i = 0; i < D; ++i) {
-                        float br = to_f32(bw == 1 ? b[xr] : b[xr * D + i]);
-                        if (pg)
-                            br = sigm(br);
-                        m += br * to_f32(k[xr * D + i]) * to_f32(k[xs * D + i]) *
-                             fast_exp2(sG[t * D + i] - sG[s * D + i]);
-                    }
-                    if (pn)
-                        m *= sRn[t] * sRn[s];
-                }
-                if ((t >> 4) == (s >> 4))
-                    sMd[t * LDX + (s & 15)] = m;
-                else
-                    sM[t * LDM + s] = from_f32<E>(m);
-            }
-            // P, straight into its fragments (zeros above the diagonal)
-            for (int e = tid; e < NP * 16 * KB; e += NTP) {
-                const int f = e / (16 * KB), r = (e / KB) % 16, kk = e % KB;
-                int I = 0;
-                while (I + 1 < NB && F::p_offset(I + 1) <= f)
-                    ++I;
-                const int m = f - F::p_offset(I);
-                const int t = 16 * I + r, s = KB * m + kk;
-                float p = 0.f;
-                if (s <= t && t < cp.L) {
-                    const int64_t xr = cp.row0 + (int64_t)t * a.H, xs = cp.row0 + (int64_t)s * a.H;
-                    for (int i = 0; i < D; ++i)
-                        p += to_f32(q[xr * D + i]) * to_f32(k[xs * D + i]) * fast_exp2(sG[t * D + i] - sG[s * D + i]);
-                    if (pn)
-                        p *= sRn[C + t] * sRn[s];
-                }
-                // lane (g, r) holds k = 4g..4g+3 of each 16-block of the fragment
-                const int k16 = kk & 15, slot = 4 * (kk >> 4) + (k16 & 3);
-                gP[f * (F::FRAG / sizeof(E)) + ((k16 >> 2) * 16 + r) * (16 / sizeof(E)) + slot] = from_f32<E>(p);
-            }
-            // K^ = k 2^(G_L - G) into the Kr rows (used below unscaled)
-            for (int e = tid; e < C * D; e += NTP) {
-                const int t = e / D, i = e % D;
-                float kh = 0.f;
-                if (t < cp.L)
-                    kh = to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) * fast_exp2(sG[(C - 1) * D + i] - sG[t * D + i]) *
-                         (pn ? sRn[t] : 1.f);
-                sKr[swz<E, D>(t, i)] = from_f32<E>(kh);
-            }
-            __syncthreads();   // every read of G is done
+            prep_exact<PRO, E, D, C>(a, cp, s, gP, ab, t0, c0, bw, G);
             if (next < a.nrec)
                 prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
         }
@@ -1027,85 +318,21 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 
         // ---- C2: X = (I + M)^-1 (wave 0); K^T and Q~ fragments (others) --
         if (wave == 0) {
-            if (gq < NB) {
-                // column cl of X_gq,gq by forward substitution
-                const float* m = sMd + gq * 16 * LDX;
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc0 = r == cl ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-                    for (int c = 0; c + 1 < r; c += 2) {
-                        acc0 -= m[r * LDX + c] * x[c];
-                        acc1 -= m[r * LDX + c + 1] * x[c + 1];
-                    }
-                    if (r & 1)
-                        acc0 -= m[r * LDX + r - 1] * x[r - 1];
-                    x[r] = acc0 + acc1;
-                }
-                float* xc = sXc + (gq * 16 + cl) * LDX;
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    *reinterpret_cast<f32x4*>(xc + 4 * r4) = f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
-            }
-            lds_fence_wave();
-            f32x4 Xt[NB][NB];
-            typename M16::Frag nx[NB];
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                // accumulator tile X_II[4gq + i][cl]
-                Xt[I][I] = *reinterpret_cast<const f32x4*>(sXc + (16 * I + cl) * LDX + 4 * gq);
-                // A operand -X_II[cl][4gq + i]
-                f32x4 t;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    t[i] = -sXc[(16 * I + 4 * gq + i) * LDX + cl];
-                nx[I] = M16::pack(t);
-            }
-#pragma unroll
-            for (int d = 1; d < NB; ++d) {
-#pragma unroll
-                for (int I = d; I < NB; ++I) {
-                    const int J = I - d;
-                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int K = J; K < I; ++K)
-                        y = M16::mma(M16::load(sM + (16 * I + cl) * LDM + 16 * K + 4 * gq), M16::pack(Xt[K][J]), y);
-                    Xt[I][J] = M16::mma(nx[I], M16::pack(y), f32x4{0.f, 0.f, 0.f, 0.f});
-                }
-            }
-            // X into LDS rows in fragment k order
-#pragma unroll
-            for (int I = 0; I < NB; ++I)
-#pragma unroll
-                for (int J = 0; J <= I; ++J)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sX[(16 * I + 4 * gq + i) * LDXP + kpos<E>(16 * J + cl)] = from_f32<E>(Xt[I][J][i]);
+            prep_inverse<E, D, C>(s, lane);
         } else {
             constexpr int NK = (D / 16) * NKC, NQ = NB * NKS;
-            E* gKh = (E*)a.Kh + rec * (F::K_BYTES / sizeof(E));
-            E* gQt = (E*)a.Qt + rec * (F::W_BYTES / sizeof(E));
+            unsigned char* gKh = (unsigned char*)a.Kh + rec * F::K_BYTES;
+            unsigned char* gQt = (unsigned char*)a.Qt + rec * F::W_BYTES;
             for (int task = wave - 1; task < NK + NQ; task += NWP - 1) {
                 if (task < NK) {
                     // K^T fragment (channel block c, token step m)
-                    const int c = task / NKC, m = task % NKC;
-                    f32x4 acc[KT];
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) {
-                        const int tb = KT * m + kt;
-                        acc[kt] = M16::mma(row4<E, D>(sKr, 16 * tb + cl, 16 * c + 4 * gq), ident,
-                                           f32x4{0.f, 0.f, 0.f, 0.f});
-                        const float f = guard ? 1.f : sFk[(NH == 2 ? (tb >> 1) : 0) * D + 16 * c + cl];
-                        acc[kt] = acc[kt] * f;
-                    }
-                    stg16(reinterpret_cast<unsigned char*>(gKh) + task * F::FRAG + lane * 16,
-                          __builtin_bit_cast(u32x4, frag_of<E>(acc)));
+                    stg16(gKh + task * F::FRAG + lane * 16,
+                          prep_kt_frag<E, D, C>(s, task / NKC, task % NKC, guard, ident, lane));
                 } else {
                     // Q~ fragment (token block T, channel step m)
                     const int fq = task - NK, T = fq / NKS, m = fq % NKS;
                     const bool sec = NH == 2 && T >= 2;
-                    const E* src = sec ? sQ2 : sQh;
+                    const E* src = sec ? s.Q2 : s.Qh;
                     const int r = sec ? 16 * T - 32 + cl : 16 * T + cl;
                     u32x4 v;
                     if constexpr (sizeof(E) == 2) {
@@ -1115,7 +342,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
                     } else {
                         v = __builtin_bit_cast(u32x4, row4<E, D>(src, r, KB * m + 4 * gq));
                     }
-                    stg16(reinterpret_cast<unsigned char*>(gQt) + fq * F::FRAG + lane * 16, v);
+                    stg16(gQt + fq * F::FRAG + lane * 16, v);
                 }
             }
         }
@@ -1124,76 +351,27 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         // ---- D: -W fragments (waves 0-3), U~ tiles (waves 4-7) ------------
         {
             typename MM::Frag xf[NP];
-#pragma unroll
-            for (int T = 0; T < NB; ++T)
-#pragma unroll
-                for (int m = 0; m <= T / KT; ++m)
-                    xf[F::p_offset(T) + m] =
-                        *reinterpret_cast<const typename MM::Frag*>(sX + (16 * T + cl) * LDXP + KB * m + VEC * gq);
+            prep_x_frags<E, D, C>(s, xf, lane);
             if (wave < NWP / 2) {
-                E* gWn = (E*)a.Wn + rec * (F::W_BYTES / sizeof(E));
-                for (int m2 = wave; m2 < NKS; m2 += NWP / 2) {
-                    // E~^T fragments of channel blocks KT*m2.., every token step
-                    typename MM::Frag ea[KT][NKC];
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) {
-                        const int cb = KT * m2 + kt;
-#pragma unroll
-                        for (int m = 0; m < NKC; ++m) {
-                            f32x4 tt[KT];
-#pragma unroll
-                            for (int k2 = 0; k2 < KT; ++k2) {
-                                const int tb = KT * m + k2;
-                                const bool sec = NH == 2 && tb >= 2;
-                                tt[k2] = M16::mma(row4<E, D>(sec ? sE2 : sEh, sec ? 16 * tb - 32 + cl : 16 * tb + cl,
-                                                             16 * cb + 4 * gq),
-                                                  ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                            }
-                            ea[kt][m] = frag_of<E>(tt);
-                        }
-                    }
-#pragma unroll
-                    for (int T = 0; T < NB; ++T) {
-                        f32x4 wt[KT];
-#pragma unroll
-                        for (int kt = 0; kt < KT; ++kt) {
-                            wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int m = 0; m <= T / KT; ++m)
-                                wt[kt] = MM::mma(ea[kt][m], xf[F::p_offset(T) + m], wt[kt]);
-                            wt[kt] = -wt[kt];
-                        }
-                        stg16(reinterpret_cast<unsigned char*>(gWn) + (T * NKS + m2) * F::FRAG + lane * 16,
-                              __builtin_bit_cast(u32x4, frag_of<E>(wt)));
-                    }
-                }
+                unsigned char* gWn = (unsigned char*)a.Wn + rec * F::W_BYTES;
+                for (int m2 = wave; m2 < NKS; m2 += NWP / 2)
+                    prep_w<E, D, C>(s, xf, m2, gWn, ident, lane);
             } else {
                 E* gUt = (E*)a.Ut + rec * (F::U_BYTES / sizeof(E));
                 for (int n = wave - NWP / 2; n < D / 16; n += NWP / 2) {
-                    typename MM::Frag ub[NKC];
-#pragma unroll
-                    for (int m = 0; m < NKC; ++m) {
-                        f32x4 tt[KT];
-#pragma unroll
-                        for (int k2 = 0; k2 < KT; ++k2)
-                            tt[k2] = M16::mma(row4<E, D>(sU, 16 * (KT * m + k2) + cl, 16 * n + 4 * gq), ident,
-                                              f32x4{0.f, 0.f, 0.f, 0.f});
-                        ub[m] = frag_of<E>(tt);
-                    }
+                    f32x4 ut[NB];
+                    prep_u_tile<D, E, D, C>(s, xf, n, ut, ident, lane);
 #pragma unroll
                     for (int T = 0; T < NB; ++T) {
-                        f32x4 ut = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int m = 0; m <= T / KT; ++m)
-                            ut = MM::mma(xf[F::p_offset(T) + m], ub[m], ut);
                         E* dst = gUt + (n * NB + T) * (F::TILE_U / sizeof(E)) + lane * 4;
-                        *reinterpret_cast<typename Mma16<E>::Frag*>(dst) = M16::pack(ut);
+                        *reinterpret_cast<typename Mma16<E>::Frag*>(dst) = M16::pack(ut[T]);
                     }
                 }
             }
         }
     }
 }
+
 
 // ---------------------------------------------------------------------------
 // chunk_state: carries the fp32 state through the chunks of one sequence and
@@ -1232,8 +410,6 @@ struct StateShape {
     static_assert(U_SLICE % 1024 == 0, "U~ slice copies");
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Copy BYTES (a multiple of 1 KB) from global to LDS, 16 bytes per lane per
 // instruction; instruction j belongs to wave j % 4.
 template <size_t BYTES>
@@ -1261,22 +437,6 @@ __device__ __forceinline__ void state_fetch(const StateArgs& a, int64_t rec, int
     if (wave == (NT / 64) - 1 && lane < D / 4)
         __builtin_amdgcn_global_load_lds(a.gam + rec * D + lane * 4, (lds_void*)(buf + S::OFF_G), 16, 0, 0);
 }
-
-// Scheduling hint for a phase of N MFMAs fed from LDS: issue the first
-// group of fragment reads, then alternate one MFMA with one more read, so
-// reads run ahead of the MFMAs that consume them.
-template <int N>
-__device__ __forceinline__ void sched_pipeline()
-{
-    constexpr int AHEAD = N < 8 ? N : 8;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);   // DS reads
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // DS reads
-    }
-}
-
 
 template <typename E, int D, int C, int BV>
 __device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
@@ -1989,9 +1149,17 @@ hipError_t launch_span_fold(float* span, int64_t nbh, int64_t nseg, int D, hipSt
     return hipGetLastError();
 }
 
+// AUTO runs the staged kernels (one pass or segmented): at the training
+// shape the fused kernel is slower (it repeats each chunk's factors in both
+// value-column workgroups of a head, and the factors are compute-bound).
+int forward_algo(const gdr2_fwd_args& a)
+{
+    return a.algo == GDR2_ALGO_FUSED ? GDR2_ALGO_FUSED : GDR2_ALGO_STAGED;
+}
+
 size_t staged_workspace_bytes(const gdr2_fwd_args& a)
 {
-    if (a.B * a.H * a.T == 0)
+    if (a.B * a.H * a.T == 0 || forward_algo(a) == GDR2_ALGO_FUSED)
         return 0;
     return staged_layout(a.B, a.H, a.T, (int)a.Dk, a.chunk, a.dtype == GDR2_BF16 ? 2 : 4, seg_plan(a).nseg).total;
 }

@@ -12,6 +12,13 @@ namespace gdr2 {
 // Launchers: arguments are already validated; they only enqueue work.
 hipError_t launch_decode(const gdr2_decode_args& a, hipStream_t stream);
 hipError_t launch_forward_staged(const gdr2_fwd_args& a, hipStream_t stream);
+hipError_t launch_forward_fused(const gdr2_fwd_args& a, hipStream_t stream);
+
+// The fused forward has a kernel for these arguments (dtype, sizes).
+bool fused_supported(const gdr2_fwd_args& a);
+// The algorithm a forward call runs: GDR2_ALGO_FUSED, or STAGED (which
+// may segment, per segment_plan).
+int forward_algo(const gdr2_fwd_args& a);
 hipError_t launch_state_copy(const float* src, float* dst, int64_t n_floats, hipStream_t stream);
 hipError_t launch_backward(const gdr2_bwd_args& a, hipStream_t stream);
 

@@ -105,7 +105,7 @@ typedef enum gdr2_algo {
     GDR2_ALGO_STAGED = 1,  /* intra-chunk kernel writes per-chunk factors to the
                               workspace; a propagation kernel carries the state
                               through the chunks and writes o */
-    GDR2_ALGO_SEGMENTED = 2 /* STAGED with the chunks of each sequence cut into
+    GDR2_ALGO_SEGMENTED = 2, /* STAGED with the chunks of each sequence cut into
                               segments that run in parallel: a span kernel
                               forms each segment's chunk product and local
                               state, a fold kernel chains the segments' start
@@ -115,6 +115,15 @@ typedef enum gdr2_algo {
                               many chunks).  AUTO takes it when one pass would
                               leave most of the GPU idle.  Same results as
                               STAGED up to rounding order. */
+    GDR2_ALGO_FUSED = 3    /* one kernel per (sequence, head, 64 value
+                              columns): each workgroup forms every chunk's
+                              factors in LDS and carries the state through
+                              the chunks, so nothing per chunk goes through
+                              device memory and no workspace is needed.
+                              bf16 only (GDR2_ERR_UNSUPPORTED otherwise), and
+                              only with GDR2_STAGE_ALL.  AUTO does not take
+                              it.  Same results as STAGED up to rounding
+                              order. */
 } gdr2_algo;
 
 /* Which kernels of GDR2_ALGO_STAGED one call runs.  Two calls on the same

@@ -67,7 +67,7 @@ def fake(i, off=0):
 def good_fwd(B=2, T=100, H=3, D=128, chunk=64, dtype=gdr2.BF16, widths=None):
     a = gdr2.FwdArgs()
     a.B, a.T, a.H, a.Dk, a.Dv = B, T, H, D, D
-    a.chunk, a.dtype, a.algo = chunk, dtype, gdr2.ALGO_AUTO
+    a.chunk, a.dtype, a.algo = chunk, dtype, gdr2.ALGO_STAGED
     a.b_width, a.w_width, a.g_width = widths or (D, D, D)
     a.q, a.k, a.v, a.b, a.w, a.g = (fake(i) for i in range(6))
     a.S0, a.o, a.S_out = fake(6), fake(7), fake(8)
@@ -119,6 +119,9 @@ FWD_CASES = [
     ("S_chunks_overlaps_S_out", _mod(S_chunks=fake(8, 64)), gdr2.ERR_INVALID_ARG),
     ("S_chunks_overlaps_S0", _mod(S_chunks=fake(6, 0)), gdr2.ERR_INVALID_ARG),
     ("workspace_overlaps_S_chunks", _mod(S_chunks=fake(10), workspace=fake(10, 4096)), gdr2.ERR_INVALID_ARG),
+    ("fused_f32", _mod(algo=gdr2.ALGO_FUSED, dtype=gdr2.F32, Dk=64, Dv=64, b_width=64, w_width=64, g_width=64),
+     gdr2.ERR_UNSUPPORTED),
+    ("fused_with_stage", _mod(algo=gdr2.ALGO_FUSED, stage=1), gdr2.ERR_UNSUPPORTED),
 ]
 
 
@@ -168,6 +171,24 @@ def test_workspace_size_formula(lib):
     assert lib.gdr2_forward_workspace_size(ctypes.byref(a)) == 0
 
 
+def test_fused_needs_no_workspace(lib):
+    """GDR2_ALGO_FUSED keeps every chunk's factors on chip: no workspace, and
+    a call without one passes validation (then fails on purpose, on a NULL
+    output, so nothing launches).  AUTO keeps the staged kernels."""
+    def size(algo, stage=0, **kw):
+        a = good_fwd(**kw)
+        a.algo, a.stage = algo, stage
+        return lib.gdr2_forward_workspace_size(ctypes.byref(a))
+    big = dict(B=8, T=4096, H=16, D=128)
+    assert size(gdr2.ALGO_FUSED, **big) == 0
+    assert size(gdr2.ALGO_AUTO, **big) == size(gdr2.ALGO_STAGED, **big) > 0
+    a = good_fwd()
+    a.algo, a.workspace, a.workspace_bytes = gdr2.ALGO_FUSED, None, 0
+    a.o = None
+    assert lib.gdr2_forward_chunked(ctypes.byref(a), None) == gdr2.ERR_INVALID_ARG
+    assert b"o is NULL" in lib.gdr2_last_error()
+
+
 def test_segmented_workspace_size(lib):
     """The two-level scan adds two D x D fp32 matrices per (b, h) and per
     segment but the last.  Plans on a 256-CU device (the host without a GPU
@@ -193,9 +214,10 @@ def test_segmented_workspace_size(lib):
     base = size(gdr2.ALGO_STAGED, **shape)
     assert size(gdr2.ALGO_AUTO, **shape) == base + al(4 * 24 * 2 * 64 * 64 * 4)
     assert size(gdr2.ALGO_SEGMENTED, **shape) == base + al(4 * 49 * 2 * 64 * 64 * 4)
-    for kw in (dict(B=1, T=12 * 64, H=1, D=128),        # 12 chunks: 3 segments < 4
-               dict(B=8, T=4096, H=16, D=128)):         # 256 workgroups already
-        assert size(gdr2.ALGO_AUTO, **kw) == size(gdr2.ALGO_STAGED, **kw)
+    for kw in (dict(B=1, T=12 * 64, H=1),               # 12 chunks: 3 segments < 4
+               dict(B=8, T=4096, H=16)):                # 128 or 256 workgroups already
+        assert size(gdr2.ALGO_AUTO, D=64, dtype=gdr2.F32, **kw) == size(gdr2.ALGO_STAGED, D=64, dtype=gdr2.F32, **kw)
+        assert size(gdr2.ALGO_AUTO, D=128, **kw) == size(gdr2.ALGO_STAGED, D=128, **kw)
     assert size(gdr2.ALGO_SEGMENTED, B=1, T=64, H=1, D=128) == size(gdr2.ALGO_STAGED, B=1, T=64, H=1, D=128)
 
 

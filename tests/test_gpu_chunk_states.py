@@ -19,9 +19,14 @@ CASES = [
     # name, B, T, H, D, dtype, chunk, S0 std, algo
     ("f32_d64_c32", 1, 100, 2, 64, "f32", 32, 0.05, "auto"),
     ("f32_d64_c64", 2, 130, 1, 64, "f32", 64, 0.0, "auto"),
-    ("bf16_d128_c64_ragged", 2, 150, 2, 128, "bf16", 64, 0.05, "auto"),
-    ("bf16_d128_c32", 1, 96, 3, 128, "bf16", 32, 0.02, "auto"),
-    ("bf16_d64_c64", 1, 64, 2, 64, "bf16", 64, 0.05, "auto"),
+    ("bf16_d128_c64_ragged", 2, 150, 2, 128, "bf16", 64, 0.05, "staged"),
+    ("bf16_d128_c32", 1, 96, 3, 128, "bf16", 32, 0.02, "staged"),
+    ("bf16_d64_c64", 1, 64, 2, 64, "bf16", 64, 0.05, "staged"),
+    # the fused kernel
+    ("bf16_d128_c64_ragged_fused", 2, 150, 2, 128, "bf16", 64, 0.05, "fused"),
+    ("bf16_d128_c32_fused", 1, 96, 3, 128, "bf16", 32, 0.02, "fused"),
+    ("bf16_d64_c64_fused", 1, 64, 2, 64, "bf16", 64, 0.05, "fused"),
+    ("bf16_d64_c32_fused", 2, 200, 2, 64, "bf16", 32, 0.0, "fused"),
     # two-level scan: every segment emits its own chunks' starts
     ("bf16_d128_c64_segmented", 2, 700, 2, 128, "bf16", 64, 0.05, "segmented"),
     ("f32_d64_c32_segmented", 1, 300, 2, 64, "f32", 32, 0.0, "segmented"),
@@ -57,8 +62,8 @@ def test_chunk_states_written_by_the_state_stage():
     inp = draw(Workload("ck_stages", "forward", 1, 200, 2, 128, "bf16", "full", 0.05, 64, 402))
     d = to_dev(inp)
     args = [d[n] for n in NAMES]
-    o1, S1, ck1 = gdr2.forward(*args, S0=d["S0"], chunk=64, chunk_states=True)
-    ws = torch.empty(gdr2.workspace_size(*args, chunk=64), dtype=torch.uint8, device="cuda")
+    o1, S1, ck1 = gdr2.forward(*args, S0=d["S0"], chunk=64, chunk_states=True, algo="staged")
+    ws = torch.empty(gdr2.workspace_size(*args, chunk=64, algo="staged"), dtype=torch.uint8, device="cuda")
     o2, S2 = torch.empty_like(o1), torch.empty_like(S1)
     ck2 = torch.full_like(ck1, float("nan"))
     gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="prep",

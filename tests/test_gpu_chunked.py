@@ -41,15 +41,18 @@ def test_tiny_f32_workload():
     check(draw(wl), wl.chunk, wl.dtype, "tiny_f32")
 
 
-SMALL = [(dt, D, C) for dt in ("bf16", "f32") for D in (64, 128) for C in (32, 64)
-         if not (dt == "f32" and D * C > 4096)]
+# (dtype, D, C, algo): the staged kernels for every supported size, and the
+# fused kernel (bf16 only) likewise
+SMALL = [(dt, D, C, al) for dt in ("bf16", "f32") for D in (64, 128) for C in (32, 64)
+         for al in ("staged", "fused")
+         if not (dt == "f32" and D * C > 4096) and not (dt == "f32" and al == "fused")]
 
 
-@pytest.mark.parametrize("dtype,D,C", SMALL, ids=[f"{a}-d{b}-c{c}" for a, b, c in SMALL])
+@pytest.mark.parametrize("dtype,D,C,algo", SMALL, ids=[f"{a}-d{b}-c{c}-{d}" for a, b, c, d in SMALL])
 @pytest.mark.parametrize("T", [1, 15, 33, 64, 130])
-def test_ragged_lengths(dtype, D, C, T):
+def test_ragged_lengths(dtype, D, C, algo, T):
     wl = Workload("small", "forward", 2, T, 2, D, dtype, "full", 0.05, C, 7 * T + D + C)
-    check(draw(wl), C, dtype, f"{dtype} D={D} C={C} T={T}")
+    check(draw(wl), C, dtype, f"{dtype} D={D} C={C} T={T} {algo}", algo=algo)
 
 
 # The prep pass is persistent (one workgroup per CU, items visited with a
@@ -67,17 +70,27 @@ WALK_CASES = [
 @pytest.mark.parametrize("B,T,H", WALK_CASES, ids=[f"B{b}_T{t}_H{h}" for b, t, h in WALK_CASES])
 def test_prep_item_walk(B, T, H):
     wl = Workload("walk", "forward", B, T, H, 64, "bf16", "full", 0.05, 64, 17 * H + T + B)
-    check(draw(wl), 64, "bf16", f"walk B={B} T={T} H={H}")
+    check(draw(wl), 64, "bf16", f"walk B={B} T={T} H={H}", algo="staged")
 
 
-WIDTH_CFGS = [("bf16", 128, 64), ("f32", 64, 32), ("bf16", 64, 32)]
+@pytest.mark.parametrize("B,T,H", [(1, 64, 300), (3, 200, 100), (2, 70, 13)], ids=["H300", "B3_H100", "B2_H13"])
+def test_fused_grid_mapping(B, T, H):
+    """The fused kernel's workgroups: B*H (sequence, head) pairs times the
+    value slices, grouped 8 pairs per XCD; counts that are not multiples of
+    8 leave idle workgroups in the last group."""
+    wl = Workload("fgrid", "forward", B, T, H, 128, "bf16", "full", 0.05, 64, 19 * H + T + B)
+    check(draw(wl), 64, "bf16", f"fused grid B={B} T={T} H={H}", algo="fused")
+
+
+WIDTH_CFGS = [("bf16", 128, 64, "staged"), ("f32", 64, 32, "staged"), ("bf16", 64, 32, "staged"),
+              ("bf16", 128, 64, "fused"), ("bf16", 64, 32, "fused")]
 WIDTH_MIXES = [(nb, nw, ng) for nb in (0, 1) for nw in (0, 1) for ng in (0, 1)]
 
 
-@pytest.mark.parametrize("dtype,D,C", WIDTH_CFGS, ids=[f"{a}-d{b}-c{c}" for a, b, c in WIDTH_CFGS])
+@pytest.mark.parametrize("dtype,D,C,algo", WIDTH_CFGS, ids=[f"{a}-d{b}-c{c}-{d}" for a, b, c, d in WIDTH_CFGS])
 @pytest.mark.parametrize("mix", WIDTH_MIXES, ids=["b%s_w%s_g%s" % tuple("1" if x else "d" for x in m)
                                                   for m in WIDTH_MIXES])
-def test_gate_widths(dtype, D, C, mix):
+def test_gate_widths(dtype, D, C, algo, mix):
     """Every gate-width mix (b, w, g each of width 1 or d; each mix has its
     own compiled prep kernel): scalar gates broadcast, and the result must
     equal the oracle on the same (width-1) inputs."""
@@ -86,17 +99,18 @@ def test_gate_widths(dtype, D, C, mix):
     for n, narrow in zip(("b", "w", "g"), mix):
         if narrow:
             inp[n] = inp[n][..., :1].contiguous()
-    check(inp, C, dtype, f"widths {mix} {dtype} D={D} C={C}")
+    check(inp, C, dtype, f"widths {mix} {dtype} D={D} C={C} {algo}", algo=algo)
 
 
+@pytest.mark.parametrize("algo", ["staged", "fused"])
 @pytest.mark.parametrize("g_const,g_scale", [(0.0, 1.0), (-80.0, 1.0), (None, 0.01), (-1e-4, 1.0)],
                          ids=["no_decay", "steep_decay", "weak_decay", "tiny_decay"])
-def test_decay_extremes(g_const, g_scale):
+def test_decay_extremes(g_const, g_scale, algo):
     """g = 0 (no decay), g = -80 (every factor underflows; the block-span
     guard takes the exact path), g scaled by 0.01 (long memory)."""
     wl = Workload("decay", "forward", 1, 200, 2, 128, "bf16", "full", 0.05, 64, 77,
                   g_scale=g_scale, g_const=g_const)
-    check(draw(wl), 64, "bf16", f"decay const={g_const} scale={g_scale}")
+    check(draw(wl), 64, "bf16", f"decay const={g_const} scale={g_scale} {algo}", algo=algo)
 
 
 # Around the half-chunk span guard: a constant log-decay of c nats per token
@@ -106,14 +120,18 @@ def test_decay_extremes(g_const, g_scale):
 # interface: the decay factors then exceed 1.
 @pytest.mark.parametrize("g_const", [-1.6, -1.7, -1.75, -1.8, 0.01, 0.05],
                          ids=["span_73.9", "span_78.5", "span_80.8", "span_83.1", "growth_0.01", "growth_0.05"])
-@pytest.mark.parametrize("dtype,D,C", [("bf16", 128, 64), ("bf16", 64, 32), ("f32", 64, 64)],
-                         ids=["bf16-d128-c64", "bf16-d64-c32", "f32-d64-c64"])
-def test_decay_near_guard_and_growth(g_const, dtype, D, C):
+@pytest.mark.parametrize("dtype,D,C,algo", [("bf16", 128, 64, "staged"), ("bf16", 64, 32, "staged"),
+                                             ("f32", 64, 64, "staged"), ("bf16", 128, 64, "fused"),
+                                             ("bf16", 64, 32, "fused")],
+                         ids=["bf16-d128-c64", "bf16-d64-c32", "f32-d64-c64", "bf16-d128-c64-fused",
+                              "bf16-d64-c32-fused"])
+def test_decay_near_guard_and_growth(g_const, dtype, D, C, algo):
     wl = Workload("guard", "forward", 1, 300, 2, D, dtype, "full", 0.05, C, 79, g_const=g_const)
-    check(draw(wl), C, dtype, f"g={g_const} {dtype} D={D} C={C}")
+    check(draw(wl), C, dtype, f"g={g_const} {dtype} D={D} C={C} {algo}", algo=algo)
 
 
-def test_decay_mixed_steep_channels():
+@pytest.mark.parametrize("algo", ["staged", "fused"])
+def test_decay_mixed_steep_channels(algo):
     """Standard decay on most key channels, and on a few channels a decay
     steep enough to trip the span guard in some chunks only: those chunks
     take the exact path while their neighbours take the MFMA path."""
@@ -123,17 +141,18 @@ def test_decay_mixed_steep_channels():
     g[:, 100:170, :, ::17] = -3.0        # chunks 1 and 2 of every head
     g[1, 300:310, 2, 5] = -20.0          # one channel of one chunk
     inp["g"] = g
-    check(inp, 64, "bf16", "mixed steep channels")
+    check(inp, 64, "bf16", f"mixed steep channels {algo}", algo=algo)
 
 
-def test_growth_scalar_and_per_channel_decay():
+@pytest.mark.parametrize("algo", ["staged", "fused"])
+def test_growth_scalar_and_per_channel_decay(algo):
     """Positive log-decay with per-channel and scalar decay widths."""
     wl = Workload("grow", "forward", 1, 260, 2, 128, "bf16", "full", 0.05, 64, 81)
     inp = draw(wl)
     inp["g"] = (inp["g"] * -0.02).contiguous()          # g in (0, ~0.1]
-    check(inp, 64, "bf16", "growth per channel")
+    check(inp, 64, "bf16", f"growth per channel {algo}", algo=algo)
     inp["g"] = inp["g"][..., :1].contiguous()
-    check(inp, 64, "bf16", "growth scalar")
+    check(inp, 64, "bf16", f"growth scalar {algo}", algo=algo)
 
 
 def test_steep_decay_f32():
@@ -141,18 +160,19 @@ def test_steep_decay_f32():
     check(draw(wl), 32, "f32", "steep decay f32")
 
 
-def test_inplace_state_and_chaining():
+@pytest.mark.parametrize("algo", ["staged", "fused"])
+def test_inplace_state_and_chaining(algo):
     """S_out may alias S0; running x[:T1] then x[T1:] from the state it ends
     in reproduces one call (within rounding)."""
     wl = Workload("chain", "forward", 2, 300, 2, 128, "bf16", "full", 0.05, 64, 31)
     inp = draw(wl)
     d = to_dev(inp)
-    o_all, S_all = gdr2.forward(*(d[n] for n in NAMES), S0=d["S0"], chunk=64)
+    o_all, S_all = gdr2.forward(*(d[n] for n in NAMES), S0=d["S0"], chunk=64, algo=algo)
     S = d["S0"].clone()
     parts = []
     for lo, hi in ((0, 100), (100, 101), (101, 300)):
         sl = {n: d[n][:, lo:hi].contiguous() for n in NAMES}
-        o, _ = gdr2.forward(*(sl[n] for n in NAMES), S0=S, S_out=S, chunk=64)
+        o, _ = gdr2.forward(*(sl[n] for n in NAMES), S0=S, S_out=S, chunk=64, algo=algo)
         parts.append(o)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_forward(inp)
@@ -188,18 +208,22 @@ def test_zero_length_copies_state():
     assert torch.count_nonzero(S) == 0
 
 
-def test_deterministic_and_no_uninitialised_reads():
+@pytest.mark.parametrize("algo", ["staged", "fused"])
+def test_deterministic_and_no_uninitialised_reads(algo):
     """Two runs agree bit for bit (no atomics anywhere), and a workspace
-    poisoned with NaN before the call leaves no NaN in the results."""
+    poisoned with NaN before the call, and outputs poisoned likewise, leave
+    no NaN in the results."""
     wl = Workload("det", "forward", 2, 257, 3, 128, "bf16", "full", 0.05, 64, 8)
     inp = draw(wl)
     d = to_dev(inp)
     args = [d[n] for n in NAMES]
-    need = gdr2.workspace_size(*args, chunk=64)
+    need = max(gdr2.workspace_size(*args, chunk=64, algo=algo), 16)
     ws = torch.full((need // 4,), float("nan"), device="cuda").view(torch.uint8)
-    o1, S1 = gdr2.forward(*args, S0=d["S0"], chunk=64, workspace=ws)
+    o1 = torch.full_like(d["v"], float("nan"))
+    S1 = torch.full_like(d["S0"], float("nan"))
+    gdr2.forward(*args, S0=d["S0"], chunk=64, workspace=ws, out=o1, S_out=S1, algo=algo)
     ws.view(torch.float32).fill_(float("nan"))
-    o2, S2 = gdr2.forward(*args, S0=d["S0"], chunk=64, workspace=ws)
+    o2, S2 = gdr2.forward(*args, S0=d["S0"], chunk=64, workspace=ws, algo=algo)
     torch.cuda.synchronize()
     assert finite(o1) and finite(S1)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
@@ -211,25 +235,28 @@ def test_gdn_scalar_workload():
     check(draw(wl), wl.chunk, wl.dtype, "gdn_scalar")
 
 
-def _whole(wl, label):
+def _whole(wl, label, algos=("auto",)):
     """The GPU forward over the whole workload in the launch configuration
-    the benchmark times, and the oracle over every (b, h) recurrence of it."""
+    the benchmark times (algo "auto"; others as given), and the oracle over
+    every (b, h) recurrence of it."""
     inp = draw(wl)
-    o, S = gpu_forward(inp, wl.chunk)
-    assert finite(o) and finite(S)
     o_ref, S_ref = oracle_forward(inp)
-    o64 = to_f64(o)
-    eo = normwise(o64, o_ref)
-    es = normwise(to_f64(S), S_ref, "state")
-    print(f"{label} (all {wl.B * wl.H} (b,h) slices): o {eo:.2e}  S {es:.2e}", flush=True)
-    assert eo <= TOL[wl.dtype] and es <= TOL[wl.dtype]
+    for algo in algos:
+        o, S = gpu_forward(inp, wl.chunk, algo=algo)
+        assert finite(o) and finite(S)
+        o64 = to_f64(o)
+        eo = normwise(o64, o_ref)
+        es = normwise(to_f64(S), S_ref, "state")
+        print(f"{label} {algo} (all {wl.B * wl.H} (b,h) slices): o {eo:.2e}  S {es:.2e}", flush=True)
+        assert eo <= TOL[wl.dtype] and es <= TOL[wl.dtype], algo
     return o64, o_ref
 
 
 def test_train_4k_workload_all_heads():
     """The benchmark workload (B=8 H=16 T=4096 d=128 bf16, chunk 64): every
-    one of the 128 (b, h) slices of o and S_final against the oracle."""
-    _whole(WORKLOADS["train_4k"], "train_4k")
+    one of the 128 (b, h) slices of o and S_final against the oracle, for the
+    algorithm the library picks and the fused kernel."""
+    _whole(WORKLOADS["train_4k"], "train_4k", algos=("auto", "fused"))
 
 
 def per_chunk_errors(x, y, chunk):
@@ -322,8 +349,8 @@ def test_stage_split_equals_one_call():
     inp = draw(wl)
     d = to_dev(inp)
     args = [d[n] for n in NAMES]
-    o1, S1 = gdr2.forward(*args, S0=d["S0"], chunk=64)
-    ws = torch.empty(gdr2.workspace_size(*args, chunk=64), dtype=torch.uint8, device="cuda")
+    o1, S1 = gdr2.forward(*args, S0=d["S0"], chunk=64, algo="staged")
+    ws = torch.empty(gdr2.workspace_size(*args, chunk=64, algo="staged"), dtype=torch.uint8, device="cuda")
     o2 = torch.empty_like(o1)
     S2 = torch.empty_like(S1)
     gdr2.forward(*args, S0=d["S0"], chunk=64, out=o2, S_out=S2, workspace=ws, stage="prep")

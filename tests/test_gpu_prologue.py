@@ -60,9 +60,13 @@ def _fwd_check(name, wl, bits, chunk, algo="auto"):
     assert eo <= tol and es <= tol and ec <= tol, f"{name}: {eo:.3e} {es:.3e} {ec:.3e}"
 
 
+@pytest.mark.parametrize("algo", ["staged", "fused"])
 @pytest.mark.parametrize("name,B,T,H,D,dtype,gates,s0,chunk,bits", FWD_CASES, ids=[c[0] for c in FWD_CASES])
-def test_forward_prologue_matches_oracle(name, B, T, H, D, dtype, gates, s0, chunk, bits):
-    _fwd_check(name, Workload(name, "forward", B, T, H, D, dtype, gates, s0, chunk, 801), bits, chunk)
+def test_forward_prologue_matches_oracle(name, B, T, H, D, dtype, gates, s0, chunk, bits, algo):
+    """Both forward algorithms (the fused one for bf16 only)."""
+    if algo == "fused" and dtype != "bf16":
+        pytest.skip("the fused kernel takes bf16 inputs only")
+    _fwd_check(name, Workload(name, "forward", B, T, H, D, dtype, gates, s0, chunk, 801), bits, chunk, algo=algo)
 
 
 @pytest.mark.parametrize("dtype,D,chunk", [("bf16", 128, 64), ("f32", 64, 32)])
@@ -74,12 +78,13 @@ def test_forward_prologue_two_level_scan(dtype, D, chunk):
                algo="segmented")
 
 
-def test_forward_prologue_steep_decay_exact_path():
+@pytest.mark.parametrize("algo", ["staged", "fused"])
+def test_forward_prologue_steep_decay_exact_path(algo):
     """Decay pre-activation 80: log-decay -softplus(80) ~ -80 per token, so
-    the prep kernel takes its exact pair-by-pair path, which reads the raw
-    inputs again and must apply the prologue there too."""
+    the chunk's factors take the exact pair-by-pair path, which reads the
+    raw inputs again and must apply the prologue there too."""
     wl = Workload("steep_pro", "forward", 1, 80, 2, 128, "bf16", "full", 0.05, 64, 802, g_const=80.0)
-    _fwd_check("steep_pro", wl, pro.ALL, 64)
+    _fwd_check("steep_pro", wl, pro.ALL, 64, algo=algo)
 
 
 def test_prologue_off_is_unchanged():
