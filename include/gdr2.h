@@ -121,9 +121,12 @@ typedef enum gdr2_algo {
                               the chunks, so nothing per chunk goes through
                               device memory and no workspace is needed.
                               bf16 only (GDR2_ERR_UNSUPPORTED otherwise), and
-                              only with GDR2_STAGE_ALL.  AUTO does not take
-                              it.  Same results as STAGED up to rounding
-                              order. */
+                              only with GDR2_STAGE_ALL.  AUTO takes it for
+                              bf16 at Dk = 64 when B*H is at least the GPU's
+                              compute-unit count (there it is faster than
+                              STAGED; at Dk = 128 each head's two column
+                              workgroups would repeat the chunk's factors).
+                              Same results as STAGED up to rounding order. */
 } gdr2_algo;
 
 /* Which kernels of GDR2_ALGO_STAGED one call runs.  Two calls on the same

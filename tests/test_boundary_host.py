@@ -182,6 +182,12 @@ def test_fused_needs_no_workspace(lib):
     big = dict(B=8, T=4096, H=16, D=128)
     assert size(gdr2.ALGO_FUSED, **big) == 0
     assert size(gdr2.ALGO_AUTO, **big) == size(gdr2.ALGO_STAGED, **big) > 0
+    # d = 64 with B*H >= the compute units (256 on a host without a GPU):
+    # AUTO takes the fused kernel; fewer pairs, fp32, or a stage: staged
+    assert size(gdr2.ALGO_AUTO, B=16, T=4096, H=16, D=64) == 0
+    assert size(gdr2.ALGO_AUTO, B=8, T=4096, H=16, D=64) > 0
+    assert size(gdr2.ALGO_AUTO, B=16, T=4096, H=16, D=64, dtype=gdr2.F32) > 0
+    assert size(gdr2.ALGO_AUTO, stage=1, B=16, T=4096, H=16, D=64) > 0
     a = good_fwd()
     a.algo, a.workspace, a.workspace_bytes = gdr2.ALGO_FUSED, None, 0
     a.o = None

@@ -82,6 +82,19 @@ def test_fused_grid_mapping(B, T, H):
     check(draw(wl), 64, "bf16", f"fused grid B={B} T={T} H={H}", algo="fused")
 
 
+def test_auto_takes_fused_at_d64_when_pairs_fill_the_gpu():
+    """d = 64 with B*H >= the compute units: AUTO runs the fused kernel (no
+    workspace), and the result matches the oracle and the staged kernels."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    wl = Workload("auto_fused", "forward", 2, 130, (ncu + 1) // 2, 64, "bf16", "full", 0.05, 64, 91)
+    inp = draw(wl)
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    assert gdr2.workspace_size(*args, chunk=64) == 0 < gdr2.workspace_size(*args, chunk=64, algo="staged")
+    check(inp, 64, "bf16", "auto (fused) d=64")
+    check(inp, 64, "bf16", "staged d=64", algo="staged")
+
+
 WIDTH_CFGS = [("bf16", 128, 64, "staged"), ("f32", 64, 32, "staged"), ("bf16", 64, 32, "staged"),
               ("bf16", 128, 64, "fused"), ("bf16", 64, 32, "fused")]
 WIDTH_MIXES = [(nb, nw, ng) for nb in (0, 1) for nw in (0, 1) for ng in (0, 1)]
