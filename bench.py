@@ -218,6 +218,41 @@ def host_cpu_info() -> dict:
             "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
+def bench_fused(torch, gdr2, lib, steps: int):
+    """The fused forward (one kernel, no workspace) beside the staged one:
+    at the training shape, and at d = 64 with B*H = 256 (sequences x heads
+    filling the GPU), where the library's default takes it."""
+    from gated_delta_rule_86_amd.inputs import WORKLOADS, draw
+
+    out = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    for label, wl in (("train_4k", WORKLOADS["train_4k"]), ("B16_H16_T4096_d64", WORKLOADS["train_4k"].with_(B=16, D=64))):
+        d = {n: (None if t is None else t.cuda()) for n, t in draw(wl).items()}
+        x = [d[n] for n in NAMES]
+        o = torch.empty_like(d["v"])
+        S_out = torch.empty((wl.B, wl.H, wl.D, wl.D), dtype=torch.float32, device="cuda")
+        for algo in ("staged", "fused"):
+            ws = torch.empty(max(gdr2.workspace_size(*x, chunk=wl.chunk, algo=algo), 16), dtype=torch.uint8,
+                             device="cuda")
+            a = gdr2.fwd_args(*x, S0=d["S0"], o=o, S_out=S_out, chunk=wl.chunk, workspace=ws, algo=algo)
+            for _ in range(20):
+                assert lib.gdr2_forward_chunked(ctypes.byref(a), stream) == 0, lib.gdr2_last_error()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                lib.gdr2_forward_chunked(ctypes.byref(a), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            out[f"{label}_{algo}_ms"] = round(ms, 4)
+            out[f"{label}_{algo}_tokens_per_s"] = round(wl.B * wl.T / (ms * 1e-3), 1)
+            del ws
+        del d, x, o, S_out
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, wl):
     """The fp64 oracle (as it stands) on the host cores over the whole
     workload batch: every (b, h) recurrence, OpenMP over them, with as many
@@ -417,10 +452,17 @@ def main():
     ap.add_argument("--no-gate-widths", action="store_true", help="skip the gate-width sweep")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy bandwidth reference")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context forward")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-kernel comparison")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the training-shape forward legs (warm-up, timed loop, repeats, per-kernel split): "
+                         "for a profile of the headline kernels alone")
     ap.add_argument("--long-only", action="store_true",
                     help="time only the long-context forward and print its JSON object (for a profile of "
                          "those kernels alone)")
     args = ap.parse_args()
+    if args.headline_only:
+        args.no_decode = args.no_long = args.no_fused = args.no_gate_widths = args.no_backward = True
+        args.no_copy = args.no_cpu_baseline = True
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards across GPUs without communication by (batch, head); "
@@ -457,6 +499,8 @@ def main():
                                            for n in (2, 4)]
     if not args.no_long:
         extra["long_context"] = bench_long(torch, gdr2, lib, max(1, K // 2), 5)
+    if not args.no_fused:
+        extra["fused"] = bench_fused(torch, gdr2, lib, K)
 
     wl = WORKLOADS["train_4k"]
     inp = draw(wl)

@@ -160,9 +160,6 @@ gdr2_status validate_forward(const gdr2_fwd_args* a, int64_t* state_bytes, bool 
         return fail(GDR2_ERR_INVALID_ARG, "unknown prologue bits 0x%x", a->prologue);
     if (a->chunk != 32 && a->chunk != 64)
         return fail(GDR2_ERR_UNSUPPORTED, "supported chunk sizes: 32, 64 (got %d)", a->chunk);
-    if (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096)
-        return fail(GDR2_ERR_UNSUPPORTED, "fp32 needs Dk * chunk <= 4096 (got %lld * %d)",
-                    (long long)a->Dk, a->chunk);
     if (a->algo == GDR2_ALGO_FUSED && !gdr2::fused_supported(*a))
         return fail(GDR2_ERR_UNSUPPORTED, "GDR2_ALGO_FUSED supports bf16 inputs only");
     if (a->algo == GDR2_ALGO_FUSED && a->stage != GDR2_STAGE_ALL)
@@ -343,7 +340,6 @@ size_t gdr2_forward_workspace_size(const gdr2_fwd_args* a)
         return 0;
     if (a->Dk != a->Dv || (a->Dk != 64 && a->Dk != 128) || (a->chunk != 32 && a->chunk != 64) ||
         (a->dtype != GDR2_F32 && a->dtype != GDR2_BF16) ||
-        (a->dtype == GDR2_F32 && a->Dk * a->chunk > 4096) ||
         (a->algo != GDR2_ALGO_AUTO && a->algo != GDR2_ALGO_STAGED && a->algo != GDR2_ALGO_SEGMENTED &&
          a->algo != GDR2_ALGO_FUSED))
         return 0;

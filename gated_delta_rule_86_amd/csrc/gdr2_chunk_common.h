@@ -250,14 +250,39 @@ struct PrepGeom {
     static_assert(NWB == NWP || NH == 1, "halves need every wave in phase B");
 };
 
-// LDS arrays of the phases.  U holds UC value columns per row (u_lo ..
-// u_lo + UC - 1); the others full rows of D.
-template <typename E>
+}  // namespace
+
+// The kernel's dynamic LDS (every extern __shared__ array of a kernel names
+// the same base).
+extern __shared__ __align__(16) unsigned char dyn_lds[];
+
+namespace {
+
+// LDS arrays of the phases, at the byte offsets OFF_* of the kernel's layout
+// L in its dynamic LDS (compile-time offsets, so every access is an LDS
+// address with a constant offset).  U holds UC value columns per row
+// (u_lo .. u_lo + UC - 1); the others full rows of D.  G (the raw or
+// cumulative log-decay) and BW (width-1 b and w of the chunk, [2][C] words)
+// are the kernel's static LDS arrays.
+template <typename E, typename L>
 struct PrepLds {
-    E *Eh, *Qh, *Kr, *U, *E2, *Q2, *M, *X;
-    float *Md, *Xc, *Tot, *Fk, *Rn, *G;
-    int* Flag;
-    unsigned int* BW;      // width-1 b and w of the chunk, [2][C] words
+    float* G;
+    unsigned int* BW;
+    template <typename T> static __device__ __forceinline__ T* at(size_t off) { return reinterpret_cast<T*>(dyn_lds + off); }
+    static __device__ __forceinline__ E* Eh() { return at<E>(L::OFF_EH); }
+    static __device__ __forceinline__ E* Qh() { return at<E>(L::OFF_QH); }
+    static __device__ __forceinline__ E* Kr() { return at<E>(L::OFF_KR); }
+    static __device__ __forceinline__ E* U() { return at<E>(L::OFF_U); }
+    static __device__ __forceinline__ E* E2() { return at<E>(L::OFF_E2); }
+    static __device__ __forceinline__ E* Q2() { return at<E>(L::OFF_Q2); }
+    static __device__ __forceinline__ E* M() { return at<E>(L::OFF_M); }
+    static __device__ __forceinline__ E* X() { return at<E>(L::OFF_X); }
+    static __device__ __forceinline__ float* Md() { return at<float>(L::OFF_MD); }
+    static __device__ __forceinline__ float* Xc() { return at<float>(L::OFF_XC); }
+    static __device__ __forceinline__ float* Tot() { return at<float>(L::OFF_TOT); }
+    static __device__ __forceinline__ float* Fk() { return at<float>(L::OFF_FK); }
+    static __device__ __forceinline__ float* Rn() { return at<float>(L::OFF_RN); }
+    static __device__ __forceinline__ int* Flag() { return at<int>(L::OFF_FLAG); }
 };
 
 // Row swizzle of the [rows][D] operand arrays: 16-byte chunk j of row r
@@ -372,10 +397,10 @@ __device__ __forceinline__ void prep_copy_bw(const PrepIn& a, const ChunkPos& cp
 // Phase B for one lane: decay-referenced operands of its tokens into LDS.
 // VALID: every token of the chunk is valid (no zeroing needed).  u = w v is
 // stored only for the value columns u_lo .. u_lo + UC - 1 (rows of UC).
-template <bool VALID, bool SECOND, bool PRO, int UC, typename E, int D, int C>
+template <bool VALID, bool SECOND, bool PRO, int UC, typename E, int D, int C, typename SL>
 __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const float (*G)[16 / sizeof(E)],
                                                const float* gh, int bw, int ww, int L, int t0, int c0,
-                                               const PrepLds<E>& s, int u_lo, int pro)
+                                               const SL& s, int u_lo, int pro)
 {
     typedef PrepGeom<E, D, C> S;
     constexpr int VEC = S::VEC;
@@ -419,7 +444,7 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
                 for (int x = 0; x < VEC; ++x)
                     kk[x] *= rk;
                 if (c0 == 0)
-                    s.Rn[t] = rk;
+                    s.Rn()[t] = rk;
             }
         }
 #pragma unroll
@@ -428,7 +453,7 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
             tmp[x] = kk[x] * fast_exp2(-d[x]);
             eh[x] = fast_exp2(d[x]);
         }
-        sts16(s.Kr + o, pack_vec<E>(tmp));
+        sts16(s.Kr() + o, pack_vec<E>(tmp));
         __builtin_amdgcn_sched_barrier(0);
         {
             float bb[VEC];
@@ -449,9 +474,9 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
                     tmp2[x] = tmp[x] * fh[x];
             }
         }
-        sts16(s.Eh + o, pack_vec<E>(tmp));
+        sts16(s.Eh() + o, pack_vec<E>(tmp));
         if (SECOND)
-            sts16(s.E2 + o2, pack_vec<E>(tmp2));
+            sts16(s.E2() + o2, pack_vec<E>(tmp2));
         __builtin_amdgcn_sched_barrier(0);
         {
             float qq[VEC];
@@ -470,7 +495,7 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
                     for (int x = 0; x < VEC; ++x)
                         qq[x] *= rq;
                     if (c0 == 0)
-                        s.Rn[C + t] = rq;
+                        s.Rn()[C + t] = rq;
                 }
             }
 #pragma unroll
@@ -480,9 +505,9 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
                     tmp2[x] = tmp[x] * fh[x];
             }
         }
-        sts16(s.Qh + o, pack_vec<E>(tmp));
+        sts16(s.Qh() + o, pack_vec<E>(tmp));
         if (SECOND)
-            sts16(s.Q2 + o2, pack_vec<E>(tmp2));
+            sts16(s.Q2() + o2, pack_vec<E>(tmp2));
         __builtin_amdgcn_sched_barrier(0);
         if (own_u) {
             float vv[VEC], wv[VEC];
@@ -500,7 +525,7 @@ __device__ __forceinline__ float prep_operands(const PrepRegs<E, D, C>& R, const
 #pragma unroll
             for (int x = 0; x < VEC; ++x)
                 tmp[x] = (valid ? (ww == 1 ? ws : wv[x]) : 0.f) * vv[x];
-            sts16(s.U + swz<E, UC>(t, c0 - u_lo), pack_vec<E>(tmp));
+            sts16(s.U() + swz<E, UC>(t, c0 - u_lo), pack_vec<E>(tmp));
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -537,11 +562,11 @@ __device__ __forceinline__ typename Mma16<E>::Frag identity16(int gq, int cl)
 // ---------------------------------------------------------------------------
 // Phase A: cumulative log2-decay of this lane's TPL tokens, in registers.
 // The prefix sum runs within the lane, across the LPC lanes sharing the
-// channels (DPP row shifts); each wave's totals go to s.Tot for phase B.
+// channels (DPP row shifts); each wave's totals go to s.Tot() for phase B.
 // Only waves < NWB call it.
 // ---------------------------------------------------------------------------
-template <int WG, bool PRO, typename E, int D, int C>
-__device__ __forceinline__ void prep_cumsum(const PrepIn& a, const PrepLds<E>& s, int L, int t0, int c0, int lpc,
+template <int WG, bool PRO, typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_cumsum(const PrepIn& a, const SL& s, int L, int t0, int c0, int lpc,
                                             int wave, float (&G)[PrepGeom<E, D, C>::TPL][16 / sizeof(E)],
                                             float (&excl)[16 / sizeof(E)])
 {
@@ -611,7 +636,7 @@ __device__ __forceinline__ void prep_cumsum(const PrepIn& a, const PrepLds<E>& s
     if (lpc == S::LPC - 1) {
 #pragma unroll
         for (int x4 = 0; x4 < VEC / 4; ++x4)
-            *reinterpret_cast<f32x4*>(s.Tot + wave * D + c0 + 4 * x4) =
+            *reinterpret_cast<f32x4*>(s.Tot() + wave * D + c0 + 4 * x4) =
                 f32x4{inc[4 * x4], inc[4 * x4 + 1], inc[4 * x4 + 2], inc[4 * x4 + 3]};
     }
 }
@@ -619,12 +644,12 @@ __device__ __forceinline__ void prep_cumsum(const PrepIn& a, const PrepLds<E>& s
 // ---------------------------------------------------------------------------
 // Phase B: the chunk-level offsets from the wave totals (G becomes the
 // cumulative decay from the chunk start; gh the decay at the half boundary),
-// gamma = 2^G_L and the K^ factors 2^(G_L - Gh) per half into s.Fk (gamma
+// gamma = 2^G_L and the K^ factors 2^(G_L - Gh) per half into s.Fk() (gamma
 // also to gam_out when it is given), then the decay-referenced operands.
-// Sets *s.Flag when a factor would exceed 2^kSpanMax.  Only waves < NWB.
+// Sets *s.Flag() when a factor would exceed 2^kSpanMax.  Only waves < NWB.
 // ---------------------------------------------------------------------------
-template <bool PRO, int UC, typename E, int D, int C>
-__device__ __forceinline__ void prep_offsets_operands(const PrepIn& a, const PrepRegs<E, D, C>& R, const PrepLds<E>& s,
+template <bool PRO, int UC, typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_offsets_operands(const PrepIn& a, const PrepRegs<E, D, C>& R, const SL& s,
                                                       int L, int t0, int c0, int lpc, int wave, bool second,
                                                       float (&G)[PrepGeom<E, D, C>::TPL][16 / sizeof(E)],
                                                       const float (&excl)[16 / sizeof(E)], float* gam_out,
@@ -641,7 +666,7 @@ __device__ __forceinline__ void prep_offsets_operands(const PrepIn& a, const Pre
         if (w2 < wave) {
 #pragma unroll
             for (int x4 = 0; x4 < VEC / 4; ++x4) {
-                const f32x4 tv = *reinterpret_cast<const f32x4*>(s.Tot + w2 * D + c0 + 4 * x4);
+                const f32x4 tv = *reinterpret_cast<const f32x4*>(s.Tot() + w2 * D + c0 + 4 * x4);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     off[4 * x4 + i] += tv[i];
@@ -670,11 +695,11 @@ __device__ __forceinline__ void prep_offsets_operands(const PrepIn& a, const Pre
 #pragma unroll
         for (int x4 = 0; x4 < VEC / 4; ++x4) {
             const f32x4 v0 = f32x4{f0[4 * x4], f0[4 * x4 + 1], f0[4 * x4 + 2], f0[4 * x4 + 3]};
-            *reinterpret_cast<f32x4*>(s.Fk + c0 + 4 * x4) = v0;
+            *reinterpret_cast<f32x4*>(s.Fk() + c0 + 4 * x4) = v0;
             if (gam_out)
                 *reinterpret_cast<f32x4*>(gam_out + c0 + 4 * x4) = v0;
             if (NH == 2)
-                *reinterpret_cast<f32x4*>(s.Fk + D + c0 + 4 * x4) =
+                *reinterpret_cast<f32x4*>(s.Fk() + D + c0 + 4 * x4) =
                     f32x4{f1[4 * x4], f1[4 * x4 + 1], f1[4 * x4 + 2], f1[4 * x4 + 3]};
         }
     }
@@ -687,17 +712,17 @@ __device__ __forceinline__ void prep_offsets_operands(const PrepIn& a, const Pre
         mx = full_chunk ? prep_operands<true, false, PRO, UC, E, D, C>(R, G, gh, bw, ww, L, t0, c0, s, u_lo, a.pro)
                         : prep_operands<false, false, PRO, UC, E, D, C>(R, G, gh, bw, ww, L, t0, c0, s, u_lo, a.pro);
     if (mx > kSpanMax)
-        *s.Flag = 1;
+        *s.Flag() = 1;
 }
 
 // ---------------------------------------------------------------------------
-// Phase C1 (no steep decay): M tiles into s.M / s.Md (waves 0 .. NWP/2-1, as
+// Phase C1 (no steep decay): M tiles into s.M() / s.Md() (waves 0 .. NWP/2-1, as
 // transposed products so each lane holds four consecutive columns of one
 // row) and the P fragments (the other waves; their accumulators are the
 // fragments) to dP, fragment f at dP + f KB + 16 lane.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C>
-__device__ __forceinline__ void prep_gram(const PrepLds<E>& s, unsigned char* dP, int wave, int lane)
+template <typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_gram(const SL& s, unsigned char* dP, int wave, int lane)
 {
     typedef PrepGeom<E, D, C> S;
     typedef Frags<E, D, C> F;
@@ -714,21 +739,21 @@ __device__ __forceinline__ void prep_gram(const PrepLds<E>& s, unsigned char* dP
                 ++I;
             const int J = tile - I * (I + 1) / 2;
             const bool same = NH == 1 || (I >> 1) == (J >> 1);
-            const E* Bs = same ? s.Eh : s.E2;
+            const E* Bs = same ? s.Eh() : s.E2();
             const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                acc = MM::mma(row_frag<E, D>(s.Kr, 16 * J + cl, 4 * ks + gq), row_frag<E, D>(Bs, rb, 4 * ks + gq), acc);
+                acc = MM::mma(row_frag<E, D>(s.Kr(), 16 * J + cl, 4 * ks + gq), row_frag<E, D>(Bs, rb, 4 * ks + gq), acc);
             // lane: M[16I + cl][16J + 4gq + i]
             if (J < I) {
-                *reinterpret_cast<typename M16::Frag*>(s.M + (16 * I + cl) * LDM + 16 * J + 4 * gq) = M16::pack(acc);
+                *reinterpret_cast<typename M16::Frag*>(s.M() + (16 * I + cl) * LDM + 16 * J + 4 * gq) = M16::pack(acc);
             } else {
                 f32x4 m;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     m[i] = 4 * gq + i < cl ? acc[i] : 0.f;
-                *reinterpret_cast<f32x4*>(s.Md + (16 * I + cl) * LDX + 4 * gq) = m;
+                *reinterpret_cast<f32x4*>(s.Md() + (16 * I + cl) * LDX + 4 * gq) = m;
             }
         }
     } else {
@@ -745,11 +770,11 @@ __device__ __forceinline__ void prep_gram(const PrepLds<E>& s, unsigned char* dP
                 if (J > I)
                     continue;
                 const bool same = NH == 1 || (I >> 1) == (J >> 1);
-                const E* Bs = same ? s.Qh : s.Q2;
+                const E* Bs = same ? s.Qh() : s.Q2();
                 const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    acc[kt] = MM::mma(row_frag<E, D>(s.Kr, 16 * J + cl, 4 * ks + gq),
+                    acc[kt] = MM::mma(row_frag<E, D>(s.Kr(), 16 * J + cl, 4 * ks + gq),
                                       row_frag<E, D>(Bs, rb, 4 * ks + gq), acc[kt]);
                 if (J == I) {
 #pragma unroll
@@ -769,8 +794,8 @@ __device__ __forceinline__ void prep_gram(const PrepLds<E>& s, unsigned char* dP
 // s.G (phase A has read them all).  Every thread calls it; it ends with a
 // barrier after the last read of s.G.
 // ---------------------------------------------------------------------------
-template <bool PRO, typename E, int D, int C>
-__device__ __forceinline__ void prep_exact(const PrepIn& a, const ChunkPos& cp, const PrepLds<E>& s, unsigned char* dP,
+template <bool PRO, typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_exact(const PrepIn& a, const ChunkPos& cp, const SL& s, unsigned char* dP,
                                            bool ab, int t0, int c0, int bw,
                                            const float (&G)[PrepGeom<E, D, C>::TPL][16 / sizeof(E)])
 {
@@ -791,7 +816,7 @@ __device__ __forceinline__ void prep_exact(const PrepIn& a, const ChunkPos& cp, 
     const E* k = (const E*)a.k;
     const E* b = (const E*)a.b;
     // prologue: per-token 1/|k|, 1/|q| from phase B, sigmoid on b
-    const float* sRn = s.Rn;
+    const float* sRn = s.Rn();
     const bool pn = PRO && (a.pro & GDR2_PROLOGUE_NORM_QK), pg = PRO && (a.pro & GDR2_PROLOGUE_GATES);
     const float* sG = s.G;
     // M, every pair s < t
@@ -812,9 +837,9 @@ __device__ __forceinline__ void prep_exact(const PrepIn& a, const ChunkPos& cp, 
                 m *= sRn[t] * sRn[u];
         }
         if ((t >> 4) == (u >> 4))
-            s.Md[t * LDX + (u & 15)] = m;
+            s.Md()[t * LDX + (u & 15)] = m;
         else
-            s.M[t * LDM + u] = from_f32<E>(m);
+            s.M()[t * LDM + u] = from_f32<E>(m);
     }
     // P, straight into its fragments (zeros above the diagonal)
     E* gP = reinterpret_cast<E*>(dP);
@@ -844,20 +869,20 @@ __device__ __forceinline__ void prep_exact(const PrepIn& a, const ChunkPos& cp, 
         if (t < cp.L)
             kh = to_f32(k[(cp.row0 + (int64_t)t * a.H) * D + i]) * fast_exp2(sG[(C - 1) * D + i] - sG[t * D + i]) *
                  (pn ? sRn[t] : 1.f);
-        s.Kr[swz<E, D>(t, i)] = from_f32<E>(kh);
+        s.Kr()[swz<E, D>(t, i)] = from_f32<E>(kh);
     }
     __syncthreads();   // every read of G is done
 }
 
 // ---------------------------------------------------------------------------
-// Phase C2, wave 0: X = (I + M)^-1 into s.X (fragment k order).  The 16x16
+// Phase C2, wave 0: X = (I + M)^-1 into s.X() (fragment k order).  The 16x16
 // diagonal blocks by lane-per-column substitution (fp32), then
 // X_IJ = -X_II sum_K M_IK X_KJ block by block on MFMA with the earlier blocks
-// kept as accumulators.  Entries of s.X above the diagonal are not written
+// kept as accumulators.  Entries of s.X() above the diagonal are not written
 // (the caller keeps them zero).
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C>
-__device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
+template <typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_inverse(const SL& s, int lane)
 {
     typedef PrepGeom<E, D, C> S;
     typedef Mma16<E> M16;
@@ -865,7 +890,7 @@ __device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
     const int gq = lane >> 4, cl = lane & 15;
     if (gq < NB) {
         // column cl of X_gq,gq by forward substitution
-        const float* m = s.Md + gq * 16 * LDX;
+        const float* m = s.Md() + gq * 16 * LDX;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -879,7 +904,7 @@ __device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
                 acc0 -= m[r * LDX + r - 1] * x[r - 1];
             x[r] = acc0 + acc1;
         }
-        float* xc = s.Xc + (gq * 16 + cl) * LDX;
+        float* xc = s.Xc() + (gq * 16 + cl) * LDX;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             *reinterpret_cast<f32x4*>(xc + 4 * r4) = f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
@@ -890,12 +915,12 @@ __device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
         // accumulator tile X_II[4gq + i][cl]
-        Xt[I][I] = *reinterpret_cast<const f32x4*>(s.Xc + (16 * I + cl) * LDX + 4 * gq);
+        Xt[I][I] = *reinterpret_cast<const f32x4*>(s.Xc() + (16 * I + cl) * LDX + 4 * gq);
         // A operand -X_II[cl][4gq + i]
         f32x4 t;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            t[i] = -s.Xc[(16 * I + 4 * gq + i) * LDX + cl];
+            t[i] = -s.Xc()[(16 * I + 4 * gq + i) * LDX + cl];
         nx[I] = M16::pack(t);
     }
 #pragma unroll
@@ -906,7 +931,7 @@ __device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int K = J; K < I; ++K)
-                y = M16::mma(M16::load(s.M + (16 * I + cl) * LDM + 16 * K + 4 * gq), M16::pack(Xt[K][J]), y);
+                y = M16::mma(M16::load(s.M() + (16 * I + cl) * LDM + 16 * K + 4 * gq), M16::pack(Xt[K][J]), y);
             Xt[I][J] = M16::mma(nx[I], M16::pack(y), f32x4{0.f, 0.f, 0.f, 0.f});
         }
     }
@@ -917,7 +942,7 @@ __device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
         for (int J = 0; J <= I; ++J)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                s.X[(16 * I + 4 * gq + i) * LDXP + kpos<E>(16 * J + cl)] = from_f32<E>(Xt[I][J][i]);
+                s.X()[(16 * I + 4 * gq + i) * LDXP + kpos<E>(16 * J + cl)] = from_f32<E>(Xt[I][J][i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -926,8 +951,8 @@ __device__ __forceinline__ void prep_inverse(const PrepLds<E>& s, int lane)
 // exact path, whose Kr rows hold K^ already); the accumulators are the
 // fragment.  Returns it as 16 bytes per lane.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C>
-__device__ __forceinline__ u32x4 prep_kt_frag(const PrepLds<E>& s, int c, int m, bool guard,
+template <typename E, int D, int C, typename SL>
+__device__ __forceinline__ u32x4 prep_kt_frag(const SL& s, int c, int m, bool guard,
                                               const typename Mma16<E>::Frag& ident, int lane)
 {
     typedef PrepGeom<E, D, C> S;
@@ -939,16 +964,16 @@ __device__ __forceinline__ u32x4 prep_kt_frag(const PrepLds<E>& s, int c, int m,
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         const int tb = KT * m + kt;
-        acc[kt] = M16::mma(row4<E, D>(s.Kr, 16 * tb + cl, 16 * c + 4 * gq), ident, f32x4{0.f, 0.f, 0.f, 0.f});
-        const float f = guard ? 1.f : s.Fk[(NH == 2 ? (tb >> 1) : 0) * D + 16 * c + cl];
+        acc[kt] = M16::mma(row4<E, D>(s.Kr(), 16 * tb + cl, 16 * c + 4 * gq), ident, f32x4{0.f, 0.f, 0.f, 0.f});
+        const float f = guard ? 1.f : s.Fk()[(NH == 2 ? (tb >> 1) : 0) * D + 16 * c + cl];
         acc[kt] = acc[kt] * f;
     }
     return __builtin_bit_cast(u32x4, frag_of<E>(acc));
 }
 
-// The X fragments of phase D: row block T, token step m (m*KT <= T), from s.X.
-template <typename E, int D, int C>
-__device__ __forceinline__ void prep_x_frags(const PrepLds<E>& s, typename Mma<E>::Frag* xf, int lane)
+// The X fragments of phase D: row block T, token step m (m*KT <= T), from s.X().
+template <typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_x_frags(const SL& s, typename Mma<E>::Frag* xf, int lane)
 {
     typedef PrepGeom<E, D, C> S;
     typedef Frags<E, D, C> F;
@@ -959,7 +984,7 @@ __device__ __forceinline__ void prep_x_frags(const PrepLds<E>& s, typename Mma<E
 #pragma unroll
         for (int m = 0; m <= T / KT; ++m)
             xf[F::p_offset(T) + m] =
-                *reinterpret_cast<const typename Mma<E>::Frag*>(s.X + (16 * T + cl) * LDXP + KB * m + VEC * gq);
+                *reinterpret_cast<const typename Mma<E>::Frag*>(s.X() + (16 * T + cl) * LDXP + KB * m + VEC * gq);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,8 +992,8 @@ __device__ __forceinline__ void prep_x_frags(const PrepLds<E>& s, typename Mma<E
 // fragments (T, m2) of every token block T in registers; each goes to
 // dW + (T NKS + m2) KB + 16 lane.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C>
-__device__ __forceinline__ void prep_w(const PrepLds<E>& s, const typename Mma<E>::Frag* xf, int m2,
+template <typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_w(const SL& s, const typename Mma<E>::Frag* xf, int m2,
                                        unsigned char* dW, const typename Mma16<E>::Frag& ident, int lane)
 {
     typedef PrepGeom<E, D, C> S;
@@ -989,7 +1014,7 @@ __device__ __forceinline__ void prep_w(const PrepLds<E>& s, const typename Mma<E
             for (int k2 = 0; k2 < KT; ++k2) {
                 const int tb = KT * m + k2;
                 const bool sec = NH == 2 && tb >= 2;
-                tt[k2] = M16::mma(row4<E, D>(sec ? s.E2 : s.Eh, sec ? 16 * tb - 32 + cl : 16 * tb + cl, 16 * cb + 4 * gq),
+                tt[k2] = M16::mma(row4<E, D>(sec ? s.E2() : s.Eh(), sec ? 16 * tb - 32 + cl : 16 * tb + cl, 16 * cb + 4 * gq),
                                   ident, f32x4{0.f, 0.f, 0.f, 0.f});
             }
             ea[kt][m] = frag_of<E>(tt);
@@ -1011,11 +1036,11 @@ __device__ __forceinline__ void prep_w(const PrepLds<E>& s, const typename Mma<E
 }
 
 // ---------------------------------------------------------------------------
-// Phase D, U~ = X u for value tile n of the UC columns in s.U: the
+// Phase D, U~ = X u for value tile n of the UC columns in s.U(): the
 // accumulator tiles of every token block T into ut[T].
 // ---------------------------------------------------------------------------
-template <int UC, typename E, int D, int C>
-__device__ __forceinline__ void prep_u_tile(const PrepLds<E>& s, const typename Mma<E>::Frag* xf, int n, f32x4* ut,
+template <int UC, typename E, int D, int C, typename SL>
+__device__ __forceinline__ void prep_u_tile(const SL& s, const typename Mma<E>::Frag* xf, int n, f32x4* ut,
                                             const typename Mma16<E>::Frag& ident, int lane)
 {
     typedef PrepGeom<E, D, C> S;
@@ -1030,7 +1055,7 @@ __device__ __forceinline__ void prep_u_tile(const PrepLds<E>& s, const typename 
         f32x4 tt[KT];
 #pragma unroll
         for (int k2 = 0; k2 < KT; ++k2)
-            tt[k2] = M16::mma(row4<E, UC>(s.U, 16 * (KT * m + k2) + cl, 16 * n + 4 * gq), ident,
+            tt[k2] = M16::mma(row4<E, UC>(s.U(), 16 * (KT * m + k2) + cl, 16 * n + 4 * gq), ident,
                               f32x4{0.f, 0.f, 0.f, 0.f});
         ub[m] = frag_of<E>(tt);
     }

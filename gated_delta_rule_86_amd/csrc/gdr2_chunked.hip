@@ -89,9 +89,11 @@ struct StateArgs {
     const float* gam;
     const float* S0;
     float* S_out;
-    float* S_chunks;          // optional: the state at the start of every chunk
+    float* S_chunks;          // optional: the state at the start of every ck_every-th chunk
     void* o;
     int64_t T, H, NC, nbh;
+    int ck_every;             // chunks per requested chunk (> 1: evaluated in smaller chunks)
+    int64_t NCK;              // entries of S_chunks per (b, h): ceil(NC / ck_every)
     int64_t nseg, seg_len;    // chunk segments of the two-level scan (1, NC: one pass)
     float* span;              // segment area (nseg > 1)
 };
@@ -201,21 +203,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ __align__(16) float sG[C * D];
     __shared__ __align__(16) unsigned int sBW[2 * C];   // width-1 b and w of the chunk
-    PrepLds<E> s;
-    s.Eh = reinterpret_cast<E*>(smem + S::OFF_EH);
-    s.Qh = reinterpret_cast<E*>(smem + S::OFF_QH);
-    s.Kr = reinterpret_cast<E*>(smem + S::OFF_KR);
-    s.U = reinterpret_cast<E*>(smem + S::OFF_U);
-    s.E2 = reinterpret_cast<E*>(smem + S::OFF_E2);
-    s.Q2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
-    s.M = reinterpret_cast<E*>(smem + S::OFF_M);
-    s.X = reinterpret_cast<E*>(smem + S::OFF_X);
-    s.Md = reinterpret_cast<float*>(smem + S::OFF_MD);
-    s.Xc = reinterpret_cast<float*>(smem + S::OFF_XC);
-    s.Tot = reinterpret_cast<float*>(smem + S::OFF_TOT);
-    s.Fk = reinterpret_cast<float*>(smem + S::OFF_FK);
-    s.Rn = reinterpret_cast<float*>(smem + S::OFF_RN);
-    s.Flag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
+    PrepLds<E, S> s;
     s.G = sG;
     s.BW = sBW;
 
@@ -226,7 +214,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
 
     // X: the blocks above the diagonal that fragments cover stay zero
     for (int e = threadIdx.x; e < C * LDXP; e += NTP)
-        s.X[e] = from_f32<E>(0.f);
+        s.X()[e] = from_f32<E>(0.f);
 
     // Token inputs: two register sets, Rn receives chunk n+1 while chunk n
     // computes from R, so every token load is issued a whole chunk ahead of
@@ -283,7 +271,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         if (ab)
             prep_cumsum<WG, PRO, E, D, C>(a, s, cp.L, t0, c0, lpc, wave, G, excl);
         if (tid == 0)
-            *s.Flag = 0;
+            *s.Flag() = 0;
         lds_barrier();   // B1: wave totals; the previous chunk is done with LDS
         if (pre)
             prep_load<2, WB, WW>(a, np, Rn, t0, c0);
@@ -302,7 +290,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         unsigned char* gP = (unsigned char*)a.P + rec * F::P_BYTES;
         if (pre)
             prep_load<4, WB, WW>(a, np, Rn, t0, c0);
-        const bool guard = *s.Flag != 0;
+        const bool guard = *s.Flag() != 0;
         if (!guard) {
             if (next < a.nrec)
                 prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
@@ -332,7 +320,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
                     // Q~ fragment (token block T, channel step m)
                     const int fq = task - NK, T = fq / NKS, m = fq % NKS;
                     const bool sec = NH == 2 && T >= 2;
-                    const E* src = sec ? s.Q2 : s.Qh;
+                    const E* src = sec ? s.Q2() : s.Qh();
                     const int r = sec ? 16 * T - 32 + cl : 16 * T + cl;
                     u32x4 v;
                     if constexpr (sizeof(E) == 2) {
@@ -443,13 +431,15 @@ __device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, 
                                              int slice, int64_t n, int lane, int wave);
 
 // The state at the start of chunk n (this lane's column, its 4 rows per
-// tile) into the checkpoint output.
+// tile) into the checkpoint output, when n starts a requested chunk.
 template <int D>
 __device__ __forceinline__ void state_emit(const StateArgs& a, const f32x4* St, int64_t bh, int64_t n,
                                            int gq, int col)
 {
     constexpr int KTS = D / 16;
-    float* dst = a.S_chunks + (bh * a.NC + n) * D * D;
+    if (n % a.ck_every)
+        return;
+    float* dst = a.S_chunks + (bh * a.NCK + n / a.ck_every) * D * D;
 #pragma unroll
     for (int kt = 0; kt < KTS; ++kt)
 #pragma unroll
@@ -1043,10 +1033,19 @@ struct SegPlan {
     int64_t nseg, len;
 };
 
+// The chunk size the staged kernels evaluate in.  fp32 chunks of 64 tokens
+// at d = 128 do not fit the prep kernel's LDS; since the chunked form is
+// exact for every chunk size, they are evaluated as chunks of 32 (the
+// requested chunk only fixes where S_chunks samples the state).
+int eval_chunk(const gdr2_fwd_args& a)
+{
+    return (a.dtype == GDR2_F32 && a.Dk * a.chunk > 4096) ? 32 : a.chunk;
+}
+
 SegPlan seg_plan(const gdr2_fwd_args& a)
 {
     SegPlan p;
-    segment_plan(a.algo, ceil_div(a.T, a.chunk), a.B * a.H * (a.Dk / 64), &p.nseg, &p.len);
+    segment_plan(a.algo, ceil_div(a.T, eval_chunk(a)), a.B * a.H * (a.Dk / 64), &p.nseg, &p.len);
     return p;
 }
 
@@ -1100,6 +1099,8 @@ hipError_t launch_staged_t(const gdr2_fwd_args& a, hipStream_t stream)
     sa.Wn = pa.Wn; sa.Ut = pa.Ut; sa.Kh = pa.Kh; sa.Qt = pa.Qt; sa.P = pa.P; sa.gam = pa.gam;
     sa.S0 = a.S0; sa.S_out = a.S_out; sa.S_chunks = a.S_chunks; sa.o = a.o;
     sa.T = a.T; sa.H = a.H; sa.NC = pa.NC; sa.nbh = a.B * a.H;
+    sa.ck_every = a.chunk / C;
+    sa.NCK = ceil_div(a.T, a.chunk);
     sa.nseg = sp.nseg; sa.seg_len = sp.len;
     sa.span = sp.nseg > 1 ? reinterpret_cast<float*>(ws + L.span) : nullptr;
     if (sp.nseg > 1) {
@@ -1170,7 +1171,7 @@ size_t staged_workspace_bytes(const gdr2_fwd_args& a)
 {
     if (a.B * a.H * a.T == 0 || forward_algo(a) == GDR2_ALGO_FUSED)
         return 0;
-    return staged_layout(a.B, a.H, a.T, (int)a.Dk, a.chunk, a.dtype == GDR2_BF16 ? 2 : 4, seg_plan(a).nseg).total;
+    return staged_layout(a.B, a.H, a.T, (int)a.Dk, eval_chunk(a), a.dtype == GDR2_BF16 ? 2 : 4, seg_plan(a).nseg).total;
 }
 
 hipError_t launch_forward_staged(const gdr2_fwd_args& a, hipStream_t stream)
@@ -1181,7 +1182,7 @@ hipError_t launch_forward_staged(const gdr2_fwd_args& a, hipStream_t stream)
             return C == 64 ? launch_staged_t<bf16, 128, 64>(a, stream) : launch_staged_t<bf16, 128, 32>(a, stream);
         return C == 64 ? launch_staged_t<bf16, 64, 64>(a, stream) : launch_staged_t<bf16, 64, 32>(a, stream);
     }
-    if (D == 128)
+    if (D == 128)   // chunk 64 is evaluated as chunks of 32 (eval_chunk)
         return launch_staged_t<float, 128, 32>(a, stream);
     return C == 64 ? launch_staged_t<float, 64, 64>(a, stream) : launch_staged_t<float, 64, 32>(a, stream);
 }

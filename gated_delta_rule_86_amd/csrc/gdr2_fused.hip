@@ -51,6 +51,7 @@ struct FusedShape : PrepGeom<E, D, C> {
     static constexpr size_t OFF_E2 = OFF_U + SZ_U;                       // E~ second half
     static constexpr size_t OFF_Q2 = OFF_E2 + G::SZ_HALF;                // Q~ second half
     static constexpr size_t OFF_M = al256(OFF_Q2 + G::SZ_HALF);          // wave totals (A -> B), then M
+    static constexpr size_t OFF_TOT = OFF_M;
     static constexpr size_t OFF_MD = al256(OFF_M + SZ_MT);               // M_II fp32
     static constexpr size_t OFF_XC = OFF_MD + G::SZ_MD;                  // X_II fp32
     static constexpr size_t OFF_X = al256(OFF_XC + G::SZ_MD);            // X [C][LDXP]
@@ -82,7 +83,7 @@ __device__ __forceinline__ ChunkPos fused_pos(const FusedArgs& a, int64_t b, int
 // negated), O = Q~ S + P Delta, S <- diag(gamma) S + K^T Delta; O leaves
 // through the wave's staging rows with 16-byte stores.
 template <typename E, int D, int C>
-__device__ __forceinline__ void fused_state_step(const FusedArgs& a, const PrepLds<E>& s, const unsigned char* sW,
+__device__ __forceinline__ void fused_state_step(const FusedArgs& a, const PrepLds<E, FusedShape<E, D, C>>& s, const unsigned char* sW,
                                                  const unsigned char* sKT, const unsigned char* sP, E* sOw,
                                                  f32x4* St, const f32x4* ut, const ChunkPos& cp, int col0, int lane)
 {
@@ -100,7 +101,7 @@ __device__ __forceinline__ void fused_state_step(const FusedArgs& a, const PrepL
     // the operand rows in the accumulator k order
     auto qfrag = [&](int mt, int ks) -> Frag {
         const bool sec = NH == 2 && mt >= 2;
-        const E* src = sec ? s.Q2 : s.Qh;
+        const E* src = sec ? s.Q2() : s.Qh();
         const int r = sec ? 16 * mt - 32 + cl : 16 * mt + cl;
         if constexpr (sizeof(E) == 2) {
             const typename Mma16<E>::Frag lo = row4<E, D>(src, r, KB * ks + 4 * gq);
@@ -177,7 +178,7 @@ __device__ __forceinline__ void fused_state_step(const FusedArgs& a, const PrepL
                 ak[kt][kc] = frag(sKT, kt * NKC + kc);
 #pragma unroll
         for (int kt = 0; kt < KTS; ++kt)
-            St[kt] = St[kt] * *reinterpret_cast<const f32x4*>(s.Fk + 16 * kt + 4 * gq);
+            St[kt] = St[kt] * *reinterpret_cast<const f32x4*>(s.Fk() + 16 * kt + 4 * gq);
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
@@ -219,21 +220,7 @@ __global__ __launch_bounds__(NTP) void chunk_fused_kernel(FusedArgs a)
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ __align__(16) float sG[C * D];
     __shared__ __align__(16) unsigned int sBW[2 * C];   // width-1 b and w of the chunk
-    PrepLds<E> s;
-    s.Eh = reinterpret_cast<E*>(smem + S::OFF_EH);
-    s.Qh = reinterpret_cast<E*>(smem + S::OFF_QH);
-    s.Kr = reinterpret_cast<E*>(smem + S::OFF_KR);
-    s.U = reinterpret_cast<E*>(smem + S::OFF_U);
-    s.E2 = reinterpret_cast<E*>(smem + S::OFF_E2);
-    s.Q2 = reinterpret_cast<E*>(smem + S::OFF_Q2);
-    s.M = reinterpret_cast<E*>(smem + S::OFF_M);
-    s.X = reinterpret_cast<E*>(smem + S::OFF_X);
-    s.Md = reinterpret_cast<float*>(smem + S::OFF_MD);
-    s.Xc = reinterpret_cast<float*>(smem + S::OFF_XC);
-    s.Tot = reinterpret_cast<float*>(smem + S::OFF_M);
-    s.Fk = reinterpret_cast<float*>(smem + S::OFF_FK);
-    s.Rn = reinterpret_cast<float*>(smem + S::OFF_RN);
-    s.Flag = reinterpret_cast<int*>(smem + S::OFF_FLAG);
+    PrepLds<E, S> s;
     s.G = sG;
     s.BW = sBW;
     unsigned char* sW = smem + S::OFF_KR;      // -W fragments over the Kr rows (after C2)
@@ -262,7 +249,7 @@ __global__ __launch_bounds__(NTP) void chunk_fused_kernel(FusedArgs a)
 
     // X: the blocks above the diagonal that fragments cover stay zero
     for (int e = threadIdx.x; e < C * LDXP; e += NTP)
-        s.X[e] = from_f32<E>(0.f);
+        s.X()[e] = from_f32<E>(0.f);
 
     // the start state, this lane's column, 4 rows per accumulator tile
     f32x4 St[KTS];
@@ -320,7 +307,7 @@ __global__ __launch_bounds__(NTP) void chunk_fused_kernel(FusedArgs a)
         if (ab)
             prep_cumsum<WG, PRO, E, D, C>(a, s, cp.L, t0, c0, lpc, wave, G, excl);
         if (tid == 0)
-            *s.Flag = 0;
+            *s.Flag() = 0;
         lds_barrier();   // B1: wave totals
 
         // ---- B: decay-referenced operands; the next chunk's tokens ---------
@@ -338,7 +325,7 @@ __global__ __launch_bounds__(NTP) void chunk_fused_kernel(FusedArgs a)
         lds_barrier();   // B2: operands in LDS
         if (more)        // phase B has read this chunk's width-1 gates
             prep_copy_bw<WB, WW, E, D, C>(a, np, sBW, wave, lane);
-        const bool guard = *s.Flag != 0;
+        const bool guard = *s.Flag() != 0;
         if (!guard) {
             if (more)
                 prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
@@ -362,22 +349,25 @@ __global__ __launch_bounds__(NTP) void chunk_fused_kernel(FusedArgs a)
         }
         lds_barrier();   // B4: X and K^T in LDS; the Kr rows are free
 
-        // ---- D: -W fragments (waves 0-3) into LDS, U~ tiles (waves 4-7) ---
-        f32x4 ut[NB];
-        {
+        // ---- D: -W fragments (waves 0-3) into LDS ------------------------
+        if (wave < NWP / 2) {
             typename MM::Frag xf[NP];
             prep_x_frags<E, D, C>(s, xf, lane);
-            if (wave < NWP / 2) {
-                for (int m2 = wave; m2 < NKS; m2 += NWP / 2)
-                    prep_w<E, D, C>(s, xf, m2, sW, ident, lane);
-            } else if (sw) {
-                prep_u_tile<BV, E, D, C>(s, xf, tile, ut, ident, lane);
-            }
+            for (int m2 = wave; m2 < NKS; m2 += NWP / 2)
+                prep_w<E, D, C>(s, xf, m2, sW, ident, lane);
         }
         lds_barrier();   // B5: -W in LDS
 
-        // ---- the state recurrence over this chunk (waves 4-7) -------------
+        // ---- the state recurrence over this chunk (waves 4-7): U~ = X u for
+        // the wave's 16 columns (X stays in LDS until the next chunk's C2),
+        // then the state step
         if (sw) {
+            f32x4 ut[NB];
+            {
+                typename MM::Frag xf[NP];
+                prep_x_frags<E, D, C>(s, xf, lane);
+                prep_u_tile<BV, E, D, C>(s, xf, tile, ut, ident, lane);
+            }
             if (a.S_chunks) {
                 float* dst = a.S_chunks + (bh * a.NC + n) * D * D;
 #pragma unroll

@@ -3,6 +3,7 @@ under profiles/.
 
     python -m gated_delta_rule_86_amd.rocprof_summary stats  <kernel_stats.csv> <out.md> --command "..."
     python -m gated_delta_rule_86_amd.rocprof_summary traffic <fetch_dir> <write_dir> <out.md> --command "..."
+    python -m gated_delta_rule_86_amd.rocprof_summary counters <pmc_dir> <out.md> --command "..."
 
 `stats` summarises a --kernel-trace --stats run (calls, average and total
 duration per kernel).  `traffic` takes two --pmc runs (FETCH_SIZE, then
@@ -10,7 +11,9 @@ WRITE_SIZE; KiB per dispatch) of ``bench.py --calibrate-copy``, scales each
 counter by what it reads for the plain device copy of known size the
 benchmark runs, and reports HBM bytes per launch for each kernel.  The
 summary records a hash of the kernel sources it was measured on; bench.py
-reports the traffic only while the sources still hash the same.
+reports the traffic only while the sources still hash the same.  `counters`
+tabulates the per-kernel medians of any other --pmc run (MFMA and VALU
+utilisation, LDS bank conflicts).
 """
 from __future__ import annotations
 
@@ -25,7 +28,8 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 # Kernel-name fragments -> short names used in the summaries and bench.py.
-KERNELS = (("chunk_prep_kernel", "gdr2_chunk_prep"), ("chunk_state_kernel", "gdr2_chunk_state"),
+KERNELS = (("chunk_prep_kernel", "gdr2_chunk_prep"), ("chunk_fused_kernel", "gdr2_chunk_fused"),
+           ("chunk_state_kernel", "gdr2_chunk_state"), ("bwd_gate_sum_kernel", "gdr2_bwd_gate_sum"),
            ("chunk_span_kernel", "gdr2_chunk_span"), ("span_fold_kernel", "gdr2_span_fold"),
            ("decode_step_kernel", "gdr2_decode_step"), ("bwd_prep_kernel", "gdr2_bwd_prep"),
            ("bwd_dout_kernel", "gdr2_bwd_dout"), ("bwd_frag_kernel", "gdr2_bwd_frag"),
@@ -45,20 +49,29 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-_PREP_VARIANT = re.compile(r"chunk_prep_kernel(?:ILi(\d+)ELi(\d+)ELi(\d+)ELb(\d)|<(\d+), (\d+), (\d+), (true|false))")
+_PREP_VARIANT = re.compile(r"chunk_(?:prep|fused)_kernel(?:ILi(\d+)ELi(\d+)ELi(\d+)ELb(\d)|<(\d+), (\d+), (\d+), (true|false))")
+_SHAPE = re.compile(r"chunk_(?:prep|fused)_kernel(?:I.*?E(DF16b|f)Li(\d+)ELi(\d+)E|<[^>]*?, (__bf16|float), (\d+), (\d+)>)")
 
 
 def short_name(kernel: str) -> str | None:
     for frag, name in KERNELS:
         if frag in kernel:
-            if name == "gdr2_chunk_prep":
-                # one prep kernel per gate-width mix (0 = widths read at run time)
+            if name in ("gdr2_chunk_prep", "gdr2_chunk_fused"):
+                # one kernel per gate-width mix (0 = widths read at run time)
                 m = _PREP_VARIANT.search(kernel)
                 if m:
                     g = m.groups()
                     wb, ww, wg, pro = g[0:4] if g[0] is not None else g[4:8]
                     tag = ",".join("x" if x == "0" else ("1" if x == "1" else "d") for x in (wb, ww, wg))
                     name += f"[b,w,g={tag}" + (",prologue]" if pro in ("1", "true") else "]")
+                # other shapes than bf16, d = 128, chunk 64 are named
+                m = _SHAPE.search(kernel)
+                if m:
+                    g = m.groups()
+                    dt, d, c = g[0:3] if g[0] is not None else g[3:6]
+                    dt = "bf16" if dt in ("DF16b", "__bf16") else "f32"
+                    if (dt, d, c) != ("bf16", "128", "64"):
+                        name += f"[{dt},d{d},c{c}]"
             return name
     return None
 
@@ -130,6 +143,32 @@ def traffic(args):
     print("\n".join(out))
 
 
+def counters(args):
+    """Per-kernel medians of every counter (or derived metric) of one --pmc
+    run, one row per kernel."""
+    f = _find(args.pmc_dir, "*counter_collection.csv")
+    vals = {}
+    names = []
+    for r in csv.DictReader(open(f)):
+        kn = short_name(r["Kernel_Name"])
+        if not kn:
+            continue
+        c = r["Counter_Name"]
+        if c not in names:
+            names.append(c)
+        vals.setdefault(kn, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    out = [f"# rocprofv3 counters per launch: {args.title}", "",
+           "Command (from the repository root on the GPU box):", "", f"    {args.command}", "",
+           f"Kernel sources hash: `{source_hash()}`", "", args.note, "",
+           "| kernel | launches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for kn in sorted(vals):
+        row = [f"{statistics.median(vals[kn][c]):.4g}" if c in vals[kn] else "" for c in names]
+        n = max(len(v) for v in vals[kn].values())
+        out.append(f"| {kn} | {n} | " + " | ".join(row) + " |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def read_traffic(path: str) -> dict | None:
     """Bytes per launch by kernel from a traffic summary, if it was measured on
     the current sources; else None."""
@@ -158,8 +197,14 @@ def main():
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--title", default="benchmark")
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dir")
+    c.add_argument("out")
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", default="benchmark")
+    c.add_argument("--note", default="")
     a = ap.parse_args()
-    stats(a) if a.cmd == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "counters": counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

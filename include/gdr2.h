@@ -70,7 +70,10 @@ typedef enum gdr2_status {
     GDR2_ERR_INVALID_ARG = 1,  /* null / misaligned / overlapping pointer, bad size */
     GDR2_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set below */
     GDR2_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
-    GDR2_ERR_HIP = 4           /* the HIP runtime reported an error */
+    GDR2_ERR_HIP = 4,          /* the HIP runtime reported an error */
+    GDR2_STATUS_RANGE_ = 0x7fffffff  /* not a status: makes every 32-bit value a
+                                        valid gdr2_status, so an unknown code
+                                        passed to gdr2_status_string is defined */
 } gdr2_status;
 
 /* Element type of q, k, v, b, w and o.  g, S0, S_out and state are fp32. */
@@ -163,10 +166,13 @@ typedef enum gdr2_stage {
  *                               쓸까?".  Written by the STATE stage; must
  *                               not overlap anything else.
  *   o must not overlap any input.
- * Supported set: Dk == Dv in {64, 128}; chunk in {32, 64}; dtype F32 or BF16,
- * with Dk * chunk <= 4096 for F32; B, T, H >= 0 (T need not be a multiple of
- * chunk; T == 0 writes S0, or zeros, to S_out).  Anything else returns
- * GDR2_ERR_UNSUPPORTED.
+ * Supported set: Dk == Dv in {64, 128}; chunk in {32, 64}; dtype F32 or BF16;
+ * B, T, H >= 0 (T need not be a multiple of chunk; T == 0 writes S0, or
+ * zeros, to S_out).  Anything else returns GDR2_ERR_UNSUPPORTED.  The chunked
+ * form is exact for every chunk size, so the chunk changes results only by
+ * rounding; F32 with Dk = 128 and chunk 64 is evaluated in chunks of 32 (a
+ * 64 x 128 fp32 chunk does not fit the intra-chunk kernel's LDS), with
+ * S_chunks still sampled every 64 tokens.
  */
 typedef struct gdr2_fwd_args {
     int64_t B, T, H, Dk, Dv;

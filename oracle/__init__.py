@@ -49,15 +49,22 @@ def build(src: str = _SRC, out: str = _LIB) -> str:
 
 
 def load(path: str | None = None):
-    """Load (building first if absent) the oracle library; returns the CDLL."""
+    """Load (building first if absent) the oracle library; returns the CDLL.
+    GDR2_ORACLE_LIB, when set, names another build of the same source to
+    load instead (the sanitizer test runs the pins against an ASan/UBSan
+    build this way)."""
     global _lib
     if path is not None:
         return _bind(ctypes.CDLL(path))
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
-                build()
-            _lib = _bind(ctypes.CDLL(_LIB))
+            alt = os.environ.get("GDR2_ORACLE_LIB")
+            if alt:
+                _lib = _bind(ctypes.CDLL(alt))
+            else:
+                if not os.path.exists(_LIB):
+                    build()
+                _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
 
 

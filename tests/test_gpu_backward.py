@@ -31,11 +31,9 @@ def _narrow(inp, widths):
     return out
 
 
-def _gpu_backward(d, fwd_chunk=64, fwd_algo="auto", bwd_algo="auto"):
+def _gpu_backward(d, fwd_algo="auto", bwd_algo="auto"):
     args = [d[n] for n in NAMES]
-    _, _, ck = gdr2.forward(*args, S0=d["S0"], chunk=fwd_chunk, chunk_states=True, algo=fwd_algo)
-    if fwd_chunk != 64:                     # chunk-64 starts are every other chunk-32 start
-        ck = ck[:, :, ::64 // fwd_chunk].contiguous()
+    _, _, ck = gdr2.forward(*args, S0=d["S0"], chunk=64, chunk_states=True, algo=fwd_algo)
     return gdr2.backward(*args, S_chunks=ck, dO=d["dO"], dS_final=d["dS_final"], algo=bwd_algo)
 
 
@@ -82,7 +80,7 @@ def test_backward_matches_oracle(name, B, T, H, D, dtype, gates, s0, ds, widths)
     if widths:
         inp = _narrow(inp, widths)
     d = to_dev(inp)
-    got = _gpu_backward(d, fwd_chunk=32 if (dtype == "f32" and D == 128) else 64)
+    got = _gpu_backward(d)
     torch.cuda.synchronize()
     _compare(name, got, _oracle_backward(inp), TOL[dtype])
 
@@ -147,7 +145,7 @@ def test_backward_two_level_scan(name, B, T, H, D, dtype, gs, ds, algo):
     wl = Workload(name, "forward", B, T, H, D, dtype, "full", 0.05, 64, 612, g_scale=gs)
     inp = draw(wl)
     inp.update(draw_cotangents(wl, ds))
-    got = _gpu_backward(to_dev(inp), fwd_chunk=32 if (dtype == "f32" and D == 128) else 64, bwd_algo=algo)
+    got = _gpu_backward(to_dev(inp), bwd_algo=algo)
     torch.cuda.synchronize()
     _compare(name, got, _oracle_backward(inp), TOL[dtype])
 
