@@ -283,62 +283,75 @@ template <typename T>
 __device__ __forceinline__ typename Raw4<T>::V ld_raw4(const T* p) { return *reinterpret_cast<const typename Raw4<T>::V*>(p); }
 __device__ __forceinline__ f32x4 bcast4(float x) { return f32x4{x, x, x, x}; }
 
-// bwd_prep step 1 for one gate-width mix (B1, W1, G1: b, w, g of width 1):
-// the chunk's raw rows into LDS (G, k, q, e = b*k) and U = w*v to the
-// workspace, 4 channels per item.  Every item's loads are issued before
-// any is used; rows past the valid length re-read the last valid row and
-// are zeroed at use.  e and u of every item stay in keepE, keepU for step 3.
-// Returns whether a valid log-decay is positive.
+// bwd_prep step 1 for one gate-width mix (B1, W1, G1: b, w, g of width 1),
+// in two parts so that a record's loads can be in flight while the
+// previous record is processed.  prep_rows_load issues every load of this
+// thread's items (token t, 4 channels) into `raw`; rows past the valid
+// length re-read the last valid row.  prep_rows_use then writes the chunk's
+// raw rows to LDS (G, k, q, e = b*k) and U = w*v to the workspace, zeroing
+// rows past the valid length; e and u of every item stay in keepE, keepU
+// for step 3.  It returns whether a valid log-decay is positive.
 template <bool B1, bool W1, bool G1, typename E, int D>
-__device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_t r, int tid, float* sm, float* sRN,
-                                         f32x4* keepE, f32x4* keepU)
+struct PrepRaw {
+    static constexpr int NIT = BC * (D / 4) / NTP;
+    static_assert(BC * (D / 4) % NTP == 0, "whole items per thread");
+    typename Raw4<E>::V rk[NIT], rq[NIT], rv[NIT], rb[NIT], rw[NIT];
+    f32x4 rg[NIT];
+    E sb[NIT], sw[NIT];
+    float sg[NIT];
+};
+
+template <bool B1, bool W1, bool G1, typename E, int D>
+__device__ __forceinline__ void prep_rows_load(const BwdArgs& a, const Rec& rc, int tid, PrepRaw<B1, W1, G1, E, D>& x)
 {
-    typedef BwdPrepShape<D> PS;
-    typedef Raw4<E> R;
-    constexpr int C = BC, LD = PS::LD, Q4 = D / 4, NIT = C * Q4 / NTP;
-    static_assert(C * Q4 % NTP == 0, "whole items per thread");
+    constexpr int Q4 = D / 4, NIT = PrepRaw<B1, W1, G1, E, D>::NIT;
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
     const E* b = (const E*)a.b;
     const E* w = (const E*)a.w;
-    float* ws = a.ws;
-    const size_t cdo = (size_t)r * C * D;
-
-    typename R::V rk[NIT], rq[NIT], rv[NIT], rb[NIT], rw[NIT];
-    f32x4 rg[NIT];
-    E sb[NIT], sw[NIT];
-    float sg[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4);
         const int64_t row = rc.row0 + (int64_t)min(t, rc.L - 1) * a.H;
-        rk[it] = ld_raw4(k + row * D + i);
-        rq[it] = ld_raw4(q + row * D + i);
-        rv[it] = ld_raw4(v + row * D + i);
+        x.rk[it] = ld_raw4(k + row * D + i);
+        x.rq[it] = ld_raw4(q + row * D + i);
+        x.rv[it] = ld_raw4(v + row * D + i);
         if (B1)
-            sb[it] = b[row];
+            x.sb[it] = b[row];
         else
-            rb[it] = ld_raw4(b + row * D + i);
+            x.rb[it] = ld_raw4(b + row * D + i);
         if (W1)
-            sw[it] = w[row];
+            x.sw[it] = w[row];
         else
-            rw[it] = ld_raw4(w + row * D + i);
+            x.rw[it] = ld_raw4(w + row * D + i);
         if (G1)
-            sg[it] = a.g[row];
+            x.sg[it] = a.g[row];
         else
-            rg[it] = load4(a.g + row * D + i);
+            x.rg[it] = load4(a.g + row * D + i);
     }
+}
+
+template <bool B1, bool W1, bool G1, typename E, int D>
+__device__ __forceinline__ int prep_rows_use(const BwdArgs& a, const Rec& rc, int64_t r, int tid, float* sm,
+                                             float* sRN, f32x4* keepE, f32x4* keepU,
+                                             const PrepRaw<B1, W1, G1, E, D>& x)
+{
+    typedef BwdPrepShape<D> PS;
+    typedef Raw4<E> R;
+    constexpr int C = BC, LD = PS::LD, Q4 = D / 4, NIT = PrepRaw<B1, W1, G1, E, D>::NIT;
+    float* ws = a.ws;
+    const size_t cdo = (size_t)r * C * D;
     int growth = 0;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        const size_t x = cdo + (size_t)t * D + i;
+        const size_t xo = cdo + (size_t)t * D + i;
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 gv = G1 ? bcast4(sg[it]) : rg[it];
-        f32x4 kv = R::cvt(rk[it]), qv = R::cvt(rq[it]);
-        f32x4 bv = B1 ? bcast4(to_f32(sb[it])) : R::cvt(rb[it]);
-        f32x4 wv = W1 ? bcast4(to_f32(sw[it])) : R::cvt(rw[it]);
+        f32x4 gv = G1 ? bcast4(x.sg[it]) : x.rg[it];
+        f32x4 kv = R::cvt(x.rk[it]), qv = R::cvt(x.rq[it]);
+        f32x4 bv = B1 ? bcast4(to_f32(x.sb[it])) : R::cvt(x.rb[it]);
+        f32x4 wv = W1 ? bcast4(to_f32(x.sw[it])) : R::cvt(x.rw[it]);
         if (a.pro & GDR2_PROLOGUE_GATES) {
             bv = bsigm4(bv);
             wv = bsigm4(wv);
@@ -346,7 +359,7 @@ __device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_
             for (int j = 0; j < 4; ++j)
                 gv[j] = bneg_softplus(gv[j]);
         }
-        f32x4 ev = bv, uv = wv * R::cvt(rv[it]);
+        f32x4 ev = bv, uv = wv * R::cvt(x.rv[it]);
         if (t >= rc.L) {
             gv = zero;
             kv = zero;
@@ -378,16 +391,17 @@ __device__ __forceinline__ int prep_rows(const BwdArgs& a, const Rec& rc, int64_
         st4s(sm + PS::OFF_K + l, kv);
         st4s(sm + PS::OFF_Q + l, qv);
         st4s(sm + PS::OFF_E + l, ev);
-        store4(reinterpret_cast<E*>(ws + a.L.U) + x, uv);
+        store4(reinterpret_cast<E*>(ws + a.L.U) + xo, uv);
         keepE[it] = ev;
         keepU[it] = uv;
     }
     return growth;
 }
 
-template <typename E, int D>
+template <typename E, int D, int MIX>
 __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 {
+    constexpr bool B1 = MIX & 4, W1 = MIX & 2, G1 = MIX & 1;   // gates of width 1
     typedef BwdPrepShape<D> PS;
     constexpr int C = BC, LD = PS::LD, LDM = PS::LDM, Q4 = D / 4;
     extern __shared__ __align__(16) float sm[];
@@ -398,348 +412,356 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
     float* sM = sm + PS::OFF_M;     // [C][LDM] M
     __shared__ int sOr[2 * (NTP / 64)];
     __shared__ float sRN[2 * C];    // prologue: 1/|k|, 1/|q| per token
-    const int64_t r = blockIdx.x;
-    const Rec rc = rec_of(r, a.NC, a.T, a.H);
-    const int tid = threadIdx.x;
-    const E* q = (const E*)a.q;
-    const E* k = (const E*)a.k;
-    const E* v = (const E*)a.v;
-    const E* b = (const E*)a.b;
-    const E* w = (const E*)a.w;
     float* ws = a.ws;
-    const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
-    // the scan's operand fragments of this record (K^, P^T, Q~^T, -W^T; the
-    // frag pass adds dO^T), in the input dtype
     typedef ScanFrags<E, D> SF;
-    unsigned char* sfr = reinterpret_cast<unsigned char*>(ws + a.L.SF) + (size_t)r * SF::REC;
-    auto pT = [&](int s_, int t) -> E* {            // P^T[s][t] = P[t][s]
-        return reinterpret_cast<E*>(sfr + SF::OFF_P + frag_at<E>(s_, t, SF::NKC));
-    };
+    // persistent: records blockIdx.x, + gridDim.x, ... (the grid is at most
+    // nrec), each record's input rows loaded while the previous record is
+    // processed; barriers wait for LDS only, so a record's stores drain
+    // during the next
+    PrepRaw<B1, W1, G1, E, D> raw;
+    prep_rows_load<B1, W1, G1, E, D>(a, rec_of(blockIdx.x, a.NC, a.T, a.H), threadIdx.x, raw);
+    for (int64_t r = blockIdx.x; r < a.nrec; r += gridDim.x) {
+        // the thread index, opaque to the compiler in each iteration: no
+        // address derived from it is hoisted out of the loop to occupy a
+        // register throughout
+        int tid = threadIdx.x;
+        __asm__ __volatile__("" : "+v"(tid));
+        const Rec rc = rec_of(r, a.NC, a.T, a.H);
+        const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
+        // the scan's operand fragments of this record (K^, P^T, Q~^T, -W^T; the
+        // frag pass adds dO^T), in the input dtype
+        unsigned char* sfr = reinterpret_cast<unsigned char*>(ws + a.L.SF) + (size_t)r * SF::REC;
+        auto pT = [&](int s_, int t) -> E* {            // P^T[s][t] = P[t][s]
+            return reinterpret_cast<E*>(sfr + SF::OFF_P + frag_at<E>(s_, t, SF::NKC));
+        };
 
-    // 1. raw rows (zero past the chunk's valid length), 4 channels per item
-    constexpr int NIT1 = C * Q4 / NTP;
-    f32x4 keepE[NIT1], keepU[NIT1];  // e = b k and u = w v of this thread's items, for step 3
-    int growth;
-    switch ((a.bw == 1 ? 4 : 0) | (a.ww == 1 ? 2 : 0) | (a.gw == 1 ? 1 : 0)) {
-    case 0: growth = prep_rows<false, false, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    case 1: growth = prep_rows<false, false, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    case 2: growth = prep_rows<false, true, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    case 3: growth = prep_rows<false, true, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    case 4: growth = prep_rows<true, false, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    case 5: growth = prep_rows<true, false, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    case 6: growth = prep_rows<true, true, false, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    default: growth = prep_rows<true, true, true, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU); break;
-    }
-    growth = lds_barrier_or<NTP / 64>(growth, sOr);
-    {
-        // cumulative sum over the chunk per channel: thread (group gi, channel
-        // i) scans its TPG consecutive tokens, then adds the earlier groups'
-        // totals (through the M area, free until step 2)
-        constexpr int NG = NTP / D, TPG = C / NG;
-        static_assert(NTP % D == 0 && C % NG == 0, "whole token groups");
-        const int i = tid % D, gi = tid / D;
-        float* sTot = sM;
-        float v[TPG];
-#pragma unroll
-        for (int m = 0; m < TPG; ++m)
-            v[m] = sG[(gi * TPG + m) * LD + i];
-#pragma unroll
-        for (int m = 1; m < TPG; ++m)
-            v[m] += v[m - 1];
-        sTot[gi * D + i] = v[TPG - 1];
+        // 1. raw rows (zero past the chunk's valid length), 4 channels per item,
+        // once every wave is done with the previous record's LDS; then the next
+        // record's loads (the last record's re-reads itself)
+        constexpr int NIT1 = C * Q4 / NTP;
+        f32x4 keepE[NIT1], keepU[NIT1];  // e = b k and u = w v of this thread's items, for step 3
         lds_barrier();
-        float off = 0.f;
-        for (int g2 = 0; g2 < gi; ++g2)
-            off += sTot[g2 * D + i];
+        int growth = prep_rows_use<B1, W1, G1, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU, raw);
+        prep_rows_load<B1, W1, G1, E, D>(a, rec_of(std::min<int64_t>(r + gridDim.x, a.nrec - 1), a.NC, a.T, a.H),
+                                         tid, raw);
+        growth = lds_barrier_or<NTP / 64>(growth, sOr);
+        {
+            // cumulative sum over the chunk per channel: thread (group gi, channel
+            // i) scans its TPG consecutive tokens, then adds the earlier groups'
+            // totals (through the M area, free until step 2)
+            constexpr int NG = NTP / D, TPG = C / NG;
+            static_assert(NTP % D == 0 && C % NG == 0, "whole token groups");
+            const int i = tid % D, gi = tid / D;
+            float* sTot = sM;
+            float v[TPG];
 #pragma unroll
-        for (int m = 0; m < TPG; ++m)
-            sG[(gi * TPG + m) * LD + i] = v[m] + off;
-    }
-    lds_barrier();
-    for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
-        const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        const size_t x = cdo + (size_t)t * D + i;
-        const f32x4 G = ld4s(sG + l), GL = ld4s(sG + (C - 1) * LD + i);
-        f32x4 eg, kd;
+            for (int m = 0; m < TPG; ++m)
+                v[m] = sG[(gi * TPG + m) * LD + i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            eg[j] = expf(G[j]);
-            kd[j] = expf(GL[j] - G[j]);
-        }
-        st4s(ws + a.L.G + x, G);
-        store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ld4s(sE + l) * eg);
-        // K^ straight into the scan's fragments (row = token, k = channel)
-        store4(reinterpret_cast<E*>(sfr + SF::OFF_K + frag_at<E>(t, i, SF::NKS)), ld4s(sK + l) * kd);
-        if (t == 0) {
-            f32x4 gm;
+            for (int m = 1; m < TPG; ++m)
+                v[m] += v[m - 1];
+            sTot[gi * D + i] = v[TPG - 1];
+            lds_barrier();
+            float off = 0.f;
+            for (int g2 = 0; g2 < gi; ++g2)
+                off += sTot[g2 * D + i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                gm[j] = expf(GL[j]);
-            st4s(ws + a.L.gam + (size_t)r * D + i, gm);
-        }
-    }
-    // Q~ = q e^G into the scan's Q~^T fragments (row = channel, k = token):
-    // an item is one channel at 4 consecutive tokens, read from the raw
-    // rows before step 2 re-references them
-    for (int e = tid; e < D * (C / 4); e += NTP) {
-        const int i = e % D, t0 = 4 * (e / D);
-        f32x4 qv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            qv[j] = sQ[(t0 + j) * LD + i] * expf(sG[(t0 + j) * LD + i]);
-        store4(reinterpret_cast<E*>(sfr + SF::OFF_Q + frag_at<E>(i, t0, SF::NKC)), qv);
-    }
-
-    // 2. M (strictly lower) and P (lower).
-    if (!growth) {
-        // Decays only.  The rows are re-referenced to their 16-token block in
-        // place,  E^ = e e^{G - G_16T},  Q^ = q e^{G - G_16T},  K- = k e^{G_16T+15 - G},
-        // so the block (T, S), S <= T, is  M_TS = (E^_T c_TS) K-_S^T  (and P
-        // with Q^), c_TS = e^{G_16T - G_16S+15}: <= 1 below the diagonal,
-        // e^{span of block T} on it.  A block whose span exceeds kDiagSpan in
-        // some channel sends the diagonal blocks pair by pair (2a) instead.
-        float* sCf = sm + PS::OFF_CF;
-        int steep = 0;
-        for (int e = tid; e < (C / 16) * D; e += NTP) {
-            const int T = e / D, i = e % D;
-            steep |= sG[16 * T * LD + i] - sG[(16 * T + 15) * LD + i] > kDiagSpan;
-        }
-        steep = lds_barrier_or<NTP / 64>(steep, sOr + NTP / 64);
-        // 2a. (steep) the diagonal 16x16 blocks pair by pair, from the raw rows
-        for (int e = steep ? tid : 4 * 136; e < 4 * 136; e += NTP) {
-            const int blk = e / 136, pr = e % 136;
-            int rr = 0;
-            while ((rr + 1) * (rr + 2) / 2 <= pr)
-                ++rr;
-            const int cc = pr - rr * (rr + 1) / 2, t = 16 * blk + rr, s_ = 16 * blk + cc;
-            float m = 0.f, p = 0.f;
-            for (int i = 0; i < D; ++i) {
-                const float f = __expf(sG[t * LD + i] - sG[s_ * LD + i]) * sK[s_ * LD + i];
-                m += sE[t * LD + i] * f;
-                p += sQ[t * LD + i] * f;
-            }
-            sM[t * LDM + s_] = cc < rr ? m : 0.f;
-            *pT(s_, t) = from_f32<E>(p);
-            if (cc < rr) {
-                sM[s_ * LDM + t] = 0.f;
-                *pT(t, s_) = from_f32<E>(0.f);
-            }
+            for (int m = 0; m < TPG; ++m)
+                sG[(gi * TPG + m) * LD + i] = v[m] + off;
         }
         lds_barrier();
-        // 2b. re-referenced rows, and c_TS (pairs 0..5 below the diagonal in
-        // the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); 6 + T on it)
         for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
-            const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i, T = t / 16;
-            const f32x4 G = ld4s(sG + l), G0 = ld4s(sG + 16 * T * LD + i), G1 = ld4s(sG + (16 * T + 15) * LD + i);
-            f32x4 fa, fb;
+            const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+            const size_t x = cdo + (size_t)t * D + i;
+            const f32x4 G = ld4s(sG + l), GL = ld4s(sG + (C - 1) * LD + i);
+            f32x4 eg, kd;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                fa[j] = __expf(G[j] - G0[j]);
-                fb[j] = __expf(G1[j] - G[j]);
+                eg[j] = expf(G[j]);
+                kd[j] = expf(GL[j] - G[j]);
             }
-            st4s(sE + l, ld4s(sE + l) * fa);
-            st4s(sQ + l, ld4s(sQ + l) * fa);
-            st4s(sK + l, ld4s(sK + l) * fb);
+            st4s(ws + a.L.G + x, G);
+            store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ld4s(sE + l) * eg);
+            // K^ straight into the scan's fragments (row = token, k = channel)
+            store4(reinterpret_cast<E*>(sfr + SF::OFF_K + frag_at<E>(t, i, SF::NKS)), ld4s(sK + l) * kd);
+            if (t == 0) {
+                f32x4 gm;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    gm[j] = expf(GL[j]);
+                st4s(ws + a.L.gam + (size_t)r * D + i, gm);
+            }
         }
-        for (int e = tid; e < 10 * D; e += NTP) {
-            const int pi = e / D, i = e % D;
-            const int T = pi < 1 ? 1 : pi < 3 ? 2 : pi < 6 ? 3 : pi - 6;
-            const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
-            sCf[e] = __expf(sG[16 * T * LD + i] - sG[(16 * S + 15) * LD + i]);
+        // Q~ = q e^G into the scan's Q~^T fragments (row = channel, k = token):
+        // an item is one channel at 4 consecutive tokens, read from the raw
+        // rows before step 2 re-references them
+        for (int e = tid; e < D * (C / 4); e += NTP) {
+            const int i = e % D, t0 = 4 * (e / D);
+            f32x4 qv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                qv[j] = sQ[(t0 + j) * LD + i] * expf(sG[(t0 + j) * LD + i]);
+            store4(reinterpret_cast<E*>(sfr + SF::OFF_Q + frag_at<E>(i, t0, SF::NKC)), qv);
         }
-        lds_barrier();
-        // 2c. the block products on fp32 MFMA, one wave per block pair (M and
-        // P share the K- fragments); each wave also clears the mirrored block
-        // above the diagonal
-        {
-            typedef Mma<float> MF;
-            const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
-            for (int pi = wave; pi < (steep ? 6 : 10); pi += NTP / 64) {
+
+        // 2. M (strictly lower) and P (lower).
+        if (!growth) {
+            // Decays only.  The rows are re-referenced to their 16-token block in
+            // place,  E^ = e e^{G - G_16T},  Q^ = q e^{G - G_16T},  K- = k e^{G_16T+15 - G},
+            // so the block (T, S), S <= T, is  M_TS = (E^_T c_TS) K-_S^T  (and P
+            // with Q^), c_TS = e^{G_16T - G_16S+15}: <= 1 below the diagonal,
+            // e^{span of block T} on it.  A block whose span exceeds kDiagSpan in
+            // some channel sends the diagonal blocks pair by pair (2a) instead.
+            float* sCf = sm + PS::OFF_CF;
+            int steep = 0;
+            for (int e = tid; e < (C / 16) * D; e += NTP) {
+                const int T = e / D, i = e % D;
+                steep |= sG[16 * T * LD + i] - sG[(16 * T + 15) * LD + i] > kDiagSpan;
+            }
+            steep = lds_barrier_or<NTP / 64>(steep, sOr + NTP / 64);
+            // 2a. (steep) the diagonal 16x16 blocks pair by pair, from the raw rows
+            for (int e = steep ? tid : 4 * 136; e < 4 * 136; e += NTP) {
+                const int blk = e / 136, pr = e % 136;
+                int rr = 0;
+                while ((rr + 1) * (rr + 2) / 2 <= pr)
+                    ++rr;
+                const int cc = pr - rr * (rr + 1) / 2, t = 16 * blk + rr, s_ = 16 * blk + cc;
+                float m = 0.f, p = 0.f;
+                for (int i = 0; i < D; ++i) {
+                    const float f = __expf(sG[t * LD + i] - sG[s_ * LD + i]) * sK[s_ * LD + i];
+                    m += sE[t * LD + i] * f;
+                    p += sQ[t * LD + i] * f;
+                }
+                sM[t * LDM + s_] = cc < rr ? m : 0.f;
+                *pT(s_, t) = from_f32<E>(p);
+                if (cc < rr) {
+                    sM[s_ * LDM + t] = 0.f;
+                    *pT(t, s_) = from_f32<E>(0.f);
+                }
+            }
+            lds_barrier();
+            // 2b. re-referenced rows, and c_TS (pairs 0..5 below the diagonal in
+            // the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); 6 + T on it)
+            for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
+                const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i, T = t / 16;
+                const f32x4 G = ld4s(sG + l), G0 = ld4s(sG + 16 * T * LD + i), G1 = ld4s(sG + (16 * T + 15) * LD + i);
+                f32x4 fa, fb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    fa[j] = __expf(G[j] - G0[j]);
+                    fb[j] = __expf(G1[j] - G[j]);
+                }
+                st4s(sE + l, ld4s(sE + l) * fa);
+                st4s(sQ + l, ld4s(sQ + l) * fa);
+                st4s(sK + l, ld4s(sK + l) * fb);
+            }
+            for (int e = tid; e < 10 * D; e += NTP) {
+                const int pi = e / D, i = e % D;
                 const int T = pi < 1 ? 1 : pi < 3 ? 2 : pi < 6 ? 3 : pi - 6;
                 const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
-                const float* cf = sCf + pi * D;
-                f32x4 m = {0.f, 0.f, 0.f, 0.f}, p = m;
+                sCf[e] = __expf(sG[16 * T * LD + i] - sG[(16 * S + 15) * LD + i]);
+            }
+            lds_barrier();
+            // 2c. the block products on fp32 MFMA, one wave per block pair (M and
+            // P share the K- fragments); each wave also clears the mirrored block
+            // above the diagonal
+            {
+                typedef Mma<float> MF;
+                const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+                for (int pi = wave; pi < (steep ? 6 : 10); pi += NTP / 64) {
+                    const int T = pi < 1 ? 1 : pi < 3 ? 2 : pi < 6 ? 3 : pi - 6;
+                    const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
+                    const float* cf = sCf + pi * D;
+                    f32x4 m = {0.f, 0.f, 0.f, 0.f}, p = m;
 #pragma unroll 4
-                for (int k0 = 0; k0 < D; k0 += MF::KB) {
-                    const MF::Frag kb = MF::load(sK + 16 * S * LD + k0, LD, lane);
-                    m = MF::mma(MF::load_scaled(sE + 16 * T * LD + k0, LD, cf + k0, lane), kb, m);
-                    p = MF::mma(MF::load_scaled(sQ + 16 * T * LD + k0, LD, cf + k0, lane), kb, p);
-                }
-                f32x4 pv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * T + 4 * gq + i, s_ = 16 * S + cl;
-                    sM[t * LDM + s_] = s_ < t ? m[i] : 0.f;
-                    pv[i] = s_ <= t ? p[i] : 0.f;
-                    if (S < T) {
-                        const int ta = 16 * S + 4 * gq + i, sa = 16 * T + cl;   // the block (S, T)
-                        sM[ta * LDM + sa] = 0.f;
+                    for (int k0 = 0; k0 < D; k0 += MF::KB) {
+                        const MF::Frag kb = MF::load(sK + 16 * S * LD + k0, LD, lane);
+                        m = MF::mma(MF::load_scaled(sE + 16 * T * LD + k0, LD, cf + k0, lane), kb, m);
+                        p = MF::mma(MF::load_scaled(sQ + 16 * T * LD + k0, LD, cf + k0, lane), kb, p);
                     }
+                    f32x4 pv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * T + 4 * gq + i, s_ = 16 * S + cl;
+                        sM[t * LDM + s_] = s_ < t ? m[i] : 0.f;
+                        pv[i] = s_ <= t ? p[i] : 0.f;
+                        if (S < T) {
+                            const int ta = 16 * S + 4 * gq + i, sa = 16 * T + cl;   // the block (S, T)
+                            sM[ta * LDM + sa] = 0.f;
+                        }
+                    }
+                    // the accumulator column is a P^T fragment row: 4 consecutive tokens
+                    store4(pT(16 * S + cl, 16 * T + 4 * gq), pv);
+                    if (S < T)
+                        store4(pT(16 * T + cl, 16 * S + 4 * gq), f32x4{0.f, 0.f, 0.f, 0.f});
                 }
-                // the accumulator column is a P^T fragment row: 4 consecutive tokens
-                store4(pT(16 * S + cl, 16 * T + 4 * gq), pv);
-                if (S < T)
-                    store4(pT(16 * T + cl, 16 * S + 4 * gq), f32x4{0.f, 0.f, 0.f, 0.f});
             }
-        }
-        lds_barrier();
-    } else {
-        // Some log-decay > 0 (growth): factors could exceed 1, so every
-        // pair takes its own exponential.  4x4 token blocks on and below the
-        // diagonal; two threads (channel halves) per block.
-        float m[4][4] = {}, p[4][4] = {};
-        const int half = tid / 136, bid = tid % 136;
-        int tb = 0;
-        while ((tb + 1) * (tb + 2) / 2 <= bid)
-            ++tb;
-        const int sb = bid - tb * (tb + 1) / 2, t0 = 4 * tb, s0 = 4 * sb;
-        if (tid < 272) {
-            for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
-                float gt[4], et[4], qt[4], gs[4], ks[4];
-    #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    gt[x] = sG[(t0 + x) * LD + i];
-                    et[x] = sE[(t0 + x) * LD + i];
-                    qt[x] = sQ[(t0 + x) * LD + i];
-                    gs[x] = sG[(s0 + x) * LD + i];
-                    ks[x] = sK[(s0 + x) * LD + i];
+            lds_barrier();
+        } else {
+            // Some log-decay > 0 (growth): factors could exceed 1, so every
+            // pair takes its own exponential.  4x4 token blocks on and below the
+            // diagonal; two threads (channel halves) per block.
+            float m[4][4] = {}, p[4][4] = {};
+            const int half = tid / 136, bid = tid % 136;
+            int tb = 0;
+            while ((tb + 1) * (tb + 2) / 2 <= bid)
+                ++tb;
+            const int sb = bid - tb * (tb + 1) / 2, t0 = 4 * tb, s0 = 4 * sb;
+            if (tid < 272) {
+                for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
+                    float gt[4], et[4], qt[4], gs[4], ks[4];
+        #pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        gt[x] = sG[(t0 + x) * LD + i];
+                        et[x] = sE[(t0 + x) * LD + i];
+                        qt[x] = sQ[(t0 + x) * LD + i];
+                        gs[x] = sG[(s0 + x) * LD + i];
+                        ks[x] = sK[(s0 + x) * LD + i];
+                    }
+        #pragma unroll
+                    for (int x = 0; x < 4; ++x)
+        #pragma unroll
+                        for (int y = 0; y < 4; ++y) {
+                            const float f = __expf(gt[x] - gs[y]) * ks[y];
+                            m[x][y] += et[x] * f;
+                            p[x][y] += qt[x] * f;
+                        }
                 }
-    #pragma unroll
+            }
+            lds_barrier();                  // q and k rows are no longer read
+            float* sPp = sK;                  // [C][C] partial P of the second half
+            if (tid >= 136 && tid < 272) {
+        #pragma unroll
                 for (int x = 0; x < 4; ++x)
-    #pragma unroll
+        #pragma unroll
                     for (int y = 0; y < 4; ++y) {
-                        const float f = __expf(gt[x] - gs[y]) * ks[y];
-                        m[x][y] += et[x] * f;
-                        p[x][y] += qt[x] * f;
+                        sM[(t0 + x) * LDM + s0 + y] = m[x][y];
+                        sPp[(t0 + x) * C + s0 + y] = p[x][y];
                     }
             }
-        }
-        lds_barrier();                  // q and k rows are no longer read
-        float* sPp = sK;                  // [C][C] partial P of the second half
-        if (tid >= 136 && tid < 272) {
-    #pragma unroll
-            for (int x = 0; x < 4; ++x)
-    #pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    sM[(t0 + x) * LDM + s0 + y] = m[x][y];
-                    sPp[(t0 + x) * C + s0 + y] = p[x][y];
+            lds_barrier();
+            if (tid < 136) {
+                f32x4 pv[4];                  // pv[y][x] = P[t0 + x][s0 + y]
+        #pragma unroll
+                for (int x = 0; x < 4; ++x)
+        #pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        const int t = t0 + x, s_ = s0 + y;
+                        const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
+                        sM[t * LDM + s_] = s_ < t ? mm : 0.f;
+                        pv[y][x] = s_ <= t ? pp : 0.f;
+                    }
+        #pragma unroll
+                for (int y = 0; y < 4; ++y)
+                    store4(pT(s0 + y, t0), pv[y]);
+                if (sb != tb) {               // the mirrored block above the diagonal is zero
+        #pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+        #pragma unroll
+                        for (int y = 0; y < 4; ++y)
+                            sM[(s0 + y) * LDM + t0 + x] = 0.f;
+                        store4(pT(t0 + x, s0), f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
                 }
+            }
+            lds_barrier();
+
         }
-        lds_barrier();
-        if (tid < 136) {
-            f32x4 pv[4];                  // pv[y][x] = P[t0 + x][s0 + y]
-    #pragma unroll
-            for (int x = 0; x < 4; ++x)
-    #pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const int t = t0 + x, s_ = s0 + y;
-                    const float mm = m[x][y] + sM[t * LDM + s_], pp = p[x][y] + sPp[t * C + s_];
-                    sM[t * LDM + s_] = s_ < t ? mm : 0.f;
-                    pv[y][x] = s_ <= t ? pp : 0.f;
+
+        // 3. X = (I + M)^-1 into the q area (wave 0), after every thread has
+        // staged E~ = e e^G and u of its step-1 items for step 4 (the k and E
+        // areas held re-referenced rows until now)
+        float* sX = sQ;
+        float* sU = sK;
+#pragma unroll
+        for (int it = 0; it < NIT1; ++it) {
+            const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+            const f32x4 G = ld4s(sG + l);
+            f32x4 ev = keepE[it];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ev[j] *= expf(G[j]);
+            st4s(sE + l, ev);
+            st4s(sU + l, keepU[it]);
+        }
+        if (tid < 64) {
+            typedef Mma<float> MF;
+            const int lane = tid, gq = lane >> 4, cl = lane & 15;
+            {
+                // column cl of the diagonal block X_gq,gq by forward substitution
+                // (unit diagonal), then zeros for the blocks right of it
+                const float* m = sM + 16 * gq * LDM + 16 * gq;
+                float x[16];
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    float acc = rr == cl ? 1.f : 0.f;
+#pragma unroll
+                    for (int c = 0; c < rr; ++c)
+                        acc -= m[rr * LDM + c] * x[c];
+                    x[rr] = acc;
                 }
-    #pragma unroll
-            for (int y = 0; y < 4; ++y)
-                store4(pT(s0 + y, t0), pv[y]);
-            if (sb != tb) {               // the mirrored block above the diagonal is zero
-    #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-    #pragma unroll
-                    for (int y = 0; y < 4; ++y)
-                        sM[(s0 + y) * LDM + t0 + x] = 0.f;
-                    store4(pT(t0 + x, s0), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    sX[(16 * gq + rr) * LDM + 16 * gq + cl] = x[rr];
+                    for (int J = gq + 1; J < C / 16; ++J)
+                        sX[(16 * gq + rr) * LDM + 16 * J + cl] = 0.f;
+                }
+            }
+            // X_IJ = -X_II sum_{K=J}^{I-1} M_IK X_KJ, one block diagonal at a time
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            for (int dg = 1; dg < C / 16; ++dg) {
+                lds_fence_wave();
+                for (int I = dg; I < C / 16; ++I) {
+                    const int J = I - dg;
+                    f32x4 y = zero;
+                    for (int K = J; K < I; ++K)
+                        y = MF::mma(MF::load(sM + 16 * I * LDM + 16 * K, LDM, lane),
+                                    MF::load_kn(sX + 16 * K * LDM + 16 * J, LDM, lane), y);
+                    const f32x4 xi = MF::mma(MF::load(sX + 16 * I * LDM + 16 * I, LDM, lane), MF::from_acc(&y), zero);
+#pragma unroll
+                    for (int x4 = 0; x4 < 4; ++x4)
+                        sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = -xi[x4];
                 }
             }
         }
         lds_barrier();
+        for (int e4 = tid; e4 < C * C / 4; e4 += NTP) {
+            const int t = e4 / (C / 4), c4 = 4 * (e4 % (C / 4));
+            st4s(ws + a.L.X + cco + (size_t)t * C + c4, ld4s(sX + t * LDM + c4));
+        }
 
-    }
-
-    // 3. X = (I + M)^-1 into the q area (wave 0), after every thread has
-    // staged E~ = e e^G and u of its step-1 items for step 4 (the k and E
-    // areas held re-referenced rows until now)
-    float* sX = sQ;
-    float* sU = sK;
-#pragma unroll
-    for (int it = 0; it < NIT1; ++it) {
-        const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        const f32x4 G = ld4s(sG + l);
-        f32x4 ev = keepE[it];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ev[j] *= expf(G[j]);
-        st4s(sE + l, ev);
-        st4s(sU + l, keepU[it]);
-    }
-    if (tid < 64) {
-        typedef Mma<float> MF;
-        const int lane = tid, gq = lane >> 4, cl = lane & 15;
+        // 4. W = X E~, U~ = X u
         {
-            // column cl of the diagonal block X_gq,gq by forward substitution
-            // (unit diagonal), then zeros for the blocks right of it
-            const float* m = sM + 16 * gq * LDM + 16 * gq;
-            float x[16];
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float acc = rr == cl ? 1.f : 0.f;
-#pragma unroll
-                for (int c = 0; c < rr; ++c)
-                    acc -= m[rr * LDM + c] * x[c];
-                x[rr] = acc;
-            }
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                sX[(16 * gq + rr) * LDM + 16 * gq + cl] = x[rr];
-                for (int J = gq + 1; J < C / 16; ++J)
-                    sX[(16 * gq + rr) * LDM + 16 * J + cl] = 0.f;
-            }
-        }
-        // X_IJ = -X_II sum_{K=J}^{I-1} M_IK X_KJ, one block diagonal at a time
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        for (int dg = 1; dg < C / 16; ++dg) {
-            lds_fence_wave();
-            for (int I = dg; I < C / 16; ++I) {
-                const int J = I - dg;
-                f32x4 y = zero;
-                for (int K = J; K < I; ++K)
-                    y = MF::mma(MF::load(sM + 16 * I * LDM + 16 * K, LDM, lane),
-                                MF::load_kn(sX + 16 * K * LDM + 16 * J, LDM, lane), y);
-                const f32x4 xi = MF::mma(MF::load(sX + 16 * I * LDM + 16 * I, LDM, lane), MF::from_acc(&y), zero);
-#pragma unroll
-                for (int x4 = 0; x4 < 4; ++x4)
-                    sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = -xi[x4];
-            }
-        }
-    }
-    lds_barrier();
-    for (int e = tid; e < C * C; e += NTP)
-        ws[a.L.X + cco + e] = sX[(e / C) * LDM + e % C];
-
-    // 4. W = X E~, U~ = X u
-    {
-        // 16x16 output tiles on fp32 MFMA, one wave per tile: A = rows of X
-        // (lower triangular, so tile row T needs k-tiles 0..T), B = the
-        // columns of E~ or u
-        typedef Mma<float> MF;
-        const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
-        constexpr int NTD = D / 16, NPER = (C / 16) * NTD;
-        for (int tile = wave; tile < 2 * NPER; tile += NTP / 64) {
-            const int which = tile / NPER, T = (tile % NPER) / NTD, c = tile % NTD;
-            const float* src = which == 0 ? sE : sU;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk <= T; ++kk)
-                acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
-                              MF::load_kn(src + 16 * kk * LD + 16 * c, LD, lane), acc);
-            const size_t o = cdo + (size_t)(16 * T + 4 * gq) * D + 16 * c + cl;
-            if (which == 0) {
+            // 16x16 output tiles on fp32 MFMA, one wave per tile: A = rows of X
+            // (lower triangular, so tile row T needs k-tiles 0..T), B = the
+            // columns of E~ or u
+            // Each tile goes out through a per-wave 16 x 20 LDS patch (in the
+            // M area, free by now) as row pieces of 4, one vector store per lane.
+            typedef Mma<float> MF;
+            const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+            constexpr int NTD = D / 16, NPER = (C / 16) * NTD, LP = 20;
+            static_assert((NTP / 64) * 16 * LP <= C * LDM, "the patches fit in the M area");
+            float* patch = sM + wave * 16 * LP;
+            const int pr = lane >> 2, pc = 4 * (lane & 3);   // this lane's row piece of a tile
+            for (int tile = wave; tile < 2 * NPER; tile += NTP / 64) {
+                const int which = tile / NPER, T = (tile % NPER) / NTD, c = tile % NTD;
+                const float* src = which == 0 ? sE : sU;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int kk = 0; kk <= T; ++kk)
+                    acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
+                                  MF::load_kn(src + 16 * kk * LD + 16 * c, LD, lane), acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    reinterpret_cast<E*>(ws + a.L.W)[o + (size_t)i * D] = from_f32<E>(acc[i]);
-                // and -W^T for the scan: the accumulator column is a fragment row
-                store4(reinterpret_cast<E*>(sfr + SF::OFF_W + frag_at<E>(16 * c + cl, 16 * T + 4 * gq, SF::NKC)), -acc);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ws[a.L.Ut + o + (size_t)i * D] = acc[i];
+                    patch[(4 * gq + i) * LP + cl] = acc[i];
+                const f32x4 row4 = ld4s(patch + pr * LP + pc);
+                const size_t o = cdo + (size_t)(16 * T + pr) * D + 16 * c + pc;
+                if (which == 0) {
+                    store4(reinterpret_cast<E*>(ws + a.L.W) + o, row4);
+                    // and -W^T for the scan: the accumulator column is a fragment row
+                    store4(reinterpret_cast<E*>(sfr + SF::OFF_W + frag_at<E>(16 * c + cl, 16 * T + 4 * gq, SF::NKC)), -acc);
+                } else {
+                    st4s(ws + a.L.Ut + o, row4);
+                }
             }
         }
     }
@@ -1300,6 +1322,22 @@ __global__ __launch_bounds__(NTB) void bwd_sgrad_kernel(BwdArgs a)
     gemm_tile<Mma<E>>(sA, sB, 0, 0, D, dO, Delt, 0, none, none, ws + a.L.dP + cc, C, 1.f, 0.f, nullptr, 1);
 }
 
+// A 16x16 MFMA accumulator tile (lane l: rows 4(l/16)..+3 of column l%16)
+// regrouped through a per-wave LDS patch of PATCH_LD-float rows into row
+// pieces: lane l gets row l/4, columns 4(l%4)..+3, so that the tile leaves
+// as one vector store per lane.  Within a wave the patch accesses run in
+// order, so one patch serves tile after tile.
+constexpr int PATCH_LD = 20;
+constexpr int PATCH_FLOATS = 16 * PATCH_LD;
+__device__ __forceinline__ f32x4 tile_rows(float* patch, f32x4 acc, int lane)
+{
+    const int gq = lane >> 4, cl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        patch[(4 * gq + i) * PATCH_LD + cl] = acc[i];
+    return *reinterpret_cast<const f32x4*>(patch + (lane >> 2) * PATCH_LD + 4 * (lane & 3));
+}
+
 // bf16 inputs: the same state products with every operand read from memory
 // once (the tile version above re-reads S, W, dO and Delta from memory for
 // each product, since a chunk's operands do not stay in cache).  CG waves per
@@ -1314,10 +1352,11 @@ struct SgradShape {
     static constexpr int LDG = D / 4 + 1;         // fp32 row of the dgamma partial sums
     static constexpr size_t S_OFF = 0, ST_OFF = S_OFF + (size_t)D * LDB, L_OFF = ST_OFF + (size_t)D * LDB,
                             DEL_OFF = L_OFF + (size_t)D * LDB, ELEMS = DEL_OFF + (size_t)C * LDB;
-    static constexpr size_t SMEM = ELEMS * 2 + (size_t)D * LDG * 4;
-    static_assert(SMEM <= 160 * 1024, "LDS budget");
     static constexpr int CG = 2;                     // waves (column groups) per 16 token rows
     static constexpr int NTH = CG * 64 * (C / 16);   // threads
+    static constexpr size_t PATCH_OFF = ELEMS * 2 + (size_t)D * LDG * 4;   // bytes: per-wave output patches
+    static constexpr size_t SMEM = PATCH_OFF + (size_t)(NTH / 64) * PATCH_FLOATS * 4;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert((D / 16) % CG == 0 && (C / 16) % CG == 0, "whole tiles per column group");
 };
 
@@ -1334,175 +1373,192 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     bf16* sL = sb + SH::L_OFF;       // Lam[i][j]
     bf16* sDel = sb + SH::DEL_OFF;   // Delta[t][j]
     float* sPg = reinterpret_cast<float*>(sb + SH::ELEMS);   // [D][LDG] partial sums of dgamma
-    const int64_t r = blockIdx.x;
     float* ws = a.ws;
-    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C, dd = (size_t)r * D * D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    float* patch = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sb) + SH::PATCH_OFF) + wave * PATCH_FLOATS;
     const int rw = wave & 3, t0 = 16 * rw, n0 = (wave >> 2) * NH;   // row block; first of its NH column tiles
-
-    const float* S = a.S_chunks + dd;
-    const float* Lam = ws + a.L.Lam + dd;
-    const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
-    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd + (size_t)t0 * D;
-    // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
-    // valid length)
-    const Rec rc = rec_of(r, a.NC, a.T, a.H);
-    const bool dorow = t0 + cl < rc.L;
-    const bf16* dOr = (const bf16*)a.dO + (rc.row0 + (int64_t)(dorow ? t0 + cl : 0) * a.H) * D + 4 * gq;
-    auto load_dO = [&](int ks) -> Frag {
-        Frag f = {};
-        if (dorow) {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB + 16);
-            f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-            f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-        }
-        return f;
-    };
-    const size_t orow = cd + (size_t)(t0 + 4 * gq) * D + cl;   // output element (row 4gq, column cl) of the wave
-    // this wave's global operands of the products below, loaded first so
-    // that they arrive while S and Lam are staged
-    Frag pW[NKS], pD[NKS], pO[NKS];
-    float pU[NH][4];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        pW[ks] = MM::load(W + ks * MM::KB, D, lane);
-        pD[ks] = MM::load(dDel + ks * MM::KB, D, lane);
-        pO[ks] = load_dO(ks);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NH; ++nt)
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-            pU[nt][x] = ws[a.L.Ut + orow + (size_t)x * D + 16 * (n0 + nt)];
-    // staging also forms dgamma_i = sum_j S[i][j] Lam[i][j] in fp32 (partial
-    // sums of 4 through LDS); gamma becomes gamma * dgamma, the chunk-end term
-    // of dG_L that bwd_decay adds (the scan has used gamma)
-    const float gam_i = tid < D ? ws[a.L.gam + (size_t)r * D + tid] : 0.f;
-    // every item's loads first (all in flight together), then the conversions
+    // S and Lam of a record as rows of 4 (item e: row e / (D/4), columns
+    // 4 (e % (D/4))..), loaded one record ahead of their use
     constexpr int NIT = D * D / 4 / NTH;
     static_assert(D * D / 4 % NTH == 0, "whole items per thread");
     f32x4 s4r[NIT], l4r[NIT];
+    auto load_sl = [&](int64_t rr) {
+        const float* S = a.S_chunks + (size_t)rr * D * D;
+        const float* Lam = ws + a.L.Lam + (size_t)rr * D * D;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
-        s4r[it] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
-        l4r[it] = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
-        const f32x4 s4 = s4r[it], l4 = l4r[it];
-        bf16x4 sv, lv;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            sv[x] = (bf16)s4[x];
-            lv[x] = (bf16)l4[x];
-            sSt[(j + x) * LDB + i] = sv[x];
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+            s4r[it] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
+            l4r[it] = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
         }
-        *reinterpret_cast<bf16x4*>(sS + i * LDB + j) = sv;
-        *reinterpret_cast<bf16x4*>(sL + i * LDB + j) = lv;
-        sPg[i * SH::LDG + j / 4] = s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
-    }
-    __syncthreads();
-    if (tid < D) {
-        float dg = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < D / 4; ++c)
-            dg += sPg[tid * SH::LDG + c];
-        ws[a.L.gam + (size_t)r * D + tid] = gam_i * dg;
-    }
-
-
-    // Delta = U~ - W S   (k = i: B fragments from S^T)
-    {
-        f32x4 p[NH];
-#pragma unroll
-        for (int nt = 0; nt < NH; ++nt)
-            p[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // persistent: records blockIdx.x, + gridDim.x, ... (the grid is at most
+    // nrec); the next record's S and Lam are in flight while this one's
+    // products run, and barriers wait for LDS only, so the stores of a
+    // record drain during the next.  Every global load is issued on every
+    // path (the last prefetch re-reads the last record, rows past the valid
+    // length read row 0 and are zeroed), which keeps the compiler's waits
+    // for a load from also waiting for every later one.
+    load_sl(blockIdx.x);
+    for (int64_t r = blockIdx.x; r < a.nrec; r += gridDim.x) {
+        const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
+        const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
+        const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd + (size_t)t0 * D;
+        // dO rows from the input (row t0 + lane % 16 of the chunk; zero past the
+        // valid length)
+        const Rec rc = rec_of(r, a.NC, a.T, a.H);
+        const bool dorow = t0 + cl < rc.L;
+        const bf16* dOr = (const bf16*)a.dO + (rc.row0 + (int64_t)(dorow ? t0 + cl : 0) * a.H) * D + 4 * gq;
+        auto load_dO = [&](int ks) -> Frag {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(dOr + ks * MM::KB + 16);
+            const bf16 z = (bf16)0.f;
+            Frag f;
+            f[0] = dorow ? lo[0] : z; f[1] = dorow ? lo[1] : z; f[2] = dorow ? lo[2] : z; f[3] = dorow ? lo[3] : z;
+            f[4] = dorow ? hi[0] : z; f[5] = dorow ? hi[1] : z; f[6] = dorow ? hi[2] : z; f[7] = dorow ? hi[3] : z;
+            return f;
+        };
+        const size_t orow = cd + (size_t)(t0 + 4 * gq) * D + cl;   // output element (row 4gq, column cl) of the wave
+        const size_t prow = cd + (size_t)(t0 + (lane >> 2)) * D + 4 * (lane & 3);   // the lane's row piece (tile_rows)
+        // this wave's global operands of the products below, loaded first so
+        // that they arrive while S and Lam are staged
+        Frag pW[NKS], pD[NKS], pO[NKS];
+        float pU[NH][4];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-            for (int nt = 0; nt < NH; ++nt)
-                p[nt] = MM::mma(pW[ks], MM::load(sSt + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), p[nt]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NH; ++nt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float dl = pU[nt][x] - p[nt][x];
-                sDel[(t0 + 4 * gq + x) * LDB + 16 * (n0 + nt) + cl] = (bf16)dl;
-            }
-    }
-    // dQ~ = dO S^T,  dW = -dDelta S^T   (k = j: B fragments from S)
-    {
-        f32x4 q[NH], w[NH];
-#pragma unroll
-        for (int nt = 0; nt < NH; ++nt)
-            q[nt] = w[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-            for (int nt = 0; nt < NH; ++nt) {
-                const Frag bs = MM::load(sS + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane);
-                q[nt] = MM::mma(pO[ks], bs, q[nt]);
-                w[nt] = MM::mma(pD[ks], bs, w[nt]);
-            }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NH; ++nt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                ws[a.L.dQt + orow + (size_t)x * D + 16 * (n0 + nt)] = q[nt][x];
-                reinterpret_cast<bf16*>(ws + a.L.dW)[orow + (size_t)x * D + 16 * (n0 + nt)] = (bf16)(-w[nt][x]);
-            }
-    }
-    __syncthreads();                 // every wave's Delta rows are in LDS
-    // dK^ = Delta Lam^T   (A: this wave's Delta rows; k = j: B fragments from Lam)
-    {
-        f32x4 k[NH];
-#pragma unroll
-        for (int nt = 0; nt < NH; ++nt)
-            k[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const Frag ad = MM::load(sDel + t0 * LDB + ks * MM::KB, LDB, lane);
-#pragma unroll
-            for (int nt = 0; nt < NH; ++nt)
-                k[nt] = MM::mma(ad, MM::load(sL + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), k[nt]);
+            pW[ks] = MM::load(W + ks * MM::KB, D, lane);
+            pD[ks] = MM::load(dDel + ks * MM::KB, D, lane);
+            pO[ks] = load_dO(ks);
         }
 #pragma unroll
         for (int nt = 0; nt < NH; ++nt)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                ws[a.L.dKh + orow + (size_t)x * D + 16 * (n0 + nt)] = k[nt][x];
-    }
-    // dP = tril(dO Delta^T)   (k = j: B fragments from the Delta rows s);
-    // blocks above the diagonal are zero
-    {
-        constexpr int SBH = C / 16 / SH::CG;   // token blocks per column group
-        const int s0 = (wave >> 2) * SBH;
-        f32x4 pp[SBH];
+                pU[nt][x] = ws[a.L.Ut + orow + (size_t)x * D + 16 * (n0 + nt)];
+        // staging also forms dgamma_i = sum_j S[i][j] Lam[i][j] in fp32 (partial
+        // sums of 4 through LDS); gamma becomes gamma * dgamma, the chunk-end term
+        // of dG_L that bwd_decay adds (the scan has used gamma)
+        const float gam_i = ws[a.L.gam + (size_t)r * D + tid % D];   // used by the threads tid < D
+        // the staging below waits for S and Lam only: keep it after the
+        // loads above, whose issue the wait then does not hold up
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();                   // the previous record's products are done with LDS
 #pragma unroll
-        for (int sbk = 0; sbk < SBH; ++sbk)
-            pp[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (s0 <= rw) {
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+            const f32x4 s4 = s4r[it], l4 = l4r[it];
+            bf16x4 sv, lv;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                sv[x] = (bf16)s4[x];
+                lv[x] = (bf16)l4[x];
+                sSt[(j + x) * LDB + i] = sv[x];
+            }
+            *reinterpret_cast<bf16x4*>(sS + i * LDB + j) = sv;
+            *reinterpret_cast<bf16x4*>(sL + i * LDB + j) = lv;
+            sPg[i * SH::LDG + j / 4] = s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];
+        }
+        load_sl(std::min<int64_t>(r + gridDim.x, a.nrec - 1));
+        lds_barrier();
+        if (tid < D) {
+            float dg = 0.f;
+#pragma unroll 8
+            for (int c = 0; c < D / 4; ++c)
+                dg += sPg[tid * SH::LDG + c];
+            ws[a.L.gam + (size_t)r * D + tid] = gam_i * dg;
+        }
+
+
+        // Delta = U~ - W S   (k = i: B fragments from S^T)
+        {
+            f32x4 p[NH];
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt)
+                p[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-                for (int sbk = 0; sbk < SBH; ++sbk)
-                    if (s0 + sbk <= rw)
-                        pp[sbk] = MM::mma(pO[ks], MM::load(sDel + 16 * (s0 + sbk) * LDB + ks * MM::KB, LDB, lane),
-                                          pp[sbk]);
+                for (int nt = 0; nt < NH; ++nt)
+                    p[nt] = MM::mma(pW[ks], MM::load(sSt + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), p[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float dl = pU[nt][x] - p[nt][x];
+                    sDel[(t0 + 4 * gq + x) * LDB + 16 * (n0 + nt) + cl] = (bf16)dl;
+                }
+        }
+        // dQ~ = dO S^T,  dW = -dDelta S^T   (k = j: B fragments from S)
+        {
+            f32x4 q[NH], w[NH];
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt)
+                q[nt] = w[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int nt = 0; nt < NH; ++nt) {
+                    const Frag bs = MM::load(sS + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane);
+                    q[nt] = MM::mma(pO[ks], bs, q[nt]);
+                    w[nt] = MM::mma(pD[ks], bs, w[nt]);
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt) {
+                st4s(ws + a.L.dQt + prow + 16 * (n0 + nt), tile_rows(patch, q[nt], lane));
+                store4(reinterpret_cast<bf16*>(ws + a.L.dW) + prow + 16 * (n0 + nt), tile_rows(patch, -w[nt], lane));
             }
         }
+        lds_barrier();                   // every wave's Delta rows are in LDS
+        // dK^ = Delta Lam^T   (A: this wave's Delta rows; k = j: B fragments from Lam)
+        {
+            f32x4 k[NH];
 #pragma unroll
-        for (int sbk = 0; sbk < SBH; ++sbk)
+            for (int nt = 0; nt < NH; ++nt)
+                k[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int t = t0 + 4 * gq + x, s_ = 16 * (s0 + sbk) + cl;
-                ws[a.L.dP + cc + (size_t)t * C + s_] = s_ <= t ? pp[sbk][x] : 0.f;
+            for (int ks = 0; ks < NKS; ++ks) {
+                const Frag ad = MM::load(sDel + t0 * LDB + ks * MM::KB, LDB, lane);
+#pragma unroll
+                for (int nt = 0; nt < NH; ++nt)
+                    k[nt] = MM::mma(ad, MM::load(sL + 16 * (n0 + nt) * LDB + ks * MM::KB, LDB, lane), k[nt]);
             }
+#pragma unroll
+            for (int nt = 0; nt < NH; ++nt)
+                st4s(ws + a.L.dKh + prow + 16 * (n0 + nt), tile_rows(patch, k[nt], lane));
+        }
+        // dP = tril(dO Delta^T)   (k = j: B fragments from the Delta rows s);
+        // blocks above the diagonal are zero
+        {
+            constexpr int SBH = C / 16 / SH::CG;   // token blocks per column group
+            const int s0 = (wave >> 2) * SBH;
+            f32x4 pp[SBH];
+#pragma unroll
+            for (int sbk = 0; sbk < SBH; ++sbk)
+                pp[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s0 <= rw) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                    for (int sbk = 0; sbk < SBH; ++sbk)
+                        if (s0 + sbk <= rw)
+                            pp[sbk] = MM::mma(pO[ks], MM::load(sDel + 16 * (s0 + sbk) * LDB + ks * MM::KB, LDB, lane),
+                                              pp[sbk]);
+                }
+            }
+#pragma unroll
+            for (int sbk = 0; sbk < SBH; ++sbk) {
+                f32x4 m;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int t = t0 + 4 * gq + x, s_ = 16 * (s0 + sbk) + cl;
+                    m[x] = s_ <= t ? pp[sbk][x] : 0.f;
+                }
+                st4s(ws + a.L.dP + cc + (size_t)(t0 + (lane >> 2)) * C + 16 * (s0 + sbk) + 4 * (lane & 3),
+                     tile_rows(patch, m, lane));
+            }
+        }
     }
 }
 
@@ -1544,8 +1600,9 @@ struct XgradShape {
                             DWT_OFF = DDT_OFF + (size_t)D * LC, U_OFF = DWT_OFF + (size_t)D * LC,
                             ET_OFF = U_OFF + (size_t)C * LDd, DX_OFF = ET_OFF + (size_t)C * LDd,
                             T1T_OFF = DX_OFF + (size_t)C * LC, ELEMS = T1T_OFF + (size_t)C * LC;
-    static constexpr size_t SMEM = ELEMS * 2;
     static constexpr int NTH = 2 * 64 * (C / 16);
+    static constexpr size_t PATCH_OFF = ELEMS * 2;   // bytes: per-wave output patches
+    static constexpr size_t SMEM = PATCH_OFF + (size_t)(NTH / 64) * PATCH_FLOATS * 4;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
@@ -1570,6 +1627,7 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
     const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
     const int rw = wave & 3, hf = wave >> 2, t0 = 16 * rw;
+    float* patch = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sx) + SH::PATCH_OFF) + wave * PATCH_FLOATS;
     const float* Xg = ws + a.L.X + cc;
     const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd;
     const bf16* dW = reinterpret_cast<const bf16*>(ws + a.L.dW) + cd;
@@ -1638,13 +1696,11 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
             }
         }
 #pragma unroll
-        for (int n = 0; n < NH; ++n)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const size_t o = cd + (size_t)(t0 + 4 * gq + x) * D + 16 * (hf * NH + n) + cl;
-                ws[a.L.dU + o] = du[n][x];
-                ws[a.L.dEt + o] = de[n][x];
-            }
+        for (int n = 0; n < NH; ++n) {
+            const size_t o = cd + (size_t)(t0 + (lane >> 2)) * D + 16 * (hf * NH + n) + 4 * (lane & 3);
+            st4s(ws + a.L.dU + o, tile_rows(patch, du[n], lane));
+            st4s(ws + a.L.dEt + o, tile_rows(patch, de[n], lane));
+        }
     }
     __syncthreads();                 // dX complete
     // T1 = dX X^T   (rows t, this wave's two column blocks s), stored transposed
@@ -1676,12 +1732,16 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
                     acc[n] = MM::mma(ax, MM::load(sT1t + 16 * (2 * hf + n) * LC + ks * KB, LC, lane), acc[n]);
         }
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < 2; ++n) {
+            f32x4 m;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int t = t0 + 4 * gq + x, s_ = 16 * (2 * hf + n) + cl;
-                ws[a.L.dM + cc + (size_t)t * C + s_] = s_ < t ? -acc[n][x] : 0.f;
+                m[x] = s_ < t ? -acc[n][x] : 0.f;
             }
+            st4s(ws + a.L.dM + cc + (size_t)(t0 + (lane >> 2)) * C + 16 * (2 * hf + n) + 4 * (lane & 3),
+                 tile_rows(patch, m, lane));
+        }
     }
 }
 
@@ -2244,6 +2304,19 @@ hipError_t zero_fill(float* p, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
+// bwd_prep for one gate-width mix (more than 64 KiB of dynamic LDS must be
+// requested per kernel)
+template <typename E, int D, int MIX>
+hipError_t launch_prep(int64_t grid, size_t lds, hipStream_t s, const BwdArgs& a)
+{
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_prep_kernel<E, D, MIX>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D, MIX>), dim3((unsigned)grid), dim3(NTP), lds, s, a);
+    return hipGetLastError();
+}
+
 template <typename E, int D>
 hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
 {
@@ -2266,9 +2339,7 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     const size_t lds_prep = BwdPrepShape<D>::SMEM;
     const size_t lds_decay = (size_t)(2 * C * LPC + 5 * C * LC + DC) * 4;
     // more than 64 KiB of dynamic LDS must be requested per kernel
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_prep_kernel<E, D>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_prep)) != hipSuccess ||
-        (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_decay_kernel<E, D>),
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_decay_kernel<E, D>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_decay)) != hipSuccess)
         return e;
     if constexpr (sizeof(E) == 2) {
@@ -2282,8 +2353,21 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
             return e;
     }
 
-    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)nrec), dim3(NTP), lds_prep, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        // persistent, one workgroup per compute unit (its LDS allows no more)
+        const int64_t grid = std::min<int64_t>(nrec, (int64_t)device_cu_count());
+        switch ((a.bw == 1 ? 4 : 0) | (a.ww == 1 ? 2 : 0) | (a.gw == 1 ? 1 : 0)) {
+        case 0: e = launch_prep<E, D, 0>(grid, lds_prep, s, a); break;
+        case 1: e = launch_prep<E, D, 1>(grid, lds_prep, s, a); break;
+        case 2: e = launch_prep<E, D, 2>(grid, lds_prep, s, a); break;
+        case 3: e = launch_prep<E, D, 3>(grid, lds_prep, s, a); break;
+        case 4: e = launch_prep<E, D, 4>(grid, lds_prep, s, a); break;
+        case 5: e = launch_prep<E, D, 5>(grid, lds_prep, s, a); break;
+        case 6: e = launch_prep<E, D, 6>(grid, lds_prep, s, a); break;
+        default: e = launch_prep<E, D, 7>(grid, lds_prep, s, a); break;
+        }
+        if (e != hipSuccess) return e;
+    }
     if constexpr (sizeof(E) == 4) {   // the fp32 state products read dO as zero-padded records
         hipLaunchKernelGGL((bwd_dout_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2303,7 +2387,9 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     if constexpr (sizeof(E) == 2) {
-        hipLaunchKernelGGL((bwd_sgrad_bf16_kernel<D>), dim3((unsigned)nrec), dim3(SgradShape<D>::NTH),
+        // persistent, one workgroup per compute unit (its LDS allows no more)
+        const int64_t grid = std::min<int64_t>(nrec, (int64_t)device_cu_count());
+        hipLaunchKernelGGL((bwd_sgrad_bf16_kernel<D>), dim3((unsigned)grid), dim3(SgradShape<D>::NTH),
                            SgradShape<D>::SMEM, s, a);
     } else {
         hipLaunchKernelGGL((bwd_sgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
