@@ -82,21 +82,26 @@ struct BwdLayout {
 
 constexpr int DC = 32;                 // channels per decay workgroup
 
-BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, int64_t nseg, bool narrow)
+// fp32 inputs (wide) run the chained-tile state and WY-factor kernels
+// through Delta, dU, dE~, dO, dX and the product T1 in memory; for bf16
+// inputs the fused kernels keep them on chip (dU and dE~ are formed in
+// bwd_decay) and those arrays are absent (their offsets are 0, never used).
+BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, int64_t nseg, bool narrow, bool wide)
 {
     BwdLayout L;
     L.nrec = B * H * cdiv(T, BC);
     const size_t cd = a64((size_t)L.nrec * BC * D), cc = a64((size_t)L.nrec * BC * BC);
     const size_t dd = a64((size_t)L.nrec * D * D), d1 = a64((size_t)L.nrec * D);
     size_t o = 0;
-    size_t* cds[] = {&L.G, &L.U, &L.Et, &L.W, &L.Ut, &L.Del, &L.dDel, &L.dQt, &L.dKh, &L.dW, &L.dU, &L.dEt, &L.dO};
-    for (size_t* p : cds) {
-        *p = o;
+    L.Del = L.dU = L.dEt = L.dO = L.dX = L.T1 = 0;
+    size_t* cds[] = {&L.G, &L.U, &L.Et, &L.W, &L.Ut, &L.dDel, &L.dQt, &L.dKh, &L.dW, &L.Del, &L.dU, &L.dEt, &L.dO};
+    for (int x = 0; x < (wide ? 13 : 9); ++x) {
+        *cds[x] = o;
         o += cd;
     }
-    size_t* ccs[] = {&L.X, &L.dP, &L.dX, &L.T1, &L.dM};
-    for (size_t* p : ccs) {
-        *p = o;
+    size_t* ccs[] = {&L.X, &L.dP, &L.dM, &L.dX, &L.T1};
+    for (int x = 0; x < (wide ? 5 : 3); ++x) {
+        *ccs[x] = o;
         o += cc;
     }
     L.gam = o;
@@ -1588,16 +1593,16 @@ __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
     gemm_tile<Mma<E>>(sA, sB, 0, 0, C, Xt, T1, 0, none, none, ws + a.L.dM + cc, C, -1.f, 0.f, nullptr, 2);
 }
 
-// bf16 inputs: the WY-factor products of one chunk with every operand read
-// from memory once and dX, T1 kept on chip.  Eight waves: wave w owns the
-// rows 16 (w % 4).. and half the output columns of every product.  Staged in
-// LDS in bf16 (the precision of every MFMA operand here): X and X^T, dDelta^T
-// and dW^T, U and E~, then dX and T1^T.
+// bf16 inputs: dM of one chunk with every operand read from memory once and
+// dX, T1 kept on chip (dU = X^T dDelta and dE~ = X^T dW are formed where
+// they are used, in bwd_decay).  Eight waves: wave w owns the rows
+// 16 (w % 4).. and half the output columns of every product.  Staged in LDS
+// in bf16 (the precision of every MFMA operand here): X and X^T, U and E~,
+// then dX and T1^T.
 template <int D>
 struct XgradShape {
     static constexpr int C = BC, LC = C + 8, LDd = D + 8;   // bf16 rows padded by 16 bytes
-    static constexpr size_t X_OFF = 0, XT_OFF = X_OFF + (size_t)C * LC, DDT_OFF = XT_OFF + (size_t)C * LC,
-                            DWT_OFF = DDT_OFF + (size_t)D * LC, U_OFF = DWT_OFF + (size_t)D * LC,
+    static constexpr size_t X_OFF = 0, XT_OFF = X_OFF + (size_t)C * LC, U_OFF = XT_OFF + (size_t)C * LC,
                             ET_OFF = U_OFF + (size_t)C * LDd, DX_OFF = ET_OFF + (size_t)C * LDd,
                             T1T_OFF = DX_OFF + (size_t)C * LC, ELEMS = T1T_OFF + (size_t)C * LC;
     static constexpr int NTH = 2 * 64 * (C / 16);
@@ -1616,8 +1621,6 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
     extern __shared__ __align__(16) bf16 sx[];
     bf16* sX = sx + SH::X_OFF;       // X[t][s]
     bf16* sXt = sx + SH::XT_OFF;     // X^T[s][t]
-    bf16* sDdT = sx + SH::DDT_OFF;   // dDelta^T[j][t]
-    bf16* sDwT = sx + SH::DWT_OFF;   // dW^T[i][t]
     bf16* sU = sx + SH::U_OFF;       // U[s][j]
     bf16* sEt = sx + SH::ET_OFF;     // E~[s][i]
     bf16* sdX = sx + SH::DX_OFF;     // dX[t][u]
@@ -1646,13 +1649,6 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
     for (int e = tid; e < C * D / 4; e += NTH) {
         const int t = e / (D / 4), j = 4 * (e % (D / 4));
         const size_t o = cd + (size_t)t * D + j;
-        const bf16x4 d4 = *(reinterpret_cast<const bf16x4*>(ws + a.L.dDel) + o / 4);
-        const bf16x4 w4 = *(reinterpret_cast<const bf16x4*>(ws + a.L.dW) + o / 4);
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            sDdT[(j + y) * LC + t] = d4[y];
-            sDwT[(j + y) * LC + t] = w4[y];
-        }
         *reinterpret_cast<bf16x4*>(sU + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.U) + o / 4);
         *reinterpret_cast<bf16x4*>(sEt + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.Et) + o / 4);
     }
@@ -1677,30 +1673,6 @@ __global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdA
 #pragma unroll
             for (int x = 0; x < 4; ++x)
                 sdX[(t0 + 4 * gq + x) * LC + 16 * (2 * hf + n) + cl] = (bf16)acc[n][x];
-    }
-    // dU = X^T dDelta,  dE~ = X^T dW   (rows s = 16 rw.., this wave's half of the columns)
-    {
-        constexpr int NH = D / 32;
-        f32x4 du[NH], de[NH];
-#pragma unroll
-        for (int n = 0; n < NH; ++n)
-            du[n] = de[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C / KB; ++ks) {
-            const Frag ax = MM::load(sXt + t0 * LC + ks * KB, LC, lane);
-#pragma unroll
-            for (int n = 0; n < NH; ++n) {
-                const int jb = hf * NH + n;
-                du[n] = MM::mma(ax, MM::load(sDdT + 16 * jb * LC + ks * KB, LC, lane), du[n]);
-                de[n] = MM::mma(ax, MM::load(sDwT + 16 * jb * LC + ks * KB, LC, lane), de[n]);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NH; ++n) {
-            const size_t o = cd + (size_t)(t0 + (lane >> 2)) * D + 16 * (hf * NH + n) + 4 * (lane & 3);
-            st4s(ws + a.L.dU + o, tile_rows(patch, du[n], lane));
-            st4s(ws + a.L.dEt + o, tile_rows(patch, de[n], lane));
-        }
     }
     __syncthreads();                 // dX complete
     // T1 = dX X^T   (rows t, this wave's two column blocks s), stored transposed
@@ -1799,10 +1771,12 @@ __device__ __forceinline__ void decay_loads(const BwdArgs& a, const Rec& rc, int
             xrk[p] = ws[a.L.RN + (size_t)r * 2 * C + t];
             xrq[p] = ws[a.L.RN + (size_t)r * 2 * C + C + t];
         }
-        xdEt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
+        if constexpr (sizeof(E) == 4) {   // bf16: formed in the decay kernel (decay_wy_slices)
+            xdEt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dEt + x);
+            xdU[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
+        }
         xdQt[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dQt + x);
         xdKh[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dKh + x);
-        xdU[p] = *reinterpret_cast<const f32x4*>(ws + a.L.dU + x);
         xG[p] = *reinterpret_cast<const f32x4*>(ws + a.L.G + x);
     }
 #pragma unroll
@@ -1818,6 +1792,96 @@ __device__ __forceinline__ void decay_loads(const BwdArgs& a, const Rec& rc, int
         if (!valid)
             xrk[p] = xrq[p] = 1.f;
     }
+}
+
+// bf16 inputs: dU = X^T dDelta and dE~ = X^T dW on a decay workgroup's DC
+// channels (X = (I + M)^-1; bwd_xgrad forms only dM), straight into the
+// thread's items (token t, 4 channels) as the decay kernel uses them.  Four
+// waves; wave w owns the token rows 16w..  X^T and the group's columns of
+// dDelta and dW are staged in LDS transposed, in bf16 (the MFMA operands'
+// precision), in the area the decay kernel fills only afterwards.
+template <int D>
+struct DecayWY {
+    static constexpr int C = BC, LX = C + 8;                 // bf16 rows padded by 16 bytes
+    static constexpr size_t XT = 0, DDT = XT + (size_t)C * LX, DWT = DDT + (size_t)DC * LX,
+                            END = DWT + (size_t)DC * LX;     // bf16 elements
+    static constexpr size_t OU = (END * 2 + 15) / 16 * 4;   // float offset of the dU, dE~ outputs [C][LC]
+    static constexpr size_t BYTES = OU * 4 + 2 * (size_t)C * LC * 4;
+};
+
+template <int D, int NIT>
+__device__ __forceinline__ void decay_wy_slices(const BwdArgs& a, int64_t r, int i0, int tid, float* scratch,
+                                                f32x4* xdEt, f32x4* xdU)
+{
+    typedef DecayWY<D> WY;
+    typedef Mma<bf16> MM;
+    typedef MM::Frag Frag;
+    constexpr int C = BC, LX = WY::LX, KB = MM::KB, NJ = DC / 16;
+    static_assert(NTB == 256 && C == 64 && DC == 32, "four waves, one 16-token block each; 4x4 staging blocks");
+    bf16* sx = reinterpret_cast<bf16*>(scratch);
+    bf16* sXt = sx + WY::XT;       // X^T[s][t]
+    bf16* sDdT = sx + WY::DDT;     // dDelta^T[j][t], the group's channels j
+    bf16* sDwT = sx + WY::DWT;     // dW^T[i][t]
+    float* sOU = scratch + WY::OU; // dU[t][j], the group's channels
+    float* sOE = sOU + C * LC;     // dE~[t][i]
+    const float* ws = a.ws;
+    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
+    const float* Xg = ws + a.L.X + cc;
+    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd;
+    const bf16* dW = reinterpret_cast<const bf16*>(ws + a.L.dW) + cd;
+    const int lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15, t0 = 16 * wave;
+
+    // X^T: one 4x4 block of X per thread (rows 4bi.., columns 4bj..),
+    // transposed in registers.  dDelta^T (threads 0-127) and dW^T (128-255):
+    // one 4x4 block each, tokens 4ti.., the group's channels 4jj..
+    {
+        const int bi = tid >> 4, bj = tid & 15;
+        const int half = tid >> 7, e = tid & 127, ti = e >> 3, jj = e & 7;
+        const bf16* src = half ? dW : dDel;
+        f32x4 x4[4];
+        bf16x4 d4[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            x4[y] = *reinterpret_cast<const f32x4*>(Xg + (4 * bi + y) * C + 4 * bj);
+            d4[y] = *reinterpret_cast<const bf16x4*>(src + (size_t)(4 * ti + y) * D + i0 + 4 * jj);
+        }
+        bf16* dst = half ? sDwT : sDdT;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            *reinterpret_cast<bf16x4*>(sXt + (4 * bj + x) * LX + 4 * bi) =
+                bf16x4{(bf16)x4[0][x], (bf16)x4[1][x], (bf16)x4[2][x], (bf16)x4[3][x]};
+            *reinterpret_cast<bf16x4*>(dst + (4 * jj + x) * LX + 4 * ti) = bf16x4{d4[0][x], d4[1][x], d4[2][x], d4[3][x]};
+        }
+    }
+    lds_barrier();
+    f32x4 au[NJ], ae[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+        au[jt] = ae[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C / KB; ++ks) {
+        const Frag fx = MM::load(sXt + t0 * LX + ks * KB, LX, lane);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            au[jt] = MM::mma(fx, MM::load(sDdT + 16 * jt * LX + ks * KB, LX, lane), au[jt]);
+            ae[jt] = MM::mma(fx, MM::load(sDwT + 16 * jt * LX + ks * KB, LX, lane), ae[jt]);
+        }
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            sOU[(t0 + 4 * gq + x) * LC + 16 * jt + cl] = au[jt][x];
+            sOE[(t0 + 4 * gq + x) * LC + 16 * jt + cl] = ae[jt][x];
+        }
+    lds_barrier();
+#pragma unroll
+    for (int p = 0; p < NIT; ++p) {
+        const int e4 = tid + p * NTB, t = e4 / (DC / 4), c = 4 * (e4 % (DC / 4)), l = t * LC + c;
+        xdU[p] = f32x4{sOU[l], sOU[l + 1], sOU[l + 2], sOU[l + 3]};
+        xdEt[p] = f32x4{sOE[l], sOE[l + 1], sOE[l + 2], sOE[l + 3]};
+    }
+    lds_barrier();                       // the scratch is free for the row arrays
 }
 
 template <typename E, int D>
@@ -1876,6 +1940,20 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
     case 2: decay_loads<true, false, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq, xG); break;
     default: decay_loads<true, true, E, D, NIT>(a, rc, r, tid, i0, xk, xq, xb, xw, xv, xdEt, xdQt, xdKh, xdU, xrk, xrq, xG); break;
     }
+    // dM, dP loads in flight before any LDS use
+    constexpr int NMP = C * C / 4 / NTB;
+    static_assert(C * C / 4 % NTB == 0, "whole items per thread");
+    f32x4 rM[NMP], rP[NMP];
+#pragma unroll
+    for (int it = 0; it < NMP; ++it) {
+        const int e = tid + it * NTB, t = e / (C / 4), c = 4 * (e % (C / 4));
+        rM[it] = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
+        rP[it] = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
+    }
+    if constexpr (sizeof(E) == 2) {
+        static_assert(DecayWY<D>::BYTES <= (size_t)(2 * C * LPC + 5 * C * LC + DC) * 4, "the scratch fits");
+        decay_wy_slices<D, NIT>(a, r, i0, tid, sm, xdEt, xdU);
+    }
 #pragma unroll
     for (int p = 0; p < NIT; ++p) {
         // k, q normalised and b activated under the prologue; e = b k as
@@ -1896,23 +1974,11 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
             sdG[l + j] = xdKh[p][j];     // for dG_L below (sdG is free until the main loop)
         }
     }
-    {
-        // dM, dP: every load in flight before the first LDS write
-        constexpr int NMP = C * C / 4 / NTB;
-        static_assert(C * C / 4 % NTB == 0, "whole items per thread");
-        f32x4 rM[NMP], rP[NMP];
 #pragma unroll
-        for (int it = 0; it < NMP; ++it) {
-            const int e = tid + it * NTB, t = e / (C / 4), c = 4 * (e % (C / 4));
-            rM[it] = *reinterpret_cast<const f32x4*>(ws + a.L.dM + cco + t * C + c);
-            rP[it] = *reinterpret_cast<const f32x4*>(ws + a.L.dP + cco + t * C + c);
-        }
-#pragma unroll
-        for (int it = 0; it < NMP; ++it) {
-            const int e = tid + it * NTB, t = e / (C / 4), c = 4 * (e % (C / 4));
-            *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = rM[it];
-            *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = rP[it];
-        }
+    for (int it = 0; it < NMP; ++it) {
+        const int e = tid + it * NTB, t = e / (C / 4), c = 4 * (e % (C / 4));
+        *reinterpret_cast<f32x4*>(sdM + t * LPC + c) = rM[it];
+        *reinterpret_cast<f32x4*>(sdP + t * LPC + c) = rP[it];
     }
     lds_barrier();
     // dG_L = sum_s dK^ K^ + dgamma gamma, with dgamma = rowsum(S * Lam) and
@@ -2330,7 +2396,7 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
     a.nbh = x.B * x.H;
     segment_plan(x.algo, a.NC, a.nbh * ScanShape<E, D>::NS, &a.nseg, &a.seg_len);
     const bool narrow = a.bw == 1 || a.ww == 1 || a.gw == 1;
-    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC, a.nseg, narrow);
+    a.L = bwd_layout(x.B, x.H, x.T, D, ScanFrags<E, D>::REC, a.nseg, narrow, sizeof(E) == 4);
     a.nrec = a.L.nrec;
     a.ws = static_cast<float*>(x.workspace);
     const int64_t nrec = a.nrec, rows = x.B * x.T * x.H;
@@ -2429,7 +2495,7 @@ size_t backward_workspace_bytes(const gdr2_bwd_args& a)
     int64_t nseg, len;
     segment_plan(a.algo, cdiv(a.T, BC), a.B * a.H * (a.Dk / 64), &nseg, &len);
     const bool narrow = a.b_width == 1 || a.w_width == 1 || a.g_width == 1;
-    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec, nseg, narrow).total;
+    return bwd_layout(a.B, a.H, a.T, (int)a.Dk, rec, nseg, narrow, esz == 4).total;
 }
 
 hipError_t launch_backward(const gdr2_bwd_args& a, hipStream_t stream)
