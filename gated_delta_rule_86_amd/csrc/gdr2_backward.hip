@@ -1345,21 +1345,33 @@ __device__ __forceinline__ f32x4 tile_rows(float* patch, f32x4 acc, int lane)
 
 // bf16 inputs: the same state products with every operand read from memory
 // once (the tile version above re-reads S, W, dO and Delta from memory for
-// each product, since a chunk's operands do not stay in cache).  CG waves per
-// 16 token rows: wave w owns the rows 16 (w % 4).. and a 1/CG share of the
-// output columns of every product; its row operands W, dO and dDelta come straight from memory
-// as A fragments; S (as S and S^T), Lam and Delta are staged in LDS in bf16,
-// the precision of every MFMA operand here.  Delta never leaves the
-// workgroup.
+// each product, since a chunk's operands do not stay in cache), and then the
+// WY-factor product dM that bwd_xgrad forms for fp32 inputs:
+//   dX = dDelta U^T + dW E~^T,  T1 = dX X^T,  dM = strict_tril(-X^T T1)
+// with dW, dX and T1 kept on chip (dU = X^T dDelta and dE~ = X^T dW are
+// formed where they are used, in bwd_decay).  CG waves per 16 token rows:
+// wave w owns the rows 16 (w % 4).. and a 1/CG share of the output columns
+// of every product; its row operands W, dO and dDelta come straight from
+// memory as A fragments; S (as S and S^T), Lam and Delta are staged in LDS
+// in bf16, the precision of every MFMA operand here, and afterwards, in the
+// same area, X and X^T, U, E~, the dW rows, dX and T1^T.  Delta never
+// leaves the workgroup.
 template <int D>
 struct SgradShape {
     static constexpr int C = BC, LDB = D + 8;   // bf16 rows padded by 16 bytes: conflict-free fragment reads
     static constexpr int LDG = D / 4 + 1;         // fp32 row of the dgamma partial sums
     static constexpr size_t S_OFF = 0, ST_OFF = S_OFF + (size_t)D * LDB, L_OFF = ST_OFF + (size_t)D * LDB,
                             DEL_OFF = L_OFF + (size_t)D * LDB, ELEMS = DEL_OFF + (size_t)C * LDB;
+    static constexpr int LX = C + 8;
+    static constexpr size_t X_OFF = 0, XT_OFF = X_OFF + (size_t)C * LX, U_OFF = XT_OFF + (size_t)C * LX,
+                            ET_OFF = U_OFF + (size_t)C * LDB, DW_OFF = ET_OFF + (size_t)C * LDB,
+                            DX_OFF = DW_OFF + (size_t)C * LDB, T1T_OFF = DX_OFF + (size_t)C * LX,
+                            X_END = T1T_OFF + (size_t)C * LX;
+    static constexpr size_t AREA = ELEMS > X_END ? ELEMS : X_END;   // bf16 elements of the staging area
     static constexpr int CG = 2;                     // waves (column groups) per 16 token rows
     static constexpr int NTH = CG * 64 * (C / 16);   // threads
-    static constexpr size_t PATCH_OFF = ELEMS * 2 + (size_t)D * LDG * 4;   // bytes: per-wave output patches
+    static constexpr size_t PG_OFF = AREA * 2;       // bytes: the dgamma partial sums
+    static constexpr size_t PATCH_OFF = PG_OFF + (size_t)D * LDG * 4;   // bytes: per-wave output patches
     static constexpr size_t SMEM = PATCH_OFF + (size_t)(NTH / 64) * PATCH_FLOATS * 4;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert((D / 16) % CG == 0 && (C / 16) % CG == 0, "whole tiles per column group");
@@ -1377,9 +1389,17 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     bf16* sSt = sb + SH::ST_OFF;     // S^T[j][i]
     bf16* sL = sb + SH::L_OFF;       // Lam[i][j]
     bf16* sDel = sb + SH::DEL_OFF;   // Delta[t][j]
-    float* sPg = reinterpret_cast<float*>(sb + SH::ELEMS);   // [D][LDG] partial sums of dgamma
+    float* sPg = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sb) + SH::PG_OFF);   // [D][LDG] partial sums of dgamma
+    // after the state products: the dM operands
+    bf16* sX = sb + SH::X_OFF;       // X[t][s]
+    bf16* sXt = sb + SH::XT_OFF;     // X^T[s][t]
+    bf16* sU = sb + SH::U_OFF;       // U[s][j]
+    bf16* sEt = sb + SH::ET_OFF;     // E~[s][i]
+    bf16* sDW = sb + SH::DW_OFF;     // dW[t][i]
+    bf16* sdX = sb + SH::DX_OFF;     // dX[t][u]
+    bf16* sT1t = sb + SH::T1T_OFF;   // T1^T[s][u]
     float* ws = a.ws;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int tid0 = threadIdx.x, wave = tid0 >> 6;
     float* patch = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sb) + SH::PATCH_OFF) + wave * PATCH_FLOATS;
     const int rw = wave & 3, t0 = 16 * rw, n0 = (wave >> 2) * NH;   // row block; first of its NH column tiles
     // S and Lam of a record as rows of 4 (item e: row e / (D/4), columns
@@ -1392,7 +1412,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         const float* Lam = ws + a.L.Lam + (size_t)rr * D * D;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+            const int e = tid0 + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
             s4r[it] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
             l4r[it] = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
         }
@@ -1406,6 +1426,12 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     // for a load from also waiting for every later one.
     load_sl(blockIdx.x);
     for (int64_t r = blockIdx.x; r < a.nrec; r += gridDim.x) {
+        // the lane index, opaque to the compiler in each iteration: no LDS
+        // or memory address derived from it is hoisted out of the loop to
+        // occupy a register throughout
+        int lane = tid0 & 63;
+        __asm__ __volatile__("" : "+v"(lane));
+        const int tid = 64 * wave + lane, gq = lane >> 4, cl = lane & 15;
         const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
         const bf16* W = reinterpret_cast<const bf16*>(ws + a.L.W) + cd + (size_t)t0 * D;
         const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd + (size_t)t0 * D;
@@ -1494,9 +1520,11 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
                     sDel[(t0 + 4 * gq + x) * LDB + 16 * (n0 + nt) + cl] = (bf16)dl;
                 }
         }
-        // dQ~ = dO S^T,  dW = -dDelta S^T   (k = j: B fragments from S)
+        // dQ~ = dO S^T,  dW = -dDelta S^T   (k = j: B fragments from S); the
+        // dW tiles stay in registers for the dM phase
+        f32x4 w[NH];
         {
-            f32x4 q[NH], w[NH];
+            f32x4 q[NH];
 #pragma unroll
             for (int nt = 0; nt < NH; ++nt)
                 q[nt] = w[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1564,6 +1592,112 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
                      tile_rows(patch, m, lane));
             }
         }
+
+        // the dM phase's operands from memory:
+        // X rows (fp32), U and E~ rows (bf16), 4 elements per item
+        constexpr int NXI = C * C / 4 / NTH, NUI = C * D / 4 / NTH;
+        static_assert(C * C / 4 % NTH == 0 && C * D / 4 % NTH == 0, "whole items per thread");
+        f32x4 xr[NXI];
+        bf16x4 ur[NUI], er[NUI];
+        {
+            const float* Xg = ws + a.L.X + cc;
+            const bf16x4* Ug = reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(ws + a.L.U) + cd);
+            const bf16x4* Eg = reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(ws + a.L.Et) + cd);
+#pragma unroll
+            for (int it = 0; it < NXI; ++it)
+                xr[it] = *reinterpret_cast<const f32x4*>(Xg + 4 * (tid + it * NTH));
+#pragma unroll
+            for (int it = 0; it < NUI; ++it) {
+                ur[it] = Ug[tid + it * NTH];
+                er[it] = Eg[tid + it * NTH];
+            }
+        }
+        // dM = strict_tril(-X^T T1), T1 = dX X^T, dX = dDelta U^T + dW E~^T,
+        // in the staging area once every wave is done with S, Lam and Delta
+        constexpr int LX = SH::LX, KB = MM::KB;
+        const int hf = wave >> 2;        // this wave's column blocks 2 hf, 2 hf + 1 of the C x C products
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < NXI; ++it) {
+            const int e = tid + it * NTH, t = e / (C / 4), c = 4 * (e % (C / 4));
+            bf16x4 xv;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                xv[y] = (bf16)xr[it][y];
+                sXt[(c + y) * LX + t] = xv[y];
+            }
+            *reinterpret_cast<bf16x4*>(sX + t * LX + c) = xv;
+        }
+#pragma unroll
+        for (int it = 0; it < NUI; ++it) {
+            const int e = tid + it * NTH, t = e / (D / 4), j = 4 * (e % (D / 4));
+            *reinterpret_cast<bf16x4*>(sU + t * LDB + j) = ur[it];
+            *reinterpret_cast<bf16x4*>(sEt + t * LDB + j) = er[it];
+        }
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                sDW[(t0 + 4 * gq + x) * LDB + 16 * (n0 + nt) + cl] = (bf16)(-w[nt][x]);
+        lds_barrier();
+        {
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const Frag ad = MM::load(dDel + ks * KB, D, lane);     // this wave's dDelta rows again (L2)
+                const Frag aw = MM::load(sDW + t0 * LDB + ks * KB, LDB, lane);
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int sbk = 2 * hf + n;
+                    acc[n] = MM::mma(ad, MM::load(sU + 16 * sbk * LDB + ks * KB, LDB, lane), acc[n]);
+                    acc[n] = MM::mma(aw, MM::load(sEt + 16 * sbk * LDB + ks * KB, LDB, lane), acc[n]);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    sdX[(t0 + 4 * gq + x) * LX + 16 * (2 * hf + n) + cl] = (bf16)acc[n][x];
+        }
+        lds_barrier();                   // dX complete
+        {
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < C / KB; ++ks) {
+                const Frag ad = MM::load(sdX + t0 * LX + ks * KB, LX, lane);
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    acc[n] = MM::mma(ad, MM::load(sX + 16 * (2 * hf + n) * LX + ks * KB, LX, lane), acc[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    sT1t[(16 * (2 * hf + n) + cl) * LX + t0 + 4 * gq + x] = (bf16)acc[n][x];
+        }
+        lds_barrier();                   // T1 complete
+        {
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < C / KB; ++ks) {
+                const Frag ax = MM::load(sXt + t0 * LX + ks * KB, LX, lane);
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    if (2 * hf + n <= rw)
+                        acc[n] = MM::mma(ax, MM::load(sT1t + 16 * (2 * hf + n) * LX + ks * KB, LX, lane), acc[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                f32x4 m;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int t = t0 + 4 * gq + x, s_ = 16 * (2 * hf + n) + cl;
+                    m[x] = s_ < t ? -acc[n][x] : 0.f;
+                }
+                st4s(ws + a.L.dM + cc + (size_t)(t0 + (lane >> 2)) * C + 16 * (2 * hf + n) + 4 * (lane & 3),
+                     tile_rows(patch, m, lane));
+            }
+        }
     }
 }
 
@@ -1591,130 +1725,6 @@ __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
     gemm_tile<Mma<E>>(sA, sB, 0, 0, C, dX, Xt, 0, none, none, ws + a.L.T1 + cc, C, 1.f, 0.f, nullptr, 0);
     tile_done();                        // T1 complete
     gemm_tile<Mma<E>>(sA, sB, 0, 0, C, Xt, T1, 0, none, none, ws + a.L.dM + cc, C, -1.f, 0.f, nullptr, 2);
-}
-
-// bf16 inputs: dM of one chunk with every operand read from memory once and
-// dX, T1 kept on chip (dU = X^T dDelta and dE~ = X^T dW are formed where
-// they are used, in bwd_decay).  Eight waves: wave w owns the rows
-// 16 (w % 4).. and half the output columns of every product.  Staged in LDS
-// in bf16 (the precision of every MFMA operand here): X and X^T, U and E~,
-// then dX and T1^T.
-template <int D>
-struct XgradShape {
-    static constexpr int C = BC, LC = C + 8, LDd = D + 8;   // bf16 rows padded by 16 bytes
-    static constexpr size_t X_OFF = 0, XT_OFF = X_OFF + (size_t)C * LC, U_OFF = XT_OFF + (size_t)C * LC,
-                            ET_OFF = U_OFF + (size_t)C * LDd, DX_OFF = ET_OFF + (size_t)C * LDd,
-                            T1T_OFF = DX_OFF + (size_t)C * LC, ELEMS = T1T_OFF + (size_t)C * LC;
-    static constexpr int NTH = 2 * 64 * (C / 16);
-    static constexpr size_t PATCH_OFF = ELEMS * 2;   // bytes: per-wave output patches
-    static constexpr size_t SMEM = PATCH_OFF + (size_t)(NTH / 64) * PATCH_FLOATS * 4;
-    static_assert(SMEM <= 160 * 1024, "LDS budget");
-};
-
-template <int D>
-__global__ __launch_bounds__(XgradShape<D>::NTH) void bwd_xgrad_bf16_kernel(BwdArgs a)
-{
-    typedef XgradShape<D> SH;
-    typedef Mma<bf16> MM;
-    typedef MM::Frag Frag;
-    constexpr int C = BC, LC = SH::LC, LDd = SH::LDd, KB = MM::KB, NTH = SH::NTH;
-    extern __shared__ __align__(16) bf16 sx[];
-    bf16* sX = sx + SH::X_OFF;       // X[t][s]
-    bf16* sXt = sx + SH::XT_OFF;     // X^T[s][t]
-    bf16* sU = sx + SH::U_OFF;       // U[s][j]
-    bf16* sEt = sx + SH::ET_OFF;     // E~[s][i]
-    bf16* sdX = sx + SH::DX_OFF;     // dX[t][u]
-    bf16* sT1t = sx + SH::T1T_OFF;   // T1^T[s][u]
-    const int64_t r = blockIdx.x;
-    float* ws = a.ws;
-    const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
-    const int rw = wave & 3, hf = wave >> 2, t0 = 16 * rw;
-    float* patch = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sx) + SH::PATCH_OFF) + wave * PATCH_FLOATS;
-    const float* Xg = ws + a.L.X + cc;
-    const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd;
-    const bf16* dW = reinterpret_cast<const bf16*>(ws + a.L.dW) + cd;
-
-    for (int e = tid; e < C * C / 4; e += NTH) {
-        const int t = e / (C / 4), c = 4 * (e % (C / 4));
-        const f32x4 x4 = *reinterpret_cast<const f32x4*>(Xg + t * C + c);
-        bf16x4 xv;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            xv[y] = (bf16)x4[y];
-            sXt[(c + y) * LC + t] = xv[y];
-        }
-        *reinterpret_cast<bf16x4*>(sX + t * LC + c) = xv;
-    }
-    for (int e = tid; e < C * D / 4; e += NTH) {
-        const int t = e / (D / 4), j = 4 * (e % (D / 4));
-        const size_t o = cd + (size_t)t * D + j;
-        *reinterpret_cast<bf16x4*>(sU + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.U) + o / 4);
-        *reinterpret_cast<bf16x4*>(sEt + t * LDd + j) = *(reinterpret_cast<const bf16x4*>(ws + a.L.Et) + o / 4);
-    }
-    __syncthreads();
-
-    // dX = dDelta U^T + dW E~^T   (rows t, this wave's two column blocks s)
-    {
-        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < D / KB; ++ks) {
-            const Frag ad = MM::load(dDel + (size_t)t0 * D + ks * KB, D, lane);
-            const Frag aw = MM::load(dW + (size_t)t0 * D + ks * KB, D, lane);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int sb = 2 * hf + n;
-                acc[n] = MM::mma(ad, MM::load(sU + 16 * sb * LDd + ks * KB, LDd, lane), acc[n]);
-                acc[n] = MM::mma(aw, MM::load(sEt + 16 * sb * LDd + ks * KB, LDd, lane), acc[n]);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                sdX[(t0 + 4 * gq + x) * LC + 16 * (2 * hf + n) + cl] = (bf16)acc[n][x];
-    }
-    __syncthreads();                 // dX complete
-    // T1 = dX X^T   (rows t, this wave's two column blocks s), stored transposed
-    {
-        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < C / KB; ++ks) {
-            const Frag ad = MM::load(sdX + t0 * LC + ks * KB, LC, lane);
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                acc[n] = MM::mma(ad, MM::load(sX + 16 * (2 * hf + n) * LC + ks * KB, LC, lane), acc[n]);
-        }
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                sT1t[(16 * (2 * hf + n) + cl) * LC + t0 + 4 * gq + x] = (bf16)acc[n][x];
-    }
-    __syncthreads();                 // T1 complete
-    // dM = strict_tril(-X^T T1)   (rows t, this wave's two column blocks s)
-    {
-        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < C / KB; ++ks) {
-            const Frag ax = MM::load(sXt + t0 * LC + ks * KB, LC, lane);
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                if (2 * hf + n <= rw)
-                    acc[n] = MM::mma(ax, MM::load(sT1t + 16 * (2 * hf + n) * LC + ks * KB, LC, lane), acc[n]);
-        }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            f32x4 m;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int t = t0 + 4 * gq + x, s_ = 16 * (2 * hf + n) + cl;
-                m[x] = s_ < t ? -acc[n][x] : 0.f;
-            }
-            st4s(ws + a.L.dM + cc + (size_t)(t0 + (lane >> 2)) * C + 16 * (2 * hf + n) + 4 * (lane & 3),
-                 tile_rows(patch, m, lane));
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2413,10 +2423,6 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)SgradShape<D>::SMEM)) !=
             hipSuccess)
             return e;
-        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_xgrad_bf16_kernel<D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)XgradShape<D>::SMEM)) !=
-            hipSuccess)
-            return e;
     }
 
     {
@@ -2461,13 +2467,11 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
         hipLaunchKernelGGL((bwd_sgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (sizeof(E) == 2) {
-        hipLaunchKernelGGL((bwd_xgrad_bf16_kernel<D>), dim3((unsigned)nrec), dim3(XgradShape<D>::NTH),
-                           XgradShape<D>::SMEM, s, a);
-    } else {
+    // bf16: dM is formed in bwd_sgrad_bf16, dU and dE~ in bwd_decay
+    if constexpr (sizeof(E) == 4) {
         hipLaunchKernelGGL((bwd_xgrad_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
 
     hipLaunchKernelGGL((bwd_decay_kernel<E, D>), dim3((unsigned)(cdiv(nrec, 8) * 8 * (D / DC))), dim3(NTB), lds_decay, s,
                        a);
