@@ -459,6 +459,10 @@ def main():
     ap.add_argument("--long-only", action="store_true",
                     help="time only the long-context forward and print its JSON object (for a profile of "
                          "those kernels alone)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the training-shape backward (after the forward that records the "
+                         "chunk-start states) and print its JSON object (for a profile of the backward "
+                         "kernels alone)")
     args = ap.parse_args()
     if args.headline_only:
         args.no_decode = args.no_long = args.no_fused = args.no_gate_widths = args.no_backward = True
@@ -484,6 +488,11 @@ def main():
         # the library's default algorithm only, whole calls: one kernel of each kind per call
         res = bench_long(torch, gdr2, lib, args.steps, args.warmup, algos=("auto",), stages=("all",), backward=False)
         print(json.dumps({"long_context": res}), flush=True)
+        return
+    if args.backward_only:
+        wl = WORKLOADS["train_4k"]
+        d = {n: (None if t is None else t.cuda()) for n, t in draw(wl).items()}
+        print(json.dumps({"backward": bench_backward(torch, gdr2, lib, wl, d, args.steps, args.warmup)}), flush=True)
         return
     K = args.steps
     extra = {}
