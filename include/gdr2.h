@@ -235,7 +235,10 @@ typedef struct gdr2_decode_args {
  * No output may overlap any input, another output or the workspace.
  * Supported set: Dk == Dv in {64, 128}; chunk == 64; dtype F32 or BF16;
  * B, T, H >= 0 (T == 0 writes dS_final, or zeros, to dS0).  Anything else
- * returns GDR2_ERR_UNSUPPORTED.  All arithmetic is fp32.
+ * returns GDR2_ERR_UNSUPPORTED.  Accumulation is fp32; with bf16 inputs the
+ * matrix-core operands are bf16, as in the forward.  The result does not
+ * depend on scheduling: every sum runs in a fixed order (no atomics), so a
+ * call repeated on the same arguments gives the same bits.
  */
 typedef struct gdr2_bwd_args {
     int64_t B, T, H, Dk, Dv;
