@@ -18,12 +18,14 @@
 //   and the decayed vectors E~ = E e^G, Q~ = q e^G, K^ = k e^{G_L - G},
 //   gamma = e^{G_L}; dg is the reverse cumulative sum of dG within a chunk.
 //
-// Kernels (all fp32 arithmetic; intermediates in a fp32 workspace, one
-// record per (sequence, head, chunk)):
-//   bwd_prep   one workgroup per chunk: G, U, E~, gamma; M and P as 16x16
-//              blocks through block-referenced rows (fp32 MFMA); X by
-//              blocks; W, U~ (fp32 MFMA); and the scan's K^, P^T, Q~^T,
-//              -W^T operands in MFMA fragment order.
+// Kernels (fp32 accumulation; with bf16 inputs the matrix-core operands are
+// bf16, as in the forward; intermediates in a workspace of one record per
+// (sequence, head, chunk)):
+//   bwd_prep   persistent, one workgroup per CU, a chunk record at a time
+//              (the next record's input rows in flight): G, U, E~, gamma; M
+//              and P as 16x16 blocks through block-referenced rows (fp32
+//              MFMA); X by blocks; W, U~ (fp32 MFMA); and the scan's K^, P^T,
+//              Q~^T, -W^T operands in MFMA fragment order.
 //   bwd_dout   (fp32 inputs) dO rows of every chunk into the workspace (zero
 //              past T); the other kernels read dO from the input.
 //   bwd_frag   the scan's dO^T fragments.
@@ -33,12 +35,17 @@
 //   bwd_scan   per (sequence, head, chunk segment, 64 value columns): the
 //              state gradient through the chunks in reverse (columns evolve
 //              independently), recording Lam at every chunk end and dDelta.
-//   bwd_sgrad, bwd_xgrad  per chunk: the state and WY-factor products
-//              above.  bf16 inputs: every operand read once, staged in LDS
-//              in bf16, intermediates (Delta, dX, T1) kept on chip; fp32
-//              inputs: chained 64x64 fp32 MFMA tiles through memory.
-//   bwd_decay  per chunk and 32 channels: the decay-weighted sums, dG, dg
-//              and the input gradients.
+//   bwd_sgrad  the state products per chunk.  bf16 inputs: persistent, every
+//              operand read once and staged in LDS in bf16, Delta kept on
+//              chip, then dM (the WY-factor product through dX and T1, also
+//              on chip); fp32 inputs: chained 64x64 fp32 MFMA tiles through
+//              memory.
+//   bwd_xgrad  (fp32 inputs) the WY-factor products dU, dE~, dM as chained
+//              tiles; bf16 inputs form dM in bwd_sgrad and dU, dE~ in
+//              bwd_decay.
+//   bwd_decay  per chunk and 32 channels: (bf16) dU and dE~ on its channels,
+//              the decay-weighted sums, dG, dg and the input gradients.
+//   bwd_gate_sum  width-1 gates: the channel groups' partial sums in order.
 //   bwd_norm   the prologue's normalisation, backwards (when asked for).
 #include "gdr2_device.h"
 #include "gdr2_internal.h"
@@ -198,9 +205,10 @@ __device__ __forceinline__ size_t frag_at(int row, int k, int nk)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_prep: one workgroup (NTP threads) per chunk record.
+// bwd_prep: one workgroup (NTP threads) per chunk record at a time
+// (persistent, one workgroup per CU).
 //   1. raw rows into LDS, 4 channels per item; G = cumulative log-decay;
-//      E~, Q~, K^, gamma, U written out (fp32)
+//      G, E~, gamma, U and the K^, Q~^T fragments written out
 //   2. M (strictly lower) and P (lower) by 16x16 token blocks on fp32 MFMA,
 //      through rows re-referenced to their block (every factor <= 1 below
 //      the diagonal, <= e^kDiagSpan on it); steeper diagonal blocks pair by
@@ -1701,8 +1709,8 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     }
 }
 
-// The products through the WY factor X = (I + M)^-1, one workgroup per
-// chunk record:  dX = dDelta U^T + dW E~^T,  dM = strict_tril(-X^T dX X^T),
+// fp32 inputs: the products through the WY factor X = (I + M)^-1, one
+// workgroup per chunk record:  dX = dDelta U^T + dW E~^T,  dM = strict_tril(-X^T dX X^T),
 // dU = X^T dDelta,  dE~ = X^T dW.
 template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_xgrad_kernel(BwdArgs a)
@@ -1805,7 +1813,7 @@ __device__ __forceinline__ void decay_loads(const BwdArgs& a, const Rec& rc, int
 }
 
 // bf16 inputs: dU = X^T dDelta and dE~ = X^T dW on a decay workgroup's DC
-// channels (X = (I + M)^-1; bwd_xgrad forms only dM), straight into the
+// channels (X = (I + M)^-1; bwd_sgrad forms dM), straight into the
 // thread's items (token t, 4 channels) as the decay kernel uses them.  Four
 // waves; wave w owns the token rows 16w..  X^T and the group's columns of
 // dDelta and dW are staged in LDS transposed, in bf16 (the MFMA operands'
