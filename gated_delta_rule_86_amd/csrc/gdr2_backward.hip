@@ -707,11 +707,16 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 float x[16];
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
-                    float acc = rr == cl ? 1.f : 0.f;
+                    // two interleaved partial sums: half the dependent chain
+                    float acc0 = rr == cl ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-                    for (int c = 0; c < rr; ++c)
-                        acc -= m[rr * LDM + c] * x[c];
-                    x[rr] = acc;
+                    for (int c = 0; c + 1 < rr; c += 2) {
+                        acc0 -= m[rr * LDM + c] * x[c];
+                        acc1 -= m[rr * LDM + c + 1] * x[c + 1];
+                    }
+                    if (rr & 1)
+                        acc0 -= m[rr * LDM + rr - 1] * x[rr - 1];
+                    x[rr] = acc0 + acc1;
                 }
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
@@ -720,22 +725,39 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                         sX[(16 * gq + rr) * LDM + 16 * J + cl] = 0.f;
                 }
             }
-            // X_IJ = -X_II sum_{K=J}^{I-1} M_IK X_KJ, one block diagonal at a time
+            lds_fence_wave();
+            // X_IJ = -X_II sum_{K=J}^{I-1} M_IK X_KJ, one block diagonal at a
+            // time, the blocks held in registers: an accumulator tile (rows
+            // 4 gq + i of column cl) is also the B operand of the next
+            // products, so nothing goes through LDS until the end
+            constexpr int NB = C / 16;
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            for (int dg = 1; dg < C / 16; ++dg) {
-                lds_fence_wave();
-                for (int I = dg; I < C / 16; ++I) {
+            f32x4 Xt[NB][NB];
+            MF::Frag xa[NB];                 // X_II as A operands
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                Xt[I][I] = MF::load_kn(sX + 16 * I * LDM + 16 * I, LDM, lane);
+                xa[I] = MF::load(sX + 16 * I * LDM + 16 * I, LDM, lane);
+            }
+#pragma unroll
+            for (int dg = 1; dg < NB; ++dg) {
+#pragma unroll
+                for (int I = dg; I < NB; ++I) {
                     const int J = I - dg;
                     f32x4 y = zero;
-                    for (int K = J; K < I; ++K)
-                        y = MF::mma(MF::load(sM + 16 * I * LDM + 16 * K, LDM, lane),
-                                    MF::load_kn(sX + 16 * K * LDM + 16 * J, LDM, lane), y);
-                    const f32x4 xi = MF::mma(MF::load(sX + 16 * I * LDM + 16 * I, LDM, lane), MF::from_acc(&y), zero);
 #pragma unroll
-                    for (int x4 = 0; x4 < 4; ++x4)
-                        sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = -xi[x4];
+                    for (int K = J; K < I; ++K)
+                        y = MF::mma(MF::load(sM + 16 * I * LDM + 16 * K, LDM, lane), Xt[K][J], y);
+                    Xt[I][J] = -MF::mma(xa[I], MF::from_acc(&y), zero);
                 }
             }
+#pragma unroll
+            for (int I = 1; I < NB; ++I)
+#pragma unroll
+                for (int J = 0; J < I; ++J)
+#pragma unroll
+                    for (int x4 = 0; x4 < 4; ++x4)
+                        sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = Xt[I][J][x4];
         }
         lds_barrier();
         for (int e4 = tid; e4 < C * C / 4; e4 += NTP) {
