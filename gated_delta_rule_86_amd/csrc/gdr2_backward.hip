@@ -263,6 +263,55 @@ __device__ __forceinline__ int lds_barrier_or(int v, int* slots)
 
 __device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// An fp32 product on the bf16 matrix cores in three passes: every operand is
+// split into a bf16 head and a bf16 tail (x = hi + lo up to fp32 rounding,
+// |lo| <= 2^-9 |x|), and a b ~ hi_a hi_b + hi_a lo_b + lo_a hi_b, whose
+// dropped term lo_a lo_b is about 2^-18 of the product: fp32-class accuracy
+// at a fifth of the cycles of the fp32 MFMA (three 16x16x32 bf16 products
+// against eight 16x16x4 fp32 ones per 32 k).
+struct Split {
+    Mma<bf16>::Frag hi, lo;
+};
+__device__ __forceinline__ Split bf_split(f32x4 a, f32x4 b)
+{
+    Split s;
+    s.hi = Mma<bf16>::pack(a, b);
+    f32x4 ra, rb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ra[j] = a[j] - (float)s.hi[j];
+        rb[j] = b[j] - (float)s.hi[4 + j];
+    }
+    s.lo = Mma<bf16>::pack(ra, rb);
+    return s;
+}
+__device__ __forceinline__ f32x4 mma3(const Split& a, const Split& b, f32x4 c)
+{
+    c = Mma<bf16>::mma(a.lo, b.hi, c);
+    c = Mma<bf16>::mma(a.hi, b.lo, c);
+    return Mma<bf16>::mma(a.hi, b.hi, c);
+}
+// The operands in Mma<bf16>'s fragment order from fp32 LDS: rows (lane % 16)
+// at k = 4 (lane / 16).. and 16 + 4 (lane / 16).. (scaled elementwise along k
+// by f[k], f -> k0, when f is given), or a k-major matrix's column lane % 16
+// at those k.
+__device__ __forceinline__ Split split_rows(const float* p, int ld, int lane, const float* f = nullptr)
+{
+    const int c = 4 * (lane >> 4);
+    const float* s = p + (lane & 15) * ld + c;
+    f32x4 a = ld4s(s), b = ld4s(s + 16);
+    if (f) {
+        a = a * ld4s(f + c);
+        b = b * ld4s(f + c + 16);
+    }
+    return bf_split(a, b);
+}
+__device__ __forceinline__ Split split_kn(const float* p, int ld, int lane)
+{
+    const float* s = p + 4 * (lane >> 4) * ld + (lane & 15);
+    return bf_split(f32x4{s[0], s[ld], s[2 * ld], s[3 * ld]}, f32x4{s[16 * ld], s[17 * ld], s[18 * ld], s[19 * ld]});
+}
+
 
 // Prologue activations (logistic sigmoid; log-decay -softplus(x) = log sigmoid(-x)).
 __device__ __forceinline__ float bsigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
@@ -575,9 +624,10 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 sCf[e] = __expf(sG[16 * T * LD + i] - sG[(16 * S + 15) * LD + i]);
             }
             lds_barrier();
-            // 2c. the block products on fp32 MFMA, one wave per block pair (M and
-            // P share the K- fragments); each wave also clears the mirrored block
-            // above the diagonal
+            // 2c. the block products in fp32 precision (fp32 MFMA for fp32
+            // inputs; three-pass bf16 MFMA, mma3, for bf16 inputs), one wave per
+            // block pair (M and P share the K- fragments); each wave also
+            // clears the mirrored block above the diagonal
             {
                 typedef Mma<float> MF;
                 const int wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
@@ -586,11 +636,20 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     const int S = pi < 6 ? pi - (T * (T - 1)) / 2 : T;
                     const float* cf = sCf + pi * D;
                     f32x4 m = {0.f, 0.f, 0.f, 0.f}, p = m;
+                    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+                        for (int k0 = 0; k0 < D; k0 += Mma<bf16>::KB) {
+                            const Split kb = split_rows(sK + 16 * S * LD + k0, LD, lane);
+                            m = mma3(split_rows(sE + 16 * T * LD + k0, LD, lane, cf + k0), kb, m);
+                            p = mma3(split_rows(sQ + 16 * T * LD + k0, LD, lane, cf + k0), kb, p);
+                        }
+                    } else {
 #pragma unroll 4
-                    for (int k0 = 0; k0 < D; k0 += MF::KB) {
-                        const MF::Frag kb = MF::load(sK + 16 * S * LD + k0, LD, lane);
-                        m = MF::mma(MF::load_scaled(sE + 16 * T * LD + k0, LD, cf + k0, lane), kb, m);
-                        p = MF::mma(MF::load_scaled(sQ + 16 * T * LD + k0, LD, cf + k0, lane), kb, p);
+                        for (int k0 = 0; k0 < D; k0 += MF::KB) {
+                            const MF::Frag kb = MF::load(sK + 16 * S * LD + k0, LD, lane);
+                            m = MF::mma(MF::load_scaled(sE + 16 * T * LD + k0, LD, cf + k0, lane), kb, m);
+                            p = MF::mma(MF::load_scaled(sQ + 16 * T * LD + k0, LD, cf + k0, lane), kb, p);
+                        }
                     }
                     f32x4 pv;
 #pragma unroll
@@ -782,9 +841,17 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 const int which = tile / NPER, T = (tile % NPER) / NTD, c = tile % NTD;
                 const float* src = which == 0 ? sE : sU;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int kk = 0; kk <= T; ++kk)
-                    acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
-                                  MF::load_kn(src + 16 * kk * LD + 16 * c, LD, lane), acc);
+                if constexpr (sizeof(E) == 2) {
+                    // three-pass bf16 products, 32 tokens per step (X is zero
+                    // above its diagonal)
+                    for (int k0 = 0; k0 < 16 * (T + 1); k0 += Mma<bf16>::KB)
+                        acc = mma3(split_rows(sX + 16 * T * LDM + k0, LDM, lane), split_kn(src + k0 * LD + 16 * c, LD, lane),
+                                   acc);
+                } else {
+                    for (int kk = 0; kk <= T; ++kk)
+                        acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
+                                      MF::load_kn(src + 16 * kk * LD + 16 * c, LD, lane), acc);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     patch[(4 * gq + i) * LP + cl] = acc[i];
