@@ -67,13 +67,15 @@ struct BwdLayout {
     int64_t nrec;
     // [C][D] per record
     size_t G, U, Et, W, Ut, Del, dDel, dQt, dKh, dW, dU, dEt, dO;
-    // [C][C] per record
+    // [C][C] per record (X in the input dtype: bf16 inputs take it only as
+    // a bf16 matrix-core operand after bwd_prep)
     size_t X, dP, dX, T1, dM;
     // [D] per record
     size_t gam;
     // [2][C] per record: prologue 1/|k|, 1/|q| of every token
     size_t RN;
-    // [D][D] per record: state gradient at every chunk end
+    // [D][D] per record: state gradient at every chunk end, in the input
+    // dtype (bf16 inputs: the precision of every product that takes it)
     size_t Lam;
     // scan operand fragments (ScanFrags), rec_bytes per record
     size_t SF;
@@ -106,8 +108,10 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, i
         *cds[x] = o;
         o += cd;
     }
-    size_t* ccs[] = {&L.X, &L.dP, &L.dM, &L.dX, &L.T1};
-    for (int x = 0; x < (wide ? 5 : 3); ++x) {
+    L.X = o;                            // in the input dtype
+    o += wide ? cc : a64((size_t)L.nrec * BC * BC / 2);
+    size_t* ccs[] = {&L.dP, &L.dM, &L.dX, &L.T1};
+    for (int x = 0; x < (wide ? 4 : 2); ++x) {
         *ccs[x] = o;
         o += cc;
     }
@@ -116,7 +120,7 @@ BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int D, size_t rec_bytes, i
     L.RN = o;
     o += a64((size_t)L.nrec * 2 * BC);
     L.Lam = o;
-    o += dd;
+    o += wide ? dd : a64((size_t)L.nrec * D * D / 2);
     L.SF = o;
     o += a64((size_t)L.nrec * rec_bytes / 4);
     L.span = o;
@@ -822,7 +826,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         lds_barrier();
         for (int e4 = tid; e4 < C * C / 4; e4 += NTP) {
             const int t = e4 / (C / 4), c4 = 4 * (e4 % (C / 4));
-            st4s(ws + a.L.X + cco + (size_t)t * C + c4, ld4s(sX + t * LDM + c4));
+            store4(reinterpret_cast<E*>(ws + a.L.X) + cco + (size_t)t * C + c4, ld4s(sX + t * LDM + c4));
         }
 
         // 4. W = X E~, U~ = X u
@@ -927,7 +931,9 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
 // Lam (the gradient at the current chunk end) stays in MFMA accumulators;
 // per chunk:
 //   dDelta = K^ Lam + P^T dO,   Lam <- diag(gamma) Lam + Q~^T dO - W^T dDelta
-// and Lam (before the update) and dDelta go to the workspace in fp32.  A
+// and Lam (before the update) and dDelta go to the workspace in the input
+// dtype (bf16 inputs: the precision in which every later product takes
+// them; the fp32 accumulators carry on unrounded).  A
 // chunk's fragments are copied global -> LDS with global_load_lds (no
 // register staging), double buffered when two buffers fit.
 // ---------------------------------------------------------------------------
@@ -985,12 +991,12 @@ __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char
     const float* sGam = reinterpret_cast<const float*>(buf + S::OFF_G);
 
     // the gradient at this chunk's end, for the per-chunk products
-    float* lo = a.ws + a.L.Lam + (size_t)r * D * D;
+    E* lo = reinterpret_cast<E*>(a.ws + a.L.Lam) + (size_t)r * D * D;
 #pragma unroll
     for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            lo[(16 * kt + 4 * gq + i) * D + col] = lam[kt][i];
+            lo[(16 * kt + 4 * gq + i) * D + col] = from_f32<E>(lam[kt][i]);
 
     Frag LB[NKS], OB[NKC];
 #pragma unroll
@@ -1504,15 +1510,16 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     // 4 (e % (D/4))..), loaded one record ahead of their use
     constexpr int NIT = D * D / 4 / NTH;
     static_assert(D * D / 4 % NTH == 0, "whole items per thread");
-    f32x4 s4r[NIT], l4r[NIT];
+    f32x4 s4r[NIT];
+    bf16x4 l4r[NIT];
     auto load_sl = [&](int64_t rr) {
         const float* S = a.S_chunks + (size_t)rr * D * D;
-        const float* Lam = ws + a.L.Lam + (size_t)rr * D * D;
+        const bf16* Lam = reinterpret_cast<const bf16*>(ws + a.L.Lam) + (size_t)rr * D * D;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = tid0 + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
             s4r[it] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
-            l4r[it] = *reinterpret_cast<const f32x4*>(Lam + (size_t)i * D + j);
+            l4r[it] = *reinterpret_cast<const bf16x4*>(Lam + (size_t)i * D + j);
         }
     };
     // persistent: records blockIdx.x, + gridDim.x, ... (the grid is at most
@@ -1564,9 +1571,10 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
 #pragma unroll
             for (int x = 0; x < 4; ++x)
                 pU[nt][x] = ws[a.L.Ut + orow + (size_t)x * D + 16 * (n0 + nt)];
-        // staging also forms dgamma_i = sum_j S[i][j] Lam[i][j] in fp32 (partial
-        // sums of 4 through LDS); gamma becomes gamma * dgamma, the chunk-end term
-        // of dG_L that bwd_decay adds (the scan has used gamma)
+        // staging also forms dgamma_i = sum_j S[i][j] Lam[i][j] in fp32 (Lam as
+        // the scan stored it, in bf16; partial sums of 4 through LDS); gamma
+        // becomes gamma * dgamma, the chunk-end term of dG_L that bwd_decay
+        // adds (the scan has used gamma)
         const float gam_i = ws[a.L.gam + (size_t)r * D + tid % D];   // used by the threads tid < D
         // the staging below waits for S and Lam only: keep it after the
         // loads above, whose issue the wait then does not hold up
@@ -1575,12 +1583,14 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
-            const f32x4 s4 = s4r[it], l4 = l4r[it];
-            bf16x4 sv, lv;
+            const f32x4 s4 = s4r[it];
+            const bf16x4 lv = l4r[it];
+            bf16x4 sv;
+            f32x4 l4;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 sv[x] = (bf16)s4[x];
-                lv[x] = (bf16)l4[x];
+                l4[x] = (float)lv[x];
                 sSt[(j + x) * LDB + i] = sv[x];
             }
             *reinterpret_cast<bf16x4*>(sS + i * LDB + j) = sv;
@@ -1692,18 +1702,17 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         }
 
         // the dM phase's operands from memory:
-        // X rows (fp32), U and E~ rows (bf16), 4 elements per item
+        // X, U and E~ rows (bf16), 4 elements per item
         constexpr int NXI = C * C / 4 / NTH, NUI = C * D / 4 / NTH;
         static_assert(C * C / 4 % NTH == 0 && C * D / 4 % NTH == 0, "whole items per thread");
-        f32x4 xr[NXI];
-        bf16x4 ur[NUI], er[NUI];
+        bf16x4 xr[NXI], ur[NUI], er[NUI];
         {
-            const float* Xg = ws + a.L.X + cc;
+            const bf16x4* Xg = reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(ws + a.L.X) + cc);
             const bf16x4* Ug = reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(ws + a.L.U) + cd);
             const bf16x4* Eg = reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(ws + a.L.Et) + cd);
 #pragma unroll
             for (int it = 0; it < NXI; ++it)
-                xr[it] = *reinterpret_cast<const f32x4*>(Xg + 4 * (tid + it * NTH));
+                xr[it] = Xg[tid + it * NTH];
 #pragma unroll
             for (int it = 0; it < NUI; ++it) {
                 ur[it] = Ug[tid + it * NTH];
@@ -1718,12 +1727,10 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
 #pragma unroll
         for (int it = 0; it < NXI; ++it) {
             const int e = tid + it * NTH, t = e / (C / 4), c = 4 * (e % (C / 4));
-            bf16x4 xv;
+            const bf16x4 xv = xr[it];
 #pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                xv[y] = (bf16)xr[it][y];
+            for (int y = 0; y < 4; ++y)
                 sXt[(c + y) * LX + t] = xv[y];
-            }
             *reinterpret_cast<bf16x4*>(sX + t * LX + c) = xv;
         }
 #pragma unroll
@@ -1934,7 +1941,7 @@ __device__ __forceinline__ void decay_wy_slices(const BwdArgs& a, int64_t r, int
     float* sOE = sOU + C * LC;     // dE~[t][i]
     const float* ws = a.ws;
     const size_t cd = (size_t)r * C * D, cc = (size_t)r * C * C;
-    const float* Xg = ws + a.L.X + cc;
+    const bf16* Xg = reinterpret_cast<const bf16*>(ws + a.L.X) + cc;
     const bf16* dDel = reinterpret_cast<const bf16*>(ws + a.L.dDel) + cd;
     const bf16* dW = reinterpret_cast<const bf16*>(ws + a.L.dW) + cd;
     const int lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15, t0 = 16 * wave;
@@ -1946,18 +1953,16 @@ __device__ __forceinline__ void decay_wy_slices(const BwdArgs& a, int64_t r, int
         const int bi = tid >> 4, bj = tid & 15;
         const int half = tid >> 7, e = tid & 127, ti = e >> 3, jj = e & 7;
         const bf16* src = half ? dW : dDel;
-        f32x4 x4[4];
-        bf16x4 d4[4];
+        bf16x4 x4[4], d4[4];
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            x4[y] = *reinterpret_cast<const f32x4*>(Xg + (4 * bi + y) * C + 4 * bj);
+            x4[y] = *reinterpret_cast<const bf16x4*>(Xg + (4 * bi + y) * C + 4 * bj);
             d4[y] = *reinterpret_cast<const bf16x4*>(src + (size_t)(4 * ti + y) * D + i0 + 4 * jj);
         }
         bf16* dst = half ? sDwT : sDdT;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            *reinterpret_cast<bf16x4*>(sXt + (4 * bj + x) * LX + 4 * bi) =
-                bf16x4{(bf16)x4[0][x], (bf16)x4[1][x], (bf16)x4[2][x], (bf16)x4[3][x]};
+            *reinterpret_cast<bf16x4*>(sXt + (4 * bj + x) * LX + 4 * bi) = bf16x4{x4[0][x], x4[1][x], x4[2][x], x4[3][x]};
             *reinterpret_cast<bf16x4*>(dst + (4 * jj + x) * LX + 4 * ti) = bf16x4{d4[0][x], d4[1][x], d4[2][x], d4[3][x]};
         }
     }

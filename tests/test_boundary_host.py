@@ -371,20 +371,22 @@ def test_backward_null_args_and_workspace(lib):
 def test_backward_workspace_size_formula(lib):
     # per chunk record, fp32, each array padded to 256 bytes: arrays of
     # [C][D] (G, U, E~, W, U~, dDelta, dQ~, dK^, dW; for fp32 inputs also
-    # Delta, dU, dE~, dO, which the bf16 kernels keep on chip), of [C][C]
-    # (X, dP, dM; for fp32 also dX and a product), gamma [D], the prologue's
-    # per-token 1/|k|, 1/|q| [2][C], the chunk-end state gradient [D][D];
-    # then the scan's operand fragments in the input dtype: K^, Q~^T, -W^T,
-    # dO^T (C*D each) and P^T (C*C)
+    # Delta, dU, dE~, dO, which the bf16 kernels keep on chip), X [C][C] in
+    # the input dtype, of [C][C] (dP, dM; for fp32 also dX and a product),
+    # gamma [D], the prologue's
+    # per-token 1/|k|, 1/|q| [2][C]; the chunk-end state gradient [D][D] in
+    # the input dtype; then the scan's operand fragments in the input dtype:
+    # K^, Q~^T, -W^T, dO^T (C*D each) and P^T (C*C)
     def al(x):
         return (x + 255) // 256 * 256
     for (B, T, H, D, dt, es) in [(2, 100, 3, 128, gdr2.BF16, 2), (1, 64, 1, 64, gdr2.F32, 4),
                                  (8, 4096, 16, 128, gdr2.BF16, 2), (1, 200, 2, 128, gdr2.F32, 4)]:
         a = good_bwd(B=B, T=T, H=H, D=D, dtype=dt)
         nrec = B * H * -(-T // 64)
-        ncd, ncc = (13, 5) if es == 4 else (9, 3)
-        want = (ncd * al(nrec * 64 * D * 4) + ncc * al(nrec * 64 * 64 * 4) + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
-                + al(nrec * D * D * 4) + al(nrec * (4 * 64 * D + 64 * 64) * es))
+        ncd, ncc = (13, 4) if es == 4 else (9, 2)
+        want = (ncd * al(nrec * 64 * D * 4) + al(nrec * 64 * 64 * es) + ncc * al(nrec * 64 * 64 * 4)
+                + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
+                + al(nrec * D * D * es) + al(nrec * (4 * 64 * D + 64 * 64) * es))
         assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == want
     assert lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(T=0))) == 0
     a = good_bwd()
