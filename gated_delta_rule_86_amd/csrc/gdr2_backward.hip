@@ -156,6 +156,9 @@ struct Rec {
     int L;
 };
 
+// Valid tokens of chunk n of a sequence.
+__device__ __forceinline__ int chunk_len(const BwdArgs& a, int64_t n) { return (int)min((int64_t)BC, a.T - n * BC); }
+
 __device__ __forceinline__ Rec rec_of(int64_t r, int64_t NC, int64_t T, int64_t H)
 {
     Rec x;
@@ -189,11 +192,14 @@ struct ScanFrags {
     static constexpr size_t K_BYTES = (size_t)NB * NKS * FRAG;    // C*D*sizeof(E)
     static constexpr size_t P_BYTES = (size_t)NB * NKC * FRAG;    // C*C*sizeof(E)
     static constexpr size_t T_BYTES = (size_t)DT * NKC * FRAG;    // C*D*sizeof(E)
+    // dO^T (fp32 inputs only: with bf16 inputs the scan reads the dO rows
+    // from the input and forms its fragments in LDS)
+    static constexpr bool HAS_O = sizeof(E) == 4;
     static constexpr size_t OFF_K = 0, OFF_P = K_BYTES, OFF_Q = OFF_P + P_BYTES, OFF_W = OFF_Q + T_BYTES,
-                            OFF_O = OFF_W + T_BYTES, REC = OFF_O + T_BYTES;
+                            OFF_O = OFF_W + T_BYTES, REC = OFF_O + (HAS_O ? T_BYTES : 0);
     static constexpr int NFRAG = (int)(REC / FRAG);
     static_assert(K_BYTES == (size_t)BC * D * sizeof(E), "fragment size");
-    static_assert(REC == (size_t)(4 * BC * D + BC * BC) * sizeof(E), "record size used for the workspace");
+    static_assert(REC == (size_t)((HAS_O ? 4 : 3) * BC * D + BC * BC) * sizeof(E), "record size used for the workspace");
 };
 
 // Byte offset of element (row, k) in an array of such fragments whose
@@ -894,10 +900,11 @@ template <typename E> __device__ __forceinline__ int slot_k(int gq, int j);
 template <> __device__ __forceinline__ int slot_k<bf16>(int gq, int j) { return (j < 4 ? 0 : 12) + 4 * gq + j; }
 template <> __device__ __forceinline__ int slot_k<float>(int gq, int j) { return 4 * gq + j; }
 
-// One workgroup per chunk record: the dO^T fragments of the scan (rows =
-// value columns, k = tokens), read from the input rows, zero past the valid
-// length.  bwd_prep writes the record's other fragments.  Item (fragment,
-// lane) -> 16 bytes.
+// fp32 inputs: one workgroup per chunk record: the dO^T fragments of the
+// scan (rows = value columns, k = tokens), read from the input rows, zero
+// past the valid length.  bwd_prep writes the record's other fragments.
+// Item (fragment, lane) -> 16 bytes.  (bf16 inputs: the scan copies the dO
+// rows itself, scan_fetch and o_frag.)
 template <typename E, int D>
 __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
 {
@@ -933,9 +940,11 @@ __global__ __launch_bounds__(NTB) void bwd_frag_kernel(BwdArgs a)
 //   dDelta = K^ Lam + P^T dO,   Lam <- diag(gamma) Lam + Q~^T dO - W^T dDelta
 // and Lam (before the update) and dDelta go to the workspace in the input
 // dtype (bf16 inputs: the precision in which every later product takes
-// them; the fp32 accumulators carry on unrounded).  A
-// chunk's fragments are copied global -> LDS with global_load_lds (no
-// register staging), double buffered when two buffers fit.
+// them; the fp32 accumulators carry on unrounded).  A chunk's fragments are
+// copied global -> LDS with global_load_lds (no register staging), double
+// buffered when two buffers fit; with bf16 inputs the dO rows of the
+// workgroup's value columns are copied the same way, straight from the
+// input, and the dO fragments are read out of them.
 // ---------------------------------------------------------------------------
 template <typename E, int D>
 struct ScanShape {
@@ -970,15 +979,54 @@ __device__ __forceinline__ void scan_fetch(const BwdArgs& a, int64_t r, int slic
     typedef ScanFrags<E, D> F;
     const unsigned char* rec = reinterpret_cast<const unsigned char*>(a.ws + a.L.SF) + (size_t)r * F::REC;
     copy_frags<F::OFF_O>(rec, buf, wave, lane);
-    copy_frags<S::O_SLICE>(rec + F::OFF_O + slice * S::O_SLICE, buf + S::OFF_O, wave, lane);
+    if constexpr (F::HAS_O) {
+        copy_frags<S::O_SLICE>(rec + F::OFF_O + slice * S::O_SLICE, buf + S::OFF_O, wave, lane);
+    } else {
+        // the chunk's dO rows, columns BV*slice.., as [BC][BV] rows of 2*BV
+        // bytes: instruction j copies rows 8j..8j+7 (lane: row 8j + lane/8,
+        // bytes 16 (lane % 8)..); rows past the valid length re-read the last
+        // valid row (o_frag zeroes those tokens)
+        static_assert(2 * S::BV == 128 && S::O_SLICE == (size_t)BC * 2 * S::BV, "8 rows per 1 KB instruction");
+        const Rec rc = rec_of(r, a.NC, a.T, a.H);
+        const unsigned char* dO = reinterpret_cast<const unsigned char*>(a.dO) + (slice * S::BV + 8 * (lane & 7)) * sizeof(E);
+#pragma unroll
+        for (int j = wave; j < BC / 8; j += NTB / 64) {
+            const int t = min(8 * j + (lane >> 3), rc.L - 1);
+            __builtin_amdgcn_global_load_lds(dO + (rc.row0 + (int64_t)t * a.H) * D * sizeof(E),
+                                             (lds_void*)(buf + S::OFF_O + j * 1024), 16, 0, 0);
+        }
+    }
     if (wave == NTB / 64 - 1 && lane < D / 4)
         __builtin_amdgcn_global_load_lds(a.ws + a.L.gam + (size_t)r * D + lane * 4, (lds_void*)(buf + S::OFF_G), 16,
                                          0, 0);
 }
 
+// The dO operand fragment kc (k = tokens KB kc.., n = the wave's 16 value
+// columns) of a chunk in buf: fp32 inputs, as the frag pass stored it; bf16
+// inputs, read out of the dO rows scan_fetch copied, zero at tokens >= L.
+template <typename E, int D>
+__device__ __forceinline__ typename Mma<E>::Frag o_frag(const unsigned char* buf, int kc, int wave, int lane, int L)
+{
+    typedef ScanShape<E, D> S;
+    typedef ScanFrags<E, D> F;
+    typedef typename Mma<E>::Frag Frag;
+    if constexpr (F::HAS_O) {
+        return *reinterpret_cast<const Frag*>(buf + S::OFF_O + (size_t)(wave * F::NKC + kc) * 1024 + lane * 16);
+    } else {
+        const E* sO = reinterpret_cast<const E*>(buf + S::OFF_O) + 16 * wave + (lane & 15);
+        Frag f;
+#pragma unroll
+        for (int j = 0; j < 16 / (int)sizeof(E); ++j) {
+            const int t = kc * F::KB + slot_k<E>(lane >> 4, j);
+            f[j] = t < L ? sO[t * S::BV] : (E)0.f;
+        }
+        return f;
+    }
+}
+
 template <typename E, int D>
 __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char* buf, f32x4* lam, int64_t r,
-                                           int col, int lane, int wave)
+                                           int col, int lane, int wave, int L)
 {
     typedef ScanShape<E, D> S;
     typedef ScanFrags<E, D> F;
@@ -1004,7 +1052,7 @@ __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char
         LB[ks] = MM::from_acc(&lam[ks * KT]);
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
-        OB[kc] = frag(S::OFF_O, wave * NKC + kc);
+        OB[kc] = o_frag<E, D>(buf, kc, wave, lane, L);
 
     // dDelta = K^ Lam + P^T dO  (P^T is upper triangular: k-steps from the diagonal)
     f32x4 dd[NB];
@@ -1094,20 +1142,20 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
             if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf1, wave, lane);
-            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave);
+            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave, chunk_len(a, n));
             if (n == n0)
                 break;
             wait_copies();
             __syncthreads();          // chunk n - 1 is in buf1; everyone is done with buf0
             if (n - 2 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 2, slice, buf0, wave, lane);
-            scan_chunk<E, D>(a, buf1, lam, rec0 + n - 1, col, lane, wave);
+            scan_chunk<E, D>(a, buf1, lam, rec0 + n - 1, col, lane, wave, chunk_len(a, n - 1));
         }
     } else {
         for (int64_t n = n1 - 1; n >= n0; --n) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0
-            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave);
+            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave, chunk_len(a, n));
             __syncthreads();          // everyone is done with buf0
             if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf0, wave, lane);
@@ -1136,7 +1184,7 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
 // where bwd_scan_kernel starts that segment.
 // ---------------------------------------------------------------------------
 template <bool LOCAL, typename E, int D>
-__device__ __forceinline__ void span_scan_chunk(const unsigned char* buf, f32x4* lam, int lane, int wave)
+__device__ __forceinline__ void span_scan_chunk(const unsigned char* buf, f32x4* lam, int lane, int wave, int L)
 {
     typedef ScanShape<E, D> S;
     typedef ScanFrags<E, D> F;
@@ -1155,7 +1203,7 @@ __device__ __forceinline__ void span_scan_chunk(const unsigned char* buf, f32x4*
     if (LOCAL) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
-            OB[kc] = frag(S::OFF_O, wave * NKC + kc);
+            OB[kc] = o_frag<E, D>(buf, kc, wave, lane, L);
     }
     // dDelta = K^ X (+ P^T dO for the local columns)
     f32x4 dd[NB];
@@ -1204,20 +1252,20 @@ __device__ __forceinline__ void span_scan_run(const BwdArgs& a, unsigned char* b
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
             if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf1, wave, lane);
-            span_scan_chunk<LOCAL, E, D>(buf0, lam, lane, wave);
+            span_scan_chunk<LOCAL, E, D>(buf0, lam, lane, wave, chunk_len(a, n));
             if (n == n0)
                 break;
             wait_copies();
             __syncthreads();          // chunk n - 1 is in buf1; everyone is done with buf0
             if (n - 2 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 2, slice, buf0, wave, lane);
-            span_scan_chunk<LOCAL, E, D>(buf1, lam, lane, wave);
+            span_scan_chunk<LOCAL, E, D>(buf1, lam, lane, wave, chunk_len(a, n - 1));
         }
     } else {
         for (int64_t n = n1 - 1; n >= n0; --n) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0
-            span_scan_chunk<LOCAL, E, D>(buf0, lam, lane, wave);
+            span_scan_chunk<LOCAL, E, D>(buf0, lam, lane, wave, chunk_len(a, n));
             __syncthreads();          // everyone is done with buf0
             if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf0, wave, lane);
@@ -2547,8 +2595,10 @@ hipError_t launch_backward_t(const gdr2_bwd_args& x, hipStream_t s)
         hipLaunchKernelGGL((bwd_dout_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_frag_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (ScanFrags<E, D>::HAS_O) {   // bf16: the scan reads the dO rows itself
+        hipLaunchKernelGGL((bwd_frag_kernel<E, D>), dim3((unsigned)nrec), dim3(NTB), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.nseg > 1) {
         const int64_t groups = cdiv(a.nbh * (a.nseg - 1), 8) * 8 * 2 * ScanShape<E, D>::NS;
         hipLaunchKernelGGL((bwd_span_kernel<E, D>), dim3((unsigned)groups), dim3(NTB), 0, s, a);
@@ -2598,7 +2648,7 @@ size_t backward_workspace_bytes(const gdr2_bwd_args& a)
     if (a.B * a.H * a.T == 0)
         return 0;
     const size_t esz = a.dtype == GDR2_BF16 ? 2 : 4;
-    const size_t rec = (size_t)(4 * BC * a.Dk + BC * BC) * esz;   // ScanFrags<E, D>::REC
+    const size_t rec = (size_t)((esz == 4 ? 4 : 3) * BC * a.Dk + BC * BC) * esz;   // ScanFrags<E, D>::REC
     int64_t nseg, len;
     segment_plan(a.algo, cdiv(a.T, BC), a.B * a.H * (a.Dk / 64), &nseg, &len);
     const bool narrow = a.b_width == 1 || a.w_width == 1 || a.g_width == 1;

@@ -376,7 +376,7 @@ def test_backward_workspace_size_formula(lib):
     # gamma [D], the prologue's
     # per-token 1/|k|, 1/|q| [2][C]; the chunk-end state gradient [D][D] in
     # the input dtype; then the scan's operand fragments in the input dtype:
-    # K^, Q~^T, -W^T, dO^T (C*D each) and P^T (C*C)
+    # K^, Q~^T, -W^T (and for fp32 dO^T; C*D each) and P^T (C*C)
     def al(x):
         return (x + 255) // 256 * 256
     for (B, T, H, D, dt, es) in [(2, 100, 3, 128, gdr2.BF16, 2), (1, 64, 1, 64, gdr2.F32, 4),
@@ -386,7 +386,7 @@ def test_backward_workspace_size_formula(lib):
         ncd, ncc = (13, 4) if es == 4 else (9, 2)
         want = (ncd * al(nrec * 64 * D * 4) + al(nrec * 64 * 64 * es) + ncc * al(nrec * 64 * 64 * 4)
                 + al(nrec * D * 4) + al(nrec * 2 * 64 * 4)
-                + al(nrec * D * D * es) + al(nrec * (4 * 64 * D + 64 * 64) * es))
+                + al(nrec * D * D * es) + al(nrec * ((4 if es == 4 else 3) * 64 * D + 64 * 64) * es))
         assert lib.gdr2_backward_workspace_size(ctypes.byref(a)) == want
     assert lib.gdr2_backward_workspace_size(ctypes.byref(good_bwd(T=0))) == 0
     a = good_bwd()
