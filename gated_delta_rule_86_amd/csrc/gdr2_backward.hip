@@ -954,6 +954,14 @@ struct ScanShape {
     static constexpr size_t OFF_O = F::OFF_O, OFF_G = OFF_O + O_SLICE, BUF = OFF_G + (size_t)D * 4;
     static constexpr int NBUF = 2 * BUF <= 160 * 1024 ? 2 : 1;
     static_assert(F::OFF_O % 1024 == 0 && O_SLICE % 1024 == 0, "whole fragments");
+    // bf16: Lam and dDelta leave through workgroup patches in LDS ([D] and
+    // [BC] rows of the BV columns, rows padded by 16 bytes) as 16-byte row
+    // pieces, 2 BV bytes per row, instead of one 2-byte store per element
+    static constexpr bool PATCH = sizeof(E) == 2;
+    static constexpr int PLD = (int)sizeof(E) * BV + 16;
+    static constexpr size_t PATCH_L = PATCH ? (size_t)D * PLD : 0, PATCH_D = PATCH ? (size_t)BC * PLD : 0;
+    static_assert(!PATCH || (NBUF == 2 && 2 * BUF + PATCH_L + PATCH_D <= 160 * 1024), "LDS budget");
+    static_assert(!PATCH || 2 * BV == 8 * 16, "eight 16-byte pieces per row");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -1024,9 +1032,23 @@ __device__ __forceinline__ typename Mma<E>::Frag o_frag(const unsigned char* buf
     }
 }
 
+// bf16: rows [nrows][BV] of the patch (written, then an lds_barrier) to
+// memory at dst (row stride D elements), 16 bytes per lane and instruction.
+template <typename E, int D, int NROWS>
+__device__ __forceinline__ void patch_rows_out(const unsigned char* patch, E* dst, int tid)
+{
+    typedef ScanShape<E, D> S;
+#pragma unroll
+    for (int p = tid; p < NROWS * 8; p += NTB) {
+        const int row = p >> 3, c = p & 7;
+        *reinterpret_cast<uint4*>(dst + (size_t)row * D + 8 * c) =
+            *reinterpret_cast<const uint4*>(patch + (size_t)row * S::PLD + 16 * c);
+    }
+}
+
 template <typename E, int D>
 __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char* buf, f32x4* lam, int64_t r,
-                                           int col, int lane, int wave, int L)
+                                           int col, int lane, int wave, int L, unsigned char* patch)
 {
     typedef ScanShape<E, D> S;
     typedef ScanFrags<E, D> F;
@@ -1040,11 +1062,22 @@ __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char
 
     // the gradient at this chunk's end, for the per-chunk products
     E* lo = reinterpret_cast<E*>(a.ws + a.L.Lam) + (size_t)r * D * D;
+    const int pc = 16 * wave + (lane & 15);    // the lane's column within the workgroup's BV
+    if constexpr (S::PATCH) {
 #pragma unroll
-    for (int kt = 0; kt < DT; ++kt)
+        for (int kt = 0; kt < DT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lo[(16 * kt + 4 * gq + i) * D + col] = from_f32<E>(lam[kt][i]);
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<E*>(patch + (size_t)(16 * kt + 4 * gq + i) * S::PLD + 2 * pc) = from_f32<E>(lam[kt][i]);
+        lds_barrier();
+        patch_rows_out<E, D, D>(patch, lo + (col - pc), 64 * wave + lane);
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < DT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lo[(16 * kt + 4 * gq + i) * D + col] = from_f32<E>(lam[kt][i]);
+    }
 
     Frag LB[NKS], OB[NKC];
 #pragma unroll
@@ -1070,11 +1103,22 @@ __device__ __forceinline__ void scan_chunk(const BwdArgs& a, const unsigned char
         for (int kc = st / KT; kc < NKC; ++kc)
             dd[st] = MM::mma(frag(F::OFF_P, st * NKC + kc), OB[kc], dd[st]);
     E* dq = reinterpret_cast<E*>(a.ws + a.L.dDel) + (size_t)r * BC * D;   // in the input dtype
+    if constexpr (S::PATCH) {
+        unsigned char* pd = patch + S::PATCH_L;
 #pragma unroll
-    for (int st = 0; st < NB; ++st)
+        for (int st = 0; st < NB; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dq[(16 * st + 4 * gq + i) * D + col] = from_f32<E>(dd[st][i]);
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<E*>(pd + (size_t)(16 * st + 4 * gq + i) * S::PLD + 2 * pc) = from_f32<E>(dd[st][i]);
+        lds_barrier();
+        patch_rows_out<E, D, BC>(pd, dq + (col - pc), 64 * wave + lane);
+    } else {
+#pragma unroll
+        for (int st = 0; st < NB; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dq[(16 * st + 4 * gq + i) * D + col] = from_f32<E>(dd[st][i]);
+    }
 
     // Lam <- diag(gamma) Lam + Q~^T dO - W^T dDelta  (the W fragments hold -W^T)
     Frag DB[NKC];
@@ -1100,6 +1144,7 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
     constexpr int DT = D / 16;
     __shared__ __align__(16) unsigned char buf0[S::BUF];
     __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
+    __shared__ __align__(16) unsigned char patch[S::PATCH ? S::PATCH_L + S::PATCH_D : 16];
     // workgroup -> ((b,h), chunk segment, column slice); the slices of one
     // segment share blockIdx % 8, i.e. one XCD and its L2
     const int64_t bx = blockIdx.x, grp = bx / (8 * S::NS);
@@ -1142,20 +1187,20 @@ __global__ __launch_bounds__(NTB) void bwd_scan_kernel(BwdArgs a)
             __syncthreads();          // chunk n is in buf0; everyone is done with buf1
             if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf1, wave, lane);
-            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave, chunk_len(a, n));
+            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave, chunk_len(a, n), patch);
             if (n == n0)
                 break;
             wait_copies();
             __syncthreads();          // chunk n - 1 is in buf1; everyone is done with buf0
             if (n - 2 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 2, slice, buf0, wave, lane);
-            scan_chunk<E, D>(a, buf1, lam, rec0 + n - 1, col, lane, wave, chunk_len(a, n - 1));
+            scan_chunk<E, D>(a, buf1, lam, rec0 + n - 1, col, lane, wave, chunk_len(a, n - 1), patch);
         }
     } else {
         for (int64_t n = n1 - 1; n >= n0; --n) {
             wait_copies();
             __syncthreads();          // chunk n is in buf0
-            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave, chunk_len(a, n));
+            scan_chunk<E, D>(a, buf0, lam, rec0 + n, col, lane, wave, chunk_len(a, n), patch);
             __syncthreads();          // everyone is done with buf0
             if (n - 1 >= n0)
                 scan_fetch<E, D>(a, rec0 + n - 1, slice, buf0, wave, lane);
