@@ -1842,7 +1842,7 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
             f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const Frag ad = MM::load(dDel + ks * KB, D, lane);     // this wave's dDelta rows again (L2)
+                const Frag ad = pD[ks];                                // this wave's dDelta rows, kept
                 const Frag aw = MM::load(sDW + t0 * LDB + ks * KB, LDB, lane);
 #pragma unroll
                 for (int n = 0; n < 2; ++n) {
