@@ -1599,10 +1599,20 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
     const int tid0 = threadIdx.x, wave = tid0 >> 6;
     float* patch = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sb) + SH::PATCH_OFF) + wave * PATCH_FLOATS;
     const int rw = wave & 3, t0 = 16 * rw, n0 = (wave >> 2) * NH;   // row block; first of its NH column tiles
-    // S and Lam of a record as rows of 4 (item e: row e / (D/4), columns
-    // 4 (e % (D/4))..), loaded one record ahead of their use
-    constexpr int NIT = D * D / 4 / NTH;
-    static_assert(D * D / 4 % NTH == 0, "whole items per thread");
+    // S and Lam of a record as pieces of 4 columns, loaded one record ahead
+    // of their use.  Piece (wave, it) of a lane: u = NIT wave + it picks 4
+    // rows 4 (u / NCH).. and 64 columns 64 (u % NCH)..; the lane quad q =
+    // lane / 4 takes the columns 4q.. of them, and lane r = lane % 4 the row
+    // 4 (u / NCH) + r.  A quad so holds a 4x4 block, which it transposes
+    // across its lanes for S^T: 8-byte LDS writes instead of 2-byte ones
+    // (the global reads stay 256-byte row pieces).
+    constexpr int NIT = D * D / 4 / NTH, NCH = D / 64;
+    static_assert(D * D / 4 % NTH == 0 && D % 64 == 0 && NIT * (NTH / 64) == (D / 4) * NCH, "whole pieces per lane");
+    auto piece = [&](int it, int ln, int& i, int& j) {
+        const int u = wave * NIT + it;
+        i = 4 * (u / NCH) + (ln & 3);
+        j = 64 * (u % NCH) + 4 * (ln >> 2);
+    };
     f32x4 s4r[NIT];
     bf16x4 l4r[NIT];
     auto load_sl = [&](int64_t rr) {
@@ -1610,7 +1620,8 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         const bf16* Lam = reinterpret_cast<const bf16*>(ws + a.L.Lam) + (size_t)rr * D * D;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int e = tid0 + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+            int i, j;
+            piece(it, tid0 & 63, i, j);
             s4r[it] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + j);
             l4r[it] = *reinterpret_cast<const bf16x4*>(Lam + (size_t)i * D + j);
         }
@@ -1675,17 +1686,21 @@ __global__ __launch_bounds__(SgradShape<D>::NTH) void bwd_sgrad_bf16_kernel(BwdA
         lds_barrier();                   // the previous record's products are done with LDS
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int e = tid + it * NTH, i = e / (D / 4), j = 4 * (e % (D / 4));
+            int i, j;
+            piece(it, lane, i, j);
             const f32x4 s4 = s4r[it];
             const bf16x4 lv = l4r[it];
-            bf16x4 sv;
+            bf16x4 sv, tv;
             f32x4 l4;
+            // S^T[j + r][i - r ..]: this lane's column of the quad's 4x4 block
+            const f32x4 st = quad_transpose(s4, lane & 3);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 sv[x] = (bf16)s4[x];
+                tv[x] = (bf16)st[x];
                 l4[x] = (float)lv[x];
-                sSt[(j + x) * LDB + i] = sv[x];
             }
+            *reinterpret_cast<bf16x4*>(sSt + (j + (lane & 3)) * LDB + (i - (lane & 3))) = tv;
             *reinterpret_cast<bf16x4*>(sS + i * LDB + j) = sv;
             *reinterpret_cast<bf16x4*>(sL + i * LDB + j) = lv;
             sPg[i * SH::LDG + j / 4] = s4[0] * l4[0] + s4[1] * l4[1] + s4[2] * l4[2] + s4[3] * l4[3];

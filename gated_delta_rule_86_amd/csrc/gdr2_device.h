@@ -24,6 +24,41 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // v_cvt_pk_bf16_f32: round to nearest even.
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// The value of the lane whose index differs in bit M (M = 1 or 2) within
+// its group of four lanes (a DPP quad permutation).
+template <int M>
+__device__ __forceinline__ float dpp_quad_xor(float v)
+{
+    static_assert(M == 1 || M == 2, "quad lanes");
+    constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+}
+
+// 4x4 transpose across the four lanes of a quad (two exchange rounds): lane
+// j = lane % 4 holds v[i] = X[i][j] on entry and X[j][c] in v[c] on return.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int j)
+{
+    const bool b1 = (j >> 1) & 1, b0 = j & 1;
+    float y0 = dpp_quad_xor<2>(b1 ? v[0] : v[2]), y1 = dpp_quad_xor<2>(b1 ? v[1] : v[3]);
+    if (b1) {
+        v[0] = y0;
+        v[1] = y1;
+    } else {
+        v[2] = y0;
+        v[3] = y1;
+    }
+    y0 = dpp_quad_xor<1>(b0 ? v[0] : v[1]);
+    y1 = dpp_quad_xor<1>(b0 ? v[2] : v[3]);
+    if (b0) {
+        v[0] = y0;
+        v[2] = y1;
+    } else {
+        v[1] = y0;
+        v[3] = y1;
+    }
+    return v;
+}
+
 // 2^x on the transcendental unit (v_exp_f32).  Inputs here are <= 0 or
 // bounded; large negative inputs flush to 0, which is the intended limit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
