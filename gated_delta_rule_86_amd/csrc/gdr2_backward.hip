@@ -550,8 +550,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             f32x4 eg, kd;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                eg[j] = expf(G[j]);
-                kd[j] = expf(GL[j] - G[j]);
+                eg[j] = __expf(G[j]);
+                kd[j] = __expf(GL[j] - G[j]);
             }
             st4s(ws + a.L.G + x, G);
             store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ld4s(sE + l) * eg);
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 f32x4 gm;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    gm[j] = expf(GL[j]);
+                    gm[j] = __expf(GL[j]);
                 st4s(ws + a.L.gam + (size_t)r * D + i, gm);
             }
         }
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             f32x4 qv;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                qv[j] = sQ[(t0 + j) * LD + i] * expf(sG[(t0 + j) * LD + i]);
+                qv[j] = sQ[(t0 + j) * LD + i] * __expf(sG[(t0 + j) * LD + i]);
             store4(reinterpret_cast<E*>(sfr + SF::OFF_Q + frag_at<E>(i, t0, SF::NKC)), qv);
         }
 
@@ -763,7 +763,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             f32x4 ev = keepE[it];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                ev[j] *= expf(G[j]);
+                ev[j] *= __expf(G[j]);
             st4s(sE + l, ev);
             st4s(sU + l, keepU[it]);
         }
@@ -2226,7 +2226,7 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int l = (t0 + m) * LC + il;
-            acc += sdG[l] * (sK[l] * expf(GL - sG[l]));     // dK^ staged above
+            acc += sdG[l] * (sK[l] * __expf(GL - sG[l]));     // dK^ staged above
         }
         lds_barrier();                  // every thread has read its dK^ rows
         sdG[rg * LC + il] = acc;        // sdG is free until the main loop
@@ -2413,7 +2413,7 @@ __global__ __launch_bounds__(NTB, 2) void bwd_decay_kernel(BwdArgs a)
         for (int j = 0; j < 4; ++j) {
             // E~ = E e^G, Q~ = q e^G, K^ = k e^{G_L - G}, recomputed exactly as
             // bwd_prep forms them
-            const float G = sG[l + j], eg = expf(G), kd = expf(sG[(C - 1) * LC + c + j] - G);
+            const float G = sG[l + j], eg = __expf(G), kd = __expf(sG[(C - 1) * LC + c + j] - G);
             float dG = ev[j] * sEm[l + j] + qr[j] * sQp[l + j] - kr[j] * sKm[l + j] + dEt[j] * (ev[j] * eg) +
                        dQt[j] * (qr[j] * eg) - dKh[j] * (kr[j] * kd);
             if (t == rc.L - 1)
