@@ -24,17 +24,20 @@
 //   bwd_prep   persistent, one workgroup per CU, a chunk record at a time
 //              (the next record's input rows in flight): G, U, E~, gamma; M
 //              and P as 16x16 blocks through block-referenced rows (fp32
-//              MFMA); X by blocks; W, U~ (fp32 MFMA); and the scan's K^, P^T,
-//              Q~^T, -W^T operands in MFMA fragment order.
+//              MFMA; bf16 inputs: three-pass bf16 products); X by blocks; W,
+//              U~ likewise; and the scan's K^, P^T, Q~^T, -W^T operands in
+//              MFMA fragment order.
 //   bwd_dout   (fp32 inputs) dO rows of every chunk into the workspace (zero
 //              past T); the other kernels read dO from the input.
-//   bwd_frag   the scan's dO^T fragments.
+//   bwd_frag   (fp32 inputs) the scan's dO^T fragments; with bf16 inputs the
+//              scan copies the dO rows itself.
 //   bwd_span   (few sequences x heads, many chunks) per chunk segment: the
 //              segment's transition product and local gradient, for the
 //              two-level reverse scan.
 //   bwd_scan   per (sequence, head, chunk segment, 64 value columns): the
 //              state gradient through the chunks in reverse (columns evolve
-//              independently), recording Lam at every chunk end and dDelta.
+//              independently), recording Lam at every chunk end and dDelta
+//              (in the input dtype).
 //   bwd_sgrad  the state products per chunk.  bf16 inputs: persistent, every
 //              operand read once and staged in LDS in bf16, Delta kept on
 //              chip, then dM (the WY-factor product through dX and T1, also
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         const Rec rc = rec_of(r, a.NC, a.T, a.H);
         const size_t cdo = (size_t)r * C * D, cco = (size_t)r * C * C;
         // the scan's operand fragments of this record (K^, P^T, Q~^T, -W^T; the
-        // frag pass adds dO^T), in the input dtype
+        // frag pass adds dO^T for fp32 inputs), in the input dtype
         unsigned char* sfr = reinterpret_cast<unsigned char*>(ws + a.L.SF) + (size_t)r * SF::REC;
         auto pT = [&](int s_, int t) -> E* {            // P^T[s][t] = P[t][s]
             return reinterpret_cast<E*>(sfr + SF::OFF_P + frag_at<E>(s_, t, SF::NKC));
