@@ -546,18 +546,14 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 sG[(gi * TPG + m) * LD + i] = v[m] + off;
         }
         lds_barrier();
+        // (G and E~ are written in step 3, while one wave inverts)
         for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
             const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-            const size_t x = cdo + (size_t)t * D + i;
             const f32x4 G = ld4s(sG + l), GL = ld4s(sG + (C - 1) * LD + i);
-            f32x4 eg, kd;
+            f32x4 kd;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                eg[j] = __expf(G[j]);
+            for (int j = 0; j < 4; ++j)
                 kd[j] = __expf(GL[j] - G[j]);
-            }
-            st4s(ws + a.L.G + x, G);
-            store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ld4s(sE + l) * eg);
             // K^ straight into the scan's fragments (row = token, k = channel)
             store4(reinterpret_cast<E*>(sfr + SF::OFF_K + frag_at<E>(t, i, SF::NKS)), ld4s(sK + l) * kd);
             if (t == 0) {
@@ -756,12 +752,14 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 
         // 3. X = (I + M)^-1 into the q area (wave 0), after every thread has
         // staged E~ = e e^G and u of its step-1 items for step 4 (the k and E
-        // areas held re-referenced rows until now)
+        // areas held re-referenced rows until now) and written G and E~ out:
+        // those stores drain while wave 0 inverts
         float* sX = sQ;
         float* sU = sK;
 #pragma unroll
         for (int it = 0; it < NIT1; ++it) {
             const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
+            const size_t x = cdo + (size_t)t * D + i;
             const f32x4 G = ld4s(sG + l);
             f32x4 ev = keepE[it];
 #pragma unroll
@@ -769,6 +767,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 ev[j] *= __expf(G[j]);
             st4s(sE + l, ev);
             st4s(sU + l, keepU[it]);
+            st4s(ws + a.L.G + x, G);
+            store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ev);
         }
         if (tid < 64) {
             typedef Mma<float> MF;
