@@ -410,19 +410,17 @@ __device__ __forceinline__ void prep_rows_load(const BwdArgs& a, const Rec& rc, 
 
 template <bool B1, bool W1, bool G1, typename E, int D>
 __device__ __forceinline__ int prep_rows_use(const BwdArgs& a, const Rec& rc, int64_t r, int tid, float* sm,
-                                             float* sRN, f32x4* keepE, f32x4* keepU,
+                                             float* sRN, f32x4* keepE, f32x4* keepU, f32x4* keepK,
                                              const PrepRaw<B1, W1, G1, E, D>& x)
 {
     typedef BwdPrepShape<D> PS;
     typedef Raw4<E> R;
     constexpr int C = BC, LD = PS::LD, Q4 = D / 4, NIT = PrepRaw<B1, W1, G1, E, D>::NIT;
     float* ws = a.ws;
-    const size_t cdo = (size_t)r * C * D;
     int growth = 0;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int e4 = tid + it * NTP, t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-        const size_t xo = cdo + (size_t)t * D + i;
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 gv = G1 ? bcast4(x.sg[it]) : x.rg[it];
         f32x4 kv = R::cvt(x.rk[it]), qv = R::cvt(x.rq[it]);
@@ -467,8 +465,8 @@ __device__ __forceinline__ int prep_rows_use(const BwdArgs& a, const Rec& rc, in
         st4s(sm + PS::OFF_K + l, kv);
         st4s(sm + PS::OFF_Q + l, qv);
         st4s(sm + PS::OFF_E + l, ev);
-        store4(reinterpret_cast<E*>(ws + a.L.U) + xo, uv);
         keepE[it] = ev;
+        keepK[it] = kv;
         keepU[it] = uv;
     }
     return growth;
@@ -515,9 +513,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         // once every wave is done with the previous record's LDS; then the next
         // record's loads (the last record's re-reads itself)
         constexpr int NIT1 = C * Q4 / NTP;
-        f32x4 keepE[NIT1], keepU[NIT1];  // e = b k and u = w v of this thread's items, for step 3
+        f32x4 keepE[NIT1], keepU[NIT1], keepK[NIT1];  // e = b k, u = w v and k of this thread's items, for step 3
         lds_barrier();
-        int growth = prep_rows_use<B1, W1, G1, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU, raw);
+        int growth = prep_rows_use<B1, W1, G1, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU, keepK, raw);
         prep_rows_load<B1, W1, G1, E, D>(a, rec_of(std::min<int64_t>(r + gridDim.x, a.nrec - 1), a.NC, a.T, a.H),
                                          tid, raw);
         growth = lds_barrier_or<NTP / 64>(growth, sOr);
@@ -546,24 +544,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 sG[(gi * TPG + m) * LD + i] = v[m] + off;
         }
         lds_barrier();
-        // (G and E~ are written in step 3, while one wave inverts)
-        for (int e4 = tid; e4 < C * Q4; e4 += NTP) {
-            const int t = e4 / Q4, i = 4 * (e4 % Q4), l = t * LD + i;
-            const f32x4 G = ld4s(sG + l), GL = ld4s(sG + (C - 1) * LD + i);
-            f32x4 kd;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                kd[j] = __expf(GL[j] - G[j]);
-            // K^ straight into the scan's fragments (row = token, k = channel)
-            store4(reinterpret_cast<E*>(sfr + SF::OFF_K + frag_at<E>(t, i, SF::NKS)), ld4s(sK + l) * kd);
-            if (t == 0) {
-                f32x4 gm;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    gm[j] = __expf(GL[j]);
-                st4s(ws + a.L.gam + (size_t)r * D + i, gm);
-            }
-        }
+        // (G, E~, U, gamma and K^ are written in step 3, while one wave inverts)
         // Q~ = q e^G into the scan's Q~^T fragments (row = channel, k = token):
         // an item is one channel at 4 consecutive tokens, read from the raw
         // rows before step 2 re-references them
@@ -752,8 +733,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 
         // 3. X = (I + M)^-1 into the q area (wave 0), after every thread has
         // staged E~ = e e^G and u of its step-1 items for step 4 (the k and E
-        // areas held re-referenced rows until now) and written G and E~ out:
-        // those stores drain while wave 0 inverts
+        // areas held re-referenced rows until now) and written G, E~, U,
+        // gamma and K^ out: those stores drain while wave 0 inverts
         float* sX = sQ;
         float* sU = sK;
 #pragma unroll
@@ -769,6 +750,21 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             st4s(sU + l, keepU[it]);
             st4s(ws + a.L.G + x, G);
             store4(reinterpret_cast<E*>(ws + a.L.Et) + x, ev);
+            store4(reinterpret_cast<E*>(ws + a.L.U) + x, keepU[it]);
+            // K^ straight into the scan's fragments (row = token, k = channel)
+            const f32x4 GL = ld4s(sG + (C - 1) * LD + i);
+            f32x4 kd;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                kd[j] = __expf(GL[j] - G[j]);
+            store4(reinterpret_cast<E*>(sfr + SF::OFF_K + frag_at<E>(t, i, SF::NKS)), keepK[it] * kd);
+            if (t == 0) {
+                f32x4 gm;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    gm[j] = __expf(GL[j]);
+                st4s(ws + a.L.gam + (size_t)r * D + i, gm);
+            }
         }
         if (tid < 64) {
             typedef Mma<float> MF;
