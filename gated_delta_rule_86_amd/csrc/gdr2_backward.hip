@@ -510,14 +510,12 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         };
 
         // 1. raw rows (zero past the chunk's valid length), 4 channels per item,
-        // once every wave is done with the previous record's LDS; then the next
-        // record's loads (the last record's re-reads itself)
+        // once every wave is done with the previous record's LDS (the next
+        // record's loads are issued in step 3)
         constexpr int NIT1 = C * Q4 / NTP;
         f32x4 keepE[NIT1], keepU[NIT1], keepK[NIT1];  // e = b k, u = w v and k of this thread's items, for step 3
         lds_barrier();
         int growth = prep_rows_use<B1, W1, G1, E, D>(a, rc, r, tid, sm, sRN, keepE, keepU, keepK, raw);
-        prep_rows_load<B1, W1, G1, E, D>(a, rec_of(std::min<int64_t>(r + gridDim.x, a.nrec - 1), a.NC, a.T, a.H),
-                                         tid, raw);
         growth = lds_barrier_or<NTP / 64>(growth, sOr);
         {
             // cumulative sum over the chunk per channel: thread (group gi, channel
@@ -766,6 +764,13 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                 st4s(ws + a.L.gam + (size_t)r * D + i, gm);
             }
         }
+        // the next record's input rows (the last record re-reads itself):
+        // waves 1-7 issue theirs now, while wave 0 inverts, and wave 0 after;
+        // at the start of the next record they would queue behind this one's
+        // step-4 stores
+        const Rec rnext = rec_of(std::min<int64_t>(r + gridDim.x, a.nrec - 1), a.NC, a.T, a.H);
+        if (tid >= 64)
+            prep_rows_load<B1, W1, G1, E, D>(a, rnext, tid, raw);
         if (tid < 64) {
             typedef Mma<float> MF;
             const int lane = tid, gq = lane >> 4, cl = lane & 15;
@@ -827,6 +832,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
 #pragma unroll
                     for (int x4 = 0; x4 < 4; ++x4)
                         sX[(16 * I + 4 * gq + x4) * LDM + 16 * J + cl] = Xt[I][J][x4];
+            prep_rows_load<B1, W1, G1, E, D>(a, rnext, tid, raw);
         }
         lds_barrier();
         for (int e4 = tid; e4 < C * C / 4; e4 += NTP) {
