@@ -853,6 +853,24 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
             static_assert((NTP / 64) * 16 * LP <= C * LDM, "the patches fit in the M area");
             float* patch = sM + wave * 16 * LP;
             const int pr = lane >> 2, pc = 4 * (lane & 3);   // this lane's row piece of a tile
+            // bf16 inputs: X's bf16 head and tail, split once for every tile
+            // (the three-pass A operands), in the G area (free since step 3)
+            constexpr int LXS = C + 4;    // rows of 136 bytes: 8-byte pieces stay aligned
+            bf16* sXh = reinterpret_cast<bf16*>(sG);
+            bf16* sXl = sXh + C * LXS;
+            if constexpr (sizeof(E) == 2) {
+                static_assert(2 * C * LXS * 2 <= C * LD * 4 && C * C / 8 % NTP == 0, "the split X fits the G area");
+#pragma unroll
+                for (int e = tid; e < C * C / 8; e += NTP) {
+                    const int t = e / (C / 8), c8 = 8 * (e % (C / 8));
+                    const Split sp = bf_split(ld4s(sX + t * LDM + c8), ld4s(sX + t * LDM + c8 + 4));
+                    *reinterpret_cast<bf16x4*>(sXh + t * LXS + c8) = bf16x4{sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
+                    *reinterpret_cast<bf16x4*>(sXh + t * LXS + c8 + 4) = bf16x4{sp.hi[4], sp.hi[5], sp.hi[6], sp.hi[7]};
+                    *reinterpret_cast<bf16x4*>(sXl + t * LXS + c8) = bf16x4{sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
+                    *reinterpret_cast<bf16x4*>(sXl + t * LXS + c8 + 4) = bf16x4{sp.lo[4], sp.lo[5], sp.lo[6], sp.lo[7]};
+                }
+                lds_barrier();
+            }
             for (int tile = wave; tile < 2 * NPER; tile += NTP / 64) {
                 const int which = tile / NPER, T = (tile % NPER) / NTD, c = tile % NTD;
                 const float* src = which == 0 ? sE : sU;
@@ -861,8 +879,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
                     // three-pass bf16 products, 32 tokens per step (X is zero
                     // above its diagonal)
                     for (int k0 = 0; k0 < 16 * (T + 1); k0 += Mma<bf16>::KB)
-                        acc = mma3(split_rows(sX + 16 * T * LDM + k0, LDM, lane), split_kn(src + k0 * LD + 16 * c, LD, lane),
-                                   acc);
+                        acc = mma3(Split{Mma<bf16>::load(sXh + 16 * T * LXS + k0, LXS, lane),
+                                         Mma<bf16>::load(sXl + 16 * T * LXS + k0, LXS, lane)},
+                                   split_kn(src + k0 * LD + 16 * c, LD, lane), acc);
                 } else {
                     for (int kk = 0; kk <= T; ++kk)
                         acc = MF::mma(MF::load(sX + 16 * T * LDM + 16 * kk, LDM, lane),
