@@ -380,7 +380,6 @@ struct StateShape {
     static constexpr int VEC = 16 / ES;
     static constexpr int NS = D / BV;                       // column slices per (b,h)
     static constexpr int NTU = BV / 16;                     // value tiles per slice
-    static constexpr int LDO = 16 + VEC;                    // per-wave output staging rows
     static constexpr size_t U_SLICE = (size_t)NTU * NB * F::TILE_U;
     static constexpr size_t OFF_W = 0;                      // byte offsets in one buffer
     static constexpr size_t OFF_Q = OFF_W + F::W_BYTES;
@@ -389,10 +388,9 @@ struct StateShape {
     static constexpr size_t OFF_U = OFF_P + F::P_BYTES;
     static constexpr size_t OFF_G = OFF_U + U_SLICE;        // gamma: D floats
     static constexpr size_t BUF = OFF_G + (size_t)D * 4;
-    static constexpr size_t SZ_O = (size_t)(NT / 64) * C * LDO * ES;
     // double buffering when two buffers fit; else one
-    static constexpr int NBUF = 2 * BUF + SZ_O <= 160 * 1024 ? 2 : 1;
-    static constexpr size_t SMEM = NBUF * BUF + SZ_O;
+    static constexpr int NBUF = 2 * BUF <= 160 * 1024 ? 2 : 1;
+    static constexpr size_t SMEM = NBUF * BUF;
     static_assert(BV == 16 * (NT / 64), "one 16-column tile per wave");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert(U_SLICE % 1024 == 0, "U~ slice copies");
@@ -426,9 +424,21 @@ __device__ __forceinline__ void state_fetch(const StateArgs& a, int64_t rec, int
         __builtin_amdgcn_global_load_lds(a.gam + rec * D + lane * 4, (lds_void*)(buf + S::OFF_G), 16, 0, 0);
 }
 
+// Four output values of one lane (consecutive value columns of one token)
+// in the output dtype: 8 bytes for bf16, 16 for fp32.
+template <typename E> struct OQuad;
+template <> struct OQuad<bf16> {
+    typedef bf16x4 T;
+    static __device__ __forceinline__ T pack(f32x4 v) { return T{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]}; }
+};
+template <> struct OQuad<float> {
+    typedef f32x4 T;
+    static __device__ __forceinline__ T pack(f32x4 v) { return v; }
+};
+
 template <typename E, int D, int C, int BV>
-__device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
-                                             int slice, int64_t n, int lane, int wave);
+__device__ __forceinline__ void state_store_o(const StateArgs& a, const typename OQuad<E>::T* oq, int64_t b,
+                                             int64_t h, int slice, int64_t n, int lane, int wave);
 
 // The state at the start of chunk n (this lane's column, its 4 rows per
 // tile) into the checkpoint output, when n starts a requested chunk.
@@ -448,17 +458,22 @@ __device__ __forceinline__ void state_emit(const StateArgs& a, const f32x4* St, 
 }
 
 // One chunk from buffer `buf`: Delta = U~ - W S, O = Q~ S + P Delta,
-// S <- diag(gamma) S + K^T Delta; O goes out through the wave's staging rows.
+// S <- diag(gamma) S + K^T Delta.  O is formed transposed (O^T = S^T Q~^T +
+// Delta^T P^T: the same fragments with the MFMA operands swapped, since an
+// A and a B fragment share one lane layout), so each lane ends with four
+// consecutive value columns of one token; they stay in `oq` and are stored
+// from registers during the next chunk.  No LDS is written here, so no
+// write can wait behind the copy into the other buffer.
 template <typename E, int D, int C, int BV>
-__device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned char* buf, E* sOw, f32x4* St,
-                                              int64_t b, int64_t h, int slice, int64_t n, bool store_prev,
-                                              int lane, int wave)
+__device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned char* buf,
+                                              typename OQuad<E>::T* oq, f32x4* St, int64_t b, int64_t h, int slice,
+                                              int64_t n, bool store_prev, int lane, int wave)
 {
     typedef StateShape<E, D, C, BV> S;
     typedef Frags<E, D, C> F;
     typedef Mma<E> MM;
     typedef typename MM::Frag Frag;
-    constexpr int NB = S::NB, LDO = S::LDO, KT = F::KT, NKS = F::NKS, NKC = F::NKC;
+    constexpr int NB = S::NB, KT = F::KT, NKS = F::NKS, NKC = F::NKC;
     constexpr int KTS = D / 16;
     const int gq = lane >> 4, cl = lane & 15;
     const unsigned char* fl = buf + lane * 16;
@@ -498,9 +513,9 @@ __device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned
         DB[kc] = MM::from_acc(&dl[kc * KT]);
     // the previous chunk's outputs leave while this one computes
     if (store_prev)
-        state_store_o<E, D, C, BV>(a, sOw, b, h, slice, n - 1, lane, wave);
+        state_store_o<E, D, C, BV>(a, oq, b, h, slice, n - 1, lane, wave);
 
-    // O = Q~ S + P Delta  (P is lower triangular: only stored steps).
+    // O^T = S^T Q~^T + Delta^T P^T  (P is lower triangular: only stored steps).
     f32x4 ot[NB];
     {
         Frag aq[NB][NKS], ap[F::NP];
@@ -519,12 +534,12 @@ __device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt)
-                ot[mt] = MM::mma(aq[mt][ks], SB[ks], ot[mt]);
+                ot[mt] = MM::mma(SB[ks], aq[mt][ks], ot[mt]);
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
             for (int kc = 0; kc <= mt / KT; ++kc)
-                ot[mt] = MM::mma(ap[F::p_offset(mt) + kc], DB[kc], ot[mt]);
+                ot[mt] = MM::mma(DB[kc], ap[F::p_offset(mt) + kc], ot[mt]);
         sched_pipeline<NB * NKS>();
     }
 
@@ -547,31 +562,29 @@ __device__ __forceinline__ void state_compute(const StateArgs& a, const unsigned
         sched_pipeline<KTS * NKC>();
     }
 
-    // O: into this wave's staging rows; written out during the next chunk.
+    // O: kept in registers, written out during the next chunk.
 #pragma unroll
     for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sOw[(16 * mt + 4 * gq + i) * LDO + cl] = from_f32<E>(ot[mt][i]);
+        oq[mt] = OQuad<E>::pack(ot[mt]);
 }
 
-// 16-byte stores of one wave's 16 staged output columns of chunk n.
+// The outputs of chunk n held in `oq` (tile mt: token 16 mt + lane % 16,
+// value columns 4 (lane / 16) .. + 3 of this wave's 16); tokens past the end
+// of a ragged last chunk are not stored.
 template <typename E, int D, int C, int BV>
-__device__ __forceinline__ void state_store_o(const StateArgs& a, const E* sOw, int64_t b, int64_t h,
-                                             int slice, int64_t n, int lane, int wave)
+__device__ __forceinline__ void state_store_o(const StateArgs& a, const typename OQuad<E>::T* oq, int64_t b,
+                                             int64_t h, int slice, int64_t n, int lane, int wave)
 {
-    typedef StateShape<E, D, C, BV> S;
-    constexpr int VEC = S::VEC, LDO = S::LDO, CPR = 16 / VEC;   // 16-byte pieces per staged row
+    constexpr int NB = C / 16;
+    const int gq = lane >> 4, cl = lane & 15;
     const int64_t t0 = n * C;
     const int L = (int)min((int64_t)C, a.T - t0);
-    E* o = (E*)a.o;
+    E* o = (E*)a.o + ((b * a.T + t0 + cl) * a.H + h) * D + slice * BV + 16 * wave + 4 * gq;
+    const int64_t tile = (int64_t)16 * a.H * D;    // 16 tokens
 #pragma unroll
-    for (int e = lane; e < C * CPR; e += 64) {
-        const int r = e / CPR, cg = e % CPR;
-        if (r < L)
-            *reinterpret_cast<u32x4*>(o + ((b * a.T + t0 + r) * a.H + h) * D + slice * BV + 16 * wave + cg * VEC) =
-                *reinterpret_cast<const u32x4*>(sOw + r * LDO + cg * VEC);
-    }
+    for (int mt = 0; mt < NB; ++mt)
+        if (16 * mt + cl < L)
+            *reinterpret_cast<typename OQuad<E>::T*>(o + mt * tile) = oq[mt];
 }
 
 template <typename E, int D, int C, int BV>
@@ -581,7 +594,6 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
     constexpr int KTS = D / 16;
     __shared__ __align__(16) unsigned char buf0[S::BUF];
     __shared__ __align__(16) unsigned char buf1[S::NBUF == 2 ? S::BUF : 16];
-    __shared__ __align__(16) E sO[(NT / 64) * C * S::LDO];
 
     // Workgroup -> (sequence*head, chunk segment, column slice).  The NS
     // slices of one segment read the same chunk records: give them the same
@@ -598,7 +610,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
     const int64_t n0 = seg * a.seg_len, n1 = min(a.NC, n0 + a.seg_len);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
     const int col = slice * BV + 16 * wave + cl;     // this lane's state column
-    E* sOw = sO + wave * C * S::LDO;
+    typename OQuad<E>::T oq[S::NB];                   // the previous chunk's outputs
 
     // start state: S0 (or zero) for the first segment -- with segments, the
     // span pass's copy of it, as S_out may be S0 -- else the one the segment
@@ -629,7 +641,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf1, wave, lane);
             if (a.S_chunks)
                 state_emit<D>(a, St, bh, n, gq, col);
-            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, n > n0, lane, wave);
+            state_compute<E, D, C, BV>(a, buf0, oq, St, b, h, slice, n, n > n0, lane, wave);
             if (n + 1 >= n1)
                 break;
             wait_copies();
@@ -638,7 +650,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 2, slice, buf0, wave, lane);
             if (a.S_chunks)
                 state_emit<D>(a, St, bh, n + 1, gq, col);
-            state_compute<E, D, C, BV>(a, buf1, sOw, St, b, h, slice, n + 1, true, lane, wave);
+            state_compute<E, D, C, BV>(a, buf1, oq, St, b, h, slice, n + 1, true, lane, wave);
         }
     } else {
         for (int64_t n = n0; n < n1; ++n) {
@@ -646,14 +658,14 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(StateArgs a)
             __syncthreads();          // chunk n is in buf0
             if (a.S_chunks)
                 state_emit<D>(a, St, bh, n, gq, col);
-            state_compute<E, D, C, BV>(a, buf0, sOw, St, b, h, slice, n, n > n0, lane, wave);
+            state_compute<E, D, C, BV>(a, buf0, oq, St, b, h, slice, n, n > n0, lane, wave);
             __syncthreads();          // everyone is done with buf0
             if (n + 1 < n1)
                 state_fetch<E, D, C, BV>(a, rec0 + n + 1, slice, buf0, wave, lane);
         }
     }
 
-    state_store_o<E, D, C, BV>(a, sOw, b, h, slice, n1 - 1, lane, wave);
+    state_store_o<E, D, C, BV>(a, oq, b, h, slice, n1 - 1, lane, wave);
 
     if (a.S_out && n1 == a.NC) {
         float* so = a.S_out + bh * D * D;
