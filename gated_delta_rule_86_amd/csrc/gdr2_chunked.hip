@@ -273,15 +273,15 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         if (tid == 0)
             *s.Flag() = 0;
         lds_barrier();   // B1: wave totals; the previous chunk is done with LDS
-        if (pre)
-            prep_load<2, WB, WW>(a, np, Rn, t0, c0);
 
         // ---- B: decay-referenced operands ----------------------------------
         if (ab) {
             prep_offsets_operands<PRO, D, E, D, C>(a, R, s, cp.L, t0, c0, lpc, wave, second, G, excl,
                                                    a.gam + rec * D, 0, bw, ww);
-            if (pre)
-                prep_load<3, WB, WW>(a, np, Rn, t0, c0);
+        }
+        if (pre) {
+            prep_load<2, WB, WW>(a, np, Rn, t0, c0);
+            prep_load<3, WB, WW>(a, np, Rn, t0, c0);
         }
         lds_barrier();   // B2: operands in LDS
         if (next < a.nrec)   // phase B has read this chunk's width-1 gates
