@@ -741,10 +741,17 @@ __device__ __forceinline__ void prep_gram(const SL& s, unsigned char* dP, int wa
             const bool same = NH == 1 || (I >> 1) == (J >> 1);
             const E* Bs = same ? s.Eh() : s.E2();
             const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
+            // every fragment of the tile is read before its first MFMA
+            typename MM::Frag fa[NKS], fb[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                fa[ks] = row_frag<E, D>(s.Kr(), 16 * J + cl, 4 * ks + gq);
+                fb[ks] = row_frag<E, D>(Bs, rb, 4 * ks + gq);
+            }
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                acc = MM::mma(row_frag<E, D>(s.Kr(), 16 * J + cl, 4 * ks + gq), row_frag<E, D>(Bs, rb, 4 * ks + gq), acc);
+                acc = MM::mma(fa[ks], fb[ks], acc);
             // lane: M[16I + cl][16J + 4gq + i]
             if (J < I) {
                 *reinterpret_cast<typename M16::Frag*>(s.M() + (16 * I + cl) * LDM + 16 * J + 4 * gq) = M16::pack(acc);
@@ -762,21 +769,36 @@ __device__ __forceinline__ void prep_gram(const SL& s, unsigned char* dP, int wa
             while (I + 1 < NB && F::p_offset(I + 1) <= f)
                 ++I;
             const int m = f - F::p_offset(I);
+            // the k-tiles J = KT m + kt of one step share their half, so the
+            // Q rows (B operand) serve both; every fragment of the step is read
+            // before its first MFMA (a k-tile above the diagonal reads row
+            // block I and its product is discarded)
+            const bool same = NH == 1 || (I >> 1) == ((KT * m) >> 1);
+            const E* Bs = same ? s.Qh() : s.Q2();
+            const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
+            typename MM::Frag fa[KT][NKS], fb[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                fb[ks] = row_frag<E, D>(Bs, rb, 4 * ks + gq);
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+                    fa[kt][ks] = row_frag<E, D>(s.Kr(), 16 * min(KT * m + kt, I) + cl, 4 * ks + gq);
+            }
             f32x4 acc[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+                    acc[kt] = MM::mma(fa[kt][ks], fb[ks], acc[kt]);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
                 const int J = KT * m + kt;
-                acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (J > I)
-                    continue;
-                const bool same = NH == 1 || (I >> 1) == (J >> 1);
-                const E* Bs = same ? s.Qh() : s.Q2();
-                const int rb = same ? 16 * I + cl : 16 * I - 32 + cl;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    acc[kt] = MM::mma(row_frag<E, D>(s.Kr(), 16 * J + cl, 4 * ks + gq),
-                                      row_frag<E, D>(Bs, rb, 4 * ks + gq), acc[kt]);
-                if (J == I) {
+                if (J > I) {
+                    acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                } else if (J == I) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         acc[kt][i] = 4 * gq + i <= cl ? acc[kt][i] : 0.f;

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NTP) void chunk_prep_kernel(PrepArgs a)
         unsigned char* gP = (unsigned char*)a.P + rec * F::P_BYTES;
         if (pre)
             prep_load<4, WB, WW>(a, np, Rn, t0, c0);
-        const bool guard = *s.Flag() != 0;
+        const bool guard = __builtin_amdgcn_readfirstlane(*s.Flag()) != 0;   // wave-uniform
         if (!guard) {
             if (next < a.nrec)
                 prep_copy_g<WG, E, D, C>(a, np, reinterpret_cast<unsigned char*>(sG), wave, lane);
