@@ -768,10 +768,14 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(BwdArgs a)
         // waves 1-7 issue theirs now, while wave 0 inverts, and wave 0 after;
         // at the start of the next record they would queue behind this one's
         // step-4 stores
+        // (the wave test is made wave-uniform: as a per-lane test the two
+        // branches run one after the other, and wave 0's inverse then waits
+        // for registers the other branch's loads write)
         const Rec rnext = rec_of(std::min<int64_t>(r + gridDim.x, a.nrec - 1), a.NC, a.T, a.H);
-        if (tid >= 64)
+        const bool w0 = __builtin_amdgcn_readfirstlane(tid) < 64;
+        if (!w0)
             prep_rows_load<B1, W1, G1, E, D>(a, rnext, tid, raw);
-        if (tid < 64) {
+        if (w0) {
             typedef Mma<float> MF;
             const int lane = tid, gq = lane >> 4, cl = lane & 15;
             {
