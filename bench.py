@@ -470,7 +470,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards across GPUs without communication by (batch, head); "
-              "no multi-GPU run is part of this build)", file=sys.stderr)
+              "only the one-GPU measurement is implemented)", file=sys.stderr)
         sys.exit(2)
 
     import statistics
