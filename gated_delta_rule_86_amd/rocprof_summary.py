@@ -89,7 +89,7 @@ def stats(args):
     f = _find(args.csv, "*kernel_stats.csv")
     rows = list(csv.DictReader(open(f)))
     out = [f"# rocprofv3 kernel statistics: {args.title}", "",
-           f"Command (from the repository root on the GPU box):", "", f"    {args.command}", "",
+           f"Command (from the repository root on the MI355X machine):", "", f"    {args.command}", "",
            f"Kernel sources hash: `{source_hash()}`", "",
            "| kernel | calls | average (us) | total (us) |", "|---|---|---|---|"]
     for r in rows:
@@ -124,7 +124,7 @@ def traffic(args):
     kf = copy_bytes / fetch_max["plain_copy"]
     kw = copy_bytes / write_max["plain_copy"]
     out = [f"# HBM traffic per launch (rocprofv3 --pmc): {args.title}", "",
-           "Commands (from the repository root on the GPU box), one counter per run:", "",
+           "Commands (from the repository root on the MI355X machine), one counter per run:", "",
            f"    {args.command_fetch}", f"    {args.command_write}", "",
            f"Counters are KiB per dispatch.  Each is scaled by what it reads for the "
            f"plain device copy of {copy_bytes} bytes that the benchmark runs "
@@ -158,7 +158,7 @@ def counters(args):
             names.append(c)
         vals.setdefault(kn, {}).setdefault(c, []).append(float(r["Counter_Value"]))
     out = [f"# rocprofv3 counters per launch: {args.title}", "",
-           "Command (from the repository root on the GPU box):", "", f"    {args.command}", "",
+           "Command (from the repository root on the MI355X machine):", "", f"    {args.command}", "",
            f"Kernel sources hash: `{source_hash()}`", "", args.note, "",
            "| kernel | launches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
     for kn in sorted(vals):
