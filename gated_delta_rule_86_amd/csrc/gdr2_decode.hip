@@ -11,7 +11,8 @@
 // and S' is written back in place: 2 x 4 x Dk x Dv bytes of state traffic,
 // the whole cost of the step.  The state stays fp32.
 //
-// One 256-thread workgroup per state.  Thread t owns the 4-column group
+// One 256-thread workgroup per state, four or five resident per CU (see
+// decode_lds_pad).  Thread t owns the 4-column group
 // cg = t % (Dv/4) and the rows rg, rg + RG, ... with rg = t / (Dv/4): every
 // wave reads or writes whole 512-byte rows with 16-byte lanes, so each state
 // tile moves in fully coalesced dwordx4 transactions.
@@ -169,17 +170,39 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+// Dynamic LDS the launch asks for (and leaves unused) to hold the kernel to
+// four resident workgroups per CU instead of the five its registers allow at
+// d = 128 (90-94 VGPRs per lane): taken when the n states then fill whole
+// rounds of workgroups over the CUs better than at five, so the last round
+// does not run on a partly idle chip (256 x 16 states on 256 CUs: exactly
+// four rounds at four per CU, against 3.2 at five).
+static size_t decode_lds_pad(int64_t n, int D)
+{
+    constexpr size_t kPad = 32768;   // with the kernel's ~6.7 KB: 4 x 39.5 KB fit in 160 KB, 5 do not
+    if (D != 128)
+        return 0;
+    const int64_t cus = device_cu_count();
+    if (n <= 4 * cus)
+        return 0;                    // one round either way
+    auto fill = [&](int64_t per_cu) {
+        const int64_t slots = cus * per_cu, rounds = (n + slots - 1) / slots;
+        return (double)n / (double)(rounds * slots);
+    };
+    return fill(4) > fill(5) ? kPad : 0;
+}
+
 template <int D, typename T>
 static hipError_t launch_decode_t(const gdr2_decode_args& a, hipStream_t stream)
 {
     const int64_t n = a.N * a.H;
+    const size_t pad = decode_lds_pad(n, D);
     if (a.prologue != 0)
-        hipLaunchKernelGGL((decode_step_kernel<D, T, true>), dim3((unsigned)n), dim3(256), 0, stream,
+        hipLaunchKernelGGL((decode_step_kernel<D, T, true>), dim3((unsigned)n), dim3(256), pad, stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.b,
                            (const T*)a.w, a.g, a.b_width, a.w_width, a.g_width, a.state,
                            (T*)a.o, a.prologue);
     else
-        hipLaunchKernelGGL((decode_step_kernel<D, T, false>), dim3((unsigned)n), dim3(256), 0, stream,
+        hipLaunchKernelGGL((decode_step_kernel<D, T, false>), dim3((unsigned)n), dim3(256), pad, stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.b,
                            (const T*)a.w, a.g, a.b_width, a.w_width, a.g_width, a.state,
                            (T*)a.o, 0);
